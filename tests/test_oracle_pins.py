@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a closed form, a library routine on a
+special case, an invariant, brute force or a hand-written case from the pages'
+rules.  `test_pins_catch_planted_mistakes` plants plausible mistakes in the
+oracle (on the CPU) and checks that the pins notice them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.dflash_oracle as ref
+from tests import torch_reference as tref
+from workloads import TINY, scaled, synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+SMALL = scaled(TINY, name="pin-small", n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2,
+               head_dim=16, intermediate=96, vocab=257, n_feat_layers=3, target_hidden=32)
+
+
+def small_model(cfg=SMALL, seed=0):
+    # Larger init std than the workloads so that every term moves the logits visibly.
+    return synth.drafter_weights(cfg, seed=seed, std=0.2, gain_std=0.2)
+
+
+def context(cfg, w, T, seed=0):
+    feats = synth.target_features(cfg, T, f"ctx{T}", seed=seed)
+    return ref.prefill_context(cfg, w, feats)
+
+
+# ------------------------------------------------------------------------------------------
+# Fusion and KV injection
+# ------------------------------------------------------------------------------------------
+
+def test_fuse_one_hot_selects_columns():
+    """Closed form: fusing the unit vector e_f returns column f of W_fuse."""
+    w = synth.normal("fuse-w", (8, 12), dtype="f32")
+    X = np.eye(12)[[3, 0, 11]]
+    c = ref.fuse_features(X, w)
+    np.testing.assert_array_equal(c, w.double().numpy()[:, [3, 0, 11]].T)
+
+
+def test_injection_equals_projection_of_concatenated_features():
+    """Associativity: RoPE(W_k (W_fuse X)) == RoPE((W_k W_fuse) X) with the product
+    precomputed, and likewise for V -- injection is a projection of the concatenated
+    multi-layer features into each layer's K/V (KV injection, wiki and blog)."""
+    cfg = SMALL
+    w = small_model()
+    T = 9
+    X = synth.target_features(cfg, T, "assoc").double().numpy()
+    pos = np.arange(T) + 5
+    ks, vs = [], []
+    c = ref.fuse_features(X, w["w_fuse"])
+    for l in range(cfg.n_layers):
+        k, v = ref.inject_kv(c, pos, w[f"wk.{l}"], w[f"wv.{l}"], cfg.n_kv_heads, cfg.head_dim,
+                             cfg.rope_theta)
+        Mk = w[f"wk.{l}"].double().numpy() @ w["w_fuse"].double().numpy()
+        Mv = w[f"wv.{l}"].double().numpy() @ w["w_fuse"].double().numpy()
+        k2 = tref.rope_complex(torch.from_numpy(X @ Mk.T).view(T, cfg.n_kv_heads, cfg.head_dim),
+                               torch.from_numpy(pos), cfg.rope_theta).numpy()
+        v2 = (X @ Mv.T).reshape(T, cfg.n_kv_heads, cfg.head_dim)
+        np.testing.assert_allclose(k, k2, rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(v, v2, rtol=1e-10, atol=1e-10)
+
+
+# ------------------------------------------------------------------------------------------
+# RoPE
+# ------------------------------------------------------------------------------------------
+
+def test_rope_closed_form_d4():
+    """d = 4, theta = 1e4: pair (0,2) turns by pos * 1, pair (1,3) by pos * 1e-2."""
+    z = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    out = ref.rope(z, np.array([2]), 1e4)[0, 0]
+    a, b = 2.0, 0.02
+    want = [1 * math.cos(a) - 3 * math.sin(a), 2 * math.cos(b) - 4 * math.sin(b),
+            3 * math.cos(a) + 1 * math.sin(a), 4 * math.cos(b) + 2 * math.sin(b)]
+    np.testing.assert_allclose(out, want, rtol=1e-14, atol=1e-14)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((6, 3, 16))
+    pos = rng.integers(0, 5000, 6)
+    np.testing.assert_array_equal(ref.rope(z, np.zeros(6), 1e6), z)            # pos 0 = identity
+    np.testing.assert_allclose(np.linalg.norm(ref.rope(z, pos, 1e6), axis=-1),
+                               np.linalg.norm(z, axis=-1), rtol=1e-12)          # norm preserved
+    q, k = rng.standard_normal((1, 1, 16)), rng.standard_normal((1, 1, 16))
+    dots = []
+    for shift in (0, 17, 4096):                                                 # relative position
+        qa = ref.rope(q, np.array([30 + shift]), 1e4)
+        kb = ref.rope(k, np.array([7 + shift]), 1e4)
+        dots.append(float((qa * kb).sum()))
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-9)
+
+
+def test_rope_matches_complex_rotation():
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((5, 2, 32))
+    pos = np.array([0, 1, 100, 2047, 32783])
+    want = tref.rope_complex(torch.from_numpy(z), torch.from_numpy(pos), 1.5e5).numpy()
+    np.testing.assert_allclose(ref.rope(z, pos, 1.5e5), want, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------
+# RMSNorm, attention
+# ------------------------------------------------------------------------------------------
+
+def test_rms_norm_closed_form_and_library():
+    g = np.linspace(0.5, 1.5, 8)
+    c = 3.0
+    out = ref.rms_norm(np.full((1, 8), c), g, 1e-6)
+    np.testing.assert_allclose(out[0], g * c / math.sqrt(c * c + 1e-6), rtol=1e-14)
+    z = np.random.default_rng(3).standard_normal((4, 8))
+    lib = torch.nn.functional.rms_norm(torch.from_numpy(z), (8,), torch.from_numpy(g), eps=1e-6)
+    np.testing.assert_allclose(ref.rms_norm(z, g, 1e-6), lib.numpy(), rtol=1e-13)
+
+
+def test_attention_against_sdpa_and_special_cases():
+    rng = np.random.default_rng(4)
+    R, nq, nkv, d, N = 16, 8, 2, 16, 37
+    q = rng.standard_normal((R, nq, d))
+    k = rng.standard_normal((N, nkv, d))
+    v = rng.standard_normal((N, nkv, d))
+    o = ref.attention(q, k, v)
+    qt = torch.from_numpy(q).transpose(0, 1).contiguous()
+    kt = torch.from_numpy(k).repeat_interleave(nq // nkv, 1).transpose(0, 1).contiguous()
+    vt = torch.from_numpy(v).repeat_interleave(nq // nkv, 1).transpose(0, 1).contiguous()
+    lib = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).transpose(0, 1).numpy()
+    np.testing.assert_allclose(o, lib, rtol=1e-11, atol=1e-12)
+    # one key -> its value, whatever the query
+    o1 = ref.attention(q, k[:1], v[:1])
+    np.testing.assert_allclose(o1, np.broadcast_to(v[:1].repeat(nq // nkv, 1), o1.shape),
+                               rtol=1e-14)
+    # identical keys -> mean of the values
+    kk = np.repeat(k[:1], N, axis=0)
+    o2 = ref.attention(q, kk, v)
+    np.testing.assert_allclose(o2, np.broadcast_to(v.mean(0).repeat(nq // nkv, 0), o2.shape),
+                               rtol=1e-12, atol=1e-13)
+    # no mask: the output does not depend on the order of the keys
+    perm = rng.permutation(N)
+    np.testing.assert_allclose(ref.attention(q, k[perm], v[perm]), o, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------
+# Whole draft pass
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0, 23])
+def test_draft_pass_matches_independent_torch_model(T):
+    """With zero context the step is a plain bidirectional pre-norm transformer over the
+    block; with context, the injected K/V are extra keys of every layer.  Compared with an
+    independent float64 implementation built from torch library layers."""
+    cfg = SMALL
+    w = small_model()
+    ks, vs = context(cfg, w, T) if T else ([], [])
+    out = ref.draft_block(cfg, w, ks, vs, anchor=17, want_logits=True)
+    lib = tref.draft_logits(cfg, w, ks, vs, anchor=17).numpy()
+    np.testing.assert_allclose(out["logits"], lib, rtol=1e-9, atol=1e-9)
+    np.testing.assert_array_equal(out["ids"], lib.argmax(-1))
+
+
+def test_gqa_with_replicated_kv_equals_mha():
+    cfg = SMALL
+    w = small_model()
+    T = 11
+    feats = synth.target_features(cfg, T, "gqa")
+    mha = scaled(cfg, n_kv_heads=cfg.n_q_heads)
+    wm = dict(w)
+    rep = cfg.n_q_heads // cfg.n_kv_heads
+    for l in range(cfg.n_layers):
+        for nm in ("wk", "wv"):
+            t = w[f"{nm}.{l}"].view(cfg.n_kv_heads, cfg.head_dim, cfg.hidden)
+            wm[f"{nm}.{l}"] = t.repeat_interleave(rep, 0).reshape(-1, cfg.hidden)
+    a = ref.draft_block(cfg, w, *ref.prefill_context(cfg, w, feats), anchor=3, want_logits=True)
+    b = ref.draft_block(mha, wm, *ref.prefill_context(mha, wm, feats), anchor=3, want_logits=True)
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=1e-11, atol=1e-11)
+
+
+def test_context_order_is_irrelevant_but_positions_matter():
+    """Bidirectional attention without a mask: permuting where injected entries are stored
+    (the page table) changes nothing; moving the whole frame by a constant changes nothing
+    either (RoPE depends on relative positions only)."""
+    cfg = SMALL
+    w = small_model()
+    T = 20
+    feats = synth.target_features(cfg, T, "perm")
+    ks, vs = ref.prefill_context(cfg, w, feats)
+    base = ref.draft_block(cfg, w, ks, vs, anchor=5, want_logits=True)["logits"]
+    perm = np.random.default_rng(5).permutation(T)
+    p = ref.draft_block(cfg, w, [k[perm] for k in ks], [v[perm] for v in vs], anchor=5,
+                        want_logits=True)["logits"]
+    np.testing.assert_allclose(p, base, rtol=1e-11, atol=1e-11)
+
+
+def test_argmax_planted_row_and_lowest_index_tie():
+    cfg = SMALL
+    w = small_model()
+    ks, vs = context(cfg, w, 7)
+    out = ref.draft_block(cfg, w, ks, vs, anchor=9, want_hidden=True)
+    y = ref.rms_norm(out["hidden"][-1][1:], w["final_norm"], cfg.rms_eps)   # [15, H]
+    lm = w["lm_head"].double().clone()
+    r, j = 123, 4
+    lm[r] = torch.from_numpy(y[j] / np.linalg.norm(y[j]) * 50.0)
+    w2 = dict(w, lm_head=lm)
+    o2 = ref.draft_block(cfg, w2, ks, vs, anchor=9)
+    assert o2["ids"][j] == r
+    lm[40] = lm[r]                      # exact duplicate at a lower index wins the tie
+    o3 = ref.draft_block(cfg, dict(w, lm_head=lm), ks, vs, anchor=9)
+    assert o3["ids"][j] == 40 and o3["gap"][j] == 0.0
+
+
+# ------------------------------------------------------------------------------------------
+# Greedy verify
+# ------------------------------------------------------------------------------------------
+
+def test_verify_greedy_hand_cases():
+    with open(os.path.join(HERE, "golden", "verify_greedy_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        acc, bonus, emitted = ref.verify_greedy(c["draft"], c["target"])
+        assert (acc, bonus, emitted) == (c["accept_len"], c["bonus"], c["emitted"]), c["why"]
+
+
+def test_verify_greedy_brute_force_over_all_match_masks():
+    """All 2^15 patterns of which drafts equal the target: accept_len = 1 + number of
+    trailing ones of the mask = position of the first mismatch + 1, always in [1, 16]."""
+    rng = np.random.default_rng(6)
+    for mask in range(1 << 15):
+        d = rng.integers(0, 1000, 15)
+        t = np.append(d.copy(), 7)
+        for i in range(15):
+            if not (mask >> i) & 1:
+                t[i] = d[i] + 1
+        acc, bonus, emitted = ref.verify_greedy(d, t)
+        first_zero = next((i for i in range(15) if not (mask >> i) & 1), 15)
+        assert acc == first_zero + 1 and 1 <= acc <= 16
+        assert bonus == t[first_zero] and emitted == list(d[:first_zero]) + [t[first_zero]]
+
+
+def test_planted_targets_pin_accept_length():
+    d = synth.uniform_ints("plant-d", (64, 15), 0, 99)
+    t, k = synth.planted_targets(d, 100, "plant")
+    for b in range(64):
+        assert ref.verify_greedy(d[b], t[b])[0] == k[b] + 1
+    t, k = synth.planted_targets(d, 100, "plant-full", k=np.full(64, 15))
+    assert all(ref.verify_greedy(d[b], t[b])[0] == 16 for b in range(64))
+
+
+# ------------------------------------------------------------------------------------------
+# Temperature-1 verify
+# ------------------------------------------------------------------------------------------
+
+def _cells(w):
+    """Cut points of the inverse-CDF partition of [0, 1) for weights w."""
+    c = np.cumsum(w) / np.sum(w)
+    return np.concatenate([[0.0], c])
+
+
+def _mid(lo, hi):
+    return 0.5 * (lo + hi)
+
+
+def test_verify_sampled_preserves_target_distribution_exactly():
+    """Exact enumeration over the cells of the uniforms for one draft position and a
+    4-token vocabulary: P(first emitted token = x) = p(x), the distribution-preservation
+    property of the blog's 'How it works' section, for several (q, p) pairs."""
+    rng = np.random.default_rng(7)
+    for trial in range(12):
+        dl = rng.standard_normal((1, 4)) * 2.0
+        tl = rng.standard_normal((2, 4)) * 2.0
+        q, p = ref.softmax(dl[0]), ref.softmax(tl[0])
+        prob = np.zeros(4)
+        qc = _cells(q)
+        for j in range(4):                                    # draft cell -> d = j
+            ud = _mid(qc[j], qc[j + 1])
+            ratio = min(1.0, p[j] / q[j])
+            for ua, wa in ((ratio * 0.5, ratio), (ratio + (1 - ratio) * 0.5, 1 - ratio)):
+                if wa <= 0:
+                    continue
+                r = np.maximum(p - q, 0)
+                rc = _cells(r) if r.sum() > 0 else _cells(p)
+                for x in range(4):                            # resample cell -> x
+                    wr = rc[x + 1] - rc[x]
+                    if wr <= 0:
+                        continue
+                    o = ref.verify_sampled(dl, tl, [ud], [ua], _mid(rc[x], rc[x + 1]))
+                    prob[o["emitted"][0]] += q[j] * wa * wr
+        np.testing.assert_allclose(prob, p, rtol=1e-12, atol=1e-14)
+
+
+def test_verify_sampled_equal_distributions_always_accept():
+    rng = np.random.default_rng(8)
+    logits = rng.standard_normal((16, 50))
+    for s in range(20):
+        ud, ua = rng.random(15), rng.random(15)
+        o = ref.verify_sampled(logits[:15], logits, ud, ua, rng.random())
+        assert o["accept_len"] == 16 and len(o["emitted"]) == 16
+        assert o["emitted"][:15] == list(o["draft_ids"])
+
+
+def test_verify_sampled_monte_carlo_second_position():
+    """Two draft positions, 3-token vocabulary, 20000 seeded draws: the second emitted
+    token (when there is one) follows p_2 (chi-square at the 1e-4 level)."""
+    rng = np.random.default_rng(9)
+    dl = rng.standard_normal((2, 3)) * 1.5
+    tl = rng.standard_normal((3, 3)) * 1.5
+    p2 = ref.softmax(tl[1])
+    counts = np.zeros(3)
+    for _ in range(20000):
+        o = ref.verify_sampled(dl, tl, rng.random(2), rng.random(2), rng.random())
+        if len(o["emitted"]) >= 2:
+            counts[o["emitted"][1]] += 1
+    n = counts.sum()
+    chi2 = ((counts - n * p2) ** 2 / (n * p2)).sum()
+    assert chi2 < 18.4          # chi-square, 2 dof, p = 1e-4
+
+
+# ------------------------------------------------------------------------------------------
+# The pins notice planted mistakes
+# ------------------------------------------------------------------------------------------
+
+def _whole_pass_error(cfg=SMALL, T=23):
+    w = small_model()
+    ks, vs = context(cfg, w, T)
+    a = ref.draft_block(cfg, w, ks, vs, anchor=17, want_logits=True)["logits"]
+    b = tref.draft_logits(cfg, w, ks, vs, anchor=17).numpy()
+    return float(np.abs(a - b).max())
+
+
+@pytest.mark.parametrize("mutation", ["rope_sign", "rope_interleaved", "drop_gain",
+                                      "causal_mask", "kv_group", "silu_sign", "scale"])
+def test_pins_catch_planted_mistakes(monkeypatch, mutation):
+    assert _whole_pass_error() < 1e-8
+    orig_rope, orig_rms, orig_attn, orig_silu = ref.rope, ref.rms_norm, ref.attention, ref.silu
+
+    if mutation == "rope_sign":
+        def bad(z, pos, theta):
+            return orig_rope(z, -np.asarray(pos), theta)
+        monkeypatch.setattr(ref, "rope", bad)
+    elif mutation == "rope_interleaved":
+        def bad(z, pos, theta):
+            d = z.shape[-1]
+            perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+            inv = np.argsort(perm)
+            return orig_rope(z[..., perm], pos, theta)[..., inv]
+        monkeypatch.setattr(ref, "rope", bad)
+    elif mutation == "drop_gain":
+        monkeypatch.setattr(ref, "rms_norm", lambda z, g, eps: orig_rms(z, np.ones_like(ref.f64(g)), eps))
+    elif mutation == "causal_mask":
+        def bad(q, k, v):
+            return orig_attn(q, k[: k.shape[0] - 8], v[: v.shape[0] - 8])
+        monkeypatch.setattr(ref, "attention", bad)
+    elif mutation == "kv_group":
+        def bad(q, k, v):
+            return orig_attn(q, k[:, ::-1].copy(), v[:, ::-1].copy())
+        monkeypatch.setattr(ref, "attention", bad)
+    elif mutation == "silu_sign":
+        monkeypatch.setattr(ref, "silu", lambda z: z / (1.0 + np.exp(z)))
+    elif mutation == "scale":
+        monkeypatch.setattr(ref, "attention", lambda q, k, v: orig_attn(q * math.sqrt(2), k, v))
+    assert _whole_pass_error() > 1e-4, mutation
