@@ -1,0 +1,250 @@
+"""ctypes binding of libdflash.so (argument marshalling only).
+
+Every computation of the draft step runs in the HIP kernels of libdflash.so; this module
+only turns torch device tensors into pointers, fills the C structs and checks status
+codes.  Importing it fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+DFLASH_F32, DFLASH_BF16 = 0, 1
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
+          -3: "workspace or packed buffer too small", -4: "HIP launch error"}
+
+# Symbols declared in include/dflash.h.
+EXPORTS = (
+    "dflash_packed_weights_size", "dflash_pack_weights", "dflash_workspace_size",
+    "dflash_workspace_init", "dflash_fuse_inject_kv", "dflash_draft_block",
+    "dflash_verify_accept", "dflash_verify_sampled_workspace_size",
+    "dflash_verify_accept_sampled", "dflash_error_string",
+)
+
+
+class DflashError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class Config(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("intermediate", C.c_int32), ("vocab", C.c_int32), ("feat_dim", C.c_int32),
+                ("block_size", C.c_int32), ("page_size", C.c_int32),
+                ("mask_token_id", C.c_int32), ("rope_theta", C.c_float),
+                ("rms_eps", C.c_float), ("dtype", C.c_int32)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("w_fuse", C.c_void_p), ("lm_head", C.c_void_p), ("final_norm", C.c_void_p),
+                ("attn_norm", C.POINTER(C.c_void_p)), ("wq", C.POINTER(C.c_void_p)),
+                ("wk", C.POINTER(C.c_void_p)), ("wv", C.POINTER(C.c_void_p)),
+                ("wo", C.POINTER(C.c_void_p)), ("mlp_norm", C.POINTER(C.c_void_p)),
+                ("w_gate", C.POINTER(C.c_void_p)), ("w_up", C.POINTER(C.c_void_p)),
+                ("w_down", C.POINTER(C.c_void_p))]
+
+
+class KVCache(C.Structure):
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p),
+                ("ctx_lens", C.c_void_p), ("num_pages", C.c_int32),
+                ("max_pages_per_seq", C.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> C.CDLL:
+    """Load libdflash.so; raises if it is missing (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m block_diffusion_drafter_hidden_amd.build`")
+    lib = C.CDLL(path)
+    P, S, I32, SZ = C.c_void_p, C.c_int, C.c_int32, C.c_size_t
+    sig = {
+        "dflash_packed_weights_size": (SZ, [P]),
+        "dflash_pack_weights": (S, [P, P, P, SZ, P]),
+        "dflash_workspace_size": (SZ, [P, I32, I32, I32]),
+        "dflash_workspace_init": (S, [P, SZ, P]),
+        "dflash_fuse_inject_kv": (S, [P, P, P, P, P, P, I32, P, SZ, P]),
+        "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, SZ, P]),
+        "dflash_verify_accept": (S, [P, P, I32, P, P, P, P]),
+        "dflash_verify_sampled_workspace_size": (SZ, [I32, I32]),
+        "dflash_verify_accept_sampled": (S, [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
+        "dflash_error_string": (C.c_char_p, [S]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise DflashError(status, what)
+
+
+def make_config(cfg) -> Config:
+    """C config from a workloads.DrafterConfig (or any object with the same fields)."""
+    return Config(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                  cfg.intermediate, cfg.vocab, cfg.feat_dim, cfg.block_size, cfg.page_size,
+                  cfg.mask_id, float(cfg.rope_theta), float(cfg.rms_eps),
+                  DFLASH_BF16 if cfg.dtype == "bf16" else DFLASH_F32)
+
+
+# ---------------------------------------------------------------------------------------
+# Thin wrappers with the ABI's names
+# ---------------------------------------------------------------------------------------
+
+def packed_weights_size(ccfg: Config) -> int:
+    return int(load_library().dflash_packed_weights_size(C.byref(ccfg)))
+
+
+def pack_weights(ccfg: Config, w: Dict[str, torch.Tensor], n_layers: int,
+                 packed: torch.Tensor, stream=None) -> None:
+    arr = lambda key: (C.c_void_p * n_layers)(*[w[f"{key}.{l}"].data_ptr() for l in range(n_layers)])
+    keep = {k: arr(k) for k in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate",
+                                "w_up", "w_down")}
+    cw = Weights(w["w_fuse"].data_ptr(), w["lm_head"].data_ptr(), w["final_norm"].data_ptr(),
+                 *[C.cast(keep[k], C.POINTER(C.c_void_p)) for k in
+                   ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")])
+    _check(load_library().dflash_pack_weights(C.byref(ccfg), C.byref(cw), _ptr(packed),
+                                              packed.numel() * packed.element_size(),
+                                              _stream(stream)), "dflash_pack_weights")
+
+
+def workspace_size(ccfg: Config, max_batch: int, max_inject_rows: int, max_ctx: int) -> int:
+    return int(load_library().dflash_workspace_size(C.byref(ccfg), max_batch, max_inject_rows,
+                                                    max_ctx))
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check(load_library().dflash_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream)), "dflash_workspace_init")
+
+
+def make_cache(k_pool, v_pool, block_table, ctx_lens, num_pages, max_pages) -> KVCache:
+    return KVCache(k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                   ctx_lens.data_ptr(), num_pages, max_pages)
+
+
+def fuse_inject_kv(ccfg: Config, packed, cache: KVCache, feats, seq_idx, pos, ws,
+                   stream=None) -> None:
+    n_tok = int(feats.shape[0])
+    _check(load_library().dflash_fuse_inject_kv(
+        C.byref(ccfg), _ptr(packed), C.byref(cache), _ptr(feats), _ptr(seq_idx), _ptr(pos),
+        n_tok, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "dflash_fuse_inject_kv")
+
+
+def draft_block(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_ids, ws,
+                logits_out=None, stream=None) -> None:
+    batch = int(anchor_ids.shape[0])
+    _check(load_library().dflash_draft_block(
+        C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
+        _ptr(draft_ids), _ptr(logits_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "dflash_draft_block")
+
+
+def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream=None) -> None:
+    batch = int(draft_ids.shape[0])
+    _check(load_library().dflash_verify_accept(
+        _ptr(draft_ids), _ptr(target_ids), batch, _ptr(accept_len), _ptr(bonus),
+        _ptr(emitted), _stream(stream)), "dflash_verify_accept")
+
+
+def verify_sampled_workspace_size(batch: int, vocab: int) -> int:
+    return int(load_library().dflash_verify_sampled_workspace_size(batch, vocab))
+
+
+def verify_accept_sampled(draft_logits, target_logits, u_draft, u_accept, u_resample,
+                          draft_ids, accept_len, emitted, ws, stream=None) -> None:
+    batch, _, vocab = draft_logits.shape
+    _check(load_library().dflash_verify_accept_sampled(
+        _ptr(draft_logits), _ptr(target_logits), _ptr(u_draft), _ptr(u_accept),
+        _ptr(u_resample), int(batch), int(vocab), _ptr(draft_ids), _ptr(accept_len),
+        _ptr(emitted), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "dflash_verify_accept_sampled")
+
+
+def error_string(status: int) -> str:
+    return load_library().dflash_error_string(status).decode()
+
+
+# ---------------------------------------------------------------------------------------
+# Device-memory holder for one drafter (torch owns the memory; the library fills it)
+# ---------------------------------------------------------------------------------------
+
+@dataclass
+class PagedCache:
+    k_pool: torch.Tensor          # [L, num_pages, n_kv, 16, d]
+    v_pool: torch.Tensor
+    block_table: torch.Tensor     # [B, max_pages] int32
+    ctx_lens: torch.Tensor        # [B] int32
+    num_pages: int
+    max_pages: int
+
+    def c(self) -> KVCache:
+        return make_cache(self.k_pool, self.v_pool, self.block_table, self.ctx_lens,
+                          self.num_pages, self.max_pages)
+
+
+class Drafter:
+    """Packed weights + workspace of one drafter on one device."""
+
+    def __init__(self, cfg, weights_dev: Dict[str, torch.Tensor], max_batch: int,
+                 max_ctx: int, max_inject_rows: int = 256, device="cuda"):
+        self.cfg = cfg
+        self.ccfg = make_config(cfg)
+        self.device = torch.device(device)
+        n = packed_weights_size(self.ccfg)
+        if n == 0:
+            raise DflashError(-2, "dflash_packed_weights_size")
+        self.packed = torch.empty(n, dtype=torch.uint8, device=self.device)
+        pack_weights(self.ccfg, weights_dev, cfg.n_layers, self.packed)
+        self.embed = weights_dev["embed"]
+        self.ws_bytes = workspace_size(self.ccfg, max_batch, max_inject_rows, max_ctx)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        workspace_init(self.ws)
+
+    def new_cache(self, block_table, ctx_lens, num_pages: int) -> PagedCache:
+        cfg = self.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        shape = (cfg.n_layers, num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        bt = torch.as_tensor(block_table, dtype=torch.int32).to(self.device).contiguous()
+        cl = torch.as_tensor(ctx_lens, dtype=torch.int32).to(self.device).contiguous()
+        return PagedCache(torch.zeros(shape, dtype=dt, device=self.device),
+                          torch.zeros(shape, dtype=dt, device=self.device), bt, cl,
+                          num_pages, int(bt.shape[1]))
+
+    def inject(self, cache: PagedCache, feats, seq_idx, pos, stream=None) -> None:
+        fuse_inject_kv(self.ccfg, self.packed, cache.c(), feats, seq_idx, pos, self.ws, stream)
+
+    def draft(self, cache: PagedCache, anchor_ids, draft_ids, logits_out=None,
+              stream=None) -> None:
+        draft_block(self.ccfg, self.packed, self.embed, cache.c(), anchor_ids, draft_ids,
+                    self.ws, logits_out, stream)

@@ -1,0 +1,603 @@
+// Host side of the DFlash C ABI: argument validation, packed-weight and workspace layouts,
+// GEMM planning, and the launch sequence of each step call.  Nothing here allocates device
+// memory or synchronizes; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "dflash.h"
+#include "attention.h"
+#include "gemm.h"
+#include "sampled.h"
+#include "small.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kCounterBytes = 256 * 1024;           // 65536 32-bit counters
+constexpr size_t kKeyStride = 128;                     // bytes between argmax keys
+constexpr size_t kKeyBytes = 768 * 1024;               // 6144 argmax rows
+constexpr size_t kSyncBytes = kCounterBytes + kKeyBytes;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4) - 1;  // last one: argmax done counter
+constexpr int kMaxArgmaxRows = (int)(kKeyBytes / kKeyStride);
+constexpr int kTargetWaves = 4096;
+constexpr int kAttnTargetWGs = 512;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+struct Dims {
+  int L, H, nq, nkv, d, I, V, F, G;
+  int bf16;
+  size_t es;   // element size of weights / operands
+  int ktile;   // K per k-tile
+  float theta, eps;
+  int mask;
+};
+
+dflash_status check_config(const dflash_config* c, Dims* o) {
+  if (!c) return DFLASH_ERR_INVALID_ARG;
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0 || c->feat_dim <= 0)
+    return DFLASH_ERR_INVALID_ARG;
+  if (c->block_size != 16 || c->page_size != 16) return DFLASH_ERR_UNSUPPORTED;
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_INVALID_ARG;
+  if (c->hidden % 64 || c->feat_dim % 64 || c->intermediate % 64 || c->vocab % 64)
+    return DFLASH_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (!block_attention_supported(c->head_dim, c->n_q_heads / c->n_kv_heads))
+    return DFLASH_ERR_UNSUPPORTED;
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_ERR_INVALID_ARG;
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
+  if (o) {
+    o->L = c->n_layers;
+    o->H = c->hidden;
+    o->nq = c->n_q_heads;
+    o->nkv = c->n_kv_heads;
+    o->d = c->head_dim;
+    o->I = c->intermediate;
+    o->V = c->vocab;
+    o->F = c->feat_dim;
+    o->G = c->n_q_heads / c->n_kv_heads;
+    o->bf16 = c->dtype == DFLASH_BF16;
+    o->es = o->bf16 ? 2 : 4;
+    o->ktile = o->bf16 ? 32 : 16;
+    o->theta = c->rope_theta;
+    o->eps = c->rms_eps;
+    o->mask = c->mask_token_id;
+  }
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Packed weight buffer layout.
+// ---------------------------------------------------------------------------------------
+struct Packed {
+  size_t final_norm, w_fuse, lm_head, layer0, layer_stride;
+  size_t attn_norm, mlp_norm, wqkv, wo, wgu, wd;  // offsets inside one layer
+  size_t total;
+};
+
+Packed packed_layout(const Dims& m) {
+  Packed p{};
+  size_t off = 0;
+  p.final_norm = off;
+  off = align_up(off + (size_t)m.H * 4);
+  p.w_fuse = off;
+  off = align_up(off + (size_t)m.H * m.F * m.es);
+  p.lm_head = off;
+  off = align_up(off + (size_t)m.V * m.H * m.es);
+  p.layer0 = off;
+  size_t lo = 0;
+  p.attn_norm = lo;
+  lo = align_up(lo + (size_t)m.H * 4);
+  p.mlp_norm = lo;
+  lo = align_up(lo + (size_t)m.H * 4);
+  p.wqkv = lo;
+  lo = align_up(lo + (size_t)(m.nq + 2 * m.nkv) * m.d * m.H * m.es);
+  p.wo = lo;
+  lo = align_up(lo + (size_t)m.H * m.nq * m.d * m.es);
+  p.wgu = lo;
+  lo = align_up(lo + (size_t)2 * m.I * m.H * m.es);
+  p.wd = lo;
+  lo = align_up(lo + (size_t)m.H * m.I * m.es);
+  p.layer_stride = lo;
+  p.total = off + lo * m.L;
+  return p;
+}
+
+// ---------------------------------------------------------------------------------------
+// GEMM planning.
+// ---------------------------------------------------------------------------------------
+struct Plan {
+  int mt, n_mblocks, tpw, splits, kts, targets;
+  size_t partial_bytes;
+  int counters;
+};
+
+Plan plan_gemm(int n_tiles, int KT, int M, int group, int tpw, int layers, bool allow_split) {
+  Plan p{};
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.n_mblocks = cdiv(M, 16 * p.mt);
+  p.tpw = tpw;
+  const int ksub = 4 / tpw;
+  const long long wgs = (long long)(n_tiles / tpw) * p.n_mblocks * layers;
+  int splits = 1;
+  if (allow_split) {
+    splits = (int)std::lround((double)kTargetWaves / (double)(wgs * 4));
+    const int max_splits = std::max(1, KT / (4 * ksub));
+    splits = std::max(1, std::min(splits, max_splits));
+  }
+  p.kts = cdiv(KT, splits);
+  p.splits = cdiv(KT, p.kts);
+  p.targets = (group / tpw) * p.splits;
+  const int groups = n_tiles / group;
+  if (p.targets > 1) {
+    p.partial_bytes = (size_t)layers * groups * p.n_mblocks * p.targets * tpw * p.mt * 256 * 4;
+    p.counters = layers * groups * p.n_mblocks;
+  }
+  return p;
+}
+
+GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const void* A, int lda,
+                       int M, int n_tiles, int group, float* partials, unsigned* counters) {
+  GemmParams g;
+  std::memset(&g, 0, sizeof(g));
+  g.W = W;
+  g.nt0 = nt0;
+  g.KT = KT;
+  g.A = A;
+  g.lda = lda;
+  g.M = M;
+  g.n_tiles = n_tiles;
+  g.group = group;
+  g.tpw = pl.tpw;
+  g.splits = pl.splits;
+  g.kts = pl.kts;
+  g.n_mblocks = pl.n_mblocks;
+  g.partials = partials;
+  g.counters = counters;
+  return g;
+}
+
+struct Carver {
+  size_t off;
+  explicit Carver(size_t start) : off(start) {}
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Per-call plans of the draft and inject steps.
+// ---------------------------------------------------------------------------------------
+struct DraftPlan {
+  Plan qkv, o, gu, dn, lm;
+  int nc, chunk;
+  size_t x, u, q, bk, bv, ao, h, y, part, apart_o, apart_ml;
+  size_t total;
+};
+
+DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
+  DraftPlan p{};
+  const int rows = B * 16;
+  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, m.d / 16, 1, 1, true);
+  p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 1, true);
+  p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 2, 1, true);
+  p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 1, true);
+  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, B * 15, 4, 4, 1, false);
+  const int kv_groups = B * m.nkv;
+  const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
+  p.nc = std::max(1, std::min(cdiv(kAttnTargetWGs, kv_groups), max_chunks));
+  p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
+  Carver c(kSyncBytes);
+  p.x = c.take((size_t)rows * m.H * 4);
+  p.u = c.take((size_t)rows * m.H * m.es);
+  p.q = c.take((size_t)rows * m.nq * m.d * 4);
+  p.bk = c.take((size_t)rows * m.nkv * m.d * 4);
+  p.bv = c.take((size_t)rows * m.nkv * m.d * 4);
+  p.ao = c.take((size_t)rows * m.nq * m.d * m.es);
+  p.h = c.take((size_t)rows * m.I * m.es);
+  p.y = c.take((size_t)B * 15 * m.H * m.es);
+  const size_t part = std::max({p.qkv.partial_bytes, p.o.partial_bytes, p.gu.partial_bytes,
+                                p.dn.partial_bytes, (size_t)16});
+  p.part = c.take(part);
+  const size_t R = (size_t)m.G * 16;
+  p.apart_o = c.take((size_t)kv_groups * (p.nc + 1) * R * m.d * 4);
+  p.apart_ml = c.take((size_t)kv_groups * (p.nc + 1) * R * 2 * 4);
+  p.total = c.off;
+  return p;
+}
+
+struct InjectPlan {
+  Plan fuse, kv;
+  size_t c, part, total;
+};
+
+InjectPlan inject_plan(const Dims& m, int rows) {
+  InjectPlan p{};
+  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 1, true);
+  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, m.d / 16, 1, m.L, true);
+  Carver c(kSyncBytes);
+  p.c = c.take((size_t)rows * m.H * m.es);
+  p.part = c.take(std::max({p.fuse.partial_bytes, p.kv.partial_bytes, (size_t)16}));
+  p.total = c.off;
+  return p;
+}
+
+bool counters_fit(const Plan& p) { return p.counters <= kMaxCounters; }
+
+constexpr int kInjectChunkRows = 256;
+
+#define DF_TRY(expr)                                  \
+  do {                                                \
+    hipError_t _e = (expr);                           \
+    if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
+  } while (0)
+
+}  // namespace
+
+// =========================================================================================
+// C ABI
+// =========================================================================================
+extern "C" {
+
+const char* dflash_error_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_INVALID_ARG: return "invalid argument";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DFLASH_ERR_WORKSPACE: return "workspace or packed buffer too small";
+    case DFLASH_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t dflash_packed_weights_size(const dflash_config* cfg) {
+  Dims m;
+  if (check_config(cfg, &m) != DFLASH_OK) return 0;
+  return packed_layout(m).total;
+}
+
+dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights* w,
+                                  void* packed, size_t packed_bytes, hipStream_t stream) {
+  Dims m;
+  dflash_status st = check_config(cfg, &m);
+  if (st != DFLASH_OK) return st;
+  if (!w || !packed || !w->w_fuse || !w->lm_head || !w->final_norm || !w->attn_norm ||
+      !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm || !w->w_gate || !w->w_up ||
+      !w->w_down)
+    return DFLASH_ERR_INVALID_ARG;
+  for (int l = 0; l < m.L; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] ||
+        !w->mlp_norm[l] || !w->w_gate[l] || !w->w_up[l] || !w->w_down[l])
+      return DFLASH_ERR_INVALID_ARG;
+  const Packed P = packed_layout(m);
+  if (packed_bytes < P.total) return DFLASH_ERR_WORKSPACE;
+  char* base = reinterpret_cast<char*>(packed);
+
+  auto pack1 = [&](const void* src, int N, int K, size_t off) -> hipError_t {
+    PackArgs a{};
+    a.src[0] = src;
+    a.seg_tiles[0] = N / 16;
+    a.n_segs = 1;
+    a.n_tiles_total = N / 16;
+    a.KT = K / m.ktile;
+    a.K = K;
+    a.dst = base + off;
+    return launch_pack(m.bf16, a, stream);
+  };
+  DF_TRY(launch_widen(m.bf16, w->final_norm, reinterpret_cast<float*>(base + P.final_norm), m.H,
+                      stream));
+  DF_TRY(pack1(w->w_fuse, m.H, m.F, P.w_fuse));
+  DF_TRY(pack1(w->lm_head, m.V, m.H, P.lm_head));
+  for (int l = 0; l < m.L; ++l) {
+    const size_t lb = P.layer0 + (size_t)l * P.layer_stride;
+    DF_TRY(launch_widen(m.bf16, w->attn_norm[l], reinterpret_cast<float*>(base + lb + P.attn_norm),
+                        m.H, stream));
+    DF_TRY(launch_widen(m.bf16, w->mlp_norm[l], reinterpret_cast<float*>(base + lb + P.mlp_norm),
+                        m.H, stream));
+    PackArgs q{};
+    q.src[0] = w->wq[l];
+    q.src[1] = w->wk[l];
+    q.src[2] = w->wv[l];
+    q.seg_tiles[0] = m.nq * m.d / 16;
+    q.seg_tiles[1] = m.nkv * m.d / 16;
+    q.seg_tiles[2] = m.nkv * m.d / 16;
+    q.n_segs = 3;
+    q.n_tiles_total = (m.nq + 2 * m.nkv) * m.d / 16;
+    q.KT = m.H / m.ktile;
+    q.K = m.H;
+    q.dst = base + lb + P.wqkv;
+    DF_TRY(launch_pack(m.bf16, q, stream));
+    DF_TRY(pack1(w->wo[l], m.H, m.nq * m.d, lb + P.wo));
+    PackArgs gu{};
+    gu.src[0] = w->w_gate[l];
+    gu.src[1] = w->w_up[l];
+    gu.seg_tiles[0] = m.I / 16;
+    gu.seg_tiles[1] = m.I / 16;
+    gu.n_segs = 2;
+    gu.interleave2 = 1;
+    gu.n_tiles_total = 2 * m.I / 16;
+    gu.KT = m.H / m.ktile;
+    gu.K = m.H;
+    gu.dst = base + lb + P.wgu;
+    DF_TRY(launch_pack(m.bf16, gu, stream));
+    DF_TRY(pack1(w->w_down[l], m.H, m.I, lb + P.wd));
+  }
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
+                             int32_t max_inject_rows, int32_t max_ctx) {
+  Dims m;
+  if (check_config(cfg, &m) != DFLASH_OK) return 0;
+  if (max_batch < 0 || max_inject_rows < 0 || max_ctx < 0) return 0;
+  size_t need = kSyncBytes;
+  if (max_batch > 0) need = std::max(need, draft_plan(m, max_batch, max_ctx).total);
+  if (max_inject_rows > 0)
+    need = std::max(need, inject_plan(m, std::min(max_inject_rows, kInjectChunkRows)).total);
+  return need;
+}
+
+dflash_status dflash_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!workspace) return DFLASH_ERR_INVALID_ARG;
+  if (ws_bytes < kSyncBytes) return DFLASH_ERR_WORKSPACE;
+  DF_TRY(launch_zero(workspace, kSyncBytes, stream));
+  return DFLASH_OK;
+}
+
+static dflash_status check_cache(const dflash_kv_cache* c) {
+  if (!c || !c->k_pool || !c->v_pool || !c->block_table || !c->ctx_lens) return DFLASH_ERR_INVALID_ARG;
+  if (c->num_pages <= 0 || c->max_pages_per_seq <= 0) return DFLASH_ERR_INVALID_ARG;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed,
+                                    const dflash_kv_cache* cache, const void* feats,
+                                    const int32_t* seq_idx, const int32_t* pos, int32_t n_tok,
+                                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Dims m;
+  dflash_status st = check_config(cfg, &m);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  if (!packed || !workspace || n_tok < 0) return DFLASH_ERR_INVALID_ARG;
+  if (n_tok == 0) return DFLASH_OK;
+  if (!feats || !seq_idx || !pos) return DFLASH_ERR_INVALID_ARG;
+  const int chunk_rows = std::min<int>(n_tok, kInjectChunkRows);
+  const InjectPlan ip = inject_plan(m, chunk_rows);
+  if (ws_bytes < ip.total) return DFLASH_ERR_WORKSPACE;
+  if (!counters_fit(ip.fuse) || !counters_fit(ip.kv)) return DFLASH_ERR_UNSUPPORTED;
+  const Packed P = packed_layout(m);
+  const char* wb = reinterpret_cast<const char*>(packed);
+  char* ws = reinterpret_cast<char*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  float* part = reinterpret_cast<float*>(ws + ip.part);
+  void* cbuf = ws + ip.c;
+  const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
+
+  for (int r0 = 0; r0 < n_tok; r0 += chunk_rows) {
+    const int rows = std::min(chunk_rows, n_tok - r0);
+    const InjectPlan cp = rows == chunk_rows ? ip : inject_plan(m, rows);
+    {
+      GemmParams g = base_params(cp.fuse, wb + P.w_fuse, 0, m.F / m.ktile,
+                                 reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
+                                 m.F, rows, m.H / 16, 1, part, counters);
+      g.out = cbuf;
+      g.ldo = m.H;
+      DF_TRY(launch_gemm(m.bf16, cp.fuse.mt, EPI_STORE, g, 1, stream));
+    }
+    {
+      GemmParams g = base_params(cp.kv, wb + P.layer0 + P.wqkv, m.nq * m.d / 16, m.H / m.ktile,
+                                 cbuf, m.H, rows, 2 * m.nkv * m.d / 16, m.d / 16, part,
+                                 counters);
+      g.w_zstride = (long long)P.layer_stride;
+      g.n_q = m.nq;
+      g.n_kv = m.nkv;
+      g.head_dim = m.d;
+      g.log_theta = std::log((double)m.theta);
+      g.k_pool = cache->k_pool;
+      g.v_pool = cache->v_pool;
+      g.pool_layer_elems = pool_layer;
+      g.block_table = cache->block_table;
+      g.max_pages = cache->max_pages_per_seq;
+      g.seq_idx = seq_idx + r0;
+      g.pos = pos + r0;
+      DF_TRY(launch_gemm(m.bf16, cp.kv.mt, EPI_INJECT, g, m.L, stream));
+    }
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
+                                 const void* embed, const dflash_kv_cache* cache,
+                                 const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
+                                 float* logits_out, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Dims m;
+  dflash_status st = check_config(cfg, &m);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  if (!packed || !embed || !anchor_ids || !draft_ids || !workspace || batch <= 0)
+    return DFLASH_ERR_INVALID_ARG;
+  if (batch * 15 > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
+  const int max_ctx = cache->max_pages_per_seq * 16;
+  const DraftPlan dp = draft_plan(m, batch, max_ctx);
+  if (ws_bytes < dp.total) return DFLASH_ERR_WORKSPACE;
+  if (!counters_fit(dp.qkv) || !counters_fit(dp.o) || !counters_fit(dp.gu) ||
+      !counters_fit(dp.dn) || batch * m.nkv > kMaxCounters)
+    return DFLASH_ERR_UNSUPPORTED;
+
+  const Packed P = packed_layout(m);
+  const char* wb = reinterpret_cast<const char*>(packed);
+  char* ws = reinterpret_cast<char*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
+  float* x = reinterpret_cast<float*>(ws + dp.x);
+  void* u = ws + dp.u;
+  float* part = reinterpret_cast<float*>(ws + dp.part);
+  const int rows = batch * 16;
+  const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
+  const float* fnorm = reinterpret_cast<const float*>(wb + P.final_norm);
+
+  {
+    EmbedNormArgs e{};
+    e.anchor_ids = anchor_ids;
+    e.mask_id = m.mask;
+    e.embed = embed;
+    e.hidden = m.H;
+    e.x = x;
+    e.u = u;
+    e.gain = reinterpret_cast<const float*>(wb + P.layer0 + P.attn_norm);
+    e.eps = m.eps;
+    DF_TRY(launch_embed_norm(m.bf16, e, rows, stream));
+  }
+  for (int l = 0; l < m.L; ++l) {
+    const char* lb = wb + P.layer0 + (size_t)l * P.layer_stride;
+    {  // fused Q|K|V projection with RoPE
+      GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, u, m.H, rows,
+                                 (m.nq + 2 * m.nkv) * m.d / 16, m.d / 16, part, counters);
+      g.q_out = reinterpret_cast<float*>(ws + dp.q);
+      g.bk_out = reinterpret_cast<float*>(ws + dp.bk);
+      g.bv_out = reinterpret_cast<float*>(ws + dp.bv);
+      g.ctx_lens = cache->ctx_lens;
+      g.n_q = m.nq;
+      g.n_kv = m.nkv;
+      g.head_dim = m.d;
+      g.log_theta = std::log((double)m.theta);
+      DF_TRY(launch_gemm(m.bf16, dp.qkv.mt, EPI_QKV, g, 1, stream));
+    }
+    {  // attention over injected context + block
+      AttnArgs a{};
+      a.q = reinterpret_cast<const float*>(ws + dp.q);
+      a.bk = reinterpret_cast<const float*>(ws + dp.bk);
+      a.bv = reinterpret_cast<const float*>(ws + dp.bv);
+      a.k_pool = reinterpret_cast<const char*>(cache->k_pool) + (size_t)l * pool_layer * m.es;
+      a.v_pool = reinterpret_cast<const char*>(cache->v_pool) + (size_t)l * pool_layer * m.es;
+      a.block_table = cache->block_table;
+      a.max_pages = cache->max_pages_per_seq;
+      a.ctx_lens = cache->ctx_lens;
+      a.n_q = m.nq;
+      a.n_kv = m.nkv;
+      a.head_dim = m.d;
+      a.nc = dp.nc;
+      a.chunk = dp.chunk;
+      a.scale = 1.0f / std::sqrt((float)m.d);
+      a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
+      a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
+      a.counters = counters;
+      a.out = ws + dp.ao;
+      DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
+    }
+    {  // output projection + residual
+      GemmParams g = base_params(dp.o, lb + P.wo, 0, m.nq * m.d / m.ktile, ws + dp.ao,
+                                 m.nq * m.d, rows, m.H / 16, 1, part, counters);
+      g.out = x;
+      g.ldo = m.H;
+      DF_TRY(launch_gemm(m.bf16, dp.o.mt, EPI_RESIDUAL, g, 1, stream));
+    }
+    {
+      NormArgs n{};
+      n.x = x;
+      n.u = u;
+      n.gain = reinterpret_cast<const float*>(lb + P.mlp_norm);
+      n.hidden = m.H;
+      n.eps = m.eps;
+      DF_TRY(launch_rmsnorm(m.bf16, n, rows, stream));
+    }
+    {  // gate|up with SiLU * up
+      GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, u, m.H, rows,
+                                 2 * m.I / 16, 2, part, counters);
+      g.out = ws + dp.h;
+      g.ldo = m.I;
+      DF_TRY(launch_gemm(m.bf16, dp.gu.mt, EPI_SWIGLU, g, 1, stream));
+    }
+    {  // down projection + residual
+      GemmParams g = base_params(dp.dn, lb + P.wd, 0, m.I / m.ktile, ws + dp.h, m.I, rows,
+                                 m.H / 16, 1, part, counters);
+      g.out = x;
+      g.ldo = m.H;
+      DF_TRY(launch_gemm(m.bf16, dp.dn.mt, EPI_RESIDUAL, g, 1, stream));
+    }
+    {
+      NormArgs n{};
+      n.x = x;
+      n.hidden = m.H;
+      n.eps = m.eps;
+      if (l + 1 < m.L) {
+        n.u = u;
+        n.gain = reinterpret_cast<const float*>(wb + P.layer0 + (size_t)(l + 1) * P.layer_stride +
+                                                P.attn_norm);
+        DF_TRY(launch_rmsnorm(m.bf16, n, rows, stream));
+      } else {
+        n.u = ws + dp.y;
+        n.gain = fnorm;
+        n.drop_slot0 = 1;
+        DF_TRY(launch_rmsnorm(m.bf16, n, batch * 15, stream));
+      }
+    }
+  }
+  {  // shared LM head + argmax over the vocabulary
+    GemmParams g = base_params(dp.lm, wb + P.lm_head, 0, m.H / m.ktile, ws + dp.y, m.H,
+                               batch * 15, m.V / 16, 4, part, counters);
+    g.keys = keys;
+    g.ids_out = draft_ids;
+    g.logits_out = logits_out;
+    g.ldo = m.V;
+    g.done_counter = counters + kMaxCounters;
+    g.total_wgs = (m.V / 16 / 4) * dp.lm.n_mblocks;
+    DF_TRY(launch_gemm(m.bf16, dp.lm.mt, EPI_ARGMAX, g, 1, stream));
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
+                                   int32_t batch, int32_t* accept_len, int32_t* bonus,
+                                   int32_t* emitted, hipStream_t stream) {
+  if (!draft_ids || !target_ids || !accept_len || !bonus || batch < 0)
+    return DFLASH_ERR_INVALID_ARG;
+  if (batch == 0) return DFLASH_OK;
+  DF_TRY(launch_verify_greedy(draft_ids, target_ids, batch, accept_len, bonus, emitted, stream));
+  return DFLASH_OK;
+}
+
+size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab) {
+  if (batch <= 0 || vocab <= 0) return 0;
+  return align_up((size_t)batch * 31 * 2 * sizeof(float));
+}
+
+dflash_status dflash_verify_accept_sampled(const float* draft_logits,
+                                           const float* target_logits, const float* u_draft,
+                                           const float* u_accept, const float* u_resample,
+                                           int32_t batch, int32_t vocab, int32_t* draft_ids,
+                                           int32_t* accept_len, int32_t* emitted,
+                                           void* workspace, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (!draft_logits || !target_logits || !u_draft || !u_accept || !u_resample || !draft_ids ||
+      !accept_len || !emitted || !workspace || batch <= 0 || vocab <= 0)
+    return DFLASH_ERR_INVALID_ARG;
+  if (ws_bytes < dflash_verify_sampled_workspace_size(batch, vocab)) return DFLASH_ERR_WORKSPACE;
+  SampledArgs a{};
+  a.draft_logits = draft_logits;
+  a.target_logits = target_logits;
+  a.u_draft = u_draft;
+  a.u_accept = u_accept;
+  a.u_resample = u_resample;
+  a.vocab = vocab;
+  a.stats = reinterpret_cast<float*>(workspace);
+  a.draft_ids = draft_ids;
+  a.accept_len = accept_len;
+  a.emitted = emitted;
+  DF_TRY(launch_verify_sampled(a, batch, stream));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Launch interface of the block attention kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dflash {
+
+struct AttnArgs {
+  const float* q;          // [B*16][n_q][d], RoPE applied
+  const float* bk;         // [B*16][n_kv][d], block keys (RoPE applied)
+  const float* bv;         // [B*16][n_kv][d]
+  const void* k_pool;      // this layer's pool [num_pages][n_kv][16][d]
+  const void* v_pool;
+  const int* block_table;  // [B][max_pages]
+  int max_pages;
+  const int* ctx_lens;     // [B]
+  int n_q, n_kv, head_dim;
+  int nc;                  // context chunks per request
+  int chunk;               // context keys per chunk
+  float scale;             // 1 / sqrt(d)
+  float* part_o;           // [B][n_kv][nc+1][R][d]
+  float* part_ml;          // [B][n_kv][nc+1][R][2]
+  unsigned* counters;      // [B][n_kv], zero on entry and exit
+  void* out;               // [B*16][n_q*d] operand type
+};
+
+hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
+                                  hipStream_t stream);
+bool block_attention_supported(int head_dim, int group);
+
+}  // namespace dflash

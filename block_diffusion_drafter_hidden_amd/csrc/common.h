@@ -1,0 +1,100 @@
+// Device-side helpers shared by the DFlash kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;      // block slots: anchor + 15 masks
+constexpr int kDrafts = 15;
+constexpr int kPage = 16;
+
+// ---------------------------------------------------------------------------------------
+// Element types.  A "k-tile" is the K extent one lane loads as 16 bytes per MFMA row/col:
+// 8 bf16 or 4 fp32 per lane, 4 lane groups -> 32 (bf16) or 16 (fp32) K values per tile.
+// ---------------------------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<bf16> {
+  static constexpr int kPerLane = 8;
+  static constexpr int kTile = 32;
+  __device__ static inline float to_f(bf16 v) { return (float)v; }
+  __device__ static inline bf16 from_f(float v) { return (bf16)v; }
+};
+template <> struct Elem<float> {
+  static constexpr int kPerLane = 4;
+  static constexpr int kTile = 16;
+  __device__ static inline float to_f(float v) { return v; }
+  __device__ static inline float from_f(float v) { return v; }
+};
+
+// 16x16 output tile += A(16 x kTile) * B(kTile x 16) for one k-tile.  `a` and `b` are the
+// 16-byte lane fragments: lane l holds row (A) / column (B) l % 16 and k-slice l / 16.
+// Output layout: lane l holds rows 4*(l/16)+j, column l%16, j = 0..3.
+template <typename T> __device__ inline f32x4 mfma_tile(i32x4 a, i32x4 b, f32x4 c);
+
+template <> __device__ inline f32x4 mfma_tile<bf16>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x4 mfma_tile<float>(i32x4 a, i32x4 b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
+                                           __builtin_bit_cast(float, b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y),
+                                           __builtin_bit_cast(float, b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z),
+                                           __builtin_bit_cast(float, b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w),
+                                           __builtin_bit_cast(float, b.w), c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave reductions (wave64) through ds_swizzle-free shuffles.
+// ---------------------------------------------------------------------------------------
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Orderable key for (value, index) argmax: larger value wins, then lower index.
+__device__ inline unsigned long long argmax_key(float v, int idx) {
+  unsigned u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)idx);
+}
+__device__ inline int argmax_key_index(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
+}
+
+// Device-scope release/acquire helpers for the "last workgroup finishes" pattern.
+__device__ inline unsigned arrive_counter(unsigned* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// RoPE angle for pair index i of a head of width d at position pos, computed in fp64.
+__device__ inline void rope_cos_sin(int pos, int i, int d, double log_theta, float* c,
+                                    float* s) {
+  double inv = exp(-(2.0 * (double)i / (double)d) * log_theta);
+  double a = (double)pos * inv;
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace dflash

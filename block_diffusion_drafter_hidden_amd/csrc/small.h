@@ -1,0 +1,48 @@
+// Launch interfaces of the small DFlash kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dflash {
+
+struct PackArgs {
+  const void* src[3];   // source segments, row-major [rows][K]
+  int seg_tiles[3];     // 16-row tiles per segment
+  int n_segs;
+  int interleave2;      // 1: destination tile 2j+s = tile j of segment s
+  int n_tiles_total;    // destination n-tiles
+  int KT;               // k-tiles (K / kTile)
+  long long K;          // source row length in elements
+  void* dst;
+};
+
+struct EmbedNormArgs {
+  const int* anchor_ids;
+  int mask_id;
+  const void* embed;
+  int hidden;
+  float* x;             // [rows][hidden] fp32 residual
+  void* u;              // [rows][hidden] operand type
+  const float* gain;
+  float eps;
+};
+
+struct NormArgs {
+  const float* x;
+  void* u;
+  const float* gain;
+  int hidden;
+  float eps;
+  int drop_slot0;
+};
+
+hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream);
+hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream);
+hipError_t launch_embed_norm(int bf16_dtype, const EmbedNormArgs& a, int rows,
+                             hipStream_t stream);
+hipError_t launch_rmsnorm(int bf16_dtype, const NormArgs& a, int rows, hipStream_t stream);
+hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
+                                int* bonus, int* emitted, hipStream_t stream);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace dflash

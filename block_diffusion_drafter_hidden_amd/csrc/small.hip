@@ -1,0 +1,198 @@
+// Small kernels of the DFlash step: weight packing, block embedding, RMSNorm,
+// greedy verification and workspace clearing.
+#include "common.h"
+#include "small.h"
+
+namespace dflash {
+
+// ------------------------------------------------------------------------------------------
+// Weight packing into the MFMA tile layout (see gemm.h).  One thread writes one 16-byte lane
+// chunk.  Destination n-tile `dt` takes its 16 rows from source segment `s` as follows:
+//   CONCAT:       segments are stacked along N (Q | K | V).
+//   INTERLEAVE2:  dt = 2*j + s takes n-tile j of segment s (gate, up interleaved by tile).
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void pack_kernel(PackArgs a) {
+  const long long chunk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.n_tiles_total * a.KT * kWave;
+  if (chunk >= total) return;
+  const int lane = (int)(chunk % kWave);
+  const long long tile = chunk / kWave;
+  const int kt = (int)(tile % a.KT);
+  const int dt = (int)(tile / a.KT);
+  int seg, st;
+  if (a.interleave2) {
+    seg = dt & 1;
+    st = dt >> 1;
+  } else {
+    seg = 0;
+    st = dt;
+    while (seg + 1 < a.n_segs && st >= a.seg_tiles[seg]) {
+      st -= a.seg_tiles[seg];
+      ++seg;
+    }
+  }
+  const int row = st * 16 + (lane & 15);
+  const long long col = (long long)kt * Elem<T>::kTile + (lane >> 4) * Elem<T>::kPerLane;
+  const T* src = reinterpret_cast<const T*>(a.src[seg]) + (long long)row * a.K + col;
+  i32x4 v = *reinterpret_cast<const i32x4*>(src);
+  reinterpret_cast<i32x4*>(a.dst)[chunk] = v;
+}
+
+hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream) {
+  const long long total = (long long)a.n_tiles_total * a.KT * kWave;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  if (bf16_dtype)
+    pack_kernel<bf16><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
+  else
+    pack_kernel<float><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Norm gains widened to fp32.
+template <typename T>
+__global__ void widen_kernel(const T* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = Elem<T>::to_f(src[i]);
+}
+
+hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream) {
+  const int threads = 256;
+  const int blocks = (n + threads - 1) / threads;
+  if (bf16_dtype)
+    widen_kernel<bf16><<<blocks, threads, 0, stream>>>(reinterpret_cast<const bf16*>(src), dst, n);
+  else
+    widen_kernel<float><<<blocks, threads, 0, stream>>>(reinterpret_cast<const float*>(src), dst,
+                                                        n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Block embedding + first RMSNorm.  Row m = b*16 + j: token = anchor[b] for j == 0, else the
+// mask id.  x (fp32 residual) = E[token]; u = RMSNorm(x) * gain in the operand type.
+// One workgroup per row.
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__device__ inline float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  const int nw = blockDim.x / kWave;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(EmbedNormArgs a) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int b = m / kBlock, j = m % kBlock;
+  const int tok = j == 0 ? a.anchor_ids[b] : a.mask_id;
+  const T* e = reinterpret_cast<const T*>(a.embed) + (long long)tok * a.hidden;
+  float* x = a.x + (long long)m * a.hidden;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) {
+    const float v = Elem<T>::to_f(e[i]);
+    x[i] = v;
+    ss += v * v;
+  }
+  ss = block_sum<T>(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+  T* u = reinterpret_cast<T*>(a.u) + (long long)m * a.hidden;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x)
+    u[i] = Elem<T>::from_f(x[i] * rstd * a.gain[i]);
+}
+
+// RMSNorm of fp32 rows into the operand type.  With `drop_slot0`, source row b*16 + j
+// (j >= 1) lands in destination row b*15 + j - 1 (the LM-head rows).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
+  __shared__ float red[4];
+  int src_row = blockIdx.x;
+  int dst_row = blockIdx.x;
+  if (a.drop_slot0) {
+    const int b = blockIdx.x / kDrafts, j = blockIdx.x % kDrafts + 1;
+    src_row = b * kBlock + j;
+  }
+  const float* x = a.x + (long long)src_row * a.hidden;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) ss += x[i] * x[i];
+  ss = block_sum<T>(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+  T* u = reinterpret_cast<T*>(a.u) + (long long)dst_row * a.hidden;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x)
+    u[i] = Elem<T>::from_f(x[i] * rstd * a.gain[i]);
+}
+
+hipError_t launch_embed_norm(int bf16_dtype, const EmbedNormArgs& a, int rows,
+                             hipStream_t stream) {
+  if (bf16_dtype)
+    embed_norm_kernel<bf16><<<rows, 256, 0, stream>>>(a);
+  else
+    embed_norm_kernel<float><<<rows, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int bf16_dtype, const NormArgs& a, int rows, hipStream_t stream) {
+  if (bf16_dtype)
+    rmsnorm_kernel<bf16><<<rows, 256, 0, stream>>>(a);
+  else
+    rmsnorm_kernel<float><<<rows, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Greedy verification, one wave per request.  Lane i < 15 compares d_{i+1} with t_i; the
+// ballot of mismatches gives m = index of the lowest mismatching lane (15 if none), with
+// no data-dependent branch.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void verify_greedy_kernel(const int* __restrict__ draft,
+                                                           const int* __restrict__ target,
+                                                           int batch, int* __restrict__ accept,
+                                                           int* __restrict__ bonus,
+                                                           int* __restrict__ emitted) {
+  const int b = blockIdx.x;
+  const int l = threadIdx.x;
+  const int d = l < kDrafts ? draft[(long long)b * kDrafts + l] : 0;
+  const int t = l < kBlock ? target[(long long)b * kBlock + l] : 0;
+  const unsigned long long miss = __ballot(l < kDrafts && d != t) | (1ull << kDrafts);
+  const int m = __ffsll((long long)miss) - 1;  // lowest set bit
+  if (l == 0) {
+    accept[b] = m + 1;
+    bonus[b] = target[(long long)b * kBlock + m];
+  }
+  if (emitted && l < kBlock) {
+    const int tm = __shfl(t, m, kWave);
+    emitted[(long long)b * kBlock + l] = l < m ? d : (l == m ? tm : -1);
+  }
+}
+
+hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
+                                int* bonus, int* emitted, hipStream_t stream) {
+  verify_greedy_kernel<<<batch, 64, 0, stream>>>(draft, target, batch, accept, bonus, emitted);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Zero fill (used for the workspace synchronization area; a kernel, not a memset node, so
+// it is safe inside captured graphs).
+// ------------------------------------------------------------------------------------------
+__global__ void fill_zero_kernel(i32x4* p, long long n16) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = i32x4{0, 0, 0, 0};
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const long long n16 = (long long)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int threads = 256;
+  fill_zero_kernel<<<(unsigned)((n16 + threads - 1) / threads), threads, 0, stream>>>(
+      reinterpret_cast<i32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

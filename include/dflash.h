@@ -1,0 +1,207 @@
+/*
+ * dflash.h - C ABI of the DFlash draft-step library for AMD Instinct MI355X (gfx950).
+ *
+ * One speculative step of DFlash (block-diffusion drafting with target-feature KV
+ * injection) as three calls, plus set-up helpers:
+ *
+ *   dflash_fuse_inject_kv   fuse multi-layer target hidden states with one linear
+ *                           projection and write them as K/V into every draft layer's
+ *                           paged KV cache ("DFlash" wiki page, section "Conditioning on
+ *                           target-model features", items 1 and 2; NVIDIA technical blog
+ *                           on DFlash, section "How does DFlash speculative decoding
+ *                           work?": context features go into the key-value projections of
+ *                           the draft layers).
+ *   dflash_draft_block      one non-causal forward pass over the block [anchor, mask x 15]
+ *                           that drafts 15 tokens with the shared LM head and argmax (wiki,
+ *                           "Parallel drafting with block diffusion"; blog, same section:
+ *                           one forward pass predicts a block of masked future tokens).
+ *   dflash_verify_accept    greedy verification: the longest prefix of drafts that matches
+ *                           the target's argmax, plus one target token (blog, same section:
+ *                           the target accepts the longest valid prefix).
+ *   dflash_verify_accept_sampled
+ *                           temperature-1 verification (speculative accept/reject with
+ *                           residual resampling, which keeps the target's output
+ *                           distribution; blog, same section; wiki, "Performance
+ *                           comparison", sampling at temperature 1).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *     every buffer (weights, packed weights, KV pools, tables, inputs, outputs, workspace).
+ *   - Calls are asynchronous on `stream` and never synchronize the device.  The library
+ *     allocates no device memory and keeps no global state.
+ *   - Arguments are validated on the host before anything is launched; on a negative
+ *     status nothing was enqueued.  Device-side data (token ids in [0, vocab), page ids in
+ *     [0, num_pages), positions below max_pages_per_seq * page_size) is a precondition
+ *     that is not checked.
+ *   - Two calls that share a workspace must be ordered on one stream.
+ *   - Matrices are row-major.  Linear weights use the logical [out, in] layout.
+ *
+ * Numerics: bf16 models store weights, features, KV cache and GEMM operands in bf16 and
+ * accumulate in fp32; the residual stream, norms, softmax and RoPE angles (computed in
+ * fp64, rounded to fp32) stay in fp32.  f32 models use fp32 everywhere.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, inconsistent shape   */
+  DFLASH_ERR_UNSUPPORTED = -2,  /* a shape or dtype the kernels do not implement         */
+  DFLASH_ERR_WORKSPACE = -3,    /* workspace or packed buffer smaller than required      */
+  DFLASH_ERR_HIP = -4           /* a HIP launch reported an error                        */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  Requirements checked by every call: block_size == 16,
+ * page_size == 16, hidden % 64 == 0, feat_dim % 64 == 0, intermediate % 64 == 0,
+ * vocab % 16 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
+ * n_q_heads / n_kv_heads * 16 <= 128. */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;         /* H */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;       /* d */
+  int32_t intermediate;   /* I, SwiGLU width */
+  int32_t vocab;          /* V */
+  int32_t feat_dim;       /* F = (number of fused target layers) * (target hidden size) */
+  int32_t block_size;     /* 16: slot 0 = last accepted token, slots 1..15 = mask */
+  int32_t page_size;      /* 16 tokens per KV page */
+  int32_t mask_token_id;
+  float rope_theta;
+  float rms_eps;
+  int32_t dtype;          /* dflash_dtype of weights, features and KV cache */
+} dflash_config;
+
+/* Logical weights for dflash_pack_weights.  Every pointer is a device pointer to a
+ * row-major tensor of the model dtype.  Per-layer members point to HOST arrays of
+ * n_layers device pointers.
+ *   w_fuse [H, F]   lm_head [V, H]   final_norm [H]
+ *   attn_norm[l] [H]   wq[l] [n_q*d, H]   wk[l], wv[l] [n_kv*d, H]   wo[l] [H, n_q*d]
+ *   mlp_norm[l] [H]    w_gate[l], w_up[l] [I, H]   w_down[l] [H, I]                    */
+typedef struct {
+  const void* w_fuse;
+  const void* lm_head;
+  const void* final_norm;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* mlp_norm;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+} dflash_weights;
+
+/* Paged KV cache of the draft layers (injected context only; block K/V are never
+ * stored).  Pools are [n_layers][num_pages][n_kv_heads][page_size][head_dim] in the model
+ * dtype; one physical page id addresses the same page in every layer.
+ * block_table [batch][max_pages_per_seq] maps logical page p of request b to a physical
+ * page; ctx_lens [batch] is T_b, the number of context positions already injected. */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int32_t num_pages;
+  int32_t max_pages_per_seq;
+} dflash_kv_cache;
+
+/* Size in bytes of the packed weight buffer for `cfg` (0 if cfg is invalid). */
+size_t dflash_packed_weights_size(const dflash_config* cfg);
+
+/* Repack the logical weights into the MFMA tile layout the kernels stream (norm gains
+ * widened to fp32; Q|K|V concatenated; gate and up interleaved by 16-row tile).
+ * `packed` (device, >= dflash_packed_weights_size bytes) is owned by the caller and is
+ * the `packed` argument of the step calls.  Run once at load time. */
+dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights* w,
+                                  void* packed, size_t packed_bytes, hipStream_t stream);
+
+/* Bytes of workspace the step calls need for up to `max_batch` requests and up to
+ * `max_inject_rows` rows per dflash_fuse_inject_kv launch chunk (larger n_tok are
+ * processed in chunks of this many rows).  `max_ctx` bounds T_b + 16 (attention
+ * split sizing).  Returns 0 if the arguments are invalid. */
+size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
+                             int32_t max_inject_rows, int32_t max_ctx);
+
+/* Zero the synchronization area at the head of a new workspace.  Must be called once
+ * after the workspace is allocated; the step calls leave that area zeroed again. */
+dflash_status dflash_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Feature fusion + KV injection.
+ *   feats   [n_tok, F] model dtype: concatenated target hidden states, one row per
+ *           context position to inject (layer-major concatenation).
+ *   seq_idx [n_tok] int32: request of each row (index into block_table).
+ *   pos     [n_tok] int32: context position of each row; the row lands in page
+ *           block_table[seq][pos / 16], slot pos % 16, of every layer, K rotated at pos.
+ * ctx_lens is not read or changed: the caller advances it.  Rows whose positions repeat
+ * are written in an unspecified order. */
+dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed,
+                                    const dflash_kv_cache* cache, const void* feats,
+                                    const int32_t* seq_idx, const int32_t* pos, int32_t n_tok,
+                                    void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Draft one block per request.
+ *   embed      [V, H] model dtype: the target's embedding table (shared, not packed).
+ *   anchor_ids [batch] int32: last accepted token of each request (block slot 0).
+ *   draft_ids  [batch, 15] int32 out: argmax over the vocabulary of slots 1..15, exact
+ *              fp32 ties resolved to the lowest id.
+ *   logits_out [batch, 15, V] fp32 out, may be NULL: the LM-head logits of slots 1..15.
+ * Slot j of request b sits at position ctx_lens[b] + j and attends, without a mask, to
+ * the ctx_lens[b] cached context entries and the 16 block slots. */
+dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
+                                 const void* embed, const dflash_kv_cache* cache,
+                                 const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
+                                 float* logits_out, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Greedy verification.
+ *   draft_ids  [batch, 15] int32: d_1..d_15.
+ *   target_ids [batch, 16] int32: t_0..t_15, the target's argmax after block slot j.
+ *   accept_len [batch] int32 out: m + 1, m = number of leading i with d_i == t_{i-1}.
+ *   bonus      [batch] int32 out: t_m.
+ *   emitted    [batch, 16] int32 out, may be NULL: d_1..d_m, t_m, then -1 padding. */
+dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
+                                   int32_t batch, int32_t* accept_len, int32_t* bonus,
+                                   int32_t* emitted, hipStream_t stream);
+
+/* Workspace bytes for dflash_verify_accept_sampled. */
+size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
+
+/* Temperature-1 verification.
+ *   draft_logits  [batch, 15, vocab] fp32, target_logits [batch, 16, vocab] fp32.
+ *   u_draft, u_accept [batch, 15], u_resample [batch]: uniforms in [0, 1).
+ * q_i = softmax(draft_logits[i-1]), p_i = softmax(target_logits[i-1]).
+ * d_i = smallest j with cumsum(q_i)[j] > u_draft * sum(q_i); accept d_i while
+ * u_accept * q_i(d_i) < p_i(d_i); at the first rejection emit the inverse-CDF sample of
+ * max(0, p_i - q_i) (of p_i if that is all zero) at u_resample and stop; if all 15 are
+ * accepted emit the sample of p_16 at u_resample.
+ *   draft_ids [batch, 15], accept_len [batch] (number of emitted tokens, 1..16),
+ *   emitted [batch, 16] (-1 padded) int32 out. */
+dflash_status dflash_verify_accept_sampled(const float* draft_logits,
+                                           const float* target_logits, const float* u_draft,
+                                           const float* u_accept, const float* u_resample,
+                                           int32_t batch, int32_t vocab, int32_t* draft_ids,
+                                           int32_t* accept_len, int32_t* emitted,
+                                           void* workspace, size_t ws_bytes,
+                                           hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dflash_error_string(dflash_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

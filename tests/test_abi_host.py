@@ -1,0 +1,88 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the header
+declares, sizes its buffers, and rejects bad arguments before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_hidden_amd import binding as B
+from workloads import WORKLOADS, TINY, QWEN3_8B, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load_library()
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    for code, text in B.STATUS.items():
+        assert B.error_string(code) == text
+    assert B.error_string(7) == "unknown status"
+
+
+@pytest.mark.parametrize("key", list(WORKLOADS))
+def test_packed_size_covers_all_weights(key):
+    cfg = WORKLOADS[key].cfg
+    n = B.packed_weights_size(B.make_config(cfg))
+    es = 2 if cfg.dtype == "bf16" else 4
+    assert n >= cfg.n_params(include_embed=False) * es
+    assert n <= cfg.n_params(include_embed=False) * es + 4 * 1024 * 1024
+
+
+def test_workspace_size_grows_with_batch_and_context():
+    c = B.make_config(QWEN3_8B)
+    a = B.workspace_size(c, 1, 16, 2048)
+    b = B.workspace_size(c, 32, 512, 8192)
+    assert 0 < a < b
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block_size", 8, -2), ("page_size", 32, -2), ("head_dim", 96, -2), ("hidden", 100, -2),
+    ("n_kv_heads", 3, -1), ("dtype", 5, -2), ("mask_token_id", -1, -1), ("vocab", 4000, -2)])
+def test_invalid_config_rejected(field, value, status):
+    c = B.make_config(TINY)
+    setattr(c, field, value)
+    assert B.packed_weights_size(c) == 0
+    assert B.workspace_size(c, 1, 16, 128) == 0
+    lib = B.load_library()
+    # Rejected on the host before any pointer is touched.
+    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None, 0,
+                                  None) == status
+
+
+def test_null_arguments_rejected_before_launch():
+    lib = B.load_library()
+    c = B.make_config(TINY)
+    assert lib.dflash_verify_accept(None, None, 4, None, None, None, None) == -1
+    assert lib.dflash_workspace_init(None, 0, None) == -1
+    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None, 0,
+                                  None) == -1
+    assert lib.dflash_fuse_inject_kv(C.byref(c), None, None, None, None, None, 4, None, 0,
+                                     None) == -1
+    assert lib.dflash_verify_accept_sampled(None, None, None, None, None, 1, 8, None, None,
+                                            None, None, 0, None) == -1
+    assert lib.dflash_verify_sampled_workspace_size(0, 8) == 0
+
+
+def test_small_workspace_rejected_before_launch():
+    lib = B.load_library()
+    c = B.make_config(TINY)
+    cache = B.KVCache(1, 1, 1, 1, 16, 8)
+    fake = C.c_void_p(16)  # never dereferenced: the size check fails first
+    st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(cache), fake, 1, fake, None,
+                                fake, 1024, None)
+    assert st == -3
+    st = lib.dflash_workspace_init(fake, 16, None)
+    assert st == -3
