@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of one DFlash speculative step on one GPU.
+
+A step is the whole hot path over one batch: feature fusion + KV injection of the 16 most
+recently accepted context positions of every request (rewriting positions T-16..T-1 with
+the same features, so every step sees the same cache), one block-diffusion draft pass
+(16-slot block, 15 drafted tokens per request) and greedy verification.  The step is
+captured once in a HIP graph and replayed.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen3_b1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=30)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_hidden_amd import Drafter, binding as B
+    from workloads import WORKLOADS, synth
+
+    wl = WORKLOADS[args.workload]
+    cfg = wl.cfg
+    Bn = wl.batch
+    ctx = synth.context_lengths(wl)
+    n_new = cfg.block_size
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] workload {wl.name}: generating weights")
+    w = synth.drafter_weights(cfg, seed=wl.seed)
+    wd = {k: v.to(dev) for k, v in w.items()}
+    table, num_pages = synth.page_table(wl.name, ctx, cfg.page_size, wl.seed)
+    dr = Drafter(cfg, wd, max_batch=Bn, max_ctx=table.shape[1] * cfg.page_size,
+                 max_inject_rows=256, device=dev)
+    embed = wd["embed"]
+    del wd
+    torch.cuda.empty_cache()
+    cache = dr.new_cache(table, ctx, num_pages)
+
+    log("[bench] prefill: injecting the context")
+    feats = [synth.target_features(cfg, int(T), f"bench/ctx/b{b}", seed=wl.seed)
+             for b, T in enumerate(ctx)]
+    for b, T in enumerate(ctx):
+        f = feats[b].to(dev)
+        dr.inject(cache, f, torch.full((int(T),), b, dtype=torch.int32, device=dev),
+                  torch.arange(int(T), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+
+    # Step inputs: the last n_new positions of every request, re-injected.
+    new_feats = torch.cat([feats[b][int(T) - n_new:] for b, T in enumerate(ctx)]).to(dev)
+    new_seq = torch.as_tensor(np.repeat(np.arange(Bn), n_new).astype(np.int32)).to(dev)
+    new_pos = torch.as_tensor(np.concatenate([np.arange(int(T) - n_new, int(T)) for T in ctx])
+                              .astype(np.int32)).to(dev)
+    anchors_h = synth.anchor_ids(cfg, Bn, wl.seed)
+    anchors = torch.as_tensor(anchors_h).to(dev)
+    draft_ids = torch.zeros((Bn, 15), dtype=torch.int32, device=dev)
+    accept = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    bonus = torch.zeros(Bn, dtype=torch.int32, device=dev)
+
+    # ---------------- CPU oracle leg (rank 0, bounded sample: request 0, one step) -------
+    cpu = None
+    orc = None
+    if not args.no_cpu_baseline:
+        import oracle.dflash_oracle as ref
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count()
+        T0 = int(ctx[0])
+        log("[bench] oracle: prefill of request 0 (untimed)")
+        ks, vs = ref.prefill_context(cfg, w, feats[0][:T0 - n_new])
+        tgt_dummy = np.zeros(16, dtype=np.int32)
+        log("[bench] oracle: timed step (inject 16 + draft + verify)")
+        t0 = time.perf_counter()
+        orc = ref.draft_step(cfg, w, ks, vs, feats[0][T0 - n_new:], int(anchors_h[0]), tgt_dummy)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(15.0 / dt, 3), "unit": "drafted tokens/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"request 0 of the batch, one step: inject {n_new} positions, draft "
+                         f"one block over context {T0}, greedy verify; float64 numpy; "
+                         f"prefill untimed; {dt:.2f} s"}
+        del ks, vs
+
+    if orc is not None:
+        tgt_rows = [synth.planted_targets(orc["ids"][None], cfg.vocab, f"bench/plant/{b}",
+                                          wl.seed)[0][0] for b in range(Bn)]
+    else:
+        fake = synth.uniform_ints("bench/ref-drafts", (Bn, 15), 0, cfg.vocab - 1, wl.seed)
+        tgt_rows = list(synth.planted_targets(fake, cfg.vocab, "bench/plant", wl.seed)[0])
+    target = torch.as_tensor(np.stack(tgt_rows).astype(np.int32)).to(dev)
+    del w
+
+    def step():
+        dr.inject(cache, new_feats, new_seq, new_pos)
+        dr.draft(cache, anchors, draft_ids)
+        B.verify_accept(draft_ids, target, accept, bonus)
+
+    # ---------------- GPU timed region ----------------
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(args.steps):
+            run()
+        e1.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # ---------------- dominant kernel: LM head + argmax, timed alone ----------------
+    rows = Bn * 15
+    y = torch.randn((rows, cfg.hidden), device=dev, dtype=torch.float32)
+    ids_tmp = torch.empty(rows, dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
+        for a, b in evs:
+            a.record(s)
+            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
+            b.record(s)
+    torch.cuda.synchronize()
+    lm_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    es = 2 if cfg.dtype == "bf16" else 4
+    lm_bytes = cfg.vocab * cfg.hidden * es + rows * cfg.hidden * 4 + rows * 4
+    lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+
+    # ---------------- parity of the timed step's drafts (request 0) ----------------
+    parity = None
+    if orc is not None:
+        import oracle.dflash_oracle as ref
+        got = draft_ids.cpu().numpy()[0]
+        tie = ref.near_tie(orc["gap"], orc["top1"], orc["top2"], cfg.dtype)
+        parity = {"request": 0, "mismatches": int(((got != orc["ids"]) & ~tie).sum()),
+                  "near_ties_excused": int(tie.sum()),
+                  "accept_len_gpu": int(accept.cpu()[0]),
+                  "accept_len_oracle": int(ref.verify_greedy(orc["ids"], tgt_rows[0])[0])}
+
+    # Algorithmic bytes of one step (weights once, KV once, features, small activations).
+    H, F, V, I = cfg.hidden, cfg.feat_dim, cfg.vocab, cfg.intermediate
+    L, qd, kvd = cfg.n_layers, cfg.q_dim, cfg.kv_dim
+    w_layer = (qd + 2 * kvd) * H + H * qd + 2 * I * H + H * I
+    step_bytes = es * (H * F + L * 2 * kvd * H + L * w_layer + V * H)
+    step_bytes += es * Bn * n_new * F                                   # features read
+    step_bytes += es * int(sum(int(T) for T in ctx)) * L * 2 * kvd       # context K/V read
+    drafted = Bn * 15
+    value = drafted / (ms * 1e-3)
+    out = {
+        "metric": "drafted tokens/s (DFlash b16 draft step: inject + draft + verify)",
+        "value": round(value, 1),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) target features, random ids)",
+        "config": {"workload": wl.name, "batch": Bn, "context": int(ctx.max()),
+                   "context_min": int(ctx.min()), "block": cfg.block_size,
+                   "layers": cfg.n_layers, "hidden": H, "vocab": V, "graph": graph is not None},
+        "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "roofline": {"kernel": "gemm_stream<bf16,1,EPI_ARGMAX> (shared LM head + argmax)",
+                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_us": round(lm_us, 2),
+                     "bytes_per_launch": int(lm_bytes)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
 EXPORTS = (
     "dflash_packed_weights_size", "dflash_pack_weights", "dflash_workspace_size",
     "dflash_workspace_init", "dflash_fuse_inject_kv", "dflash_draft_block",
+    "dflash_lm_head_argmax",
     "dflash_verify_accept", "dflash_verify_sampled_workspace_size",
     "dflash_verify_accept_sampled", "dflash_error_string",
 )
@@ -78,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dflash_workspace_init": (S, [P, SZ, P]),
         "dflash_fuse_inject_kv": (S, [P, P, P, P, P, P, I32, P, SZ, P]),
         "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, SZ, P]),
+        "dflash_lm_head_argmax": (S, [P, P, P, I32, P, P, P, SZ, P]),
         "dflash_verify_accept": (S, [P, P, I32, P, P, P, P]),
         "dflash_verify_sampled_workspace_size": (SZ, [I32, I32]),
         "dflash_verify_accept_sampled": (S, [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
@@ -168,6 +170,13 @@ def draft_block(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_i
         C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
         _ptr(draft_ids), _ptr(logits_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "dflash_draft_block")
+
+
+def lm_head_argmax(ccfg: Config, packed, y, ids_out, ws, logits_out=None, stream=None) -> None:
+    rows = int(y.shape[0])
+    _check(load_library().dflash_lm_head_argmax(
+        C.byref(ccfg), _ptr(packed), _ptr(y), rows, _ptr(ids_out), _ptr(logits_out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "dflash_lm_head_argmax")
 
 
 def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream=None) -> None:

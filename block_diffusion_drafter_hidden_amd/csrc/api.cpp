@@ -200,13 +200,13 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
-  p.u = c.take((size_t)rows * m.H * m.es);
+  p.u = c.take((size_t)rows * m.H * 4);
   p.q = c.take((size_t)rows * m.nq * m.d * 4);
   p.bk = c.take((size_t)rows * m.nkv * m.d * 4);
   p.bv = c.take((size_t)rows * m.nkv * m.d * 4);
-  p.ao = c.take((size_t)rows * m.nq * m.d * m.es);
-  p.h = c.take((size_t)rows * m.I * m.es);
-  p.y = c.take((size_t)B * 15 * m.H * m.es);
+  p.ao = c.take((size_t)rows * m.nq * m.d * 4);
+  p.h = c.take((size_t)rows * m.I * 4);
+  p.y = c.take((size_t)B * 15 * m.H * 4);
   const size_t part = std::max({p.qkv.partial_bytes, p.o.partial_bytes, p.gu.partial_bytes,
                                 p.dn.partial_bytes, (size_t)16});
   p.part = c.take(part);
@@ -227,7 +227,7 @@ InjectPlan inject_plan(const Dims& m, int rows) {
   p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 1, true);
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, m.d / 16, 1, m.L, true);
   Carver c(kSyncBytes);
-  p.c = c.take((size_t)rows * m.H * m.es);
+  p.c = c.take((size_t)rows * m.H * 4);
   p.part = c.take(std::max({p.fuse.partial_bytes, p.kv.partial_bytes, (size_t)16}));
   p.total = c.off;
   return p;
@@ -242,6 +242,25 @@ constexpr int kInjectChunkRows = 256;
     hipError_t _e = (expr);                           \
     if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
   } while (0)
+
+// Shared LM head + argmax over the vocabulary for `rows` normed rows y.
+dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* y,
+                             int rows, int* ids_out, float* logits_out, char* ws,
+                             hipStream_t stream) {
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
+  const Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 4, 1, false);
+  GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, y, m.H, rows, m.V / 16, 4,
+                             nullptr, counters);
+  g.keys = keys;
+  g.ids_out = ids_out;
+  g.logits_out = logits_out;
+  g.ldo = m.V;
+  g.done_counter = counters + kMaxCounters;
+  g.total_wgs = (m.V / 16 / 4) * pl.n_mblocks;
+  DF_TRY(launch_gemm(m.bf16, 0, pl.mt, EPI_ARGMAX, g, 1, stream));
+  return DFLASH_OK;
+}
 
 }  // namespace
 
@@ -393,7 +412,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
                                  m.F, rows, m.H / 16, 1, part, counters);
       g.out = cbuf;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, cp.fuse.mt, EPI_STORE, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, m.bf16, cp.fuse.mt, EPI_STORE, g, 1, stream));
     }
     {
       GemmParams g = base_params(cp.kv, wb + P.layer0 + P.wqkv, m.nq * m.d / 16, m.H / m.ktile,
@@ -411,7 +430,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.max_pages = cache->max_pages_per_seq;
       g.seq_idx = seq_idx + r0;
       g.pos = pos + r0;
-      DF_TRY(launch_gemm(m.bf16, cp.kv.mt, EPI_INJECT, g, m.L, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, cp.kv.mt, EPI_INJECT, g, m.L, stream));
     }
   }
   return DFLASH_OK;
@@ -440,9 +459,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   const char* wb = reinterpret_cast<const char*>(packed);
   char* ws = reinterpret_cast<char*>(workspace);
   unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
   float* x = reinterpret_cast<float*>(ws + dp.x);
-  void* u = ws + dp.u;
+  float* u = reinterpret_cast<float*>(ws + dp.u);
   float* part = reinterpret_cast<float*>(ws + dp.part);
   const int rows = batch * 16;
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
@@ -473,7 +491,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.n_kv = m.nkv;
       g.head_dim = m.d;
       g.log_theta = std::log((double)m.theta);
-      DF_TRY(launch_gemm(m.bf16, dp.qkv.mt, EPI_QKV, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.qkv.mt, EPI_QKV, g, 1, stream));
     }
     {  // attention over injected context + block
       AttnArgs a{};
@@ -494,7 +512,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
       a.counters = counters;
-      a.out = ws + dp.ao;
+      a.out = reinterpret_cast<float*>(ws + dp.ao);
       DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
     }
     {  // output projection + residual
@@ -502,7 +520,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  m.nq * m.d, rows, m.H / 16, 1, part, counters);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, dp.o.mt, EPI_RESIDUAL, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.o.mt, EPI_RESIDUAL, g, 1, stream));
     }
     {
       NormArgs n{};
@@ -518,14 +536,14 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  2 * m.I / 16, 2, part, counters);
       g.out = ws + dp.h;
       g.ldo = m.I;
-      DF_TRY(launch_gemm(m.bf16, dp.gu.mt, EPI_SWIGLU, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.gu.mt, EPI_SWIGLU, g, 1, stream));
     }
     {  // down projection + residual
       GemmParams g = base_params(dp.dn, lb + P.wd, 0, m.I / m.ktile, ws + dp.h, m.I, rows,
                                  m.H / 16, 1, part, counters);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, dp.dn.mt, EPI_RESIDUAL, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.dn.mt, EPI_RESIDUAL, g, 1, stream));
     }
     {
       NormArgs n{};
@@ -538,25 +556,28 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                                 P.attn_norm);
         DF_TRY(launch_rmsnorm(m.bf16, n, rows, stream));
       } else {
-        n.u = ws + dp.y;
+        n.u = reinterpret_cast<float*>(ws + dp.y);
         n.gain = fnorm;
         n.drop_slot0 = 1;
         DF_TRY(launch_rmsnorm(m.bf16, n, batch * 15, stream));
       }
     }
   }
-  {  // shared LM head + argmax over the vocabulary
-    GemmParams g = base_params(dp.lm, wb + P.lm_head, 0, m.H / m.ktile, ws + dp.y, m.H,
-                               batch * 15, m.V / 16, 4, part, counters);
-    g.keys = keys;
-    g.ids_out = draft_ids;
-    g.logits_out = logits_out;
-    g.ldo = m.V;
-    g.done_counter = counters + kMaxCounters;
-    g.total_wgs = (m.V / 16 / 4) * dp.lm.n_mblocks;
-    DF_TRY(launch_gemm(m.bf16, dp.lm.mt, EPI_ARGMAX, g, 1, stream));
-  }
-  return DFLASH_OK;
+  return launch_lm_head(m, P, wb, ws + dp.y, batch * 15, draft_ids, logits_out, ws, stream);
+}
+
+dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
+                                    const void* y, int32_t rows, int32_t* ids_out,
+                                    float* logits_out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  Dims m;
+  dflash_status st = check_config(cfg, &m);
+  if (st != DFLASH_OK) return st;
+  if (!packed || !y || !ids_out || !workspace || rows <= 0) return DFLASH_ERR_INVALID_ARG;
+  if (rows > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
+  if (ws_bytes < kSyncBytes) return DFLASH_ERR_WORKSPACE;
+  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), y, rows,
+                        ids_out, logits_out, reinterpret_cast<char*>(workspace), stream);
 }
 
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
@@ -571,7 +592,7 @@ dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* targ
 
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab) {
   if (batch <= 0 || vocab <= 0) return 0;
-  return align_up((size_t)batch * 31 * 2 * sizeof(float));
+  return align_up((size_t)batch * 31 * 2 * sizeof(double));
 }
 
 dflash_status dflash_verify_accept_sampled(const float* draft_logits,
@@ -592,7 +613,7 @@ dflash_status dflash_verify_accept_sampled(const float* draft_logits,
   a.u_accept = u_accept;
   a.u_resample = u_resample;
   a.vocab = vocab;
-  a.stats = reinterpret_cast<float*>(workspace);
+  a.stats = reinterpret_cast<double*>(workspace);
   a.draft_ids = draft_ids;
   a.accept_len = accept_len;
   a.emitted = emitted;

@@ -21,7 +21,7 @@ struct AttnArgs {
   float* part_o;           // [B][n_kv][nc+1][R][d]
   float* part_ml;          // [B][n_kv][nc+1][R][2]
   unsigned* counters;      // [B][n_kv], zero on entry and exit
-  void* out;               // [B*16][n_q*d] operand type
+  float* out;              // [B*16][n_q*d] fp32
 };
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void block_attention_kernel(AttnArgs a) {
   // Merge the nc + 1 partials in chunk order.
   {
     const int i = tid % D, r0 = tid / D;
-    T* out = reinterpret_cast<T*>(a.out);
+    float* out = a.out;
 #pragma unroll
     for (int n = 0; n < NRO; ++n) {
       const int r = r0 + n * OPH;
@@ -169,8 +169,7 @@ __global__ __launch_bounds__(256) void block_attention_kernel(AttnArgs a) {
         }
       }
       const int j = r / G, hh = r % G;
-      out[(long long)(b * kBlock + j) * (nq * D) + (g * G + hh) * D + i] =
-          Elem<T>::from_f(acc / L);
+      out[(long long)(b * kBlock + j) * (nq * D) + (g * G + hh) * D + i] = acc / L;
     }
   }
   if (tid == 0)

@@ -44,16 +44,66 @@ template <> __device__ inline f32x4 mfma_tile<bf16>(i32x4 a, i32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 template <> __device__ inline f32x4 mfma_tile<float>(i32x4 a, i32x4 b, f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
-                                           __builtin_bit_cast(float, b.x), c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y),
-                                           __builtin_bit_cast(float, b.y), c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z),
-                                           __builtin_bit_cast(float, b.z), c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w),
-                                           __builtin_bit_cast(float, b.w), c, 0, 0, 0);
+  // Element-wise reinterpretation through scalars: bit-casting an ext-vector element
+  // lvalue directly makes clang read element 0 for every step.
+  const int a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+  const int b0 = b[0], b1 = b[1], b2 = b[2], b3 = b[3];
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a0), __int_as_float(b0), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a1), __int_as_float(b1), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a2), __int_as_float(b2), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a3), __int_as_float(b3), c, 0, 0, 0);
   return c;
 }
+
+// ---------------------------------------------------------------------------------------
+// Activation (A operand) fragments.  Activations live in memory as fp32 (or as the bf16
+// target features).  For bf16 weights an fp32 activation is fed to the bf16 MFMA as a sum
+// of bf16 pieces, one MFMA per piece (bf16 x bf16 products are exact in fp32).
+// ---------------------------------------------------------------------------------------
+template <typename WT, typename AT, int Terms = 2> struct AFrag;
+
+template <int Terms> struct AFrag<bf16, bf16, Terms> {   // bf16 input features: exact
+  static constexpr int kTerms = 1;
+  i32x4 part[1];
+  __device__ inline void load(const bf16* p, bool valid) {
+    part[0] = valid ? *reinterpret_cast<const i32x4*>(p) : i32x4{0, 0, 0, 0};
+  }
+};
+
+// fp32 activations split into Terms bf16 pieces: a = p0 + p1 (+ p2), each piece the bf16
+// rounding of what the previous ones left over (the leftovers are exact in fp32).  Two
+// pieces carry ~16 significant bits (relative error < 2^-16), three carry all 24.
+template <int Terms> struct AFrag<bf16, float, Terms> {
+  static constexpr int kTerms = Terms;
+  i32x4 part[Terms];
+  __device__ inline void load(const float* p, bool valid) {
+    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      v0 = *reinterpret_cast<const f32x4*>(p);
+      v1 = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+    for (int t = 0; t < Terms; ++t) {
+      bf16x8 h;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16 hb = (bf16)f[i];
+        h[i] = hb;
+        f[i] = f[i] - (float)hb;
+      }
+      part[t] = __builtin_bit_cast(i32x4, h);
+    }
+  }
+};
+
+template <int Terms> struct AFrag<float, float, Terms> {  // fp32 model
+  static constexpr int kTerms = 1;
+  i32x4 part[1];
+  __device__ inline void load(const float* p, bool valid) {
+    part[0] = valid ? *reinterpret_cast<const i32x4*>(p) : i32x4{0, 0, 0, 0};
+  }
+};
 
 // ---------------------------------------------------------------------------------------
 // Wave reductions (wave64) through ds_swizzle-free shuffles.

@@ -15,7 +15,7 @@ namespace dflash {
 constexpr int kTileBytes = 1024;
 
 enum Epi : int {
-  EPI_STORE = 0,     // out[m][n] = acc, stored in the operand type (fusion output c)
+  EPI_STORE = 0,     // out[m][n] = acc, fp32 (fusion output c)
   EPI_RESIDUAL = 1,  // x[m][n] += acc, fp32 residual stream
   EPI_SWIGLU = 2,    // group = (gate tile, up tile): h[m][16*grp + c] = silu(gate) * up
   EPI_QKV = 3,       // group = one head of the fused Q|K|V projection: RoPE + scatter
@@ -29,7 +29,7 @@ struct GemmParams {
   long long w_zstride;      // bytes between grid.z slices
   int nt0;                  // first n-tile of this launch inside the packed matrix
   int KT;                   // k-tiles per n-tile row of the packed matrix
-  const void* A;            // activations, row-major [M][lda], operand type
+  const void* A;            // activations, row-major [M][lda]: fp32, or bf16 target features
   int lda;
   int M;                    // valid rows
   int n_tiles;              // n-tiles computed per grid.z slice
@@ -42,8 +42,8 @@ struct GemmParams {
   unsigned* counters;       // one per (z, group, m-block); zero on entry and on exit
 
   // Epilogue operands
-  void* out;                // EPI_STORE: [M][ldo] operand type; EPI_RESIDUAL: fp32 x;
-                            // EPI_SWIGLU: [M][ldo] operand type h
+  void* out;                // EPI_STORE: [M][ldo] fp32 c; EPI_RESIDUAL: fp32 x;
+                            // EPI_SWIGLU: [M][ldo] fp32 h
   int ldo;
   // EPI_QKV
   float* q_out;             // [M][n_q][d]
@@ -68,7 +68,9 @@ struct GemmParams {
   int total_wgs;
 };
 
-hipError_t launch_gemm(int dtype_bf16, int mt, int epi, const GemmParams& p, int layers,
-                       hipStream_t stream);
+// dtype_bf16: weight type; a_bf16: activation type of A (bf16 only for the fusion GEMM over
+// the target features; otherwise fp32).
+hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int epi, const GemmParams& p,
+                       int layers, hipStream_t stream);
 
 }  // namespace dflash

@@ -1,5 +1,7 @@
 // Weight-streaming GEMM for the DFlash drafter: out = A . W^T with a fused epilogue.
 //
+// Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory and enter a
+// bf16 MFMA as a hi + lo pair (see AFrag), except the bf16 target features of the fusion.
 // Every drafter GEMM has few rows (16 block slots per request, or the injected context
 // rows) and a large weight matrix, so at small batch the kernel's job is to stream the
 // packed bf16 weights from HBM at full bandwidth and feed each 16-byte lane chunk straight
@@ -37,7 +39,7 @@ __device__ inline i32x4 load16(const void* p) {
 // Epilogues: run on the dense fp32 group tile sm.tile[MT*16][group*16].
 // ------------------------------------------------------------------------------------------
 template <typename T, int MT, int EPI>
-__device__ void run_epilogue(const GemmParams& p, GemmSmem<MT>& sm, int group, int mblock,
+__device__ void run_epilogue_impl(const GemmParams& p, GemmSmem<MT>& sm, int group, int mblock,
                              int z) {
   const int g = p.group;
   const int rows = MT * 16;
@@ -53,7 +55,7 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem<MT>& sm, int group, i
       if (m >= p.M) continue;
       const float v = sm.tile[r][c];
       if constexpr (EPI == EPI_STORE) {
-        reinterpret_cast<T*>(p.out)[(long long)m * p.ldo + n0 + c] = Elem<T>::from_f(v);
+        reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + n0 + c] = v;
       } else {
         float* x = reinterpret_cast<float*>(p.out) + (long long)m * p.ldo + n0 + c;
         *x = *x + v;
@@ -66,8 +68,8 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem<MT>& sm, int group, i
       if (m >= p.M) continue;
       const float gate = sm.tile[r][c];
       const float up = sm.tile[r][16 + c];
-      reinterpret_cast<T*>(p.out)[(long long)m * p.ldo + group * 16 + c] =
-          Elem<T>::from_f(silu(gate) * up);
+      reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + group * 16 + c] =
+          silu(gate) * up;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int d = p.head_dim, half = d / 2;
@@ -160,7 +162,7 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem<MT>& sm, int group, i
 // ------------------------------------------------------------------------------------------
 // Main kernel
 // ------------------------------------------------------------------------------------------
-template <typename T, int MT, int EPI>
+template <typename T, typename AT, int MT, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
   __shared__ GemmSmem<MT> sm;
   const int lane = threadIdx.x & (kWave - 1);
@@ -183,9 +185,9 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
 
   const char* wp = p.W + (long long)z * p.w_zstride +
                    (long long)(p.nt0 + nt_rel) * p.KT * kTileBytes + lane * 16;
-  const T* A = reinterpret_cast<const T*>(p.A);
+  const AT* A = reinterpret_cast<const AT*>(p.A);
   const int m_base = mblock * MT * 16;
-  const T* arow[MT];
+  const AT* arow[MT];
   bool aval[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -199,9 +201,12 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const i32x4 zero = {0, 0, 0, 0};
+  // The injection GEMM writes the bf16 KV cache: carry its input at full fp32 precision so
+  // the stored values round from as close to the exact product as fp32 accumulation allows.
+  typedef AFrag<T, AT, EPI == EPI_INJECT ? 3 : 2> Frag;
   for (int kt = kb; kt < ke; kt += kUnroll) {
     i32x4 b[kUnroll];
-    i32x4 a[kUnroll][MT];
+    Frag a[kUnroll][MT];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
       b[u] = (kt + u < ke) ? load16<T>(wp + (long long)(kt + u) * kTileBytes) : zero;
@@ -209,13 +214,14 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        a[u][mt] = (kt + u < ke && aval[mt])
-                       ? load16<T>(arow[mt] + (long long)(kt + u) * Elem<T>::kTile)
-                       : zero;
+        a[u][mt].load(arow[mt] + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke && aval[mt]);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_tile<T>(a[u][mt], b[u], acc[mt]);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < Frag::kTerms; ++t)
+          acc[mt] = mfma_tile<T>(a[u][mt].part[t], b[u], acc[mt]);
   }
 
   // Reduce the k sub-ranges of one n-tile inside the workgroup, in wave order.
@@ -282,37 +288,46 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
       __hip_atomic_store(&p.counters[gm], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
-  run_epilogue<T, MT, EPI>(p, sm, group, mblock, z);
+  run_epilogue_impl<T, MT, EPI>(p, sm, group, mblock, z);
 }
 
-template <typename T, int MT>
+template <typename T, typename AT, int MT>
 static hipError_t launch_mt(int epi, const GemmParams& p, int layers, hipStream_t stream) {
   dim3 grid((p.n_tiles / p.tpw) * p.splits, p.n_mblocks, layers);
   dim3 block(kThreads);
-  switch (epi) {
-    case EPI_STORE: gemm_stream<T, MT, EPI_STORE><<<grid, block, 0, stream>>>(p); break;
-    case EPI_RESIDUAL: gemm_stream<T, MT, EPI_RESIDUAL><<<grid, block, 0, stream>>>(p); break;
-    case EPI_SWIGLU: gemm_stream<T, MT, EPI_SWIGLU><<<grid, block, 0, stream>>>(p); break;
-    case EPI_QKV: gemm_stream<T, MT, EPI_QKV><<<grid, block, 0, stream>>>(p); break;
-    case EPI_INJECT: gemm_stream<T, MT, EPI_INJECT><<<grid, block, 0, stream>>>(p); break;
-    case EPI_ARGMAX: gemm_stream<T, MT, EPI_ARGMAX><<<grid, block, 0, stream>>>(p); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(AT) == 2) {
+    // bf16 activations only occur as the target features entering the fusion GEMM.
+    if (epi != EPI_STORE) return hipErrorInvalidValue;
+    gemm_stream<T, AT, MT, EPI_STORE><<<grid, block, 0, stream>>>(p);
+  } else {
+    switch (epi) {
+      case EPI_STORE: gemm_stream<T, AT, MT, EPI_STORE><<<grid, block, 0, stream>>>(p); break;
+      case EPI_RESIDUAL: gemm_stream<T, AT, MT, EPI_RESIDUAL><<<grid, block, 0, stream>>>(p); break;
+      case EPI_SWIGLU: gemm_stream<T, AT, MT, EPI_SWIGLU><<<grid, block, 0, stream>>>(p); break;
+      case EPI_QKV: gemm_stream<T, AT, MT, EPI_QKV><<<grid, block, 0, stream>>>(p); break;
+      case EPI_INJECT: gemm_stream<T, AT, MT, EPI_INJECT><<<grid, block, 0, stream>>>(p); break;
+      case EPI_ARGMAX: gemm_stream<T, AT, MT, EPI_ARGMAX><<<grid, block, 0, stream>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype_bf16, int mt, int epi, const GemmParams& p, int layers,
-                       hipStream_t stream) {
-  if (dtype_bf16) {
-    if (mt == 1) return launch_mt<bf16, 1>(epi, p, layers, stream);
-    if (mt == 2) return launch_mt<bf16, 2>(epi, p, layers, stream);
-    if (mt == 4) return launch_mt<bf16, 4>(epi, p, layers, stream);
-  } else {
-    if (mt == 1) return launch_mt<float, 1>(epi, p, layers, stream);
-    if (mt == 2) return launch_mt<float, 2>(epi, p, layers, stream);
-    if (mt == 4) return launch_mt<float, 4>(epi, p, layers, stream);
-  }
+template <typename T, typename AT>
+static hipError_t launch_a(int mt, int epi, const GemmParams& p, int layers, hipStream_t stream) {
+  if (mt == 1) return launch_mt<T, AT, 1>(epi, p, layers, stream);
+  if (mt == 2) return launch_mt<T, AT, 2>(epi, p, layers, stream);
+  if (mt == 4) return launch_mt<T, AT, 4>(epi, p, layers, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int epi, const GemmParams& p,
+                       int layers, hipStream_t stream) {
+  if (dtype_bf16)
+    return a_bf16 ? launch_a<bf16, bf16>(mt, epi, p, layers, stream)
+                  : launch_a<bf16, float>(mt, epi, p, layers, stream);
+  if (a_bf16) return hipErrorInvalidValue;
+  return launch_a<float, float>(mt, epi, p, layers, stream);
 }
 
 }  // namespace dflash

@@ -12,7 +12,7 @@ struct SampledArgs {
   const float* u_accept;       // [B][15]
   const float* u_resample;     // [B]
   int vocab;
-  float* stats;                // [B][31][2] workspace: (max, sum exp) per row
+  double* stats;               // [B][31][2] workspace: (max, sum exp) per row, fp64
   int* draft_ids;              // [B][15]
   int* accept_len;             // [B]
   int* emitted;                // [B][16]

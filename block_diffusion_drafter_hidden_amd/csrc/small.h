@@ -22,14 +22,14 @@ struct EmbedNormArgs {
   const void* embed;
   int hidden;
   float* x;             // [rows][hidden] fp32 residual
-  void* u;              // [rows][hidden] operand type
+  float* u;             // [rows][hidden] fp32 normed activations
   const float* gain;
   float eps;
 };
 
 struct NormArgs {
   const float* x;
-  void* u;
+  float* u;
   const float* gain;
   int hidden;
   float eps;

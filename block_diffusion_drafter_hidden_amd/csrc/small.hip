@@ -70,7 +70,7 @@ hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipS
 
 // ------------------------------------------------------------------------------------------
 // Block embedding + first RMSNorm.  Row m = b*16 + j: token = anchor[b] for j == 0, else the
-// mask id.  x (fp32 residual) = E[token]; u = RMSNorm(x) * gain in the operand type.
+// mask id.  x (fp32 residual) = E[token]; u = RMSNorm(x) * gain (fp32).
 // One workgroup per row.
 // ------------------------------------------------------------------------------------------
 template <typename T>
@@ -102,12 +102,11 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedNormArgs a) {
   }
   ss = block_sum<T>(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-  T* u = reinterpret_cast<T*>(a.u) + (long long)m * a.hidden;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x)
-    u[i] = Elem<T>::from_f(x[i] * rstd * a.gain[i]);
+  float* u = a.u + (long long)m * a.hidden;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) u[i] = x[i] * rstd * a.gain[i];
 }
 
-// RMSNorm of fp32 rows into the operand type.  With `drop_slot0`, source row b*16 + j
+// RMSNorm of fp32 rows (fp32 out).  With `drop_slot0`, source row b*16 + j
 // (j >= 1) lands in destination row b*15 + j - 1 (the LM-head rows).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
@@ -123,9 +122,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) ss += x[i] * x[i];
   ss = block_sum<T>(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-  T* u = reinterpret_cast<T*>(a.u) + (long long)dst_row * a.hidden;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x)
-    u[i] = Elem<T>::from_f(x[i] * rstd * a.gain[i]);
+  float* u = a.u + (long long)dst_row * a.hidden;
+  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) u[i] = x[i] * rstd * a.gain[i];
 }
 
 hipError_t launch_embed_norm(int bf16_dtype, const EmbedNormArgs& a, int rows,

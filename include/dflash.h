@@ -36,9 +36,11 @@
  *   - Two calls that share a workspace must be ordered on one stream.
  *   - Matrices are row-major.  Linear weights use the logical [out, in] layout.
  *
- * Numerics: bf16 models store weights, features, KV cache and GEMM operands in bf16 and
- * accumulate in fp32; the residual stream, norms, softmax and RoPE angles (computed in
- * fp64, rounded to fp32) stay in fp32.  f32 models use fp32 everywhere.
+ * Numerics: bf16 models keep weights, target features and the KV cache in bf16; every
+ * activation (fused feature, residual stream, normed inputs, q/k/v, attention output,
+ * SwiGLU product, logits) is fp32 in memory and enters the bf16 MFMA as a hi + lo pair of
+ * bf16 values, accumulating in fp32.  RoPE angles are computed in fp64.  f32 models use
+ * fp32 everywhere.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -64,7 +66,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Drafter shape.  Requirements checked by every call: block_size == 16,
  * page_size == 16, hidden % 64 == 0, feat_dim % 64 == 0, intermediate % 64 == 0,
- * vocab % 16 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
+ * vocab % 64 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
  * n_q_heads / n_kv_heads * 16 <= 128. */
 typedef struct {
   int32_t n_layers;
@@ -130,8 +132,8 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
 
 /* Bytes of workspace the step calls need for up to `max_batch` requests and up to
  * `max_inject_rows` rows per dflash_fuse_inject_kv launch chunk (larger n_tok are
- * processed in chunks of this many rows).  `max_ctx` bounds T_b + 16 (attention
- * split sizing).  Returns 0 if the arguments are invalid. */
+ * processed in chunks of this many rows, at most 256).  `max_ctx` bounds the cached
+ * context (max_pages_per_seq * 16 of the cache).  Returns 0 if an argument is invalid. */
 size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
                              int32_t max_inject_rows, int32_t max_ctx);
 
@@ -165,6 +167,17 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
                                  float* logits_out, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* The shared LM head with fused argmax on its own (the last stage of dflash_draft_block).
+ *   y          [rows, H] fp32: final-normed hidden states, one row per draft slot.
+ *   ids_out    [rows] int32 out: argmax over the vocabulary of y . W_lm^T, ties -> lowest id.
+ *   logits_out [rows, V] fp32 out, may be NULL.
+ * `workspace` is a step workspace sized for batch >= ceil(rows / 15) and initialized with
+ * dflash_workspace_init.  The draft step runs exactly this launch for its 15*batch rows. */
+dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
+                                    const void* y, int32_t rows, int32_t* ids_out,
+                                    float* logits_out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* Greedy verification.
  *   draft_ids  [batch, 15] int32: d_1..d_15.

@@ -43,6 +43,13 @@ Readings where the pages are silent (each is listed again in the design doc):
   R18 draft i (slot i, i = 1..15) is compared with the target's prediction
       after slot i-1; the bonus is the target's prediction at the first
       mismatch (or after slot 15).
+  R19 precision of a bf16 drafter: its weights, the target features it reads
+      and its KV cache are bf16; every activation (fused feature, residual
+      stream, norms, q/k/v, attention, SwiGLU, logits) is carried at full
+      precision.  The cache is the one value the model itself writes in bf16,
+      so `precision="bf16"` rounds (to nearest, ties to even, 8 significant
+      bits) exactly the injected K and V; "exact" rounds nowhere.  f32 models
+      use "exact".
 """
 from __future__ import annotations
 
@@ -69,6 +76,27 @@ def f64(x) -> np.ndarray:
 # ------------------------------------------------------------------------------------------
 # Building blocks
 # ------------------------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits, ties to even), from the
+    definition of the format: x = m * 2^e with m in [0.5, 1); keep round(m * 2^8) / 2^8.
+    Valid for normal values below the bf16 maximum (no subnormal or overflow handling; the
+    drafter's tensors stay many binades away from both limits)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def store(x, precision: str) -> np.ndarray:
+    """A value written to the KV cache (reading R19)."""
+    return round_bf16(x) if precision == "bf16" else np.asarray(x, dtype=np.float64)
+
+
+def precision_of(cfg, precision=None) -> str:
+    if precision is not None:
+        return precision
+    return "bf16" if cfg.dtype == "bf16" else "exact"
+
 
 def fuse_features(feats, w_fuse) -> np.ndarray:
     """Feature fusion [wiki, Conditioning item 1]: c[t] = W_fuse . X[t].
@@ -157,11 +185,12 @@ def top2(logits: np.ndarray):
 # The draft step
 # ------------------------------------------------------------------------------------------
 
-def prefill_context(cfg, weights: Dict, feats, positions=None):
+def prefill_context(cfg, weights: Dict, feats, positions=None, precision=None):
     """Inject a whole context: fuse every position, then K/V for every layer.
 
     Returns per-layer lists K[l], V[l] of shape [T, n_kv, d] (contiguous per request;
     paging is a storage detail of the GPU cache)."""
+    p = precision_of(cfg, precision)
     T = feats.shape[0]
     pos = np.arange(T) if positions is None else np.asarray(positions)
     c = fuse_features(feats, weights["w_fuse"])
@@ -169,13 +198,14 @@ def prefill_context(cfg, weights: Dict, feats, positions=None):
     for l in range(cfg.n_layers):
         k, v = inject_kv(c, pos, weights[f"wk.{l}"], weights[f"wv.{l}"], cfg.n_kv_heads,
                          cfg.head_dim, cfg.rope_theta)
-        ks.append(k)
-        vs.append(v)
+        ks.append(store(k, p))
+        vs.append(store(v, p))
     return ks, vs
 
 
 def draft_block(cfg, weights: Dict, k_ctx: Sequence[np.ndarray], v_ctx: Sequence[np.ndarray],
-                anchor: int, want_logits: bool = False, want_hidden: bool = False) -> Dict:
+                anchor: int, want_logits: bool = False, want_hidden: bool = False,
+                precision=None) -> Dict:
     """One block-diffusion forward pass over [anchor, mask x 15] [wiki, Parallel drafting;
     blog, How it works], attending to the injected context K/V of every layer.
 
@@ -183,6 +213,7 @@ def draft_block(cfg, weights: Dict, k_ctx: Sequence[np.ndarray], v_ctx: Sequence
     Returns draft ids [15] (argmax of the shared LM head over slots 1..15), the top-1 and
     top-2 logit values and their gap, and optionally the logits [15, V] and per-layer
     residual streams."""
+    p = precision_of(cfg, precision)
     H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
     nb = cfg.block_size
     T = 0 if len(k_ctx) == 0 else k_ctx[0].shape[0]
@@ -321,9 +352,10 @@ def verify_sampled(draft_logits, target_logits, u_draft, u_accept, u_resample: f
 # ------------------------------------------------------------------------------------------
 
 def draft_step(cfg, weights: Dict, k_ctx: List[np.ndarray], v_ctx: List[np.ndarray],
-               new_feats, anchor: int, target_ids) -> Dict:
+               new_feats, anchor: int, target_ids, precision=None) -> Dict:
     """Inject `new_feats` [n_new, F] at the positions after the current context, draft a
     block from the grown context, then greedily verify against `target_ids` [16]."""
+    p = precision_of(cfg, precision)
     T0 = 0 if len(k_ctx) == 0 else k_ctx[0].shape[0]
     n_new = new_feats.shape[0]
     pos = T0 + np.arange(n_new)
@@ -332,12 +364,13 @@ def draft_step(cfg, weights: Dict, k_ctx: List[np.ndarray], v_ctx: List[np.ndarr
     for l in range(cfg.n_layers):
         k, v = inject_kv(c, pos, weights[f"wk.{l}"], weights[f"wv.{l}"], cfg.n_kv_heads,
                          cfg.head_dim, cfg.rope_theta)
+        k, v = store(k, p), store(v, p)
         if T0:
             k = np.concatenate([k_ctx[l], k], axis=0)
             v = np.concatenate([v_ctx[l], v], axis=0)
         ks.append(k)
         vs.append(v)
-    dr = draft_block(cfg, weights, ks, vs, anchor)
+    dr = draft_block(cfg, weights, ks, vs, anchor, precision=p)
     acc, bonus, emitted = verify_greedy(dr["ids"], target_ids)
     dr.update({"accept_len": acc, "bonus": bonus, "emitted": emitted})
     return dr

@@ -79,6 +79,27 @@ def run_draft(s: Setup, anchors, want_logits=False):
     return ids.cpu().numpy(), (logits.cpu().numpy() if want_logits else None)
 
 
+def cache_matches(gpu, exact, dtype, rel=2e-5, max_flip_frac=0.01):
+    """GPU cache values against the exact (float64) injected values.
+
+    fp32 cache: within 1e-5 of RMS.  bf16 cache: every value must be the bf16 rounding of
+    some number within delta = rel * (|exact| + RMS) of the exact value -- fp32 accumulation
+    of the projection lands that close, and rounding is monotone, so the value must lie in
+    [round(exact - delta), round(exact + delta)] -- and at most `max_flip_frac` of the values
+    may differ from round(exact) at all."""
+    exact = np.asarray(exact, dtype=np.float64)
+    rms = np.sqrt(np.mean(exact * exact))
+    if dtype == "f32":
+        err = np.abs(gpu - exact).max() / rms
+        return bool(err <= 1e-5), {"rel_err": float(err)}
+    delta = rel * (np.abs(exact) + rms)
+    lo, hi = ref.round_bf16(exact - delta), ref.round_bf16(exact + delta)
+    inside = (gpu >= lo) & (gpu <= hi)
+    frac = float((gpu != ref.round_bf16(exact)).mean())
+    ok = bool(inside.all() and frac < max_flip_frac)
+    return ok, {"outside": int((~inside).sum()), "flip_frac": frac}
+
+
 def compare_ids(gpu_ids, orc, dtype):
     """Bit-exact ids except at the oracle's near-ties.  Returns (mismatches, excused)."""
     tie = ref.near_tie(orc["gap"], orc["top1"], orc["top2"], dtype)

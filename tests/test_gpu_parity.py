@@ -2,8 +2,15 @@
 
 Tolerances: drafted ids bit-exact except where the oracle's top-1/top-2 gap is below
 1e-4 relative (fp32 model) or 2e-2 absolute (bf16 model with fp32 accumulation); accept
-lengths and bonus tokens bit-exact; cached K/V within max|diff| / RMS(ref) <= 1e-5 (fp32)
-or 1e-2 (bf16 storage, the rounding of the stored value itself is 2^-9 relative).
+lengths and bonus tokens bit-exact.  Cached K/V: fp32 within 1e-5 of RMS(ref); bf16 must be
+the bf16 rounding of a value within 2e-5 (|exact| + RMS) of the exact one (fp32 accumulation
+of the projection lands that close; a value near a rounding boundary may go either way),
+and under 1% of elements may differ from the rounding of the exact value.
+Logits (diagnostic, both sides bf16 cache): mean error below 5e-3 and max below 5e-2; the
+residual difference is exactly those near-midpoint cache values, amplified by attention
+whose scores spread over several units.  Temperature-1 verify:
+bit-exact except where the oracle's decision margin is below 1e-9 of the mass (both sides
+evaluate the weights and their sums in fp64).
 """
 import numpy as np
 import pytest
@@ -61,15 +68,16 @@ def test_verify_greedy_bit_exact():
 # KV injection
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg,tol", [(TINY, 1e-5), (SMALL_BF16, 1e-2), (SMALL_OSS, 1e-2)])
-def test_injected_cache_matches_oracle(cfg, tol):
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_OSS])
+def test_injected_cache_matches_oracle(cfg):
     s = G.build(cfg, [37, 300, 16], tag="inj")
     for b, T in enumerate(s.ctx_lens):
-        ks, vs = G.oracle_context(s, b)
+        ks, vs = ref.prefill_context(cfg, s.w, s.feats[b], precision="exact")
         gk, gv = G.gather_pool(s, b, T, "k"), G.gather_pool(s, b, T, "v")
         for l in range(cfg.n_layers):
-            assert rel_err(gk[l], ks[l]) <= tol, (b, l, "k")
-            assert rel_err(gv[l], vs[l]) <= tol, (b, l, "v")
+            for name, g, e in (("k", gk[l], ks[l]), ("v", gv[l], vs[l])):
+                ok, info = G.cache_matches(g, e, cfg.dtype)
+                assert ok, (b, l, name, info)
 
 
 def test_injection_in_two_calls_equals_one_call():
@@ -101,11 +109,11 @@ def test_draft_ids_and_logits_match_oracle(cfg, ctx):
         orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
         bad, excused = G.compare_ids(ids[b], orc, cfg.dtype)
         assert bad == 0, (ids[b], orc["ids"], orc["gap"])
-        err = np.abs(logits[b] - orc["logits"]).max()
+        err = np.abs(logits[b] - orc["logits"])
         if cfg.dtype == "f32":
-            assert err <= 1e-4 * np.abs(orc["logits"]).max()
+            assert err.max() <= 1e-4 * np.abs(orc["logits"]).max()
         else:
-            assert err < 2e-2, err
+            assert err.mean() < 5e-3 and err.max() < 5e-2, (err.mean(), err.max())
 
 
 def test_ragged_batch_with_permuted_pages_matches_per_request_oracle():
@@ -189,7 +197,7 @@ def test_verify_sampled_matches_oracle(batch, vocab):
     excused = 0
     for b in range(batch):
         o = ref.verify_sampled(dl[b], tl[b], ud[b], ua[b], float(ur[b]))
-        near = [m for m in o["margins"] if m[2] <= 1e-4]
+        near = [m for m in o["margins"] if m[2] <= 1e-9]
         if near:
             excused += 1
             continue

@@ -216,6 +216,46 @@ def test_argmax_planted_row_and_lowest_index_tie():
 
 
 # ------------------------------------------------------------------------------------------
+# bf16 storage points (reading R19)
+# ------------------------------------------------------------------------------------------
+
+def test_round_bf16_matches_library_conversion():
+    """Round-to-nearest-even to bf16, checked against torch's float32 -> bfloat16 cast on
+    float32 inputs, including exact halfway cases and values across many binades."""
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    expo = (bits >> 7) & 0xFF
+    bits = bits[(expo >= 1) & (expo <= 253)]                      # normal, far from overflow
+    halfway = ((bits << 16) | 0x8000).view(np.float32)           # exactly between two bf16
+    for v in (x, halfway):
+        want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(ref.round_bf16(v.astype(np.float64)), want)
+
+
+def test_bf16_model_matches_torch_model_with_the_same_casts():
+    """A bf16 drafter (reading R19: bf16 KV cache, full-precision activations) computed by
+    the oracle equals an independent torch float64 model that casts its cached K/V to
+    bf16; and it stays within bf16 noise of the exact model while differing from it (the
+    rounding is really applied)."""
+    cfg = scaled(SMALL, name="pin-small-bf16", dtype="bf16")
+    w = synth.drafter_weights(cfg, seed=0, std=0.2, gain_std=0.2)
+    feats = synth.target_features(cfg, 19, "bf16pin")
+    ks, vs = ref.prefill_context(cfg, w, feats)
+    tk, tv = tref.context_kv(cfg, w, feats, bf16=True)
+    for a, b in zip(ks + vs, tk + tv):
+        np.testing.assert_array_equal(a, b.numpy())
+        np.testing.assert_array_equal(ref.round_bf16(a), a)
+    out = ref.draft_block(cfg, w, ks, vs, anchor=11, want_logits=True)
+    lib = tref.draft_logits(cfg, w, tk, tv, anchor=11).numpy()
+    np.testing.assert_allclose(out["logits"], lib, rtol=1e-9, atol=1e-9)
+    exact = ref.draft_block(cfg, w, *ref.prefill_context(cfg, w, feats, precision="exact"),
+                            anchor=11, want_logits=True, precision="exact")["logits"]
+    diff = np.abs(exact - out["logits"]).max() / np.abs(exact).max()
+    assert 1e-5 < diff < 5e-2
+
+
+# ------------------------------------------------------------------------------------------
 # Greedy verify
 # ------------------------------------------------------------------------------------------
 

@@ -28,6 +28,25 @@ def rope_complex(z: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tens
     return torch.cat([zc.real, zc.imag], dim=-1)
 
 
+def _bf(x: torch.Tensor, on: bool) -> torch.Tensor:
+    return x.float().to(torch.bfloat16).to(torch.float64) if on else x
+
+
+def context_kv(cfg, weights, feats, bf16: bool = False):
+    """Injected K/V of every layer for context features [T, F] (positions 0..T-1); with
+    `bf16`, the cached values are cast to bf16 as a bf16 drafter's cache holds them."""
+    T = feats.shape[0]
+    c = F.linear(_t(feats), _t(weights["w_fuse"]))
+    pos = torch.arange(T)
+    ks, vs = [], []
+    for l in range(cfg.n_layers):
+        k = F.linear(c, _t(weights[f"wk.{l}"])).view(T, cfg.n_kv_heads, cfg.head_dim)
+        v = F.linear(c, _t(weights[f"wv.{l}"])).view(T, cfg.n_kv_heads, cfg.head_dim)
+        ks.append(_bf(rope_complex(k, pos, cfg.rope_theta), bf16))
+        vs.append(_bf(v, bf16))
+    return ks, vs
+
+
 def draft_logits(cfg, weights, k_ctx, v_ctx, anchor: int) -> torch.Tensor:
     """Logits [15, V] of the block-diffusion pass, float64."""
     nb, d = cfg.block_size, cfg.head_dim
