@@ -113,40 +113,34 @@ Packed packed_layout(const Dims& m) {
 }
 
 // ---------------------------------------------------------------------------------------
-// GEMM planning.
+// GEMM planning.  Waves split the k range of a tile group (ksub), a workgroup holds tgpw tile
+// groups; the plan aims at >= kTargetWaves waves in flight with >= 8 k-tiles per wave.
 // ---------------------------------------------------------------------------------------
 struct Plan {
-  int mt, n_mblocks, tpw, splits, kts, targets;
-  size_t partial_bytes;
-  int counters;
+  int mt, n_mblocks, npw, ksub, tgpw;
 };
 
-Plan plan_gemm(int n_tiles, int KT, int M, int group, int tpw, int layers, bool allow_split) {
+Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers) {
   Plan p{};
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.n_mblocks = cdiv(M, 16 * p.mt);
-  p.tpw = tpw;
-  const int ksub = 4 / tpw;
-  const long long wgs = (long long)(n_tiles / tpw) * p.n_mblocks * layers;
-  int splits = 1;
-  if (allow_split) {
-    splits = (int)std::lround((double)kTargetWaves / (double)(wgs * 4));
-    const int max_splits = std::max(1, KT / (4 * ksub));
-    splits = std::max(1, std::min(splits, max_splits));
-  }
-  p.kts = cdiv(KT, splits);
-  p.splits = cdiv(KT, p.kts);
-  p.targets = (group / tpw) * p.splits;
-  const int groups = n_tiles / group;
-  if (p.targets > 1) {
-    p.partial_bytes = (size_t)layers * groups * p.n_mblocks * p.targets * tpw * p.mt * 256 * 4;
-    p.counters = layers * groups * p.n_mblocks;
-  }
+  p.n_mblocks = cdiv(std::max(M, 1), 16 * p.mt);
+  p.npw = npw;
+  const long long units = (long long)(n_tiles / npw) * p.n_mblocks * layers;
+  const int max_waves = std::max(1, 16 / (npw * p.mt));  // LDS reduction slots
+  p.ksub = 1;
+  while (p.ksub < 16 && units * p.ksub < kTargetWaves && KT / (p.ksub * 2) >= 8 &&
+         p.ksub * 2 <= max_waves)
+    p.ksub *= 2;
+  p.tgpw = 1;
+  while (p.ksub * p.tgpw < 4 && p.ksub * p.tgpw * 2 <= max_waves &&
+         (n_tiles / npw) % (p.tgpw * 2) == 0 &&
+         p.mt * 16 * (p.tgpw * 2 * npw * 16 + 1) <= 64 * 65)
+    p.tgpw *= 2;
   return p;
 }
 
 GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const void* A, int lda,
-                       int M, int n_tiles, int group, float* partials, unsigned* counters) {
+                       int M, int n_tiles) {
   GemmParams g;
   std::memset(&g, 0, sizeof(g));
   g.W = W;
@@ -155,14 +149,11 @@ GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const voi
   g.A = A;
   g.lda = lda;
   g.M = M;
+  g.a_mode = A_PLAIN;
   g.n_tiles = n_tiles;
-  g.group = group;
-  g.tpw = pl.tpw;
-  g.splits = pl.splits;
-  g.kts = pl.kts;
+  g.ksub = pl.ksub;
+  g.tgpw = pl.tgpw;
   g.n_mblocks = pl.n_mblocks;
-  g.partials = partials;
-  g.counters = counters;
   return g;
 }
 
@@ -182,34 +173,29 @@ struct Carver {
 struct DraftPlan {
   Plan qkv, o, gu, dn, lm;
   int nc, chunk;
-  size_t x, u, q, bk, bv, ao, h, y, part, apart_o, apart_ml;
+  size_t x, q, bk, bv, ao, h, apart_o, apart_ml;
   size_t total;
 };
 
 DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   DraftPlan p{};
   const int rows = B * 16;
-  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, m.d / 16, 1, 1, true);
-  p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 1, true);
-  p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 2, 1, true);
-  p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 1, true);
-  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, B * 15, 4, 4, 1, false);
+  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 1, 1);
+  p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1);
+  p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1);
+  p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1);
+  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, B * 15, 4, 1);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   p.nc = std::max(1, std::min(cdiv(kAttnTargetWGs, kv_groups), max_chunks));
   p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
-  p.u = c.take((size_t)rows * m.H * 4);
   p.q = c.take((size_t)rows * m.nq * m.d * 4);
   p.bk = c.take((size_t)rows * m.nkv * m.d * 4);
   p.bv = c.take((size_t)rows * m.nkv * m.d * 4);
   p.ao = c.take((size_t)rows * m.nq * m.d * 4);
   p.h = c.take((size_t)rows * m.I * 4);
-  p.y = c.take((size_t)B * 15 * m.H * 4);
-  const size_t part = std::max({p.qkv.partial_bytes, p.o.partial_bytes, p.gu.partial_bytes,
-                                p.dn.partial_bytes, (size_t)16});
-  p.part = c.take(part);
   const size_t R = (size_t)m.G * 16;
   p.apart_o = c.take((size_t)kv_groups * (p.nc + 1) * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * (p.nc + 1) * R * 2 * 4);
@@ -219,21 +205,18 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
 
 struct InjectPlan {
   Plan fuse, kv;
-  size_t c, part, total;
+  size_t c, total;
 };
 
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
-  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 1, true);
-  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, m.d / 16, 1, m.L, true);
+  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);
+  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 1, m.L);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)rows * m.H * 4);
-  p.part = c.take(std::max({p.fuse.partial_bytes, p.kv.partial_bytes, (size_t)16}));
   p.total = c.off;
   return p;
 }
-
-bool counters_fit(const Plan& p) { return p.counters <= kMaxCounters; }
 
 constexpr int kInjectChunkRows = 256;
 
@@ -243,22 +226,22 @@ constexpr int kInjectChunkRows = 256;
     if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
   } while (0)
 
-// Shared LM head + argmax over the vocabulary for `rows` normed rows y.
-dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* y,
-                             int rows, int* ids_out, float* logits_out, char* ws,
-                             hipStream_t stream) {
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+// Final RMSNorm + shared LM head + argmax over the vocabulary.  `x` holds fp32 hidden rows;
+// with draft_rows the rows are the 15 draft slots of each 16-slot block.
+dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* x,
+                             int rows, bool draft_rows, int* ids_out, float* logits_out,
+                             char* ws, hipStream_t stream) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
-  const Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 4, 1, false);
-  GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, y, m.H, rows, m.V / 16, 4,
-                             nullptr, counters);
+  const Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
+  GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, x, m.H, rows, m.V / 16);
+  g.a_mode = draft_rows ? A_NORM_DRAFT : A_NORM;
+  g.gamma = reinterpret_cast<const float*>(wb + P.final_norm);
+  g.eps = m.eps;
   g.keys = keys;
-  g.ids_out = ids_out;
   g.logits_out = logits_out;
   g.ldo = m.V;
-  g.done_counter = counters + kMaxCounters;
-  g.total_wgs = (m.V / 16 / 4) * pl.n_mblocks;
-  DF_TRY(launch_gemm(m.bf16, 0, pl.mt, EPI_ARGMAX, g, 1, stream));
+  DF_TRY(launch_gemm(m.bf16, 0, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
+  DF_TRY(launch_argmax_finalize(keys, ids_out, rows, stream));
   return DFLASH_OK;
 }
 
@@ -308,6 +291,7 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
     a.src[0] = src;
     a.seg_tiles[0] = N / 16;
     a.n_segs = 1;
+    a.mode = PACK_CONCAT;
     a.n_tiles_total = N / 16;
     a.KT = K / m.ktile;
     a.K = K;
@@ -332,6 +316,9 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
     q.seg_tiles[1] = m.nkv * m.d / 16;
     q.seg_tiles[2] = m.nkv * m.d / 16;
     q.n_segs = 3;
+    q.mode = PACK_CONCAT;
+    q.rope_segs = 2;   // Q and K heads: rotation pairs side by side
+    q.head_dim = m.d;
     q.n_tiles_total = (m.nq + 2 * m.nkv) * m.d / 16;
     q.KT = m.H / m.ktile;
     q.K = m.H;
@@ -344,7 +331,7 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
     gu.seg_tiles[0] = m.I / 16;
     gu.seg_tiles[1] = m.I / 16;
     gu.n_segs = 2;
-    gu.interleave2 = 1;
+    gu.mode = PACK_GATE_UP;
     gu.n_tiles_total = 2 * m.I / 16;
     gu.KT = m.H / m.ktile;
     gu.K = m.H;
@@ -394,30 +381,26 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
   const int chunk_rows = std::min<int>(n_tok, kInjectChunkRows);
   const InjectPlan ip = inject_plan(m, chunk_rows);
   if (ws_bytes < ip.total) return DFLASH_ERR_WORKSPACE;
-  if (!counters_fit(ip.fuse) || !counters_fit(ip.kv)) return DFLASH_ERR_UNSUPPORTED;
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);
   char* ws = reinterpret_cast<char*>(workspace);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* part = reinterpret_cast<float*>(ws + ip.part);
-  void* cbuf = ws + ip.c;
+  float* cbuf = reinterpret_cast<float*>(ws + ip.c);
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
 
   for (int r0 = 0; r0 < n_tok; r0 += chunk_rows) {
     const int rows = std::min(chunk_rows, n_tok - r0);
     const InjectPlan cp = rows == chunk_rows ? ip : inject_plan(m, rows);
-    {
+    {  // fusion of the concatenated target features: c = W_fuse . X (fp32 out)
       GemmParams g = base_params(cp.fuse, wb + P.w_fuse, 0, m.F / m.ktile,
                                  reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
-                                 m.F, rows, m.H / 16, 1, part, counters);
+                                 m.F, rows, m.H / 16);
       g.out = cbuf;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, m.bf16, cp.fuse.mt, EPI_STORE, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, m.bf16, cp.fuse.mt, cp.fuse.npw, EPI_STORE, g, 1, stream));
     }
-    {
+    {  // every layer's K|V projection of c, RoPE on K, written into the paged cache
       GemmParams g = base_params(cp.kv, wb + P.layer0 + P.wqkv, m.nq * m.d / 16, m.H / m.ktile,
-                                 cbuf, m.H, rows, 2 * m.nkv * m.d / 16, m.d / 16, part,
-                                 counters);
+                                 cbuf, m.H, rows, 2 * m.nkv * m.d / 16);
       g.w_zstride = (long long)P.layer_stride;
       g.n_q = m.nq;
       g.n_kv = m.nkv;
@@ -430,7 +413,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.max_pages = cache->max_pages_per_seq;
       g.seq_idx = seq_idx + r0;
       g.pos = pos + r0;
-      DF_TRY(launch_gemm(m.bf16, 0, cp.kv.mt, EPI_INJECT, g, m.L, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, cp.kv.mt, cp.kv.npw, EPI_INJECT, g, m.L, stream));
     }
   }
   return DFLASH_OK;
@@ -447,42 +430,37 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
   if (!packed || !embed || !anchor_ids || !draft_ids || !workspace || batch <= 0)
     return DFLASH_ERR_INVALID_ARG;
-  if (batch * 15 > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
+  if (batch * 15 > kMaxArgmaxRows || batch * m.nkv > kMaxCounters) return DFLASH_ERR_UNSUPPORTED;
   const int max_ctx = cache->max_pages_per_seq * 16;
   const DraftPlan dp = draft_plan(m, batch, max_ctx);
   if (ws_bytes < dp.total) return DFLASH_ERR_WORKSPACE;
-  if (!counters_fit(dp.qkv) || !counters_fit(dp.o) || !counters_fit(dp.gu) ||
-      !counters_fit(dp.dn) || batch * m.nkv > kMaxCounters)
-    return DFLASH_ERR_UNSUPPORTED;
 
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);
   char* ws = reinterpret_cast<char*>(workspace);
   unsigned* counters = reinterpret_cast<unsigned*>(ws);
   float* x = reinterpret_cast<float*>(ws + dp.x);
-  float* u = reinterpret_cast<float*>(ws + dp.u);
-  float* part = reinterpret_cast<float*>(ws + dp.part);
   const int rows = batch * 16;
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
-  const float* fnorm = reinterpret_cast<const float*>(wb + P.final_norm);
 
-  {
+  {  // x = embedding rows of [anchor, mask x 15]
     EmbedNormArgs e{};
     e.anchor_ids = anchor_ids;
     e.mask_id = m.mask;
     e.embed = embed;
     e.hidden = m.H;
     e.x = x;
-    e.u = u;
-    e.gain = reinterpret_cast<const float*>(wb + P.layer0 + P.attn_norm);
-    e.eps = m.eps;
+    e.u = nullptr;
     DF_TRY(launch_embed_norm(m.bf16, e, rows, stream));
   }
   for (int l = 0; l < m.L; ++l) {
     const char* lb = wb + P.layer0 + (size_t)l * P.layer_stride;
-    {  // fused Q|K|V projection with RoPE
-      GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, u, m.H, rows,
-                                 (m.nq + 2 * m.nkv) * m.d / 16, m.d / 16, part, counters);
+    {  // RMSNorm + fused Q|K|V projection + RoPE
+      GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, x, m.H, rows,
+                                 (m.nq + 2 * m.nkv) * m.d / 16);
+      g.a_mode = A_NORM;
+      g.gamma = reinterpret_cast<const float*>(lb + P.attn_norm);
+      g.eps = m.eps;
       g.q_out = reinterpret_cast<float*>(ws + dp.q);
       g.bk_out = reinterpret_cast<float*>(ws + dp.bk);
       g.bv_out = reinterpret_cast<float*>(ws + dp.bv);
@@ -491,7 +469,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.n_kv = m.nkv;
       g.head_dim = m.d;
       g.log_theta = std::log((double)m.theta);
-      DF_TRY(launch_gemm(m.bf16, 0, dp.qkv.mt, EPI_QKV, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.qkv.mt, dp.qkv.npw, EPI_QKV, g, 1, stream));
     }
     {  // attention over injected context + block
       AttnArgs a{};
@@ -517,67 +495,44 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     }
     {  // output projection + residual
       GemmParams g = base_params(dp.o, lb + P.wo, 0, m.nq * m.d / m.ktile, ws + dp.ao,
-                                 m.nq * m.d, rows, m.H / 16, 1, part, counters);
+                                 m.nq * m.d, rows, m.H / 16);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.o.mt, EPI_RESIDUAL, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.o.mt, dp.o.npw, EPI_RESIDUAL, g, 1, stream));
     }
-    {
-      NormArgs n{};
-      n.x = x;
-      n.u = u;
-      n.gain = reinterpret_cast<const float*>(lb + P.mlp_norm);
-      n.hidden = m.H;
-      n.eps = m.eps;
-      DF_TRY(launch_rmsnorm(m.bf16, n, rows, stream));
-    }
-    {  // gate|up with SiLU * up
-      GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, u, m.H, rows,
-                                 2 * m.I / 16, 2, part, counters);
+    {  // RMSNorm + gate|up + SiLU * up
+      GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, x, m.H, rows, 2 * m.I / 16);
+      g.a_mode = A_NORM;
+      g.gamma = reinterpret_cast<const float*>(lb + P.mlp_norm);
+      g.eps = m.eps;
       g.out = ws + dp.h;
       g.ldo = m.I;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.gu.mt, EPI_SWIGLU, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, 0, dp.gu.mt, dp.gu.npw, EPI_SWIGLU, g, 1, stream));
     }
     {  // down projection + residual
       GemmParams g = base_params(dp.dn, lb + P.wd, 0, m.I / m.ktile, ws + dp.h, m.I, rows,
-                                 m.H / 16, 1, part, counters);
+                                 m.H / 16);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.dn.mt, EPI_RESIDUAL, g, 1, stream));
-    }
-    {
-      NormArgs n{};
-      n.x = x;
-      n.hidden = m.H;
-      n.eps = m.eps;
-      if (l + 1 < m.L) {
-        n.u = u;
-        n.gain = reinterpret_cast<const float*>(wb + P.layer0 + (size_t)(l + 1) * P.layer_stride +
-                                                P.attn_norm);
-        DF_TRY(launch_rmsnorm(m.bf16, n, rows, stream));
-      } else {
-        n.u = reinterpret_cast<float*>(ws + dp.y);
-        n.gain = fnorm;
-        n.drop_slot0 = 1;
-        DF_TRY(launch_rmsnorm(m.bf16, n, batch * 15, stream));
-      }
+      DF_TRY(launch_gemm(m.bf16, 0, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }
-  return launch_lm_head(m, P, wb, ws + dp.y, batch * 15, draft_ids, logits_out, ws, stream);
+  return launch_lm_head(m, P, wb, x, batch * 15, true, draft_ids, logits_out, ws, stream);
 }
 
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
-                                    const void* y, int32_t rows, int32_t* ids_out,
+                                    const float* hidden, int32_t rows, int32_t* ids_out,
                                     float* logits_out, void* workspace, size_t ws_bytes,
                                     hipStream_t stream) {
   Dims m;
   dflash_status st = check_config(cfg, &m);
   if (st != DFLASH_OK) return st;
-  if (!packed || !y || !ids_out || !workspace || rows <= 0) return DFLASH_ERR_INVALID_ARG;
+  if (!packed || !hidden || !ids_out || !workspace || rows <= 0) return DFLASH_ERR_INVALID_ARG;
   if (rows > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
   if (ws_bytes < kSyncBytes) return DFLASH_ERR_WORKSPACE;
-  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), y, rows,
-                        ids_out, logits_out, reinterpret_cast<char*>(workspace), stream);
+  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), hidden,
+                        rows, false, ids_out, logits_out, reinterpret_cast<char*>(workspace),
+                        stream);
 }
 
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,

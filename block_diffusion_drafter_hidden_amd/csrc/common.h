@@ -76,13 +76,10 @@ template <int Terms> struct AFrag<bf16, bf16, Terms> {   // bf16 input features:
 template <int Terms> struct AFrag<bf16, float, Terms> {
   static constexpr int kTerms = Terms;
   i32x4 part[Terms];
-  __device__ inline void load(const float* p, bool valid) {
-    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      v0 = *reinterpret_cast<const f32x4*>(p);
-      v1 = *reinterpret_cast<const f32x4*>(p + 4);
-    }
-    float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  __device__ inline void from_floats(const float* src) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = src[i];
 #pragma unroll
     for (int t = 0; t < Terms; ++t) {
       bf16x8 h;
@@ -100,8 +97,9 @@ template <int Terms> struct AFrag<bf16, float, Terms> {
 template <int Terms> struct AFrag<float, float, Terms> {  // fp32 model
   static constexpr int kTerms = 1;
   i32x4 part[1];
-  __device__ inline void load(const float* p, bool valid) {
-    part[0] = valid ? *reinterpret_cast<const i32x4*>(p) : i32x4{0, 0, 0, 0};
+  __device__ inline void from_floats(const float* f) {
+    part[0] = i32x4{__float_as_int(f[0]), __float_as_int(f[1]), __float_as_int(f[2]),
+                    __float_as_int(f[3])};
   }
 };
 

@@ -8,19 +8,31 @@ namespace dflash {
 
 // Packed weight layout ("MFMA tile layout").  A weight W[N][K] is cut into tiles of 16 rows
 // by kTile columns (kTile = 32 for bf16, 16 for fp32).  Tile (nt, kt) is 1024 contiguous
-// bytes: lane l (0..63) owns 16 bytes holding W[16*nt + l%16][kTile*kt + kPerLane*(l/16) + j]
+// bytes: lane l (0..63) owns 16 bytes holding W[row(nt, l%16)][kTile*kt + kPerLane*(l/16) + j]
 // for j < kPerLane.  Tiles are stored nt-major: byte offset (nt * KT + kt) * 1024 with
-// KT = K / kTile.  One wave streaming one n-tile therefore reads contiguous 1 KB blocks,
-// and each 16-byte lane chunk is directly the B operand of one MFMA step.
+// KT = K / kTile.  One wave streaming one n-tile reads contiguous 1 KB blocks, and each
+// 16-byte lane chunk is directly the B operand of one MFMA step.
+//
+// row(nt, r) is the identity except where an epilogue needs two rows side by side:
+//   * RoPE heads (Q and K): tile t of a head holds dims i = 8t + r/2 (r even) and
+//     i + d/2 (r odd), so each rotation pair sits in two adjacent columns of one tile;
+//   * gate/up: tile j holds gate rows 8j..8j+7 (r < 8) and up rows 8j..8j+7 (r >= 8).
 constexpr int kTileBytes = 1024;
 
 enum Epi : int {
   EPI_STORE = 0,     // out[m][n] = acc, fp32 (fusion output c)
   EPI_RESIDUAL = 1,  // x[m][n] += acc, fp32 residual stream
-  EPI_SWIGLU = 2,    // group = (gate tile, up tile): h[m][16*grp + c] = silu(gate) * up
-  EPI_QKV = 3,       // group = one head of the fused Q|K|V projection: RoPE + scatter
-  EPI_INJECT = 4,    // group = one K or V head of a layer: RoPE + paged-cache write
-  EPI_ARGMAX = 5,    // LM head: running argmax per row, final ids by the last workgroup
+  EPI_SWIGLU = 2,    // tile j: h[m][8j + c] = silu(gate) * up, c < 8
+  EPI_QKV = 3,       // fused Q|K|V projection: RoPE on Q/K pairs, scatter to q / block k, v
+  EPI_INJECT = 4,    // one layer's K|V projection: RoPE on K pairs, write the paged cache
+  EPI_ARGMAX = 5,    // LM head: per-row (value, index) maximum merged with atomicMax
+};
+
+// How A rows are read.
+enum AMode : int {
+  A_PLAIN = 0,       // A[m][k]
+  A_NORM = 1,        // x[m][k] * gamma[k]; the row's RMS scale is applied in the epilogue
+  A_NORM_DRAFT = 2,  // as A_NORM over the draft rows: row m reads x row (m/15)*16 + m%15 + 1
 };
 
 struct GemmParams {
@@ -29,17 +41,16 @@ struct GemmParams {
   long long w_zstride;      // bytes between grid.z slices
   int nt0;                  // first n-tile of this launch inside the packed matrix
   int KT;                   // k-tiles per n-tile row of the packed matrix
-  const void* A;            // activations, row-major [M][lda]: fp32, or bf16 target features
+  const void* A;            // activations: fp32 rows, or bf16 target features
   int lda;
   int M;                    // valid rows
+  int a_mode;
+  const float* gamma;       // A_NORM*: RMSNorm gain [K]
+  float eps;
   int n_tiles;              // n-tiles computed per grid.z slice
-  int group;                // n-tiles per epilogue group
-  int tpw;                  // n-tiles per workgroup (divides group; 1, 2 or 4)
-  int splits;               // k-splits
-  int kts;                  // k-tiles per split
+  int ksub;                 // waves splitting the k range of one tile group
+  int tgpw;                 // tile groups per workgroup (waves per workgroup = ksub * tgpw)
   int n_mblocks;            // grid.y
-  float* partials;          // split-K partial tiles (when a group spans >1 workgroup)
-  unsigned* counters;       // one per (z, group, m-block); zero on entry and on exit
 
   // Epilogue operands
   void* out;                // EPI_STORE: [M][ldo] fp32 c; EPI_RESIDUAL: fp32 x;
@@ -61,16 +72,17 @@ struct GemmParams {
   const int* seq_idx;
   const int* pos;
   // EPI_ARGMAX
-  unsigned long long* keys; // [M] running (value, index) keys, stride 16 words; zero on entry/exit
-  int* ids_out;             // [M]
+  unsigned long long* keys; // [M] (value, index) keys, stride 16 words; zero before the launch
   float* logits_out;        // [M][ldo] or null
-  unsigned* done_counter;   // launch-wide counter; zero on entry and exit
-  int total_wgs;
 };
 
 // dtype_bf16: weight type; a_bf16: activation type of A (bf16 only for the fusion GEMM over
-// the target features; otherwise fp32).
-hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int epi, const GemmParams& p,
-                       int layers, hipStream_t stream);
+// the target features; otherwise fp32); npw: n-tiles per wave (1, 2 or 4).
+hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int npw, int epi,
+                       const GemmParams& p, int layers, hipStream_t stream);
+
+// ids[m] = index encoded in keys[m * 16]; keys reset to zero for the next launch.
+hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows,
+                                  hipStream_t stream);
 
 }  // namespace dflash

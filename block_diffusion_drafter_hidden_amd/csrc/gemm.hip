@@ -1,160 +1,159 @@
 // Weight-streaming GEMM for the DFlash drafter: out = A . W^T with a fused epilogue.
 //
-// Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory and enter a
-// bf16 MFMA as a hi + lo pair (see AFrag), except the bf16 target features of the fusion.
-// Every drafter GEMM has few rows (16 block slots per request, or the injected context
-// rows) and a large weight matrix, so at small batch the kernel's job is to stream the
-// packed bf16 weights from HBM at full bandwidth and feed each 16-byte lane chunk straight
-// into a 16x16 MFMA step (no LDS staging of W, no reuse to exploit).  Work split:
-//   * a workgroup (4 waves) owns `tpw` n-tiles of 16 output columns and one k-split;
-//     its waves divide the split's k-tiles (4 / tpw sub-ranges per n-tile) and reduce
-//     through LDS in a fixed order;
-//   * an epilogue "group" is the set of n-tiles whose outputs must be seen together (a
-//     RoPE head, a gate/up pair, an argmax slab).  When a group spans several workgroups
-//     (k-splits or wide heads), each writes its partial tile, and the last one to arrive
-//     (device-scope counter) sums the partials in split order and runs the epilogue.  The
-//     sum order is fixed, so results are bitwise repeatable run to run.
+// Every drafter GEMM has few rows (16 block slots per request, or the injected context rows)
+// and a large weight matrix, so at small batch the kernel's job is to stream the packed bf16
+// weights from HBM at full bandwidth and feed each 16-byte lane chunk straight into a 16x16
+// MFMA step.  Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory
+// and enter a bf16 MFMA as a sum of bf16 pieces (see AFrag), except the bf16 target
+// features of the fusion GEMM.
+//
+// Work split.  A wave owns NPW consecutive n-tiles (16 output columns each) and a slice of
+// the k range; the `ksub` waves of a tile group cover the whole k range and are reduced
+// through LDS in wave order, so a workgroup produces complete outputs and no workgroup
+// ever waits on another.  RMSNorm of the input is folded in: with A_NORM the kernel reads
+// x * gamma, accumulates the row's sum of squares from the same loads, and scales the
+// finished row by 1/sqrt(mean + eps) before the epilogue.
 #include "common.h"
 #include "gemm.h"
 
 namespace dflash {
 
-constexpr int kThreads = 256;
-constexpr int kGroupMax = 8;
-constexpr int kUnroll = 8;
+constexpr int kMaxWaves = 16;
+constexpr int kRedSlots = 16;          // waves * NPW * MT <= 16 (checked on the host)
+constexpr int kTileFloats = 64 * 65;   // (MT*16) * (cols + 1) <= 4160 (checked on the host)
 
-template <int MT>
 struct GemmSmem {
-  f32x4 red[4][MT][kWave];
-  float tile[MT * 16][kGroupMax * 16 + 1];
-  unsigned flag;
+  f32x4 red[kRedSlots][kWave];
+  float tile[kTileFloats];
+  float ss[kMaxWaves][64];
+  float rstd[64];
 };
 
-template <typename T>
-__device__ inline i32x4 load16(const void* p) {
-  return *reinterpret_cast<const i32x4*>(p);
+__device__ inline i32x4 load16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
+
+// Raw A values of one k-tile fragment for one lane (kPerLane consecutive k).
+template <typename T, typename AT>
+__device__ inline void load_a_raw(const AT* p, bool valid, float* f) {
+  constexpr int n = Elem<T>::kPerLane;
+  if constexpr (sizeof(AT) == 4) {
+#pragma unroll
+    for (int q = 0; q < n / 4; ++q) {
+      const f32x4 v = valid ? *reinterpret_cast<const f32x4*>(p + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[4 * q + i] = v[i];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
-// Epilogues: run on the dense fp32 group tile sm.tile[MT*16][group*16].
+// Epilogues on the workgroup's dense fp32 tile: rows MT*16, columns cols (tile-major).
 // ------------------------------------------------------------------------------------------
 template <typename T, int MT, int EPI>
-__device__ void run_epilogue_impl(const GemmParams& p, GemmSmem<MT>& sm, int group, int mblock,
+__device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int tile0, int mblock,
                              int z) {
-  const int g = p.group;
   const int rows = MT * 16;
-  const int cols = g * 16;
+  const int ld = cols + 1;
   const int m0 = mblock * rows;
-  const int n0 = group * cols;  // relative to nt0
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const float* tl = sm.tile;
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESIDUAL) {
-    for (int idx = tid; idx < rows * cols; idx += kThreads) {
+    for (int idx = tid; idx < rows * cols; idx += nthr) {
       const int r = idx / cols, c = idx % cols;
       const int m = m0 + r;
       if (m >= p.M) continue;
-      const float v = sm.tile[r][c];
-      if constexpr (EPI == EPI_STORE) {
-        reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + n0 + c] = v;
-      } else {
-        float* x = reinterpret_cast<float*>(p.out) + (long long)m * p.ldo + n0 + c;
-        *x = *x + v;
-      }
+      float* o = reinterpret_cast<float*>(p.out) + (long long)m * p.ldo + tile0 * 16 + c;
+      if constexpr (EPI == EPI_STORE) *o = tl[r * ld + c];
+      else *o = *o + tl[r * ld + c];
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int idx = tid; idx < rows * 16; idx += kThreads) {
-      const int r = idx / 16, c = idx % 16;
+    const int half_cols = cols / 2;
+    for (int idx = tid; idx < rows * half_cols; idx += nthr) {
+      const int r = idx / half_cols, q = idx % half_cols;
+      const int jt = q / 8, c = q % 8;  // tile within the workgroup, gate column
       const int m = m0 + r;
       if (m >= p.M) continue;
-      const float gate = sm.tile[r][c];
-      const float up = sm.tile[r][16 + c];
-      reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + group * 16 + c] =
+      const float gate = tl[r * ld + jt * 16 + c];
+      const float up = tl[r * ld + jt * 16 + 8 + c];
+      reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + (tile0 + jt) * 8 + c] =
           silu(gate) * up;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
-    const int d = p.head_dim, half = d / 2;
-    const int head = group;
-    for (int idx = tid; idx < rows * half; idx += kThreads) {
-      const int r = idx / half, i = idx % half;
+    const int d = p.head_dim, half = d / 2, tph = d / 16;
+    const int pairs = cols / 2;
+    for (int idx = tid; idx < rows * pairs; idx += nthr) {
+      const int r = idx / pairs, q = idx % pairs;
+      const int jt = q / 8, pp = q % 8;
       const int m = m0 + r;
       if (m >= p.M) continue;
-      float x1 = sm.tile[r][i], x2 = sm.tile[r][i + half];
+      const int j = tile0 + jt;  // n-tile within the launch
+      const int head = j / tph, t = j % tph;
+      float a0 = tl[r * ld + jt * 16 + 2 * pp], a1 = tl[r * ld + jt * 16 + 2 * pp + 1];
+      const bool rope = EPI == EPI_QKV ? head < p.n_q + p.n_kv : head < p.n_kv;
+      int d0, d1;  // head dims of the two columns
+      int position;
       if constexpr (EPI == EPI_QKV) {
-        const int b = m / kBlock, j = m % kBlock;
-        const int position = p.ctx_lens[b] + j;
+        position = p.ctx_lens[m / kBlock] + m % kBlock;
+      } else {
+        position = p.pos[m];
+      }
+      if (rope) {
+        const int i = 8 * t + pp;
+        float cs, sn;
+        rope_cos_sin(position, i, d, p.log_theta, &cs, &sn);
+        const float y0 = a0 * cs - a1 * sn, y1 = a1 * cs + a0 * sn;
+        a0 = y0;
+        a1 = y1;
+        d0 = i;
+        d1 = i + half;
+      } else {
+        d0 = 16 * t + 2 * pp;
+        d1 = d0 + 1;
+      }
+      if constexpr (EPI == EPI_QKV) {
         float* dst;
-        if (head < p.n_q + p.n_kv) {
-          float cs, sn;
-          rope_cos_sin(position, i, d, p.log_theta, &cs, &sn);
-          const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-          x1 = y1;
-          x2 = y2;
-          dst = head < p.n_q ? p.q_out + ((long long)m * p.n_q + head) * d
-                             : p.bk_out + ((long long)m * p.n_kv + (head - p.n_q)) * d;
-        } else {
-          dst = p.bv_out + ((long long)m * p.n_kv + (head - p.n_q - p.n_kv)) * d;
-        }
-        dst[i] = x1;
-        dst[i + half] = x2;
+        if (head < p.n_q) dst = p.q_out + ((long long)m * p.n_q + head) * d;
+        else if (head < p.n_q + p.n_kv) dst = p.bk_out + ((long long)m * p.n_kv + head - p.n_q) * d;
+        else dst = p.bv_out + ((long long)m * p.n_kv + head - p.n_q - p.n_kv) * d;
+        dst[d0] = a0;
+        dst[d1] = a1;
       } else {
         const int seq = p.seq_idx[m];
-        const int ps = p.pos[m];
-        const int page = p.block_table[(long long)seq * p.max_pages + ps / kPage];
-        const int slot = ps % kPage;
-        const bool is_k = head < p.n_kv;
-        const int h = is_k ? head : head - p.n_kv;
-        if (is_k) {
-          float cs, sn;
-          rope_cos_sin(ps, i, d, p.log_theta, &cs, &sn);
-          const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-          x1 = y1;
-          x2 = y2;
-        }
-        T* pool = reinterpret_cast<T*>(is_k ? p.k_pool : p.v_pool);
+        const int page = p.block_table[(long long)seq * p.max_pages + position / kPage];
+        const int slot = position % kPage;
+        const int h = rope ? head : head - p.n_kv;
+        T* pool = reinterpret_cast<T*>(rope ? p.k_pool : p.v_pool);
         T* dst = pool + (long long)z * p.pool_layer_elems +
                  (((long long)page * p.n_kv + h) * kPage + slot) * d;
-        dst[i] = Elem<T>::from_f(x1);
-        dst[i + half] = Elem<T>::from_f(x2);
+        dst[d0] = Elem<T>::from_f(a0);
+        dst[d1] = Elem<T>::from_f(a1);
       }
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
     if (p.logits_out) {
-      for (int idx = tid; idx < rows * cols; idx += kThreads) {
+      for (int idx = tid; idx < rows * cols; idx += nthr) {
         const int r = idx / cols, c = idx % cols;
         const int m = m0 + r;
-        if (m < p.M) p.logits_out[(long long)m * p.ldo + n0 + c] = sm.tile[r][c];
+        if (m < p.M) p.logits_out[(long long)m * p.ldo + tile0 * 16 + c] = tl[r * ld + c];
       }
     }
-    if (tid < rows) {
-      const int m = m0 + tid;
-      if (m < p.M) {
-        float best = sm.tile[tid][0];
-        int bi = 0;
-        for (int c = 1; c < cols; ++c) {
-          const float v = sm.tile[tid][c];
-          if (v > best) {
-            best = v;
-            bi = c;
-          }
-        }
-        atomicMax(&p.keys[(long long)m * 16], argmax_key(best, n0 + bi));
+    // One wave per row: lanes scan columns, then a wave-wide (value, index) maximum.
+    const int lane = tid % kWave, wave = tid / kWave, nw = nthr / kWave;
+    for (int r = wave; r < rows; r += nw) {
+      const int m = m0 + r;
+      if (m >= p.M) continue;
+      unsigned long long best = 0;
+      for (int c = lane; c < cols; c += kWave) {
+        const unsigned long long k = argmax_key(tl[r * ld + c], tile0 * 16 + c);
+        best = k > best ? k : best;
       }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sm.flag = (arrive_counter(p.done_counter) == (unsigned)(p.total_wgs - 1));
-    __syncthreads();
-    if (sm.flag) {
-      __threadfence();
-      for (int m = tid; m < p.M; m += kThreads) {
-        unsigned long long* kp = &p.keys[(long long)m * 16];
-        const unsigned long long k =
-            __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p.ids_out[m] = argmax_key_index(k);
-        __hip_atomic_store(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long other = __shfl_xor(best, o, kWave);
+        best = other > best ? other : best;
       }
-      if (tid == 0)
-        __hip_atomic_store(p.done_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) atomicMax(&p.keys[(long long)m * 16], best);
     }
   }
 }
@@ -162,172 +161,239 @@ __device__ void run_epilogue_impl(const GemmParams& p, GemmSmem<MT>& sm, int gro
 // ------------------------------------------------------------------------------------------
 // Main kernel
 // ------------------------------------------------------------------------------------------
-template <typename T, typename AT, int MT, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_stream(GemmParams p) {
-  __shared__ GemmSmem<MT> sm;
+template <typename T, typename AT, int MT, int NPW, int EPI, bool NORM>
+__global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
+  __shared__ GemmSmem sm;
+  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
+  typedef AFrag<T, AT, kTerms> Frag;
+  constexpr int kPer = Elem<T>::kPerLane;
+  // k-tiles whose loads are issued together; bounded by the 128 VGPRs a 1024-thread
+  // workgroup leaves each lane (raw fp32 A + gamma for the normed variants).
+  constexpr int U0 = (NPW * MT >= 4) ? 2 : (NPW * MT == 2 ? 4 : 8);
+  constexpr int U = (NORM || kTerms > 2) ? (U0 > 2 ? U0 / 2 : 2) : U0;
+
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int ksub = 4 / p.tpw;
-  const int wgn = blockIdx.x / p.splits;
-  const int split = blockIdx.x % p.splits;
-  const int mblock = blockIdx.y;
-  const int z = blockIdx.z;
-  const int tile_in_wg = wave / ksub;
-  const int ks = wave % ksub;
-  const int nt_rel = wgn * p.tpw + tile_in_wg;
+  const int ksub = p.ksub;
+  const int tg = wave / ksub, ks = wave % ksub;
+  const int wg_tile0 = blockIdx.x * p.tgpw * NPW;
+  const int tile0 = wg_tile0 + tg * NPW;
+  const int mblock = blockIdx.y, z = blockIdx.z;
+  const int kw = (p.KT + ksub - 1) / ksub;
+  const int kb = min(ks * kw, p.KT), ke = min(kb + kw, p.KT);
 
-  // k-tile range of this wave
-  const int k0 = split * p.kts;
-  const int k1 = min(k0 + p.kts, p.KT);
-  const int kw = (k1 - k0 + ksub - 1) / ksub;
-  const int kb = min(k0 + ks * kw, k1);
-  const int ke = min(kb + kw, k1);
+  const char* wp[NPW];
+#pragma unroll
+  for (int t = 0; t < NPW; ++t)
+    wp[t] = p.W + (long long)z * p.w_zstride +
+            (long long)(p.nt0 + tile0 + t) * p.KT * kTileBytes + lane * 16;
 
-  const char* wp = p.W + (long long)z * p.w_zstride +
-                   (long long)(p.nt0 + nt_rel) * p.KT * kTileBytes + lane * 16;
   const AT* A = reinterpret_cast<const AT*>(p.A);
-  const int m_base = mblock * MT * 16;
   const AT* arow[MT];
   bool aval[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = m_base + mt * 16 + (lane & 15);
+    const int r = mblock * MT * 16 + mt * 16 + (lane & 15);
     aval[mt] = r < p.M;
-    arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * Elem<T>::kPerLane;
+    int src = aval[mt] ? r : 0;
+    if (p.a_mode == A_NORM_DRAFT) src = (src / kDrafts) * kBlock + src % kDrafts + 1;
+    arow[mt] = A + (long long)src * p.lda + (lane >> 4) * kPer;
   }
+  const float* gptr = NORM ? p.gamma + (lane >> 4) * kPer : nullptr;
 
-  f32x4 acc[MT];
+  f32x4 acc[NPW][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NPW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ssq[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) ssq[mt] = 0.f;
 
   const i32x4 zero = {0, 0, 0, 0};
-  // The injection GEMM writes the bf16 KV cache: carry its input at full fp32 precision so
-  // the stored values round from as close to the exact product as fp32 accumulation allows.
-  typedef AFrag<T, AT, EPI == EPI_INJECT ? 3 : 2> Frag;
-  for (int kt = kb; kt < ke; kt += kUnroll) {
-    i32x4 b[kUnroll];
-    Frag a[kUnroll][MT];
+  for (int kt = kb; kt < ke; kt += U) {
+    i32x4 b[U][NPW];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      b[u] = (kt + u < ke) ? load16<T>(wp + (long long)(kt + u) * kTileBytes) : zero;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+      for (int t = 0; t < NPW; ++t)
+        b[u][t] = (kt + u < ke) ? load16(wp[t] + (long long)(kt + u) * kTileBytes) : zero;
+    if constexpr (sizeof(AT) == 2) {
+      Frag a[U][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[u][mt].load(arow[mt] + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke && aval[mt]);
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+        for (int mt = 0; mt < MT; ++mt)
+          a[u][mt].load(arow[mt] + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke && aval[mt]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < Frag::kTerms; ++t)
-          acc[mt] = mfma_tile<T>(a[u][mt].part[t], b[u], acc[mt]);
-  }
-
-  // Reduce the k sub-ranges of one n-tile inside the workgroup, in wave order.
-  if (ksub > 1) {
+        for (int t = 0; t < NPW; ++t)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sm.red[wave][mt][lane] = acc[mt];
-    __syncthreads();
-    if (ks == 0) {
+          for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = mfma_tile<T>(a[u][mt].part[0], b[u][t], acc[t][mt]);
+    } else {
+      float f[U][MT][kPer];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 s = sm.red[wave][mt][lane];
-        for (int q = 1; q < ksub; ++q) s += sm.red[wave + q][mt][lane];
-        acc[mt] = s;
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          load_a_raw<T, AT>(arow[mt] + (long long)(kt + u) * Elem<T>::kTile,
+                            kt + u < ke && aval[mt], f[u][mt]);
+      float g[NORM ? U : 1][kPer];
+      if constexpr (NORM) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          load_a_raw<T, float>(gptr + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke, g[u]);
       }
+      // Split each fragment right before its MFMAs to keep few pieces alive.
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if constexpr (NORM) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+              ssq[mt] += f[u][mt][i] * f[u][mt][i];
+              f[u][mt][i] *= g[u][i];
+            }
+          }
+          Frag a;
+          a.from_floats(f[u][mt]);
+#pragma unroll
+          for (int t = 0; t < NPW; ++t)
+#pragma unroll
+            for (int q = 0; q < Frag::kTerms; ++q)
+              acc[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc[t][mt]);
+        }
     }
   }
 
-  const int g = p.group;
-  const int n_groups = p.n_tiles / g;
-  const int cols_per_group = g / p.tpw;  // workgroup columns per group
-  const int group = (wgn * p.tpw) / g;
-  const int wgcol = wgn % cols_per_group;
-  const int targets = cols_per_group * p.splits;
-
-  if (targets == 1) {
-    if (ks == 0) {
+  // k-slices of a tile group: park slices 1.., add them to slice 0 in wave order.
+  if (ksub > 1 && ks > 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < NPW; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sm.tile[mt * 16 + (lane >> 4) * 4 + j][tile_in_wg * 16 + (lane & 15)] = acc[mt][j];
+      for (int mt = 0; mt < MT; ++mt) sm.red[(wave * NPW + t) * MT + mt][lane] = acc[t][mt];
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float s = ssq[mt];
+      s += __shfl_xor(s, 16, kWave);
+      s += __shfl_xor(s, 32, kWave);
+      if (tg == 0 && lane < 16) sm.ss[ks][mt * 16 + lane] = s;
     }
-    __syncthreads();
-  } else {
-    const long long gm = ((long long)z * n_groups + group) * p.n_mblocks + mblock;
-    const int slot = split * cols_per_group + wgcol;
-    f32x4* part = reinterpret_cast<f32x4*>(p.partials);
-    if (ks == 0) {
+  }
+  __syncthreads();
+  if (ksub > 1 && ks == 0) {
+    for (int q = 1; q < ksub; ++q)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        part[(((gm * targets + slot) * p.tpw + tile_in_wg) * MT + mt) * kWave + lane] = acc[mt];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      sm.flag = (arrive_counter(&p.counters[gm]) == (unsigned)(targets - 1));
-    __syncthreads();
-    if (!sm.flag) return;
-    __threadfence();
-    for (int idx = threadIdx.x; idx < g * MT * kWave; idx += kThreads) {
-      const int t = idx / (MT * kWave);
-      const int mt = (idx / kWave) % MT;
-      const int ln = idx % kWave;
-      const int col = t / p.tpw, tiw = t % p.tpw;
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < p.splits; ++sp) {
-        const int sl = sp * cols_per_group + col;
-        s += part[(((gm * targets + sl) * p.tpw + tiw) * MT + mt) * kWave + ln];
-      }
+      for (int t = 0; t < NPW; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.tile[mt * 16 + (ln >> 4) * 4 + j][t * 16 + (ln & 15)] = s[j];
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += sm.red[((wave + q) * NPW + t) * MT + mt][lane];
+  }
+  if constexpr (NORM) {
+    if (threadIdx.x < MT * 16) {
+      float s = 0.f;
+      for (int q = 0; q < ksub; ++q) s += sm.ss[q][threadIdx.x];
+      sm.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)(p.KT * Elem<T>::kTile) + p.eps);
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&p.counters[gm], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
-  run_epilogue_impl<T, MT, EPI>(p, sm, group, mblock, z);
+  const int cols = p.tgpw * NPW * 16;
+  const int ld = cols + 1;
+  if (ks == 0) {
+#pragma unroll
+    for (int t = 0; t < NPW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = mt * 16 + (lane >> 4) * 4 + j;
+          float v = acc[t][mt][j];
+          if constexpr (NORM) v *= sm.rstd[r];
+          sm.tile[r * ld + (tg * NPW + t) * 16 + (lane & 15)] = v;
+        }
+  }
+  __syncthreads();
+  run_epilogue<T, MT, EPI>(p, sm, cols, wg_tile0, mblock, z);
 }
 
-template <typename T, typename AT, int MT>
-static hipError_t launch_mt(int epi, const GemmParams& p, int layers, hipStream_t stream) {
-  dim3 grid((p.n_tiles / p.tpw) * p.splits, p.n_mblocks, layers);
-  dim3 block(kThreads);
-  if constexpr (sizeof(AT) == 2) {
-    // bf16 activations only occur as the target features entering the fusion GEMM.
-    if (epi != EPI_STORE) return hipErrorInvalidValue;
-    gemm_stream<T, AT, MT, EPI_STORE><<<grid, block, 0, stream>>>(p);
-  } else {
-    switch (epi) {
-      case EPI_STORE: gemm_stream<T, AT, MT, EPI_STORE><<<grid, block, 0, stream>>>(p); break;
-      case EPI_RESIDUAL: gemm_stream<T, AT, MT, EPI_RESIDUAL><<<grid, block, 0, stream>>>(p); break;
-      case EPI_SWIGLU: gemm_stream<T, AT, MT, EPI_SWIGLU><<<grid, block, 0, stream>>>(p); break;
-      case EPI_QKV: gemm_stream<T, AT, MT, EPI_QKV><<<grid, block, 0, stream>>>(p); break;
-      case EPI_INJECT: gemm_stream<T, AT, MT, EPI_INJECT><<<grid, block, 0, stream>>>(p); break;
-      case EPI_ARGMAX: gemm_stream<T, AT, MT, EPI_ARGMAX><<<grid, block, 0, stream>>>(p); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+// ------------------------------------------------------------------------------------------
+// Launch
+// ------------------------------------------------------------------------------------------
+template <typename T, typename AT, int MT, int NPW, int EPI, bool NORM>
+static hipError_t go(const GemmParams& p, int layers, hipStream_t stream) {
+  dim3 grid(p.n_tiles / (p.tgpw * NPW), p.n_mblocks, layers);
+  dim3 block(kWave * p.ksub * p.tgpw);
+  gemm_stream<T, AT, MT, NPW, EPI, NORM><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <typename T, typename AT>
-static hipError_t launch_a(int mt, int epi, const GemmParams& p, int layers, hipStream_t stream) {
-  if (mt == 1) return launch_mt<T, AT, 1>(epi, p, layers, stream);
-  if (mt == 2) return launch_mt<T, AT, 2>(epi, p, layers, stream);
-  if (mt == 4) return launch_mt<T, AT, 4>(epi, p, layers, stream);
+template <typename T, int MT>
+static hipError_t launch_mt(int a_bf16, int npw, int epi, const GemmParams& p, int layers,
+                            hipStream_t stream) {
+  const bool norm = p.a_mode != A_PLAIN;
+  if (a_bf16) {
+    if constexpr (sizeof(T) == 2) {
+      if (epi == EPI_STORE && npw == 1 && !norm)
+        return go<T, bf16, MT, 1, EPI_STORE, false>(p, layers, stream);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (epi) {
+    case EPI_STORE:
+      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_STORE, false>(p, layers, stream);
+      break;
+    case EPI_RESIDUAL:
+      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_RESIDUAL, false>(p, layers, stream);
+      break;
+    case EPI_INJECT:
+      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_INJECT, false>(p, layers, stream);
+      break;
+    case EPI_QKV:
+      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_QKV, true>(p, layers, stream);
+      break;
+    case EPI_SWIGLU:
+      if (npw == 2 && norm) return go<T, float, MT, 2, EPI_SWIGLU, true>(p, layers, stream);
+      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_SWIGLU, true>(p, layers, stream);
+      break;
+    case EPI_ARGMAX:
+      if (npw == 4 && norm) return go<T, float, MT, 4, EPI_ARGMAX, true>(p, layers, stream);
+      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_ARGMAX, true>(p, layers, stream);
+      break;
+    default:
+      break;
+  }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int epi, const GemmParams& p,
-                       int layers, hipStream_t stream) {
-  if (dtype_bf16)
-    return a_bf16 ? launch_a<bf16, bf16>(mt, epi, p, layers, stream)
-                  : launch_a<bf16, float>(mt, epi, p, layers, stream);
-  if (a_bf16) return hipErrorInvalidValue;
-  return launch_a<float, float>(mt, epi, p, layers, stream);
+hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int npw, int epi,
+                       const GemmParams& p, int layers, hipStream_t stream) {
+  if (dtype_bf16) {
+    if (mt == 1) return launch_mt<bf16, 1>(a_bf16, npw, epi, p, layers, stream);
+    if (mt == 2) return launch_mt<bf16, 2>(a_bf16, npw, epi, p, layers, stream);
+    if (mt == 4) return launch_mt<bf16, 4>(a_bf16, npw, epi, p, layers, stream);
+  } else if (!a_bf16) {
+    if (mt == 1) return launch_mt<float, 1>(0, npw, epi, p, layers, stream);
+    if (mt == 2) return launch_mt<float, 2>(0, npw, epi, p, layers, stream);
+    if (mt == 4) return launch_mt<float, 4>(0, npw, epi, p, layers, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+__global__ void argmax_finalize_kernel(unsigned long long* keys, int* ids, int rows) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= rows) return;
+  ids[m] = argmax_key_index(keys[(long long)m * 16]);
+  keys[(long long)m * 16] = 0ull;
+}
+
+hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows,
+                                  hipStream_t stream) {
+  argmax_finalize_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(keys, ids, rows);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

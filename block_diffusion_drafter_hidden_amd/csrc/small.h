@@ -5,11 +5,15 @@
 
 namespace dflash {
 
+enum PackMode : int { PACK_CONCAT = 0, PACK_GATE_UP = 1 };
+
 struct PackArgs {
   const void* src[3];   // source segments, row-major [rows][K]
   int seg_tiles[3];     // 16-row tiles per segment
   int n_segs;
-  int interleave2;      // 1: destination tile 2j+s = tile j of segment s
+  int mode;             // PackMode
+  int rope_segs;        // PACK_CONCAT: leading segments laid out as RoPE pairs
+  int head_dim;
   int n_tiles_total;    // destination n-tiles
   int KT;               // k-tiles (K / kTile)
   long long K;          // source row length in elements
@@ -22,7 +26,7 @@ struct EmbedNormArgs {
   const void* embed;
   int hidden;
   float* x;             // [rows][hidden] fp32 residual
-  float* u;             // [rows][hidden] fp32 normed activations
+  float* u;             // [rows][hidden] fp32 normed activations, or null (x only)
   const float* gain;
   float eps;
 };

@@ -7,9 +7,11 @@ namespace dflash {
 
 // ------------------------------------------------------------------------------------------
 // Weight packing into the MFMA tile layout (see gemm.h).  One thread writes one 16-byte lane
-// chunk.  Destination n-tile `dt` takes its 16 rows from source segment `s` as follows:
-//   CONCAT:       segments are stacked along N (Q | K | V).
-//   INTERLEAVE2:  dt = 2*j + s takes n-tile j of segment s (gate, up interleaved by tile).
+// chunk.  Destination n-tile `dt`, tile row `rho` takes its source row as follows:
+//   PACK_CONCAT:  segments stacked along N; the first `rope_segs` segments are RoPE heads of
+//                 width d whose tile t holds dims 8t + rho/2 (+ d/2 for odd rho), so each
+//                 rotation pair lands in two adjacent output columns.
+//   PACK_GATE_UP: tile j holds rows 8j..8j+7 of segment 0 (gate) then of segment 1 (up).
 // ------------------------------------------------------------------------------------------
 template <typename T>
 __global__ void pack_kernel(PackArgs a) {
@@ -20,19 +22,26 @@ __global__ void pack_kernel(PackArgs a) {
   const long long tile = chunk / kWave;
   const int kt = (int)(tile % a.KT);
   const int dt = (int)(tile / a.KT);
-  int seg, st;
-  if (a.interleave2) {
-    seg = dt & 1;
-    st = dt >> 1;
+  const int rho = lane & 15;
+  int seg, row;
+  if (a.mode == PACK_GATE_UP) {
+    seg = rho < 8 ? 0 : 1;
+    row = dt * 8 + (rho & 7);
   } else {
     seg = 0;
-    st = dt;
+    int st = dt;
     while (seg + 1 < a.n_segs && st >= a.seg_tiles[seg]) {
       st -= a.seg_tiles[seg];
       ++seg;
     }
+    if (seg < a.rope_segs) {
+      const int tph = a.head_dim / 16;
+      const int head = st / tph, t = st % tph;
+      row = head * a.head_dim + 8 * t + (rho >> 1) + (rho & 1) * (a.head_dim / 2);
+    } else {
+      row = st * 16 + rho;
+    }
   }
-  const int row = st * 16 + (lane & 15);
   const long long col = (long long)kt * Elem<T>::kTile + (lane >> 4) * Elem<T>::kPerLane;
   const T* src = reinterpret_cast<const T*>(a.src[seg]) + (long long)row * a.K + col;
   i32x4 v = *reinterpret_cast<const i32x4*>(src);
@@ -69,8 +78,8 @@ hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipS
 }
 
 // ------------------------------------------------------------------------------------------
-// Block embedding + first RMSNorm.  Row m = b*16 + j: token = anchor[b] for j == 0, else the
-// mask id.  x (fp32 residual) = E[token]; u = RMSNorm(x) * gain (fp32).
+// Block embedding (+ optionally the first RMSNorm).  Row m = b*16 + j: token = anchor[b] for
+// j == 0, else the mask id.  x (fp32 residual) = E[token]; if u is set, u = RMSNorm(x) * gain.
 // One workgroup per row.
 // ------------------------------------------------------------------------------------------
 template <typename T>
@@ -100,6 +109,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedNormArgs a) {
     x[i] = v;
     ss += v * v;
   }
+  if (!a.u) return;
   ss = block_sum<T>(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
   float* u = a.u + (long long)m * a.hidden;

@@ -168,14 +168,15 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  float* logits_out, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
-/* The shared LM head with fused argmax on its own (the last stage of dflash_draft_block).
- *   y          [rows, H] fp32: final-normed hidden states, one row per draft slot.
- *   ids_out    [rows] int32 out: argmax over the vocabulary of y . W_lm^T, ties -> lowest id.
+/* The last stage of dflash_draft_block on its own: final RMSNorm, the shared LM head and
+ * the argmax over the vocabulary.
+ *   hidden     [rows, H] fp32: residual-stream rows (before the final norm).
+ *   ids_out    [rows] int32 out: argmax of RMSNorm(hidden) . W_lm^T, ties -> lowest id.
  *   logits_out [rows, V] fp32 out, may be NULL.
- * `workspace` is a step workspace sized for batch >= ceil(rows / 15) and initialized with
- * dflash_workspace_init.  The draft step runs exactly this launch for its 15*batch rows. */
+ * `workspace` is any step workspace initialized with dflash_workspace_init (only its
+ * synchronization area is used).  Launches the same kernels as the draft step. */
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
-                                    const void* y, int32_t rows, int32_t* ids_out,
+                                    const float* hidden, int32_t rows, int32_t* ids_out,
                                     float* logits_out, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
 
