@@ -51,7 +51,8 @@ dflash_status check_config(const dflash_config* c, Dims* o) {
   if (c->hidden % 64 || c->feat_dim % 64 || c->intermediate % 64 || c->vocab % 64)
     return DFLASH_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
-  if (!block_attention_supported(c->head_dim, c->n_q_heads / c->n_kv_heads))
+  if (!block_attention_supported(c->dtype == DFLASH_BF16, c->head_dim,
+                                 c->n_q_heads / c->n_kv_heads))
     return DFLASH_ERR_UNSUPPORTED;
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_ERR_INVALID_ARG;
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_ERR_INVALID_ARG;
@@ -438,7 +439,6 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);
   char* ws = reinterpret_cast<char*>(workspace);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
   float* x = reinterpret_cast<float*>(ws + dp.x);
   const int rows = batch * 16;
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
@@ -489,7 +489,6 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.scale = 1.0f / std::sqrt((float)m.d);
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
-      a.counters = counters;
       a.out = reinterpret_cast<float*>(ws + dp.ao);
       DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
     }

@@ -18,14 +18,13 @@ struct AttnArgs {
   int nc;                  // context chunks per request
   int chunk;               // context keys per chunk
   float scale;             // 1 / sqrt(d)
-  float* part_o;           // [B][n_kv][nc+1][R][d]
+  float* part_o;           // [B][n_kv][nc+1][R][d], rows r = head_in_group*16 + slot
   float* part_ml;          // [B][n_kv][nc+1][R][2]
-  unsigned* counters;      // [B][n_kv], zero on entry and exit
   float* out;              // [B*16][n_q*d] fp32
 };
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
                                   hipStream_t stream);
-bool block_attention_supported(int head_dim, int group);
+bool block_attention_supported(int bf16_dtype, int head_dim, int group);
 
 }  // namespace dflash
