@@ -26,7 +26,7 @@ constexpr size_t kSyncBytes = kCounterBytes + kKeyBytes;
 constexpr int kMaxCounters = (int)(kCounterBytes / 4) - 1;  // last one: argmax done counter
 constexpr int kMaxArgmaxRows = (int)(kKeyBytes / kKeyStride);
 constexpr int kTargetWaves = 4096;
-constexpr int kAttnTargetWGs = 512;
+constexpr int kAttnTargetWGs = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -147,6 +147,8 @@ GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const voi
   g.W = W;
   g.nt0 = nt0;
   g.KT = KT;
+  g.nt_stride = KT;
+  g.kt_stride = 1;
   g.A = A;
   g.lda = lda;
   g.M = M;
@@ -188,7 +190,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.lm = plan_gemm(m.V / 16, m.H / m.ktile, B * 15, 4, 1);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
-  p.nc = std::max(1, std::min(cdiv(kAttnTargetWGs, kv_groups), max_chunks));
+  p.nc = std::max(1, std::min({cdiv(kAttnTargetWGs, kv_groups), max_chunks, kAttnMaxChunks}));
   p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);

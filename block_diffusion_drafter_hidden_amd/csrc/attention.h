@@ -5,6 +5,8 @@
 
 namespace dflash {
 
+constexpr int kAttnMaxChunks = 256;   // context chunks per (request, KV group)
+
 struct AttnArgs {
   const float* q;          // [B*16][n_q][d], RoPE applied
   const float* bk;         // [B*16][n_kv][d], block keys (RoPE applied)

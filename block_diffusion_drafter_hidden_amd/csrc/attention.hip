@@ -376,33 +376,63 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Merge: one workgroup per (query head, request).
+// Merge: one workgroup per (query head, request).  First the per-row maximum and total sum
+// over chunks (16 threads per row, fixed order), kept as per-chunk weights in LDS; then
+// every output element is the weighted sum of the chunk partials, chunks in order.
 // ------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
+  __shared__ float w_s[kAttnMaxChunks + 1][kBlock];
+  __shared__ float red[kThreads / kBlock][kBlock];
+  __shared__ float M_s[kBlock], L_s[kBlock];
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.n_q / a.n_kv;
   const int g = h / G, hh = h % G;
   const int R = G * kBlock;
-  const long long slot0 = ((long long)b * a.n_kv + g) * (a.nc + 1);
-  for (int idx = threadIdx.x; idx < kBlock * D; idx += kThreads) {
-    const int j = idx / D, i = idx % D;
-    const int r = hh * kBlock + j;
+  const int nch = a.nc + 1;
+  const long long slot0 = ((long long)b * a.n_kv + g) * nch;
+  const int tid = threadIdx.x;
+  const int j = tid % kBlock, lanec = tid / kBlock;        // row, chunk lane (16 lanes)
+  const int r = hh * kBlock + j;
+
+  float mx = -INFINITY;
+  for (int c = lanec; c < nch; c += kThreads / kBlock) {
+    const float l = a.part_ml[((slot0 + c) * R + r) * 2 + 1];
+    if (l > 0.f) mx = fmaxf(mx, a.part_ml[((slot0 + c) * R + r) * 2 + 0]);
+  }
+  red[lanec][j] = mx;
+  __syncthreads();
+  if (tid < kBlock) {
     float M = -INFINITY;
-    for (int cc = 0; cc <= a.nc; ++cc) {
-      const float l = a.part_ml[((slot0 + cc) * R + r) * 2 + 1];
-      if (l > 0.f) M = fmaxf(M, a.part_ml[((slot0 + cc) * R + r) * 2 + 0]);
-    }
-    float L = 0.f, acc = 0.f;
-    for (int cc = 0; cc <= a.nc; ++cc) {
-      const float l = a.part_ml[((slot0 + cc) * R + r) * 2 + 1];
-      if (l > 0.f) {
-        const float w = expf(a.part_ml[((slot0 + cc) * R + r) * 2 + 0] - M);
-        L += l * w;
-        acc += a.part_o[((slot0 + cc) * R + r) * D + i] * w;
-      }
-    }
-    a.out[(long long)(b * kBlock + j) * (a.n_q * D) + h * D + i] = acc / L;
+    for (int q = 0; q < kThreads / kBlock; ++q) M = fmaxf(M, red[q][tid]);
+    M_s[tid] = M;
+  }
+  __syncthreads();
+  const float M = M_s[j];
+  float lsum = 0.f;
+  for (int c = lanec; c < nch; c += kThreads / kBlock) {
+    const float l = a.part_ml[((slot0 + c) * R + r) * 2 + 1];
+    const float w = l > 0.f ? expf(a.part_ml[((slot0 + c) * R + r) * 2 + 0] - M) : 0.f;
+    w_s[c][j] = w;
+    lsum += l * w;
+  }
+  red[lanec][j] = lsum;
+  __syncthreads();
+  if (tid < kBlock) {
+    float L = 0.f;
+    for (int q = 0; q < kThreads / kBlock; ++q) L += red[q][tid];
+    L_s[tid] = 1.0f / L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kBlock * D; idx += kThreads) {
+    const int jj = idx / D, i = idx % D;
+    const int rr = hh * kBlock + jj;
+    const float* src = a.part_o + (slot0 * R + rr) * D + i;
+    const long long cstride = (long long)R * D;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < nch; ++c) acc += w_s[c][jj] * src[c * cstride];
+    a.out[(long long)(b * kBlock + jj) * (a.n_q * D) + h * D + i] = acc * L_s[jj];
   }
 }
 

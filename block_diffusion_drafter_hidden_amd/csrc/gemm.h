@@ -41,6 +41,8 @@ struct GemmParams {
   long long w_zstride;      // bytes between grid.z slices
   int nt0;                  // first n-tile of this launch inside the packed matrix
   int KT;                   // k-tiles per n-tile row of the packed matrix
+  long long nt_stride;      // tiles between consecutive n-tiles (KT for the n-tile-major packing)
+  long long kt_stride;      // tiles between consecutive k-tiles (1 for the n-tile-major packing)
   const void* A;            // activations: fp32 rows, or bf16 target features
   int lda;
   int M;                    // valid rows
@@ -49,6 +51,7 @@ struct GemmParams {
   float eps;
   int n_tiles;              // n-tiles computed per grid.z slice
   int ksub;                 // waves splitting the k range of one tile group
+  int kinter;               // 1: wave ks takes k-tiles ks, ks+ksub, ...; 0: a contiguous range
   int tgpw;                 // tile groups per workgroup (waves per workgroup = ksub * tgpw)
   int n_mblocks;            // grid.y
 

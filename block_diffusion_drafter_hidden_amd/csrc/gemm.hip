@@ -13,6 +13,8 @@
 // ever waits on another.  RMSNorm of the input is folded in: with A_NORM the kernel reads
 // x * gamma, accumulates the row's sum of squares from the same loads, and scales the
 // finished row by 1/sqrt(mean + eps) before the epilogue.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -179,14 +181,18 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
   const int wg_tile0 = blockIdx.x * p.tgpw * NPW;
   const int tile0 = wg_tile0 + tg * NPW;
   const int mblock = blockIdx.y, z = blockIdx.z;
+  // k-tiles of this wave: kt = kb + i*kstep for kt < ke.
   const int kw = (p.KT + ksub - 1) / ksub;
-  const int kb = min(ks * kw, p.KT), ke = min(kb + kw, p.KT);
+  const int kstep = p.kinter ? ksub : 1;
+  const int kb = p.kinter ? ks : min(ks * kw, p.KT);
+  const int ke = p.kinter ? p.KT : min(kb + kw, p.KT);
 
   const char* wp[NPW];
 #pragma unroll
   for (int t = 0; t < NPW; ++t)
     wp[t] = p.W + (long long)z * p.w_zstride +
-            (long long)(p.nt0 + tile0 + t) * p.KT * kTileBytes + lane * 16;
+            (long long)(p.nt0 + tile0 + t) * p.nt_stride * kTileBytes + lane * 16;
+  const long long kbytes = p.kt_stride * kTileBytes;
 
   const AT* A = reinterpret_cast<const AT*>(p.A);
   const AT* arow[MT];
@@ -211,20 +217,22 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
   for (int mt = 0; mt < MT; ++mt) ssq[mt] = 0.f;
 
   const i32x4 zero = {0, 0, 0, 0};
-  for (int kt = kb; kt < ke; kt += U) {
+  for (int kt = kb; kt < ke; kt += U * kstep) {
     i32x4 b[U][NPW];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int t = 0; t < NPW; ++t)
-        b[u][t] = (kt + u < ke) ? load16(wp[t] + (long long)(kt + u) * kTileBytes) : zero;
+        b[u][t] = (kt + u * kstep < ke) ? load16(wp[t] + (long long)(kt + u * kstep) * kbytes)
+                                        : zero;
     if constexpr (sizeof(AT) == 2) {
       Frag a[U][MT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          a[u][mt].load(arow[mt] + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke && aval[mt]);
+          a[u][mt].load(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile,
+                        kt + u * kstep < ke && aval[mt]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -238,13 +246,14 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          load_a_raw<T, AT>(arow[mt] + (long long)(kt + u) * Elem<T>::kTile,
-                            kt + u < ke && aval[mt], f[u][mt]);
+          load_a_raw<T, AT>(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile,
+                            kt + u * kstep < ke && aval[mt], f[u][mt]);
       float g[NORM ? U : 1][kPer];
       if constexpr (NORM) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          load_a_raw<T, float>(gptr + (long long)(kt + u) * Elem<T>::kTile, kt + u < ke, g[u]);
+          load_a_raw<T, float>(gptr + (long long)(kt + u * kstep) * Elem<T>::kTile,
+                               kt + u * kstep < ke, g[u]);
       }
       // Split each fragment right before its MFMAs to keep few pieces alive.
 #pragma unroll
@@ -337,31 +346,42 @@ static hipError_t launch_mt(int a_bf16, int npw, int epi, const GemmParams& p, i
   const bool norm = p.a_mode != A_PLAIN;
   if (a_bf16) {
     if constexpr (sizeof(T) == 2) {
-      if (epi == EPI_STORE && npw == 1 && !norm)
-        return go<T, bf16, MT, 1, EPI_STORE, false>(p, layers, stream);
+      if (epi == EPI_STORE && !norm) {
+        if (npw == 1) return go<T, bf16, MT, 1, EPI_STORE, false>(p, layers, stream);
+        if (npw == 2) return go<T, bf16, MT, 2, EPI_STORE, false>(p, layers, stream);
+        if (npw == 4) return go<T, bf16, MT, 4, EPI_STORE, false>(p, layers, stream);
+      }
     }
     return hipErrorInvalidValue;
   }
+  auto by_npw = [&](auto epi_c, auto norm_c) -> hipError_t {
+    constexpr int E = decltype(epi_c)::value;
+    constexpr bool N = decltype(norm_c)::value;
+    if (npw == 1) return go<T, float, MT, 1, E, N>(p, layers, stream);
+    if (npw == 2) return go<T, float, MT, 2, E, N>(p, layers, stream);
+    if (npw == 4) return go<T, float, MT, 4, E, N>(p, layers, stream);
+    return hipErrorInvalidValue;
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
   switch (epi) {
     case EPI_STORE:
-      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_STORE, false>(p, layers, stream);
+      if (!norm) return by_npw(std::integral_constant<int, EPI_STORE>{}, F{});
       break;
     case EPI_RESIDUAL:
-      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_RESIDUAL, false>(p, layers, stream);
+      if (!norm) return by_npw(std::integral_constant<int, EPI_RESIDUAL>{}, F{});
       break;
     case EPI_INJECT:
-      if (npw == 1 && !norm) return go<T, float, MT, 1, EPI_INJECT, false>(p, layers, stream);
+      if (!norm) return by_npw(std::integral_constant<int, EPI_INJECT>{}, F{});
       break;
     case EPI_QKV:
-      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_QKV, true>(p, layers, stream);
+      if (norm) return by_npw(std::integral_constant<int, EPI_QKV>{}, Tr{});
       break;
     case EPI_SWIGLU:
-      if (npw == 2 && norm) return go<T, float, MT, 2, EPI_SWIGLU, true>(p, layers, stream);
-      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_SWIGLU, true>(p, layers, stream);
+      if (norm) return by_npw(std::integral_constant<int, EPI_SWIGLU>{}, Tr{});
       break;
     case EPI_ARGMAX:
-      if (npw == 4 && norm) return go<T, float, MT, 4, EPI_ARGMAX, true>(p, layers, stream);
-      if (npw == 1 && norm) return go<T, float, MT, 1, EPI_ARGMAX, true>(p, layers, stream);
+      if (norm) return by_npw(std::integral_constant<int, EPI_ARGMAX>{}, Tr{});
       break;
     default:
       break;
