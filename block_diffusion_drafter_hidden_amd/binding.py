@@ -211,7 +211,7 @@ def error_string(status: int) -> str:
 @dataclass
 class PagedCache:
     k_pool: torch.Tensor          # [L, num_pages, n_kv, 16, d]
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor          # [L, num_pages, n_kv, d, 16] (pages transposed)
     block_table: torch.Tensor     # [B, max_pages] int32
     ctx_lens: torch.Tensor        # [B] int32
     num_pages: int
@@ -243,11 +243,12 @@ class Drafter:
     def new_cache(self, block_table, ctx_lens, num_pages: int) -> PagedCache:
         cfg = self.cfg
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        shape = (cfg.n_layers, num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        k_shape = (cfg.n_layers, num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        v_shape = (cfg.n_layers, num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(self.device).contiguous()
         cl = torch.as_tensor(ctx_lens, dtype=torch.int32).to(self.device).contiguous()
-        return PagedCache(torch.zeros(shape, dtype=dt, device=self.device),
-                          torch.zeros(shape, dtype=dt, device=self.device), bt, cl,
+        return PagedCache(torch.zeros(k_shape, dtype=dt, device=self.device),
+                          torch.zeros(v_shape, dtype=dt, device=self.device), bt, cl,
                           num_pages, int(bt.shape[1]))
 
     def inject(self, cache: PagedCache, feats, seq_idx, pos, stream=None) -> None:

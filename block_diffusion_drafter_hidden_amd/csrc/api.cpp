@@ -152,7 +152,8 @@ GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const voi
   g.A = A;
   g.lda = lda;
   g.M = M;
-  g.a_mode = A_PLAIN;
+  g.a_kind = A_SWZ;
+  g.norm = 0;
   g.n_tiles = n_tiles;
   g.ksub = pl.ksub;
   g.tgpw = pl.tgpw;
@@ -187,7 +188,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1);
-  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, B * 15, 4, 1);
+  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   p.nc = std::max(1, std::min({cdiv(kAttnTargetWGs, kv_groups), max_chunks, kAttnMaxChunks}));
@@ -216,7 +217,7 @@ InjectPlan inject_plan(const Dims& m, int rows) {
   p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 1, m.L);
   Carver c(kSyncBytes);
-  p.c = c.take((size_t)rows * m.H * 4);
+  p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
   p.total = c.off;
   return p;
 }
@@ -229,22 +230,25 @@ constexpr int kInjectChunkRows = 256;
     if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
   } while (0)
 
-// Final RMSNorm + shared LM head + argmax over the vocabulary.  `x` holds fp32 hidden rows;
-// with draft_rows the rows are the 15 draft slots of each 16-slot block.
+// Final RMSNorm + shared LM head + argmax over the vocabulary.  With draft_rows, `x` is the
+// residual stream in the fragment layout (rows = 16-slot blocks; slot 0 is computed and
+// dropped); otherwise fp32 row-major hidden rows.
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* x,
                              int rows, bool draft_rows, int* ids_out, float* logits_out,
                              char* ws, hipStream_t stream) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
   const Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
   GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, x, m.H, rows, m.V / 16);
-  g.a_mode = draft_rows ? A_NORM_DRAFT : A_NORM;
+  g.a_kind = draft_rows ? A_SWZ : A_ROW_F32;
+  g.norm = 1;
   g.gamma = reinterpret_cast<const float*>(wb + P.final_norm);
   g.eps = m.eps;
   g.keys = keys;
   g.logits_out = logits_out;
   g.ldo = m.V;
-  DF_TRY(launch_gemm(m.bf16, 0, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
-  DF_TRY(launch_argmax_finalize(keys, ids_out, rows, stream));
+  g.draft_rows = draft_rows ? 1 : 0;
+  DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
+  DF_TRY(launch_argmax_finalize(keys, ids_out, rows, draft_rows ? 1 : 0, stream));
   return DFLASH_OK;
 }
 
@@ -397,9 +401,10 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       GemmParams g = base_params(cp.fuse, wb + P.w_fuse, 0, m.F / m.ktile,
                                  reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
                                  m.F, rows, m.H / 16);
+      g.a_kind = m.bf16 ? A_ROW_BF16 : A_ROW_F32;
       g.out = cbuf;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, m.bf16, cp.fuse.mt, cp.fuse.npw, EPI_STORE, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, cp.fuse.mt, cp.fuse.npw, EPI_STORE, g, 1, stream));
     }
     {  // every layer's K|V projection of c, RoPE on K, written into the paged cache
       GemmParams g = base_params(cp.kv, wb + P.layer0 + P.wqkv, m.nq * m.d / 16, m.H / m.ktile,
@@ -416,7 +421,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.max_pages = cache->max_pages_per_seq;
       g.seq_idx = seq_idx + r0;
       g.pos = pos + r0;
-      DF_TRY(launch_gemm(m.bf16, 0, cp.kv.mt, cp.kv.npw, EPI_INJECT, g, m.L, stream));
+      DF_TRY(launch_gemm(m.bf16, cp.kv.mt, cp.kv.npw, EPI_INJECT, g, m.L, stream));
     }
   }
   return DFLASH_OK;
@@ -433,7 +438,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
   if (!packed || !embed || !anchor_ids || !draft_ids || !workspace || batch <= 0)
     return DFLASH_ERR_INVALID_ARG;
-  if (batch * 15 > kMaxArgmaxRows || batch * m.nkv > kMaxCounters) return DFLASH_ERR_UNSUPPORTED;
+  if (batch * 16 > kMaxArgmaxRows || batch * m.nkv > kMaxCounters) return DFLASH_ERR_UNSUPPORTED;
   const int max_ctx = cache->max_pages_per_seq * 16;
   const DraftPlan dp = draft_plan(m, batch, max_ctx);
   if (ws_bytes < dp.total) return DFLASH_ERR_WORKSPACE;
@@ -446,21 +451,20 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
 
   {  // x = embedding rows of [anchor, mask x 15]
-    EmbedNormArgs e{};
+    EmbedArgs e{};
     e.anchor_ids = anchor_ids;
     e.mask_id = m.mask;
     e.embed = embed;
     e.hidden = m.H;
     e.x = x;
-    e.u = nullptr;
-    DF_TRY(launch_embed_norm(m.bf16, e, rows, stream));
+    DF_TRY(launch_embed(m.bf16, e, rows, stream));
   }
   for (int l = 0; l < m.L; ++l) {
     const char* lb = wb + P.layer0 + (size_t)l * P.layer_stride;
     {  // RMSNorm + fused Q|K|V projection + RoPE
       GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, x, m.H, rows,
                                  (m.nq + 2 * m.nkv) * m.d / 16);
-      g.a_mode = A_NORM;
+      g.norm = 1;
       g.gamma = reinterpret_cast<const float*>(lb + P.attn_norm);
       g.eps = m.eps;
       g.q_out = reinterpret_cast<float*>(ws + dp.q);
@@ -471,7 +475,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.n_kv = m.nkv;
       g.head_dim = m.d;
       g.log_theta = std::log((double)m.theta);
-      DF_TRY(launch_gemm(m.bf16, 0, dp.qkv.mt, dp.qkv.npw, EPI_QKV, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, dp.qkv.mt, dp.qkv.npw, EPI_QKV, g, 1, stream));
     }
     {  // attention over injected context + block
       AttnArgs a{};
@@ -492,6 +496,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
       a.out = reinterpret_cast<float*>(ws + dp.ao);
+      a.out_kper = m.bf16 ? 8 : 4;
       DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
     }
     {  // output projection + residual
@@ -499,26 +504,26 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  m.nq * m.d, rows, m.H / 16);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.o.mt, dp.o.npw, EPI_RESIDUAL, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, dp.o.mt, dp.o.npw, EPI_RESIDUAL, g, 1, stream));
     }
     {  // RMSNorm + gate|up + SiLU * up
       GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, x, m.H, rows, 2 * m.I / 16);
-      g.a_mode = A_NORM;
+      g.norm = 1;
       g.gamma = reinterpret_cast<const float*>(lb + P.mlp_norm);
       g.eps = m.eps;
       g.out = ws + dp.h;
       g.ldo = m.I;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.gu.mt, dp.gu.npw, EPI_SWIGLU, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, dp.gu.mt, dp.gu.npw, EPI_SWIGLU, g, 1, stream));
     }
     {  // down projection + residual
       GemmParams g = base_params(dp.dn, lb + P.wd, 0, m.I / m.ktile, ws + dp.h, m.I, rows,
                                  m.H / 16);
       g.out = x;
       g.ldo = m.H;
-      DF_TRY(launch_gemm(m.bf16, 0, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
+      DF_TRY(launch_gemm(m.bf16, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }
-  return launch_lm_head(m, P, wb, x, batch * 15, true, draft_ids, logits_out, ws, stream);
+  return launch_lm_head(m, P, wb, x, batch * 16, true, draft_ids, logits_out, ws, stream);
 }
 
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,

@@ -9,10 +9,10 @@ constexpr int kAttnMaxChunks = 256;   // context chunks per (request, KV group)
 
 struct AttnArgs {
   const float* q;          // [B*16][n_q][d], RoPE applied
-  const float* bk;         // [B*16][n_kv][d], block keys (RoPE applied)
-  const float* bv;         // [B*16][n_kv][d]
-  const void* k_pool;      // this layer's pool [num_pages][n_kv][16][d]
-  const void* v_pool;
+  const float* bk;         // [B][n_kv][16][d], block keys (RoPE applied)
+  const float* bv;         // [B][n_kv][d][16], block values, transposed
+  const void* k_pool;      // this layer's K pool [num_pages][n_kv][16][d]
+  const void* v_pool;      // this layer's V pool [num_pages][n_kv][d][16]
   const int* block_table;  // [B][max_pages]
   int max_pages;
   const int* ctx_lens;     // [B]
@@ -20,9 +20,10 @@ struct AttnArgs {
   int nc;                  // context chunks per request
   int chunk;               // context keys per chunk
   float scale;             // 1 / sqrt(d)
-  float* part_o;           // [B][n_kv][nc+1][R][d], rows r = head_in_group*16 + slot
-  float* part_ml;          // [B][n_kv][nc+1][R][2]
-  float* out;              // [B*16][n_q*d] fp32
+  float* part_o;           // [B][n_kv][nc+1][G][d/16][4][16 rows][4]
+  float* part_ml;          // [B][n_kv][nc+1][G][16 rows][2]
+  float* out;              // [B*16][n_q*d] fp32 in the fragment layout (swz_off)
+  int out_kper;            // fragment layout parameter of the consumer GEMM (8 bf16, 4 fp32)
 };
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,

@@ -3,52 +3,92 @@
 // the 16 block keys.
 //
 // Pass 1 (partials), grid (nc + 1, n_kv, batch): workgroup c < nc covers context keys
-// [c*chunk, min((c+1)*chunk, T_b)); workgroup nc covers the 16 block keys.  All G query
-// heads of the KV group are handled together, one 16-row tile per head (rows = block
-// slots), so one pass over a K/V page serves G heads.  Each workgroup keeps an online
-// softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
+// [c*chunk, min((c+1)*chunk, T_b)); workgroup nc covers the 16 block keys.  One wave per
+// query head of the KV group.  Each wave keeps an online softmax (running max m, sum l,
+// unnormalized output o) and writes (m, l, o).
 // Pass 2 (merge), grid (n_q, batch): rescales the nc + 1 partials of each head to a common
-// maximum and divides by the total sum, in chunk order, so results do not depend on
+// maximum and divides by the total sum, chunks in order, so results do not depend on
 // scheduling.
 //
-// bf16 models run QK^T and PV on 16x16x32 bf16 MFMA: cache K/V are exact bf16 operands,
-// fp32 queries, probabilities and block keys/values enter as hi + lo bf16 pairs (products
-// of the two lo pieces, ~2^-32 relative, are dropped).  K is staged in LDS row-major, V
-// transposed, so every MFMA B fragment is one 16-byte LDS read.  fp32 models use a VALU
-// version of pass 1 with the same partial layout.
+// bf16 models run on 16x16x32 bf16 MFMA in transposed form, S^T = K Q^T and
+// O^T += V^T P^T, so that every operand comes straight from memory or from the lane that
+// computed it:
+//   * a K fragment (16 keys x 32 dims) is one 16-byte load per lane from a K page
+//     ([16 keys][d], row-major);
+//   * a V^T fragment (16 dims x 32 keys) is two 8-byte loads per lane from the V pages,
+//     which the cache keeps transposed ([d][16 keys]);
+//   * the S^T output leaves lane l with keys 4*(l/16)+i of every 16-key page for query
+//     row l%16 -- exactly the P^T fragment the PV product needs once the MFMA k index is
+//     read as key (4*(l/16)+j) of the first page for j < 4 and of the second for j >= 4,
+//     the same order the V^T fragment uses.
+// No LDS and no barriers.  Cache K/V are exact bf16 operands; fp32 queries, probabilities
+// and block keys/values enter as hi + lo bf16 pairs (the lo x lo product, ~2^-32 relative,
+// is dropped).  fp32 models use a VALU version of pass 1 with the same partial layout.
+//
+// Partial layout: part_o[slot][head_in_group][dt][q][row][i] holds output dim
+// 16*dt + 4*q + i of block row `row` (a float4 per (dt, q, row)); part_ml[slot][head][row]
+// holds (m, l).  slot = (b * n_kv + g) * (nc + 1) + c.
 #include "attention.h"
 #include "common.h"
 
 namespace dflash {
 
-constexpr int kKeys = 32;       // keys per step (one MFMA k range of PV)
-constexpr int kThreads = 256;   // 4 waves
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// ------------------------------------------------------------------------------------------
-// bf16: MFMA partial kernel
-// ------------------------------------------------------------------------------------------
-template <int D, int G>
-struct AttnSmem {
-  static constexpr int kLd = D + 8;          // K row stride (bf16), padded against conflicts
-  static constexpr int vLd = kKeys + 8;      // V^T row stride (bf16)
-  bf16 k[2][kKeys][kLd];                     // [piece][key][dim]
-  bf16 vt[2][D][vLd];                        // [piece][dim][key]
-  float p[4][16][kKeys + 1];                 // per-wave probability tile (row, key)
-};
+__device__ inline long long part_o_index(long long slot, int G, int hh, int D, int row,
+                                         int dim) {
+  return ((((slot * G + hh) * (D / 16) + dim / 16) * 4 + (dim % 16) / 4) * kBlock + row) * 4 +
+         dim % 4;
+}
 
 __device__ inline void split2(float v, bf16& hi, bf16& lo) {
   hi = (bf16)v;
   lo = (bf16)(v - (float)hi);
 }
 
+// 8 floats -> hi and lo bf16 fragments.
+__device__ inline void split8(const float (&f)[8], i32x4& hi, i32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16 hb, lb;
+    split2(f[i], hb, lb);
+    h[i] = hb;
+    l[i] = lb;
+  }
+  hi = __builtin_bit_cast(i32x4, h);
+  lo = __builtin_bit_cast(i32x4, l);
+}
+
+// Zero the bf16 keys of a V^T fragment that lie at or beyond `nk` valid keys of the
+// 32-key step (element j is key 4q + j of the first page for j < 4, 16 + 4q + j - 4 else).
+__device__ inline i32x4 mask_vt(i32x4 v, int q, int nk) {
+  bf16x8 e = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int key = (j < 4 ? 0 : 16) + 4 * q + (j & 3);
+    if (key >= nk) e[j] = (bf16)0.f;
+  }
+  return __builtin_bit_cast(i32x4, e);
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16: MFMA partial kernel, one wave per query head of the group
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct StepRegs {
+  i32x4 k[2][D / 32];      // two pages x dim steps
+  i32x2 v[D / 16][2];      // dim tiles x pages
+  int nk;                  // valid keys of the step (1..32)
+};
+
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void attn_partial_bf16(AttnArgs a) {
-  __shared__ AttnSmem<D, G> sm;
-  constexpr int KS = D / 32;            // k-steps of QK^T
-  constexpr int DT = D / 16;            // dim tiles of PV
-  constexpr int RT = (G + 3) / 4;       // row tiles (heads) per wave
+__global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
+  constexpr int KS = D / 32;            // dim steps of S^T
+  constexpr int DT = D / 16;            // dim tiles of O^T
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
+  const int n = lane & 15, q = lane >> 4;
   const int nq = a.n_q, nkv = a.n_kv;
   const int T_b = a.ctx_lens[b];
   const bool is_block = c == a.nc;
@@ -60,202 +100,175 @@ __global__ __launch_bounds__(kThreads) void attn_partial_bf16(AttnArgs a) {
     kbeg = (int)min((long long)c * a.chunk, (long long)T_b);
     kend = min(kbeg + a.chunk, T_b);
   }
-  const int npieces = is_block ? 2 : 1;
 
-  // Query fragments (A operand of QK^T): lane l holds row l%16 (block slot), dims
-  // 32*ks + 8*(l/16) .. +8, split into hi/lo; scaled by 1/sqrt(d).
-  i32x4 qf[RT][KS][2];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int hh = wave + 4 * rt;
+  // Q^T fragments (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8,
+  // scaled by 1/sqrt(d) and split hi/lo.
+  i32x4 qf[KS][2];
+  {
+    const float* src = a.q + ((long long)(b * kBlock + n) * nq + g * G + hh) * D + q * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 h, l;
-      if (hh < G) {
-        const float* src = a.q + ((long long)(b * kBlock + (lane & 15)) * nq + g * G + hh) * D +
-                           ks * 32 + (lane >> 4) * 8;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
-        const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          bf16 hb, lb;
-          split2(f[i] * a.scale, hb, lb);
-          h[i] = hb;
-          l[i] = lb;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = l[i] = (bf16)0.f;
-      }
-      qf[rt][ks][0] = __builtin_bit_cast(i32x4, h);
-      qf[rt][ks][1] = __builtin_bit_cast(i32x4, l);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + ks * 32);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
+      const float f[8] = {v0[0] * a.scale, v0[1] * a.scale, v0[2] * a.scale, v0[3] * a.scale,
+                          v1[0] * a.scale, v1[1] * a.scale, v1[2] * a.scale, v1[3] * a.scale};
+      split8(f, qf[ks][0], qf[ks][1]);
     }
   }
 
-  f32x4 o[RT][DT];
-  float mrow[RT][4], lrow[RT][4];
+  f32x4 o[DT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mrow[rt][i] = -INFINITY;
-      lrow[rt][i] = 0.f;
-    }
-  }
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
 
-  const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
-  const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
-  for (int k0 = kbeg; k0 < kend; k0 += kKeys) {
-    const int nk = min(kKeys, kend - k0);
-    // Stage K (row-major) and V (transposed) for 32 keys: 16-byte chunks of 8 dims.
-    for (int idx = tid; idx < kKeys * (D / 8); idx += kThreads) {
-      const int kk = idx / (D / 8), d8 = (idx % (D / 8)) * 8;
-      bf16x8 kh, vh, kl, vl;
-      if (kk < nk) {
-        const int t = k0 + kk;
-        if (is_block) {
-          const long long off = ((long long)(b * kBlock + t) * nkv + g) * D + d8;
-          const f32x4 k0v = *reinterpret_cast<const f32x4*>(a.bk + off);
-          const f32x4 k1v = *reinterpret_cast<const f32x4*>(a.bk + off + 4);
-          const f32x4 v0v = *reinterpret_cast<const f32x4*>(a.bv + off);
-          const f32x4 v1v = *reinterpret_cast<const f32x4*>(a.bv + off + 4);
-          const float kf[8] = {k0v[0], k0v[1], k0v[2], k0v[3], k1v[0], k1v[1], k1v[2], k1v[3]};
-          const float vf[8] = {v0v[0], v0v[1], v0v[2], v0v[3], v1v[0], v1v[1], v1v[2], v1v[3]};
+  // Online-softmax update for one 32-key step given S^T tiles s[2]; returns the P^T
+  // fragment (hi, lo).
+  auto softmax_step = [&](const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
+    float x[8];
+    float mx = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            bf16 h1, l1, h2, l2;
-            split2(kf[i], h1, l1);
-            split2(vf[i], h2, l2);
-            kh[i] = h1;
-            kl[i] = l1;
-            vh[i] = h2;
-            vl[i] = l2;
-          }
-        } else {
-          const int page = a.block_table[(long long)b * a.max_pages + t / kPage];
-          const long long off = (((long long)page * nkv + g) * kPage + t % kPage) * D + d8;
-          kh = *reinterpret_cast<const bf16x8*>(kpool + off);
-          vh = *reinterpret_cast<const bf16x8*>(vpool + off);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kl[i] = vl[i] = (bf16)0.f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kh[i] = vh[i] = kl[i] = vl[i] = (bf16)0.f;
-      }
-      *reinterpret_cast<bf16x8*>(&sm.k[0][kk][d8]) = kh;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.vt[0][d8 + i][kk] = vh[i];
-      if (is_block) {
-        *reinterpret_cast<bf16x8*>(&sm.k[1][kk][d8]) = kl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sm.vt[1][d8 + i][kk] = vl[i];
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (wave + 4 * rt >= G) continue;
-      // S = Q K^T for two 16-key tiles.
-      f32x4 s[2];
-#pragma unroll
-      for (int kt2 = 0; kt2 < 2; ++kt2) {
-        s[kt2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          for (int pb = 0; pb < npieces; ++pb) {
-            const i32x4 kb = *reinterpret_cast<const i32x4*>(
-                &sm.k[pb][kt2 * 16 + (lane & 15)][ks * 32 + (lane >> 4) * 8]);
-            s[kt2] = mfma_tile<bf16>(qf[rt][ks][0], kb, s[kt2]);
-            if (pb == 0) s[kt2] = mfma_tile<bf16>(qf[rt][ks][1], kb, s[kt2]);
-          }
-        }
-      }
-      // Online softmax over the 32 keys.  Lane holds rows 4*(lane/16)+i, key lane%16 of
-      // each tile; a row's keys are the 16 lanes sharing lane/16.
-      float corr[4];
+    for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool v0 = (lane & 15) < nk, v1 = 16 + (lane & 15) < nk;
-        float x0 = v0 ? s[0][i] : -INFINITY, x1 = v1 ? s[1][i] : -INFINITY;
-        float mx = fmaxf(x0, x1);
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-        const float mnew = fmaxf(mrow[rt][i], mx);
-        const float p0 = v0 ? expf(x0 - mnew) : 0.f, p1 = v1 ? expf(x1 - mnew) : 0.f;
-        float ps = p0 + p1;
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, kWave);
-        corr[i] = expf(mrow[rt][i] - mnew);
-        lrow[rt][i] = lrow[rt][i] * corr[i] + ps;
-        mrow[rt][i] = mnew;
-        sm.p[wave][(lane >> 4) * 4 + i][lane & 15] = p0;
-        sm.p[wave][(lane >> 4) * 4 + i][16 + (lane & 15)] = p1;
+        const bool valid = 16 * pg + 4 * q + i < nk;
+        x[pg * 4 + i] = valid ? s[pg][i] : -INFINITY;
+        mx = fmaxf(mx, x[pg * 4 + i]);
       }
-      // o (rows 4*(lane/16)+i) *= corr
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);     // finite: every step has a valid key
+    float pv[8], ps = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = x[e] == -INFINITY ? 0.f : expf(x[e] - m_new);
+      ps += pv[e];
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    const float corr = expf(m_run - m_new);   // 0 on the first step
+    l_run = l_run * corr + ps;
+    m_run = m_new;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[rt][dt][i] *= corr[i];
-      // The probability tile is written and read back by the same wave (transpose of the
-      // MFMA output layout into the A-operand layout): order the LDS accesses.
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      // P as the A operand: lane holds row lane%16, keys 8*(lane/16) .. +8, split hi/lo.
-      i32x4 pa[2];
-      {
-        bf16x8 h, l;
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+    split8(pv, p_hi, p_lo);
+  };
+
+  if (is_block) {
+    // Block keys/values: fp32 [b][g][16][d] keys and [b][g][d][16] transposed values.
+    const float* kb = a.bk + ((long long)(b * nkv + g) * kBlock + n) * D + q * 8;
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16 hb, lb;
-          split2(sm.p[wave][lane & 15][(lane >> 4) * 8 + e], hb, lb);
-          h[e] = hb;
-          l[e] = lb;
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(kb + ks * 32);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(kb + ks * 32 + 4);
+      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      i32x4 kh, kl;
+      split8(f, kh, kl);
+      s[0] = mfma_tile<bf16>(kh, qf[ks][0], s[0]);
+      s[0] = mfma_tile<bf16>(kh, qf[ks][1], s[0]);
+      s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
+    }
+    i32x4 ph, pl;
+    softmax_step(s, kBlock, ph, pl);
+    const float* vb = a.bv + ((long long)(b * nkv + g) * D + n) * kBlock + q * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(vb + dt * 16 * kBlock);
+      const float f[8] = {v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f};
+      i32x4 vh, vl;
+      split8(f, vh, vl);
+      o[dt] = mfma_tile<bf16>(vh, ph, o[dt]);
+      o[dt] = mfma_tile<bf16>(vh, pl, o[dt]);
+      o[dt] = mfma_tile<bf16>(vl, ph, o[dt]);
+    }
+  } else if (kend > kbeg) {
+    const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
+    const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
+    const int* table = a.block_table + (long long)b * a.max_pages;
+    const int pg0 = kbeg / kPage;                     // chunks start on a page boundary
+    const int npg = (kend - kbeg + kPage - 1) / kPage;
+    const int nsteps = (kend - kbeg + 31) / 32;
+    // Physical page ids, 64 logical pages per window: lane i holds page window*64 + i.
+    int win = -1, pid = 0;
+    auto page_of = [&](int pi) -> int {
+      if (pi / kWave != win) {
+        win = pi / kWave;
+        const int li = win * kWave + lane;
+        pid = li < npg ? table[pg0 + li] : 0;
+      }
+      return __builtin_amdgcn_readlane(pid, pi % kWave);
+    };
+    auto load_step = [&](int st, StepRegs<D>& r) {
+      r.nk = min(32, kend - kbeg - 32 * st);
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        if (16 * pg < r.nk) {
+          const long long page = page_of(2 * st + pg);
+          const bf16* kp = kpool + ((page * nkv + g) * kPage + n) * D + q * 8;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = *reinterpret_cast<const i32x4*>(kp + ks * 32);
+          const bf16* vp = vpool + ((page * nkv + g) * D + n) * kPage + q * 4;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            r.v[dt][pg] = *reinterpret_cast<const i32x2*>(vp + dt * 16 * kPage);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) r.v[dt][pg] = i32x2{0, 0};
         }
-        pa[0] = __builtin_bit_cast(i32x4, h);
-        pa[1] = __builtin_bit_cast(i32x4, l);
       }
+    };
+    auto compute_step = [&](const StepRegs<D>& r) {
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][0], s[pg]);
+          s[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][1], s[pg]);
+        }
+      i32x4 ph, pl;
+      softmax_step(s, r.nk, ph, pl);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        for (int pb = 0; pb < npieces; ++pb) {
-          const i32x4 vb = *reinterpret_cast<const i32x4*>(
-              &sm.vt[pb][dt * 16 + (lane & 15)][(lane >> 4) * 8]);
-          o[rt][dt] = mfma_tile<bf16>(pa[0], vb, o[rt][dt]);
-          if (pb == 0) o[rt][dt] = mfma_tile<bf16>(pa[1], vb, o[rt][dt]);
-        }
+        i32x4 v = i32x4{r.v[dt][0][0], r.v[dt][0][1], r.v[dt][1][0], r.v[dt][1][1]};
+        if (r.nk < 32) v = mask_vt(v, q, r.nk);   // stale cache slots may hold any bits
+        o[dt] = mfma_tile<bf16>(v, ph, o[dt]);
+        o[dt] = mfma_tile<bf16>(v, pl, o[dt]);
       }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    };
+    // Two steps in flight: the next step's loads are issued before this step's math.
+    StepRegs<D> ra, rb;
+    load_step(0, ra);
+    for (int st = 0; st < nsteps; st += 2) {
+      if (st + 1 < nsteps) load_step(st + 1, rb);
+      compute_step(ra);
+      if (st + 1 < nsteps) {
+        if (st + 2 < nsteps) load_step(st + 2, ra);
+        compute_step(rb);
+      }
     }
-    __syncthreads();
   }
 
-  // Partial of this chunk: rows r = head*16 + slot.
+  // Partial of this chunk.  O^T layout: lane holds dims 16dt + 4q + i of block row n.
   const long long slot = ((long long)b * nkv + g) * (a.nc + 1) + c;
-  constexpr int R = G * 16;
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kBlock);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int hh = wave + 4 * rt;
-    if (hh >= G) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = hh * 16 + (lane >> 4) * 4 + i;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        a.part_o[(slot * R + row) * D + dt * 16 + (lane & 15)] = o[rt][dt][i];
-      if ((lane & 15) == 0) {
-        a.part_ml[(slot * R + row) * 2 + 0] = mrow[rt][i];
-        a.part_ml[(slot * R + row) * 2 + 1] = lrow[rt][i];
-      }
-    }
+  for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kBlock + n] = o[dt];
+  if (q == 0) {
+    float* ml = a.part_ml + ((slot * G + hh) * kBlock + n) * 2;
+    ml[0] = m_run;
+    ml[1] = l_run;
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // fp32: VALU partial kernel (rows r = head*16 + slot)
 // ------------------------------------------------------------------------------------------
+constexpr int kKeys = 32;       // keys per step
+constexpr int kThreads = 256;   // 4 waves
+
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   constexpr int G = R / kBlock;
@@ -306,14 +319,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
       if (kk < nk) {
         const int t = k0 + kk;
         if (is_block) {
-          const long long off = ((long long)(b * kBlock + t) * nkv + g) * D + i;
-          kv = a.bk[off];
-          vv = a.bv[off];
+          kv = a.bk[((long long)(b * nkv + g) * kBlock + t) * D + i];
+          vv = a.bv[((long long)(b * nkv + g) * D + i) * kBlock + t];
         } else {
-          const int page = a.block_table[(long long)b * a.max_pages + t / kPage];
-          const long long off = (((long long)page * nkv + g) * kPage + t % kPage) * D + i;
-          kv = kpool[off];
-          vv = vpool[off];
+          const long long page = a.block_table[(long long)b * a.max_pages + t / kPage];
+          kv = kpool[((page * nkv + g) * kPage + t % kPage) * D + i];
+          vv = vpool[((page * nkv + g) * D + i) * kPage + t % kPage];
         }
       }
       k_s[kk][i] = kv;
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 #pragma unroll
   for (int n = 0; n < NRO; ++n) {
     const int r = r0 + n * OPH;
-    a.part_o[(slot * R + r) * D + i] = o[n];
+    a.part_o[part_o_index(slot, G, r / kBlock, D, r % kBlock, i)] = o[n];
   }
   if (tid < R) {
     a.part_ml[(slot * R + tid) * 2 + 0] = m_s[tid];
@@ -376,100 +387,122 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Merge: one workgroup per (query head, request).  First the per-row maximum and total sum
-// over chunks (16 threads per row, fixed order), kept as per-chunk weights in LDS; then
-// every output element is the weighted sum of the chunk partials, chunks in order.
+// Merge: one workgroup per (query head, request), one thread per float4 of the head's
+// 16 x d output, written in the fragment layout the output projection reads.  The partial outputs of the first chunks are loaded before the (m, l)
+// pass so both travel in one round trip; the per-row maximum and sum come from 16 rows x
+// (threads / 16) chunk lanes through LDS; the weighted sum runs over chunks in order.
 // ------------------------------------------------------------------------------------------
+constexpr int kMergeBatch = 16;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
+__global__ __launch_bounds__(D * 4) void attn_merge(AttnArgs a) {
+  constexpr int NT = D * 4;                 // threads = float4 positions of 16 x D
+  constexpr int NCL = NT / kBlock;          // chunk lanes per row
   __shared__ float w_s[kAttnMaxChunks + 1][kBlock];
-  __shared__ float red[kThreads / kBlock][kBlock];
-  __shared__ float M_s[kBlock], L_s[kBlock];
+  __shared__ float m_s[kAttnMaxChunks + 1][kBlock];
+  __shared__ float red[NCL][kBlock];
+  __shared__ float M_s[kBlock], invL_s[kBlock];
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.n_q / a.n_kv;
   const int g = h / G, hh = h % G;
-  const int R = G * kBlock;
   const int nch = a.nc + 1;
   const long long slot0 = ((long long)b * a.n_kv + g) * nch;
   const int tid = threadIdx.x;
-  const int j = tid % kBlock, lanec = tid / kBlock;        // row, chunk lane (16 lanes)
-  const int r = hh * kBlock + j;
+  const long long cstride = (long long)G * NT;   // float4s between chunks
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + (slot0 * G + hh) * NT + tid;
 
+  f32x4 v[kMergeBatch];
+#pragma unroll
+  for (int c = 0; c < kMergeBatch; ++c)
+    v[c] = c < nch ? src[c * cstride] : f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Row maximum and weights.  Thread (row j, chunk lane cl).
+  const int j = tid % kBlock, cl = tid / kBlock;
   float mx = -INFINITY;
-  for (int c = lanec; c < nch; c += kThreads / kBlock) {
-    const float l = a.part_ml[((slot0 + c) * R + r) * 2 + 1];
-    if (l > 0.f) mx = fmaxf(mx, a.part_ml[((slot0 + c) * R + r) * 2 + 0]);
+  for (int c = cl; c < nch; c += NCL) {
+    const float* ml = a.part_ml + (((slot0 + c) * G + hh) * kBlock + j) * 2;
+    const float m = ml[0], l = ml[1];
+    const float mm = l > 0.f ? m : -INFINITY;   // empty chunks carry no weight
+    m_s[c][j] = mm;
+    w_s[c][j] = l;
+    mx = fmaxf(mx, mm);
   }
-  red[lanec][j] = mx;
+  red[cl][j] = mx;
   __syncthreads();
   if (tid < kBlock) {
     float M = -INFINITY;
-    for (int q = 0; q < kThreads / kBlock; ++q) M = fmaxf(M, red[q][tid]);
+    for (int r = 0; r < NCL; ++r) M = fmaxf(M, red[r][tid]);
     M_s[tid] = M;
   }
   __syncthreads();
-  const float M = M_s[j];
   float lsum = 0.f;
-  for (int c = lanec; c < nch; c += kThreads / kBlock) {
-    const float l = a.part_ml[((slot0 + c) * R + r) * 2 + 1];
-    const float w = l > 0.f ? expf(a.part_ml[((slot0 + c) * R + r) * 2 + 0] - M) : 0.f;
+  for (int c = cl; c < nch; c += NCL) {
+    const float mm = m_s[c][j];
+    const float w = mm == -INFINITY ? 0.f : expf(mm - M_s[j]);
+    lsum += w_s[c][j] * w;
     w_s[c][j] = w;
-    lsum += l * w;
   }
-  red[lanec][j] = lsum;
+  __syncthreads();
+  red[cl][j] = lsum;
   __syncthreads();
   if (tid < kBlock) {
     float L = 0.f;
-    for (int q = 0; q < kThreads / kBlock; ++q) L += red[q][tid];
-    L_s[tid] = 1.0f / L;
+    for (int r = 0; r < NCL; ++r) L += red[r][tid];
+    invL_s[tid] = 1.0f / L;
   }
   __syncthreads();
-  for (int idx = tid; idx < kBlock * D; idx += kThreads) {
-    const int jj = idx / D, i = idx % D;
-    const int rr = hh * kBlock + jj;
-    const float* src = a.part_o + (slot0 * R + rr) * D + i;
-    const long long cstride = (long long)R * D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < nch; ++c) acc += w_s[c][jj] * src[c * cstride];
-    a.out[(long long)(b * kBlock + jj) * (a.n_q * D) + h * D + i] = acc * L_s[jj];
+
+  // Thread tid holds float4 (dt, q, row) = tid: row tid % 16, dims 16*(tid/64) + 4*((tid/16)%4).
+  const int row = tid % kBlock;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kMergeBatch; ++c)
+    if (c < nch) acc += w_s[c][row] * v[c];
+  for (int c0 = kMergeBatch; c0 < nch; c0 += kMergeBatch) {
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      v[c] = c0 + c < nch ? src[(c0 + c) * cstride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c0 + c < nch) acc += w_s[c0 + c][row] * v[c];
   }
+  const int dim = 16 * (tid / (4 * kBlock)) + 4 * ((tid / kBlock) % 4);
+  const int kto = a.n_q * D / (4 * a.out_kper);
+  *reinterpret_cast<f32x4*>(a.out + swz_off(b * kBlock + row, h * D + dim, kto, a.out_kper)) =
+      acc * invL_s[row];
 }
 
 // ------------------------------------------------------------------------------------------
 // Launch
 // ------------------------------------------------------------------------------------------
+template <int D>
+static void launch_partial_bf16(int G, dim3 grid, const AttnArgs& a, hipStream_t stream) {
+  switch (G) {
+    case 1: attn_partial_bf16<D, 1><<<grid, 1 * kWave, 0, stream>>>(a); break;
+    case 2: attn_partial_bf16<D, 2><<<grid, 2 * kWave, 0, stream>>>(a); break;
+    case 4: attn_partial_bf16<D, 4><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 8: attn_partial_bf16<D, 8><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    default: break;
+  }
+}
+
 static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
                                  hipStream_t stream) {
   dim3 grid(a.nc + 1, a.n_kv, batch);
   const int G = a.n_q / a.n_kv;
+  if (!block_attention_supported(bf16_dtype, a.head_dim, G)) return hipErrorInvalidValue;
   if (bf16_dtype) {
-    if (a.head_dim == 128) {
-      if (G == 2) attn_partial_bf16<128, 2><<<grid, kThreads, 0, stream>>>(a);
-      else if (G == 4) attn_partial_bf16<128, 4><<<grid, kThreads, 0, stream>>>(a);
-      else if (G == 8) attn_partial_bf16<128, 8><<<grid, kThreads, 0, stream>>>(a);
-      else return hipErrorInvalidValue;
-    } else if (a.head_dim == 64) {
-      if (G == 2) attn_partial_bf16<64, 2><<<grid, kThreads, 0, stream>>>(a);
-      else if (G == 4) attn_partial_bf16<64, 4><<<grid, kThreads, 0, stream>>>(a);
-      else if (G == 8) attn_partial_bf16<64, 8><<<grid, kThreads, 0, stream>>>(a);
-      else return hipErrorInvalidValue;
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (a.head_dim == 128) launch_partial_bf16<128>(G, grid, a, stream);
+    else launch_partial_bf16<64>(G, grid, a, stream);
   } else {
     const int R = G * kBlock;
     if (a.head_dim == 128) {
       if (R == 32) attn_partial_f32<128, 32><<<grid, kThreads, 0, stream>>>(a);
-      else if (R == 64) attn_partial_f32<128, 64><<<grid, kThreads, 0, stream>>>(a);
-      else return hipErrorInvalidValue;
-    } else if (a.head_dim == 64) {
+      else attn_partial_f32<128, 64><<<grid, kThreads, 0, stream>>>(a);
+    } else {
       if (R == 32) attn_partial_f32<64, 32><<<grid, kThreads, 0, stream>>>(a);
       else if (R == 64) attn_partial_f32<64, 64><<<grid, kThreads, 0, stream>>>(a);
-      else if (R == 128) attn_partial_f32<64, 128><<<grid, kThreads, 0, stream>>>(a);
-      else return hipErrorInvalidValue;
-    } else {
-      return hipErrorInvalidValue;
+      else attn_partial_f32<64, 128><<<grid, kThreads, 0, stream>>>(a);
     }
   }
   return hipGetLastError();
@@ -477,18 +510,21 @@ static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
                                   hipStream_t stream) {
+  if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk % 32 != 0) return hipErrorInvalidValue;
   hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
   if (e != hipSuccess) return e;
   dim3 grid(a.n_q, batch);
-  if (a.head_dim == 128) attn_merge<128><<<grid, kThreads, 0, stream>>>(a);
-  else attn_merge<64><<<grid, kThreads, 0, stream>>>(a);
+  if (a.head_dim == 128) attn_merge<128><<<grid, 128 * 4, 0, stream>>>(a);
+  else attn_merge<64><<<grid, 64 * 4, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 bool block_attention_supported(int bf16_dtype, int head_dim, int group) {
   if (head_dim != 64 && head_dim != 128) return false;
+  if (bf16_dtype) return group == 1 || group == 2 || group == 4 || group == 8;
+  // fp32 VALU kernel: 32..128 query rows per group, LDS-bounded at d = 128.
   if (group != 2 && group != 4 && group != 8) return false;
-  return bf16_dtype || !(head_dim == 128 && group == 8);  // fp32 kernel: LDS limit
+  return !(head_dim == 128 && group == 8);
 }
 
 }  // namespace dflash

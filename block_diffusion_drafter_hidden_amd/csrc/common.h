@@ -127,9 +127,19 @@ __device__ inline int argmax_key_index(unsigned long long k) {
   return (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
 }
 
-// Device-scope release/acquire helpers for the "last workgroup finishes" pattern.
-__device__ inline unsigned arrive_counter(unsigned* ctr) {
-  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------------------------------
+// Fragment ("swizzled") layout of fp32 activations.  An activation matrix [M][K] that feeds
+// a GEMM is stored as the GEMM's A fragments: for each 16-row m-tile and each k-tile of
+// kTile = 4 * kPer columns, the 16 x kTile values are kPer / 4 blocks of 64 lanes x 4
+// floats, lane l holding row l % 16 and columns kPer * (l / 16) + 4 * block + e.  Loading
+// one k-tile of A is then kPer / 4 fully coalesced 1 KB reads.  Rows are padded to 16.
+// Offset in floats of element (r, k) for a matrix of KT k-tiles:
+// ---------------------------------------------------------------------------------------
+__device__ inline long long swz_off(int r, int k, int KT, int kPer) {
+  const int kTile = 4 * kPer;
+  const int kt = k / kTile, kk = k % kTile;
+  const int lane = (r & 15) + 16 * (kk / kPer), j = kk % kPer;
+  return (((long long)(r >> 4) * KT + kt) * (kPer / 4) + j / 4) * 256 + lane * 4 + (j & 3);
 }
 
 // RoPE angle for pair index i of a head of width d at position pos, computed in fp64.

@@ -28,11 +28,11 @@ enum Epi : int {
   EPI_ARGMAX = 5,    // LM head: per-row (value, index) maximum merged with atomicMax
 };
 
-// How A rows are read.
-enum AMode : int {
-  A_PLAIN = 0,       // A[m][k]
-  A_NORM = 1,        // x[m][k] * gamma[k]; the row's RMS scale is applied in the epilogue
-  A_NORM_DRAFT = 2,  // as A_NORM over the draft rows: row m reads x row (m/15)*16 + m%15 + 1
+// Where the activations (A) come from.
+enum AKind : int {
+  A_SWZ = 0,       // fp32 in the fragment layout (every activation the drafter produces)
+  A_ROW_F32 = 1,   // fp32 row-major [M][lda] (hidden rows handed in by a caller)
+  A_ROW_BF16 = 2,  // bf16 row-major [M][lda] (target features of the fusion GEMM)
 };
 
 struct GemmParams {
@@ -43,11 +43,12 @@ struct GemmParams {
   int KT;                   // k-tiles per n-tile row of the packed matrix
   long long nt_stride;      // tiles between consecutive n-tiles (KT for the n-tile-major packing)
   long long kt_stride;      // tiles between consecutive k-tiles (1 for the n-tile-major packing)
-  const void* A;            // activations: fp32 rows, or bf16 target features
-  int lda;
+  const void* A;            // activations (AKind)
+  int lda;                  // row stride of the row-major kinds
   int M;                    // valid rows
-  int a_mode;
-  const float* gamma;       // A_NORM*: RMSNorm gain [K]
+  int a_kind;               // AKind
+  int norm;                 // 1: RMSNorm of the A rows folded in (gain `gamma`)
+  const float* gamma;       // RMSNorm gain [K]
   float eps;
   int n_tiles;              // n-tiles computed per grid.z slice
   int ksub;                 // waves splitting the k range of one tile group
@@ -56,13 +57,13 @@ struct GemmParams {
   int n_mblocks;            // grid.y
 
   // Epilogue operands
-  void* out;                // EPI_STORE: [M][ldo] fp32 c; EPI_RESIDUAL: fp32 x;
-                            // EPI_SWIGLU: [M][ldo] fp32 h
+  void* out;                // EPI_STORE: c, EPI_RESIDUAL: x, EPI_SWIGLU: h; all fp32 in
+                            // the fragment layout with ldo columns
   int ldo;
   // EPI_QKV
   float* q_out;             // [M][n_q][d]
-  float* bk_out;            // [M][n_kv][d]
-  float* bv_out;            // [M][n_kv][d]
+  float* bk_out;            // [batch][n_kv][16 slots][d]
+  float* bv_out;            // [batch][n_kv][d][16 slots] (transposed)
   const int* ctx_lens;      // [batch]; slot j of request b sits at ctx_lens[b] + j
   int n_q, n_kv, head_dim;
   double log_theta;
@@ -76,16 +77,19 @@ struct GemmParams {
   const int* pos;
   // EPI_ARGMAX
   unsigned long long* keys; // [M] (value, index) keys, stride 16 words; zero before the launch
-  float* logits_out;        // [M][ldo] or null
+  float* logits_out;        // [rows][ldo] or null
+  int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
 };
 
-// dtype_bf16: weight type; a_bf16: activation type of A (bf16 only for the fusion GEMM over
-// the target features; otherwise fp32); npw: n-tiles per wave (1, 2 or 4).
-hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int npw, int epi,
-                       const GemmParams& p, int layers, hipStream_t stream);
+// dtype_bf16: weight type; npw: n-tiles per wave (1, 2 or 4); the A kind and RMSNorm come
+// from p.a_kind / p.norm.
+hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
+                       int layers, hipStream_t stream);
 
-// ids[m] = index encoded in keys[m * 16]; keys reset to zero for the next launch.
-hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows,
+// ids = indices encoded in keys[m * 16] for m < rows; with draft_rows the rows are 16-slot
+// blocks and only slots 1..15 produce ids (block b, slot j -> ids[b*15 + j-1]).  Keys are
+// reset to zero for the next launch.
+hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows, int draft_rows,
                                   hipStream_t stream);
 
 }  // namespace dflash

@@ -5,12 +5,14 @@
 // weights from HBM at full bandwidth and feed each 16-byte lane chunk straight into a 16x16
 // MFMA step.  Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory
 // and enter a bf16 MFMA as a sum of bf16 pieces (see AFrag), except the bf16 target
-// features of the fusion GEMM.
+// features of the fusion GEMM.  Activations the drafter produces itself live in the
+// fragment layout (swz_off), so a wave's A operand for one k-tile is a couple of fully
+// coalesced 1 KB reads; the epilogues write their outputs in that layout for the next GEMM.
 //
 // Work split.  A wave owns NPW consecutive n-tiles (16 output columns each) and a slice of
 // the k range; the `ksub` waves of a tile group cover the whole k range and are reduced
 // through LDS in wave order, so a workgroup produces complete outputs and no workgroup
-// ever waits on another.  RMSNorm of the input is folded in: with A_NORM the kernel reads
+// ever waits on another.  RMSNorm of the input is folded in: with p.norm the kernel reads
 // x * gamma, accumulates the row's sum of squares from the same loads, and scales the
 // finished row by 1/sqrt(mean + eps) before the epilogue.
 #include <type_traits>
@@ -60,12 +62,14 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
   const int nthr = blockDim.x;
   const float* tl = sm.tile;
 
+  constexpr int kPer = Elem<T>::kPerLane;
+  const int kto = p.ldo / (4 * kPer);   // k-tiles of the output as the next GEMM's A
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESIDUAL) {
     for (int idx = tid; idx < rows * cols; idx += nthr) {
       const int r = idx / cols, c = idx % cols;
       const int m = m0 + r;
       if (m >= p.M) continue;
-      float* o = reinterpret_cast<float*>(p.out) + (long long)m * p.ldo + tile0 * 16 + c;
+      float* o = reinterpret_cast<float*>(p.out) + swz_off(m, tile0 * 16 + c, kto, kPer);
       if constexpr (EPI == EPI_STORE) *o = tl[r * ld + c];
       else *o = *o + tl[r * ld + c];
     }
@@ -78,7 +82,7 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
       if (m >= p.M) continue;
       const float gate = tl[r * ld + jt * 16 + c];
       const float up = tl[r * ld + jt * 16 + 8 + c];
-      reinterpret_cast<float*>(p.out)[(long long)m * p.ldo + (tile0 + jt) * 8 + c] =
+      reinterpret_cast<float*>(p.out)[swz_off(m, (tile0 + jt) * 8 + c, kto, kPer)] =
           silu(gate) * up;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
@@ -114,22 +118,36 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
         d1 = d0 + 1;
       }
       if constexpr (EPI == EPI_QKV) {
-        float* dst;
-        if (head < p.n_q) dst = p.q_out + ((long long)m * p.n_q + head) * d;
-        else if (head < p.n_q + p.n_kv) dst = p.bk_out + ((long long)m * p.n_kv + head - p.n_q) * d;
-        else dst = p.bv_out + ((long long)m * p.n_kv + head - p.n_q - p.n_kv) * d;
-        dst[d0] = a0;
-        dst[d1] = a1;
+        const int b = m / kBlock, slot = m % kBlock;
+        if (head < p.n_q) {
+          float* dst = p.q_out + ((long long)m * p.n_q + head) * d;
+          dst[d0] = a0;
+          dst[d1] = a1;
+        } else if (head < p.n_q + p.n_kv) {
+          float* dst = p.bk_out + (((long long)b * p.n_kv + head - p.n_q) * kBlock + slot) * d;
+          dst[d0] = a0;
+          dst[d1] = a1;
+        } else {
+          float* dst = p.bv_out + ((long long)b * p.n_kv + head - p.n_q - p.n_kv) * d * kBlock;
+          dst[d0 * kBlock + slot] = a0;
+          dst[d1 * kBlock + slot] = a1;
+        }
       } else {
         const int seq = p.seq_idx[m];
         const int page = p.block_table[(long long)seq * p.max_pages + position / kPage];
         const int slot = position % kPage;
         const int h = rope ? head : head - p.n_kv;
-        T* pool = reinterpret_cast<T*>(rope ? p.k_pool : p.v_pool);
-        T* dst = pool + (long long)z * p.pool_layer_elems +
-                 (((long long)page * p.n_kv + h) * kPage + slot) * d;
-        dst[d0] = Elem<T>::from_f(a0);
-        dst[d1] = Elem<T>::from_f(a1);
+        if (rope) {   // K page: [16 slots][d]
+          T* dst = reinterpret_cast<T*>(p.k_pool) + (long long)z * p.pool_layer_elems +
+                   (((long long)page * p.n_kv + h) * kPage + slot) * d;
+          dst[d0] = Elem<T>::from_f(a0);
+          dst[d1] = Elem<T>::from_f(a1);
+        } else {      // V page, transposed: [d][16 slots]
+          T* dst = reinterpret_cast<T*>(p.v_pool) + (long long)z * p.pool_layer_elems +
+                   ((long long)page * p.n_kv + h) * d * kPage + slot;
+          dst[d0 * kPage] = Elem<T>::from_f(a0);
+          dst[d1 * kPage] = Elem<T>::from_f(a1);
+        }
       }
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
@@ -137,7 +155,9 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
       for (int idx = tid; idx < rows * cols; idx += nthr) {
         const int r = idx / cols, c = idx % cols;
         const int m = m0 + r;
-        if (m < p.M) p.logits_out[(long long)m * p.ldo + tile0 * 16 + c] = tl[r * ld + c];
+        if (m >= p.M || (p.draft_rows && m % kBlock == 0)) continue;
+        const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
+        p.logits_out[orow * p.ldo + tile0 * 16 + c] = tl[r * ld + c];
       }
     }
     // One wave per row: lanes scan columns, then a wave-wide (value, index) maximum.
@@ -163,10 +183,11 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
 // ------------------------------------------------------------------------------------------
 // Main kernel
 // ------------------------------------------------------------------------------------------
-template <typename T, typename AT, int MT, int NPW, int EPI, bool NORM>
+template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
   __shared__ GemmSmem sm;
   constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
+  typedef typename std::conditional<AK == A_ROW_BF16, bf16, float>::type AT;
   typedef AFrag<T, AT, kTerms> Frag;
   constexpr int kPer = Elem<T>::kPerLane;
   // k-tiles whose loads are issued together; bounded by the 128 VGPRs a 1024-thread
@@ -194,16 +215,21 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
             (long long)(p.nt0 + tile0 + t) * p.nt_stride * kTileBytes + lane * 16;
   const long long kbytes = p.kt_stride * kTileBytes;
 
+  // A pointers per m-tile.  Row-major kinds: this lane's row and k-slice; fragment layout:
+  // this lane's 16 bytes of k-tile 0 (k-tiles are kPer/4 KB apart).
+  constexpr int kGroups = kPer / 4;
   const AT* A = reinterpret_cast<const AT*>(p.A);
   const AT* arow[MT];
   bool aval[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = mblock * MT * 16 + mt * 16 + (lane & 15);
+    const int mtile = mblock * MT + mt;
+    const int r = mtile * 16 + (lane & 15);
     aval[mt] = r < p.M;
-    int src = aval[mt] ? r : 0;
-    if (p.a_mode == A_NORM_DRAFT) src = (src / kDrafts) * kBlock + src % kDrafts + 1;
-    arow[mt] = A + (long long)src * p.lda + (lane >> 4) * kPer;
+    if constexpr (AK == A_SWZ)
+      arow[mt] = A + (long long)mtile * p.KT * kGroups * 256 + lane * 4;
+    else
+      arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * kPer;
   }
   const float* gptr = NORM ? p.gamma + (lane >> 4) * kPer : nullptr;
 
@@ -245,9 +271,23 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          load_a_raw<T, AT>(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile,
-                            kt + u * kstep < ke && aval[mt], f[u][mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          const bool v = kt + u * kstep < ke && aval[mt];
+          if constexpr (AK == A_SWZ) {
+#pragma unroll
+            for (int gq = 0; gq < kGroups; ++gq) {
+              const f32x4 a4 =
+                  v ? *reinterpret_cast<const f32x4*>(
+                          arow[mt] + ((long long)(kt + u * kstep) * kGroups + gq) * 256)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) f[u][mt][4 * gq + i] = a4[i];
+            }
+          } else {
+            load_a_raw<T, AT>(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile, v,
+                              f[u][mt]);
+          }
+        }
       float g[NORM ? U : 1][kPer];
       if constexpr (NORM) {
 #pragma unroll
@@ -332,56 +372,43 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
 // ------------------------------------------------------------------------------------------
 // Launch
 // ------------------------------------------------------------------------------------------
-template <typename T, typename AT, int MT, int NPW, int EPI, bool NORM>
+template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 static hipError_t go(const GemmParams& p, int layers, hipStream_t stream) {
   dim3 grid(p.n_tiles / (p.tgpw * NPW), p.n_mblocks, layers);
   dim3 block(kWave * p.ksub * p.tgpw);
-  gemm_stream<T, AT, MT, NPW, EPI, NORM><<<grid, block, 0, stream>>>(p);
+  gemm_stream<T, AK, MT, NPW, EPI, NORM><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
 }
 
+template <typename T, int AK, int MT, int EPI, bool NORM>
+static hipError_t by_npw(int npw, const GemmParams& p, int layers, hipStream_t stream) {
+  if (npw == 1) return go<T, AK, MT, 1, EPI, NORM>(p, layers, stream);
+  if (npw == 2) return go<T, AK, MT, 2, EPI, NORM>(p, layers, stream);
+  if (npw == 4) return go<T, AK, MT, 4, EPI, NORM>(p, layers, stream);
+  return hipErrorInvalidValue;
+}
+
+// The instantiated (A kind, epilogue, norm) combinations are the ones the drafter uses.
 template <typename T, int MT>
-static hipError_t launch_mt(int a_bf16, int npw, int epi, const GemmParams& p, int layers,
+static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
                             hipStream_t stream) {
-  const bool norm = p.a_mode != A_PLAIN;
-  if (a_bf16) {
-    if constexpr (sizeof(T) == 2) {
-      if (epi == EPI_STORE && !norm) {
-        if (npw == 1) return go<T, bf16, MT, 1, EPI_STORE, false>(p, layers, stream);
-        if (npw == 2) return go<T, bf16, MT, 2, EPI_STORE, false>(p, layers, stream);
-        if (npw == 4) return go<T, bf16, MT, 4, EPI_STORE, false>(p, layers, stream);
+  const bool norm = p.norm != 0;
+  switch (p.a_kind) {
+    case A_SWZ:
+      if (epi == EPI_RESIDUAL && !norm) return by_npw<T, A_SWZ, MT, EPI_RESIDUAL, false>(npw, p, layers, stream);
+      if (epi == EPI_INJECT && !norm) return by_npw<T, A_SWZ, MT, EPI_INJECT, false>(npw, p, layers, stream);
+      if (epi == EPI_QKV && norm) return by_npw<T, A_SWZ, MT, EPI_QKV, true>(npw, p, layers, stream);
+      if (epi == EPI_SWIGLU && norm) return by_npw<T, A_SWZ, MT, EPI_SWIGLU, true>(npw, p, layers, stream);
+      if (epi == EPI_ARGMAX && norm) return by_npw<T, A_SWZ, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
+      break;
+    case A_ROW_F32:
+      if (epi == EPI_STORE && !norm) return by_npw<T, A_ROW_F32, MT, EPI_STORE, false>(npw, p, layers, stream);
+      if (epi == EPI_ARGMAX && norm) return by_npw<T, A_ROW_F32, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
+      break;
+    case A_ROW_BF16:
+      if constexpr (sizeof(T) == 2) {
+        if (epi == EPI_STORE && !norm) return by_npw<T, A_ROW_BF16, MT, EPI_STORE, false>(npw, p, layers, stream);
       }
-    }
-    return hipErrorInvalidValue;
-  }
-  auto by_npw = [&](auto epi_c, auto norm_c) -> hipError_t {
-    constexpr int E = decltype(epi_c)::value;
-    constexpr bool N = decltype(norm_c)::value;
-    if (npw == 1) return go<T, float, MT, 1, E, N>(p, layers, stream);
-    if (npw == 2) return go<T, float, MT, 2, E, N>(p, layers, stream);
-    if (npw == 4) return go<T, float, MT, 4, E, N>(p, layers, stream);
-    return hipErrorInvalidValue;
-  };
-  using F = std::false_type;
-  using Tr = std::true_type;
-  switch (epi) {
-    case EPI_STORE:
-      if (!norm) return by_npw(std::integral_constant<int, EPI_STORE>{}, F{});
-      break;
-    case EPI_RESIDUAL:
-      if (!norm) return by_npw(std::integral_constant<int, EPI_RESIDUAL>{}, F{});
-      break;
-    case EPI_INJECT:
-      if (!norm) return by_npw(std::integral_constant<int, EPI_INJECT>{}, F{});
-      break;
-    case EPI_QKV:
-      if (norm) return by_npw(std::integral_constant<int, EPI_QKV>{}, Tr{});
-      break;
-    case EPI_SWIGLU:
-      if (norm) return by_npw(std::integral_constant<int, EPI_SWIGLU>{}, Tr{});
-      break;
-    case EPI_ARGMAX:
-      if (norm) return by_npw(std::integral_constant<int, EPI_ARGMAX>{}, Tr{});
       break;
     default:
       break;
@@ -389,30 +416,33 @@ static hipError_t launch_mt(int a_bf16, int npw, int epi, const GemmParams& p, i
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int dtype_bf16, int a_bf16, int mt, int npw, int epi,
-                       const GemmParams& p, int layers, hipStream_t stream) {
+hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
+                       int layers, hipStream_t stream) {
   if (dtype_bf16) {
-    if (mt == 1) return launch_mt<bf16, 1>(a_bf16, npw, epi, p, layers, stream);
-    if (mt == 2) return launch_mt<bf16, 2>(a_bf16, npw, epi, p, layers, stream);
-    if (mt == 4) return launch_mt<bf16, 4>(a_bf16, npw, epi, p, layers, stream);
-  } else if (!a_bf16) {
-    if (mt == 1) return launch_mt<float, 1>(0, npw, epi, p, layers, stream);
-    if (mt == 2) return launch_mt<float, 2>(0, npw, epi, p, layers, stream);
-    if (mt == 4) return launch_mt<float, 4>(0, npw, epi, p, layers, stream);
+    if (mt == 1) return launch_mt<bf16, 1>(npw, epi, p, layers, stream);
+    if (mt == 2) return launch_mt<bf16, 2>(npw, epi, p, layers, stream);
+    if (mt == 4) return launch_mt<bf16, 4>(npw, epi, p, layers, stream);
+  } else {
+    if (mt == 1) return launch_mt<float, 1>(npw, epi, p, layers, stream);
+    if (mt == 2) return launch_mt<float, 2>(npw, epi, p, layers, stream);
+    if (mt == 4) return launch_mt<float, 4>(npw, epi, p, layers, stream);
   }
   return hipErrorInvalidValue;
 }
 
-__global__ void argmax_finalize_kernel(unsigned long long* keys, int* ids, int rows) {
+__global__ void argmax_finalize_kernel(unsigned long long* keys, int* ids, int rows,
+                                       int draft_rows) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= rows) return;
-  ids[m] = argmax_key_index(keys[(long long)m * 16]);
+  const int idx = argmax_key_index(keys[(long long)m * 16]);
   keys[(long long)m * 16] = 0ull;
+  if (!draft_rows) ids[m] = idx;
+  else if (m % kBlock != 0) ids[(m / kBlock) * kDrafts + m % kBlock - 1] = idx;
 }
 
-hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows,
+hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows, int draft_rows,
                                   hipStream_t stream) {
-  argmax_finalize_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(keys, ids, rows);
+  argmax_finalize_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(keys, ids, rows, draft_rows);
   return hipGetLastError();
 }
 

@@ -20,31 +20,17 @@ struct PackArgs {
   void* dst;
 };
 
-struct EmbedNormArgs {
-  const int* anchor_ids;
+struct EmbedArgs {
+  const int* anchor_ids;  // [batch]
   int mask_id;
-  const void* embed;
+  const void* embed;      // [vocab][hidden] model dtype
   int hidden;
-  float* x;             // [rows][hidden] fp32 residual
-  float* u;             // [rows][hidden] fp32 normed activations, or null (x only)
-  const float* gain;
-  float eps;
-};
-
-struct NormArgs {
-  const float* x;
-  float* u;
-  const float* gain;
-  int hidden;
-  float eps;
-  int drop_slot0;
+  float* x;               // residual stream, fp32 fragment layout (rows = batch * 16)
 };
 
 hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream);
 hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream);
-hipError_t launch_embed_norm(int bf16_dtype, const EmbedNormArgs& a, int rows,
-                             hipStream_t stream);
-hipError_t launch_rmsnorm(int bf16_dtype, const NormArgs& a, int rows, hipStream_t stream);
+hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream);
 hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
                                 int* bonus, int* emitted, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

@@ -77,79 +77,28 @@ hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipS
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------------------------
-// Block embedding (+ optionally the first RMSNorm).  Row m = b*16 + j: token = anchor[b] for
-// j == 0, else the mask id.  x (fp32 residual) = E[token]; if u is set, u = RMSNorm(x) * gain.
-// One workgroup per row.
-// ------------------------------------------------------------------------------------------
+// Block embedding: row b*16 + j of x is the embedding of the anchor (j = 0) or of the mask
+// token (j >= 1), widened to fp32 and written in the fragment layout (4 columns per store).
 template <typename T>
-__device__ inline float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  __syncthreads();
-  if (l == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-  const int nw = blockDim.x / kWave;
-  for (int i = 0; i < nw; ++i) s += red[i];
-  return s;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void embed_norm_kernel(EmbedNormArgs a) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int m = blockIdx.x;
   const int b = m / kBlock, j = m % kBlock;
   const int tok = j == 0 ? a.anchor_ids[b] : a.mask_id;
   const T* e = reinterpret_cast<const T*>(a.embed) + (long long)tok * a.hidden;
-  float* x = a.x + (long long)m * a.hidden;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) {
-    const float v = Elem<T>::to_f(e[i]);
-    x[i] = v;
-    ss += v * v;
+  constexpr int kPer = Elem<T>::kPerLane;
+  const int KT = a.hidden / (4 * kPer);
+  for (int i = 4 * threadIdx.x; i < a.hidden; i += 4 * blockDim.x) {
+    const f32x4 v = {Elem<T>::to_f(e[i]), Elem<T>::to_f(e[i + 1]), Elem<T>::to_f(e[i + 2]),
+                     Elem<T>::to_f(e[i + 3])};
+    *reinterpret_cast<f32x4*>(a.x + swz_off(m, i, KT, kPer)) = v;
   }
-  if (!a.u) return;
-  ss = block_sum<T>(ss, red);
-  const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-  float* u = a.u + (long long)m * a.hidden;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) u[i] = x[i] * rstd * a.gain[i];
 }
 
-// RMSNorm of fp32 rows (fp32 out).  With `drop_slot0`, source row b*16 + j
-// (j >= 1) lands in destination row b*15 + j - 1 (the LM-head rows).
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
-  __shared__ float red[4];
-  int src_row = blockIdx.x;
-  int dst_row = blockIdx.x;
-  if (a.drop_slot0) {
-    const int b = blockIdx.x / kDrafts, j = blockIdx.x % kDrafts + 1;
-    src_row = b * kBlock + j;
-  }
-  const float* x = a.x + (long long)src_row * a.hidden;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) ss += x[i] * x[i];
-  ss = block_sum<T>(ss, red);
-  const float rstd = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-  float* u = a.u + (long long)dst_row * a.hidden;
-  for (int i = threadIdx.x; i < a.hidden; i += blockDim.x) u[i] = x[i] * rstd * a.gain[i];
-}
-
-hipError_t launch_embed_norm(int bf16_dtype, const EmbedNormArgs& a, int rows,
-                             hipStream_t stream) {
+hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream) {
   if (bf16_dtype)
-    embed_norm_kernel<bf16><<<rows, 256, 0, stream>>>(a);
+    embed_kernel<bf16><<<rows, 256, 0, stream>>>(a);
   else
-    embed_norm_kernel<float><<<rows, 256, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_rmsnorm(int bf16_dtype, const NormArgs& a, int rows, hipStream_t stream) {
-  if (bf16_dtype)
-    rmsnorm_kernel<bf16><<<rows, 256, 0, stream>>>(a);
-  else
-    rmsnorm_kernel<float><<<rows, 256, 0, stream>>>(a);
+    embed_kernel<float><<<rows, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -66,8 +66,9 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Drafter shape.  Requirements checked by every call: block_size == 16,
  * page_size == 16, hidden % 64 == 0, feat_dim % 64 == 0, intermediate % 64 == 0,
- * vocab % 64 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
- * n_q_heads / n_kv_heads * 16 <= 128. */
+ * vocab % 64 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0, and a query-head
+ * group G = n_q_heads / n_kv_heads in {1, 2, 4, 8} for bf16 (in {2, 4, 8}, and not 8 with
+ * head_dim 128, for fp32). */
 typedef struct {
   int32_t n_layers;
   int32_t hidden;         /* H */
@@ -107,8 +108,11 @@ typedef struct {
 } dflash_weights;
 
 /* Paged KV cache of the draft layers (injected context only; block K/V are never
- * stored).  Pools are [n_layers][num_pages][n_kv_heads][page_size][head_dim] in the model
- * dtype; one physical page id addresses the same page in every layer.
+ * stored).  In the model dtype, one physical page id addressing the same page in every
+ * layer:
+ *   k_pool [n_layers][num_pages][n_kv_heads][page_size][head_dim]  (a page is row-major)
+ *   v_pool [n_layers][num_pages][n_kv_heads][head_dim][page_size]  (a page is transposed,
+ *          so the attention kernel reads 4 consecutive positions of one dim at once).
  * block_table [batch][max_pages_per_seq] maps logical page p of request b to a physical
  * page; ctx_lens [batch] is T_b, the number of context positions already injected. */
 typedef struct {

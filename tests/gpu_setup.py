@@ -58,10 +58,15 @@ def inject_rows(s: Setup, feats_per_req, pos_per_req) -> None:
 
 def gather_pool(s: Setup, b: int, T: int, which: str = "k") -> np.ndarray:
     """Cached K or V of request b, positions 0..T-1, as [L, T, n_kv, d] float64 (host)."""
-    pool = (s.cache.k_pool if which == "k" else s.cache.v_pool).float().cpu().numpy()
     t = np.arange(T)
     pages = s.table[b, t // s.cfg.page_size]
-    return pool[:, pages, :, t % s.cfg.page_size, :].transpose(1, 0, 2, 3).astype(np.float64)
+    if which == "k":   # [L, pages, n_kv, 16, d]
+        pool = s.cache.k_pool.float().cpu().numpy()
+        g = pool[:, pages, :, t % s.cfg.page_size, :]
+    else:              # [L, pages, n_kv, d, 16]
+        pool = s.cache.v_pool.float().cpu().numpy()
+        g = pool[:, pages, :, :, t % s.cfg.page_size]
+    return g.transpose(1, 0, 2, 3).astype(np.float64)
 
 
 def oracle_context(s: Setup, b: int):
