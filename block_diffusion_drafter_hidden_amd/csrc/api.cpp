@@ -25,7 +25,7 @@ constexpr size_t kKeyBytes = 768 * 1024;               // 6144 argmax rows
 constexpr size_t kSyncBytes = kCounterBytes + kKeyBytes;
 constexpr int kMaxCounters = (int)(kCounterBytes / 4) - 1;  // last one: argmax done counter
 constexpr int kMaxArgmaxRows = (int)(kKeyBytes / kKeyStride);
-constexpr int kTargetWaves = 4096;
+constexpr int kTargetWaves = 2048;
 constexpr int kAttnTargetWGs = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -116,6 +116,8 @@ Packed packed_layout(const Dims& m) {
 // ---------------------------------------------------------------------------------------
 // GEMM planning.  Waves split the k range of a tile group (ksub), a workgroup holds tgpw tile
 // groups; the plan aims at >= kTargetWaves waves in flight with >= 8 k-tiles per wave.
+// (Sweeps over the batch-1 shapes on MI355X put the best plans at 2048-4096 waves of 8-16
+// k-tiles each; the LM head prefers 2 waves per k range and 2 tile groups of 4 n-tiles.)
 // ---------------------------------------------------------------------------------------
 struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
@@ -175,8 +177,8 @@ struct Carver {
 // Per-call plans of the draft and inject steps.
 // ---------------------------------------------------------------------------------------
 struct DraftPlan {
-  Plan qkv, o, gu, dn, lm;
-  int nc, chunk;
+  Plan qkv, o, gu, dn;
+  int nc;
   size_t x, q, bk, bv, ao, h, apart_o, apart_ml;
   size_t total;
 };
@@ -184,15 +186,13 @@ struct DraftPlan {
 DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   DraftPlan p{};
   const int rows = B * 16;
-  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 1, 1);
+  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 2, 1);
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1);
-  p.lm = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   p.nc = std::max(1, std::min({cdiv(kAttnTargetWGs, kv_groups), max_chunks, kAttnMaxChunks}));
-  p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
   p.q = c.take((size_t)rows * m.nq * m.d * 4);
@@ -201,8 +201,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.ao = c.take((size_t)rows * m.nq * m.d * 4);
   p.h = c.take((size_t)rows * m.I * 4);
   const size_t R = (size_t)m.G * 16;
-  p.apart_o = c.take((size_t)kv_groups * (p.nc + 1) * R * m.d * 4);
-  p.apart_ml = c.take((size_t)kv_groups * (p.nc + 1) * R * 2 * 4);
+  p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
+  p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
   p.total = c.off;
   return p;
 }
@@ -230,16 +230,19 @@ constexpr int kInjectChunkRows = 256;
     if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
   } while (0)
 
-// Final RMSNorm + shared LM head + argmax over the vocabulary.  With draft_rows, `x` is the
-// residual stream in the fragment layout (rows = 16-slot blocks; slot 0 is computed and
-// dropped); otherwise fp32 row-major hidden rows.
+// Final RMSNorm + shared LM head + argmax over the vocabulary.  `x` is fp32 in the fragment
+// layout; with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* x,
                              int rows, bool draft_rows, int* ids_out, float* logits_out,
                              char* ws, hipStream_t stream) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
-  const Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
+  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
+  if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
+    pl.ksub = 2;
+    pl.tgpw = 2;
+  }
   GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, x, m.H, rows, m.V / 16);
-  g.a_kind = draft_rows ? A_SWZ : A_ROW_F32;
+  g.a_kind = A_SWZ;
   g.norm = 1;
   g.gamma = reinterpret_cast<const float*>(wb + P.final_norm);
   g.eps = m.eps;
@@ -491,7 +494,6 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.n_kv = m.nkv;
       a.head_dim = m.d;
       a.nc = dp.nc;
-      a.chunk = dp.chunk;
       a.scale = 1.0f / std::sqrt((float)m.d);
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
@@ -535,10 +537,15 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   if (st != DFLASH_OK) return st;
   if (!packed || !hidden || !ids_out || !workspace || rows <= 0) return DFLASH_ERR_INVALID_ARG;
   if (rows > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
-  if (ws_bytes < kSyncBytes) return DFLASH_ERR_WORKSPACE;
-  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), hidden,
-                        rows, false, ids_out, logits_out, reinterpret_cast<char*>(workspace),
-                        stream);
+  // The rows are first rewritten into the fragment layout, in the area a draft step keeps
+  // its residual stream, so the LM head runs exactly the draft step's kernel.
+  const size_t frag_bytes = (size_t)cdiv(rows, 16) * 16 * m.H * 4;
+  if (ws_bytes < kSyncBytes + frag_bytes) return DFLASH_ERR_WORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* xs = reinterpret_cast<float*>(ws + kSyncBytes);
+  DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16 ? 8 : 4, xs, stream));
+  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), xs, rows,
+                        false, ids_out, logits_out, ws, stream);
 }
 
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,

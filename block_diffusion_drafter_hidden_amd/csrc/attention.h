@@ -17,11 +17,10 @@ struct AttnArgs {
   int max_pages;
   const int* ctx_lens;     // [B]
   int n_q, n_kv, head_dim;
-  int nc;                  // context chunks per request
-  int chunk;               // context keys per chunk
+  int nc;                  // context chunks per request (each T_b / nc keys, rounded to 32)
   float scale;             // 1 / sqrt(d)
-  float* part_o;           // [B][n_kv][nc+1][G][d/16][4][16 rows][4]
-  float* part_ml;          // [B][n_kv][nc+1][G][16 rows][2]
+  float* part_o;           // [B][n_kv][nc][G][d/16][4][16 rows][4]
+  float* part_ml;          // [B][n_kv][nc][G][16 rows][2]
   float* out;              // [B*16][n_q*d] fp32 in the fragment layout (swz_off)
   int out_kper;            // fragment layout parameter of the consumer GEMM (8 bf16, 4 fp32)
 };

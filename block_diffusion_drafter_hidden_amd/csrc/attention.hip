@@ -2,12 +2,13 @@
 // group attend, without a mask, to the request's injected context (paged KV cache) and to
 // the 16 block keys.
 //
-// Pass 1 (partials), grid (nc + 1, n_kv, batch): workgroup c < nc covers context keys
-// [c*chunk, min((c+1)*chunk, T_b)); workgroup nc covers the 16 block keys.  One wave per
-// query head of the KV group.  Each wave keeps an online softmax (running max m, sum l,
-// unnormalized output o) and writes (m, l, o).
-// Pass 2 (merge), grid (n_q, batch): rescales the nc + 1 partials of each head to a common
-// maximum and divides by the total sum, chunks in order, so results do not depend on
+// Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
+// [c*chunk_b, min((c+1)*chunk_b, T_b)) with chunk_b = T_b / nc rounded up to 32 keys, and
+// the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
+// the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
+// online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
+// Pass 2 (merge), grid (n_q, d / 32, batch): rescales the nc partials of each head to a
+// common maximum and divides by the total sum, chunks in order, so results do not depend on
 // scheduling.
 //
 // bf16 models run on 16x16x32 bf16 MFMA in transposed form, S^T = K Q^T and
@@ -27,7 +28,7 @@
 //
 // Partial layout: part_o[slot][head_in_group][dt][q][row][i] holds output dim
 // 16*dt + 4*q + i of block row `row` (a float4 per (dt, q, row)); part_ml[slot][head][row]
-// holds (m, l).  slot = (b * n_kv + g) * (nc + 1) + c.
+// holds (m, l).  slot = (b * n_kv + g) * nc + c.
 #include "attention.h"
 #include "common.h"
 
@@ -40,6 +41,10 @@ __device__ inline long long part_o_index(long long slot, int G, int hh, int D, i
   return ((((slot * G + hh) * (D / 16) + dim / 16) * 4 + (dim % 16) / 4) * kBlock + row) * 4 +
          dim % 4;
 }
+
+// Context keys per chunk for a request with T cached positions: T split over nc chunks,
+// rounded up to whole 32-key steps (chunks start on page boundaries).
+__device__ inline int context_chunk(int T, int nc) { return ((T + nc - 1) / nc + 31) / 32 * 32; }
 
 __device__ inline void split2(float v, bf16& hi, bf16& lo) {
   hi = (bf16)v;
@@ -91,15 +96,28 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
   const int n = lane & 15, q = lane >> 4;
   const int nq = a.n_q, nkv = a.n_kv;
   const int T_b = a.ctx_lens[b];
-  const bool is_block = c == a.nc;
-  int kbeg, kend;
-  if (is_block) {
-    kbeg = 0;
-    kend = kBlock;
-  } else {
-    kbeg = (int)min((long long)c * a.chunk, (long long)T_b);
-    kend = min(kbeg + a.chunk, T_b);
-  }
+  const bool has_block = c == a.nc - 1;
+  const int chunk = context_chunk(T_b, a.nc);
+  const int kbeg = min(c * chunk, T_b);
+  const int kend = min(kbeg + chunk, T_b);
+
+  // Block keys/values of the last chunk's workgroup, fp32 [b][g][16][d] keys and
+  // [b][g][d][16] transposed values; loaded up front (so they travel with the first loads)
+  // unless the workgroup is too large to keep them in registers.
+  constexpr bool kEarlyBlock = G * kWave <= 256;
+  f32x4 bkr[KS][2], bvr[DT];
+  auto load_block = [&]() {
+    const float* kb = a.bk + ((long long)(b * nkv + g) * kBlock + n) * D + q * 8;
+    const float* vb = a.bv + ((long long)(b * nkv + g) * D + n) * kBlock + q * 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bkr[ks][0] = *reinterpret_cast<const f32x4*>(kb + ks * 32);
+      bkr[ks][1] = *reinterpret_cast<const f32x4*>(kb + ks * 32 + 4);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) bvr[dt] = *reinterpret_cast<const f32x4*>(vb + dt * 16 * kBlock);
+  };
+  if (kEarlyBlock && has_block) load_block();
 
   // Q^T fragments (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8,
   // scaled by 1/sqrt(d) and split hi/lo.
@@ -153,35 +171,7 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
     split8(pv, p_hi, p_lo);
   };
 
-  if (is_block) {
-    // Block keys/values: fp32 [b][g][16][d] keys and [b][g][d][16] transposed values.
-    const float* kb = a.bk + ((long long)(b * nkv + g) * kBlock + n) * D + q * 8;
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(kb + ks * 32);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(kb + ks * 32 + 4);
-      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      i32x4 kh, kl;
-      split8(f, kh, kl);
-      s[0] = mfma_tile<bf16>(kh, qf[ks][0], s[0]);
-      s[0] = mfma_tile<bf16>(kh, qf[ks][1], s[0]);
-      s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
-    }
-    i32x4 ph, pl;
-    softmax_step(s, kBlock, ph, pl);
-    const float* vb = a.bv + ((long long)(b * nkv + g) * D + n) * kBlock + q * 4;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(vb + dt * 16 * kBlock);
-      const float f[8] = {v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f};
-      i32x4 vh, vl;
-      split8(f, vh, vl);
-      o[dt] = mfma_tile<bf16>(vh, ph, o[dt]);
-      o[dt] = mfma_tile<bf16>(vh, pl, o[dt]);
-      o[dt] = mfma_tile<bf16>(vl, ph, o[dt]);
-    }
-  } else if (kend > kbeg) {
+  if (kend > kbeg) {
     const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
     const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
     const int* table = a.block_table + (long long)b * a.max_pages;
@@ -251,8 +241,34 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
     }
   }
 
+  if (has_block) {   // the 16 block keys, hi + lo on both operands
+    if (!kEarlyBlock) load_block();
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float f[8] = {bkr[ks][0][0], bkr[ks][0][1], bkr[ks][0][2], bkr[ks][0][3],
+                          bkr[ks][1][0], bkr[ks][1][1], bkr[ks][1][2], bkr[ks][1][3]};
+      i32x4 kh, kl;
+      split8(f, kh, kl);
+      s[0] = mfma_tile<bf16>(kh, qf[ks][0], s[0]);
+      s[0] = mfma_tile<bf16>(kh, qf[ks][1], s[0]);
+      s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
+    }
+    i32x4 ph, pl;
+    softmax_step(s, kBlock, ph, pl);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float f[8] = {bvr[dt][0], bvr[dt][1], bvr[dt][2], bvr[dt][3], 0.f, 0.f, 0.f, 0.f};
+      i32x4 vh, vl;
+      split8(f, vh, vl);
+      o[dt] = mfma_tile<bf16>(vh, ph, o[dt]);
+      o[dt] = mfma_tile<bf16>(vh, pl, o[dt]);
+      o[dt] = mfma_tile<bf16>(vl, ph, o[dt]);
+    }
+  }
+
   // Partial of this chunk.  O^T layout: lane holds dims 16dt + 4q + i of block row n.
-  const long long slot = ((long long)b * nkv + g) * (a.nc + 1) + c;
+  const long long slot = ((long long)b * nkv + g) * a.nc + c;
   f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kBlock);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kBlock + n] = o[dt];
@@ -286,15 +302,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   const int tid = threadIdx.x;
   const int nq = a.n_q, nkv = a.n_kv;
   const int T_b = a.ctx_lens[b];
-  const bool is_block = c == a.nc;
-  int kbeg, kend;
-  if (is_block) {
-    kbeg = 0;
-    kend = kBlock;
-  } else {
-    kbeg = (int)min((long long)c * a.chunk, (long long)T_b);
-    kend = min(kbeg + a.chunk, T_b);
-  }
+  const bool has_block = c == a.nc - 1;
+  const int chunk = context_chunk(T_b, a.nc);
+  const int kbeg = min(c * chunk, T_b);
+  const int kend = min(kbeg + chunk, T_b);
   for (int idx = tid; idx < R * D; idx += kThreads) {
     const int r = idx / D, i = idx % D;
     const int hh = r / kBlock, j = r % kBlock;
@@ -311,8 +322,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 
   const float* kpool = reinterpret_cast<const float*>(a.k_pool);
   const float* vpool = reinterpret_cast<const float*>(a.v_pool);
-  for (int k0 = kbeg; k0 < kend; k0 += kKeys) {
-    const int nk = min(kKeys, kend - k0);
+  // Context steps of 32 keys, then (last workgroup) one step over the 16 block keys.
+  const int n_ctx_steps = (kend - kbeg + kKeys - 1) / kKeys;
+  for (int st = 0; st < n_ctx_steps + (has_block ? 1 : 0); ++st) {
+    const bool is_block = st == n_ctx_steps;
+    const int k0 = is_block ? 0 : kbeg + st * kKeys;
+    const int nk = is_block ? kBlock : min(kKeys, kend - k0);
     for (int idx = tid; idx < kKeys * D; idx += kThreads) {
       const int kk = idx / D, i = idx % D;
       float kv = 0.f, vv = 0.f;
@@ -373,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
     }
     __syncthreads();
   }
-  const long long slot = ((long long)b * nkv + g) * (a.nc + 1) + c;
+  const long long slot = ((long long)b * nkv + g) * a.nc + c;
   const int i = tid % D, r0 = tid / D;
 #pragma unroll
   for (int n = 0; n < NRO; ++n) {
@@ -387,29 +402,32 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Merge: one workgroup per (query head, request), one thread per float4 of the head's
-// 16 x d output, written in the fragment layout the output projection reads.  The partial outputs of the first chunks are loaded before the (m, l)
-// pass so both travel in one round trip; the per-row maximum and sum come from 16 rows x
-// (threads / 16) chunk lanes through LDS; the weighted sum runs over chunks in order.
+// Merge: one workgroup per (query head, 32-dim slice, request), one thread per float4 of the
+// slice (16 rows x 32 dims).  The slice's partials of the first kMergeBatch chunks are loaded
+// before the (m, l) pass so both travel in one round trip; the per-row maximum and sum come
+// from 16 rows x 8 chunk lanes through LDS; the weighted sum runs over chunks in order.  The
+// result is written in the fragment layout the output projection reads.
 // ------------------------------------------------------------------------------------------
-constexpr int kMergeBatch = 16;
+constexpr int kMergeBatch = 40;
+constexpr int kMergeThreads = 128;   // float4s of a 16 x 32 slice
 
 template <int D>
-__global__ __launch_bounds__(D * 4) void attn_merge(AttnArgs a) {
-  constexpr int NT = D * 4;                 // threads = float4 positions of 16 x D
-  constexpr int NCL = NT / kBlock;          // chunk lanes per row
+__global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
+  constexpr int NCL = kMergeThreads / kBlock;   // chunk lanes per row
+  constexpr int NT = D * 4;                     // float4s of one head's 16 x D partial
   __shared__ float w_s[kAttnMaxChunks + 1][kBlock];
   __shared__ float m_s[kAttnMaxChunks + 1][kBlock];
   __shared__ float red[NCL][kBlock];
   __shared__ float M_s[kBlock], invL_s[kBlock];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
   const int G = a.n_q / a.n_kv;
   const int g = h / G, hh = h % G;
-  const int nch = a.nc + 1;
+  const int nch = a.nc;
   const long long slot0 = ((long long)b * a.n_kv + g) * nch;
   const int tid = threadIdx.x;
+  const int f = slice * kMergeThreads + tid;     // float4 index (dt, q, row) within the head
   const long long cstride = (long long)G * NT;   // float4s between chunks
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + (slot0 * G + hh) * NT + tid;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + (slot0 * G + hh) * NT + f;
 
   f32x4 v[kMergeBatch];
 #pragma unroll
@@ -452,8 +470,8 @@ __global__ __launch_bounds__(D * 4) void attn_merge(AttnArgs a) {
   }
   __syncthreads();
 
-  // Thread tid holds float4 (dt, q, row) = tid: row tid % 16, dims 16*(tid/64) + 4*((tid/16)%4).
-  const int row = tid % kBlock;
+  // float4 f = (dt, q, row): row f % 16, dims 16*(f/64) + 4*((f/16)%4) .. +3.
+  const int row = f % kBlock;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kMergeBatch; ++c)
@@ -466,7 +484,7 @@ __global__ __launch_bounds__(D * 4) void attn_merge(AttnArgs a) {
     for (int c = 0; c < kMergeBatch; ++c)
       if (c0 + c < nch) acc += w_s[c0 + c][row] * v[c];
   }
-  const int dim = 16 * (tid / (4 * kBlock)) + 4 * ((tid / kBlock) % 4);
+  const int dim = 16 * (f / (4 * kBlock)) + 4 * ((f / kBlock) % 4);
   const int kto = a.n_q * D / (4 * a.out_kper);
   *reinterpret_cast<f32x4*>(a.out + swz_off(b * kBlock + row, h * D + dim, kto, a.out_kper)) =
       acc * invL_s[row];
@@ -488,7 +506,7 @@ static void launch_partial_bf16(int G, dim3 grid, const AttnArgs& a, hipStream_t
 
 static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
                                  hipStream_t stream) {
-  dim3 grid(a.nc + 1, a.n_kv, batch);
+  dim3 grid(a.nc, a.n_kv, batch);
   const int G = a.n_q / a.n_kv;
   if (!block_attention_supported(bf16_dtype, a.head_dim, G)) return hipErrorInvalidValue;
   if (bf16_dtype) {
@@ -510,12 +528,12 @@ static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
                                   hipStream_t stream) {
-  if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk % 32 != 0) return hipErrorInvalidValue;
+  if (a.nc < 1 || a.nc > kAttnMaxChunks) return hipErrorInvalidValue;
   hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
   if (e != hipSuccess) return e;
-  dim3 grid(a.n_q, batch);
-  if (a.head_dim == 128) attn_merge<128><<<grid, 128 * 4, 0, stream>>>(a);
-  else attn_merge<64><<<grid, 64 * 4, 0, stream>>>(a);
+  dim3 grid(a.n_q, a.head_dim / 32, batch);
+  if (a.head_dim == 128) attn_merge<128><<<grid, kMergeThreads, 0, stream>>>(a);
+  else attn_merge<64><<<grid, kMergeThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -52,9 +52,16 @@ __device__ inline void load_a_raw(const AT* p, bool valid, float* f) {
 // ------------------------------------------------------------------------------------------
 // Epilogues on the workgroup's dense fp32 tile: rows MT*16, columns cols (tile-major).
 // ------------------------------------------------------------------------------------------
-template <typename T, int MT, int EPI>
+// Residual values a thread adds in the epilogue, read at kernel start so the epilogue has no
+// dependent global load: iteration i of the epilogue loop uses xpre[i].
+template <int MT, int NPW>
+struct ResidualPrefetch {
+  static constexpr int kN = 4 * NPW * MT <= 8 ? 4 * NPW * MT : 0;   // per thread, ksub = 1 bound
+};
+
+template <typename T, int MT, int EPI, int NPRE>
 __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int tile0, int mblock,
-                             int z) {
+                             int z, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
   const int rows = MT * 16;
   const int ld = cols + 1;
   const int m0 = mblock * rows;
@@ -70,8 +77,14 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
       const int m = m0 + r;
       if (m >= p.M) continue;
       float* o = reinterpret_cast<float*>(p.out) + swz_off(m, tile0 * 16 + c, kto, kPer);
-      if constexpr (EPI == EPI_STORE) *o = tl[r * ld + c];
-      else *o = *o + tl[r * ld + c];
+      if constexpr (EPI == EPI_STORE) {
+        *o = tl[r * ld + c];
+      } else if constexpr (NPRE > 0) {
+        const int i = (idx - tid) / nthr;
+        *o = (i < NPRE ? xpre[i < NPRE ? i : 0] : *o) + tl[r * ld + c];
+      } else {
+        *o = *o + tl[r * ld + c];
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     const int half_cols = cols / 2;
@@ -242,6 +255,22 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) ssq[mt] = 0.f;
 
+  constexpr int NPRE = EPI == EPI_RESIDUAL ? ResidualPrefetch<MT, NPW>::kN : 0;
+  float xpre[NPRE > 0 ? NPRE : 1];
+  if constexpr (NPRE > 0) {
+    const int rows = MT * 16, cols = p.tgpw * NPW * 16;
+    const int kto = p.ldo / (4 * kPer);
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x;
+      const int m = mblock * rows + idx / cols;
+      xpre[i] = idx < rows * cols && m < p.M
+                    ? reinterpret_cast<const float*>(p.out)[swz_off(m, wg_tile0 * 16 + idx % cols,
+                                                                   kto, kPer)]
+                    : 0.f;
+    }
+  }
+
   const i32x4 zero = {0, 0, 0, 0};
   for (int kt = kb; kt < ke; kt += U * kstep) {
     i32x4 b[U][NPW];
@@ -366,7 +395,7 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
         }
   }
   __syncthreads();
-  run_epilogue<T, MT, EPI>(p, sm, cols, wg_tile0, mblock, z);
+  run_epilogue<T, MT, EPI, NPRE>(p, sm, cols, wg_tile0, mblock, z, xpre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -403,7 +432,6 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
       break;
     case A_ROW_F32:
       if (epi == EPI_STORE && !norm) return by_npw<T, A_ROW_F32, MT, EPI_STORE, false>(npw, p, layers, stream);
-      if (epi == EPI_ARGMAX && norm) return by_npw<T, A_ROW_F32, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
       break;
     case A_ROW_BF16:
       if constexpr (sizeof(T) == 2) {

@@ -31,6 +31,9 @@ struct EmbedArgs {
 hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream);
 hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream);
 hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream);
+// Row-major fp32 [rows][cols] -> fragment layout (swz_off with kper); cols % 4 == 0.
+hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper, float* dst,
+                                    hipStream_t stream);
 hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
                                 int* bonus, int* emitted, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

@@ -102,6 +102,22 @@ hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void rows_to_fragments_kernel(const float* __restrict__ src,
+                                                                int cols, int kper,
+                                                                float* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int KT = cols / (4 * kper);
+  for (int c = 4 * threadIdx.x; c < cols; c += 4 * blockDim.x)
+    *reinterpret_cast<f32x4*>(dst + swz_off(r, c, KT, kper)) =
+        *reinterpret_cast<const f32x4*>(src + (long long)r * cols + c);
+}
+
+hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper, float* dst,
+                                    hipStream_t stream) {
+  rows_to_fragments_kernel<<<rows, 256, 0, stream>>>(src, cols, kper, dst);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------
 // Greedy verification, one wave per request.  Lane i < 15 compares d_{i+1} with t_i; the
 // ballot of mismatches gives m = index of the lowest mismatching lane (15 if none), with

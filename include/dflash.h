@@ -177,8 +177,10 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
  *   hidden     [rows, H] fp32: residual-stream rows (before the final norm).
  *   ids_out    [rows] int32 out: argmax of RMSNorm(hidden) . W_lm^T, ties -> lowest id.
  *   logits_out [rows, V] fp32 out, may be NULL.
- * `workspace` is any step workspace initialized with dflash_workspace_init (only its
- * synchronization area is used).  Launches the same kernels as the draft step. */
+ * `workspace`: a step workspace initialized with dflash_workspace_init and sized by
+ * dflash_workspace_size for max_batch >= ceil(rows / 16); the rows are copied into the
+ * fragment layout there, then the draft step's LM-head kernels run on them.
+ * DFLASH_ERR_WORKSPACE if it is smaller. */
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
                                     const float* hidden, int32_t rows, int32_t* ids_out,
                                     float* logits_out, void* workspace, size_t ws_bytes,
