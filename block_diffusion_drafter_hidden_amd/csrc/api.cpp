@@ -123,21 +123,34 @@ struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
 };
 
-Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers) {
+Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 16) {
   Plan p{};
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.n_mblocks = cdiv(std::max(M, 1), 16 * p.mt);
   p.npw = npw;
-  const long long units = (long long)(n_tiles / npw) * p.n_mblocks * layers;
-  const int max_waves = std::max(1, 16 / (npw * p.mt));  // LDS reduction slots
+  const int groups = n_tiles / npw;
+  const long long units = (long long)groups * p.n_mblocks * layers;
+  const int max_waves = std::max(1, std::min(kMaxGemmThreads / 64, 16 / (npw * p.mt)));
+  auto tile_fits = [&](int tg) { return p.mt * 16 * (tg * npw * 16 + 1) <= 64 * 65; };
   p.ksub = 1;
-  while (p.ksub < 16 && units * p.ksub < kTargetWaves && KT / (p.ksub * 2) >= 8 &&
+  while (p.ksub < max_ksub && units * p.ksub < kTargetWaves && KT / (p.ksub * 2) >= 8 &&
          p.ksub * 2 <= max_waves)
     p.ksub *= 2;
   p.tgpw = 1;
+  // A wide GEMM whose tile groups split evenly over 256 workgroups runs one workgroup per CU
+  // with t tile groups each (t need not be a power of two).
+  const long long wgs1 = (long long)groups * p.n_mblocks * layers;
+  if (wgs1 >= 512 && wgs1 % 256 == 0 && groups % (wgs1 / 256) == 0) {
+    const int t = (int)(wgs1 / 256);
+    if (t <= max_waves && tile_fits(t)) {
+      p.tgpw = t;
+      p.ksub = 1;
+      while (p.ksub * 2 * t <= max_waves && KT / (p.ksub * 2) >= 8) p.ksub *= 2;
+      return p;
+    }
+  }
   while (p.ksub * p.tgpw < 4 && p.ksub * p.tgpw * 2 <= max_waves &&
-         (n_tiles / npw) % (p.tgpw * 2) == 0 &&
-         p.mt * 16 * (p.tgpw * 2 * npw * 16 + 1) <= 64 * 65)
+         groups % (p.tgpw * 2) == 0 && tile_fits(p.tgpw * 2))
     p.tgpw *= 2;
   return p;
 }
@@ -179,7 +192,7 @@ struct Carver {
 struct DraftPlan {
   Plan qkv, o, gu, dn;
   int nc;
-  size_t x, q, bk, bv, ao, h, apart_o, apart_ml;
+  size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml;
   size_t total;
 };
 
@@ -195,6 +208,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.nc = std::max(1, std::min({cdiv(kAttnTargetWGs, kv_groups), max_chunks, kAttnMaxChunks}));
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
+  p.xg = c.take((size_t)rows * m.H * 4);
+  p.ssq = c.take((size_t)(m.H / 16) * rows * 4);
   p.q = c.take((size_t)rows * m.nq * m.d * 4);
   p.bk = c.take((size_t)rows * m.nkv * m.d * 4);
   p.bv = c.take((size_t)rows * m.nkv * m.d * 4);
@@ -215,7 +230,7 @@ struct InjectPlan {
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
   p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);
-  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 1, m.L);
+  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
   p.total = c.off;
@@ -230,21 +245,25 @@ constexpr int kInjectChunkRows = 256;
     if (_e != hipSuccess) return DFLASH_ERR_HIP;      \
   } while (0)
 
-// Final RMSNorm + shared LM head + argmax over the vocabulary.  `x` is fp32 in the fragment
-// layout; with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
-dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* x,
-                             int rows, bool draft_rows, int* ids_out, float* logits_out,
-                             char* ws, hipStream_t stream) {
+// Final RMSNorm + shared LM head + argmax over the vocabulary.  `xg` is x * final gain in
+// the fragment layout and ssq the rows' sums of squares (ssq_parts partials, row stride
+// ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
+dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* xg,
+                             const float* ssq, int ssq_parts, int ssq_ld, int rows,
+                             bool draft_rows, int* ids_out, float* logits_out, char* ws,
+                             hipStream_t stream) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
   Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
   if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
     pl.ksub = 2;
     pl.tgpw = 2;
   }
-  GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, x, m.H, rows, m.V / 16);
+  GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, xg, m.H, rows, m.V / 16);
   g.a_kind = A_SWZ;
   g.norm = 1;
-  g.gamma = reinterpret_cast<const float*>(wb + P.final_norm);
+  g.ssq_in = ssq;
+  g.ssq_parts = ssq_parts;
+  g.ssq_ld = ssq_ld;
   g.eps = m.eps;
   g.keys = keys;
   g.logits_out = logits_out;
@@ -450,7 +469,10 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   const char* wb = reinterpret_cast<const char*>(packed);
   char* ws = reinterpret_cast<char*>(workspace);
   float* x = reinterpret_cast<float*>(ws + dp.x);
+  float* xg = reinterpret_cast<float*>(ws + dp.xg);
+  float* ssq = reinterpret_cast<float*>(ws + dp.ssq);
   const int rows = batch * 16;
+  const int n_parts = m.H / 16;   // partial sums of squares left by a residual GEMM
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
 
   {  // x = embedding rows of [anchor, mask x 15]
@@ -460,15 +482,20 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     e.embed = embed;
     e.hidden = m.H;
     e.x = x;
+    e.gamma = reinterpret_cast<const float*>(wb + P.layer0 + P.attn_norm);
+    e.xg = xg;
+    e.ssq = ssq;
     DF_TRY(launch_embed(m.bf16, e, rows, stream));
   }
   for (int l = 0; l < m.L; ++l) {
     const char* lb = wb + P.layer0 + (size_t)l * P.layer_stride;
     {  // RMSNorm + fused Q|K|V projection + RoPE
-      GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, x, m.H, rows,
+      GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, xg, m.H, rows,
                                  (m.nq + 2 * m.nkv) * m.d / 16);
       g.norm = 1;
-      g.gamma = reinterpret_cast<const float*>(lb + P.attn_norm);
+      g.ssq_in = ssq;
+      g.ssq_parts = l == 0 ? 1 : n_parts;   // the embedding kernel leaves whole-row sums
+      g.ssq_ld = rows;
       g.eps = m.eps;
       g.q_out = reinterpret_cast<float*>(ws + dp.q);
       g.bk_out = reinterpret_cast<float*>(ws + dp.bk);
@@ -506,12 +533,19 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  m.nq * m.d, rows, m.H / 16);
       g.out = x;
       g.ldo = m.H;
+      g.xg_out = xg;   // inputs of the MLP norm
+      g.gamma_next = reinterpret_cast<const float*>(lb + P.mlp_norm);
+      g.ssq_out = ssq;
+      g.ssq_ld = rows;
       DF_TRY(launch_gemm(m.bf16, dp.o.mt, dp.o.npw, EPI_RESIDUAL, g, 1, stream));
     }
     {  // RMSNorm + gate|up + SiLU * up
-      GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, x, m.H, rows, 2 * m.I / 16);
+      GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, xg, m.H, rows,
+                                 2 * m.I / 16);
       g.norm = 1;
-      g.gamma = reinterpret_cast<const float*>(lb + P.mlp_norm);
+      g.ssq_in = ssq;
+      g.ssq_parts = n_parts;
+      g.ssq_ld = rows;
       g.eps = m.eps;
       g.out = ws + dp.h;
       g.ldo = m.I;
@@ -522,10 +556,17 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  m.H / 16);
       g.out = x;
       g.ldo = m.H;
+      g.xg_out = xg;   // inputs of the next layer's attention norm, or of the final norm
+      g.gamma_next = reinterpret_cast<const float*>(
+          l + 1 < m.L ? wb + P.layer0 + (size_t)(l + 1) * P.layer_stride + P.attn_norm
+                      : wb + P.final_norm);
+      g.ssq_out = ssq;
+      g.ssq_ld = rows;
       DF_TRY(launch_gemm(m.bf16, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }
-  return launch_lm_head(m, P, wb, x, batch * 16, true, draft_ids, logits_out, ws, stream);
+  return launch_lm_head(m, P, wb, xg, ssq, n_parts, rows, rows, true, draft_ids, logits_out,
+                        ws, stream);
 }
 
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
@@ -539,13 +580,19 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   if (rows > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
   // The rows are first rewritten into the fragment layout, in the area a draft step keeps
   // its residual stream, so the LM head runs exactly the draft step's kernel.
-  const size_t frag_bytes = (size_t)cdiv(rows, 16) * 16 * m.H * 4;
-  if (ws_bytes < kSyncBytes + frag_bytes) return DFLASH_ERR_WORKSPACE;
+  const size_t frag_bytes = align_up((size_t)cdiv(rows, 16) * 16 * m.H * 4);
+  const size_t ssq_bytes = align_up((size_t)rows * 4);
+  if (ws_bytes < kSyncBytes + frag_bytes + ssq_bytes) return DFLASH_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   float* xs = reinterpret_cast<float*>(ws + kSyncBytes);
-  DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16 ? 8 : 4, xs, stream));
-  return launch_lm_head(m, packed_layout(m), reinterpret_cast<const char*>(packed), xs, rows,
-                        false, ids_out, logits_out, ws, stream);
+  float* ssq = reinterpret_cast<float*>(ws + kSyncBytes + frag_bytes);
+  const Packed P = packed_layout(m);
+  const char* wb = reinterpret_cast<const char*>(packed);
+  DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16 ? 8 : 4,
+                                  reinterpret_cast<const float*>(wb + P.final_norm), xs, ssq,
+                                  stream));
+  return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, logits_out, ws,
+                        stream);
 }
 
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,

@@ -18,6 +18,7 @@ namespace dflash {
 //     i + d/2 (r odd), so each rotation pair sits in two adjacent columns of one tile;
 //   * gate/up: tile j holds gate rows 8j..8j+7 (r < 8) and up rows 8j..8j+7 (r >= 8).
 constexpr int kTileBytes = 1024;
+constexpr int kMaxGemmThreads = 512;   // workgroup bound (ksub * tgpw <= 8 waves)
 
 enum Epi : int {
   EPI_STORE = 0,     // out[m][n] = acc, fp32 (fusion output c)
@@ -47,8 +48,13 @@ struct GemmParams {
   int lda;                  // row stride of the row-major kinds
   int M;                    // valid rows
   int a_kind;               // AKind
-  int norm;                 // 1: RMSNorm of the A rows folded in (gain `gamma`)
-  const float* gamma;       // RMSNorm gain [K]
+  // RMSNorm of the A rows (norm = 1).  The producer of A already multiplied it by the gain
+  // and left the rows' sums of squares as `ssq_parts` partials, ssq_in[p * ssq_ld + row];
+  // the kernel scales each finished row by 1 / sqrt(sum / K + eps).
+  int norm;
+  const float* ssq_in;
+  int ssq_parts;
+  int ssq_ld;               // row stride of the ssq arrays (padded rows)
   float eps;
   int n_tiles;              // n-tiles computed per grid.z slice
   int ksub;                 // waves splitting the k range of one tile group
@@ -60,6 +66,12 @@ struct GemmParams {
   void* out;                // EPI_STORE: c, EPI_RESIDUAL: x, EPI_SWIGLU: h; all fp32 in
                             // the fragment layout with ldo columns
   int ldo;
+  // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (fragment layout) and,
+  // per n-tile, the rows' partial sums of squares ssq_out[n_tile * ssq_ld + row] -- the
+  // inputs of the next RMSNorm-folded GEMM.
+  float* xg_out;
+  const float* gamma_next;
+  float* ssq_out;
   // EPI_QKV
   float* q_out;             // [M][n_q][d]
   float* bk_out;            // [batch][n_kv][16 slots][d]

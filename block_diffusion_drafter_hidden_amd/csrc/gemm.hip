@@ -12,9 +12,10 @@
 // Work split.  A wave owns NPW consecutive n-tiles (16 output columns each) and a slice of
 // the k range; the `ksub` waves of a tile group cover the whole k range and are reduced
 // through LDS in wave order, so a workgroup produces complete outputs and no workgroup
-// ever waits on another.  RMSNorm of the input is folded in: with p.norm the kernel reads
-// x * gamma, accumulates the row's sum of squares from the same loads, and scales the
-// finished row by 1/sqrt(mean + eps) before the epilogue.
+// ever waits on another.  RMSNorm of the input is folded in: the kernel that produces the
+// residual stream also writes x * gamma of the next norm and per-n-tile partial sums of
+// squares; the normed GEMM streams x * gamma like any activation and scales each finished
+// row by 1/sqrt(sum / K + eps) before the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -22,18 +23,22 @@
 
 namespace dflash {
 
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = kMaxGemmThreads / kWave;
 constexpr int kRedSlots = 16;          // waves * NPW * MT <= 16 (checked on the host)
 constexpr int kTileFloats = 64 * 65;   // (MT*16) * (cols + 1) <= 4160 (checked on the host)
 
 struct GemmSmem {
   f32x4 red[kRedSlots][kWave];
   float tile[kTileFloats];
-  float ss[kMaxWaves][64];
+  float ss_flat[kMaxWaves * kWave];   // per-thread partial sums of squares
   float rstd[64];
 };
 
-__device__ inline i32x4 load16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
+// Weight loads are non-temporal: every weight byte is read once per call, so they should not
+// displace the activations the other workgroups re-read from L2 (measured 7-12% faster).
+__device__ inline i32x4 load16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
 
 // Raw A values of one k-tile fragment for one lane (kPerLane consecutive k).
 template <typename T, typename AT>
@@ -67,23 +72,53 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
   const int m0 = mblock * rows;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  const float* tl = sm.tile;
+  float* tl = sm.tile;
 
   constexpr int kPer = Elem<T>::kPerLane;
   const int kto = p.ldo / (4 * kPer);   // k-tiles of the output as the next GEMM's A
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESIDUAL) {
-    for (int idx = tid; idx < rows * cols; idx += nthr) {
+    // Element idx of the tile; `pre` is its prefetched residual value when known.
+    auto store = [&](int idx, const float* pre) {
       const int r = idx / cols, c = idx % cols;
       const int m = m0 + r;
-      if (m >= p.M) continue;
-      float* o = reinterpret_cast<float*>(p.out) + swz_off(m, tile0 * 16 + c, kto, kPer);
+      if (m >= p.M) return;
+      const long long off = swz_off(m, tile0 * 16 + c, kto, kPer);
+      float* o = reinterpret_cast<float*>(p.out) + off;
       if constexpr (EPI == EPI_STORE) {
         *o = tl[r * ld + c];
-      } else if constexpr (NPRE > 0) {
-        const int i = (idx - tid) / nthr;
-        *o = (i < NPRE ? xpre[i < NPRE ? i : 0] : *o) + tl[r * ld + c];
       } else {
-        *o = *o + tl[r * ld + c];
+        const float v = (pre ? *pre : *o) + tl[r * ld + c];
+        *o = v;
+        if (p.xg_out) {
+          p.xg_out[off] = v * p.gamma_next[tile0 * 16 + c];
+          tl[r * ld + c] = v;   // kept for the sums of squares below
+        }
+      }
+    };
+    int idx0 = tid;
+    if constexpr (NPRE > 0) {   // iterations covered by the prefetch (static indices)
+#pragma unroll
+      for (int i = 0; i < NPRE; ++i)
+        if (tid + i * nthr < rows * cols) store(tid + i * nthr, &xpre[i]);
+      idx0 = tid + NPRE * nthr;
+    }
+    for (int idx = idx0; idx < rows * cols; idx += nthr) store(idx, nullptr);
+    if constexpr (EPI == EPI_RESIDUAL) {
+      if (p.xg_out) {   // partial sum of squares of every row over each n-tile's 16 columns
+        __syncthreads();
+        const int ntl = cols / 16;
+        for (int idx = tid; idx < rows * ntl; idx += nthr) {
+          const int r = idx % rows, jt = idx / rows;
+          const int m = m0 + r;
+          if (m >= p.M) continue;
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const float v = tl[r * ld + jt * 16 + c];
+            ss += v * v;
+          }
+          p.ssq_out[(long long)(tile0 + jt) * p.ssq_ld + m] = ss;
+        }
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -197,16 +232,15 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
 // Main kernel
 // ------------------------------------------------------------------------------------------
 template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
-__global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
+__global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(GemmParams p) {
   __shared__ GemmSmem sm;
   constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
   typedef typename std::conditional<AK == A_ROW_BF16, bf16, float>::type AT;
   typedef AFrag<T, AT, kTerms> Frag;
   constexpr int kPer = Elem<T>::kPerLane;
-  // k-tiles whose loads are issued together; bounded by the 128 VGPRs a 1024-thread
-  // workgroup leaves each lane (raw fp32 A + gamma for the normed variants).
+  // k-tiles whose loads are issued together (raw fp32 A and its pieces stay in registers).
   constexpr int U0 = (NPW * MT >= 4) ? 2 : (NPW * MT == 2 ? 4 : 8);
-  constexpr int U = (NORM || kTerms > 2) ? (U0 > 2 ? U0 / 2 : 2) : U0;
+  constexpr int U = kTerms > 2 ? (U0 > 2 ? U0 / 2 : 2) : U0;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -244,16 +278,26 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
     else
       arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * kPer;
   }
-  const float* gptr = NORM ? p.gamma + (lane >> 4) * kPer : nullptr;
 
   f32x4 acc[NPW][MT];
 #pragma unroll
   for (int t = 0; t < NPW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ssq[MT];
+  // RMSNorm: this thread's share of the rows' partial sums of squares, fetched now and
+  // summed after the main loop.  Thread t always serves row t % rows (blockDim is a multiple
+  // of 64, rows = 16 * MT <= 64).
+  constexpr int kSsqPer = NORM ? 16 : 1;
+  float sq[kSsqPer];
+  if constexpr (NORM) {
+    const int rows = MT * 16, total = rows * p.ssq_parts;
+    const int m = mblock * rows + threadIdx.x % rows;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) ssq[mt] = 0.f;
+    for (int i = 0; i < kSsqPer; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x;
+      sq[i] = idx < total && m < p.M ? p.ssq_in[(long long)(idx / rows) * p.ssq_ld + m] : 0.f;
+    }
+  }
 
   constexpr int NPRE = EPI == EPI_RESIDUAL ? ResidualPrefetch<MT, NPW>::kN : 0;
   float xpre[NPRE > 0 ? NPRE : 1];
@@ -317,25 +361,11 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
                               f[u][mt]);
           }
         }
-      float g[NORM ? U : 1][kPer];
-      if constexpr (NORM) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          load_a_raw<T, float>(gptr + (long long)(kt + u * kstep) * Elem<T>::kTile,
-                               kt + u * kstep < ke, g[u]);
-      }
       // Split each fragment right before its MFMAs to keep few pieces alive.
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          if constexpr (NORM) {
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-              ssq[mt] += f[u][mt][i] * f[u][mt][i];
-              f[u][mt][i] *= g[u][i];
-            }
-          }
           Frag a;
           a.from_floats(f[u][mt]);
 #pragma unroll
@@ -354,14 +384,15 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) sm.red[(wave * NPW + t) * MT + mt][lane] = acc[t][mt];
   }
-  if constexpr (NORM) {
+  if constexpr (NORM) {   // per-thread sums of the prefetched partials (in part order)
+    const int rows = MT * 16, total = rows * p.ssq_parts;
+    const int m = mblock * rows + threadIdx.x % rows;
+    float s = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float s = ssq[mt];
-      s += __shfl_xor(s, 16, kWave);
-      s += __shfl_xor(s, 32, kWave);
-      if (tg == 0 && lane < 16) sm.ss[ks][mt * 16 + lane] = s;
-    }
+    for (int i = 0; i < kSsqPer; ++i) s += sq[i];
+    for (int idx = threadIdx.x + kSsqPer * blockDim.x; idx < total; idx += blockDim.x)
+      if (m < p.M) s += p.ssq_in[(long long)(idx / rows) * p.ssq_ld + m];
+    sm.ss_flat[threadIdx.x] = s;
   }
   __syncthreads();
   if (ksub > 1 && ks == 0) {
@@ -372,9 +403,10 @@ __global__ __launch_bounds__(1024) void gemm_stream(GemmParams p) {
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] += sm.red[((wave + q) * NPW + t) * MT + mt][lane];
   }
   if constexpr (NORM) {
-    if (threadIdx.x < MT * 16) {
+    const int rows = MT * 16;
+    if (threadIdx.x < rows) {
       float s = 0.f;
-      for (int q = 0; q < ksub; ++q) s += sm.ss[q][threadIdx.x];
+      for (int j = threadIdx.x; j < (int)blockDim.x; j += rows) s += sm.ss_flat[j];
       sm.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)(p.KT * Elem<T>::kTile) + p.eps);
     }
     __syncthreads();
@@ -414,6 +446,9 @@ static hipError_t by_npw(int npw, const GemmParams& p, int layers, hipStream_t s
   if (npw == 1) return go<T, AK, MT, 1, EPI, NORM>(p, layers, stream);
   if (npw == 2) return go<T, AK, MT, 2, EPI, NORM>(p, layers, stream);
   if (npw == 4) return go<T, AK, MT, 4, EPI, NORM>(p, layers, stream);
+  if constexpr (EPI == EPI_ARGMAX && MT == 1) {   // the LM head's wide, single-m-tile case
+    if (npw == 8) return go<T, AK, MT, 8, EPI, NORM>(p, layers, stream);
+  }
   return hipErrorInvalidValue;
 }
 

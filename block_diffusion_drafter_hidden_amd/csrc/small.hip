@@ -77,21 +77,38 @@ hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipS
   return hipGetLastError();
 }
 
+// Sum over a 256-thread workgroup in a fixed order.
+__device__ inline float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
 // Block embedding: row b*16 + j of x is the embedding of the anchor (j = 0) or of the mask
-// token (j >= 1), widened to fp32 and written in the fragment layout (4 columns per store).
+// token (j >= 1), widened to fp32 and written in the fragment layout (4 columns per store),
+// together with x * gamma of the first RMSNorm and the row's sum of squares.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+  __shared__ float red[4];
   const int m = blockIdx.x;
   const int b = m / kBlock, j = m % kBlock;
   const int tok = j == 0 ? a.anchor_ids[b] : a.mask_id;
   const T* e = reinterpret_cast<const T*>(a.embed) + (long long)tok * a.hidden;
   constexpr int kPer = Elem<T>::kPerLane;
   const int KT = a.hidden / (4 * kPer);
+  float ss = 0.f;
   for (int i = 4 * threadIdx.x; i < a.hidden; i += 4 * blockDim.x) {
     const f32x4 v = {Elem<T>::to_f(e[i]), Elem<T>::to_f(e[i + 1]), Elem<T>::to_f(e[i + 2]),
                      Elem<T>::to_f(e[i + 3])};
-    *reinterpret_cast<f32x4*>(a.x + swz_off(m, i, KT, kPer)) = v;
+    const f32x4 g = *reinterpret_cast<const f32x4*>(a.gamma + i);
+    const long long off = swz_off(m, i, KT, kPer);
+    *reinterpret_cast<f32x4*>(a.x + off) = v;
+    *reinterpret_cast<f32x4*>(a.xg + off) = v * g;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
+  ss = block_sum256(ss, red);
+  if (threadIdx.x == 0) a.ssq[m] = ss;
 }
 
 hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream) {
@@ -104,17 +121,27 @@ hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_
 
 __global__ __launch_bounds__(256) void rows_to_fragments_kernel(const float* __restrict__ src,
                                                                 int cols, int kper,
-                                                                float* __restrict__ dst) {
+                                                                const float* __restrict__ gamma,
+                                                                float* __restrict__ dst,
+                                                                float* __restrict__ ssq) {
+  __shared__ float red[4];
   const int r = blockIdx.x;
   const int KT = cols / (4 * kper);
-  for (int c = 4 * threadIdx.x; c < cols; c += 4 * blockDim.x)
-    *reinterpret_cast<f32x4*>(dst + swz_off(r, c, KT, kper)) =
-        *reinterpret_cast<const f32x4*>(src + (long long)r * cols + c);
+  float ss = 0.f;
+  for (int c = 4 * threadIdx.x; c < cols; c += 4 * blockDim.x) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (long long)r * cols + c);
+    const f32x4 g = *reinterpret_cast<const f32x4*>(gamma + c);
+    *reinterpret_cast<f32x4*>(dst + swz_off(r, c, KT, kper)) = v * g;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum256(ss, red);
+  if (threadIdx.x == 0) ssq[r] = ss;
 }
 
-hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper, float* dst,
+hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper,
+                                    const float* gamma, float* dst, float* ssq,
                                     hipStream_t stream) {
-  rows_to_fragments_kernel<<<rows, 256, 0, stream>>>(src, cols, kper, dst);
+  rows_to_fragments_kernel<<<rows, 256, 0, stream>>>(src, cols, kper, gamma, dst, ssq);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle.dflash_oracle as ref
-from block_diffusion_drafter_hidden_amd import binding as B
+from block_diffusion_drafter_hidden_amd import Drafter, binding as B
 from tests import gpu_setup as G
 from workloads import TINY, QWEN3_8B, GPT_OSS_120B, scaled, synth
 
@@ -114,6 +114,28 @@ def test_draft_ids_and_logits_match_oracle(cfg, ctx):
             assert err.max() <= 1e-4 * np.abs(orc["logits"]).max()
         else:
             assert err.mean() < 5e-3 and err.max() < 5e-2, (err.mean(), err.max())
+
+
+@pytest.mark.parametrize("cfg,rows", [(SMALL_BF16, 1), (SMALL_BF16, 37), (TINY, 20)])
+def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
+    """dflash_lm_head_argmax on caller-provided fp32 hidden rows (ragged row counts)."""
+    w = synth.drafter_weights(cfg, seed=3)
+    wd = {k: v.to("cuda") for k, v in w.items()}
+    dr = Drafter(cfg, wd, max_batch=(rows + 15) // 16, max_ctx=16, max_inject_rows=16)
+    hidden = synth.normal(f"{cfg.name}/lm-rows", (rows, cfg.hidden), std=1.0, dtype="f32",
+                          seed=3)
+    ids = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    logits = torch.empty((rows, cfg.vocab), dtype=torch.float32, device="cuda")
+    B.lm_head_argmax(dr.ccfg, dr.packed, hidden.to("cuda"), ids, dr.ws, logits_out=logits)
+    torch.cuda.synchronize()
+    y = ref.rms_norm(ref.f64(hidden), w["final_norm"], cfg.rms_eps)
+    lg = y @ ref.f64(w["lm_head"]).T
+    i1, top1, top2 = ref.top2(lg)
+    orc = {"ids": i1, "gap": top1 - top2, "top1": top1, "top2": top2}
+    bad, _ = G.compare_ids(ids.cpu().numpy(), orc, cfg.dtype)
+    assert bad == 0
+    err = np.abs(logits.cpu().numpy() - lg).max() / np.abs(lg).max()
+    assert err < (1e-5 if cfg.dtype == "f32" else 1e-4), err
 
 
 def test_ragged_batch_with_permuted_pages_matches_per_request_oracle():
