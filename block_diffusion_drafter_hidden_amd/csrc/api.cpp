@@ -155,6 +155,12 @@ Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 1
   return p;
 }
 
+// RoPE frequencies theta^(-2i/d) in fp64 for the epilogues that rotate q and k.
+void set_rope(const Dims& m, GemmParams& g) {
+  const double log_theta = std::log((double)m.theta);
+  for (int i = 0; i < m.d / 2; ++i) g.inv_freq[i] = std::exp(-(2.0 * i / m.d) * log_theta);
+}
+
 GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const void* A, int lda,
                        int M, int n_tiles) {
   GemmParams g;
@@ -435,7 +441,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.n_q = m.nq;
       g.n_kv = m.nkv;
       g.head_dim = m.d;
-      g.log_theta = std::log((double)m.theta);
+      set_rope(m, g);
       g.k_pool = cache->k_pool;
       g.v_pool = cache->v_pool;
       g.pool_layer_elems = pool_layer;
@@ -504,7 +510,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.n_q = m.nq;
       g.n_kv = m.nkv;
       g.head_dim = m.d;
-      g.log_theta = std::log((double)m.theta);
+      set_rope(m, g);
       DF_TRY(launch_gemm(m.bf16, dp.qkv.mt, dp.qkv.npw, EPI_QKV, g, 1, stream));
     }
     {  // attention over injected context + block

@@ -142,15 +142,18 @@ __device__ inline long long swz_off(int r, int k, int KT, int kPer) {
   return (((long long)(r >> 4) * KT + kt) * (kPer / 4) + j / 4) * 256 + lane * 4 + (j & 3);
 }
 
-// RoPE angle for pair index i of a head of width d at position pos, computed in fp64.
-__device__ inline void rope_cos_sin(int pos, int i, int d, double log_theta, float* c,
-                                    float* s) {
-  double inv = exp(-(2.0 * (double)i / (double)d) * log_theta);
-  double a = (double)pos * inv;
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+// RoPE rotation for frequency `inv` (theta^(-2i/d), computed in fp64 on the host) at
+// position pos: the angle pos * inv is formed and reduced modulo 2*pi in fp64 (two-part
+// constant), so the fp32 sine and cosine of the reduced angle are accurate to about one fp32
+// ulp for every position a cache can hold.
+__device__ inline void rope_cos_sin(int pos, double inv, float* c, float* s) {
+  constexpr double kTwoPiHi = 6.283185307179586;            // 2*pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;       // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  const double a = (double)pos * inv;
+  const double k = rint(a * kInvTwoPi);
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
+  sincosf((float)r, s, c);
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }

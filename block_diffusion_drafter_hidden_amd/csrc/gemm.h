@@ -78,7 +78,7 @@ struct GemmParams {
   float* bv_out;            // [batch][n_kv][d][16 slots] (transposed)
   const int* ctx_lens;      // [batch]; slot j of request b sits at ctx_lens[b] + j
   int n_q, n_kv, head_dim;
-  double log_theta;
+  double inv_freq[64];      // RoPE frequencies theta^(-2i/d), i < d/2 (d <= 128)
   // EPI_INJECT
   void* k_pool;
   void* v_pool;

@@ -155,7 +155,7 @@ __device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int ti
       if (rope) {
         const int i = 8 * t + pp;
         float cs, sn;
-        rope_cos_sin(position, i, d, p.log_theta, &cs, &sn);
+        rope_cos_sin(position, p.inv_freq[i], &cs, &sn);
         const float y0 = a0 * cs - a1 * sn, y1 = a1 * cs + a0 * sn;
         a0 = y0;
         a1 = y1;
