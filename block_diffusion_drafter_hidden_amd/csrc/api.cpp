@@ -123,8 +123,22 @@ struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
 };
 
-Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 16) {
+// Rows above which bf16 GEMMs over fragment-layout activations use the 128 x 128 tall kernel
+// (weights read once per 128 rows instead of once per 64).
+constexpr int kTallRows = 64;
+constexpr int kTallMT = 8, kTallNT = 8;
+
+Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 16,
+               bool tall_ok = false) {
   Plan p{};
+  if (tall_ok && M > kTallRows && n_tiles % kTallNT == 0) {
+    p.mt = kTallMT;
+    p.n_mblocks = cdiv(M, 16 * kTallMT);
+    p.npw = 1;
+    p.ksub = 1;
+    p.tgpw = 1;
+    return p;
+  }
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.n_mblocks = cdiv(std::max(M, 1), 16 * p.mt);
   p.npw = npw;
@@ -205,13 +219,18 @@ struct DraftPlan {
 DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   DraftPlan p{};
   const int rows = B * 16;
-  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 2, 1);
-  p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1);
-  p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1);
-  p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1);
+  const bool tall = m.bf16 != 0;
+  p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
+  p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
+  p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
+  p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
-  p.nc = std::max(1, std::min({cdiv(kAttnTargetWGs, kv_groups), max_chunks, kAttnMaxChunks}));
+  // Context chunks per (request, KV group): enough workgroups to fill the chip at small
+  // batch, and chunks of at most ~512 keys for long contexts so that ragged batches balance.
+  const int want = std::max(cdiv(kAttnTargetWGs, kv_groups),
+                            std::min(cdiv(std::max(max_ctx, 1), 512), 64));
+  p.nc = std::max(1, std::min({want, max_chunks, kAttnMaxChunks}));
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
   p.xg = c.take((size_t)rows * m.H * 4);
@@ -236,7 +255,7 @@ struct InjectPlan {
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
   p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);
-  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4);
+  p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4, m.bf16 != 0);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
   p.total = c.off;
@@ -259,7 +278,7 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
                              bool draft_rows, int* ids_out, float* logits_out, char* ws,
                              hipStream_t stream) {
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
-  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1);
+  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1, 16, m.bf16 != 0);
   if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
     pl.ksub = 2;
     pl.tgpw = 2;

@@ -24,6 +24,7 @@
 namespace dflash {
 
 constexpr int kMaxWaves = kMaxGemmThreads / kWave;
+constexpr int kXcds = 8;               // accelerator complex dies (one L2 each)
 constexpr int kRedSlots = 16;          // waves * NPW * MT <= 16 (checked on the host)
 constexpr int kTileFloats = 64 * 65;   // (MT*16) * (cols + 1) <= 4160 (checked on the host)
 
@@ -65,14 +66,13 @@ struct ResidualPrefetch {
 };
 
 template <typename T, int MT, int EPI, int NPRE>
-__device__ void run_epilogue(const GemmParams& p, GemmSmem& sm, int cols, int tile0, int mblock,
+__device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0, int mblock,
                              int z, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
   const int rows = MT * 16;
   const int ld = cols + 1;
   const int m0 = mblock * rows;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  float* tl = sm.tile;
 
   constexpr int kPer = Elem<T>::kPerLane;
   const int kto = p.ldo / (4 * kPer);   // k-tiles of the output as the next GEMM's A
@@ -246,9 +246,29 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   const int wave = threadIdx.x / kWave;
   const int ksub = p.ksub;
   const int tg = wave / ksub, ks = wave % ksub;
-  const int wg_tile0 = blockIdx.x * p.tgpw * NPW;
+  // Workgroup -> (tile group, m-block).  With several m-blocks every weight tile is needed by
+  // n_mblocks workgroups: workgroups are dispatched round-robin over the 8 XCDs, so the
+  // m-blocks of one tile group are given ids that land on the same XCD back to back and the
+  // repeated weight reads hit that XCD's L2 instead of HBM.
+  int group, mblock;
+  {
+    const int L = blockIdx.x, nm = p.n_mblocks;
+    const int n_groups = p.n_tiles / (p.tgpw * NPW);
+    if (nm == 1) {
+      group = L;
+      mblock = 0;
+    } else if (n_groups % kXcds == 0) {
+      const int xcd = L % kXcds, slot = L / kXcds;
+      group = (slot / nm) * kXcds + xcd;
+      mblock = slot % nm;
+    } else {
+      group = L / nm;
+      mblock = L % nm;
+    }
+  }
+  const int wg_tile0 = group * p.tgpw * NPW;
   const int tile0 = wg_tile0 + tg * NPW;
-  const int mblock = blockIdx.y, z = blockIdx.z;
+  const int z = blockIdx.z;
   // k-tiles of this wave: kt = kb + i*kstep for kt < ke.
   const int kw = (p.KT + ksub - 1) / ksub;
   const int kstep = p.kinter ? ksub : 1;
@@ -427,7 +447,185 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
         }
   }
   __syncthreads();
-  run_epilogue<T, MT, EPI, NPRE>(p, sm, cols, wg_tile0, mblock, z, xpre);
+  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, xpre);
+}
+
+
+// ------------------------------------------------------------------------------------------
+// Tall variant for many rows (batched drafts, prefill chunks): a workgroup of 4 waves owns a
+// 128-row x 128-column output block and walks K one 32-wide k-tile at a time.  Each k-tile's
+// A block (8 m-tiles of fp32 fragments, 16 KB) and W block (8 n-tiles, 8 KB) are staged in
+// LDS once (double-buffered, next k-tile's loads in flight during this one's MFMAs) and each
+// wave computes a 64 x 64 quarter from them: 4 A and 4 W fragments feed 16 tile products,
+// each as hi + lo (+ mid) bf16 MFMAs.  Weights are thus read once per 128 rows and
+// activations once per 128 columns.  The finished block goes through LDS to the same
+// epilogues as the streaming kernel.
+// ------------------------------------------------------------------------------------------
+constexpr int kTallM = 128, kTallN = 128;
+constexpr int kTallMT = kTallM / 16, kTallNT = kTallN / 16;
+
+struct TallStage {
+  f32x4 a[2][kTallMT][2][kWave];   // [buf][m-tile][group][lane]: fp32 A fragments
+  i32x4 w[2][kTallNT][kWave];      // [buf][n-tile][lane]: packed bf16 B fragments
+};
+union TallSmem {
+  TallStage st;
+  float tile[kTallM * (kTallN + 1)];
+};
+
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
+  __shared__ TallSmem sm;
+  __shared__ float rstd_s[kTallM];
+  __shared__ float ssq_s[256];
+  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
+  typedef AFrag<bf16, float, kTerms> Frag;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
+  const int z = blockIdx.z;
+
+  // Workgroup -> (column block, row block), row-block major: the workgroups resident at one
+  // time share a row block, whose activations (128 rows x K) then stay in L2 while the
+  // weights stream past.
+  const int ncb = p.n_tiles / kTallNT;
+  const int cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
+  const int KT = p.KT;
+  const int mtile0 = rb * kTallMT;                   // first m-tile of the block
+  const int n_mtiles_valid = (p.M + 15) / 16;
+  const float* A = reinterpret_cast<const float*>(p.A);
+  const char* W = p.W + (long long)z * p.w_zstride +
+                  (long long)(p.nt0 + cb * kTallNT) * p.nt_stride * kTileBytes;
+
+  // RMSNorm: partial sums of squares of this block's rows, summed in a fixed order later.
+  float sq[NORM ? 8 : 1];
+  if constexpr (NORM) {
+    const int r = tid % kTallM, m = rb * kTallM + r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int part = tid / kTallM + 2 * i;
+      sq[i] = part < p.ssq_parts && m < p.M ? p.ssq_in[(long long)part * p.ssq_ld + m] : 0.f;
+    }
+  }
+
+  // Global -> register staging of one k-tile: 4 A chunks and 2 W chunks of 16 bytes per
+  // thread.  A ring of kRing register stages keeps kRing - 1 k-tiles of loads in flight
+  // beyond the one being multiplied, so memory latency overlaps several k-tiles of MFMAs.
+  constexpr int kRing = 2;
+  f32x4 ra[kRing][4];
+  i32x4 rw[kRing][2];
+  // Loads are unconditional (no divergent branches, so the waits stay precise): k-tiles past
+  // the end re-read the last one, and m-tiles past the rows re-read the last valid m-tile --
+  // those rows only reach output rows the epilogue never stores.
+  auto load_stage = [&](int kt, f32x4 (&a)[4], i32x4 (&w)[2]) {
+    const int ktc = min(kt, KT - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256, mt = c / 128, g = (c / 64) % 2, l = c % 64;
+      const int mtc = min(mtile0 + mt, n_mtiles_valid - 1);
+      a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * KT + ktc) * 2 + g) * 256 +
+                                             l * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256, nt = c / 64, l = c % 64;
+      w[i] = load16(W + ((long long)nt * p.nt_stride + (long long)ktc * p.kt_stride) *
+                            kTileBytes + l * 16);
+    }
+  };
+  auto store_stage = [&](int buf, const f32x4 (&a)[4], const i32x4 (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256;
+      sm.st.a[buf][c / 128][(c / 64) % 2][c % 64] = a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      sm.st.w[buf][c / 64][c % 64] = w[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    i32x4 wf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[j] = sm.st.w[buf][wn * 4 + j][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 a0 = sm.st.a[buf][wm * 4 + i][0][lane], a1 = sm.st.a[buf][wm * 4 + i][1][lane];
+      const float f[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      Frag a;
+      a.from_floats(f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < Frag::kTerms; ++q) acc[i][j] = mfma_tile<bf16>(a.part[q], wf[j], acc[i][j]);
+    }
+  };
+
+  // Prologue: k-tiles 0 .. kRing-1 in flight, k-tile 0 in LDS buffer 0.
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) load_stage(r, ra[r], rw[r]);
+  store_stage(0, ra[0], rw[0]);
+  __syncthreads();
+  // Iteration kt: ring stage kt % kRing is free (its k-tile is in LDS) and is refilled with
+  // k-tile kt + kRing; k-tile kt is multiplied from LDS; k-tile kt + 1 moves to LDS.
+  // Full rounds of kRing k-tiles without conditions, then the remainder.
+  const int KTr = KT - KT % kRing;
+  for (int kt0 = 0; kt0 < KTr; kt0 += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      const int kt = kt0 + r;
+      load_stage(kt + kRing, ra[r], rw[r]);
+      compute(kt & 1);
+      store_stage((kt + 1) & 1, ra[(r + 1) % kRing], rw[(r + 1) % kRing]);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r) {
+    const int kt = KTr + r;
+    if (kt < KT) {
+      compute(kt & 1);
+      store_stage((kt + 1) & 1, ra[(r + 1) % kRing], rw[(r + 1) % kRing]);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (NORM) {
+    const int r = tid % kTallM, m = rb * kTallM + r;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += sq[i];
+    for (int part = tid / kTallM + 16; part < p.ssq_parts; part += 2)
+      if (m < p.M) s += p.ssq_in[(long long)part * p.ssq_ld + m];
+    ssq_s[tid] = s;
+    __syncthreads();
+    if (tid < kTallM)
+      rstd_s[tid] =
+          1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(KT * 32) + p.eps);
+    __syncthreads();
+  }
+  constexpr int ld = kTallN + 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        float v = acc[i][j][e];
+        if constexpr (NORM) v *= rstd_s[r];
+        sm.tile[r * ld + wn * 64 + j * 16 + (lane & 15)] = v;
+      }
+  __syncthreads();
+  const float xpre[1] = {0.f};
+  run_epilogue<bf16, kTallMT, EPI, 0>(p, sm.tile, kTallN, cb * kTallNT, rb, z, xpre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -435,7 +633,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
 // ------------------------------------------------------------------------------------------
 template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 static hipError_t go(const GemmParams& p, int layers, hipStream_t stream) {
-  dim3 grid(p.n_tiles / (p.tgpw * NPW), p.n_mblocks, layers);
+  dim3 grid(p.n_tiles / (p.tgpw * NPW) * p.n_mblocks, 1, layers);
   dim3 block(kWave * p.ksub * p.tgpw);
   gemm_stream<T, AK, MT, NPW, EPI, NORM><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
@@ -479,8 +677,25 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
   return hipErrorInvalidValue;
 }
 
+template <int EPI, bool NORM>
+static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
+  dim3 grid(p.n_tiles / kTallNT * p.n_mblocks, 1, layers);
+  gemm_tall<EPI, NORM><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
                        int layers, hipStream_t stream) {
+  if (mt == kTallMT) {   // 128-row blocks: bf16 weights, fragment-layout A
+    if (!dtype_bf16 || p.a_kind != A_SWZ || p.n_tiles % kTallNT) return hipErrorInvalidValue;
+    const bool norm = p.norm != 0;
+    if (epi == EPI_RESIDUAL && !norm) return go_tall<EPI_RESIDUAL, false>(p, layers, stream);
+    if (epi == EPI_INJECT && !norm) return go_tall<EPI_INJECT, false>(p, layers, stream);
+    if (epi == EPI_QKV && norm) return go_tall<EPI_QKV, true>(p, layers, stream);
+    if (epi == EPI_SWIGLU && norm) return go_tall<EPI_SWIGLU, true>(p, layers, stream);
+    if (epi == EPI_ARGMAX && norm) return go_tall<EPI_ARGMAX, true>(p, layers, stream);
+    return hipErrorInvalidValue;
+  }
   if (dtype_bf16) {
     if (mt == 1) return launch_mt<bf16, 1>(npw, epi, p, layers, stream);
     if (mt == 2) return launch_mt<bf16, 2>(npw, epi, p, layers, stream);
