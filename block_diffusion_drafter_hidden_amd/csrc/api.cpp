@@ -206,13 +206,28 @@ struct Carver {
   }
 };
 
+// The LM head's plan (the streaming kernel prefers 2 waves per k range and 2 tile groups of
+// 4 n-tiles at one m-tile) and the bytes of its argmax partials.
+Plan lm_plan(const Dims& m, int rows) {
+  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1, 16, m.bf16 != 0);
+  if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
+    pl.ksub = 2;
+    pl.tgpw = 2;
+  }
+  return pl;
+}
+size_t lm_keys_bytes(const Dims& m, int rows) {
+  const Plan pl = lm_plan(m, rows);
+  return (size_t)argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw) * rows * 8;
+}
+
 // ---------------------------------------------------------------------------------------
 // Per-call plans of the draft and inject steps.
 // ---------------------------------------------------------------------------------------
 struct DraftPlan {
   Plan qkv, o, gu, dn;
   int nc;
-  size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml;
+  size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml, keys;
   size_t total;
 };
 
@@ -243,6 +258,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   const size_t R = (size_t)m.G * 16;
   p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
+  p.keys = c.take(lm_keys_bytes(m, rows));
   p.total = c.off;
   return p;
 }
@@ -273,16 +289,13 @@ constexpr int kInjectChunkRows = 256;
 // Final RMSNorm + shared LM head + argmax over the vocabulary.  `xg` is x * final gain in
 // the fragment layout and ssq the rows' sums of squares (ssq_parts partials, row stride
 // ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
+// keys: workspace for the per-column-block argmax partials, lm_keys_bytes(m, rows) bytes.
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* xg,
                              const float* ssq, int ssq_parts, int ssq_ld, int rows,
-                             bool draft_rows, int* ids_out, float* logits_out, char* ws,
-                             hipStream_t stream) {
-  unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + kCounterBytes);
-  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1, 16, m.bf16 != 0);
-  if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
-    pl.ksub = 2;
-    pl.tgpw = 2;
-  }
+                             bool draft_rows, int* ids_out, float* logits_out,
+                             unsigned long long* keys, hipStream_t stream) {
+  const Plan pl = lm_plan(m, rows);
+  const int parts = argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw);
   GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, xg, m.H, rows, m.V / 16);
   g.a_kind = A_SWZ;
   g.norm = 1;
@@ -291,11 +304,12 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.ssq_ld = ssq_ld;
   g.eps = m.eps;
   g.keys = keys;
+  g.keys_ld = rows;
   g.logits_out = logits_out;
   g.ldo = m.V;
   g.draft_rows = draft_rows ? 1 : 0;
   DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
-  DF_TRY(launch_argmax_finalize(keys, ids_out, rows, draft_rows ? 1 : 0, stream));
+  DF_TRY(launch_argmax_finalize(keys, parts, rows, ids_out, rows, draft_rows ? 1 : 0, stream));
   return DFLASH_OK;
 }
 
@@ -591,7 +605,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     }
   }
   return launch_lm_head(m, P, wb, xg, ssq, n_parts, rows, rows, true, draft_ids, logits_out,
-                        ws, stream);
+                        reinterpret_cast<unsigned long long*>(ws + dp.keys), stream);
 }
 
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
@@ -607,16 +621,18 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   // its residual stream, so the LM head runs exactly the draft step's kernel.
   const size_t frag_bytes = align_up((size_t)cdiv(rows, 16) * 16 * m.H * 4);
   const size_t ssq_bytes = align_up((size_t)rows * 4);
-  if (ws_bytes < kSyncBytes + frag_bytes + ssq_bytes) return DFLASH_ERR_WORKSPACE;
+  const size_t key_bytes = align_up(lm_keys_bytes(m, rows));
+  if (ws_bytes < kSyncBytes + frag_bytes + ssq_bytes + key_bytes) return DFLASH_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   float* xs = reinterpret_cast<float*>(ws + kSyncBytes);
   float* ssq = reinterpret_cast<float*>(ws + kSyncBytes + frag_bytes);
+  auto* keys = reinterpret_cast<unsigned long long*>(ws + kSyncBytes + frag_bytes + ssq_bytes);
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);
   DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16 ? 8 : 4,
                                   reinterpret_cast<const float*>(wb + P.final_norm), xs, ssq,
                                   stream));
-  return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, logits_out, ws,
+  return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, logits_out, keys,
                         stream);
 }
 

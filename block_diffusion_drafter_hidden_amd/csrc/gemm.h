@@ -88,7 +88,10 @@ struct GemmParams {
   const int* seq_idx;
   const int* pos;
   // EPI_ARGMAX
-  unsigned long long* keys; // [M] (value, index) keys, stride 16 words; zero before the launch
+  // (value, index) keys of each workgroup's best column per row, keys[part * keys_ld + row],
+  // part = the workgroup's column block; reduced over parts by the finalize kernel.
+  unsigned long long* keys;
+  int keys_ld;
   float* logits_out;        // [rows][ldo] or null
   int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
 };
@@ -98,10 +101,15 @@ struct GemmParams {
 hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
                        int layers, hipStream_t stream);
 
-// ids = indices encoded in keys[m * 16] for m < rows; with draft_rows the rows are 16-slot
-// blocks and only slots 1..15 produce ids (block b, slot j -> ids[b*15 + j-1]).  Keys are
-// reset to zero for the next launch.
-hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows, int draft_rows,
-                                  hipStream_t stream);
+// ids[m] = index of the largest key over parts, keys[part * keys_ld + m], for m < rows; with
+// draft_rows the rows are 16-slot blocks and only slots 1..15 produce ids (block b, slot j
+// -> ids[b*15 + j-1]).
+hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int keys_ld,
+                                  int* ids, int rows, int draft_rows, hipStream_t stream);
+
+// Column blocks (argmax parts) of an EPI_ARGMAX launch with this plan.
+inline int argmax_parts(int n_tiles, int mt, int npw, int tgpw) {
+  return mt == 8 ? n_tiles / 8 : n_tiles / (npw * tgpw);
+}
 
 }  // namespace dflash

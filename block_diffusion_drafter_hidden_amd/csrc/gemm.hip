@@ -208,7 +208,8 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         p.logits_out[orow * p.ldo + tile0 * 16 + c] = tl[r * ld + c];
       }
     }
-    // One wave per row: lanes scan columns, then a wave-wide (value, index) maximum.
+    // One wave per row: lanes scan columns, then a wave-wide (value, index) maximum, stored
+    // as this workgroup's part of the row.
     const int lane = tid % kWave, wave = tid / kWave, nw = nthr / kWave;
     for (int r = wave; r < rows; r += nw) {
       const int m = m0 + r;
@@ -223,7 +224,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         const unsigned long long other = __shfl_xor(best, o, kWave);
         best = other > best ? other : best;
       }
-      if (lane == 0) atomicMax(&p.keys[(long long)m * 16], best);
+      if (lane == 0) p.keys[(long long)(tile0 / (cols / 16)) * p.keys_ld + m] = best;
     }
   }
 }
@@ -299,11 +300,13 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
       arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * kPer;
   }
 
-  f32x4 acc[NPW][MT];
+  // acc takes the products of the first A piece, acc_lo those of the others: two
+  // independent MFMA chains per tile (added together after the loop).
+  f32x4 acc[NPW][MT], acc_lo[NPW][MT];
 #pragma unroll
   for (int t = 0; t < NPW; ++t)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = acc_lo[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // RMSNorm: this thread's share of the rows' partial sums of squares, fetched now and
   // summed after the main loop.  Thread t always serves row t % rows (blockDim is a multiple
   // of 64, rows = 16 * MT <= 64).
@@ -392,10 +395,16 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
           for (int t = 0; t < NPW; ++t)
 #pragma unroll
             for (int q = 0; q < Frag::kTerms; ++q)
-              acc[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc[t][mt]);
+              if (q == 0) acc[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc[t][mt]);
+              else acc_lo[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc_lo[t][mt]);
         }
     }
   }
+
+#pragma unroll
+  for (int t = 0; t < NPW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] += acc_lo[t][mt];
 
   // k-slices of a tile group: park slices 1.., add them to slice 0 in wave order.
   if (ksub > 1 && ks > 0) {
@@ -551,21 +560,31 @@ __global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One k-tile from LDS: every fragment read first (one wait), then the MFMAs ordered piece-
+  // major so the two (three) products into one accumulator are 16 instructions apart.
   auto compute = [&](int buf) {
     i32x4 wf[4];
+    f32x4 ar[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) wf[j] = sm.st.w[buf][wn * 4 + j][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 a0 = sm.st.a[buf][wm * 4 + i][0][lane], a1 = sm.st.a[buf][wm * 4 + i][1][lane];
-      const float f[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      Frag a;
-      a.from_floats(f);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < Frag::kTerms; ++q) acc[i][j] = mfma_tile<bf16>(a.part[q], wf[j], acc[i][j]);
+      ar[i][0] = sm.st.a[buf][wm * 4 + i][0][lane];
+      ar[i][1] = sm.st.a[buf][wm * 4 + i][1][lane];
     }
+    Frag a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f[8] = {ar[i][0][0], ar[i][0][1], ar[i][0][2], ar[i][0][3],
+                          ar[i][1][0], ar[i][1][1], ar[i][1][2], ar[i][1][3]};
+      a[i].from_floats(f);
+    }
+#pragma unroll
+    for (int q = 0; q < Frag::kTerms; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_tile<bf16>(a[i].part[q], wf[j], acc[i][j]);
   };
 
   // Prologue: k-tiles 0 .. kRing-1 in flight, k-tile 0 in LDS buffer 0.
@@ -708,19 +727,33 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
   return hipErrorInvalidValue;
 }
 
-__global__ void argmax_finalize_kernel(unsigned long long* keys, int* ids, int rows,
-                                       int draft_rows) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row: lanes take the parts in strides, then a wave-wide maximum.
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* keys,
+                                                              int parts, int keys_ld, int* ids,
+                                                              int rows, int draft_rows) {
+  const int lane = threadIdx.x % kWave;
+  const int m = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (m >= rows) return;
-  const int idx = argmax_key_index(keys[(long long)m * 16]);
-  keys[(long long)m * 16] = 0ull;
+  unsigned long long best = 0;
+  for (int q = lane; q < parts; q += kWave) {
+    const unsigned long long k = keys[(long long)q * keys_ld + m];
+    best = k > best ? k : best;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long other = __shfl_xor(best, o, kWave);
+    best = other > best ? other : best;
+  }
+  if (lane != 0) return;
+  const int idx = argmax_key_index(best);
   if (!draft_rows) ids[m] = idx;
   else if (m % kBlock != 0) ids[(m / kBlock) * kDrafts + m % kBlock - 1] = idx;
 }
 
-hipError_t launch_argmax_finalize(unsigned long long* keys, int* ids, int rows, int draft_rows,
-                                  hipStream_t stream) {
-  argmax_finalize_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(keys, ids, rows, draft_rows);
+hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int keys_ld,
+                                  int* ids, int rows, int draft_rows, hipStream_t stream) {
+  argmax_finalize_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(keys, parts, keys_ld, ids, rows,
+                                                            draft_rows);
   return hipGetLastError();
 }
 
