@@ -226,7 +226,7 @@ size_t lm_keys_bytes(const Dims& m, int rows) {
 // ---------------------------------------------------------------------------------------
 struct DraftPlan {
   Plan qkv, o, gu, dn;
-  int nc;
+  int nc, chunk;
   size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml, keys;
   size_t total;
 };
@@ -246,6 +246,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   const int want = std::max(cdiv(kAttnTargetWGs, kv_groups),
                             std::min(cdiv(std::max(max_ctx, 1), 512), 64));
   p.nc = std::max(1, std::min({want, max_chunks, kAttnMaxChunks}));
+  p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
   p.xg = c.take((size_t)rows * m.H * 4);
@@ -560,6 +561,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.n_kv = m.nkv;
       a.head_dim = m.d;
       a.nc = dp.nc;
+      a.chunk = dp.chunk;
       a.scale = 1.0f / std::sqrt((float)m.d);
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);

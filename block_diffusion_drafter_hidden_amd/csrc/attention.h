@@ -17,7 +17,8 @@ struct AttnArgs {
   int max_pages;
   const int* ctx_lens;     // [B]
   int n_q, n_kv, head_dim;
-  int nc;                  // context chunks per request (each T_b / nc keys, rounded to 32)
+  int nc;                  // context chunks per request
+  int chunk;               // context keys per chunk, a multiple of 32 (nc * chunk >= T_b)
   float scale;             // 1 / sqrt(d)
   float* part_o;           // [B][n_kv][nc][G][d/16][4][16 rows][4]
   float* part_ml;          // [B][n_kv][nc][G][16 rows][2]

@@ -3,9 +3,9 @@
 // the 16 block keys.
 //
 // Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
-// [c*chunk_b, min((c+1)*chunk_b, T_b)) with chunk_b = T_b / nc rounded up to 32 keys, and
-// the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
-// the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
+// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32 fixed by the caller, so the page
+// ids of a chunk can be fetched before T_b arrives), and the last workgroup also the 16
+// block keys (so a grid of nc * n_kv * batch workgroups fills the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
 // online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
 // Pass 2 (merge), grid (n_q, d / 32, batch): rescales the nc partials of each head to a
 // common maximum and divides by the total sum, chunks in order, so results do not depend on
@@ -41,10 +41,6 @@ __device__ inline long long part_o_index(long long slot, int G, int hh, int D, i
   return ((((slot * G + hh) * (D / 16) + dim / 16) * 4 + (dim % 16) / 4) * kBlock + row) * 4 +
          dim % 4;
 }
-
-// Context keys per chunk for a request with T cached positions: T split over nc chunks,
-// rounded up to whole 32-key steps (chunks start on page boundaries).
-__device__ inline int context_chunk(int T, int nc) { return ((T + nc - 1) / nc + 31) / 32 * 32; }
 
 __device__ inline void split2(float v, bf16& hi, bf16& lo) {
   hi = (bf16)v;
@@ -95,11 +91,15 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int n = lane & 15, q = lane >> 4;
   const int nq = a.n_q, nkv = a.n_kv;
+  // Physical page ids of the chunk's first 64 logical pages (lane i: page i), fetched
+  // together with T_b; indices are clamped into the table row.
+  const int kbeg0 = c * a.chunk;
+  const int* table = a.block_table + (long long)b * a.max_pages;
+  int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
   const int T_b = a.ctx_lens[b];
   const bool has_block = c == a.nc - 1;
-  const int chunk = context_chunk(T_b, a.nc);
-  const int kbeg = min(c * chunk, T_b);
-  const int kend = min(kbeg + chunk, T_b);
+  const int kbeg = min(kbeg0, T_b);
+  const int kend = min(kbeg0 + a.chunk, T_b);
 
   // Block keys/values of the last chunk's workgroup, fp32 [b][g][16][d] keys and
   // [b][g][d][16] transposed values; loaded up front (so they travel with the first loads)
@@ -174,12 +174,12 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
   if (kend > kbeg) {
     const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
     const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
-    const int* table = a.block_table + (long long)b * a.max_pages;
     const int pg0 = kbeg / kPage;                     // chunks start on a page boundary
     const int npg = (kend - kbeg + kPage - 1) / kPage;
     const int nsteps = (kend - kbeg + 31) / 32;
-    // Physical page ids, 64 logical pages per window: lane i holds page window*64 + i.
-    int win = -1, pid = 0;
+    // Physical page ids, 64 logical pages per window: lane i holds page window*64 + i
+    // (window 0 was fetched at the start).
+    int win = 0;
     auto page_of = [&](int pi) -> int {
       if (pi / kWave != win) {
         win = pi / kWave;
@@ -303,9 +303,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   const int nq = a.n_q, nkv = a.n_kv;
   const int T_b = a.ctx_lens[b];
   const bool has_block = c == a.nc - 1;
-  const int chunk = context_chunk(T_b, a.nc);
-  const int kbeg = min(c * chunk, T_b);
-  const int kend = min(kbeg + chunk, T_b);
+  const int kbeg = min(c * a.chunk, T_b);
+  const int kend = min(kbeg + a.chunk, T_b);
   for (int idx = tid; idx < R * D; idx += kThreads) {
     const int r = idx / D, i = idx % D;
     const int hh = r / kBlock, j = r % kBlock;
@@ -528,7 +527,7 @@ static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
                                   hipStream_t stream) {
-  if (a.nc < 1 || a.nc > kAttnMaxChunks) return hipErrorInvalidValue;
+  if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk < 32 || a.chunk % 32) return hipErrorInvalidValue;
   hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
   if (e != hipSuccess) return e;
   dim3 grid(a.n_q, a.head_dim / 32, batch);

@@ -652,6 +652,13 @@ __global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
 // ------------------------------------------------------------------------------------------
 template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 static hipError_t go(const GemmParams& p, int layers, hipStream_t stream) {
+  // The shape must fit the kernel's static resources: workgroup size bound, LDS reduction
+  // slots and the epilogue tile; every tile group must be whole.
+  const int waves = p.ksub * p.tgpw;
+  if (p.ksub < 1 || p.tgpw < 1 || waves > kMaxWaves || waves * NPW * MT > kRedSlots ||
+      MT * 16 * (p.tgpw * NPW * 16 + 1) > kTileFloats || p.n_tiles % (p.tgpw * NPW) != 0 ||
+      (NPW >= 8 && waves * kWave > 256))
+    return hipErrorInvalidValue;
   dim3 grid(p.n_tiles / (p.tgpw * NPW) * p.n_mblocks, 1, layers);
   dim3 block(kWave * p.ksub * p.tgpw);
   gemm_stream<T, AK, MT, NPW, EPI, NORM><<<grid, block, 0, stream>>>(p);
@@ -727,15 +734,16 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
   return hipErrorInvalidValue;
 }
 
-// One wave per row: lanes take the parts in strides, then a wave-wide maximum.
+// One 256-thread workgroup per row: threads take the parts in strides (8 loads in flight
+// each), then a wave-wide and a workgroup-wide maximum.
 __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* keys,
                                                               int parts, int keys_ld, int* ids,
                                                               int rows, int draft_rows) {
-  const int lane = threadIdx.x % kWave;
-  const int m = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (m >= rows) return;
+  __shared__ unsigned long long red[256 / kWave];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
   unsigned long long best = 0;
-  for (int q = lane; q < parts; q += kWave) {
+#pragma unroll 8
+  for (int q = tid; q < parts; q += 256) {
     const unsigned long long k = keys[(long long)q * keys_ld + m];
     best = k > best ? k : best;
   }
@@ -744,7 +752,10 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
     const unsigned long long other = __shfl_xor(best, o, kWave);
     best = other > best ? other : best;
   }
-  if (lane != 0) return;
+  if (lane == 0) red[tid / kWave] = best;
+  __syncthreads();
+  if (tid != 0) return;
+  for (int w = 1; w < 256 / kWave; ++w) best = red[w] > best ? red[w] : best;
   const int idx = argmax_key_index(best);
   if (!draft_rows) ids[m] = idx;
   else if (m % kBlock != 0) ids[(m / kBlock) * kDrafts + m % kBlock - 1] = idx;
@@ -752,8 +763,8 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
 
 hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int keys_ld,
                                   int* ids, int rows, int draft_rows, hipStream_t stream) {
-  argmax_finalize_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(keys, parts, keys_ld, ids, rows,
-                                                            draft_rows);
+  argmax_finalize_kernel<<<rows, 256, 0, stream>>>(keys, parts, keys_ld, ids, rows,
+                                                  draft_rows);
   return hipGetLastError();
 }
 
