@@ -19,12 +19,9 @@ using namespace dflash;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kCounterBytes = 256 * 1024;           // 65536 32-bit counters
-constexpr size_t kKeyStride = 128;                     // bytes between argmax keys
-constexpr size_t kKeyBytes = 768 * 1024;               // 6144 argmax rows
-constexpr size_t kSyncBytes = kCounterBytes + kKeyBytes;
-constexpr int kMaxCounters = (int)(kCounterBytes / 4) - 1;  // last one: argmax done counter
-constexpr int kMaxArgmaxRows = (int)(kKeyBytes / kKeyStride);
+constexpr size_t kSyncBytes = kAlign;                  // reserved head of a workspace
+constexpr int kMaxBatch = 4096;                         // requests per draft call
+constexpr int kMaxPagesPerSeq = kAttnMaxChunks * kAttnMaxChunkKeys / 16;
 constexpr int kTargetWaves = 2048;
 constexpr int kAttnTargetWGs = 256;
 
@@ -245,7 +242,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   // batch, and chunks of at most ~512 keys for long contexts so that ragged batches balance.
   const int want = std::max(cdiv(kAttnTargetWGs, kv_groups),
                             std::min(cdiv(std::max(max_ctx, 1), 512), 64));
-  p.nc = std::max(1, std::min({want, max_chunks, kAttnMaxChunks}));
+  p.nc = std::max({1, std::min({want, max_chunks, kAttnMaxChunks}),
+                   cdiv(std::max(max_ctx, 1), kAttnMaxChunkKeys)});
   p.chunk = cdiv(cdiv(std::max(max_ctx, 1), p.nc), 32) * 32;
   Carver c(kSyncBytes);
   p.x = c.take((size_t)rows * m.H * 4);
@@ -500,7 +498,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
   if (!packed || !embed || !anchor_ids || !draft_ids || !workspace || batch <= 0)
     return DFLASH_ERR_INVALID_ARG;
-  if (batch * 16 > kMaxArgmaxRows || batch * m.nkv > kMaxCounters) return DFLASH_ERR_UNSUPPORTED;
+  if (batch > kMaxBatch || cache->max_pages_per_seq > kMaxPagesPerSeq)
+    return DFLASH_ERR_UNSUPPORTED;
   const int max_ctx = cache->max_pages_per_seq * 16;
   const DraftPlan dp = draft_plan(m, batch, max_ctx);
   if (ws_bytes < dp.total) return DFLASH_ERR_WORKSPACE;
@@ -618,7 +617,7 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   dflash_status st = check_config(cfg, &m);
   if (st != DFLASH_OK) return st;
   if (!packed || !hidden || !ids_out || !workspace || rows <= 0) return DFLASH_ERR_INVALID_ARG;
-  if (rows > kMaxArgmaxRows) return DFLASH_ERR_UNSUPPORTED;
+  if (rows > kMaxBatch * 16) return DFLASH_ERR_UNSUPPORTED;
   // The rows are first rewritten into the fragment layout, in the area a draft step keeps
   // its residual stream, so the LM head runs exactly the draft step's kernel.
   const size_t frag_bytes = align_up((size_t)cdiv(rows, 16) * 16 * m.H * 4);

@@ -5,7 +5,8 @@
 
 namespace dflash {
 
-constexpr int kAttnMaxChunks = 256;   // context chunks per (request, KV group)
+constexpr int kAttnMaxChunks = 256;       // context chunks per (request, KV group)
+constexpr int kAttnMaxChunkKeys = 1024;   // keys per chunk (64 pages)
 
 struct AttnArgs {
   const float* q;          // [B*16][n_q][d], RoPE applied

@@ -3,9 +3,10 @@
 // the 16 block keys.
 //
 // Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
-// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32 fixed by the caller, so the page
-// ids of a chunk can be fetched before T_b arrives), and the last workgroup also the 16
-// block keys (so a grid of nc * n_kv * batch workgroups fills the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
+// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most 1024, fixed by the
+// caller, so the page ids of a chunk are one load per lane issued before T_b arrives), and
+// the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
+// the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
 // online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
 // Pass 2 (merge), grid (n_q, d / 32, batch): rescales the nc partials of each head to a
 // common maximum and divides by the total sum, chunks in order, so results do not depend on
@@ -73,6 +74,33 @@ __device__ inline i32x4 mask_vt(i32x4 v, int q, int nk) {
   return __builtin_bit_cast(i32x4, e);
 }
 
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Scores are kept in base-2 units: the queries are scaled by log2(e) / sqrt(d), so every
+// exponential is a plain exp2 and partial maxima m are log2-scaled (the merge uses exp2 too).
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Maximum / sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48):
+// each row-swap permute hands every lane its partner row's value, so after the 16- and the
+// 32-lane swap every lane holds the same result (both operands of each step commute).
+__device__ inline float rows_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ inline float rows_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // ------------------------------------------------------------------------------------------
 // bf16: MFMA partial kernel, one wave per query head of the group
 // ------------------------------------------------------------------------------------------
@@ -84,54 +112,98 @@ struct StepRegs {
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
-  constexpr int KS = D / 32;            // dim steps of S^T
-  constexpr int DT = D / 16;            // dim tiles of O^T
+__global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
+  constexpr int KS = D / 32;                  // dim steps of S^T
+  constexpr int DT = D / 16;                  // dim tiles of O^T
+  constexpr int kBlockBytes = kBlock * D * 4; // the block's K, or its V^T, in fp32
+  constexpr int kCopies = 2 * kBlockBytes / 1024;   // 1 KB (64 lanes x 16 B) per copy
+  static_assert(kCopies % G == 0, "block copies split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlockBytes];   // K, then V^T
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int n = lane & 15, q = lane >> 4;
   const int nq = a.n_q, nkv = a.n_kv;
-  // Physical page ids of the chunk's first 64 logical pages (lane i: page i), fetched
+  // Physical page ids of the chunk's (at most 64) logical pages (lane i: page i), fetched
   // together with T_b; indices are clamped into the table row.
   const int kbeg0 = c * a.chunk;
   const int* table = a.block_table + (long long)b * a.max_pages;
-  int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
+  const int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
   const int T_b = a.ctx_lens[b];
   const bool has_block = c == a.nc - 1;
   const int kbeg = min(kbeg0, T_b);
   const int kend = min(kbeg0 + a.chunk, T_b);
 
-  // Block keys/values of the last chunk's workgroup, fp32 [b][g][16][d] keys and
-  // [b][g][d][16] transposed values; loaded up front (so they travel with the first loads)
-  // unless the workgroup is too large to keep them in registers.
-  constexpr bool kEarlyBlock = G * kWave <= 256;
-  f32x4 bkr[KS][2], bvr[DT];
-  auto load_block = [&]() {
-    const float* kb = a.bk + ((long long)(b * nkv + g) * kBlock + n) * D + q * 8;
-    const float* vb = a.bv + ((long long)(b * nkv + g) * D + n) * kBlock + q * 4;
+  // The last chunk's workgroup copies the block's fp32 keys [16][d] and transposed values
+  // [d][16] (contiguous per KV group) into LDS with direct loads, which need no registers.
+  // The other workgroups issue the same copies from the first kilobyte of the arrays (and
+  // never read them), so that every wave's load count is the same on every path.
+  {
+    const long long grp = has_block ? (long long)(b * nkv + g) * kBlockBytes : 0;
+    const char* srck = reinterpret_cast<const char*>(a.bk) + grp;
+    const char* srcv = reinterpret_cast<const char*>(a.bv) + grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bkr[ks][0] = *reinterpret_cast<const f32x4*>(kb + ks * 32);
-      bkr[ks][1] = *reinterpret_cast<const f32x4*>(kb + ks * 32 + 4);
+    for (int j = 0; j < kCopies / G; ++j) {
+      const int i = hh + j * G;
+      const int half = i / (kCopies / 2), off = (i % (kCopies / 2)) * 1024;
+      const char* src = (half ? srcv : srck) + (has_block ? off : 0) + lane * 16;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src,
+                                       (lds_void_ptr)(blk_s + half * kBlockBytes + off), 16, 0,
+                                       0);
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) bvr[dt] = *reinterpret_cast<const f32x4*>(vb + dt * 16 * kBlock);
-  };
-  if (kEarlyBlock && has_block) load_block();
+  }
+  // Issue all of the above before the page ids are waited for (the compiler waits for every
+  // outstanding load once a direct-to-LDS load is pending, so that first wait retires them).
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Q^T fragments (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8,
-  // scaled by 1/sqrt(d) and split hi/lo.
-  i32x4 qf[KS][2];
+  // Q^T rows of this head (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8.
+  f32x4 qraw[KS][2];
   {
     const float* src = a.q + ((long long)(b * kBlock + n) * nq + g * G + hh) * D + q * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + ks * 32);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
-      const float f[8] = {v0[0] * a.scale, v0[1] * a.scale, v0[2] * a.scale, v0[3] * a.scale,
-                          v1[0] * a.scale, v1[1] * a.scale, v1[2] * a.scale, v1[3] * a.scale};
-      split8(f, qf[ks][0], qf[ks][1]);
+      qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
+      qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
     }
+  }
+
+  const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
+  const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
+  const int npg = (kend - kbeg + kPage - 1) / kPage;   // 0..64 (chunk <= 1024 keys)
+  const int nsteps = (kend - kbeg + 31) / 32;
+  // Step st reads logical pages 2st and 2st+1 of the chunk, whose physical ids lanes 2st
+  // and 2st+1 of `pid` hold; a page past the chunk's last is read from the last one (its
+  // keys are masked).  Every step issues the same loads with no branch, so the compiler
+  // can wait for one step's loads while the next step's stay in flight.
+  const int pid_safe = npg > 0 ? pid : 0;
+  auto load_step = [&](int st, StepRegs<D>& r) {
+    r.nk = min(32, kend - kbeg - 32 * st);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const long long page =
+          __builtin_amdgcn_readlane(pid_safe, max(min(2 * st + pg, npg - 1), 0));
+      const bf16* kp = kpool + ((page * nkv + g) * kPage + n) * D + q * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = *reinterpret_cast<const i32x4*>(kp + ks * 32);
+      const bf16* vp = vpool + ((page * nkv + g) * D + n) * kPage + q * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        r.v[dt][pg] = *reinterpret_cast<const i32x2*>(vp + dt * 16 * kPage);
+    }
+  };
+  // Two register sets: while one step's math runs, the next step's loads are in flight.
+  StepRegs<D> ra, rb;
+  load_step(0, ra);
+  load_step(min(1, max(nsteps - 1, 0)), rb);
+  __builtin_amdgcn_sched_barrier(0);   // keep every prologue load ahead of the math below
+
+  // Q^T fragments, scaled by log2(e) / sqrt(d) and split hi/lo.
+  i32x4 qf[KS][2];
+  const float qscale = a.scale * kLog2e;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const f32x4 v0 = qraw[ks][0] * qscale, v1 = qraw[ks][1] * qscale;
+    const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    split8(f, qf[ks][0], qf[ks][1]);
   }
 
   f32x4 o[DT];
@@ -139,115 +211,89 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Online-softmax update for one 32-key step given S^T tiles s[2]; returns the P^T
-  // fragment (hi, lo).
+  // Online-softmax update for one 32-key step given S^T tiles s[2] (lane: keys
+  // 16 pg + 4q + i for query n); returns the P^T fragment (hi, lo).  The accumulator is
+  // rescaled only when some row's maximum grew (a branch uniform over the wave).
   auto softmax_step = [&](const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
     float x[8];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
+    for (int e = 0; e < 8; ++e) x[e] = s[e / 4][e % 4];
+    if (nk < 32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = 16 * pg + 4 * q + i < nk;
-        x[pg * 4 + i] = valid ? s[pg][i] : -INFINITY;
-        mx = fmaxf(mx, x[pg * 4 + i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);     // finite: every step has a valid key
+      for (int e = 0; e < 8; ++e)
+        if (16 * (e / 4) + 4 * q + e % 4 >= nk) x[e] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float m_new = fmaxf(m_run, rows_max(mx));   // finite: key 0 of a step is valid
+    if (__ballot(m_new > m_run)) {
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+      m_run = m_new;
+    }
     float pv[8], ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = x[e] == -INFINITY ? 0.f : expf(x[e] - m_new);
-      ps += pv[e];
-    }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    const float corr = expf(m_run - m_new);   // 0 on the first step
-    l_run = l_run * corr + ps;
-    m_run = m_new;
+    for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
+    if (nk < 32) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+      for (int e = 0; e < 8; ++e)
+        if (16 * (e / 4) + 4 * q + e % 4 >= nk) pv[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ps += pv[e];
+    l_run += rows_sum(ps);
     split8(pv, p_hi, p_lo);
   };
 
-  if (kend > kbeg) {
-    const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
-    const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
-    const int pg0 = kbeg / kPage;                     // chunks start on a page boundary
-    const int npg = (kend - kbeg + kPage - 1) / kPage;
-    const int nsteps = (kend - kbeg + 31) / 32;
-    // Physical page ids, 64 logical pages per window: lane i holds page window*64 + i
-    // (window 0 was fetched at the start).
-    int win = 0;
-    auto page_of = [&](int pi) -> int {
-      if (pi / kWave != win) {
-        win = pi / kWave;
-        const int li = win * kWave + lane;
-        pid = li < npg ? table[pg0 + li] : 0;
-      }
-      return __builtin_amdgcn_readlane(pid, pi % kWave);
-    };
-    auto load_step = [&](int st, StepRegs<D>& r) {
-      r.nk = min(32, kend - kbeg - 32 * st);
+  auto compute_step = [&](const StepRegs<D>& r) {
+    // Q hi and Q lo products accumulate separately: four independent MFMA chains.
+    f32x4 sh[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 sl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
-        if (16 * pg < r.nk) {
-          const long long page = page_of(2 * st + pg);
-          const bf16* kp = kpool + ((page * nkv + g) * kPage + n) * D + q * 8;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = *reinterpret_cast<const i32x4*>(kp + ks * 32);
-          const bf16* vp = vpool + ((page * nkv + g) * D + n) * kPage + q * 4;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            r.v[dt][pg] = *reinterpret_cast<const i32x2*>(vp + dt * 16 * kPage);
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = i32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) r.v[dt][pg] = i32x2{0, 0};
-        }
+        sh[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][0], sh[pg]);
+        sl[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][1], sl[pg]);
       }
-    };
-    auto compute_step = [&](const StepRegs<D>& r) {
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const f32x4 s[2] = {sh[0] + sl[0], sh[1] + sl[1]};
+    i32x4 ph, pl;
+    softmax_step(s, r.nk, ph, pl);
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][0], s[pg]);
-          s[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][1], s[pg]);
-        }
-      i32x4 ph, pl;
-      softmax_step(s, r.nk, ph, pl);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        i32x4 v = i32x4{r.v[dt][0][0], r.v[dt][0][1], r.v[dt][1][0], r.v[dt][1][1]};
-        if (r.nk < 32) v = mask_vt(v, q, r.nk);   // stale cache slots may hold any bits
-        o[dt] = mfma_tile<bf16>(v, ph, o[dt]);
-        o[dt] = mfma_tile<bf16>(v, pl, o[dt]);
-      }
-    };
-    // Two steps in flight: the next step's loads are issued before this step's math.
-    StepRegs<D> ra, rb;
-    load_step(0, ra);
-    for (int st = 0; st < nsteps; st += 2) {
-      if (st + 1 < nsteps) load_step(st + 1, rb);
-      compute_step(ra);
-      if (st + 1 < nsteps) {
-        if (st + 2 < nsteps) load_step(st + 2, ra);
-        compute_step(rb);
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      i32x4 v = i32x4{r.v[dt][0][0], r.v[dt][0][1], r.v[dt][1][0], r.v[dt][1][1]};
+      if (r.nk < 32) v = mask_vt(v, q, r.nk);   // stale cache slots may hold any bits
+      o[dt] = mfma_tile<bf16>(v, ph, o[dt]);
+      o[dt] = mfma_tile<bf16>(v, pl, o[dt]);
     }
+  };
+  // Steady state: ra holds step st, rb step st + 1, and both prefetches exist.
+  int st = 0;
+  for (; st + 3 < nsteps; st += 2) {
+    compute_step(ra);
+    load_step(st + 2, ra);
+    compute_step(rb);
+    load_step(st + 3, rb);
   }
+  // 0..3 steps remain.
+  if (st < nsteps) compute_step(ra);
+  if (st + 2 < nsteps) load_step(st + 2, ra);
+  if (st + 1 < nsteps) compute_step(rb);
+  if (st + 2 < nsteps) compute_step(ra);
 
-  if (has_block) {   // the 16 block keys, hi + lo on both operands
-    if (!kEarlyBlock) load_block();
+  if (has_block) {   // the 16 block keys, hi + lo on both operands, from LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const float* bk_s = reinterpret_cast<const float*>(blk_s);
+    const float* bv_s = reinterpret_cast<const float*>(blk_s + kBlockBytes);
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float f[8] = {bkr[ks][0][0], bkr[ks][0][1], bkr[ks][0][2], bkr[ks][0][3],
-                          bkr[ks][1][0], bkr[ks][1][1], bkr[ks][1][2], bkr[ks][1][3]};
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(bk_s + n * D + ks * 32 + q * 8);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(bk_s + n * D + ks * 32 + q * 8 + 4);
+      const float f[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
       i32x4 kh, kl;
       split8(f, kh, kl);
       s[0] = mfma_tile<bf16>(kh, qf[ks][0], s[0]);
@@ -258,7 +304,8 @@ __global__ __launch_bounds__(G * kWave) void attn_partial_bf16(AttnArgs a) {
     softmax_step(s, kBlock, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const float f[8] = {bvr[dt][0], bvr[dt][1], bvr[dt][2], bvr[dt][3], 0.f, 0.f, 0.f, 0.f};
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(bv_s + (16 * dt + n) * kBlock + q * 4);
+      const float f[8] = {vv[0], vv[1], vv[2], vv[3], 0.f, 0.f, 0.f, 0.f};
       i32x4 vh, vl;
       split8(f, vh, vl);
       o[dt] = mfma_tile<bf16>(vh, ph, o[dt]);
@@ -303,12 +350,13 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   const int nq = a.n_q, nkv = a.n_kv;
   const int T_b = a.ctx_lens[b];
   const bool has_block = c == a.nc - 1;
+  const float qscale = a.scale * kLog2e;   // base-2 scores, as in the MFMA kernel
   const int kbeg = min(c * a.chunk, T_b);
   const int kend = min(kbeg + a.chunk, T_b);
   for (int idx = tid; idx < R * D; idx += kThreads) {
     const int r = idx / D, i = idx % D;
     const int hh = r / kBlock, j = r % kBlock;
-    q_s[r][i] = a.q[((long long)(b * kBlock + j) * nq + g * G + hh) * D + i] * a.scale;
+    q_s[r][i] = a.q[((long long)(b * kBlock + j) * nq + g * G + hh) * D + i] * qscale;
   }
   if (tid < R) {
     m_s[tid] = -INFINITY;
@@ -363,10 +411,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
       const float mold = m_s[tid];
       float mx = mold;
       for (int cc = 0; cc < nk; ++cc) mx = fmaxf(mx, p_s[tid][cc]);
-      const float sc = expf(mold - mx);
+      const float sc = exp2f(mold - mx);
       float l = l_s[tid] * sc;
       for (int cc = 0; cc < kKeys; ++cc) {
-        const float pe = cc < nk ? expf(p_s[tid][cc] - mx) : 0.f;
+        const float pe = cc < nk ? exp2f(p_s[tid][cc] - mx) : 0.f;
         p_s[tid][cc] = pe;
         l += pe;
       }
@@ -455,7 +503,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
   float lsum = 0.f;
   for (int c = cl; c < nch; c += NCL) {
     const float mm = m_s[c][j];
-    const float w = mm == -INFINITY ? 0.f : expf(mm - M_s[j]);
+    const float w = mm == -INFINITY ? 0.f : exp2f(mm - M_s[j]);
     lsum += w_s[c][j] * w;
     w_s[c][j] = w;
   }
@@ -527,7 +575,9 @@ static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
                                   hipStream_t stream) {
-  if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk < 32 || a.chunk % 32) return hipErrorInvalidValue;
+  if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk < 32 || a.chunk % 32 ||
+      a.chunk > kAttnMaxChunkKeys)
+    return hipErrorInvalidValue;
   hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
   if (e != hipSuccess) return e;
   dim3 grid(a.n_q, a.head_dim / 32, batch);

@@ -141,8 +141,9 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
 size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
                              int32_t max_inject_rows, int32_t max_ctx);
 
-/* Zero the synchronization area at the head of a new workspace.  Must be called once
- * after the workspace is allocated; the step calls leave that area zeroed again. */
+/* Prepare a new workspace (zeroes its 256-byte reserved head).  Must be called once after
+ * the workspace is allocated; no step call needs the workspace's contents to survive
+ * between calls. */
 dflash_status dflash_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Feature fusion + KV injection.
@@ -165,7 +166,9 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
  *              fp32 ties resolved to the lowest id.
  *   logits_out [batch, 15, V] fp32 out, may be NULL: the LM-head logits of slots 1..15.
  * Slot j of request b sits at position ctx_lens[b] + j and attends, without a mask, to
- * the ctx_lens[b] cached context entries and the 16 block slots. */
+ * the ctx_lens[b] cached context entries and the 16 block slots.
+ * DFLASH_ERR_UNSUPPORTED if batch > 4096 or the cache's max_pages_per_seq > 16384
+ * (262144 positions: at most 256 attention chunks of at most 1024 keys). */
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
@@ -180,7 +183,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
  * `workspace`: a step workspace initialized with dflash_workspace_init and sized by
  * dflash_workspace_size for max_batch >= ceil(rows / 16); the rows are copied into the
  * fragment layout there, then the draft step's LM-head kernels run on them.
- * DFLASH_ERR_WORKSPACE if it is smaller. */
+ * DFLASH_ERR_WORKSPACE if it is smaller; DFLASH_ERR_UNSUPPORTED if rows > 65536. */
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
                                     const float* hidden, int32_t rows, int32_t* ids_out,
                                     float* logits_out, void* workspace, size_t ws_bytes,
