@@ -23,7 +23,7 @@ constexpr size_t kSyncBytes = kAlign;                  // reserved head of a wor
 constexpr int kMaxBatch = 4096;                         // requests per draft call
 constexpr int kMaxPagesPerSeq = kAttnMaxChunks * kAttnMaxChunkKeys / 16;
 constexpr int kTargetWaves = 2048;
-constexpr int kAttnTargetWGs = 256;
+constexpr int kAttnTargetWGs = 128;   // context-chunk workgroups wanted at small batch
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }

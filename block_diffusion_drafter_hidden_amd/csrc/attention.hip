@@ -102,119 +102,41 @@ __device__ inline float rows_sum(float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16: MFMA partial kernel, one wave per query head of the group
+// bf16 MFMA partials.  One wave per query head of the group; the per-head state and the
+// math of one 32-key step are shared by two kernels that differ in how K/V reach the wave:
+//   attn_partial_bf16  (G <= 2): every wave loads its step fragments straight from the
+//                      paged cache into registers;
+//   attn_partial_lds   (G >= 4): the workgroup loads each step once, as coalesced 16-byte
+//                      pieces spread over all its threads, into an LDS double buffer that
+//                      the G head waves then read (G times less cache traffic).
 // ------------------------------------------------------------------------------------------
 template <int D>
-struct StepRegs {
-  i32x4 k[2][D / 32];      // two pages x dim steps
-  i32x2 v[D / 16][2];      // dim tiles x pages
-  int nk;                  // valid keys of the step (1..32)
-};
+struct HeadState {
+  static constexpr int KS = D / 32;   // dim steps of S^T
+  static constexpr int DT = D / 16;   // dim tiles of O^T
+  i32x4 qf[KS][2];                    // Q^T fragments (hi, lo), base-2 scaled
+  f32x4 o[DT];                        // O^T accumulator: dims 16dt + 4q + i of block row n
+  float m_run, l_run;
+  int q;                              // lane / 16
 
-template <int D, int G>
-__global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
-  constexpr int KS = D / 32;                  // dim steps of S^T
-  constexpr int DT = D / 16;                  // dim tiles of O^T
-  constexpr int kBlockBytes = kBlock * D * 4; // the block's K, or its V^T, in fp32
-  constexpr int kCopies = 2 * kBlockBytes / 1024;   // 1 KB (64 lanes x 16 B) per copy
-  static_assert(kCopies % G == 0, "block copies split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlockBytes];   // K, then V^T
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
-  const int n = lane & 15, q = lane >> 4;
-  const int nq = a.n_q, nkv = a.n_kv;
-  // Physical page ids of the chunk's (at most 64) logical pages (lane i: page i), fetched
-  // together with T_b; indices are clamped into the table row.
-  const int kbeg0 = c * a.chunk;
-  const int* table = a.block_table + (long long)b * a.max_pages;
-  const int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
-  const int T_b = a.ctx_lens[b];
-  const bool has_block = c == a.nc - 1;
-  const int kbeg = min(kbeg0, T_b);
-  const int kend = min(kbeg0 + a.chunk, T_b);
-
-  // The last chunk's workgroup copies the block's fp32 keys [16][d] and transposed values
-  // [d][16] (contiguous per KV group) into LDS with direct loads, which need no registers.
-  // The other workgroups issue the same copies from the first kilobyte of the arrays (and
-  // never read them), so that every wave's load count is the same on every path.
-  {
-    const long long grp = has_block ? (long long)(b * nkv + g) * kBlockBytes : 0;
-    const char* srck = reinterpret_cast<const char*>(a.bk) + grp;
-    const char* srcv = reinterpret_cast<const char*>(a.bv) + grp;
-#pragma unroll
-    for (int j = 0; j < kCopies / G; ++j) {
-      const int i = hh + j * G;
-      const int half = i / (kCopies / 2), off = (i % (kCopies / 2)) * 1024;
-      const char* src = (half ? srcv : srck) + (has_block ? off : 0) + lane * 16;
-      __builtin_amdgcn_global_load_lds((global_void_ptr)src,
-                                       (lds_void_ptr)(blk_s + half * kBlockBytes + off), 16, 0,
-                                       0);
-    }
-  }
-  // Issue all of the above before the page ids are waited for (the compiler waits for every
-  // outstanding load once a direct-to-LDS load is pending, so that first wait retires them).
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Q^T rows of this head (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8.
-  f32x4 qraw[KS][2];
-  {
-    const float* src = a.q + ((long long)(b * kBlock + n) * nq + g * G + hh) * D + q * 8;
+  __device__ void init(const f32x4 (&qraw)[KS][2], float qscale, int lane) {
+    q = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
-      qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
+      const f32x4 v0 = qraw[ks][0] * qscale, v1 = qraw[ks][1] * qscale;
+      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      split8(f, qf[ks][0], qf[ks][1]);
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
   }
-
-  const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
-  const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
-  const int npg = (kend - kbeg + kPage - 1) / kPage;   // 0..64 (chunk <= 1024 keys)
-  const int nsteps = (kend - kbeg + 31) / 32;
-  // Step st reads logical pages 2st and 2st+1 of the chunk, whose physical ids lanes 2st
-  // and 2st+1 of `pid` hold; a page past the chunk's last is read from the last one (its
-  // keys are masked).  Every step issues the same loads with no branch, so the compiler
-  // can wait for one step's loads while the next step's stay in flight.
-  const int pid_safe = npg > 0 ? pid : 0;
-  auto load_step = [&](int st, StepRegs<D>& r) {
-    r.nk = min(32, kend - kbeg - 32 * st);
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const long long page =
-          __builtin_amdgcn_readlane(pid_safe, max(min(2 * st + pg, npg - 1), 0));
-      const bf16* kp = kpool + ((page * nkv + g) * kPage + n) * D + q * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = *reinterpret_cast<const i32x4*>(kp + ks * 32);
-      const bf16* vp = vpool + ((page * nkv + g) * D + n) * kPage + q * 4;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        r.v[dt][pg] = *reinterpret_cast<const i32x2*>(vp + dt * 16 * kPage);
-    }
-  };
-  // Two register sets: while one step's math runs, the next step's loads are in flight.
-  StepRegs<D> ra, rb;
-  load_step(0, ra);
-  load_step(min(1, max(nsteps - 1, 0)), rb);
-  __builtin_amdgcn_sched_barrier(0);   // keep every prologue load ahead of the math below
-
-  // Q^T fragments, scaled by log2(e) / sqrt(d) and split hi/lo.
-  i32x4 qf[KS][2];
-  const float qscale = a.scale * kLog2e;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const f32x4 v0 = qraw[ks][0] * qscale, v1 = qraw[ks][1] * qscale;
-    const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    split8(f, qf[ks][0], qf[ks][1]);
-  }
-
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
 
   // Online-softmax update for one 32-key step given S^T tiles s[2] (lane: keys
   // 16 pg + 4q + i for query n); returns the P^T fragment (hi, lo).  The accumulator is
   // rescaled only when some row's maximum grew (a branch uniform over the wave).
-  auto softmax_step = [&](const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
+  __device__ void softmax(const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s[e / 4][e % 4];
@@ -223,8 +145,8 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
       for (int e = 0; e < 8; ++e)
         if (16 * (e / 4) + 4 * q + e % 4 >= nk) x[e] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float m_new = fmaxf(m_run, rows_max(mx));   // finite: key 0 of a step is valid
     if (__ballot(m_new > m_run)) {
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
@@ -245,9 +167,11 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
     for (int e = 0; e < 8; ++e) ps += pv[e];
     l_run += rows_sum(ps);
     split8(pv, p_hi, p_lo);
-  };
+  }
 
-  auto compute_step = [&](const StepRegs<D>& r) {
+  // One 32-key step: k[pg][ks] is the K fragment (16 keys of page pg x dims 32ks + 8q..+8),
+  // v[dt][pg] the V^T half-fragment (dim 16dt + n x keys 4q..4q+3 of page pg).
+  __device__ void step(const i32x4 (&k)[2][KS], const i32x2 (&v)[DT][2], int nk) {
     // Q hi and Q lo products accumulate separately: four independent MFMA chains.
     f32x4 sh[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 sl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -255,39 +179,26 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
-        sh[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][0], sh[pg]);
-        sl[pg] = mfma_tile<bf16>(r.k[pg][ks], qf[ks][1], sl[pg]);
+        sh[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][0], sh[pg]);
+        sl[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][1], sl[pg]);
       }
     const f32x4 s[2] = {sh[0] + sl[0], sh[1] + sl[1]};
     i32x4 ph, pl;
-    softmax_step(s, r.nk, ph, pl);
+    softmax(s, nk, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      i32x4 v = i32x4{r.v[dt][0][0], r.v[dt][0][1], r.v[dt][1][0], r.v[dt][1][1]};
-      if (r.nk < 32) v = mask_vt(v, q, r.nk);   // stale cache slots may hold any bits
-      o[dt] = mfma_tile<bf16>(v, ph, o[dt]);
-      o[dt] = mfma_tile<bf16>(v, pl, o[dt]);
+      i32x4 vv = i32x4{v[dt][0][0], v[dt][0][1], v[dt][1][0], v[dt][1][1]};
+      if (nk < 32) vv = mask_vt(vv, q, nk);   // stale cache slots may hold any bits
+      o[dt] = mfma_tile<bf16>(vv, ph, o[dt]);
+      o[dt] = mfma_tile<bf16>(vv, pl, o[dt]);
     }
-  };
-  // Steady state: ra holds step st, rb step st + 1, and both prefetches exist.
-  int st = 0;
-  for (; st + 3 < nsteps; st += 2) {
-    compute_step(ra);
-    load_step(st + 2, ra);
-    compute_step(rb);
-    load_step(st + 3, rb);
   }
-  // 0..3 steps remain.
-  if (st < nsteps) compute_step(ra);
-  if (st + 2 < nsteps) load_step(st + 2, ra);
-  if (st + 1 < nsteps) compute_step(rb);
-  if (st + 2 < nsteps) compute_step(ra);
 
-  if (has_block) {   // the 16 block keys, hi + lo on both operands, from LDS
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // The 16 block keys from LDS (fp32 K [16][D], then V^T [D][16]), hi + lo on both
+  // operands.
+  __device__ void block(const char* blk_s, int n) {
     const float* bk_s = reinterpret_cast<const float*>(blk_s);
-    const float* bv_s = reinterpret_cast<const float*>(blk_s + kBlockBytes);
+    const float* bv_s = reinterpret_cast<const float*>(blk_s + kBlock * D * 4);
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -301,7 +212,7 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
       s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
     }
     i32x4 ph, pl;
-    softmax_step(s, kBlock, ph, pl);
+    softmax(s, kBlock, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 vv = *reinterpret_cast<const f32x4*>(bv_s + (16 * dt + n) * kBlock + q * 4);
@@ -314,16 +225,296 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
     }
   }
 
-  // Partial of this chunk.  O^T layout: lane holds dims 16dt + 4q + i of block row n.
-  const long long slot = ((long long)b * nkv + g) * a.nc + c;
-  f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kBlock);
+  // Partial of this chunk (layout in the file header).
+  __device__ void store(const AttnArgs& a, long long slot, int G, int hh, int n) const {
+    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kBlock);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kBlock + n] = o[dt];
-  if (q == 0) {
-    float* ml = a.part_ml + ((slot * G + hh) * kBlock + n) * 2;
-    ml[0] = m_run;
-    ml[1] = l_run;
+    for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kBlock + n] = o[dt];
+    if (q == 0) {
+      float* ml = a.part_ml + ((slot * G + hh) * kBlock + n) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
+    }
   }
+};
+
+// Everything a partial workgroup needs before its first step: the chunk's key range, the
+// page ids (lane i: logical page i of the chunk, at most 64, clamped into the table row and
+// fetched together with T_b), the block K/V copied into LDS by the last chunk's workgroup,
+// and this wave's Q rows.
+template <int D>
+struct ChunkSetup {
+  int kbeg, kend, npg, nsteps, pid_safe;
+  bool has_block;
+};
+
+template <int D, int G>
+__device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
+                                            f32x4 (&qraw)[D / 32][2]) {
+  constexpr int kBlockBytes = kBlock * D * 4;        // the block's K, or its V^T, in fp32
+  constexpr int kCopies = 2 * kBlockBytes / 1024;    // 1 KB (64 lanes x 16 B) per copy
+  static_assert(kCopies % G == 0, "block copies split evenly over the waves");
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
+  const int n = lane & 15, q = lane >> 4;
+  ChunkSetup<D> cs;
+  const int kbeg0 = c * a.chunk;
+  const int* table = a.block_table + (long long)b * a.max_pages;
+  const int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
+  const int T_b = a.ctx_lens[b];
+  cs.has_block = c == a.nc - 1;
+  cs.kbeg = min(kbeg0, T_b);
+  cs.kend = min(kbeg0 + a.chunk, T_b);
+
+  // The last chunk's workgroup copies the block's fp32 keys [16][d] and transposed values
+  // [d][16] (contiguous per KV group) into LDS with direct loads, which need no registers.
+  // The other workgroups issue the same copies from the first kilobyte of the arrays (and
+  // never read them), so that every wave's load count is the same on every path.
+  {
+    const long long grp = cs.has_block ? (long long)(b * a.n_kv + g) * kBlockBytes : 0;
+    const char* srck = reinterpret_cast<const char*>(a.bk) + grp;
+    const char* srcv = reinterpret_cast<const char*>(a.bv) + grp;
+#pragma unroll
+    for (int j = 0; j < kCopies / G; ++j) {
+      const int i = hh + j * G;
+      const int half = i / (kCopies / 2), off = (i % (kCopies / 2)) * 1024;
+      const char* src = (half ? srcv : srck) + (cs.has_block ? off : 0) + lane * 16;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src,
+                                       (lds_void_ptr)(blk_s + half * kBlockBytes + off), 16, 0,
+                                       0);
+    }
+  }
+  // Issue all of the above before the page ids are waited for (the compiler waits for every
+  // outstanding load once a direct-to-LDS load is pending, so that first wait retires them).
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Q^T rows of this head (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8.
+  const float* src = a.q + ((long long)(b * kBlock + n) * a.n_q + g * G + hh) * D + q * 8;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
+    qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
+  }
+  cs.npg = (cs.kend - cs.kbeg + kPage - 1) / kPage;   // 0..64 (chunk <= 1024 keys)
+  cs.nsteps = (cs.kend - cs.kbeg + 31) / 32;
+  // A page past the chunk's last is read from the last one (its keys are masked), and an
+  // empty chunk reads physical page 0 and uses nothing.
+  cs.pid_safe = cs.npg > 0 ? pid : 0;
+  return cs;
+}
+
+// Physical page of the chunk's logical page li (wave-uniform li), clamped as above.
+template <int D>
+__device__ inline long long chunk_page(const ChunkSetup<D>& cs, int li) {
+  return __builtin_amdgcn_readlane(cs.pid_safe, max(min(li, cs.npg - 1), 0));
+}
+
+template <int D>
+struct StepRegs {
+  i32x4 k[2][D / 32];      // two pages x dim steps
+  i32x2 v[D / 16][2];      // dim tiles x pages
+  int nk;                  // valid keys of the step (1..32)
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
+  constexpr int KS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlock * D * 4];   // K, then V^T
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
+  const int n = lane & 15, q = lane >> 4;
+  const int nkv = a.n_kv;
+  f32x4 qraw[KS][2];
+  const ChunkSetup<D> cs = chunk_setup<D, G>(a, blk_s, qraw);
+
+  const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
+  const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
+  // Step st reads logical pages 2st and 2st+1 of the chunk.  Every step issues the same
+  // loads with no branch, so the compiler can wait for one step's loads while the next
+  // step's stay in flight.
+  auto load_step = [&](int st, StepRegs<D>& r) {
+    r.nk = min(32, cs.kend - cs.kbeg - 32 * st);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const long long page = chunk_page(cs, 2 * st + pg);
+      const bf16* kp = kpool + ((page * nkv + g) * kPage + n) * D + q * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) r.k[pg][ks] = *reinterpret_cast<const i32x4*>(kp + ks * 32);
+      const bf16* vp = vpool + ((page * nkv + g) * D + n) * kPage + q * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        r.v[dt][pg] = *reinterpret_cast<const i32x2*>(vp + dt * 16 * kPage);
+    }
+  };
+  // Two register sets: while one step's math runs, the next step's loads are in flight.
+  StepRegs<D> ra, rb;
+  load_step(0, ra);
+  load_step(min(1, max(cs.nsteps - 1, 0)), rb);
+  __builtin_amdgcn_sched_barrier(0);   // keep every prologue load ahead of the math below
+
+  HeadState<D> hs;
+  hs.init(qraw, a.scale * kLog2e, lane);
+  const int nsteps = cs.nsteps;
+  // Steady state: ra holds step st, rb step st + 1, and both prefetches exist.
+  int st = 0;
+  for (; st + 3 < nsteps; st += 2) {
+    hs.step(ra.k, ra.v, ra.nk);
+    load_step(st + 2, ra);
+    hs.step(rb.k, rb.v, rb.nk);
+    load_step(st + 3, rb);
+  }
+  // 0..3 steps remain.
+  if (st < nsteps) hs.step(ra.k, ra.v, ra.nk);
+  if (st + 2 < nsteps) load_step(st + 2, ra);
+  if (st + 1 < nsteps) hs.step(rb.k, rb.v, rb.nk);
+  if (st + 2 < nsteps) hs.step(ra.k, ra.v, ra.nk);
+
+  if (cs.has_block) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    hs.block(blk_s, n);
+  }
+  hs.store(a, ((long long)blockIdx.z * nkv + g) * a.nc + blockIdx.x, G, hh, n);
+}
+
+// ------------------------------------------------------------------------------------------
+// LDS-staged variant (G >= 4).  A step (two pages of K and of V, 128 d bytes) is loaded as
+// 16-byte pieces, d / (8 G) per thread: piece p of the step (p = j * 64G + thread) is bytes
+// 16 (p mod 2d) .. +16 of quarter p / 2d, the quarters being K page 0, K page 1, V page 0
+// and V page 1 (32 d bytes each, contiguous in the cache).  Pieces are staged in registers RS steps
+// ahead and written to an LDS double buffer, XOR-swizzled so that the fragment reads hit
+// distinct banks:
+//   K row r (2d bytes): 16-byte piece j sits at piece j ^ swz(r), swz(r) = r & 15 (d = 128)
+//                       or (r >> 1) & 7 (d = 64);
+//   V row `dim` (32 bytes, keys 0..15): 16-byte half h sits at half h ^ ((dim >> 3) & 1).
+// One barrier per step: after it, the stage holding step t is complete and every wave has
+// finished reading step t - 1, whose stage the step-(t + 1) pieces then overwrite.
+// ------------------------------------------------------------------------------------------
+template <int D, int G>
+struct LdsStep {
+  static constexpr int kStepBytes = 128 * D;              // K + V of 32 keys
+  static constexpr int kQuarter = 32 * D;                 // one page of K or of V
+  static constexpr int kPieces = kStepBytes / 16;
+  static constexpr int kThreads = G * kWave;
+  static constexpr int NL = kPieces / kThreads;           // 16-byte loads per thread
+  static_assert(kPieces % kThreads == 0, "pieces split evenly over the threads");
+  static_assert((2 * D) % kWave == 0, "a wave's 64 pieces stay inside one quarter");
+};
+
+template <int D>
+__device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int D, int G>
+__global__ __launch_bounds__(G * kWave, 2) void attn_partial_lds(
+    AttnArgs a) {
+  using L = LdsStep<D, G>;
+  constexpr int KS = D / 32, DT = D / 16, NL = L::NL;
+  constexpr int RS = 4;                                   // register stages (steps ahead)
+  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlock * D * 4];
+  __shared__ __attribute__((aligned(16))) char kv_s[2][L::kStepBytes];
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid % kWave, hh = tid / kWave;
+  const int n = lane & 15, q = lane >> 4;
+  const int nkv = a.n_kv;
+  f32x4 qraw[KS][2];
+  const ChunkSetup<D> cs = chunk_setup<D, G>(a, blk_s, qraw);
+  const int nsteps = cs.nsteps;
+
+  // Static description of this thread's pieces: quarter (page, K or V), source byte offset
+  // inside the page's K or V block, and LDS byte offset inside a stage.
+  int src_off[NL], dst_off[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int p = j * L::kThreads + tid;
+    const int quarter = p / (2 * D), e = p % (2 * D);
+    int dst;
+    if (quarter < 2) {                  // K: row r, piece jj
+      const int r = e / (D / 8), jj = e % (D / 8);
+      src_off[j] = e * 16;
+      dst = r * 2 * D + ((jj ^ k_swz<D>(r)) * 16);
+    } else {                            // V^T: row dim, half h
+      const int dim = e / 2, h = e % 2;
+      src_off[j] = e * 16;
+      dst = dim * 32 + ((h ^ ((dim >> 3) & 1)) * 16);
+    }
+    dst_off[j] = quarter * L::kQuarter + dst;
+  }
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  auto load_pieces = [&](int st, i32x4 (&r)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      // quarter is uniform over the wave (a wave's 64 pieces lie inside one quarter)
+      const int quarter = (j * L::kThreads + hh * kWave) / (2 * D);
+      const long long page = chunk_page(cs, 2 * st + (quarter & 1));
+      const char* base = (quarter < 2 ? kbase : vbase) + (page * nkv + g) * (long long)L::kQuarter;
+      r[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + src_off[j]));
+    }
+  };
+  auto store_pieces = [&](int stage, const i32x4 (&r)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) *reinterpret_cast<i32x4*>(kv_s[stage] + dst_off[j]) = r[j];
+  };
+  // Fragments of one step from a stage (layouts as in attn_partial_bf16).
+  auto compute = [&](HeadState<D>& hs, int stage, int st) {
+    const char* sb = kv_s[stage];
+    i32x4 k[2][KS];
+    i32x2 v[DT][2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        k[pg][ks] = *reinterpret_cast<const i32x4*>(
+            sb + pg * L::kQuarter + n * 2 * D + (((ks * 4 + q) ^ k_swz<D>(n)) * 16));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dim = 16 * dt + n;
+        v[dt][pg] = *reinterpret_cast<const i32x2*>(
+            sb + (2 + pg) * L::kQuarter + dim * 32 + ((q ^ (((dim >> 3) & 1) * 2)) * 8));
+      }
+    }
+    hs.step(k, v, min(32, cs.kend - cs.kbeg - 32 * st));
+  };
+
+  i32x4 rs[RS][NL];
+  // Prologue: steps 0 .. RS-1 in flight (with no branch: a step past the last repeats it),
+  // step 0 staged.
+#pragma unroll
+  for (int s = 0; s < RS; ++s) load_pieces(min(s, max(nsteps - 1, 0)), rs[s]);
+  __builtin_amdgcn_sched_barrier(0);
+  HeadState<D> hs;
+  hs.init(qraw, a.scale * kLog2e, lane);
+  if (nsteps > 0) store_pieces(0, rs[0]);
+  __syncthreads();
+
+  // Steady state, RS steps per trip: every load issued here is of a real step.
+  int t = 0;
+  for (; t + 2 * RS <= nsteps; t += RS) {
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      load_pieces(t + i + RS, rs[i]);
+      compute(hs, i & 1, t + i);
+      store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
+      __syncthreads();
+    }
+  }
+  // Tail: fewer than 2 RS steps remain; step t + i is in register set i % RS.
+#pragma unroll
+  for (int i = 0; i < 2 * RS - 1; ++i) {
+    if (t + i < nsteps) {
+      if (i < RS && t + i + RS < nsteps) load_pieces(t + i + RS, rs[i % RS]);
+      compute(hs, i & 1, t + i);
+      if (t + i + 1 < nsteps) store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
+      __syncthreads();
+    }
+  }
+
+  if (cs.has_block) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    hs.block(blk_s, n);
+  }
+  hs.store(a, ((long long)blockIdx.z * nkv + g) * a.nc + blockIdx.x, G, hh, n);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -545,8 +736,8 @@ static void launch_partial_bf16(int G, dim3 grid, const AttnArgs& a, hipStream_t
   switch (G) {
     case 1: attn_partial_bf16<D, 1><<<grid, 1 * kWave, 0, stream>>>(a); break;
     case 2: attn_partial_bf16<D, 2><<<grid, 2 * kWave, 0, stream>>>(a); break;
-    case 4: attn_partial_bf16<D, 4><<<grid, 4 * kWave, 0, stream>>>(a); break;
-    case 8: attn_partial_bf16<D, 8><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    case 4: attn_partial_lds<D, 4><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 8: attn_partial_lds<D, 8><<<grid, 8 * kWave, 0, stream>>>(a); break;
     default: break;
   }
 }

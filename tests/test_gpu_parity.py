@@ -138,6 +138,31 @@ def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
     assert err < (1e-5 if cfg.dtype == "f32" else 1e-4), err
 
 
+@pytest.mark.parametrize("n_q,n_kv,d", [(2, 2, 128), (4, 2, 128), (8, 2, 128), (16, 2, 128),
+                                       (4, 2, 64), (8, 2, 64), (16, 2, 64)])
+def test_multi_step_chunks_every_head_group(n_q, n_kv, d):
+    """bf16 attention at every head group G = n_q / n_kv the kernels take (G <= 2: direct
+    register loads, G >= 4: K/V staged through LDS), in a batch large enough that each
+    context chunk spans several 32-key steps (steady-state loop and tail), with ragged
+    contexts; sampled requests against the oracle."""
+    cfg = scaled(SMALL_BF16, name=f"chunks-q{n_q}-kv{n_kv}-d{d}", n_q_heads=n_q,
+                 n_kv_heads=n_kv, head_dim=d)
+    Bn = 40
+    rng = np.random.Generator(np.random.PCG64(synth.stream_seed(11, cfg.name)))
+    ctx = rng.integers(1, 1100, size=Bn).tolist()
+    ctx[0], ctx[1] = 1100, 33
+    s = G.build(cfg, ctx, tag="chunks")
+    anchors = synth.anchor_ids(cfg, Bn, tag="chunks-anchor")
+    ids, logits = G.run_draft(s, anchors, want_logits=True)
+    for b in (0, 1, 17):
+        ks, vs = G.oracle_context(s, b)
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
+        bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
+        assert bad == 0, (b, ids[b], orc["ids"])
+        err = np.abs(logits[b] - orc["logits"])
+        assert err.mean() < 5e-3 and err.max() < 5e-2, (b, err.mean(), err.max())
+
+
 def test_ragged_batch_with_permuted_pages_matches_per_request_oracle():
     cfg = SMALL_BF16
     ctx = [0, 5, 16, 17, 300, 129]
