@@ -172,6 +172,10 @@ void set_rope(const Dims& m, GemmParams& g) {
   for (int i = 0; i < m.d / 2; ++i) g.inv_freq[i] = std::exp(-(2.0 * i / m.d) * log_theta);
 }
 
+// How the drafter's own activations are stored: bf16 models keep them as ready-made hi/lo
+// bf16 pieces (pair fragment layout), fp32 models as fp32 fragments.
+int act_kind(const Dims& m) { return m.bf16 ? A_HILO : A_SWZ; }
+
 GemmParams base_params(const Plan& pl, const char* W, int nt0, int KT, const void* A, int lda,
                        int M, int n_tiles) {
   GemmParams g;
@@ -289,14 +293,14 @@ constexpr int kInjectChunkRows = 256;
 // the fragment layout and ssq the rows' sums of squares (ssq_parts partials, row stride
 // ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
 // keys: workspace for the per-column-block argmax partials, lm_keys_bytes(m, rows) bytes.
-dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const float* xg,
+dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* xg,
                              const float* ssq, int ssq_parts, int ssq_ld, int rows,
                              bool draft_rows, int* ids_out, float* logits_out,
                              unsigned long long* keys, hipStream_t stream) {
   const Plan pl = lm_plan(m, rows);
   const int parts = argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw);
   GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, xg, m.H, rows, m.V / 16);
-  g.a_kind = A_SWZ;
+  g.a_kind = act_kind(m);
   g.norm = 1;
   g.ssq_in = ssq;
   g.ssq_parts = ssq_parts;
@@ -531,6 +535,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     {  // RMSNorm + fused Q|K|V projection + RoPE
       GemmParams g = base_params(dp.qkv, lb + P.wqkv, 0, m.H / m.ktile, xg, m.H, rows,
                                  (m.nq + 2 * m.nkv) * m.d / 16);
+      g.a_kind = act_kind(m);
       g.norm = 1;
       g.ssq_in = ssq;
       g.ssq_parts = l == 0 ? 1 : n_parts;   // the embedding kernel leaves whole-row sums
@@ -564,13 +569,14 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.scale = 1.0f / std::sqrt((float)m.d);
       a.part_o = reinterpret_cast<float*>(ws + dp.apart_o);
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
-      a.out = reinterpret_cast<float*>(ws + dp.ao);
-      a.out_kper = m.bf16 ? 8 : 4;
+      a.out = ws + dp.ao;
+      a.out_hilo = m.bf16;
       DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
     }
     {  // output projection + residual
       GemmParams g = base_params(dp.o, lb + P.wo, 0, m.nq * m.d / m.ktile, ws + dp.ao,
                                  m.nq * m.d, rows, m.H / 16);
+      g.a_kind = act_kind(m);
       g.out = x;
       g.ldo = m.H;
       g.xg_out = xg;   // inputs of the MLP norm
@@ -582,6 +588,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     {  // RMSNorm + gate|up + SiLU * up
       GemmParams g = base_params(dp.gu, lb + P.wgu, 0, m.H / m.ktile, xg, m.H, rows,
                                  2 * m.I / 16);
+      g.a_kind = act_kind(m);
       g.norm = 1;
       g.ssq_in = ssq;
       g.ssq_parts = n_parts;
@@ -594,6 +601,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     {  // down projection + residual
       GemmParams g = base_params(dp.dn, lb + P.wd, 0, m.I / m.ktile, ws + dp.h, m.I, rows,
                                  m.H / 16);
+      g.a_kind = act_kind(m);
       g.out = x;
       g.ldo = m.H;
       g.xg_out = xg;   // inputs of the next layer's attention norm, or of the final norm
@@ -630,7 +638,7 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   auto* keys = reinterpret_cast<unsigned long long*>(ws + kSyncBytes + frag_bytes + ssq_bytes);
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);
-  DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16 ? 8 : 4,
+  DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16,
                                   reinterpret_cast<const float*>(wb + P.final_norm), xs, ssq,
                                   stream));
   return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, logits_out, keys,

@@ -23,8 +23,9 @@ struct AttnArgs {
   float scale;             // 1 / sqrt(d)
   float* part_o;           // [B][n_kv][nc][G][d/16][4][16 rows][4]
   float* part_ml;          // [B][n_kv][nc][G][16 rows][2]
-  float* out;              // [B*16][n_q*d] fp32 in the fragment layout (swz_off)
-  int out_kper;            // fragment layout parameter of the consumer GEMM (8 bf16, 4 fp32)
+  void* out;               // [B*16][n_q*d]: pair fragment layout (hilo_off) when out_hilo,
+                           // else fp32 fragment layout (swz_off, kPer 4)
+  int out_hilo;            // 1 for bf16 models, 0 for fp32 models
 };
 
 hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,

@@ -35,7 +35,6 @@
 
 namespace dflash {
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline long long part_o_index(long long slot, int G, int hh, int D, int row,
                                          int dim) {
@@ -644,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 // slice (16 rows x 32 dims).  The slice's partials of the first kMergeBatch chunks are loaded
 // before the (m, l) pass so both travel in one round trip; the per-row maximum and sum come
 // from 16 rows x 8 chunk lanes through LDS; the weighted sum runs over chunks in order.  The
-// result is written in the fragment layout the output projection reads.
+// result is written in the layout the output projection reads.
 // ------------------------------------------------------------------------------------------
 constexpr int kMergeBatch = 40;
 constexpr int kMergeThreads = 128;   // float4s of a 16 x 32 slice
@@ -723,9 +722,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
       if (c0 + c < nch) acc += w_s[c0 + c][row] * v[c];
   }
   const int dim = 16 * (f / (4 * kBlock)) + 4 * ((f / kBlock) % 4);
-  const int kto = a.n_q * D / (4 * a.out_kper);
-  *reinterpret_cast<f32x4*>(a.out + swz_off(b * kBlock + row, h * D + dim, kto, a.out_kper)) =
-      acc * invL_s[row];
+  const f32x4 res = acc * invL_s[row];
+  if (a.out_hilo) {
+    store_hilo4(reinterpret_cast<bf16*>(a.out),
+                hilo_off(b * kBlock + row, h * D + dim, a.n_q * D / 32), res);
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) +
+                              swz_off(b * kBlock + row, h * D + dim, a.n_q * D / 16, 4)) = res;
+  }
 }
 
 // ------------------------------------------------------------------------------------------

@@ -8,6 +8,8 @@ namespace dflash {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,6 +142,39 @@ __device__ inline long long swz_off(int r, int k, int KT, int kPer) {
   const int kt = k / kTile, kk = k % kTile;
   const int lane = (r & 15) + 16 * (kk / kPer), j = kk % kPer;
   return (((long long)(r >> 4) * KT + kt) * (kPer / 4) + j / 4) * 256 + lane * 4 + (j & 3);
+}
+
+// ---------------------------------------------------------------------------------------
+// Pair fragment layout of the fp32 activations of a bf16 model.  Every such activation
+// enters the bf16 MFMA as two pieces, hi = bf16(v) and lo = bf16(v - hi), so the producer
+// stores the pieces ready-made: for each 16-row m-tile and 32-column k-tile, 1024 bf16 --
+// the 64 lanes' hi fragments (lane l: row l % 16, columns 8 (l / 16) .. + 8), then their lo
+// fragments.  Same bytes as fp32; a consumer loads each piece with one 16-byte read per lane
+// and splits nothing.  Offset in bf16 elements of the hi piece of (r, k) for a matrix of KT
+// k-tiles; the lo piece is kHiLoStride further.
+// ---------------------------------------------------------------------------------------
+constexpr int kHiLoStride = 512;
+__device__ inline long long hilo_off(int r, int k, int KT) {
+  const int kk = k & 31;
+  const int lane = (r & 15) + 16 * (kk >> 3);
+  return ((long long)(r >> 4) * KT + (k >> 5)) * 1024 + lane * 8 + (kk & 7);
+}
+// Store v as its hi and lo pieces at hilo offset `off`.
+__device__ inline void store_hilo(bf16* base, long long off, float v) {
+  const bf16 h = (bf16)v;
+  base[off] = h;
+  base[off + kHiLoStride] = (bf16)(v - (float)h);
+}
+// Store four consecutive columns k .. k + 3 (k % 4 == 0) of one row: two 8-byte stores.
+__device__ inline void store_hilo4(bf16* base, long long off, f32x4 v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (bf16)v[e];
+    l[e] = (bf16)(v[e] - (float)h[e]);
+  }
+  *reinterpret_cast<bf16x4*>(base + off) = h;
+  *reinterpret_cast<bf16x4*>(base + off + kHiLoStride) = l;
 }
 
 // RoPE rotation for frequency `inv` (theta^(-2i/d), computed in fp64 on the host) at

@@ -26,14 +26,16 @@ enum Epi : int {
   EPI_SWIGLU = 2,    // tile j: h[m][8j + c] = silu(gate) * up, c < 8
   EPI_QKV = 3,       // fused Q|K|V projection: RoPE on Q/K pairs, scatter to q / block k, v
   EPI_INJECT = 4,    // one layer's K|V projection: RoPE on K pairs, write the paged cache
-  EPI_ARGMAX = 5,    // LM head: per-row (value, index) maximum merged with atomicMax
+  EPI_ARGMAX = 5,    // LM head: per-row (value, index) maximum of each column block
 };
 
 // Where the activations (A) come from.
 enum AKind : int {
-  A_SWZ = 0,       // fp32 in the fragment layout (every activation the drafter produces)
+  A_SWZ = 0,       // fp32 in the fragment layout (fp32 models; the fused feature c, which
+                   // the injection splits into three bf16 pieces)
   A_ROW_F32 = 1,   // fp32 row-major [M][lda] (hidden rows handed in by a caller)
   A_ROW_BF16 = 2,  // bf16 row-major [M][lda] (target features of the fusion GEMM)
+  A_HILO = 3,      // bf16 model activations as hi/lo pieces in the pair fragment layout
 };
 
 struct GemmParams {
@@ -63,13 +65,14 @@ struct GemmParams {
   int n_mblocks;            // grid.y
 
   // Epilogue operands
-  void* out;                // EPI_STORE: c, EPI_RESIDUAL: x, EPI_SWIGLU: h; all fp32 in
-                            // the fragment layout with ldo columns
+  void* out;                // EPI_STORE: c, EPI_RESIDUAL: x (fp32 fragment layout);
+                            // EPI_SWIGLU: h (pair fragment layout for bf16 models, fp32
+                            // fragment layout for fp32 models); ldo columns
   int ldo;
-  // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (fragment layout) and,
-  // per n-tile, the rows' partial sums of squares ssq_out[n_tile * ssq_ld + row] -- the
-  // inputs of the next RMSNorm-folded GEMM.
-  float* xg_out;
+  // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (as h) and, per n-tile,
+  // the rows' partial sums of squares ssq_out[n_tile * ssq_ld + row] -- the inputs of the
+  // next RMSNorm-folded GEMM.
+  void* xg_out;
   const float* gamma_next;
   float* ssq_out;
   // EPI_QKV

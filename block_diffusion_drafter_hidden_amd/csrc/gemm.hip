@@ -90,7 +90,11 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         const float v = (pre ? *pre : *o) + tl[r * ld + c];
         *o = v;
         if (p.xg_out) {
-          p.xg_out[off] = v * p.gamma_next[tile0 * 16 + c];
+          const float xg = v * p.gamma_next[tile0 * 16 + c];
+          if constexpr (std::is_same<T, bf16>::value)
+            store_hilo(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, tile0 * 16 + c, kto), xg);
+          else
+            reinterpret_cast<float*>(p.xg_out)[off] = xg;
           tl[r * ld + c] = v;   // kept for the sums of squares below
         }
       }
@@ -130,8 +134,11 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       if (m >= p.M) continue;
       const float gate = tl[r * ld + jt * 16 + c];
       const float up = tl[r * ld + jt * 16 + 8 + c];
-      reinterpret_cast<float*>(p.out)[swz_off(m, (tile0 + jt) * 8 + c, kto, kPer)] =
-          silu(gate) * up;
+      const float h = silu(gate) * up;
+      if constexpr (std::is_same<T, bf16>::value)
+        store_hilo(reinterpret_cast<bf16*>(p.out), hilo_off(m, (tile0 + jt) * 8 + c, kto), h);
+      else
+        reinterpret_cast<float*>(p.out)[swz_off(m, (tile0 + jt) * 8 + c, kto, kPer)] = h;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int d = p.head_dim, half = d / 2, tph = d / 16;
@@ -236,7 +243,8 @@ template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(GemmParams p) {
   __shared__ GemmSmem sm;
   constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
-  typedef typename std::conditional<AK == A_ROW_BF16, bf16, float>::type AT;
+  static_assert(AK != A_HILO || std::is_same<T, bf16>::value, "pair pieces feed bf16 MFMAs");
+  typedef typename std::conditional<AK == A_ROW_BF16 || AK == A_HILO, bf16, float>::type AT;
   typedef AFrag<T, AT, kTerms> Frag;
   constexpr int kPer = Elem<T>::kPerLane;
   // k-tiles whose loads are issued together (raw fp32 A and its pieces stay in registers).
@@ -296,6 +304,8 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
     aval[mt] = r < p.M;
     if constexpr (AK == A_SWZ)
       arow[mt] = A + (long long)mtile * p.KT * kGroups * 256 + lane * 4;
+    else if constexpr (AK == A_HILO)
+      arow[mt] = A + (long long)mtile * p.KT * 1024 + lane * 8;
     else
       arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * kPer;
   }
@@ -347,7 +357,28 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
       for (int t = 0; t < NPW; ++t)
         b[u][t] = (kt + u * kstep < ke) ? load16(wp[t] + (long long)(kt + u * kstep) * kbytes)
                                         : zero;
-    if constexpr (sizeof(AT) == 2) {
+    if constexpr (AK == A_HILO) {
+      // Ready-made pieces: hi feeds acc, lo feeds acc_lo.
+      i32x4 ah[U][MT], al[U][MT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bool v = kt + u * kstep < ke && aval[mt];
+          const AT* src = arow[mt] + (long long)(kt + u * kstep) * 1024;
+          ah[u][mt] = v ? *reinterpret_cast<const i32x4*>(src) : zero;
+          al[u][mt] = v ? *reinterpret_cast<const i32x4*>(src + kHiLoStride) : zero;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < NPW; ++t) {
+            acc[t][mt] = mfma_tile<T>(ah[u][mt], b[u][t], acc[t][mt]);
+            acc_lo[t][mt] = mfma_tile<T>(al[u][mt], b[u][t], acc_lo[t][mt]);
+          }
+    } else if constexpr (sizeof(AT) == 2) {
       Frag a[U][MT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -474,7 +505,7 @@ constexpr int kTallM = 128, kTallN = 128;
 constexpr int kTallMT = kTallM / 16, kTallNT = kTallN / 16;
 
 struct TallStage {
-  f32x4 a[2][kTallMT][2][kWave];   // [buf][m-tile][group][lane]: fp32 A fragments
+  i32x4 a[2][3][kTallMT][kWave];   // [buf][piece][m-tile][lane]: bf16 pieces of A fragments
   i32x4 w[2][kTallNT][kWave];      // [buf][n-tile][lane]: packed bf16 B fragments
 };
 union TallSmem {
@@ -482,13 +513,14 @@ union TallSmem {
   float tile[kTallM * (kTallN + 1)];
 };
 
-template <int EPI, bool NORM>
-__global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
+template <int AK, int EPI, bool NORM>
+__global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   __shared__ TallSmem sm;
   __shared__ float rstd_s[kTallM];
   __shared__ float ssq_s[256];
-  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
-  typedef AFrag<bf16, float, kTerms> Frag;
+  static_assert(AK == A_HILO || AK == A_SWZ, "fragment-layout activations");
+  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;   // bf16 pieces per fp32 A value
+  static_assert(AK == A_SWZ || kTerms == 2, "pair pieces carry two terms");
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
   const int z = blockIdx.z;
@@ -519,20 +551,32 @@ __global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
   // Global -> register staging of one k-tile: 4 A chunks and 2 W chunks of 16 bytes per
   // thread.  A ring of kRing register stages keeps kRing - 1 k-tiles of loads in flight
   // beyond the one being multiplied, so memory latency overlaps several k-tiles of MFMAs.
-  constexpr int kRing = 2;
+  constexpr int kRing = AK == A_HILO ? 3 : 2;   // the three-piece split needs registers
   f32x4 ra[kRing][4];
   i32x4 rw[kRing][2];
   // Loads are unconditional (no divergent branches, so the waits stay precise): k-tiles past
   // the end re-read the last one, and m-tiles past the rows re-read the last valid m-tile --
   // those rows only reach output rows the epilogue never stores.
+  // A chunk c (16 bytes: 4 floats of one fragment lane) is m-tile c / 128, lane (c / 2) % 64,
+  // half c % 2 of the lane's 8 k values, so neighbouring threads write neighbouring 8-byte
+  // halves of the LDS fragments.
+  // Pair layout: chunk c is m-tile c / 128, piece (c / 64) % 2, lane c % 64, copied as is.
   auto load_stage = [&](int kt, f32x4 (&a)[4], i32x4 (&w)[2]) {
     const int ktc = min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256, mt = c / 128, g = (c / 64) % 2, l = c % 64;
+      const int c = tid + i * 256, mt = c / 128;
       const int mtc = min(mtile0 + mt, n_mtiles_valid - 1);
-      a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * KT + ktc) * 2 + g) * 256 +
-                                             l * 4);
+      if constexpr (AK == A_HILO) {
+        const int piece = (c / 64) % 2, l = c % 64;
+        a[i] = *reinterpret_cast<const f32x4*>(
+            reinterpret_cast<const bf16*>(p.A) + ((long long)mtc * KT + ktc) * 1024 +
+            piece * kHiLoStride + l * 8);
+      } else {
+        const int g = c % 2, l = (c / 2) % 64;
+        a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * KT + ktc) * 2 + g) * 256 +
+                                               l * 4);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -541,11 +585,29 @@ __global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
                             kTileBytes + l * 16);
     }
   };
+  // The fp32 A values are split into their bf16 pieces here, once per workgroup, and the
+  // pieces stored as MFMA fragments.
   auto store_stage = [&](int buf, const f32x4 (&a)[4], const i32x4 (&w)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      sm.st.a[buf][c / 128][(c / 64) % 2][c % 64] = a[i];
+      const int c = tid + i * 256, mt = c / 128;
+      if constexpr (AK == A_HILO) {
+        sm.st.a[buf][(c / 64) % 2][mt][c % 64] = __builtin_bit_cast(i32x4, a[i]);
+        continue;
+      }
+      const int g = c % 2, l = (c / 2) % 64;
+      float f[4] = {a[i][0], a[i][1], a[i][2], a[i][3]};
+#pragma unroll
+      for (int t = 0; t < kTerms; ++t) {
+        bf16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16 hb = (bf16)f[e];
+          h[e] = hb;
+          f[e] = f[e] - (float)hb;
+        }
+        reinterpret_cast<i32x2*>(&sm.st.a[buf][t][mt][l])[g] = __builtin_bit_cast(i32x2, h);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -563,28 +625,19 @@ __global__ __launch_bounds__(256) void gemm_tall(GemmParams p) {
   // One k-tile from LDS: every fragment read first (one wait), then the MFMAs ordered piece-
   // major so the two (three) products into one accumulator are 16 instructions apart.
   auto compute = [&](int buf) {
-    i32x4 wf[4];
-    f32x4 ar[4][2];
+    i32x4 wf[4], af[kTerms][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) wf[j] = sm.st.w[buf][wn * 4 + j][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ar[i][0] = sm.st.a[buf][wm * 4 + i][0][lane];
-      ar[i][1] = sm.st.a[buf][wm * 4 + i][1][lane];
-    }
-    Frag a[4];
+    for (int q = 0; q < kTerms; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float f[8] = {ar[i][0][0], ar[i][0][1], ar[i][0][2], ar[i][0][3],
-                          ar[i][1][0], ar[i][1][1], ar[i][1][2], ar[i][1][3]};
-      a[i].from_floats(f);
-    }
+      for (int i = 0; i < 4; ++i) af[q][i] = sm.st.a[buf][q][wm * 4 + i][lane];
 #pragma unroll
-    for (int q = 0; q < Frag::kTerms; ++q)
+    for (int q = 0; q < kTerms; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_tile<bf16>(a[i].part[q], wf[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_tile<bf16>(af[q][i], wf[j], acc[i][j]);
   };
 
   // Prologue: k-tiles 0 .. kRing-1 in flight, k-tile 0 in LDS buffer 0.
@@ -681,13 +734,24 @@ template <typename T, int MT>
 static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
                             hipStream_t stream) {
   const bool norm = p.norm != 0;
+  constexpr bool kBf16 = std::is_same<T, bf16>::value;
   switch (p.a_kind) {
-    case A_SWZ:
-      if (epi == EPI_RESIDUAL && !norm) return by_npw<T, A_SWZ, MT, EPI_RESIDUAL, false>(npw, p, layers, stream);
+    case A_SWZ:   // fp32 models: every activation; bf16 models: the injection's input
       if (epi == EPI_INJECT && !norm) return by_npw<T, A_SWZ, MT, EPI_INJECT, false>(npw, p, layers, stream);
-      if (epi == EPI_QKV && norm) return by_npw<T, A_SWZ, MT, EPI_QKV, true>(npw, p, layers, stream);
-      if (epi == EPI_SWIGLU && norm) return by_npw<T, A_SWZ, MT, EPI_SWIGLU, true>(npw, p, layers, stream);
-      if (epi == EPI_ARGMAX && norm) return by_npw<T, A_SWZ, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
+      if constexpr (!kBf16) {
+        if (epi == EPI_RESIDUAL && !norm) return by_npw<T, A_SWZ, MT, EPI_RESIDUAL, false>(npw, p, layers, stream);
+        if (epi == EPI_QKV && norm) return by_npw<T, A_SWZ, MT, EPI_QKV, true>(npw, p, layers, stream);
+        if (epi == EPI_SWIGLU && norm) return by_npw<T, A_SWZ, MT, EPI_SWIGLU, true>(npw, p, layers, stream);
+        if (epi == EPI_ARGMAX && norm) return by_npw<T, A_SWZ, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
+      }
+      break;
+    case A_HILO:  // bf16 models: everything the drafter produces except the injection input
+      if constexpr (kBf16) {
+        if (epi == EPI_RESIDUAL && !norm) return by_npw<T, A_HILO, MT, EPI_RESIDUAL, false>(npw, p, layers, stream);
+        if (epi == EPI_QKV && norm) return by_npw<T, A_HILO, MT, EPI_QKV, true>(npw, p, layers, stream);
+        if (epi == EPI_SWIGLU && norm) return by_npw<T, A_HILO, MT, EPI_SWIGLU, true>(npw, p, layers, stream);
+        if (epi == EPI_ARGMAX && norm) return by_npw<T, A_HILO, MT, EPI_ARGMAX, true>(npw, p, layers, stream);
+      }
       break;
     case A_ROW_F32:
       if (epi == EPI_STORE && !norm) return by_npw<T, A_ROW_F32, MT, EPI_STORE, false>(npw, p, layers, stream);
@@ -703,23 +767,25 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
   return hipErrorInvalidValue;
 }
 
-template <int EPI, bool NORM>
+template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   dim3 grid(p.n_tiles / kTallNT * p.n_mblocks, 1, layers);
-  gemm_tall<EPI, NORM><<<grid, 256, 0, stream>>>(p);
+  gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
                        int layers, hipStream_t stream) {
   if (mt == kTallMT) {   // 128-row blocks: bf16 weights, fragment-layout A
-    if (!dtype_bf16 || p.a_kind != A_SWZ || p.n_tiles % kTallNT) return hipErrorInvalidValue;
+    if (!dtype_bf16 || p.n_tiles % kTallNT) return hipErrorInvalidValue;
     const bool norm = p.norm != 0;
-    if (epi == EPI_RESIDUAL && !norm) return go_tall<EPI_RESIDUAL, false>(p, layers, stream);
-    if (epi == EPI_INJECT && !norm) return go_tall<EPI_INJECT, false>(p, layers, stream);
-    if (epi == EPI_QKV && norm) return go_tall<EPI_QKV, true>(p, layers, stream);
-    if (epi == EPI_SWIGLU && norm) return go_tall<EPI_SWIGLU, true>(p, layers, stream);
-    if (epi == EPI_ARGMAX && norm) return go_tall<EPI_ARGMAX, true>(p, layers, stream);
+    if (p.a_kind == A_SWZ && epi == EPI_INJECT && !norm)
+      return go_tall<A_SWZ, EPI_INJECT, false>(p, layers, stream);
+    if (p.a_kind != A_HILO) return hipErrorInvalidValue;
+    if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
+    if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
+    if (epi == EPI_SWIGLU && norm) return go_tall<A_HILO, EPI_SWIGLU, true>(p, layers, stream);
+    if (epi == EPI_ARGMAX && norm) return go_tall<A_HILO, EPI_ARGMAX, true>(p, layers, stream);
     return hipErrorInvalidValue;
   }
   if (dtype_bf16) {

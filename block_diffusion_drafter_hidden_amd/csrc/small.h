@@ -27,18 +27,18 @@ struct EmbedArgs {
   int hidden;
   float* x;               // residual stream, fp32 fragment layout (rows = batch * 16)
   const float* gamma;     // first layer's attention RMSNorm gain [hidden]
-  float* xg;              // x * gamma, fragment layout
+  void* xg;               // x * gamma: pair fragment layout (bf16 models), else as x
   float* ssq;             // [rows] sum of squares of each row
 };
 
 hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream);
 hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream);
 hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream);
-// Row-major fp32 [rows][cols] -> dst = src * gamma in the fragment layout (swz_off with
-// kper) and ssq[r] = sum of squares of row r (the inputs of an RMSNorm-folded GEMM);
-// cols % 4 == 0.
-hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper,
-                                    const float* gamma, float* dst, float* ssq,
+// Row-major fp32 [rows][cols] -> dst = src * gamma, in the pair fragment layout (hilo = 1,
+// bf16 models) or the fp32 fragment layout with kPer 4 (fp32 models), and ssq[r] = sum of
+// squares of row r (the inputs of an RMSNorm-folded GEMM); cols % 32 == 0.
+hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hilo,
+                                    const float* gamma, void* dst, float* ssq,
                                     hipStream_t stream);
 hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
                                 int* bonus, int* emitted, hipStream_t stream);

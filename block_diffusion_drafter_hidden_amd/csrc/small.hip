@@ -1,5 +1,7 @@
 // Small kernels of the DFlash step: weight packing, block embedding, RMSNorm,
 // greedy verification and workspace clearing.
+#include <type_traits>
+
 #include "common.h"
 #include "small.h"
 
@@ -87,7 +89,8 @@ __device__ inline float block_sum256(float v, float* red) {
 
 // Block embedding: row b*16 + j of x is the embedding of the anchor (j = 0) or of the mask
 // token (j >= 1), widened to fp32 and written in the fragment layout (4 columns per store),
-// together with x * gamma of the first RMSNorm and the row's sum of squares.
+// together with x * gamma of the first RMSNorm (pair fragment layout for bf16 models) and
+// the row's sum of squares.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   __shared__ float red[4];
@@ -104,7 +107,10 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     const f32x4 g = *reinterpret_cast<const f32x4*>(a.gamma + i);
     const long long off = swz_off(m, i, KT, kPer);
     *reinterpret_cast<f32x4*>(a.x + off) = v;
-    *reinterpret_cast<f32x4*>(a.xg + off) = v * g;
+    if constexpr (std::is_same<T, bf16>::value)
+      store_hilo4(reinterpret_cast<bf16*>(a.xg), hilo_off(m, i, a.hidden / 32), v * g);
+    else
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.xg) + off) = v * g;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   ss = block_sum256(ss, red);
@@ -120,28 +126,31 @@ hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_
 }
 
 __global__ __launch_bounds__(256) void rows_to_fragments_kernel(const float* __restrict__ src,
-                                                                int cols, int kper,
+                                                                int cols, int hilo,
                                                                 const float* __restrict__ gamma,
-                                                                float* __restrict__ dst,
+                                                                void* __restrict__ dst,
                                                                 float* __restrict__ ssq) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  const int KT = cols / (4 * kper);
   float ss = 0.f;
   for (int c = 4 * threadIdx.x; c < cols; c += 4 * blockDim.x) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(src + (long long)r * cols + c);
     const f32x4 g = *reinterpret_cast<const f32x4*>(gamma + c);
-    *reinterpret_cast<f32x4*>(dst + swz_off(r, c, KT, kper)) = v * g;
+    if (hilo)
+      store_hilo4(reinterpret_cast<bf16*>(dst), hilo_off(r, c, cols / 32), v * g);
+    else
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + swz_off(r, c, cols / 16, 4)) =
+          v * g;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   ss = block_sum256(ss, red);
   if (threadIdx.x == 0) ssq[r] = ss;
 }
 
-hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int kper,
-                                    const float* gamma, float* dst, float* ssq,
+hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hilo,
+                                    const float* gamma, void* dst, float* ssq,
                                     hipStream_t stream) {
-  rows_to_fragments_kernel<<<rows, 256, 0, stream>>>(src, cols, kper, gamma, dst, ssq);
+  rows_to_fragments_kernel<<<rows, 256, 0, stream>>>(src, cols, hilo, gamma, dst, ssq);
   return hipGetLastError();
 }
 
