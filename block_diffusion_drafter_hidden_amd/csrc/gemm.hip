@@ -503,6 +503,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
 // ------------------------------------------------------------------------------------------
 constexpr int kTallM = 128, kTallN = 128;
 constexpr int kTallMT = kTallM / 16, kTallNT = kTallN / 16;
+constexpr int kTallColRows = 4;   // row blocks up to which the order is column-block major
 
 struct TallStage {
   i32x4 a[2][3][kTallMT][kWave];   // [buf][piece][m-tile][lane]: bf16 pieces of A fragments
@@ -525,11 +526,24 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
   const int z = blockIdx.z;
 
-  // Workgroup -> (column block, row block), row-block major: the workgroups resident at one
-  // time share a row block, whose activations (128 rows x K) then stay in L2 while the
-  // weights stream past.
-  const int ncb = p.n_tiles / kTallNT;
-  const int cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
+  // Workgroup -> (column block, row block).  Up to kTallColRows row blocks: workgroups are
+  // dealt round-robin to the 8 XCDs and the ids are arranged so that each XCD takes whole
+  // column blocks, all their row blocks back to back -- a weight block comes from HBM once
+  // and is re-read from that XCD's L2 (the grid is padded to whole rounds of 8 column
+  // blocks; padding workgroups exit at once).  More row blocks: row-block major, so the
+  // workgroups resident at one time share a row block whose activations stay in L2 while
+  // the weights stream past (measured faster once the activations outgrow an XCD's L2).
+  const int ncb = p.n_tiles / kTallNT, nrb = p.n_mblocks;
+  int cb, rb;
+  if (nrb <= kTallColRows) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    cb = (slot / nrb) * kXcds + xcd;
+    rb = slot % nrb;
+    if (cb >= ncb) return;
+  } else {
+    cb = blockIdx.x % ncb;
+    rb = blockIdx.x / ncb;
+  }
   const int KT = p.KT;
   const int mtile0 = rb * kTallMT;                   // first m-tile of the block
   const int n_mtiles_valid = (p.M + 15) / 16;
@@ -769,7 +783,9 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
 
 template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
-  dim3 grid(p.n_tiles / kTallNT * p.n_mblocks, 1, layers);
+  const int ncb = p.n_tiles / kTallNT;
+  const int ncb_grid = p.n_mblocks <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
+  dim3 grid(ncb_grid * p.n_mblocks, 1, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
