@@ -120,15 +120,15 @@ struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
 };
 
-// Rows above which bf16 GEMMs over fragment-layout activations use the 128 x 128 tall kernel
-// (weights read once per 128 rows instead of once per 64).
+// Rows above which bf16 GEMMs use the 128 x 128 tall kernel (weights read once per 128 rows
+// instead of once per 64; a ragged last column block is allowed).
 constexpr int kTallRows = 64;
-constexpr int kTallMT = 8, kTallNT = 8;
+constexpr int kTallMT = 8;
 
 Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 16,
                bool tall_ok = false) {
   Plan p{};
-  if (tall_ok && M > kTallRows && n_tiles % kTallNT == 0) {
+  if (tall_ok && M > kTallRows) {
     p.mt = kTallMT;
     p.n_mblocks = cdiv(M, 16 * kTallMT);
     p.npw = 1;
@@ -273,7 +273,7 @@ struct InjectPlan {
 
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
-  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);
+  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);   // narrow N, deep K: split-K
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4, m.bf16 != 0);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded

@@ -112,7 +112,7 @@ hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int
 
 // Column blocks (argmax parts) of an EPI_ARGMAX launch with this plan.
 inline int argmax_parts(int n_tiles, int mt, int npw, int tgpw) {
-  return mt == 8 ? n_tiles / 8 : n_tiles / (npw * tgpw);
+  return mt == 8 ? (n_tiles + 7) / 8 : n_tiles / (npw * tgpw);
 }
 
 }  // namespace dflash

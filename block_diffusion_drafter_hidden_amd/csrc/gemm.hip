@@ -65,9 +65,10 @@ struct ResidualPrefetch {
   static constexpr int kN = 4 * NPW * MT <= 8 ? 4 * NPW * MT : 0;   // per thread, ksub = 1 bound
 };
 
+// `part`: the workgroup's column-block index (the argmax partial it writes).
 template <typename T, int MT, int EPI, int NPRE>
 __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0, int mblock,
-                             int z, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
+                             int z, int part, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
   const int rows = MT * 16;
   const int ld = cols + 1;
   const int m0 = mblock * rows;
@@ -231,7 +232,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         const unsigned long long other = __shfl_xor(best, o, kWave);
         best = other > best ? other : best;
       }
-      if (lane == 0) p.keys[(long long)(tile0 / (cols / 16)) * p.keys_ld + m] = best;
+      if (lane == 0) p.keys[(long long)part * p.keys_ld + m] = best;
     }
   }
 }
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
         }
   }
   __syncthreads();
-  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, xpre);
+  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, group, xpre);
 }
 
 
@@ -520,8 +521,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   __shared__ float rstd_s[kTallM];
   __shared__ float ssq_s[256];
   static_assert(AK == A_HILO || AK == A_SWZ, "fragment-layout activations");
-  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;   // bf16 pieces per fp32 A value
-  static_assert(AK == A_SWZ || kTerms == 2, "pair pieces carry two terms");
+  // bf16 pieces per fp32 A value: two, three for the injection (its results end in the cache)
+  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
+  static_assert(AK != A_HILO || kTerms == 2, "pair pieces carry two terms");
+  constexpr int kAChunks = 4;   // 16-byte A chunks per thread
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
   const int z = blockIdx.z;
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // blocks; padding workgroups exit at once).  More row blocks: row-block major, so the
   // workgroups resident at one time share a row block whose activations stay in L2 while
   // the weights stream past (measured faster once the activations outgrow an XCD's L2).
-  const int ncb = p.n_tiles / kTallNT, nrb = p.n_mblocks;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = p.n_mblocks;
   int cb, rb;
   if (nrb <= kTallColRows) {
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
@@ -545,6 +548,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     rb = blockIdx.x / ncb;
   }
   const int KT = p.KT;
+  const int ntv = min(kTallNT, p.n_tiles - cb * kTallNT);   // valid n-tiles (ragged last)
   const int mtile0 = rb * kTallMT;                   // first m-tile of the block
   const int n_mtiles_valid = (p.M + 15) / 16;
   const float* A = reinterpret_cast<const float*>(p.A);
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // thread.  A ring of kRing register stages keeps kRing - 1 k-tiles of loads in flight
   // beyond the one being multiplied, so memory latency overlaps several k-tiles of MFMAs.
   constexpr int kRing = AK == A_HILO ? 3 : 2;   // the three-piece split needs registers
-  f32x4 ra[kRing][4];
+  f32x4 ra[kRing][kAChunks];
   i32x4 rw[kRing][2];
   // Loads are unconditional (no divergent branches, so the waits stay precise): k-tiles past
   // the end re-read the last one, and m-tiles past the rows re-read the last valid m-tile --
@@ -575,10 +579,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // half c % 2 of the lane's 8 k values, so neighbouring threads write neighbouring 8-byte
   // halves of the LDS fragments.
   // Pair layout: chunk c is m-tile c / 128, piece (c / 64) % 2, lane c % 64, copied as is.
-  auto load_stage = [&](int kt, f32x4 (&a)[4], i32x4 (&w)[2]) {
+  // n-tiles past a ragged last column block re-read its last valid n-tile (their columns are
+  // never stored).
+  auto load_stage = [&](int kt, f32x4 (&a)[kAChunks], i32x4 (&w)[2]) {
     const int ktc = min(kt, KT - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAChunks; ++i) {
       const int c = tid + i * 256, mt = c / 128;
       const int mtc = min(mtile0 + mt, n_mtiles_valid - 1);
       if constexpr (AK == A_HILO) {
@@ -594,16 +600,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256, nt = c / 64, l = c % 64;
+      const int c = tid + i * 256, nt = min(c / 64, ntv - 1), l = c % 64;
       w[i] = load16(W + ((long long)nt * p.nt_stride + (long long)ktc * p.kt_stride) *
                             kTileBytes + l * 16);
     }
   };
   // The fp32 A values are split into their bf16 pieces here, once per workgroup, and the
   // pieces stored as MFMA fragments.
-  auto store_stage = [&](int buf, const f32x4 (&a)[4], const i32x4 (&w)[2]) {
+  auto store_stage = [&](int buf, const f32x4 (&a)[kAChunks], const i32x4 (&w)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAChunks; ++i) {
       const int c = tid + i * 256, mt = c / 128;
       if constexpr (AK == A_HILO) {
         sm.st.a[buf][(c / 64) % 2][mt][c % 64] = __builtin_bit_cast(i32x4, a[i]);
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
           1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(KT * 32) + p.eps);
     __syncthreads();
   }
-  constexpr int ld = kTallN + 1;
+  const int cols = ntv * 16, ld = cols + 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -705,13 +711,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const int col = wn * 64 + j * 16 + (lane & 15);
         float v = acc[i][j][e];
         if constexpr (NORM) v *= rstd_s[r];
-        sm.tile[r * ld + wn * 64 + j * 16 + (lane & 15)] = v;
+        if (col < cols) sm.tile[r * ld + col] = v;
       }
   __syncthreads();
   const float xpre[1] = {0.f};
-  run_epilogue<bf16, kTallMT, EPI, 0>(p, sm.tile, kTallN, cb * kTallNT, rb, z, xpre);
+  run_epilogue<bf16, kTallMT, EPI, 0>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, xpre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -783,7 +790,7 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
 
 template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
-  const int ncb = p.n_tiles / kTallNT;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
   const int ncb_grid = p.n_mblocks <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
   dim3 grid(ncb_grid * p.n_mblocks, 1, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
@@ -792,8 +799,8 @@ static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
 
 hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParams& p,
                        int layers, hipStream_t stream) {
-  if (mt == kTallMT) {   // 128-row blocks: bf16 weights, fragment-layout A
-    if (!dtype_bf16 || p.n_tiles % kTallNT) return hipErrorInvalidValue;
+  if (mt == kTallMT) {   // 128-row x 128-column blocks, bf16 weights
+    if (!dtype_bf16 || p.n_tiles < 1 || p.M < 1) return hipErrorInvalidValue;
     const bool norm = p.norm != 0;
     if (p.a_kind == A_SWZ && epi == EPI_INJECT && !norm)
       return go_tall<A_SWZ, EPI_INJECT, false>(p, layers, stream);

@@ -138,15 +138,19 @@ def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
     assert err < (1e-5 if cfg.dtype == "f32" else 1e-4), err
 
 
-@pytest.mark.parametrize("n_q,n_kv,d", [(2, 2, 128), (4, 2, 128), (8, 2, 128), (16, 2, 128),
-                                       (4, 2, 64), (8, 2, 64), (16, 2, 64)])
-def test_multi_step_chunks_every_head_group(n_q, n_kv, d):
+@pytest.mark.parametrize("n_q,n_kv,d,hidden", [(2, 2, 128, 512), (4, 2, 128, 512),
+                                              (8, 2, 128, 512), (16, 2, 128, 512),
+                                              (4, 2, 64, 512), (8, 2, 64, 512),
+                                              (16, 2, 64, 512), (8, 2, 64, 576)])
+def test_multi_step_chunks_every_head_group(n_q, n_kv, d, hidden):
     """bf16 attention at every head group G = n_q / n_kv the kernels take (G <= 2: direct
     register loads, G >= 4: K/V staged through LDS), in a batch large enough that each
     context chunk spans several 32-key steps (steady-state loop and tail), with ragged
-    contexts; sampled requests against the oracle."""
-    cfg = scaled(SMALL_BF16, name=f"chunks-q{n_q}-kv{n_kv}-d{d}", n_q_heads=n_q,
-                 n_kv_heads=n_kv, head_dim=d)
+    contexts; the batch's 640 rows also run the 128-row GEMM kernel, hidden 576 with a ragged
+    last 128-column block in the output and down projections.  Sampled requests against the
+    oracle."""
+    cfg = scaled(SMALL_BF16, name=f"chunks-q{n_q}-kv{n_kv}-d{d}-h{hidden}", n_q_heads=n_q,
+                 n_kv_heads=n_kv, head_dim=d, hidden=hidden, target_hidden=hidden)
     Bn = 40
     rng = np.random.Generator(np.random.PCG64(synth.stream_seed(11, cfg.name)))
     ctx = rng.integers(1, 1100, size=Bn).tolist()
