@@ -255,7 +255,7 @@ def main():
                    "layers": cfg.n_layers, "hidden": H, "vocab": V, "graph": graph is not None},
         "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
-        "roofline": {"kernel": "shared LM head + argmax: gemm_stream<bf16,A_SWZ,1,4,EPI_ARGMAX>; "
+        "roofline": {"kernel": "shared LM head + argmax: gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>; "
                                "launch_us spans the entry point's three launches (rows to "
                                "fragment layout, LM-head GEMM, argmax finalize)",
                      "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
