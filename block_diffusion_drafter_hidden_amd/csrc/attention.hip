@@ -30,6 +30,8 @@
 // Partial layout: part_o[slot][head_in_group][dt][q][row][i] holds output dim
 // 16*dt + 4*q + i of block row `row` (a float4 per (dt, q, row)); part_ml[slot][head][row]
 // holds (m, l).  slot = (b * n_kv + g) * nc + c.
+#include <type_traits>
+
 #include "attention.h"
 #include "common.h"
 
@@ -134,12 +136,14 @@ struct HeadState {
 
   // Online-softmax update for one 32-key step given S^T tiles s[2] (lane: keys
   // 16 pg + 4q + i for query n); returns the P^T fragment (hi, lo).  The accumulator is
-  // rescaled only when some row's maximum grew (a branch uniform over the wave).
+  // rescaled only when some row's maximum grew (a branch uniform over the wave).  Only a
+  // kMasked step (the last of a chunk, or the block) can hold fewer than 32 valid keys.
+  template <bool kMasked>
   __device__ void softmax(const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s[e / 4][e % 4];
-    if (nk < 32) {
+    if (kMasked) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (16 * (e / 4) + 4 * q + e % 4 >= nk) x[e] = -INFINITY;
@@ -157,7 +161,7 @@ struct HeadState {
     float pv[8], ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
-    if (nk < 32) {
+    if (kMasked) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (16 * (e / 4) + 4 * q + e % 4 >= nk) pv[e] = 0.f;
@@ -170,6 +174,7 @@ struct HeadState {
 
   // One 32-key step: k[pg][ks] is the K fragment (16 keys of page pg x dims 32ks + 8q..+8),
   // v[dt][pg] the V^T half-fragment (dim 16dt + n x keys 4q..4q+3 of page pg).
+  template <bool kMasked>
   __device__ void step(const i32x4 (&k)[2][KS], const i32x2 (&v)[DT][2], int nk) {
     // Q hi and Q lo products accumulate separately: four independent MFMA chains.
     f32x4 sh[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -183,11 +188,11 @@ struct HeadState {
       }
     const f32x4 s[2] = {sh[0] + sl[0], sh[1] + sl[1]};
     i32x4 ph, pl;
-    softmax(s, nk, ph, pl);
+    softmax<kMasked>(s, nk, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       i32x4 vv = i32x4{v[dt][0][0], v[dt][0][1], v[dt][1][0], v[dt][1][1]};
-      if (nk < 32) vv = mask_vt(vv, q, nk);   // stale cache slots may hold any bits
+      if (kMasked) vv = mask_vt(vv, q, nk);   // stale cache slots may hold any bits
       o[dt] = mfma_tile<bf16>(vv, ph, o[dt]);
       o[dt] = mfma_tile<bf16>(vv, pl, o[dt]);
     }
@@ -211,7 +216,7 @@ struct HeadState {
       s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
     }
     i32x4 ph, pl;
-    softmax(s, kBlock, ph, pl);
+    softmax<true>(s, kBlock, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 vv = *reinterpret_cast<const f32x4*>(bv_s + (16 * dt + n) * kBlock + q * 4);
@@ -356,17 +361,20 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
   const int nsteps = cs.nsteps;
   // Steady state: ra holds step st, rb step st + 1, and both prefetches exist.
   int st = 0;
+  // Steps of the steady state are full (at least two more follow them); the tail takes the
+  // masked form, since its last step may be the chunk's partial one.
+  auto tail_step = [&](const StepRegs<D>& r) { hs.template step<true>(r.k, r.v, r.nk); };
   for (; st + 3 < nsteps; st += 2) {
-    hs.step(ra.k, ra.v, ra.nk);
+    hs.template step<false>(ra.k, ra.v, ra.nk);
     load_step(st + 2, ra);
-    hs.step(rb.k, rb.v, rb.nk);
+    hs.template step<false>(rb.k, rb.v, rb.nk);
     load_step(st + 3, rb);
   }
   // 0..3 steps remain.
-  if (st < nsteps) hs.step(ra.k, ra.v, ra.nk);
+  if (st < nsteps) tail_step(ra);
   if (st + 2 < nsteps) load_step(st + 2, ra);
-  if (st + 1 < nsteps) hs.step(rb.k, rb.v, rb.nk);
-  if (st + 2 < nsteps) hs.step(ra.k, ra.v, ra.nk);
+  if (st + 1 < nsteps) tail_step(rb);
+  if (st + 2 < nsteps) tail_step(ra);
 
   if (cs.has_block) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -404,11 +412,13 @@ template <int D>
 __device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
 template <int D, int G>
-__global__ __launch_bounds__(G * kWave, 2) void attn_partial_lds(
+__global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_partial_lds(
     AttnArgs a) {
   using L = LdsStep<D, G>;
   constexpr int KS = D / 32, DT = D / 16, NL = L::NL;
-  constexpr int RS = 4;                                   // register stages (steps ahead)
+  // Register stages (steps ahead).  d = 64 with G = 8 runs two workgroups per CU (four
+  // waves per SIMD, at most 128 registers), which needs the shallower ring.
+  constexpr int RS = (D == 64 && G == 8) ? 2 : 4;
   __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlock * D * 4];
   __shared__ __attribute__((aligned(16))) char kv_s[2][L::kStepBytes];
   const int g = blockIdx.y;
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_lds(
     for (int j = 0; j < NL; ++j) *reinterpret_cast<i32x4*>(kv_s[stage] + dst_off[j]) = r[j];
   };
   // Fragments of one step from a stage (layouts as in attn_partial_bf16).
-  auto compute = [&](HeadState<D>& hs, int stage, int st) {
+  auto compute = [&](HeadState<D>& hs, int stage, int st, auto masked) {
     const char* sb = kv_s[stage];
     i32x4 k[2][KS];
     i32x2 v[DT][2];
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_lds(
             sb + (2 + pg) * L::kQuarter + dim * 32 + ((q ^ (((dim >> 3) & 1) * 2)) * 8));
       }
     }
-    hs.step(k, v, min(32, cs.kend - cs.kbeg - 32 * st));
+    hs.template step<decltype(masked)::value>(k, v, min(32, cs.kend - cs.kbeg - 32 * st));
   };
 
   i32x4 rs[RS][NL];
@@ -492,21 +502,24 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_lds(
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
       load_pieces(t + i + RS, rs[i]);
-      compute(hs, i & 1, t + i);
+      compute(hs, i & 1, t + i, std::false_type{});   // at least RS more steps follow: full
       store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
       __syncthreads();
     }
   }
-  // Tail: fewer than 2 RS steps remain; step t + i is in register set i % RS.
+  // Tail: fewer than 2 RS steps remain; step t + i is in register set i % RS.  Every step
+  // but the chunk's last is full; the last (possibly partial) one is taken after the loop
+  // from its LDS stage.
 #pragma unroll
   for (int i = 0; i < 2 * RS - 1; ++i) {
-    if (t + i < nsteps) {
+    if (t + i + 1 < nsteps) {
       if (i < RS && t + i + RS < nsteps) load_pieces(t + i + RS, rs[i % RS]);
-      compute(hs, i & 1, t + i);
-      if (t + i + 1 < nsteps) store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
+      compute(hs, i & 1, t + i, std::false_type{});
+      store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
       __syncthreads();
     }
   }
+  if (nsteps > 0) compute(hs, (nsteps - 1) & 1, nsteps - 1, std::true_type{});
 
   if (cs.has_block) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
