@@ -81,6 +81,11 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // Scores are kept in base-2 units: the queries are scaled by log2(e) / sqrt(d), so every
 // exponential is a plain exp2 and partial maxima m are log2-scaled (the merge uses exp2 too).
 constexpr float kLog2e = 1.4426950408889634f;
+// The running reference maximum m of a row is raised only when a score exceeds it by more
+// than this (in base-2 units), so probabilities exp2(s - m) stay below 2^8 and the
+// accumulator is rescaled rarely; (m, l, o) remain an exact representation of the softmax
+// state for any reference.
+constexpr float kRescaleSlack = 8.0f;
 
 // Maximum / sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48):
 // each row-swap permute hands every lane its partner row's value, so after the 16- and the
@@ -136,8 +141,9 @@ struct HeadState {
 
   // Online-softmax update for one 32-key step given S^T tiles s[2] (lane: keys
   // 16 pg + 4q + i for query n); returns the P^T fragment (hi, lo).  The accumulator is
-  // rescaled only when some row's maximum grew (a branch uniform over the wave).  Only a
-  // kMasked step (the last of a chunk, or the block) can hold fewer than 32 valid keys.
+  // rescaled only when some row's maximum passed its reference by kRescaleSlack (a branch
+  // uniform over the wave).  Only a kMasked step (the last of a chunk, or the block) can
+  // hold fewer than 32 valid keys.
   template <bool kMasked>
   __device__ void softmax(const f32x4 (&s)[2], int nk, i32x4& p_hi, i32x4& p_lo) {
     float x[8];
@@ -151,7 +157,7 @@ struct HeadState {
     const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float m_new = fmaxf(m_run, rows_max(mx));   // finite: key 0 of a step is valid
-    if (__ballot(m_new > m_run)) {
+    if (__ballot(m_new > m_run + kRescaleSlack)) {     // always on the first step
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
       l_run *= corr;
 #pragma unroll
@@ -176,17 +182,29 @@ struct HeadState {
   // v[dt][pg] the V^T half-fragment (dim 16dt + n x keys 4q..4q+3 of page pg).
   template <bool kMasked>
   __device__ void step(const i32x4 (&k)[2][KS], const i32x2 (&v)[DT][2], int nk) {
-    // Q hi and Q lo products accumulate separately: four independent MFMA chains.
-    f32x4 sh[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    f32x4 sl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // d = 128: Q hi and Q lo products accumulate separately (four independent MFMA chains
+    // of four); d = 64: one chain per page (two chains of four, no adds).
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (KS > 2) {
+      f32x4 sl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        sh[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][0], sh[pg]);
-        sl[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][1], sl[pg]);
-      }
-    const f32x4 s[2] = {sh[0] + sl[0], sh[1] + sl[1]};
+        for (int pg = 0; pg < 2; ++pg) {
+          s[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][0], s[pg]);
+          sl[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][1], sl[pg]);
+        }
+      s[0] += sl[0];
+      s[1] += sl[1];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          s[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][0], s[pg]);
+          s[pg] = mfma_tile<bf16>(k[pg][ks], qf[ks][1], s[pg]);
+        }
+    }
     i32x4 ph, pl;
     softmax<kMasked>(s, nk, ph, pl);
 #pragma unroll
