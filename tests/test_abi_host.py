@@ -86,3 +86,22 @@ def test_small_workspace_rejected_before_launch():
     assert st == -3
     st = lib.dflash_workspace_init(fake, 16, None)
     assert st == -3
+
+
+def test_size_limits_rejected_before_launch():
+    """The kernels' static limits are checked on the host: at most 4096 requests per draft
+    call, 16384 pages (262144 positions) per request, 65536 rows for the LM-head entry."""
+    lib = B.load_library()
+    c = B.make_config(TINY)
+    fake = C.c_void_p(16)  # never dereferenced: the limit check fails first
+    ok_cache = B.KVCache(1, 1, 1, 1, 16, 8)
+    st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(ok_cache), fake, 4097, fake,
+                                None, fake, 1 << 40, None)
+    assert st == -2
+    long_cache = B.KVCache(1, 1, 1, 1, 16, 16385)
+    st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(long_cache), fake, 1, fake,
+                                None, fake, 1 << 40, None)
+    assert st == -2
+    st = lib.dflash_lm_head_argmax(C.byref(c), fake, fake, 65537, fake, None, fake, 1 << 40,
+                                   None)
+    assert st == -2

@@ -154,11 +154,11 @@ def test_multi_step_chunks_every_head_group(n_q, n_kv, d, hidden):
     Bn = 40
     rng = np.random.Generator(np.random.PCG64(synth.stream_seed(11, cfg.name)))
     ctx = rng.integers(1, 1100, size=Bn).tolist()
-    ctx[0], ctx[1] = 1100, 33
+    ctx[0], ctx[1], ctx[2] = 1100, 33, 0   # longest, one step + one key, no context at all
     s = G.build(cfg, ctx, tag="chunks")
     anchors = synth.anchor_ids(cfg, Bn, tag="chunks-anchor")
     ids, logits = G.run_draft(s, anchors, want_logits=True)
-    for b in (0, 1, 17):
+    for b in (0, 1, 2, 17):
         ks, vs = G.oracle_context(s, b)
         orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
         bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
