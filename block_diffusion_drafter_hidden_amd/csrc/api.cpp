@@ -228,9 +228,19 @@ size_t lm_keys_bytes(const Dims& m, int rows) {
 struct DraftPlan {
   Plan qkv, o, gu, dn;
   int nc, chunk;
-  size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml, keys;
+  size_t x, xg, ssq, q, bk, bv, ao, h, apart_o, apart_ml, keys, kpart;
   size_t total;
 };
+
+// k-slices of a 128-row residual GEMM: enough workgroups for two per CU, at least 32 k-tiles
+// per slice (measured: 128 output blocks leave half the chip idle at 512 rows).
+int residual_splits(const Plan& pl, int n_tiles, int KT) {
+  if (pl.mt != kTallMT) return 1;
+  const long long blocks = (long long)cdiv(n_tiles, 8) * pl.n_mblocks;
+  int s = 1;
+  while (blocks * s < 256 && KT / (s * 2) >= 32 && s < 8) s *= 2;
+  return s;
+}
 
 DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   DraftPlan p{};
@@ -240,6 +250,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
+  if (p.o.mt == kTallMT) p.o.ksub = residual_splits(p.o, m.H / 16, m.nq * m.d / m.ktile);
+  if (p.dn.mt == kTallMT) p.dn.ksub = residual_splits(p.dn, m.H / 16, m.I / m.ktile);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   // Context chunks per (request, KV group): enough workgroups to fill the chip at small
@@ -262,6 +274,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
   p.keys = c.take(lm_keys_bytes(m, rows));
+  const int splits = std::max(p.o.mt == kTallMT ? p.o.ksub : 1, p.dn.mt == kTallMT ? p.dn.ksub : 1);
+  p.kpart = c.take(splits > 1 ? (size_t)splits * rows * m.H * 4 : 0);
   p.total = c.off;
   return p;
 }
@@ -583,6 +597,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.gamma_next = reinterpret_cast<const float*>(lb + P.mlp_norm);
       g.ssq_out = ssq;
       g.ssq_ld = rows;
+      g.ksplit = dp.o.mt == kTallMT ? dp.o.ksub : 1;
+      g.partial = reinterpret_cast<float*>(ws + dp.kpart);
       DF_TRY(launch_gemm(m.bf16, dp.o.mt, dp.o.npw, EPI_RESIDUAL, g, 1, stream));
     }
     {  // RMSNorm + gate|up + SiLU * up
@@ -610,6 +626,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                       : wb + P.final_norm);
       g.ssq_out = ssq;
       g.ssq_ld = rows;
+      g.ksplit = dp.dn.mt == kTallMT ? dp.dn.ksub : 1;
+      g.partial = reinterpret_cast<float*>(ws + dp.kpart);
       DF_TRY(launch_gemm(m.bf16, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }

@@ -97,6 +97,12 @@ struct GemmParams {
   int keys_ld;
   float* logits_out;        // [rows][ldo] or null
   int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
+  // 128-row kernel with EPI_RESIDUAL: the k range is split over `ksplit` workgroups per
+  // output block (grid.y); slice s writes its fp32 partial tile to partial[s][row][col]
+  // (M rows, ldo columns) and the residual reduction kernel adds the slices in slice order
+  // and applies the residual epilogue.  ksplit <= 1: no split.
+  int ksplit;
+  float* partial;
 };
 
 // dtype_bf16: weight type; npw: n-tiles per wave (1, 2 or 4); the A kind and RMSNorm come

@@ -16,6 +16,7 @@
 // residual stream also writes x * gamma of the next norm and per-n-tile partial sums of
 // squares; the normed GEMM streams x * gamma like any activation and scales each finished
 // row by 1/sqrt(sum / K + eps) before the epilogue.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -547,7 +548,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     cb = blockIdx.x % ncb;
     rb = blockIdx.x / ncb;
   }
-  const int KT = p.KT;
+  // k-tiles [kb, kb + KT) of this workgroup's slice of the k range.
+  const int S = EPI == EPI_RESIDUAL ? max(p.ksplit, 1) : 1, sl = blockIdx.y;
+  const int kb = (sl * p.KT) / S;
+  const int KT = ((sl + 1) * p.KT) / S - kb;
   const int ntv = min(kTallNT, p.n_tiles - cb * kTallNT);   // valid n-tiles (ragged last)
   const int mtile0 = rb * kTallMT;                   // first m-tile of the block
   const int n_mtiles_valid = (p.M + 15) / 16;
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // n-tiles past a ragged last column block re-read its last valid n-tile (their columns are
   // never stored).
   auto load_stage = [&](int kt, f32x4 (&a)[kAChunks], i32x4 (&w)[2]) {
-    const int ktc = min(kt, KT - 1);
+    const int ktc = kb + min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
       const int c = tid + i * 256, mt = c / 128;
@@ -590,11 +594,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       if constexpr (AK == A_HILO) {
         const int piece = (c / 64) % 2, l = c % 64;
         a[i] = *reinterpret_cast<const f32x4*>(
-            reinterpret_cast<const bf16*>(p.A) + ((long long)mtc * KT + ktc) * 1024 +
+            reinterpret_cast<const bf16*>(p.A) + ((long long)mtc * p.KT + ktc) * 1024 +
             piece * kHiLoStride + l * 8);
       } else {
         const int g = c % 2, l = (c / 2) % 64;
-        a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * KT + ktc) * 2 + g) * 256 +
+        a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * p.KT + ktc) * 2 + g) * 256 +
                                                l * 4);
       }
     }
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     __syncthreads();
     if (tid < kTallM)
       rstd_s[tid] =
-          1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(KT * 32) + p.eps);
+          1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(p.KT * 32) + p.eps);
     __syncthreads();
   }
   const int cols = ntv * 16, ld = cols + 1;
@@ -717,6 +721,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
         if (col < cols) sm.tile[r * ld + col] = v;
       }
   __syncthreads();
+  if (EPI == EPI_RESIDUAL && S > 1) {   // k-slice partial: rows of the tile, row-major
+    for (int idx = tid; idx < kTallM * cols; idx += 256) {
+      const int r = idx / cols, c = idx % cols, m = rb * kTallM + r;
+      if (m < p.M)
+        p.partial[((long long)sl * p.M + m) * p.ldo + cb * kTallN + c] = sm.tile[r * ld + c];
+    }
+    return;
+  }
   const float xpre[1] = {0.f};
   run_epilogue<bf16, kTallMT, EPI, 0>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, xpre);
 }
@@ -788,12 +800,50 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
   return hipErrorInvalidValue;
 }
 
+// Residual reduction of a k-split 128-row GEMM: thread (row m, column quad) adds the slices'
+// four columns in slice order to x and writes x and x * gamma_next (pair layout); the four
+// threads of an n-tile (adjacent lanes) sum the squares of its 16 columns for the next norm
+// -- the residual epilogue of the unsplit kernel.
+__global__ __launch_bounds__(256) void residual_reduce_kernel(GemmParams p, int splits) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int quads = p.n_tiles * 4;
+  const bool live = idx < (long long)p.M * quads;
+  const int m = live ? (int)(idx / quads) : 0, cq = (int)(idx % quads);
+  const int kto = p.ldo / 32, col = cq * 4;
+  float ss = 0.f;
+  if (live) {
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < splits; ++sl)
+      v += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo + col);
+    f32x4* xp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, col, kto, 8));
+    const f32x4 xn = *xp + v;
+    *xp = xn;
+    if (p.xg_out) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(p.gamma_next + col);
+      store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, col, kto), xn * g);
+      ss = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+    }
+  }
+  if (p.xg_out) {   // quads of one n-tile are lanes 4t .. 4t+3 (quads per row is a multiple of 4)
+    ss += __shfl_xor(ss, 1, kWave);
+    ss += __shfl_xor(ss, 2, kWave);
+    if (live && (cq & 3) == 0) p.ssq_out[(long long)(cq / 4) * p.ssq_ld + m] = ss;
+  }
+}
+
 template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
   const int ncb_grid = p.n_mblocks <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
-  dim3 grid(ncb_grid * p.n_mblocks, 1, layers);
+  const int splits = EPI == EPI_RESIDUAL ? std::max(p.ksplit, 1) : 1;
+  if (splits > 1 && (layers != 1 || !p.partial || p.KT < splits || p.ldo % 16 != 0))
+    return hipErrorInvalidValue;
+  dim3 grid(ncb_grid * p.n_mblocks, splits, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
+  if (splits > 1) {
+    const long long threads = (long long)p.M * p.n_tiles * 4;
+    residual_reduce_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
+  }
   return hipGetLastError();
 }
 
