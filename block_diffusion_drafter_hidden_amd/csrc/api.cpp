@@ -232,9 +232,10 @@ struct DraftPlan {
   size_t total;
 };
 
-// k-slices of a 128-row residual GEMM: enough workgroups for two per CU, at least 32 k-tiles
-// per slice (measured: 128 output blocks leave half the chip idle at 512 rows).
-int residual_splits(const Plan& pl, int n_tiles, int KT) {
+// k-slices of a 128-row store or residual GEMM: at least 256 workgroups (one per CU) and at
+// least 32 k-tiles per slice (measured: 128 output blocks leave the chip underused at 512
+// rows; at 256 blocks a split no longer pays for its partials).
+int ksplit_count(const Plan& pl, int n_tiles, int KT) {
   if (pl.mt != kTallMT) return 1;
   const long long blocks = (long long)cdiv(n_tiles, 8) * pl.n_mblocks;
   int s = 1;
@@ -250,8 +251,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
-  if (p.o.mt == kTallMT) p.o.ksub = residual_splits(p.o, m.H / 16, m.nq * m.d / m.ktile);
-  if (p.dn.mt == kTallMT) p.dn.ksub = residual_splits(p.dn, m.H / 16, m.I / m.ktile);
+  if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile);
+  if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   // Context chunks per (request, KV group): enough workgroups to fill the chip at small
@@ -282,15 +283,20 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
 
 struct InjectPlan {
   Plan fuse, kv;
-  size_t c, total;
+  size_t c, fpart, total;
 };
 
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
-  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1);   // narrow N, deep K: split-K
+  // The fusion (narrow N, deep K) splits K: over waves at few rows, over workgroups in the
+  // 128-row kernel.
+  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
+  if (p.fuse.mt == kTallMT) p.fuse.ksub = ksplit_count(p.fuse, m.H / 16, m.F / m.ktile);
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4, m.bf16 != 0);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
+  const int splits = p.fuse.mt == kTallMT ? p.fuse.ksub : 1;
+  p.fpart = c.take(splits > 1 ? (size_t)splits * rows * m.H * 4 : 0);
   p.total = c.off;
   return p;
 }
@@ -474,7 +480,8 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
 
   for (int r0 = 0; r0 < n_tok; r0 += chunk_rows) {
     const int rows = std::min(chunk_rows, n_tok - r0);
-    const InjectPlan cp = rows == chunk_rows ? ip : inject_plan(m, rows);
+    InjectPlan cp = rows == chunk_rows ? ip : inject_plan(m, rows);
+    if (cp.total > ws_bytes) cp.fuse.ksub = 1;   // a short last chunk's extra k-slices: unsplit
     {  // fusion of the concatenated target features: c = W_fuse . X (fp32 out)
       GemmParams g = base_params(cp.fuse, wb + P.w_fuse, 0, m.F / m.ktile,
                                  reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
@@ -482,6 +489,8 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.a_kind = m.bf16 ? A_ROW_BF16 : A_ROW_F32;
       g.out = cbuf;
       g.ldo = m.H;
+      g.ksplit = cp.fuse.mt == kTallMT ? cp.fuse.ksub : 1;
+      g.partial = reinterpret_cast<float*>(ws + cp.fpart);
       DF_TRY(launch_gemm(m.bf16, cp.fuse.mt, cp.fuse.npw, EPI_STORE, g, 1, stream));
     }
     {  // every layer's K|V projection of c, RoPE on K, written into the paged cache

@@ -521,11 +521,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   __shared__ TallSmem sm;
   __shared__ float rstd_s[kTallM];
   __shared__ float ssq_s[256];
-  static_assert(AK == A_HILO || AK == A_SWZ, "fragment-layout activations");
-  // bf16 pieces per fp32 A value: two, three for the injection (its results end in the cache)
-  constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
+  static_assert(AK == A_HILO || AK == A_SWZ || AK == A_ROW_BF16, "activation kinds");
+  // bf16 pieces per A value: the bf16 target features are exact; fp32 values split in two,
+  // three for the injection (its results end in the cache).
+  constexpr int kTerms = AK == A_ROW_BF16 ? 1 : (EPI == EPI_INJECT ? 3 : 2);
   static_assert(AK != A_HILO || kTerms == 2, "pair pieces carry two terms");
-  constexpr int kAChunks = 4;   // 16-byte A chunks per thread
+  constexpr int kAChunks = AK == A_ROW_BF16 ? 2 : 4;   // 16-byte A chunks per thread
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
   const int z = blockIdx.z;
@@ -549,7 +550,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     rb = blockIdx.x / ncb;
   }
   // k-tiles [kb, kb + KT) of this workgroup's slice of the k range.
-  const int S = EPI == EPI_RESIDUAL ? max(p.ksplit, 1) : 1, sl = blockIdx.y;
+  const int S = (EPI == EPI_RESIDUAL || EPI == EPI_STORE) ? max(p.ksplit, 1) : 1;
+  const int sl = blockIdx.y;
   const int kb = (sl * p.KT) / S;
   const int KT = ((sl + 1) * p.KT) / S - kb;
   const int ntv = min(kTallNT, p.n_tiles - cb * kTallNT);   // valid n-tiles (ragged last)
@@ -583,13 +585,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // half c % 2 of the lane's 8 k values, so neighbouring threads write neighbouring 8-byte
   // halves of the LDS fragments.
   // Pair layout: chunk c is m-tile c / 128, piece (c / 64) % 2, lane c % 64, copied as is.
-  // n-tiles past a ragged last column block re-read its last valid n-tile (their columns are
-  // never stored).
+  // bf16 rows: chunk c is m-tile c / 64, lane c % 64 (row l % 16, k 8 (l / 16) .. + 8), read
+  // from the row (rows past M re-read row M - 1).  n-tiles past a ragged last column block
+  // re-read its last valid n-tile (their columns are never stored).
   auto load_stage = [&](int kt, f32x4 (&a)[kAChunks], i32x4 (&w)[2]) {
     const int ktc = kb + min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-      const int c = tid + i * 256, mt = c / 128;
+      const int c = tid + i * 256;
+      if constexpr (AK == A_ROW_BF16) {
+        const int l = c % 64, row = min((mtile0 + c / 64) * 16 + (l & 15), p.M - 1);
+        a[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const bf16*>(p.A) +
+                                               (long long)row * p.lda + ktc * 32 + (l >> 4) * 8);
+        continue;
+      }
+      const int mt = c / 128;
       const int mtc = min(mtile0 + mt, n_mtiles_valid - 1);
       if constexpr (AK == A_HILO) {
         const int piece = (c / 64) % 2, l = c % 64;
@@ -615,6 +625,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
       const int c = tid + i * 256, mt = c / 128;
+      if constexpr (AK == A_ROW_BF16) {
+        sm.st.a[buf][0][c / 64][c % 64] = __builtin_bit_cast(i32x4, a[i]);
+        continue;
+      }
       if constexpr (AK == A_HILO) {
         sm.st.a[buf][(c / 64) % 2][mt][c % 64] = __builtin_bit_cast(i32x4, a[i]);
         continue;
@@ -721,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
         if (col < cols) sm.tile[r * ld + col] = v;
       }
   __syncthreads();
-  if (EPI == EPI_RESIDUAL && S > 1) {   // k-slice partial: rows of the tile, row-major
+  if ((EPI == EPI_RESIDUAL || EPI == EPI_STORE) && S > 1) {   // k-slice partial, row-major
     for (int idx = tid; idx < kTallM * cols; idx += 256) {
       const int r = idx / cols, c = idx % cols, m = rb * kTallM + r;
       if (m < p.M)
@@ -800,11 +814,13 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
   return hipErrorInvalidValue;
 }
 
-// Residual reduction of a k-split 128-row GEMM: thread (row m, column quad) adds the slices'
-// four columns in slice order to x and writes x and x * gamma_next (pair layout); the four
-// threads of an n-tile (adjacent lanes) sum the squares of its 16 columns for the next norm
-// -- the residual epilogue of the unsplit kernel.
-__global__ __launch_bounds__(256) void residual_reduce_kernel(GemmParams p, int splits) {
+// Reduction of a k-split 128-row GEMM: thread (row m, column quad) adds the slices' four
+// columns in slice order.  EPI_STORE: the sum is the output (fp32 fragment layout).
+// EPI_RESIDUAL: it is added to x, and x and x * gamma_next (pair layout) are written; the
+// four threads of an n-tile (adjacent lanes) sum the squares of its 16 columns for the next
+// norm -- the epilogues of the unsplit kernel.
+template <int EPI>
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int splits) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const int quads = p.n_tiles * 4;
   const bool live = idx < (long long)p.M * quads;
@@ -816,15 +832,15 @@ __global__ __launch_bounds__(256) void residual_reduce_kernel(GemmParams p, int 
     for (int sl = 0; sl < splits; ++sl)
       v += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo + col);
     f32x4* xp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, col, kto, 8));
-    const f32x4 xn = *xp + v;
+    const f32x4 xn = EPI == EPI_RESIDUAL ? *xp + v : v;
     *xp = xn;
-    if (p.xg_out) {
+    if (EPI == EPI_RESIDUAL && p.xg_out) {
       const f32x4 g = *reinterpret_cast<const f32x4*>(p.gamma_next + col);
       store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, col, kto), xn * g);
       ss = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
     }
   }
-  if (p.xg_out) {   // quads of one n-tile are lanes 4t .. 4t+3 (quads per row is a multiple of 4)
+  if (EPI == EPI_RESIDUAL && p.xg_out) {   // an n-tile's quads: lanes 4t .. 4t+3
     ss += __shfl_xor(ss, 1, kWave);
     ss += __shfl_xor(ss, 2, kWave);
     if (live && (cq & 3) == 0) p.ssq_out[(long long)(cq / 4) * p.ssq_ld + m] = ss;
@@ -835,14 +851,16 @@ template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
   const int ncb_grid = p.n_mblocks <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
-  const int splits = EPI == EPI_RESIDUAL ? std::max(p.ksplit, 1) : 1;
+  const int splits = (EPI == EPI_RESIDUAL || EPI == EPI_STORE) ? std::max(p.ksplit, 1) : 1;
   if (splits > 1 && (layers != 1 || !p.partial || p.KT < splits || p.ldo % 16 != 0))
     return hipErrorInvalidValue;
   dim3 grid(ncb_grid * p.n_mblocks, splits, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
-  if (splits > 1) {
-    const long long threads = (long long)p.M * p.n_tiles * 4;
-    residual_reduce_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
+  if constexpr (EPI == EPI_RESIDUAL || EPI == EPI_STORE) {
+    if (splits > 1) {
+      const long long threads = (long long)p.M * p.n_tiles * 4;
+      ksplit_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
+    }
   }
   return hipGetLastError();
 }
@@ -854,6 +872,8 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
     const bool norm = p.norm != 0;
     if (p.a_kind == A_SWZ && epi == EPI_INJECT && !norm)
       return go_tall<A_SWZ, EPI_INJECT, false>(p, layers, stream);
+    if (p.a_kind == A_ROW_BF16 && epi == EPI_STORE && !norm && p.lda % 8 == 0)
+      return go_tall<A_ROW_BF16, EPI_STORE, false>(p, layers, stream);
     if (p.a_kind != A_HILO) return hipErrorInvalidValue;
     if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
     if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
