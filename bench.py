@@ -83,7 +83,7 @@ def main():
     wd = {k: v.to(dev) for k, v in w.items()}
     table, num_pages = synth.page_table(wl.name, ctx, cfg.page_size, wl.seed)
     dr = Drafter(cfg, wd, max_batch=Bn, max_ctx=table.shape[1] * cfg.page_size,
-                 max_inject_rows=256, device=dev)
+                 max_inject_rows=min(max(256, Bn * n_new), 1024), device=dev)
     embed = wd["embed"]
     del wd
     torch.cuda.empty_cache()

@@ -232,14 +232,14 @@ struct DraftPlan {
   size_t total;
 };
 
-// k-slices of a 128-row store or residual GEMM: at least 256 workgroups (one per CU) and at
-// least 32 k-tiles per slice (measured: 128 output blocks leave the chip underused at 512
-// rows; at 256 blocks a split no longer pays for its partials).
-int ksplit_count(const Plan& pl, int n_tiles, int KT) {
+// k-slices of a 128-row store or residual GEMM: at least `min_wgs` workgroups and at least
+// 32 k-tiles per slice.  Measured: the residual GEMMs want one workgroup per CU (256; at 256
+// blocks a split no longer pays for its partials), the deep-K fusion two (512).
+int ksplit_count(const Plan& pl, int n_tiles, int KT, int min_wgs) {
   if (pl.mt != kTallMT) return 1;
   const long long blocks = (long long)cdiv(n_tiles, 8) * pl.n_mblocks;
   int s = 1;
-  while (blocks * s < 256 && KT / (s * 2) >= 32 && s < 8) s *= 2;
+  while (blocks * s < min_wgs && KT / (s * 2) >= 32 && s < 8) s *= 2;
   return s;
 }
 
@@ -251,8 +251,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
-  if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile);
-  if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile);
+  if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile, 256);
+  if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile, 256);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   // Context chunks per (request, KV group): enough workgroups to fill the chip at small
@@ -291,7 +291,7 @@ InjectPlan inject_plan(const Dims& m, int rows) {
   // The fusion (narrow N, deep K) splits K: over waves at few rows, over workgroups in the
   // 128-row kernel.
   p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
-  if (p.fuse.mt == kTallMT) p.fuse.ksub = ksplit_count(p.fuse, m.H / 16, m.F / m.ktile);
+  if (p.fuse.mt == kTallMT) p.fuse.ksub = ksplit_count(p.fuse, m.H / 16, m.F / m.ktile, 512);
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4, m.bf16 != 0);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
@@ -301,7 +301,7 @@ InjectPlan inject_plan(const Dims& m, int rows) {
   return p;
 }
 
-constexpr int kInjectChunkRows = 256;
+constexpr int kInjectChunkRows = 1024;   // rows per fusion + injection launch pair, at most
 
 #define DF_TRY(expr)                                  \
   do {                                                \
@@ -469,8 +469,13 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
   if (!packed || !workspace || n_tok < 0) return DFLASH_ERR_INVALID_ARG;
   if (n_tok == 0) return DFLASH_OK;
   if (!feats || !seq_idx || !pos) return DFLASH_ERR_INVALID_ARG;
-  const int chunk_rows = std::min<int>(n_tok, kInjectChunkRows);
-  const InjectPlan ip = inject_plan(m, chunk_rows);
+  // The largest chunk (up to kInjectChunkRows rows) whose buffers fit the workspace.
+  int chunk_rows = std::min<int>(n_tok, kInjectChunkRows);
+  InjectPlan ip = inject_plan(m, chunk_rows);
+  while (ip.total > ws_bytes && chunk_rows > 16) {
+    chunk_rows = std::max(16, chunk_rows / 2);
+    ip = inject_plan(m, chunk_rows);
+  }
   if (ws_bytes < ip.total) return DFLASH_ERR_WORKSPACE;
   const Packed P = packed_layout(m);
   const char* wb = reinterpret_cast<const char*>(packed);

@@ -135,9 +135,10 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
                                   void* packed, size_t packed_bytes, hipStream_t stream);
 
 /* Bytes of workspace the step calls need for up to `max_batch` requests and up to
- * `max_inject_rows` rows per dflash_fuse_inject_kv launch chunk (larger n_tok are
- * processed in chunks of this many rows, at most 256).  `max_ctx` bounds the cached
- * context (max_pages_per_seq * 16 of the cache).  Returns 0 if an argument is invalid. */
+ * `max_inject_rows` rows per dflash_fuse_inject_kv launch chunk (dflash_fuse_inject_kv
+ * processes n_tok rows in chunks of the largest size, at most 1024 rows, whose buffers fit
+ * the workspace it is given).  `max_ctx` bounds the cached context (max_pages_per_seq * 16
+ * of the cache).  Returns 0 if an argument is invalid. */
 size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
                              int32_t max_inject_rows, int32_t max_ctx);
 
