@@ -179,9 +179,9 @@ struct HeadState {
   }
 
   // One 32-key step: k[pg][ks] is the K fragment (16 keys of page pg x dims 32ks + 8q..+8),
-  // v[dt][pg] the V^T half-fragment (dim 16dt + n x keys 4q..4q+3 of page pg).
+  // v[dt] the V^T fragment of dim 16dt + n: keys 4q..4q+3 of page 0, then of page 1.
   template <bool kMasked>
-  __device__ void step(const i32x4 (&k)[2][KS], const i32x2 (&v)[DT][2], int nk) {
+  __device__ void step(const i32x4 (&k)[2][KS], const i32x4 (&v)[DT], int nk) {
     // d = 128: Q hi and Q lo products accumulate separately (four independent MFMA chains
     // of four); d = 64: one chain per page (two chains of four, no adds).
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -209,7 +209,7 @@ struct HeadState {
     softmax<kMasked>(s, nk, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      i32x4 vv = i32x4{v[dt][0][0], v[dt][0][1], v[dt][1][0], v[dt][1][1]};
+      i32x4 vv = v[dt];
       if (kMasked) vv = mask_vt(vv, q, nk);   // stale cache slots may hold any bits
       o[dt] = mfma_tile<bf16>(vv, ph, o[dt]);
       o[dt] = mfma_tile<bf16>(vv, pl, o[dt]);
@@ -381,11 +381,25 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
   int st = 0;
   // Steps of the steady state are full (at least two more follow them); the tail takes the
   // masked form, since its last step may be the chunk's partial one.
-  auto tail_step = [&](const StepRegs<D>& r) { hs.template step<true>(r.k, r.v, r.nk); };
+  auto vfrags = [](const StepRegs<D>& r, i32x4 (&v)[DT]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      v[dt] = i32x4{r.v[dt][0][0], r.v[dt][0][1], r.v[dt][1][0], r.v[dt][1][1]};
+  };
+  auto full_step = [&](const StepRegs<D>& r) {
+    i32x4 v[DT];
+    vfrags(r, v);
+    hs.template step<false>(r.k, v, r.nk);
+  };
+  auto tail_step = [&](const StepRegs<D>& r) {
+    i32x4 v[DT];
+    vfrags(r, v);
+    hs.template step<true>(r.k, v, r.nk);
+  };
   for (; st + 3 < nsteps; st += 2) {
-    hs.template step<false>(ra.k, ra.v, ra.nk);
+    full_step(ra);
     load_step(st + 2, ra);
-    hs.template step<false>(rb.k, rb.v, rb.nk);
+    full_step(rb);
     load_step(st + 3, rb);
   }
   // 0..3 steps remain.
@@ -406,12 +420,14 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
 // LDS-staged variant (G >= 4).  A step (two pages of K and of V, 128 d bytes) is loaded as
 // 16-byte pieces, d / (8 G) per thread: piece p of the step (p = j * 64G + thread) is bytes
 // 16 (p mod 2d) .. +16 of quarter p / 2d, the quarters being K page 0, K page 1, V page 0
-// and V page 1 (32 d bytes each, contiguous in the cache).  Pieces are staged in registers RS steps
-// ahead and written to an LDS double buffer, XOR-swizzled so that the fragment reads hit
-// distinct banks:
+// and V page 1 (32 d bytes each, contiguous in the cache).  Pieces are staged in registers
+// RS steps ahead and written to an LDS double buffer, XOR-swizzled so that the fragment
+// reads hit distinct banks:
 //   K row r (2d bytes): 16-byte piece j sits at piece j ^ swz(r), swz(r) = r & 15 (d = 128)
 //                       or (r >> 1) & 7 (d = 64);
-//   V row `dim` (32 bytes, keys 0..15): 16-byte half h sits at half h ^ ((dim >> 3) & 1).
+//   V rows of both pages interleaved: row `dim` is 64 bytes, 16-byte chunk c holding keys
+//   4c'..4c'+3 of page 0 then of page 1 for c' = c ^ ((dim >> 2) & 3) -- exactly one V^T
+//   MFMA fragment, so a lane's fragment is one 16-byte read.
 // One barrier per step: after it, the stage holding step t is complete and every wave has
 // finished reading step t - 1, whose stage the step-(t + 1) pieces then overwrite.
 // ------------------------------------------------------------------------------------------
@@ -448,8 +464,9 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   const int nsteps = cs.nsteps;
 
   // Static description of this thread's pieces: quarter (page, K or V), source byte offset
-  // inside the page's K or V block, and LDS byte offset inside a stage.
-  int src_off[NL], dst_off[NL];
+  // inside the page's K or V block, and LDS byte offsets inside a stage (V pieces: the two
+  // 8-byte halves go to two places).
+  int src_off[NL], dst_off[NL], dst_off2[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const int p = j * L::kThreads + tid;
@@ -459,12 +476,13 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
       const int r = e / (D / 8), jj = e % (D / 8);
       src_off[j] = e * 16;
       dst = r * 2 * D + ((jj ^ k_swz<D>(r)) * 16);
-    } else {                            // V^T: row dim, half h
-      const int dim = e / 2, h = e % 2;
+    } else {                            // V^T: row dim, keys 8h .. 8h+7 of page quarter - 2
+      const int dim = e / 2, h = e % 2, pg = quarter - 2, sw = (dim >> 2) & 3;
       src_off[j] = e * 16;
-      dst = dim * 32 + ((h ^ ((dim >> 3) & 1)) * 16);
+      dst = 2 * L::kQuarter + dim * 64 + (((2 * h) ^ sw) * 16) + pg * 8;
+      dst_off2[j] = 2 * L::kQuarter + dim * 64 + (((2 * h + 1) ^ sw) * 16) + pg * 8;
     }
-    dst_off[j] = quarter * L::kQuarter + dst;
+    dst_off[j] = quarter < 2 ? quarter * L::kQuarter + dst : dst;
   }
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
@@ -480,25 +498,31 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   };
   auto store_pieces = [&](int stage, const i32x4 (&r)[NL]) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) *reinterpret_cast<i32x4*>(kv_s[stage] + dst_off[j]) = r[j];
+    for (int j = 0; j < NL; ++j) {
+      if ((j * L::kThreads + hh * kWave) / (2 * D) < 2) {   // K (uniform over the wave)
+        *reinterpret_cast<i32x4*>(kv_s[stage] + dst_off[j]) = r[j];
+      } else {
+        *reinterpret_cast<i32x2*>(kv_s[stage] + dst_off[j]) = i32x2{r[j][0], r[j][1]};
+        *reinterpret_cast<i32x2*>(kv_s[stage] + dst_off2[j]) = i32x2{r[j][2], r[j][3]};
+      }
+    }
   };
-  // Fragments of one step from a stage (layouts as in attn_partial_bf16).
+  // Fragments of one step from a stage: K as in attn_partial_bf16; a V^T fragment (both
+  // pages' keys 4q..4q+3 of one dim) is one 16-byte read.
   auto compute = [&](HeadState<D>& hs, int stage, int st, auto masked) {
     const char* sb = kv_s[stage];
-    i32x4 k[2][KS];
-    i32x2 v[DT][2];
+    i32x4 k[2][KS], v[DT];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
+    for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         k[pg][ks] = *reinterpret_cast<const i32x4*>(
             sb + pg * L::kQuarter + n * 2 * D + (((ks * 4 + q) ^ k_swz<D>(n)) * 16));
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int dim = 16 * dt + n;
-        v[dt][pg] = *reinterpret_cast<const i32x2*>(
-            sb + (2 + pg) * L::kQuarter + dim * 32 + ((q ^ (((dim >> 3) & 1) * 2)) * 8));
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = 16 * dt + n;
+      v[dt] = *reinterpret_cast<const i32x4*>(sb + 2 * L::kQuarter + dim * 64 +
+                                              ((q ^ ((dim >> 2) & 3)) * 16));
     }
     hs.template step<decltype(masked)::value>(k, v, min(32, cs.kend - cs.kbeg - 32 * st));
   };
