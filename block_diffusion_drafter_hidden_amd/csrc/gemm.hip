@@ -496,12 +496,15 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
 // ------------------------------------------------------------------------------------------
 // Tall variant for many rows (batched drafts, prefill chunks): a workgroup of 4 waves owns a
 // 128-row x 128-column output block and walks K one 32-wide k-tile at a time.  Each k-tile's
-// A block (8 m-tiles of fp32 fragments, 16 KB) and W block (8 n-tiles, 8 KB) are staged in
-// LDS once (double-buffered, next k-tile's loads in flight during this one's MFMAs) and each
-// wave computes a 64 x 64 quarter from them: 4 A and 4 W fragments feed 16 tile products,
-// each as hi + lo (+ mid) bf16 MFMAs.  Weights are thus read once per 128 rows and
-// activations once per 128 columns.  The finished block goes through LDS to the same
-// epilogues as the streaming kernel.
+// W block (8 n-tiles, 8 KB) is staged in LDS once (double-buffered, later k-tiles' loads in
+// flight during this one's MFMAs).  Activations in the pair layout are MFMA fragments
+// already: each wave loads the hi and lo fragments of its own 32 rows straight into
+// registers and computes a 32 x 128 strip (2 x 8 tile products, each as hi + lo bf16 MFMAs).
+// The other kinds (the injection's fp32 input, split into three pieces; the fusion's bf16
+// rows) are staged in LDS with W, converted once per workgroup, and each wave computes a
+// 64 x 64 quarter.  Weights are thus read once per 128 rows and activations once per 128
+// columns.  The finished block goes through LDS to the same epilogues as the streaming
+// kernel.
 // ------------------------------------------------------------------------------------------
 constexpr int kTallM = 128, kTallN = 128;
 constexpr int kTallMT = kTallM / 16, kTallNT = kTallN / 16;
@@ -522,10 +525,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   __shared__ float rstd_s[kTallM];
   __shared__ float ssq_s[256];
   static_assert(AK == A_HILO || AK == A_SWZ || AK == A_ROW_BF16, "activation kinds");
-  // bf16 pieces per A value: the bf16 target features are exact; fp32 values split in two,
-  // three for the injection (its results end in the cache).
-  constexpr int kTerms = AK == A_ROW_BF16 ? 1 : (EPI == EPI_INJECT ? 3 : 2);
-  static_assert(AK != A_HILO || kTerms == 2, "pair pieces carry two terms");
+  // Staged kinds, bf16 pieces per A value: the bf16 target features are exact; the fp32
+  // fused features split in three (the injection's results end in the cache).
+  constexpr int kTerms = AK == A_ROW_BF16 ? 1 : 3;
+  static_assert(AK != A_SWZ || EPI == EPI_INJECT, "fp32 fragments feed the injection");
   constexpr int kAChunks = AK == A_ROW_BF16 ? 2 : 4;   // 16-byte A chunks per thread
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;           // this wave's 64 x 64 quarter
@@ -572,10 +575,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     }
   }
 
-  // Global -> register staging of one k-tile: 4 A chunks and 2 W chunks of 16 bytes per
-  // thread.  A ring of kRing register stages keeps kRing - 1 k-tiles of loads in flight
-  // beyond the one being multiplied, so memory latency overlaps several k-tiles of MFMAs.
-  constexpr int kRing = AK == A_HILO ? 3 : 2;   // the three-piece split needs registers
+  // Staged kinds: global -> register staging of one k-tile, 4 (2) A chunks and 2 W chunks of
+  // 16 bytes per thread.  A ring of kRing register stages keeps kRing - 1 k-tiles of loads
+  // in flight beyond the one being multiplied (the three-piece split needs the registers
+  // a deeper ring would take).
+  constexpr int kRing = 2;
   f32x4 ra[kRing][kAChunks];
   i32x4 rw[kRing][2];
   // Loads are unconditional (no divergent branches, so the waits stay precise): k-tiles past
@@ -584,7 +588,6 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   // A chunk c (16 bytes: 4 floats of one fragment lane) is m-tile c / 128, lane (c / 2) % 64,
   // half c % 2 of the lane's 8 k values, so neighbouring threads write neighbouring 8-byte
   // halves of the LDS fragments.
-  // Pair layout: chunk c is m-tile c / 128, piece (c / 64) % 2, lane c % 64, copied as is.
   // bf16 rows: chunk c is m-tile c / 64, lane c % 64 (row l % 16, k 8 (l / 16) .. + 8), read
   // from the row (rows past M re-read row M - 1).  n-tiles past a ragged last column block
   // re-read its last valid n-tile (their columns are never stored).
@@ -601,16 +604,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       }
       const int mt = c / 128;
       const int mtc = min(mtile0 + mt, n_mtiles_valid - 1);
-      if constexpr (AK == A_HILO) {
-        const int piece = (c / 64) % 2, l = c % 64;
-        a[i] = *reinterpret_cast<const f32x4*>(
-            reinterpret_cast<const bf16*>(p.A) + ((long long)mtc * p.KT + ktc) * 1024 +
-            piece * kHiLoStride + l * 8);
-      } else {
-        const int g = c % 2, l = (c / 2) % 64;
-        a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * p.KT + ktc) * 2 + g) * 256 +
-                                               l * 4);
-      }
+      const int g = c % 2, l = (c / 2) % 64;
+      a[i] = *reinterpret_cast<const f32x4*>(A + (((long long)mtc * p.KT + ktc) * 2 + g) * 256 +
+                                             l * 4);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -627,10 +623,6 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       const int c = tid + i * 256, mt = c / 128;
       if constexpr (AK == A_ROW_BF16) {
         sm.st.a[buf][0][c / 64][c % 64] = __builtin_bit_cast(i32x4, a[i]);
-        continue;
-      }
-      if constexpr (AK == A_HILO) {
-        sm.st.a[buf][(c / 64) % 2][mt][c % 64] = __builtin_bit_cast(i32x4, a[i]);
         continue;
       }
       const int g = c % 2, l = (c / 2) % 64;
@@ -654,12 +646,97 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     }
   };
 
-  f32x4 acc[4][4];
+  // Wave tiles.  Staged kinds: 64 x 64 quarters (wm, wn).  Pair layout: a 32-row x 128-column
+  // strip per wave (rows 32 wave .. + 32), so no two waves need the same A fragment.
+  constexpr bool kDirect = AK == A_HILO;
+  constexpr int MI = kDirect ? 2 : 4, NJ = kDirect ? 8 : 4;
+  const int row0 = kDirect ? wave * 32 : wm * 64, col0 = kDirect ? 0 : wn * 64;
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (kDirect) {
+    // The pair layout already holds the MFMA A fragments: each wave loads its two m-tiles'
+    // hi and lo fragments (1 KB each, coalesced) straight into registers, kR k-tiles ahead.
+    // Only W is shared, so only W goes through LDS: 8 KB written and 32 KB read per k-tile
+    // instead of 24 KB and 48 KB, with a third of the LDS instructions.
+    const bf16* ap[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int mtc = min(mtile0 + wave * 2 + i, n_mtiles_valid - 1);
+      ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * p.KT * 1024 + lane * 8;
+    }
+    constexpr int kR = 3;
+    i32x4 da[kR][2][2], dw[kR][2];   // [stage][m-tile][piece], [stage][chunk]
+    auto load_a = [&](int kt, i32x4 (&a)[2][2]) {
+      const long long off = (long long)(kb + min(kt, KT - 1)) * 1024;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          a[i][q] = *reinterpret_cast<const i32x4*>(ap[i] + off + q * kHiLoStride);
+    };
+    auto load_w = [&](int kt, i32x4 (&w)[2]) {
+      const int ktc = kb + min(kt, KT - 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256, nt = min(c / 64, ntv - 1), l = c % 64;
+        w[i] = load16(W + ((long long)nt * p.nt_stride + (long long)ktc * p.kt_stride) *
+                              kTileBytes + l * 16);
+      }
+    };
+    auto store_w = [&](int buf, const i32x4 (&w)[2]) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256;
+        sm.st.w[buf][c / 64][c % 64] = w[i];
+      }
+    };
+    // Piece-major MFMA order: the two products into one accumulator are 16 apart.
+    auto compute = [&](int buf, const i32x4 (&a)[2][2]) {
+      i32x4 wf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wf[j] = sm.st.w[buf][j][lane];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = mfma_tile<bf16>(a[i][q], wf[j], acc[i][j]);
+    };
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      load_w(r, dw[r]);
+      load_a(r, da[r]);
+    }
+    store_w(0, dw[0]);
+    __syncthreads();
+    // Iteration kt: W stage kt % kR is in LDS and is refilled with k-tile kt + kR; A stage
+    // kt % kR is multiplied, then refilled; W of k-tile kt + 1 moves to LDS.
+    const int KTr = KT - KT % kR;
+    for (int kt0 = 0; kt0 < KTr; kt0 += kR) {
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int kt = kt0 + r;
+        load_w(kt + kR, dw[r]);
+        compute(kt & 1, da[r]);
+        load_a(kt + kR, da[r]);
+        store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR - 1; ++r) {
+      const int kt = KTr + r;
+      if (kt < KT) {
+        compute(kt & 1, da[r]);
+        store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+        __syncthreads();
+      }
+    }
+  } else {
   // One k-tile from LDS: every fragment read first (one wait), then the MFMAs ordered piece-
   // major so the two (three) products into one accumulator are 16 instructions apart.
   auto compute = [&](int buf) {
@@ -706,6 +783,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       __syncthreads();
     }
   }
+  }
 
   if constexpr (NORM) {
     const int r = tid % kTallM, m = rb * kTallM + r;
@@ -723,13 +801,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   }
   const int cols = ntv * 16, ld = cols + 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        const int col = wn * 64 + j * 16 + (lane & 15);
+        const int r = row0 + i * 16 + (lane >> 4) * 4 + e;
+        const int col = col0 + j * 16 + (lane & 15);
         float v = acc[i][j][e];
         if constexpr (NORM) v *= rstd_s[r];
         if (col < cols) sm.tile[r * ld + col] = v;
