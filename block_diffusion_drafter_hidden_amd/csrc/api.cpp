@@ -232,9 +232,9 @@ struct DraftPlan {
   size_t total;
 };
 
-// k-slices of a 128-row store or residual GEMM: at least `min_wgs` workgroups and at least
-// 32 k-tiles per slice.  Measured: the residual GEMMs want one workgroup per CU (256; at 256
-// blocks a split no longer pays for its partials), the deep-K fusion two (512).
+// k-slices of a 128-row store, residual or Q|K|V GEMM: at least `min_wgs` workgroups and at
+// least 32 k-tiles per slice.  Measured: the residual GEMMs want one workgroup per CU (256;
+// at 256 blocks a split no longer pays for its partials), the deep-K fusion two (512).
 int ksplit_count(const Plan& pl, int n_tiles, int KT, int min_wgs) {
   if (pl.mt != kTallMT) return 1;
   const long long blocks = (long long)cdiv(n_tiles, 8) * pl.n_mblocks;
@@ -251,6 +251,8 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
   p.gu = plan_gemm(2 * m.I / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
+  const int qkv_tiles = (m.nq + 2 * m.nkv) * m.d / 16;
+  if (p.qkv.mt == kTallMT) p.qkv.ksub = ksplit_count(p.qkv, qkv_tiles, m.H / m.ktile, 256);
   if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile, 256);
   if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile, 256);
   const int kv_groups = B * m.nkv;
@@ -275,8 +277,15 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
   p.keys = c.take(lm_keys_bytes(m, rows));
+  // k-split partials: row-major for the O and down projections, whole 128 x 128 blocks for
+  // Q|K|V (one buffer, used by one GEMM at a time).
   const int splits = std::max(p.o.mt == kTallMT ? p.o.ksub : 1, p.dn.mt == kTallMT ? p.dn.ksub : 1);
-  p.kpart = c.take(splits > 1 ? (size_t)splits * rows * m.H * 4 : 0);
+  const size_t row_part = splits > 1 ? (size_t)splits * rows * m.H * 4 : 0;
+  const int qkv_splits = p.qkv.mt == kTallMT ? p.qkv.ksub : 1;
+  const size_t tile_part = qkv_splits > 1 ? (size_t)qkv_splits * cdiv(qkv_tiles, 8) *
+                                                p.qkv.n_mblocks * kTallMT * 16 * 128 * 4
+                                          : 0;
+  p.kpart = c.take(std::max(row_part, tile_part));
   p.total = c.off;
   return p;
 }
@@ -577,6 +586,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.n_kv = m.nkv;
       g.head_dim = m.d;
       set_rope(m, g);
+      g.ksplit = dp.qkv.mt == kTallMT ? dp.qkv.ksub : 1;
+      g.partial = reinterpret_cast<float*>(ws + dp.kpart);
       DF_TRY(launch_gemm(m.bf16, dp.qkv.mt, dp.qkv.npw, EPI_QKV, g, 1, stream));
     }
     {  // attention over injected context + block

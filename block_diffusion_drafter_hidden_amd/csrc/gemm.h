@@ -97,10 +97,12 @@ struct GemmParams {
   int keys_ld;
   float* logits_out;        // [rows][ldo] or null
   int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
-  // 128-row kernel with EPI_RESIDUAL or EPI_STORE: the k range is split over `ksplit`
-  // workgroups per output block (grid.y); slice s writes its fp32 partial tile to
-  // partial[s][row][col] (M rows, ldo columns) and a reduction kernel adds the slices in
-  // slice order and applies the epilogue.  ksplit <= 1: no split.
+  // 128-row kernel with EPI_RESIDUAL, EPI_STORE or EPI_QKV: the k range is split over
+  // `ksplit` workgroups per output block (grid.y) and a reduction kernel adds the slices in
+  // slice order and applies the epilogue.  Store / residual: slice s writes its fp32 partial
+  // to partial[s][row][col] (M rows, ldo columns).  Q|K|V: slice s writes its un-normalized
+  // 128 x 128 block b (row block major) to partial[(s * blocks + b) * 16384 + r * 128 + c].
+  // ksplit <= 1: no split.
   int ksplit;
   float* partial;
 };

@@ -519,6 +519,39 @@ union TallSmem {
   float tile[kTallM * (kTallN + 1)];
 };
 
+// RMSNorm of a 128-row block: the rows' sums of squares come as ssq_parts partials.  Thread
+// t serves row t % 128 and parts t / 128 + 2 i: the first 8 of them are fetched early
+// (tall_ssq_prefetch, so the loads overlap the main loop), the rest at the end; the two
+// half sums of a row are added last (tall_rstd, which leaves 1 / rms in rstd_s).
+__device__ inline void tall_ssq_prefetch(const GemmParams& p, int rb, float (&sq)[8]) {
+  const int tid = threadIdx.x, m = rb * kTallM + tid % kTallM;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int part = tid / kTallM + 2 * i;
+    sq[i] = part < p.ssq_parts && m < p.M ? p.ssq_in[(long long)part * p.ssq_ld + m] : 0.f;
+  }
+}
+__device__ inline void tall_rstd(const GemmParams& p, int rb, const float (&sq)[8],
+                                 float* ssq_s, float* rstd_s) {
+  const int tid = threadIdx.x, m = rb * kTallM + tid % kTallM;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += sq[i];
+  for (int part = tid / kTallM + 16; part < p.ssq_parts; part += 2)
+    if (m < p.M) s += p.ssq_in[(long long)part * p.ssq_ld + m];
+  ssq_s[tid] = s;
+  __syncthreads();
+  if (tid < kTallM)
+    rstd_s[tid] = 1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(p.KT * 32) + p.eps);
+  __syncthreads();
+}
+
+// k-split modes of the 128-row kernel: store / residual epilogues reduce row-major partials
+// (ksplit_reduce_kernel); the Q|K|V epilogue reduces whole partial blocks
+// (ksplit_tile_reduce_kernel) and then runs the unsplit epilogue.
+template <int EPI> constexpr bool kRowSplit = EPI == EPI_RESIDUAL || EPI == EPI_STORE;
+template <int EPI> constexpr bool kTileSplit = EPI == EPI_QKV;
+
 template <int AK, int EPI, bool NORM>
 __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   __shared__ TallSmem sm;
@@ -553,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     rb = blockIdx.x / ncb;
   }
   // k-tiles [kb, kb + KT) of this workgroup's slice of the k range.
-  const int S = (EPI == EPI_RESIDUAL || EPI == EPI_STORE) ? max(p.ksplit, 1) : 1;
+  const int S = (kRowSplit<EPI> || kTileSplit<EPI>) ? max(p.ksplit, 1) : 1;
   const int sl = blockIdx.y;
   const int kb = (sl * p.KT) / S;
   const int KT = ((sl + 1) * p.KT) / S - kb;
@@ -564,15 +597,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   const char* W = p.W + (long long)z * p.w_zstride +
                   (long long)(p.nt0 + cb * kTallNT) * p.nt_stride * kTileBytes;
 
-  // RMSNorm: partial sums of squares of this block's rows, summed in a fixed order later.
-  float sq[NORM ? 8 : 1];
+  // RMSNorm of this block's rows (unsplit: a k-split's reduction applies it).
+  float sq[8];
   if constexpr (NORM) {
-    const int r = tid % kTallM, m = rb * kTallM + r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int part = tid / kTallM + 2 * i;
-      sq[i] = part < p.ssq_parts && m < p.M ? p.ssq_in[(long long)part * p.ssq_ld + m] : 0.f;
-    }
+    if (S == 1) tall_ssq_prefetch(p, rb, sq);
   }
 
   // Staged kinds: global -> register staging of one k-tile, 4 (2) A chunks and 2 W chunks of
@@ -786,18 +814,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
   }
 
   if constexpr (NORM) {
-    const int r = tid % kTallM, m = rb * kTallM + r;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s += sq[i];
-    for (int part = tid / kTallM + 16; part < p.ssq_parts; part += 2)
-      if (m < p.M) s += p.ssq_in[(long long)part * p.ssq_ld + m];
-    ssq_s[tid] = s;
-    __syncthreads();
-    if (tid < kTallM)
-      rstd_s[tid] =
-          1.0f / sqrtf((ssq_s[tid] + ssq_s[tid + kTallM]) / (float)(p.KT * 32) + p.eps);
-    __syncthreads();
+    if (S == 1) tall_rstd(p, rb, sq, ssq_s, rstd_s);
   }
   const int cols = ntv * 16, ld = cols + 1;
 #pragma unroll
@@ -809,15 +826,26 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
         const int r = row0 + i * 16 + (lane >> 4) * 4 + e;
         const int col = col0 + j * 16 + (lane & 15);
         float v = acc[i][j][e];
-        if constexpr (NORM) v *= rstd_s[r];
+        if constexpr (NORM) {
+          if (S == 1) v *= rstd_s[r];
+        }
         if (col < cols) sm.tile[r * ld + col] = v;
       }
   __syncthreads();
-  if ((EPI == EPI_RESIDUAL || EPI == EPI_STORE) && S > 1) {   // k-slice partial, row-major
-    for (int idx = tid; idx < kTallM * cols; idx += 256) {
-      const int r = idx / cols, c = idx % cols, m = rb * kTallM + r;
-      if (m < p.M)
-        p.partial[((long long)sl * p.M + m) * p.ldo + cb * kTallN + c] = sm.tile[r * ld + c];
+  if (S > 1) {
+    if constexpr (kRowSplit<EPI>) {   // k-slice partial, row-major [slice][row][column]
+      for (int idx = tid; idx < kTallM * cols; idx += 256) {
+        const int r = idx / cols, c = idx % cols, m = rb * kTallM + r;
+        if (m < p.M)
+          p.partial[((long long)sl * p.M + m) * p.ldo + cb * kTallN + c] = sm.tile[r * ld + c];
+      }
+    } else if constexpr (kTileSplit<EPI>) {   // whole block [slice][block][row][128 columns]
+      const long long blk = (long long)rb * ncb + cb;
+      float* dst = p.partial + ((long long)sl * ncb * nrb + blk) * (kTallM * kTallN);
+      for (int idx = tid; idx < kTallM * cols; idx += 256) {
+        const int r = idx / cols, c = idx % cols;
+        if (rb * kTallM + r < p.M) dst[r * kTallN + c] = sm.tile[r * ld + c];
+      }
     }
     return;
   }
@@ -925,19 +953,88 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
   }
 }
 
+// Reduction of a block-wise k-split: kTileSubs workgroups per 128 x 128 output block, each
+// taking 32 of its rows, add the slices' partial blocks in slice order (16-byte loads, a
+// whole slice's loads in flight at once), apply the rows' RMSNorm scale and run the
+// unsplit epilogue on the 32-row tile.
+constexpr int kTileSubs = 4, kSubRows = kTallM / kTileSubs;
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256) void ksplit_tile_reduce_kernel(GemmParams p, int splits) {
+  __shared__ float tile[kSubRows * (kTallN + 1)];
+  __shared__ float rstd_s[kSubRows];
+  __shared__ float ssq_s[256];
+  const int tid = threadIdx.x;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nblk = ncb * p.n_mblocks;
+  const int blk = blockIdx.x / kTileSubs, sub = blockIdx.x % kTileSubs;
+  const int rb = blk / ncb, cb = blk % ncb;
+  const int cols = min(kTallNT, p.n_tiles - cb * kTallNT) * 16, ld = cols + 1;
+  const int m0 = rb * kTallM + sub * kSubRows;
+  const int rows = min(kSubRows, p.M - m0);
+  if (rows <= 0) return;
+  if constexpr (NORM) {   // thread t: row t % 32, parts t / 32 + 8 i; then the 8 sums in order
+    const int r = tid % kSubRows, m = m0 + r;
+    float s = 0.f;
+    if (r < rows)
+      for (int part = tid / kSubRows; part < p.ssq_parts; part += 256 / kSubRows)
+        s += p.ssq_in[(long long)part * p.ssq_ld + m];
+    ssq_s[tid] = s;
+    __syncthreads();
+    if (tid < kSubRows) {
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < 256 / kSubRows; ++g) t += ssq_s[g * kSubRows + tid];
+      rstd_s[tid] = 1.0f / sqrtf(t / (float)(p.KT * 32) + p.eps);
+    }
+    __syncthreads();
+  }
+  const int q4 = cols / 4;   // 16-byte chunks per row
+  const float* src = p.partial + (long long)blk * (kTallM * kTallN) +
+                     (long long)sub * kSubRows * kTallN;
+  const long long sstride = (long long)nblk * (kTallM * kTallN);
+  constexpr int kPer = kSubRows * kTallN / 4 / 256;   // chunks per thread (full block)
+  f32x4 v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < splits; ++sl) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + j * 256, r = q / q4, c = (q % q4) * 4;
+      if (r < rows)
+        v[j] += *reinterpret_cast<const f32x4*>(src + sl * sstride + r * kTallN + c);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + j * 256, r = q / q4, c = (q % q4) * 4;
+    if (r < rows) {
+      const float sc = NORM ? rstd_s[r] : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[r * ld + c + e] = v[j][e] * sc;
+    }
+  }
+  __syncthreads();
+  const float xpre[1] = {0.f};
+  run_epilogue<bf16, kSubRows / 16, EPI, 0>(p, tile, cols, cb * kTallNT,
+                                             rb * kTileSubs + sub, 0, cb, xpre);
+}
+
 template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
   const int ncb_grid = p.n_mblocks <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
-  const int splits = (EPI == EPI_RESIDUAL || EPI == EPI_STORE) ? std::max(p.ksplit, 1) : 1;
-  if (splits > 1 && (layers != 1 || !p.partial || p.KT < splits || p.ldo % 16 != 0))
+  const int splits = (kRowSplit<EPI> || kTileSplit<EPI>) ? std::max(p.ksplit, 1) : 1;
+  if (splits > 1 && (layers != 1 || !p.partial || p.KT < splits ||
+                     (kRowSplit<EPI> && p.ldo % 16 != 0)))
     return hipErrorInvalidValue;
   dim3 grid(ncb_grid * p.n_mblocks, splits, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
-  if constexpr (EPI == EPI_RESIDUAL || EPI == EPI_STORE) {
-    if (splits > 1) {
+  if (splits > 1) {
+    if constexpr (kRowSplit<EPI>) {
       const long long threads = (long long)p.M * p.n_tiles * 4;
       ksplit_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
+    } else if constexpr (kTileSplit<EPI>) {
+      ksplit_tile_reduce_kernel<EPI, NORM>
+          <<<ncb * p.n_mblocks * kTileSubs, 256, 0, stream>>>(p, splits);
     }
   }
   return hipGetLastError();

@@ -100,6 +100,16 @@ def test_qwen3_8b_shape_batch32_ragged_paged():
     draft_and_check(WORKLOADS["qwen3_b32"], 2, "b32")
 
 
+def test_qwen3_8b_shape_batch8_deep_ksplits():
+    # 128 rows at the Qwen3-8B width: the Q|K|V and O GEMMs split K four ways and the down
+    # projection eight ways (few output blocks), so every k-split reduction runs at its
+    # largest slice count.
+    from workloads import QWEN3_8B, Workload
+    wl = Workload("qwen3-8b-shaped-b16-drafter-batch8-ctx256..1024", QWEN3_8B, batch=8,
+                  ctx=(256, 1024), seed=5)
+    draft_and_check(wl, 2, "b8")
+
+
 def test_llama_shape_batch64_ctx4096_draft_logits():
     draft_and_check(WORKLOADS["llama_b64"], 1, "b64")
 
