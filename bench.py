@@ -19,6 +19,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, per dtype
 
 
 def parse():
@@ -237,6 +238,27 @@ def main():
     step_bytes += es * int(sum(int(T) for T in ctx)) * L * 2 * kvd       # context K/V read
     drafted = Bn * 15
     value = drafted / (ms * 1e-3)
+
+    # The LM head is HBM-bound while its rows are few (15 flop per weight byte at one
+    # request) and MFMA-bound past the ridge (peak flops / peak bytes): the roofline object
+    # takes whichever bound is the larger time.
+    lm_flops = 2.0 * V * H * rows
+    kern = ("gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>" if rows <= 64 or cfg.dtype != "bf16"
+            else "gemm_tall<A_HILO,EPI_ARGMAX,norm>")
+    roofline = {"kernel": f"shared LM head + argmax: {kern}; launch_us spans the entry "
+                          "point's three launches (rows to fragment layout, LM-head GEMM, "
+                          "argmax finalize)",
+                "launch_us": round(lm_us, 2), "bytes_per_launch": int(lm_bytes),
+                "flops_per_launch": int(lm_flops)}
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if lm_flops / (mfma_peak * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9):
+        tf = lm_flops / (lm_us * 1e-6) / 1e12
+        roofline.update({"bound": "mfma", "achieved": round(tf, 1), "peak": mfma_peak,
+                         "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": None})
+    else:
+        roofline.update({"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(wl.name)})
     out = {
         "metric": "drafted tokens/s (DFlash b16 draft step: inject + draft + verify)",
         "value": round(value, 1),
@@ -255,13 +277,7 @@ def main():
                    "layers": cfg.n_layers, "hidden": H, "vocab": V, "graph": graph is not None},
         "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
-        "roofline": {"kernel": "shared LM head + argmax: gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>; "
-                               "launch_us spans the entry point's three launches (rows to "
-                               "fragment layout, LM-head GEMM, argmax finalize)",
-                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name), "launch_us": round(lm_us, 2),
-                     "bytes_per_launch": int(lm_bytes)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s_timed": round(t_wall, 3),

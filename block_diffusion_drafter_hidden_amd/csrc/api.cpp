@@ -124,6 +124,7 @@ struct Plan {
 // instead of once per 64; a ragged last column block is allowed).
 constexpr int kTallRows = 64;
 constexpr int kTallMT = 8;
+constexpr int kTallNT = 8;   // n-tiles per 128-column block of the 128-row kernel
 
 Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 16,
                bool tall_ok = false) {
@@ -164,6 +165,15 @@ Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 1
          groups % (p.tgpw * 2) == 0 && tile_fits(p.tgpw * 2))
     p.tgpw *= 2;
   return p;
+}
+
+// Partial sums of squares per row that a residual GEMM with this plan leaves for the next
+// norm: one per n-tile (streaming kernel), one per 128-column block (128-row kernel), one
+// whole-row sum (128-row kernel with a k-split: its reduction kernel takes a row per
+// workgroup).
+int residual_ssq_parts(const Plan& pl, int n_tiles) {
+  if (pl.mt != kTallMT) return n_tiles;
+  return pl.ksub > 1 ? 1 : cdiv(n_tiles, kTallNT);
 }
 
 // RoPE frequencies theta^(-2i/d) in fp64 for the epilogues that rotate q and k.
@@ -552,7 +562,10 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   float* xg = reinterpret_cast<float*>(ws + dp.xg);
   float* ssq = reinterpret_cast<float*>(ws + dp.ssq);
   const int rows = batch * 16;
-  const int n_parts = m.H / 16;   // partial sums of squares left by a residual GEMM
+  // Partial sums of squares per row left by the O projection (read by gate|up) and by the
+  // down projection (read by the next Q|K|V and the LM head).
+  const int o_parts = residual_ssq_parts(dp.o, m.H / 16);
+  const int dn_parts = residual_ssq_parts(dp.dn, m.H / 16);
   const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
 
   {  // x = embedding rows of [anchor, mask x 15]
@@ -575,7 +588,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.a_kind = act_kind(m);
       g.norm = 1;
       g.ssq_in = ssq;
-      g.ssq_parts = l == 0 ? 1 : n_parts;   // the embedding kernel leaves whole-row sums
+      g.ssq_parts = l == 0 ? 1 : dn_parts;   // the embedding kernel leaves whole-row sums
       g.ssq_ld = rows;
       g.eps = m.eps;
       g.q_out = reinterpret_cast<float*>(ws + dp.q);
@@ -632,7 +645,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.a_kind = act_kind(m);
       g.norm = 1;
       g.ssq_in = ssq;
-      g.ssq_parts = n_parts;
+      g.ssq_parts = o_parts;
       g.ssq_ld = rows;
       g.eps = m.eps;
       g.out = ws + dp.h;
@@ -656,7 +669,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       DF_TRY(launch_gemm(m.bf16, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }
-  return launch_lm_head(m, P, wb, xg, ssq, n_parts, rows, rows, true, draft_ids, logits_out,
+  return launch_lm_head(m, P, wb, xg, ssq, dn_parts, rows, rows, true, draft_ids, logits_out,
                         reinterpret_cast<unsigned long long*>(ws + dp.keys), stream);
 }
 

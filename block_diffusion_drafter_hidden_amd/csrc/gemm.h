@@ -69,9 +69,10 @@ struct GemmParams {
                             // EPI_SWIGLU: h (pair fragment layout for bf16 models, fp32
                             // fragment layout for fp32 models); ldo columns
   int ldo;
-  // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (as h) and, per n-tile,
-  // the rows' partial sums of squares ssq_out[n_tile * ssq_ld + row] -- the inputs of the
-  // next RMSNorm-folded GEMM.
+  // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (as h) and the rows'
+  // partial sums of squares ssq_out[part * ssq_ld + row] -- the inputs of the next
+  // RMSNorm-folded GEMM.  Parts: one per n-tile (streaming kernel), one per 128-column block
+  // (128-row kernel), or one whole-row sum (128-row kernel with a k-split).
   void* xg_out;
   const float* gamma_next;
   float* ssq_out;

@@ -5,7 +5,11 @@
 // weights from HBM at full bandwidth and feed each 16-byte lane chunk straight into a 16x16
 // MFMA step.  Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory
 // and enter a bf16 MFMA as a sum of bf16 pieces (see AFrag), except the bf16 target
-// features of the fusion GEMM.  Activations the drafter produces itself live in the
+// features of the fusion GEMM and, in the 128-row kernel, the LM head's input, which enters
+// as its leading bf16 piece only (the logits are the last values computed, so the error of
+// a bf16 input does not compound through later layers; measured at one request, the
+// streaming kernel runs the LM head faster with both pieces than with one, so it keeps
+// both).  Activations the drafter produces itself live in the
 // fragment layout (swz_off), so a wave's A operand for one k-tile is a couple of fully
 // coalesced 1 KB reads; the epilogues write their outputs in that layout for the next GEMM.
 //
@@ -66,8 +70,10 @@ struct ResidualPrefetch {
   static constexpr int kN = 4 * NPW * MT <= 8 ? 4 * NPW * MT : 0;   // per thread, ksub = 1 bound
 };
 
-// `part`: the workgroup's column-block index (the argmax partial it writes).
-template <typename T, int MT, int EPI, int NPRE>
+// `part`: the workgroup's column-block index (the argmax partial it writes).  SG: n-tiles per
+// partial sum of squares of the residual epilogue (1: one per n-tile, the streaming kernel;
+// kTallNT: one per 128-column block, the 128-row kernel).
+template <typename T, int MT, int EPI, int NPRE, int SG = 1>
 __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0, int mblock,
                              int z, int part, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
   const int rows = MT * 16;
@@ -109,7 +115,21 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       idx0 = tid + NPRE * nthr;
     }
     for (int idx = idx0; idx < rows * cols; idx += nthr) store(idx, nullptr);
-    if constexpr (EPI == EPI_RESIDUAL) {
+    if constexpr (EPI == EPI_RESIDUAL && SG > 1) {
+      if (p.xg_out) {   // one partial sum of squares per row over the whole column block
+        __syncthreads();
+        for (int r = tid; r < rows; r += nthr) {
+          const int m = m0 + r;
+          if (m >= p.M) continue;
+          float ss = 0.f;
+          for (int c = 0; c < cols; ++c) {
+            const float v = tl[r * ld + c];
+            ss += v * v;
+          }
+          p.ssq_out[(long long)(tile0 / SG) * p.ssq_ld + m] = ss;
+        }
+      }
+    } else if constexpr (EPI == EPI_RESIDUAL) {
       if (p.xg_out) {   // partial sum of squares of every row over each n-tile's 16 columns
         __syncthreads();
         const int ntl = cols / 16;
@@ -697,13 +717,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * p.KT * 1024 + lane * 8;
     }
     constexpr int kR = 3;
-    i32x4 da[kR][2][2], dw[kR][2];   // [stage][m-tile][piece], [stage][chunk]
-    auto load_a = [&](int kt, i32x4 (&a)[2][2]) {
+    // Pieces per A value: the LM head multiplies the hi piece only (bf16 x bf16 products,
+    // fp32 accumulation); every other GEMM both.
+    constexpr int kQ = EPI == EPI_ARGMAX ? 1 : 2;
+    i32x4 da[kR][2][kQ], dw[kR][2];   // [stage][m-tile][piece], [stage][chunk]
+    auto load_a = [&](int kt, i32x4 (&a)[2][kQ]) {
       const long long off = (long long)(kb + min(kt, KT - 1)) * 1024;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < kQ; ++q)
           a[i][q] = *reinterpret_cast<const i32x4*>(ap[i] + off + q * kHiLoStride);
     };
     auto load_w = [&](int kt, i32x4 (&w)[2]) {
@@ -723,12 +746,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       }
     };
     // Piece-major MFMA order: the two products into one accumulator are 16 apart.
-    auto compute = [&](int buf, const i32x4 (&a)[2][2]) {
+    auto compute = [&](int buf, const i32x4 (&a)[2][kQ]) {
       i32x4 wf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) wf[j] = sm.st.w[buf][j][lane];
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < kQ; ++q)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -850,7 +873,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     return;
   }
   const float xpre[1] = {0.f};
-  run_epilogue<bf16, kTallMT, EPI, 0>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, xpre);
+  run_epilogue<bf16, kTallMT, EPI, 0, kTallNT>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, xpre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -920,36 +943,54 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
   return hipErrorInvalidValue;
 }
 
-// Reduction of a k-split 128-row GEMM: thread (row m, column quad) adds the slices' four
-// columns in slice order.  EPI_STORE: the sum is the output (fp32 fragment layout).
-// EPI_RESIDUAL: it is added to x, and x and x * gamma_next (pair layout) are written; the
-// four threads of an n-tile (adjacent lanes) sum the squares of its 16 columns for the next
-// norm -- the epilogues of the unsplit kernel.
+// Reduction of a k-split 128-row GEMM: a thread adds the slices' partials of four columns in
+// slice order.  EPI_STORE: the sum is the output (fp32 fragment layout); one thread per
+// (row, column quad).  EPI_RESIDUAL: one workgroup per row; the sum is added to x, and x and
+// x * gamma_next (pair layout) are written, and the workgroup reduces the row's squares to
+// one whole-row sum for the next norm (lanes, then waves, in a fixed order), so the next
+// RMSNorm-folded GEMM reads one partial per row instead of one per n-tile.
 template <int EPI>
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int splits) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const int quads = p.n_tiles * 4;
-  const bool live = idx < (long long)p.M * quads;
-  const int m = live ? (int)(idx / quads) : 0, cq = (int)(idx % quads);
-  const int kto = p.ldo / 32, col = cq * 4;
-  float ss = 0.f;
-  if (live) {
+  const int kto = p.ldo / 32;
+  auto reduce_quad = [&](int m, int cq) -> f32x4 {
+    const int col = cq * 4;
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < splits; ++sl)
       v += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo + col);
     f32x4* xp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, col, kto, 8));
     const f32x4 xn = EPI == EPI_RESIDUAL ? *xp + v : v;
     *xp = xn;
-    if (EPI == EPI_RESIDUAL && p.xg_out) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(p.gamma_next + col);
-      store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, col, kto), xn * g);
-      ss = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+    return xn;
+  };
+  if constexpr (EPI == EPI_RESIDUAL) {
+    __shared__ float red[256 / kWave];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    float ss = 0.f;
+#pragma unroll 4
+    for (int cq = tid; cq < quads; cq += 256) {
+      const f32x4 xn = reduce_quad(m, cq);
+      if (p.xg_out) {
+        const int col = cq * 4;
+        const f32x4 g = *reinterpret_cast<const f32x4*>(p.gamma_next + col);
+        store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, col, kto), xn * g);
+        ss += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+      }
     }
-  }
-  if (EPI == EPI_RESIDUAL && p.xg_out) {   // an n-tile's quads: lanes 4t .. 4t+3
-    ss += __shfl_xor(ss, 1, kWave);
-    ss += __shfl_xor(ss, 2, kWave);
-    if (live && (cq & 3) == 0) p.ssq_out[(long long)(cq / 4) * p.ssq_ld + m] = ss;
+    if (p.xg_out) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      if (tid % kWave == 0) red[tid / kWave] = ss;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < 256 / kWave; ++w) t += red[w];
+        p.ssq_out[m] = t;   // part 0: the whole row
+      }
+    }
+  } else {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx < (long long)p.M * quads) reduce_quad((int)(idx / quads), (int)(idx % quads));
   }
 }
 
@@ -1029,7 +1070,9 @@ static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   dim3 grid(ncb_grid * p.n_mblocks, splits, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
   if (splits > 1) {
-    if constexpr (kRowSplit<EPI>) {
+    if constexpr (EPI == EPI_RESIDUAL) {   // a workgroup per row
+      ksplit_reduce_kernel<EPI><<<(unsigned)p.M, 256, 0, stream>>>(p, splits);
+    } else if constexpr (kRowSplit<EPI>) {
       const long long threads = (long long)p.M * p.n_tiles * 4;
       ksplit_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
     } else if constexpr (kTileSplit<EPI>) {

@@ -116,7 +116,8 @@ def test_draft_ids_and_logits_match_oracle(cfg, ctx):
             assert err.mean() < 5e-3 and err.max() < 5e-2, (err.mean(), err.max())
 
 
-@pytest.mark.parametrize("cfg,rows", [(SMALL_BF16, 1), (SMALL_BF16, 37), (TINY, 20)])
+@pytest.mark.parametrize("cfg,rows", [(SMALL_BF16, 1), (SMALL_BF16, 37), (SMALL_BF16, 150),
+                                      (TINY, 20)])
 def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
     """dflash_lm_head_argmax on caller-provided fp32 hidden rows (ragged row counts)."""
     w = synth.drafter_weights(cfg, seed=3)
@@ -134,8 +135,13 @@ def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
     orc = {"ids": i1, "gap": top1 - top2, "top1": top1, "top2": top2}
     bad, _ = G.compare_ids(ids.cpu().numpy(), orc, cfg.dtype)
     assert bad == 0
-    err = np.abs(logits.cpu().numpy() - lg).max() / np.abs(lg).max()
-    assert err < (1e-5 if cfg.dtype == "f32" else 1e-4), err
+    err = np.abs(logits.cpu().numpy() - lg).max()
+    if cfg.dtype == "f32":
+        assert err < 1e-5 * np.abs(lg).max(), err
+    elif rows <= 64:   # streaming kernel: both bf16 pieces of the fp32 input
+        assert err < 1e-4 * np.abs(lg).max(), err
+    else:   # 128-row kernel: bf16 input, fp32 accumulation; well inside the 2e-2 near-tie band
+        assert err < 1e-2, err
 
 
 @pytest.mark.parametrize("n_q,n_kv,d,hidden", [(2, 2, 128, 512), (4, 2, 128, 512),
