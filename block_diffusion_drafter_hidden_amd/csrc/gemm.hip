@@ -964,17 +964,42 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
     return xn;
   };
   if constexpr (EPI == EPI_RESIDUAL) {
+    // Four quads per thread per pass; every load of a pass (slices, x, gains) is issued
+    // before its first store, which the compiler may not move loads across.
+    constexpr int kQ = 4;
     __shared__ float red[256 / kWave];
     const int m = blockIdx.x, tid = threadIdx.x;
     float ss = 0.f;
-#pragma unroll 4
-    for (int cq = tid; cq < quads; cq += 256) {
-      const f32x4 xn = reduce_quad(m, cq);
-      if (p.xg_out) {
-        const int col = cq * 4;
-        const f32x4 g = *reinterpret_cast<const f32x4*>(p.gamma_next + col);
-        store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, col, kto), xn * g);
-        ss += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+    for (int base = 0; base < quads; base += kQ * 256) {
+      f32x4 v[kQ], xo[kQ], g[kQ];
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const int cq = base + tid + j * 256;
+        v[j] = xo[j] = g[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (cq < quads) {
+          xo[j] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.out) +
+                                                 swz_off(m, cq * 4, kto, 8));
+          if (p.xg_out) g[j] = *reinterpret_cast<const f32x4*>(p.gamma_next + cq * 4);
+        }
+      }
+      for (int sl = 0; sl < splits; ++sl)
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+          const int cq = base + tid + j * 256;
+          if (cq < quads)
+            v[j] += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo +
+                                                   cq * 4);
+        }
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const int cq = base + tid + j * 256;
+        if (cq >= quads) continue;
+        const f32x4 xn = xo[j] + v[j];
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, cq * 4, kto, 8)) = xn;
+        if (p.xg_out) {
+          store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, cq * 4, kto), xn * g[j]);
+          ss += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+        }
       }
     }
     if (p.xg_out) {
