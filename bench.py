@@ -30,6 +30,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--loop", action="store_true",
+                    help="time the closed decoding loop (draft, verify, advance, inject) "
+                         "against a seeded synthetic target instead of the single step")
     ap.add_argument("--kernel-reps", type=int, default=30)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
@@ -73,6 +76,8 @@ def main():
     from workloads import WORKLOADS, synth
 
     wl = WORKLOADS[args.workload]
+    if args.loop:
+        return loop_bench(args, wl)
     cfg = wl.cfg
     Bn = wl.batch
     ctx = synth.context_lengths(wl)
@@ -282,6 +287,122 @@ def main():
         "parity": parity,
         "wall_s_timed": round(t_wall, 3),
     }
+    print(json.dumps(out), flush=True)
+
+
+def loop_bench(args, wl):
+    """The closed speculative loop, one iteration per timed step: draft a block, build the
+    synthetic target's ids (planted k ~ U{0..15} matching drafts per request and
+    iteration), greedy verify, advance (context += accept length, anchor = bonus) and inject the
+    target features of the block's 16 slots.  The graph of one iteration is replayed, so the
+    contexts grow as in decoding.  The synthetic target's own kernels (a few torch ops) are
+    timed alone and reported; accepted tokens/s excludes them."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_hidden_amd import Drafter, binding as B
+    from workloads import synth
+
+    cfg, Bn = wl.cfg, wl.batch
+    ctx = synth.context_lengths(wl)
+    dev = torch.device("cuda:0")
+    iters = args.warmup + args.steps + 2
+    w = synth.drafter_weights(cfg, seed=wl.seed)
+    wd = {k: v.to(dev) for k, v in w.items()}
+    del w
+    table, num_pages = synth.page_table(wl.name + "/loop", ctx + 16 * (iters + 1),
+                                        cfg.page_size, wl.seed)
+    dr = Drafter(cfg, wd, max_batch=Bn, max_ctx=table.shape[1] * cfg.page_size,
+                 max_inject_rows=min(max(256, Bn * 16), 1024), device=dev)
+    del wd
+    torch.cuda.empty_cache()
+    cache = dr.new_cache(table, ctx, num_pages)
+    gen = torch.Generator(device=dev).manual_seed(synth.stream_seed(wl.seed, "bench/loop/fill"))
+    for pool in (cache.k_pool, cache.v_pool):   # context K/V: seeded, of the injected scale
+        pool.normal_(0.0, 3.0, generator=gen)
+    feats = torch.cat([synth.target_features(cfg, 16, f"bench/loop/b{b}", seed=wl.seed)
+                       for b in range(Bn)]).to(dev)
+    # Planting draws per iteration (k ~ U{0..15} per request and iteration), indexed on the
+    # device by an iteration counter that the captured iteration advances.
+    draws = [synth.plant_draws(f"bench/loop/it{i}", Bn, cfg.vocab, wl.seed) for i in range(iters)]
+    k_d, fill_d, r_d = (torch.from_numpy(np.stack([np.asarray(d[j]) for d in draws])).to(dev)
+                        for j in range(3))
+    counters = [torch.zeros(1, dtype=torch.long, device=dev) for _ in range(2)]
+    anchors = torch.as_tensor(synth.anchor_ids(cfg, Bn, wl.seed)).to(dev)
+    ids = torch.zeros((Bn, 15), dtype=torch.int32, device=dev)
+    acc = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    bonus = torch.zeros_like(acc)
+    inj_seq = torch.zeros(Bn * 16, dtype=torch.int32, device=dev)
+    inj_pos = torch.zeros_like(inj_seq)
+    tgt = torch.zeros((Bn, 16), dtype=torch.int32, device=dev)
+
+    def target_stub(c=counters[1]):
+        i = torch.remainder(c, iters)
+        tgt.copy_(synth.plant_device(ids, k_d.index_select(0, i)[0], fill_d.index_select(0, i)[0],
+                                     r_d.index_select(0, i)[0], cfg.vocab))
+        c.add_(1)
+
+    def iteration():
+        dr.draft(cache, anchors, ids)
+        target_stub(counters[0])
+        B.verify_accept(ids, tgt, acc, bonus)
+        dr.advance(cache, acc, bonus, anchors, inj_seq, inj_pos)
+        dr.inject(cache, feats, inj_seq, inj_pos)
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for fn in (iteration, target_stub):
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    T_start = cache.ctx_lens.clone()
+    times = []
+    for g, n in ((graphs[0], args.steps), (graphs[1], args.steps)):
+        with torch.cuda.stream(s):
+            for _ in range(args.warmup if g is graphs[0] else 2):
+                g.replay()
+        torch.cuda.synchronize()
+        if g is graphs[0]:
+            T_start = cache.ctx_lens.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            for _ in range(n):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    grown = (cache.ctx_lens - T_start).cpu().numpy()
+    acc_per_iter = float(grown.sum()) / args.steps          # accepted tokens per iteration
+    ms, stub_ms = times
+    timed = [(1 + args.warmup + j) % iters for j in range(args.steps)]
+    planted = float(sum((np.asarray(draws[i][0]) + 1).sum() for i in timed)) / args.steps
+    out = {
+        "metric": "accepted tokens/s (closed DFlash loop: draft + greedy verify + advance + "
+                  "inject, seeded synthetic target with planted acceptance)",
+        "value": round(acc_per_iter / ((ms - stub_ms) * 1e-3), 1),
+        "unit": "accepted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "synthetic_target_ms": round(stub_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded weights, features and planted target ids)",
+        "config": {"workload": wl.name + "+closed-loop", "batch": Bn,
+                   "context_start": int(ctx.max()),
+                   "context_end": int(cache.ctx_lens.max().item()),
+                   "accepted_per_iteration": round(acc_per_iter, 2),
+                   "accepted_per_iteration_planted": planted,
+                   "graph": True},
+        "drafted_tokens_per_s": round(Bn * 15 / (ms * 1e-3), 1),
+    }
+    assert abs(acc_per_iter - planted) < 1e-6, (acc_per_iter, planted)
     print(json.dumps(out), flush=True)
 
 

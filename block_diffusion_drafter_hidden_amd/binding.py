@@ -25,7 +25,7 @@ EXPORTS = (
     "dflash_packed_weights_size", "dflash_pack_weights", "dflash_workspace_size",
     "dflash_workspace_init", "dflash_fuse_inject_kv", "dflash_draft_block",
     "dflash_lm_head_argmax",
-    "dflash_verify_accept", "dflash_verify_sampled_workspace_size",
+    "dflash_verify_accept", "dflash_advance", "dflash_verify_sampled_workspace_size",
     "dflash_verify_accept_sampled", "dflash_error_string",
 )
 
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, SZ, P]),
         "dflash_lm_head_argmax": (S, [P, P, P, I32, P, P, P, SZ, P]),
         "dflash_verify_accept": (S, [P, P, I32, P, P, P, P]),
+        "dflash_advance": (S, [P, P, I32, I32, P, P, P, P, P]),
         "dflash_verify_sampled_workspace_size": (SZ, [I32, I32]),
         "dflash_verify_accept_sampled": (S, [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "dflash_error_string": (C.c_char_p, [S]),
@@ -186,6 +187,14 @@ def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream
         _ptr(emitted), _stream(stream)), "dflash_verify_accept")
 
 
+def advance(accept_len, bonus, max_ctx: int, ctx_lens, anchor_ids, inject_seq, inject_pos,
+            stream=None) -> None:
+    batch = int(accept_len.shape[0])
+    _check(load_library().dflash_advance(
+        _ptr(accept_len), _ptr(bonus), batch, int(max_ctx), _ptr(ctx_lens), _ptr(anchor_ids),
+        _ptr(inject_seq), _ptr(inject_pos), _stream(stream)), "dflash_advance")
+
+
 def verify_sampled_workspace_size(batch: int, vocab: int) -> int:
     return int(load_library().dflash_verify_sampled_workspace_size(batch, vocab))
 
@@ -258,3 +267,8 @@ class Drafter:
               stream=None) -> None:
         draft_block(self.ccfg, self.packed, self.embed, cache.c(), anchor_ids, draft_ids,
                     self.ws, logits_out, stream)
+
+    def advance(self, cache: PagedCache, accept_len, bonus, anchor_ids, inject_seq,
+                inject_pos, stream=None) -> None:
+        advance(accept_len, bonus, cache.max_pages * self.cfg.page_size, cache.ctx_lens,
+                anchor_ids, inject_seq, inject_pos, stream)

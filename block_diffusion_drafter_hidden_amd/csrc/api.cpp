@@ -701,6 +701,18 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
                         stream);
 }
 
+dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch,
+                             int32_t max_ctx, int32_t* ctx_lens, int32_t* anchor_ids,
+                             int32_t* inject_seq, int32_t* inject_pos, hipStream_t stream) {
+  if (!accept_len || !bonus || !ctx_lens || !anchor_ids || !inject_seq || !inject_pos ||
+      batch < 0 || max_ctx < 16)
+    return DFLASH_ERR_INVALID_ARG;
+  if (batch == 0) return DFLASH_OK;
+  DF_TRY(launch_advance(accept_len, bonus, batch, max_ctx, ctx_lens, anchor_ids, inject_seq,
+                        inject_pos, stream));
+  return DFLASH_OK;
+}
+
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
                                    int32_t batch, int32_t* accept_len, int32_t* bonus,
                                    int32_t* emitted, hipStream_t stream) {

@@ -42,6 +42,11 @@ hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hi
                                     hipStream_t stream);
 hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
                                 int* bonus, int* emitted, hipStream_t stream);
+// ctx_lens[b] += accept[b], anchors[b] = bonus[b]; inj_seq / inj_pos [batch * 16] get the
+// request index and the positions old ctx_lens[b] + j (clamped to max_ctx - 1).
+hipError_t launch_advance(const int* accept, const int* bonus, int batch, int max_ctx,
+                          int* ctx_lens, int* anchors, int* inj_seq, int* inj_pos,
+                          hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace dflash

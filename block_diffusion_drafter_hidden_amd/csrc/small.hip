@@ -187,6 +187,37 @@ hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, 
 }
 
 // ------------------------------------------------------------------------------------------
+// Closed-loop bookkeeping after a verify: the block's 16 positions become the injection
+// rows of the next fuse-inject call, then the context grows by the accepted length and the
+// bonus token becomes the next anchor.  One wave per request; every lane reads T_b before
+// lane 0 rewrites it (the store depends on the loaded value).
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void advance_kernel(const int* __restrict__ accept,
+                                                     const int* __restrict__ bonus, int max_ctx,
+                                                     int* ctx_lens, int* __restrict__ anchors,
+                                                     int* __restrict__ inj_seq,
+                                                     int* __restrict__ inj_pos) {
+  const int b = blockIdx.x, l = threadIdx.x;
+  const int T = ctx_lens[b];
+  if (l < kBlock) {
+    inj_seq[(long long)b * kBlock + l] = b;
+    inj_pos[(long long)b * kBlock + l] = min(max(T + l, 0), max_ctx - 1);
+  }
+  if (l == 0) {
+    ctx_lens[b] = T + accept[b];
+    anchors[b] = bonus[b];
+  }
+}
+
+hipError_t launch_advance(const int* accept, const int* bonus, int batch, int max_ctx,
+                          int* ctx_lens, int* anchors, int* inj_seq, int* inj_pos,
+                          hipStream_t stream) {
+  advance_kernel<<<batch, 64, 0, stream>>>(accept, bonus, max_ctx, ctx_lens, anchors, inj_seq,
+                                           inj_pos);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Zero fill (used for the workspace synchronization area; a kernel, not a memset node, so
 // it is safe inside captured graphs).
 // ------------------------------------------------------------------------------------------

@@ -18,6 +18,12 @@
  *   dflash_verify_accept    greedy verification: the longest prefix of drafts that matches
  *                           the target's argmax, plus one target token (blog, same section:
  *                           the target accepts the longest valid prefix).
+ *   dflash_advance          closed-loop bookkeeping between iterations: the accepted
+ *                           tokens extend the context and the loop drafts again from the
+ *                           target's next token (blog, same section: drafting and
+ *                           verification alternate, one verification pass yielding several
+ *                           tokens; wiki, "Background": the draft model proposes, the target
+ *                           verifies in parallel).
  *   dflash_verify_accept_sampled
  *                           temperature-1 verification (speculative accept/reject with
  *                           residual resampling, which keeps the target's output
@@ -199,6 +205,27 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
                                    int32_t batch, int32_t* accept_len, int32_t* bonus,
                                    int32_t* emitted, hipStream_t stream);
+
+/* Closed-loop bookkeeping after dflash_verify_accept, so that a whole decoding iteration
+ * (draft -> verify -> advance -> inject) runs on the stream without the host reading any
+ * result.  For each request b, with T_b the context length before the call:
+ *   inject_seq [batch * 16] int32 out: b for rows b*16 .. b*16+15;
+ *   inject_pos [batch * 16] int32 out: T_b + j for row b*16 + j -- the positions of the
+ *              block's 16 slots (slot 0 = the anchor at T_b), whose target hidden features
+ *              the next dflash_fuse_inject_kv call writes into the cache;
+ *   ctx_lens   [batch] int32 in/out: T_b -> T_b + accept_len[b] (the anchor and the
+ *              accepted drafts join the context);
+ *   anchor_ids [batch] int32 out: bonus[b], slot 0 of the next block.
+ * accept_len, bonus [batch] int32: the outputs of dflash_verify_accept.  max_ctx: positions
+ * the cache holds per request (max_pages_per_seq * 16).  Rows j >= accept_len[b] write
+ * positions past the new context length: no draft reads them, and the next iteration's
+ * injection (which starts at the new T_b) overwrites them first.  Precondition:
+ * T_b + 16 <= max_ctx; positions are clamped to max_ctx - 1 so that no access leaves the
+ * request's page-table row.  DFLASH_ERR_INVALID_ARG for null pointers, batch < 0 or
+ * max_ctx < 16; batch 0 launches nothing. */
+dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch,
+                             int32_t max_ctx, int32_t* ctx_lens, int32_t* anchor_ids,
+                             int32_t* inject_seq, int32_t* inject_pos, hipStream_t stream);
 
 /* Workspace bytes for dflash_verify_accept_sampled. */
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);

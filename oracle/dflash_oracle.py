@@ -50,6 +50,10 @@ Readings where the pages are silent (each is listed again in the design doc):
       so `precision="bf16"` rounds (to nearest, ties to even, 8 significant
       bits) exactly the injected K and V; "exact" rounds nowhere.  f32 models
       use "exact".
+  R20 the closed loop: after a verify with accept length a, the anchor and the
+      a - 1 accepted drafts join the context -- the target's hidden features of
+      block slots 0..a-1 are injected at positions T..T+a-1 -- and the bonus
+      token is the next anchor.
 """
 from __future__ import annotations
 
@@ -374,3 +378,45 @@ def draft_step(cfg, weights: Dict, k_ctx: List[np.ndarray], v_ctx: List[np.ndarr
     acc, bonus, emitted = verify_greedy(dr["ids"], target_ids)
     dr.update({"accept_len": acc, "bonus": bonus, "emitted": emitted})
     return dr
+
+
+# ------------------------------------------------------------------------------------------
+# The closed speculative loop (several iterations)
+# ------------------------------------------------------------------------------------------
+
+def decode_loop(cfg, weights: Dict, k_ctx: List[np.ndarray], v_ctx: List[np.ndarray],
+                anchor: int, block_feats: Sequence, target_ids_for, precision=None) -> Dict:
+    """Drafting and verification alternating [blog, How it works: the drafter proposes a
+    block, the target accepts the longest valid prefix, so one verification pass yields
+    several tokens; wiki, Background].  Iteration i, with T the context length:
+      1. draft a block from [anchor, mask x 15] at positions T..T+15;
+      2. the target's ids for that block, target_ids_for(i, draft_ids) [16], verified
+         greedily: accept_len a, bonus token;
+      3. the anchor and the a - 1 accepted drafts join the context: the target's hidden
+         features of block slots 0..a-1, block_feats[i][:a] ([16, F] per iteration), are
+         fused and injected at positions T..T+a-1 (R20);
+      4. T += a; the bonus token is the next anchor.
+    Returns per-iteration records and the final context K/V."""
+    p = precision_of(cfg, precision)
+    ks = [np.asarray(k, dtype=np.float64) for k in k_ctx]
+    vs = [np.asarray(v, dtype=np.float64) for v in v_ctx]
+    T = 0 if len(ks) == 0 else ks[0].shape[0]
+    records = []
+    for i, feats in enumerate(block_feats):
+        dr = draft_block(cfg, weights, ks, vs, anchor, precision=p)
+        t = np.asarray(target_ids_for(i, dr["ids"]))
+        acc, bonus, emitted = verify_greedy(dr["ids"], t)
+        nk, nv = prefill_context(cfg, weights, feats[:acc], positions=T + np.arange(acc),
+                                 precision=p)
+        if T == 0 and len(ks) == 0:
+            ks, vs = nk, nv
+        else:
+            ks = [np.concatenate([a, b], axis=0) for a, b in zip(ks, nk)]
+            vs = [np.concatenate([a, b], axis=0) for a, b in zip(vs, nv)]
+        records.append({"ids": dr["ids"], "gap": dr["gap"], "top1": dr["top1"],
+                        "top2": dr["top2"], "target_ids": t, "accept_len": acc,
+                        "bonus": bonus, "emitted": emitted, "ctx_len": T, "anchor": anchor})
+        T += acc
+        anchor = bonus
+    return {"iterations": records, "k_ctx": ks, "v_ctx": vs, "ctx_len": T, "anchor": anchor}
+

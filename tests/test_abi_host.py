@@ -74,6 +74,12 @@ def test_null_arguments_rejected_before_launch():
     assert lib.dflash_verify_accept_sampled(None, None, None, None, None, 1, 8, None, None,
                                             None, None, 0, None) == -1
     assert lib.dflash_verify_sampled_workspace_size(0, 8) == 0
+    fake = C.c_void_p(16)  # never dereferenced: validation fails first
+    assert lib.dflash_advance(None, fake, 2, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 64, fake, fake, None, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, -1, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 8, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 0, 64, fake, fake, fake, fake, None) == 0
 
 
 def test_small_workspace_rejected_before_launch():

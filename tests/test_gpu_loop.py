@@ -1,0 +1,100 @@
+"""GPU parity of the closed speculative loop: draft -> greedy verify -> dflash_advance ->
+inject the block's target features, iterated on the device with no host reads in between,
+against the oracle's loop (oracle.decode_loop) on the same seeded inputs.
+
+A seeded synthetic target stands in for the target model: per iteration it supplies the
+hidden features of the block's 16 slots and target ids planted against the drafts (k ~
+U{0..15} matching drafts, so every accept length is known).  Per iteration and request:
+draft ids bit-exact except near-ties, accept length, bonus (next anchor) and context length
+exact; a request whose drafts differed at an excused near-tie is compared on lengths only
+from then on.  At the end the cache over the whole grown context matches injecting every
+accepted slot's features at once."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.dflash_oracle as ref
+from block_diffusion_drafter_hidden_amd import binding as B_
+from tests import gpu_setup as G
+from tests.test_gpu_parity import SMALL_BF16
+from workloads import TINY, synth
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+ITERS = 5
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16])
+def test_closed_loop_matches_oracle_loop(cfg):
+    ctx0 = [37, 0, 100]
+    Bn, V = len(ctx0), cfg.vocab
+    s = G.build(cfg, ctx0, tag="loop", extra=16 * (ITERS + 1))
+    anchors0 = synth.anchor_ids(cfg, Bn, tag="loop")
+    feats = [[synth.target_features(cfg, 16, f"loop/it{i}/b{b}") for b in range(Bn)]
+             for i in range(ITERS)]
+    draws = [synth.plant_draws(f"loop/it{i}", Bn, V) for i in range(ITERS)]
+    print(f"[loop {cfg.name}] contexts {ctx0}, planted k per iteration "
+          f"{[list(d[0]) for d in draws]}", flush=True)
+
+    # ---- device loop: no host reads between the calls of an iteration ----
+    anchors = torch.from_numpy(np.asarray(anchors0, dtype=np.int32)).cuda()
+    ids = torch.empty((Bn, 15), dtype=torch.int32, device="cuda")
+    acc = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    bonus = torch.empty_like(acc)
+    inj_seq = torch.empty(Bn * 16, dtype=torch.int32, device="cuda")
+    inj_pos = torch.empty_like(inj_seq)
+    dev_draws = [tuple(torch.from_numpy(np.asarray(x)).cuda() for x in d) for d in draws]
+    dev_feats = [torch.cat(f).cuda() for f in feats]
+    got = []
+    for i in range(ITERS):
+        s.dr.draft(s.cache, anchors, ids)
+        k, fill, r = dev_draws[i]
+        t = synth.plant_device(ids, k, fill, r, V)
+        B_.verify_accept(ids, t, acc, bonus)
+        s.dr.advance(s.cache, acc, bonus, anchors, inj_seq, inj_pos)
+        s.dr.inject(s.cache, dev_feats[i], inj_seq, inj_pos)
+        got.append([x.clone() for x in (ids, acc, bonus, s.cache.ctx_lens, anchors, inj_pos)])
+    torch.cuda.synchronize()
+    got = [[x.cpu().numpy() for x in g] for g in got]
+
+    # ---- oracle loop, request by request ----
+    for b in range(Bn):
+        ks, vs = G.oracle_context(s, b)
+
+        def targets(i, d, b=b):
+            k, fill, r = draws[i]
+            return synth.plant(d[None], k[b:b + 1], fill[b:b + 1], r[b:b + 1], V)[0]
+
+        out = ref.decode_loop(cfg, s.w, ks, vs, int(anchors0[b]), [f[b] for f in feats],
+                              targets)
+        diverged = False
+        for i, rec in enumerate(out["iterations"]):
+            g_ids, g_acc, g_bon, g_T, g_anc = (x[b] for x in got[i][:5])
+            T_before = rec["ctx_len"]
+            assert list(got[i][5][b * 16:(b + 1) * 16]) == list(T_before + np.arange(16)), (b, i)
+            assert g_acc == rec["accept_len"] == int(draws[i][0][b]) + 1, (b, i)
+            assert g_T == T_before + rec["accept_len"], (b, i)
+            if diverged:
+                continue
+            bad, excused = G.compare_ids(g_ids, rec, cfg.dtype)
+            assert bad == 0, (b, i, g_ids, rec["ids"])
+            if (g_ids != rec["ids"]).any():   # an excused near-tie took another id
+                diverged = True
+                print(f"[loop {cfg.name}] request {b} iteration {i}: near-tie id differs; "
+                      f"lengths only from here", flush=True)
+                continue
+            assert g_bon == rec["bonus"] and g_anc == rec["bonus"], (b, i)
+        # the cache over the grown context equals one-shot injection of the accepted slots
+        T_end = out["ctx_len"]
+        rows = ([s.feats[b]] if ctx0[b] else []) + [
+            f[b][:rec["accept_len"]] for f, rec in zip(feats, out["iterations"])]
+        ke, ve = ref.prefill_context(cfg, s.w, torch.cat(rows), precision="exact")
+        gk, gv = G.gather_pool(s, b, T_end, "k"), G.gather_pool(s, b, T_end, "v")
+        for l in range(cfg.n_layers):
+            for name, g_, e in (("k", gk[l], ke[l]), ("v", gv[l], ve[l])):
+                ok, info = G.cache_matches(g_, e, cfg.dtype)
+                assert ok, (b, l, name, info)
+        print(f"[loop {cfg.name}] request {b}: context {ctx0[b]} -> {T_end} over {ITERS} "
+              f"iterations, accept lengths {[r['accept_len'] for r in out['iterations']]}",
+              flush=True)

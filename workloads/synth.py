@@ -147,26 +147,54 @@ def page_table(name: str, ctx_caps: np.ndarray, page: int, seed: int = 0,
 # Verify inputs
 # ----------------------------------------------------------------------------------------
 
-def planted_targets(draft_ids: np.ndarray, vocab: int, name: str, seed: int = 0,
-                    k: np.ndarray = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Target ids [B, 16] with a planted matching prefix against `draft_ids` [B, 15].
-
-    k[b] ~ U{0..15} drafts match (t[i-1] = d[i] for i <= k); if k < 15 slot k is forced
-    to differ from d[k+1]; the rest are uniform.  This pins the greedy accept length
-    to k + 1.  Returns (target_ids, k)."""
-    d = np.asarray(draft_ids, dtype=np.int64)
-    B, nd = d.shape
+def plant_draws(name: str, batch: int, vocab: int, seed: int = 0, k: np.ndarray = None,
+                n_drafts: int = 15):
+    """Seeded draws of the planting rule that do not depend on the drafts: k [B] ~
+    U{0..n_drafts} matching drafts (unless given), the free target ids fill [B, n_drafts+1]
+    ~ U{0..V-1} and the mismatch offsets r [B] ~ U{0..V-2}."""
     rng = np.random.Generator(np.random.PCG64(stream_seed(seed, name + "/plant")))
     if k is None:
-        k = rng.integers(0, nd + 1, size=B)
-    k = np.asarray(k, dtype=np.int64)
-    t = rng.integers(0, vocab, size=(B, nd + 1))
-    r = rng.integers(0, vocab - 1, size=B)
+        k = rng.integers(0, n_drafts + 1, size=batch)
+    fill = rng.integers(0, vocab, size=(batch, n_drafts + 1))
+    r = rng.integers(0, vocab - 1, size=batch)
+    return np.asarray(k, dtype=np.int64), fill, r
+
+
+def plant(draft_ids: np.ndarray, k, fill, r, vocab: int) -> np.ndarray:
+    """Target ids [B, 16] from drafts [B, 15]: t[i-1] = d[i] for i <= k; if k < 15, slot k
+    is d[k+1] shifted by 1 + r (mod V), so it differs; the rest are `fill`.  This pins the
+    greedy accept length to k + 1."""
+    d = np.asarray(draft_ids, dtype=np.int64)
+    B, nd = d.shape
+    t = np.array(fill, dtype=np.int64, copy=True)
     for b in range(B):
         t[b, :k[b]] = d[b, :k[b]]
         if k[b] < nd:
             t[b, k[b]] = (d[b, k[b]] + 1 + r[b]) % vocab
-    return t.astype(np.int32), k.astype(np.int32)
+    return t.astype(np.int32)
+
+
+def plant_device(draft_ids, k, fill, r, vocab: int):
+    """`plant` on device tensors (drafts [B, 15] int32; k [B], fill [B, 16], r [B] int64), so
+    a captured decoding loop can build its synthetic target ids without the host."""
+    B, nd = draft_ids.shape
+    dev = draft_ids.device
+    j = torch.arange(nd + 1, device=dev)[None, :]
+    dpad = torch.cat([draft_ids.long(), torch.zeros((B, 1), dtype=torch.long, device=dev)], 1)
+    kk = k.long()[:, None]
+    t = torch.where(j < kk, dpad, fill.long())
+    miss = (torch.gather(dpad, 1, kk.clamp(max=nd - 1)) + 1 + r.long()[:, None]) % vocab
+    t = torch.where((j == kk) & (kk < nd), miss, t)
+    return t.to(torch.int32)
+
+
+def planted_targets(draft_ids: np.ndarray, vocab: int, name: str, seed: int = 0,
+                    k: np.ndarray = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Target ids [B, 16] with a planted matching prefix against `draft_ids` [B, 15]
+    (k[b] ~ U{0..15} unless given; see `plant`).  Returns (target_ids, k)."""
+    d = np.asarray(draft_ids, dtype=np.int64)
+    k, fill, r = plant_draws(name, d.shape[0], vocab, seed, k, d.shape[1])
+    return plant(d, k, fill, r, vocab), k.astype(np.int32)
 
 
 def sampled_verify_inputs(wl: Workload, batch: int = None, vocab: int = None):
