@@ -877,6 +877,162 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// LM head over many rows: the 128-row kernel's W staging with 256-row blocks.  The LM head
+// multiplies one bf16 piece of its input, so in the 128-row kernel every 8 KB of W a wave
+// read from LDS fed only 16 MFMAs; here each of the 4 waves owns 64 rows (4 m-tiles) x the
+// block's 128 columns, so the same W reads feed 32 MFMAs and each W block read from HBM or
+// L2 serves 256 rows.  The argmax epilogue runs in registers: a lane scales its values by
+// the row's 1/rms, keeps the best (value, index) key of its column over the 8 n-tiles, and
+// the 16 lanes of a row group reduce with shuffles; no LDS tile is needed.
+// ------------------------------------------------------------------------------------------
+constexpr int kLmRows = 256, kLmMT = kLmRows / 16;
+
+__global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
+  __shared__ i32x4 w_s[2][kTallNT][kWave];   // [buf][n-tile][lane]: packed bf16 B fragments
+  __shared__ float rstd_s[kLmRows];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kLmRows - 1) / kLmRows;
+  int cb, rb;   // same XCD-aware order as the 128-row kernel
+  if (nrb <= kTallColRows) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    cb = (slot / nrb) * kXcds + xcd;
+    rb = slot % nrb;
+    if (cb >= ncb) return;
+  } else {
+    cb = blockIdx.x % ncb;
+    rb = blockIdx.x / ncb;
+  }
+  const int KT = p.KT;
+  const int ntv = min(kTallNT, p.n_tiles - cb * kTallNT);
+  const int n_mtiles_valid = (p.M + 15) / 16;
+  const char* W = p.W + (long long)(p.nt0 + cb * kTallNT) * p.nt_stride * kTileBytes;
+
+  // RMSNorm: thread t serves row rb * 256 + t; its first 8 partials are fetched now.
+  const int my_row = rb * kLmRows + tid;
+  float sq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    sq[i] = i < p.ssq_parts && my_row < p.M ? p.ssq_in[(long long)i * p.ssq_ld + my_row] : 0.f;
+
+  // This wave's 4 m-tiles (rows past M re-read the last valid m-tile; never stored).
+  const bf16* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mtc = min(rb * kLmMT + wave * 4 + i, n_mtiles_valid - 1);
+    ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * KT * 1024 + lane * 8;
+  }
+  constexpr int kR = 2;
+  i32x4 da[kR][4], dw[kR][2];
+  auto load_a = [&](int kt, i32x4 (&a)[4]) {
+    const long long off = (long long)min(kt, KT - 1) * 1024;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const i32x4*>(ap[i] + off);
+  };
+  auto load_w = [&](int kt, i32x4 (&w)[2]) {
+    const int ktc = min(kt, KT - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256, nt = min(c / 64, ntv - 1), l = c % 64;
+      w[i] = load16(W + ((long long)nt * p.nt_stride + (long long)ktc * p.kt_stride) *
+                            kTileBytes + l * 16);
+    }
+  };
+  auto store_w = [&](int buf, const i32x4 (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      w_s[buf][c / 64][c % 64] = w[i];
+    }
+  };
+  f32x4 acc[4][kTallNT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kTallNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const i32x4 (&a)[4]) {
+#pragma unroll
+    for (int j = 0; j < kTallNT; ++j) {
+      const i32x4 wf = w_s[buf][j][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_tile<bf16>(a[i], wf, acc[i][j]);
+    }
+  };
+
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    load_w(r, dw[r]);
+    load_a(r, da[r]);
+  }
+  store_w(0, dw[0]);
+  __syncthreads();
+  // Iteration kt: W of k-tile kt is in LDS buffer kt & 1; its register stage is refilled
+  // with k-tile kt + kR; W of k-tile kt + 1 moves to the other buffer.
+  const int KTr = KT - KT % kR;
+  for (int kt0 = 0; kt0 < KTr; kt0 += kR) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int kt = kt0 + r;
+      load_w(kt + kR, dw[r]);
+      compute(kt & 1, da[r]);
+      load_a(kt + kR, da[r]);
+      store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kR - 1; ++r) {
+    const int kt = KTr + r;
+    if (kt < KT) {
+      compute(kt & 1, da[r]);
+      store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+      __syncthreads();
+    }
+  }
+
+  {  // 1 / rms of every row of the block
+    float ssum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ssum += sq[i];
+    for (int part = 8; part < p.ssq_parts; ++part)
+      if (my_row < p.M) ssum += p.ssq_in[(long long)part * p.ssq_ld + my_row];
+    rstd_s[tid] = 1.0f / sqrtf(ssum / (float)(KT * 32) + p.eps);
+  }
+  __syncthreads();
+
+  // Epilogue in registers.  acc[i][j][e]: row 64 wave + 16 i + 4 (lane / 16) + e, column
+  // 16 j + lane % 16 of the block.
+  const int cols = ntv * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
+      const int m = rb * kLmRows + rl;
+      const float rs = rstd_s[rl];
+      unsigned long long best = 0;
+#pragma unroll
+      for (int j = 0; j < kTallNT; ++j) {
+        const int c = j * 16 + (lane & 15);
+        const float v = acc[i][j][e] * rs;
+        if (c < cols) {
+          const unsigned long long k = argmax_key(v, cb * kTallN + c);
+          best = k > best ? k : best;
+          if (p.logits_out && m < p.M && !(p.draft_rows && m % kBlock == 0)) {
+            const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
+            p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const unsigned long long other = __shfl_xor(best, o, kWave);
+        best = other > best ? other : best;
+      }
+      if ((lane & 15) == 0 && m < p.M) p.keys[(long long)cb * p.keys_ld + m] = best;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Launch
 // ------------------------------------------------------------------------------------------
 template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
@@ -1121,7 +1277,13 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
     if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
     if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
     if (epi == EPI_SWIGLU && norm) return go_tall<A_HILO, EPI_SWIGLU, true>(p, layers, stream);
-    if (epi == EPI_ARGMAX && norm) return go_tall<A_HILO, EPI_ARGMAX, true>(p, layers, stream);
+    if (epi == EPI_ARGMAX && norm) {   // 256-row blocks (gemm_tall_lm)
+      if (layers != 1) return hipErrorInvalidValue;
+      const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kLmRows - 1) / kLmRows;
+      const int ncb_grid = nrb <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
+      gemm_tall_lm<<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      return hipGetLastError();
+    }
     return hipErrorInvalidValue;
   }
   if (dtype_bf16) {
