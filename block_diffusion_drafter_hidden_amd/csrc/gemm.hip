@@ -877,21 +877,31 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// LM head over many rows: the 128-row kernel's W staging with 256-row blocks.  The LM head
-// multiplies one bf16 piece of its input, so in the 128-row kernel every 8 KB of W a wave
-// read from LDS fed only 16 MFMAs; here each of the 4 waves owns 64 rows (4 m-tiles) x the
-// block's 128 columns, so the same W reads feed 32 MFMAs and each W block read from HBM or
-// L2 serves 256 rows.  The argmax epilogue runs in registers: a lane scales its values by
-// the row's 1/rms, keeps the best (value, index) key of its column over the 8 n-tiles, and
-// the 16 lanes of a row group reduce with shuffles; no LDS tile is needed.
+// 256-row blocks for the LM head and gate|up over many rows: the 128-row kernel's W staging,
+// but each of the 4 waves owns 64 rows (4 m-tiles) x the block's 128 columns, so the 8 KB of
+// W a wave reads from LDS per k-tile feed 32 MFMAs per A piece instead of 16, and each W
+// block read from HBM or L2 serves 256 rows.
+//   EPI_ARGMAX (one bf16 piece of the input): the epilogue runs in registers -- a lane
+//   scales its values by the row's 1/rms, keeps the best (value, index) key of its column
+//   over the 8 n-tiles, and the 16 lanes of a row group reduce with shuffles.
+//   EPI_SWIGLU (hi + lo pieces): the finished block goes through a 128-row LDS tile in two
+//   halves to the same epilogue as the 128-row kernel.
 // ------------------------------------------------------------------------------------------
-constexpr int kLmRows = 256, kLmMT = kLmRows / 16;
+constexpr int kWideRows = 256, kWideMT = kWideRows / 16;
 
-__global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
-  __shared__ i32x4 w_s[2][kTallNT][kWave];   // [buf][n-tile][lane]: packed bf16 B fragments
-  __shared__ float rstd_s[kLmRows];
+union WideSmem {
+  i32x4 w[2][kTallNT][kWave];          // [buf][n-tile][lane]: packed bf16 B fragments
+  float tile[kTallM * (kTallN + 1)];   // epilogue tile: 128 rows of the block
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
+  static_assert(EPI == EPI_ARGMAX || EPI == EPI_SWIGLU, "LM head and gate|up");
+  constexpr int kQ = EPI == EPI_ARGMAX ? 1 : 2;   // bf16 pieces of the input
+  __shared__ WideSmem sm;
+  __shared__ float rstd_s[kWideRows];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kLmRows - 1) / kLmRows;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kWideRows - 1) / kWideRows;
   int cb, rb;   // same XCD-aware order as the 128-row kernel
   if (nrb <= kTallColRows) {
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
@@ -908,7 +918,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
   const char* W = p.W + (long long)(p.nt0 + cb * kTallNT) * p.nt_stride * kTileBytes;
 
   // RMSNorm: thread t serves row rb * 256 + t; its first 8 partials are fetched now.
-  const int my_row = rb * kLmRows + tid;
+  const int my_row = rb * kWideRows + tid;
   float sq[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -918,15 +928,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
   const bf16* ap[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int mtc = min(rb * kLmMT + wave * 4 + i, n_mtiles_valid - 1);
+    const int mtc = min(rb * kWideMT + wave * 4 + i, n_mtiles_valid - 1);
     ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * KT * 1024 + lane * 8;
   }
   constexpr int kR = 2;
-  i32x4 da[kR][4], dw[kR][2];
-  auto load_a = [&](int kt, i32x4 (&a)[4]) {
+  i32x4 da[kR][4][kQ], dw[kR][2];
+  auto load_a = [&](int kt, i32x4 (&a)[4][kQ]) {
     const long long off = (long long)min(kt, KT - 1) * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const i32x4*>(ap[i] + off);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < kQ; ++q)
+        a[i][q] = *reinterpret_cast<const i32x4*>(ap[i] + off + q * kHiLoStride);
   };
   auto load_w = [&](int kt, i32x4 (&w)[2]) {
     const int ktc = min(kt, KT - 1);
@@ -941,7 +954,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + i * 256;
-      w_s[buf][c / 64][c % 64] = w[i];
+      sm.w[buf][c / 64][c % 64] = w[i];
     }
   };
   f32x4 acc[4][kTallNT];
@@ -949,12 +962,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kTallNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, const i32x4 (&a)[4]) {
+  auto compute = [&](int buf, const i32x4 (&a)[4][kQ]) {
 #pragma unroll
     for (int j = 0; j < kTallNT; ++j) {
-      const i32x4 wf = w_s[buf][j][lane];
+      const i32x4 wf = sm.w[buf][j][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_tile<bf16>(a[i], wf, acc[i][j]);
+      for (int q = 0; q < kQ; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma_tile<bf16>(a[i][q], wf, acc[i][j]);
     }
   };
 
@@ -999,37 +1014,61 @@ __global__ __launch_bounds__(256, 2) void gemm_tall_lm(GemmParams p) {
   }
   __syncthreads();
 
-  // Epilogue in registers.  acc[i][j][e]: row 64 wave + 16 i + 4 (lane / 16) + e, column
-  // 16 j + lane % 16 of the block.
+  // acc[i][j][e]: row 64 wave + 16 i + 4 (lane / 16) + e, column 16 j + lane % 16.
   const int cols = ntv * 16;
+  if constexpr (EPI == EPI_ARGMAX) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
-      const int m = rb * kLmRows + rl;
-      const float rs = rstd_s[rl];
-      unsigned long long best = 0;
+      for (int e = 0; e < 4; ++e) {
+        const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const int m = rb * kWideRows + rl;
+        const float rs = rstd_s[rl];
+        unsigned long long best = 0;
 #pragma unroll
-      for (int j = 0; j < kTallNT; ++j) {
-        const int c = j * 16 + (lane & 15);
-        const float v = acc[i][j][e] * rs;
-        if (c < cols) {
-          const unsigned long long k = argmax_key(v, cb * kTallN + c);
-          best = k > best ? k : best;
-          if (p.logits_out && m < p.M && !(p.draft_rows && m % kBlock == 0)) {
-            const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
-            p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
+        for (int j = 0; j < kTallNT; ++j) {
+          const int c = j * 16 + (lane & 15);
+          const float v = acc[i][j][e] * rs;
+          if (c < cols) {
+            const unsigned long long k = argmax_key(v, cb * kTallN + c);
+            best = k > best ? k : best;
+            if (p.logits_out && m < p.M && !(p.draft_rows && m % kBlock == 0)) {
+              const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
+              p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
+            }
           }
         }
-      }
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const unsigned long long other = __shfl_xor(best, o, kWave);
-        best = other > best ? other : best;
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = __shfl_xor(best, o, kWave);
+          best = other > best ? other : best;
+        }
+        if ((lane & 15) == 0 && m < p.M) p.keys[(long long)cb * p.keys_ld + m] = best;
       }
-      if ((lane & 15) == 0 && m < p.M) p.keys[(long long)cb * p.keys_ld + m] = best;
+  } else {
+    // Two halves of 128 rows through the LDS tile (which reuses the W buffers).
+    const int ld = cols + 1;
+    const float xpre[1] = {0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wave / 2 == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < kTallNT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = (wave % 2) * 64 + i * 16 + (lane >> 4) * 4 + e;   // row in the half
+              const int col = j * 16 + (lane & 15);
+              if (col < cols) sm.tile[r * ld + col] = acc[i][j][e] * rstd_s[half * kTallM + r];
+            }
+      }
+      __syncthreads();
+      run_epilogue<bf16, kTallMT, EPI, 0, kTallNT>(p, sm.tile, cols, cb * kTallNT, 2 * rb + half,
+                                                  0, cb, xpre);
+      __syncthreads();
     }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1276,12 +1315,13 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
     if (p.a_kind != A_HILO) return hipErrorInvalidValue;
     if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
     if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
-    if (epi == EPI_SWIGLU && norm) return go_tall<A_HILO, EPI_SWIGLU, true>(p, layers, stream);
-    if (epi == EPI_ARGMAX && norm) {   // 256-row blocks (gemm_tall_lm)
+    if ((epi == EPI_SWIGLU || epi == EPI_ARGMAX) && norm) {   // 256-row blocks
       if (layers != 1) return hipErrorInvalidValue;
-      const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kLmRows - 1) / kLmRows;
+      const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
+      const int nrb = (p.M + kWideRows - 1) / kWideRows;
       const int ncb_grid = nrb <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
-      gemm_tall_lm<<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      if (epi == EPI_SWIGLU) gemm_tall256<EPI_SWIGLU><<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      else gemm_tall256<EPI_ARGMAX><<<ncb_grid * nrb, 256, 0, stream>>>(p);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
