@@ -1315,10 +1315,16 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
     if (p.a_kind != A_HILO) return hipErrorInvalidValue;
     if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
     if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
+    // 256-row blocks for the LM head, and for gate|up once they still give two rounds of
+    // workgroups (at 512 rows, 384 workgroups of 256 rows left part of the chip idle: gate|up
+    // 185 -> 225 us; at 1024 rows they are faster).
+    const int ncb_t = (p.n_tiles + kTallNT - 1) / kTallNT;
+    const int nrb_w = (p.M + kWideRows - 1) / kWideRows;
+    const bool wide = epi == EPI_ARGMAX || (epi == EPI_SWIGLU && ncb_t * nrb_w >= 512);
+    if (epi == EPI_SWIGLU && norm && !wide) return go_tall<A_HILO, EPI_SWIGLU, true>(p, layers, stream);
     if ((epi == EPI_SWIGLU || epi == EPI_ARGMAX) && norm) {   // 256-row blocks
       if (layers != 1) return hipErrorInvalidValue;
-      const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
-      const int nrb = (p.M + kWideRows - 1) / kWideRows;
+      const int ncb = ncb_t, nrb = nrb_w;
       const int ncb_grid = nrb <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
       if (epi == EPI_SWIGLU) gemm_tall256<EPI_SWIGLU><<<ncb_grid * nrb, 256, 0, stream>>>(p);
       else gemm_tall256<EPI_ARGMAX><<<ncb_grid * nrb, 256, 0, stream>>>(p);
