@@ -169,11 +169,11 @@ Plan plan_gemm(int n_tiles, int KT, int M, int npw, int layers, int max_ksub = 1
 
 // Partial sums of squares per row that a residual GEMM with this plan leaves for the next
 // norm: one per n-tile (streaming kernel), one per 128-column block (128-row kernel), one
-// whole-row sum (128-row kernel with a k-split: its reduction kernel takes a row per
-// workgroup).
+// per 512-column segment (128-row kernel with a k-split: the segments of its reduction
+// kernel).
 int residual_ssq_parts(const Plan& pl, int n_tiles) {
   if (pl.mt != kTallMT) return n_tiles;
-  return pl.ksub > 1 ? 1 : cdiv(n_tiles, kTallNT);
+  return pl.ksub > 1 ? cdiv(n_tiles, 32) : cdiv(n_tiles, kTallNT);
 }
 
 // RoPE frequencies theta^(-2i/d) in fp64 for the epilogues that rotate q and k.

@@ -72,7 +72,7 @@ struct GemmParams {
   // EPI_RESIDUAL, when xg_out is set: also write xg = x * gamma_next (as h) and the rows'
   // partial sums of squares ssq_out[part * ssq_ld + row] -- the inputs of the next
   // RMSNorm-folded GEMM.  Parts: one per n-tile (streaming kernel), one per 128-column block
-  // (128-row kernel), or one whole-row sum (128-row kernel with a k-split).
+  // (128-row kernel), or one per 512-column segment (128-row kernel with a k-split).
   void* xg_out;
   const float* gamma_next;
   float* ssq_out;

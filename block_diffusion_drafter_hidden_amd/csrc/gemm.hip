@@ -1140,10 +1140,11 @@ static hipError_t launch_mt(int npw, int epi, const GemmParams& p, int layers,
 
 // Reduction of a k-split 128-row GEMM: a thread adds the slices' partials of four columns in
 // slice order.  EPI_STORE: the sum is the output (fp32 fragment layout); one thread per
-// (row, column quad).  EPI_RESIDUAL: one workgroup per row; the sum is added to x, and x and
-// x * gamma_next (pair layout) are written, and the workgroup reduces the row's squares to
-// one whole-row sum for the next norm (lanes, then waves, in a fixed order), so the next
-// RMSNorm-folded GEMM reads one partial per row instead of one per n-tile.
+// (row, column quad).  EPI_RESIDUAL: the sum is added to x, and x and x * gamma_next (pair
+// layout) are written, and the rows' squares are reduced (lanes, then waves, in a fixed
+// order) to one partial per 512-column segment for the next norm, so the next
+// RMSNorm-folded GEMM reads a few partials per row instead of one per n-tile.
+constexpr int kRedSegCols = 512;   // columns per workgroup of the residual reduction
 template <int EPI>
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int splits) {
   const int quads = p.n_tiles * 4;
@@ -1159,53 +1160,59 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
     return xn;
   };
   if constexpr (EPI == EPI_RESIDUAL) {
-    // Four quads per thread per pass; every load of a pass (slices, x, gains) is issued
-    // before its first store, which the compiler may not move loads across.
-    constexpr int kQ = 4;
-    __shared__ float red[256 / kWave];
-    const int m = blockIdx.x, tid = threadIdx.x;
-    float ss = 0.f;
-    for (int base = 0; base < quads; base += kQ * 256) {
-      f32x4 v[kQ], xo[kQ], g[kQ];
+    // Workgroup (m-tile, 512-column segment): in the fragment layout the segment of an
+    // m-tile is 32 KB contiguous, so thread t takes its 16-byte pieces t + 256 i, all of row
+    // t % 16; every load is issued before the first store.  The row's squares over the
+    // segment are reduced over the 16 threads of that row (lanes, then waves) to one
+    // partial: parts = 512-column segments.
+    constexpr int kP = kRedSegCols / 32 * 128 / 256;   // pieces per thread (8)
+    __shared__ float red[256 / kWave][16];
+    const int mt = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x;
+    const int kt0 = seg * (kRedSegCols / 32), nkt = min(kRedSegCols / 32, kto - kt0);
+    const int r = mt * 16 + tid % 16;
+    const bool row_ok = r < p.M;
+    f32x4 v[kP], xo[kP], g[kP];
+    long long xoff[kP];
+    int col[kP];
+    bool ok[kP];
 #pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        const int cq = base + tid + j * 256;
-        v[j] = xo[j] = g[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (cq < quads) {
-          xo[j] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.out) +
-                                                 swz_off(m, cq * 4, kto, 8));
-          if (p.xg_out) g[j] = *reinterpret_cast<const f32x4*>(p.gamma_next + cq * 4);
-        }
+    for (int i = 0; i < kP; ++i) {
+      const int pc = tid + 256 * i, ktl = pc / 128, jb = (pc / 64) % 2, ln = pc % 64;
+      ok[i] = row_ok && ktl < nkt;
+      col[i] = (kt0 + ktl) * 32 + 8 * (ln / 16) + 4 * jb;
+      xoff[i] = (((long long)mt * kto + kt0 + ktl) * 2 + jb) * 256 + ln * 4;
+      v[i] = xo[i] = g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok[i]) {
+        xo[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.out) + xoff[i]);
+        if (p.xg_out) g[i] = *reinterpret_cast<const f32x4*>(p.gamma_next + col[i]);
       }
-      for (int sl = 0; sl < splits; ++sl)
+    }
+    for (int sl = 0; sl < splits; ++sl)
 #pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-          const int cq = base + tid + j * 256;
-          if (cq < quads)
-            v[j] += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo +
-                                                   cq * 4);
-        }
+      for (int i = 0; i < kP; ++i)
+        if (ok[i])
+          v[i] += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + r) * p.ldo +
+                                                 col[i]);
+    float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        const int cq = base + tid + j * 256;
-        if (cq >= quads) continue;
-        const f32x4 xn = xo[j] + v[j];
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, cq * 4, kto, 8)) = xn;
-        if (p.xg_out) {
-          store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, cq * 4, kto), xn * g[j]);
-          ss += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
-        }
+    for (int i = 0; i < kP; ++i) {
+      if (!ok[i]) continue;
+      const f32x4 xn = xo[i] + v[i];
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + xoff[i]) = xn;
+      if (p.xg_out) {
+        store_hilo4(reinterpret_cast<bf16*>(p.xg_out), hilo_off(r, col[i], kto), xn * g[i]);
+        ss += xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
       }
     }
     if (p.xg_out) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-      if (tid % kWave == 0) red[tid / kWave] = ss;
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      if (tid % kWave < 16) red[tid / kWave][tid % 16] = ss;
       __syncthreads();
-      if (tid == 0) {
+      if (tid < 16 && r < p.M) {
         float t = 0.f;
-        for (int w = 0; w < 256 / kWave; ++w) t += red[w];
-        p.ssq_out[m] = t;   // part 0: the whole row
+        for (int w = 0; w < 256 / kWave; ++w) t += red[w][tid];
+        p.ssq_out[(long long)seg * p.ssq_ld + r] = t;
       }
     }
   } else {
@@ -1290,8 +1297,9 @@ static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   dim3 grid(ncb_grid * p.n_mblocks, splits, layers);
   gemm_tall<AK, EPI, NORM><<<grid, 256, 0, stream>>>(p);
   if (splits > 1) {
-    if constexpr (EPI == EPI_RESIDUAL) {   // a workgroup per row
-      ksplit_reduce_kernel<EPI><<<(unsigned)p.M, 256, 0, stream>>>(p, splits);
+    if constexpr (EPI == EPI_RESIDUAL) {   // a workgroup per (m-tile, 512-column segment)
+      const dim3 rg((unsigned)((p.M + 15) / 16), (unsigned)((p.ldo + kRedSegCols - 1) / kRedSegCols));
+      ksplit_reduce_kernel<EPI><<<rg, 256, 0, stream>>>(p, splits);
     } else if constexpr (kRowSplit<EPI>) {
       const long long threads = (long long)p.M * p.n_tiles * 4;
       ksplit_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
