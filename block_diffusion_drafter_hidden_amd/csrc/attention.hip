@@ -44,25 +44,14 @@ __device__ inline long long part_o_index(long long slot, int G, int hh, int D, i
          dim % 4;
 }
 
-__device__ inline void split2(float v, bf16& hi, bf16& lo) {
-  hi = (bf16)v;
-  lo = (bf16)(v - (float)hi);
-}
-
-// 8 floats -> hi and lo bf16 fragments.  Pairs are rounded together (one packed convert
-// per two values) and the hi pieces widened back by bit moves; the pieces are the same as
-// element-wise split2.
+// 8 floats -> hi and lo bf16 fragments (pairs rounded by one packed convert each).
 __device__ inline void split8(const float (&f)[8], i32x4& hi, i32x4& lo) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   int h[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f32x2 v = {f[2 * i], f[2 * i + 1]};
-    const int hp = __builtin_bit_cast(int, __builtin_convertvector(v, bf16x2));
-    const f32x2 hv = {__int_as_float(hp << 16), __int_as_float(hp & (int)0xffff0000u)};
-    h[i] = hp;
-    l[i] = __builtin_bit_cast(int, __builtin_convertvector(v - hv, bf16x2));
+    float a = f[2 * i], b = f[2 * i + 1];
+    h[i] = bf16_pair_split(a, b);
+    l[i] = bf16_pair(a, b);
   }
   hi = i32x4{h[0], h[1], h[2], h[3]};
   lo = i32x4{l[0], l[1], l[2], l[3]};

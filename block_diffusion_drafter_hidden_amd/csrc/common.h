@@ -58,6 +58,23 @@ template <> __device__ inline f32x4 mfma_tile<float>(i32x4 a, i32x4 b, f32x4 c) 
 }
 
 // ---------------------------------------------------------------------------------------
+// Pairs of floats to bf16 with one packed round-to-nearest-even convert (v_cvt_pk_bf16_f32).
+// bf16_pair_split also leaves in a and b what the bf16 pieces did not carry (exact in
+// fp32), so repeated calls peel off successive pieces.
+// ---------------------------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline int bf16_pair(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ inline int bf16_pair_split(float& a, float& b) {
+  const int hp = bf16_pair(a, b);
+  a -= __int_as_float(hp << 16);
+  b -= __int_as_float(hp & (int)0xffff0000u);
+  return hp;
+}
+
+// ---------------------------------------------------------------------------------------
 // Activation (A operand) fragments.  Activations live in memory as fp32 (or as the bf16
 // target features).  For bf16 weights an fp32 activation is fed to the bf16 MFMA as a sum
 // of bf16 pieces, one MFMA per piece (bf16 x bf16 products are exact in fp32).
@@ -84,14 +101,10 @@ template <int Terms> struct AFrag<bf16, float, Terms> {
     for (int i = 0; i < 8; ++i) f[i] = src[i];
 #pragma unroll
     for (int t = 0; t < Terms; ++t) {
-      bf16x8 h;
+      int h[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16 hb = (bf16)f[i];
-        h[i] = hb;
-        f[i] = f[i] - (float)hb;
-      }
-      part[t] = __builtin_bit_cast(i32x4, h);
+      for (int i = 0; i < 4; ++i) h[i] = bf16_pair_split(f[2 * i], f[2 * i + 1]);
+      part[t] = i32x4{h[0], h[1], h[2], h[3]};
     }
   }
 };
@@ -167,14 +180,10 @@ __device__ inline void store_hilo(bf16* base, long long off, float v) {
 }
 // Store four consecutive columns k .. k + 3 (k % 4 == 0) of one row: two 8-byte stores.
 __device__ inline void store_hilo4(bf16* base, long long off, f32x4 v) {
-  bf16x4 h, l;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = (bf16)v[e];
-    l[e] = (bf16)(v[e] - (float)h[e]);
-  }
-  *reinterpret_cast<bf16x4*>(base + off) = h;
-  *reinterpret_cast<bf16x4*>(base + off + kHiLoStride) = l;
+  float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+  const int h01 = bf16_pair_split(a0, a1), h23 = bf16_pair_split(a2, a3);
+  *reinterpret_cast<i32x2*>(base + off) = i32x2{h01, h23};
+  *reinterpret_cast<i32x2*>(base + off + kHiLoStride) = i32x2{bf16_pair(a0, a1), bf16_pair(a2, a3)};
 }
 
 // RoPE rotation for frequency `inv` (theta^(-2i/d), computed in fp64 on the host) at

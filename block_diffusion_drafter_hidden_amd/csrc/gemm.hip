@@ -677,14 +677,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       float f[4] = {a[i][0], a[i][1], a[i][2], a[i][3]};
 #pragma unroll
       for (int t = 0; t < kTerms; ++t) {
-        bf16x4 h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16 hb = (bf16)f[e];
-          h[e] = hb;
-          f[e] = f[e] - (float)hb;
-        }
-        reinterpret_cast<i32x2*>(&sm.st.a[buf][t][mt][l])[g] = __builtin_bit_cast(i32x2, h);
+        const int h01 = bf16_pair_split(f[0], f[1]), h23 = bf16_pair_split(f[2], f[3]);
+        reinterpret_cast<i32x2*>(&sm.st.a[buf][t][mt][l])[g] = i32x2{h01, h23};
       }
     }
 #pragma unroll
