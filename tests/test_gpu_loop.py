@@ -7,8 +7,9 @@ hidden features of the block's 16 slots and target ids planted against the draft
 U{0..15} matching drafts, so every accept length is known).  Per iteration and request:
 draft ids bit-exact except near-ties, accept length, bonus (next anchor) and context length
 exact; a request whose drafts differed at an excused near-tie is compared on lengths only
-from then on.  At the end the cache over the whole grown context matches injecting every
-accepted slot's features at once."""
+from then on.  At the end the positions the loop added match injecting every accepted
+slot's features at once.  Cases: fp32 and bf16 models with contexts 37 / 0 / 100 over five
+iterations, and the Qwen3-8B shape at batch 1 with a 2048-token context over three."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +18,7 @@ import oracle.dflash_oracle as ref
 from block_diffusion_drafter_hidden_amd import binding as B_
 from tests import gpu_setup as G
 from tests.test_gpu_parity import SMALL_BF16
-from workloads import TINY, synth
+from workloads import TINY, WORKLOADS, synth
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -27,13 +28,22 @@ ITERS = 5
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16])
 def test_closed_loop_matches_oracle_loop(cfg):
-    ctx0 = [37, 0, 100]
+    _run_loop(cfg, [37, 0, 100], ITERS)
+
+
+def test_closed_loop_qwen3_8b_shape_batch1_ctx2048():
+    """The loop at the full Qwen3-8B shape and the benchmark's context, three iterations."""
+    wl = WORKLOADS["qwen3_b1"]
+    _run_loop(wl.cfg, list(synth.context_lengths(wl)), 3, seed=wl.seed)
+
+
+def _run_loop(cfg, ctx0, iters, seed=0):
     Bn, V = len(ctx0), cfg.vocab
-    s = G.build(cfg, ctx0, tag="loop", extra=16 * (ITERS + 1))
+    s = G.build(cfg, ctx0, tag="loop", extra=16 * (iters + 1), seed=seed)
     anchors0 = synth.anchor_ids(cfg, Bn, tag="loop")
     feats = [[synth.target_features(cfg, 16, f"loop/it{i}/b{b}") for b in range(Bn)]
-             for i in range(ITERS)]
-    draws = [synth.plant_draws(f"loop/it{i}", Bn, V) for i in range(ITERS)]
+             for i in range(iters)]
+    draws = [synth.plant_draws(f"loop/it{i}", Bn, V) for i in range(iters)]
     print(f"[loop {cfg.name}] contexts {ctx0}, planted k per iteration "
           f"{[list(d[0]) for d in draws]}", flush=True)
 
@@ -47,7 +57,7 @@ def test_closed_loop_matches_oracle_loop(cfg):
     dev_draws = [tuple(torch.from_numpy(np.asarray(x)).cuda() for x in d) for d in draws]
     dev_feats = [torch.cat(f).cuda() for f in feats]
     got = []
-    for i in range(ITERS):
+    for i in range(iters):
         s.dr.draft(s.cache, anchors, ids)
         k, fill, r = dev_draws[i]
         t = synth.plant_device(ids, k, fill, r, V)
@@ -85,16 +95,16 @@ def test_closed_loop_matches_oracle_loop(cfg):
                       f"lengths only from here", flush=True)
                 continue
             assert g_bon == rec["bonus"] and g_anc == rec["bonus"], (b, i)
-        # the cache over the grown context equals one-shot injection of the accepted slots
-        T_end = out["ctx_len"]
-        rows = ([s.feats[b]] if ctx0[b] else []) + [
-            f[b][:rec["accept_len"]] for f, rec in zip(feats, out["iterations"])]
-        ke, ve = ref.prefill_context(cfg, s.w, torch.cat(rows), precision="exact")
+        # the positions the loop added hold the one-shot injection of the accepted slots
+        T_end, T0 = out["ctx_len"], int(ctx0[b])
+        rows = [f[b][:rec["accept_len"]] for f, rec in zip(feats, out["iterations"])]
+        ke, ve = ref.prefill_context(cfg, s.w, torch.cat(rows), positions=np.arange(T0, T_end),
+                                     precision="exact")
         gk, gv = G.gather_pool(s, b, T_end, "k"), G.gather_pool(s, b, T_end, "v")
         for l in range(cfg.n_layers):
-            for name, g_, e in (("k", gk[l], ke[l]), ("v", gv[l], ve[l])):
+            for name, g_, e in (("k", gk[l][T0:], ke[l]), ("v", gv[l][T0:], ve[l])):
                 ok, info = G.cache_matches(g_, e, cfg.dtype)
                 assert ok, (b, l, name, info)
-        print(f"[loop {cfg.name}] request {b}: context {ctx0[b]} -> {T_end} over {ITERS} "
+        print(f"[loop {cfg.name}] request {b}: context {ctx0[b]} -> {T_end} over {iters} "
               f"iterations, accept lengths {[r['accept_len'] for r in out['iterations']]}",
               flush=True)
