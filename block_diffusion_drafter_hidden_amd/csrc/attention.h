@@ -6,7 +6,7 @@
 namespace dflash {
 
 constexpr int kAttnMaxChunks = 256;       // context chunks per (request, KV group)
-constexpr int kAttnMaxChunkKeys = 1024;   // keys per chunk (64 pages)
+constexpr int kAttnMaxChunkKeys = 2048;   // keys per chunk (128 pages: two page ids per lane)
 
 struct AttnArgs {
   const float* q;          // [B*16][n_q][d], RoPE applied

@@ -3,8 +3,8 @@
 // the 16 block keys.
 //
 // Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
-// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most 1024, fixed by the
-// caller, so the page ids of a chunk are one load per lane issued before T_b arrives), and
+// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most 2048, fixed by the
+// caller, so the page ids of a chunk are two loads per lane issued before T_b arrives), and
 // the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
 // the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
 // online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
@@ -260,7 +260,8 @@ struct HeadState {
 // and this wave's Q rows.
 template <int D>
 struct ChunkSetup {
-  int kbeg, kend, npg, nsteps, pid_safe;
+  int kbeg, kend, npg, nsteps;
+  int pid_lo, pid_hi;   // lane i: physical page of logical page i (lo) and 64 + i (hi)
   bool has_block;
 };
 
@@ -276,7 +277,8 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
   ChunkSetup<D> cs;
   const int kbeg0 = c * a.chunk;
   const int* table = a.block_table + (long long)b * a.max_pages;
-  const int pid = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
+  const int pid0 = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
+  const int pid1 = table[min(kbeg0 / kPage + kWave + lane, a.max_pages - 1)];
   const int T_b = a.ctx_lens[b];
   cs.has_block = c == a.nc - 1;
   cs.kbeg = min(kbeg0, T_b);
@@ -311,18 +313,22 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
     qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
     qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
   }
-  cs.npg = (cs.kend - cs.kbeg + kPage - 1) / kPage;   // 0..64 (chunk <= 1024 keys)
+  cs.npg = (cs.kend - cs.kbeg + kPage - 1) / kPage;   // 0..128 (chunk <= 2048 keys)
   cs.nsteps = (cs.kend - cs.kbeg + 31) / 32;
   // A page past the chunk's last is read from the last one (its keys are masked), and an
   // empty chunk reads physical page 0 and uses nothing.
-  cs.pid_safe = cs.npg > 0 ? pid : 0;
+  cs.pid_lo = cs.npg > 0 ? pid0 : 0;
+  cs.pid_hi = cs.npg > 0 ? pid1 : 0;
   return cs;
 }
 
 // Physical page of the chunk's logical page li (wave-uniform li), clamped as above.
 template <int D>
 __device__ inline long long chunk_page(const ChunkSetup<D>& cs, int li) {
-  return __builtin_amdgcn_readlane(cs.pid_safe, max(min(li, cs.npg - 1), 0));
+  const int lc = max(min(li, cs.npg - 1), 0);
+  const int lo = __builtin_amdgcn_readlane(cs.pid_lo, min(lc, kWave - 1));
+  const int hi = __builtin_amdgcn_readlane(cs.pid_hi, max(lc - kWave, 0));
+  return lc < kWave ? lo : hi;
 }
 
 template <int D>
