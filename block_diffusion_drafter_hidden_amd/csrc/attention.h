@@ -6,7 +6,8 @@
 namespace dflash {
 
 constexpr int kAttnMaxChunks = 256;       // context chunks per (request, KV group)
-constexpr int kAttnMaxChunkKeys = 2048;   // keys per chunk (128 pages: two page ids per lane)
+constexpr int kAttnMaxChunkKeys = 4096;   // keys per chunk (256 pages)
+constexpr int kAttnPidRegs = kAttnMaxChunkKeys / 16 / 64;   // page ids per lane of a chunk
 
 struct AttnArgs {
   const float* q;          // [B*16][n_q][d], RoPE applied

@@ -3,8 +3,9 @@
 // the 16 block keys.
 //
 // Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
-// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most 2048, fixed by the
-// caller, so the page ids of a chunk are two loads per lane issued before T_b arrives), and
+// [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most kAttnMaxChunkKeys,
+// fixed by the caller, so the page ids of a chunk are a few loads per lane issued before T_b
+// arrives), and
 // the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
 // the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
 // online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
@@ -261,7 +262,7 @@ struct HeadState {
 template <int D>
 struct ChunkSetup {
   int kbeg, kend, npg, nsteps;
-  int pid_lo, pid_hi;   // lane i: physical page of logical page i (lo) and 64 + i (hi)
+  int pid[kAttnPidRegs];   // pid[r] in lane i: physical page of logical page 64 r + i
   bool has_block;
 };
 
@@ -277,8 +278,10 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
   ChunkSetup<D> cs;
   const int kbeg0 = c * a.chunk;
   const int* table = a.block_table + (long long)b * a.max_pages;
-  const int pid0 = table[min(kbeg0 / kPage + lane, a.max_pages - 1)];
-  const int pid1 = table[min(kbeg0 / kPage + kWave + lane, a.max_pages - 1)];
+  int pid[kAttnPidRegs];
+#pragma unroll
+  for (int r = 0; r < kAttnPidRegs; ++r)
+    pid[r] = table[min(kbeg0 / kPage + r * kWave + lane, a.max_pages - 1)];
   const int T_b = a.ctx_lens[b];
   cs.has_block = c == a.nc - 1;
   cs.kbeg = min(kbeg0, T_b);
@@ -313,22 +316,26 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
     qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
     qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 32 + 4);
   }
-  cs.npg = (cs.kend - cs.kbeg + kPage - 1) / kPage;   // 0..128 (chunk <= 2048 keys)
+  cs.npg = (cs.kend - cs.kbeg + kPage - 1) / kPage;   // 0 .. kAttnMaxChunkKeys / 16
   cs.nsteps = (cs.kend - cs.kbeg + 31) / 32;
   // A page past the chunk's last is read from the last one (its keys are masked), and an
   // empty chunk reads physical page 0 and uses nothing.
-  cs.pid_lo = cs.npg > 0 ? pid0 : 0;
-  cs.pid_hi = cs.npg > 0 ? pid1 : 0;
+#pragma unroll
+  for (int r = 0; r < kAttnPidRegs; ++r) cs.pid[r] = cs.npg > 0 ? pid[r] : 0;
   return cs;
 }
 
 // Physical page of the chunk's logical page li (wave-uniform li), clamped as above.
 template <int D>
 __device__ inline long long chunk_page(const ChunkSetup<D>& cs, int li) {
-  const int lc = max(min(li, cs.npg - 1), 0);
-  const int lo = __builtin_amdgcn_readlane(cs.pid_lo, min(lc, kWave - 1));
-  const int hi = __builtin_amdgcn_readlane(cs.pid_hi, max(lc - kWave, 0));
-  return lc < kWave ? lo : hi;
+  const int lc = max(min(li, cs.npg - 1), 0), reg = lc / kWave, ln = lc % kWave;
+  int page = __builtin_amdgcn_readlane(cs.pid[0], ln);
+#pragma unroll
+  for (int r = 1; r < kAttnPidRegs; ++r) {
+    const int v = __builtin_amdgcn_readlane(cs.pid[r], ln);
+    page = reg == r ? v : page;
+  }
+  return page;
 }
 
 template <int D>
