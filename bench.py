@@ -30,6 +30,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--latency-shape", action="store_true",
+                    help="time one draft pass of the batch-1 Qwen3-8B-shaped drafter at 1, 2, "
+                         "3, 5 and 8 layers, and 8 sequential passes of the 1-layer drafter")
     ap.add_argument("--loop", action="store_true",
                     help="time the closed decoding loop (draft, verify, advance, inject) "
                          "against a seeded synthetic target instead of the single step")
@@ -78,6 +81,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.loop:
         return loop_bench(args, wl)
+    if args.latency_shape:
+        return latency_bench(args, wl)
     cfg = wl.cfg
     Bn = wl.batch
     ctx = synth.context_lengths(wl)
@@ -403,6 +408,89 @@ def loop_bench(args, wl):
         "drafted_tokens_per_s": round(Bn * 15 / (ms * 1e-3), 1),
     }
     assert abs(acc_per_iter - planted) < 1e-6, (acc_per_iter, planted)
+    print(json.dumps(out), flush=True)
+
+
+def latency_bench(args, wl):
+    """Draft latency against drafter depth: one block pass (16 slots, 15 drafted tokens) of
+    the workload's drafter shape at batch 1 with 1, 2, 3, 5 and 8 layers, and 8 sequential
+    passes of the 1-layer drafter, each waiting for the previous one -- the cost shape of a
+    1-layer drafter that proposes one token per pass (at batch 1 a pass streams the layer and
+    LM-head weights whatever its row count, so a one-token pass costs what a block pass
+    costs).  Context K/V are seeded values (their content does not change the work)."""
+    import torch
+
+    from block_diffusion_drafter_hidden_amd import Drafter
+    from workloads import scaled, synth
+
+    depths = [1, 2, 3, 5, 8]
+    dev = torch.device("cuda:0")
+    T = int(synth.context_lengths(wl).max())
+    cfg_max = scaled(wl.cfg, n_layers=max(depths))
+    log(f"[latency] generating a {max(depths)}-layer {wl.cfg.name} drafter")
+    w_all = synth.drafter_weights(cfg_max, seed=wl.seed)
+    table, num_pages = synth.page_table(wl.name + "/latency", [T + 16], wl.cfg.page_size, wl.seed)
+    anchors = torch.as_tensor(synth.anchor_ids(wl.cfg, 1, wl.seed)).to(dev)
+    ids = torch.zeros((1, 15), dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+
+    def timed(fn, reps):
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for _ in range(max(args.warmup, 3)):
+                g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows, ar_ms = [], None
+    for L in depths:
+        cfg = scaled(wl.cfg, n_layers=L)
+        keep = set(cfg.weight_shapes())
+        wd = {k: v.to(dev) for k, v in w_all.items() if k in keep}
+        dr = Drafter(cfg, wd, max_batch=1, max_ctx=table.shape[1] * cfg.page_size,
+                     max_inject_rows=256, device=dev)
+        del wd
+        cache = dr.new_cache(table, [T], num_pages)
+        gen = torch.Generator(device=dev).manual_seed(synth.stream_seed(wl.seed, "latency/fill"))
+        for pool in (cache.k_pool, cache.v_pool):
+            pool.normal_(0.0, 3.0, generator=gen)
+        ms = timed(lambda: dr.draft(cache, anchors, ids), args.steps)
+        rows.append({"layers": L, "ms_per_block": round(ms, 4),
+                     "drafted_tokens_per_ms": round(15.0 / ms, 2)})
+        log(f"[latency] {L} layers: {ms:.4f} ms per 16-slot pass")
+        if L == 1:
+            def ar8():
+                for _ in range(8):
+                    dr.draft(cache, anchors, ids)
+            ar_ms = timed(ar8, max(args.steps // 4, 5))
+            log(f"[latency] 1 layer, 8 sequential passes: {ar_ms:.4f} ms")
+        del dr, cache
+        torch.cuda.empty_cache()
+    five = next(r["ms_per_block"] for r in rows if r["layers"] == 5)
+    out = {
+        "metric": "draft latency: one 16-slot block pass by drafter depth vs 8 sequential "
+                  "1-layer passes (batch 1)",
+        "value": round(five, 4), "unit": "ms per block (5 layers)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "dtype": wl.cfg.dtype, "data": "synthetic (seeded weights, seeded context K/V)",
+        "config": {"workload": f"{wl.cfg.name}-batch1-ctx{T}-depth-sweep", "context": T},
+        "rows": rows,
+        "one_layer_8_sequential_passes_ms": round(ar_ms, 4),
+        "five_layer_block_vs_8_sequential_1_layer": round(five / ar_ms, 3),
+    }
     print(json.dumps(out), flush=True)
 
 
