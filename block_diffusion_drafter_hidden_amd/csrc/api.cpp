@@ -350,6 +350,10 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.keys = keys;
   g.keys_ld = rows;
   g.logits_out = logits_out;
+  // The two waves of a k range take alternate k-tiles, so a workgroup reads its n-tiles'
+  // weights front to back together (streaming kernel; LM-head launch 204.5 -> 202.5 us at one
+  // request, same box; the other GEMMs measured slower this way).
+  g.kinter = 1;
   g.ldo = m.V;
   g.draft_rows = draft_rows ? 1 : 0;
   DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
