@@ -28,7 +28,7 @@ library primitive.  Sources, by page and section:
           projections of the draft layers; the target's output distribution is
           preserved).
 
-Readings where the pages are silent (each is listed again in the design doc):
+Readings where the pages are silent:
   R1 block = [anchor (last accepted token), mask x 15]; 15 drafted tokens.
   R3 context occupies positions 0..T-1, the block T..T+15, one RoPE frame.
   R4 the fusion is one linear map without bias or norm.
