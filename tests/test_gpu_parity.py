@@ -35,6 +35,14 @@ SMALL_OSS = scaled(GPT_OSS_120B, name="small-oss", n_layers=2, hidden=576, n_q_h
                    n_feat_layers=3, target_hidden=576)
 
 
+# Narrow hidden width (576: 4.5 column blocks of 128 and 18 k-tiles, so 128-column blocks
+# and the 512-column segments of the residual reduction end ragged) with K deep enough
+# (2048) for the 128-row O and down projections to split it, at 80 rows.
+NARROW_SPLIT = scaled(QWEN3_8B, name="narrow-split", n_layers=2, hidden=576, n_q_heads=16,
+                      n_kv_heads=4, head_dim=128, intermediate=2048, vocab=4160,
+                      n_feat_layers=3, target_hidden=576)
+
+
 def rel_err(a, b):
     return float(np.abs(a - b).max() / np.sqrt(np.mean(b * b)))
 
@@ -99,8 +107,11 @@ def test_injection_in_two_calls_equals_one_call():
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cfg,ctx", [(TINY, [128]), (TINY, [0]), (SMALL_BF16, [200]),
-                                     (SMALL_OSS, [77])])
+                                     (SMALL_OSS, [77]), (NARROW_SPLIT, [40, 0, 77, 130, 16])])
 def test_draft_ids_and_logits_match_oracle(cfg, ctx):
+    """Draft ids and logits against the oracle; the five-request NARROW_SPLIT case runs the
+    128-row kernels with k-splits over ragged blocks and the 256-row LM head on a partial
+    block."""
     s = G.build(cfg, ctx, tag="draft")
     anchors = synth.anchor_ids(cfg, len(ctx))
     ids, logits = G.run_draft(s, anchors, want_logits=True)
