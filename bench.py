@@ -246,6 +246,25 @@ def main():
     step_bytes = es * (H * F + L * 2 * kvd * H + L * w_layer + V * H)
     step_bytes += es * Bn * n_new * F                                   # features read
     step_bytes += es * int(sum(int(T) for T in ctx)) * L * 2 * kvd       # context K/V read
+
+    # Roofline time of the step: every kernel at the larger of its HBM time (algorithmic
+    # bytes / peak bandwidth) and its MFMA time (algorithmic flops / dense peak of the dtype),
+    # summed.  At one request every kernel is HBM-bound (this equals the HBM fraction); with a
+    # batch the GEMMs cross the ridge and the sum grows by their MFMA time.
+    peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
+
+    def roof_us(nbytes, flops):
+        return max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (peak_tf * 1e6))
+
+    R, Rn = Bn * 16, Bn * n_new
+    roof = roof_us(es * (H * F + Rn * F), 2.0 * Rn * H * F)                     # fusion
+    roof += roof_us(es * L * 2 * kvd * H, 2.0 * Rn * L * 2 * kvd * H)          # K|V injection
+    for n_out, k_in in (((qd + 2 * kvd), H), (H, qd), (2 * I, H), (H, I)):     # per layer
+        roof += L * roof_us(es * n_out * k_in, 2.0 * R * n_out * k_in)
+    keys = int(sum(int(T) + 16 for T in ctx))
+    roof += L * roof_us(es * int(sum(int(T) for T in ctx)) * 2 * kvd,         # attention
+                        4.0 * 16 * cfg.n_q_heads * cfg.head_dim * keys)
+    roof += roof_us(es * V * H, 2.0 * Bn * 15 * V * H)                        # LM head
     drafted = Bn * 15
     value = drafted / (ms * 1e-3)
 
@@ -287,6 +306,8 @@ def main():
                    "layers": cfg.n_layers, "hidden": H, "vocab": V, "graph": graph is not None},
         "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
+        "step_roofline_us": round(roof, 1),
+        "step_roofline_fraction": round(roof / (ms * 1e3), 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
