@@ -273,7 +273,7 @@ def main():
     # takes whichever bound is the larger time.
     lm_flops = 2.0 * V * H * rows
     kern = ("gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>" if rows <= 64 or cfg.dtype != "bf16"
-            else "gemm_tall<A_HILO,EPI_ARGMAX,norm>")
+            else "gemm_tall256<EPI_ARGMAX> (256-row blocks)")
     roofline = {"kernel": f"shared LM head + argmax: {kern}; launch_us spans the entry "
                           "point's three launches (rows to fragment layout, LM-head GEMM, "
                           "argmax finalize)",
