@@ -175,7 +175,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
  * Slot j of request b sits at position ctx_lens[b] + j and attends, without a mask, to
  * the ctx_lens[b] cached context entries and the 16 block slots.
  * DFLASH_ERR_UNSUPPORTED if batch > 4096 or the cache's max_pages_per_seq > 16384
- * (262144 positions: at most 256 attention chunks of at most 1024 keys). */
+ * (262144 positions per request). */
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
