@@ -44,9 +44,11 @@
  *
  * Numerics: bf16 models keep weights, target features and the KV cache in bf16; every
  * activation (fused feature, residual stream, normed inputs, q/k/v, attention output,
- * SwiGLU product, logits) is fp32 in memory and enters the bf16 MFMA as a hi + lo pair of
- * bf16 values, accumulating in fp32.  RoPE angles are computed in fp64.  f32 models use
- * fp32 everywhere.
+ * SwiGLU product) is fp32 in memory and enters the bf16 MFMA as a hi + lo pair of bf16
+ * values (the fused feature as three pieces), accumulating in fp32.  The LM head's normed
+ * input enters as its hi piece alone when the call has more than 64 rows (bf16 x bf16
+ * products, fp32 logits).  RoPE angles are computed in fp64.  f32 models use fp32
+ * everywhere.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
