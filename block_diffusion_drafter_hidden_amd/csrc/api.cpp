@@ -244,14 +244,14 @@ struct DraftPlan {
   size_t total;
 };
 
-// k-slices of a 128-row store, residual or Q|K|V GEMM: at least `min_wgs` workgroups and at
-// least 32 k-tiles per slice.  Measured: the residual GEMMs want one workgroup per CU (256;
-// at 256 blocks a split no longer pays for its partials), the deep-K fusion two (512).
-int ksplit_count(const Plan& pl, int n_tiles, int KT, int min_wgs) {
+// k-slices of a 128-row store, residual or Q|K|V GEMM: at least `min_wgs` workgroups (up to
+// max_s slices) and at least 32 k-tiles per slice.  Measured: Q|K|V wants one workgroup per
+// CU (256), the residual GEMMs two rounds but at most two slices, the deep-K fusion 512.
+int ksplit_count(const Plan& pl, int n_tiles, int KT, int min_wgs, int max_s = 8) {
   if (pl.mt != kTallMT) return 1;
   const long long blocks = (long long)cdiv(n_tiles, 8) * pl.n_mblocks;
   int s = 1;
-  while (blocks * s < min_wgs && KT / (s * 2) >= 32 && s < 8) s *= 2;
+  while (blocks * s < min_wgs && KT / (s * 2) >= 32 && s < max_s) s *= 2;
   return s;
 }
 
@@ -265,8 +265,11 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   p.dn = plan_gemm(m.H / 16, m.I / m.ktile, rows, 1, 1, 16, tall);
   const int qkv_tiles = (m.nq + 2 * m.nkv) * m.d / 16;
   if (p.qkv.mt == kTallMT) p.qkv.ksub = ksplit_count(p.qkv, qkv_tiles, m.H / m.ktile, 256);
-  if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile, 256);
-  if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile, 256);
+  // O and down: two rounds of workgroups (512), but at most two k-slices (same box: LLaMA
+  // batch 64 7.27 -> 7.16 ms, gpt-oss batch 128 22.37 -> 21.99 ms per step; four slices at
+  // 512 rows were slower than two).
+  if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile, 512, 2);
+  if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile, 512, 2);
   const int kv_groups = B * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   // Context chunks per (request, KV group): enough workgroups to fill the chip at small
