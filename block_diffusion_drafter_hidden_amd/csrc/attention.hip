@@ -707,15 +707,17 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 // from 16 rows x 8 chunk lanes through LDS; the weighted sum runs over chunks in order.  The
 // result is written in the layout the output projection reads.
 // ------------------------------------------------------------------------------------------
-constexpr int kMergeBatch = 40;
 constexpr int kMergeThreads = 128;   // float4s of a 16 x 32 slice
 
-template <int D>
+// NCMAX: the most chunks the instance takes (its LDS weights and its loads in flight are
+// sized by it; 16 covers every plan but very long contexts at small batch).
+template <int D, int NCMAX>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
+  constexpr int kMergeBatch = NCMAX < 40 ? NCMAX : 40;
   constexpr int NCL = kMergeThreads / kBlock;   // chunk lanes per row
   constexpr int NT = D * 4;                     // float4s of one head's 16 x D partial
-  __shared__ float w_s[kAttnMaxChunks + 1][kBlock];
-  __shared__ float m_s[kAttnMaxChunks + 1][kBlock];
+  __shared__ float w_s[NCMAX + 1][kBlock];
+  __shared__ float m_s[NCMAX + 1][kBlock];
   __shared__ float red[NCL][kBlock];
   __shared__ float M_s[kBlock], invL_s[kBlock];
   const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
@@ -838,8 +840,14 @@ hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
   hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
   if (e != hipSuccess) return e;
   dim3 grid(a.n_q, a.head_dim / 32, batch);
-  if (a.head_dim == 128) attn_merge<128><<<grid, kMergeThreads, 0, stream>>>(a);
-  else attn_merge<64><<<grid, kMergeThreads, 0, stream>>>(a);
+  constexpr int kSmallNc = 16;
+  if (a.head_dim == 128) {
+    if (a.nc <= kSmallNc) attn_merge<128, kSmallNc><<<grid, kMergeThreads, 0, stream>>>(a);
+    else attn_merge<128, kAttnMaxChunks><<<grid, kMergeThreads, 0, stream>>>(a);
+  } else {
+    if (a.nc <= kSmallNc) attn_merge<64, kSmallNc><<<grid, kMergeThreads, 0, stream>>>(a);
+    else attn_merge<64, kAttnMaxChunks><<<grid, kMergeThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

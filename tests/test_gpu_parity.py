@@ -107,11 +107,13 @@ def test_injection_in_two_calls_equals_one_call():
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cfg,ctx", [(TINY, [128]), (TINY, [0]), (SMALL_BF16, [200]),
-                                     (SMALL_OSS, [77]), (NARROW_SPLIT, [40, 0, 77, 130, 16])])
+                                     (SMALL_OSS, [77]), (NARROW_SPLIT, [40, 0, 77, 130, 16]),
+                                     (SMALL_BF16, [1100])])
 def test_draft_ids_and_logits_match_oracle(cfg, ctx):
     """Draft ids and logits against the oracle; the five-request NARROW_SPLIT case runs the
     128-row kernels with k-splits over ragged blocks and the 256-row LM head on a partial
-    block."""
+    block; one request of two KV groups at context 1100 splits the context into 35 chunks
+    (the merge instance for more than 16 chunks)."""
     s = G.build(cfg, ctx, tag="draft")
     anchors = synth.anchor_ids(cfg, len(ctx))
     ids, logits = G.run_draft(s, anchors, want_logits=True)
