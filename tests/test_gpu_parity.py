@@ -202,6 +202,40 @@ def test_ragged_batch_with_permuted_pages_matches_per_request_oracle():
     assert total_excused < len(ctx) * 15
 
 
+def test_maximum_context_per_request():
+    """A request at the largest context the cache geometry allows (16384 pages of 16 slots:
+    262128 context positions plus the 16-slot block) beside a short one: 64 chunks of 4096
+    keys per KV group, 1024 injection calls' worth of rows through the chunked entry point.
+    Draft ids and logits against the oracle; the cached K/V of the last page and of a
+    sample of earlier positions against the exact injected values."""
+    cfg = TINY
+    ctx = [16384 * cfg.page_size - 16, 5]
+    s = G.build(cfg, ctx, tag="maxctx")
+    assert s.table.shape[1] == 16384
+    anchors = synth.anchor_ids(cfg, len(ctx), tag="maxctx-anchor")
+    ids, logits = G.run_draft(s, anchors, want_logits=True)
+    for b in range(len(ctx)):
+        ks, vs = G.oracle_context(s, b)
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
+        bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
+        assert bad == 0, (b, ids[b], orc["ids"], orc["gap"])
+        err = np.abs(logits[b] - orc["logits"])
+        assert err.max() <= 1e-4 * np.abs(orc["logits"]).max(), (b, err.max())
+        if b == 0:
+            T = ctx[0]
+            rng = np.random.Generator(np.random.PCG64(7))
+            pos = np.unique(np.concatenate([rng.integers(0, T, 512), np.arange(T - 16, T)]))
+            pages = s.table[0, pos // cfg.page_size]
+            slot = pos % cfg.page_size
+            kp = s.cache.k_pool.cpu().numpy()   # [L, pages, n_kv, 16, d]
+            vp = s.cache.v_pool.cpu().numpy()   # [L, pages, n_kv, d, 16]
+            for l in range(cfg.n_layers):
+                gk = kp[l, pages, :, slot, :].astype(np.float64)
+                gv = vp[l, pages, :, :, slot].astype(np.float64)
+                assert rel_err(gk, ks[l][pos]) <= 1e-5
+                assert rel_err(gv, vs[l][pos]) <= 1e-5
+
+
 def test_batch_rows_are_independent_and_repeatable():
     """Each request's drafts equal its batch-1 drafts; two runs agree bit for bit."""
     cfg = SMALL_BF16
