@@ -236,6 +236,51 @@ def test_maximum_context_per_request():
                 assert rel_err(gv, vs[l][pos]) <= 1e-5
 
 
+def test_maximum_batch_and_empty_injection():
+    """The largest batch one draft call takes (4096 requests, 65536 block rows through the
+    128- and 256-row kernels) with short ragged contexts, some empty: 48 sampled requests
+    (every empty-context one among them) against the oracle, and greedy verify of planted
+    targets on all 4096 against the oracle's prefix matcher.  An injection of zero rows
+    returns without touching the cache."""
+    cfg = SMALL_BF16
+    n = 4096
+    ctx = synth.uniform_ints("maxbatch/ctx", (n,), 0, 40)
+    ctx[:3] = 0
+    s = G.build(cfg, ctx, tag="maxbatch")
+    k0, v0 = s.cache.k_pool.clone(), s.cache.v_pool.clone()
+    none_i = torch.empty(0, dtype=torch.int32, device="cuda")
+    s.dr.inject(s.cache, torch.empty((0, cfg.feat_dim), dtype=torch.bfloat16, device="cuda"),
+                none_i, none_i)
+    torch.cuda.synchronize()
+    assert torch.equal(k0, s.cache.k_pool) and torch.equal(v0, s.cache.v_pool)
+    del k0, v0
+
+    anchors = synth.anchor_ids(cfg, n, tag="maxbatch-anchor")
+    ids, _ = G.run_draft(s, anchors)
+    rng = np.random.Generator(np.random.PCG64(11))
+    sample = np.unique(np.concatenate([[0, 1, 2, n - 1], np.flatnonzero(ctx == 0),
+                                       rng.integers(0, n, 48)]))[:48]
+    excused = 0
+    for b in sample:
+        ks, vs = G.oracle_context(s, b)
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]))
+        bad, exc = G.compare_ids(ids[b], orc, cfg.dtype)
+        excused += exc
+        assert bad == 0, (b, ids[b], orc["ids"], orc["gap"])
+    assert excused < len(sample) * 15
+
+    tgt, k = synth.planted_targets(ids, cfg.vocab, "maxbatch-verify")
+    acc = torch.empty(n, dtype=torch.int32, device="cuda")
+    bon = torch.empty_like(acc)
+    B.verify_accept(torch.from_numpy(ids).cuda(), torch.from_numpy(tgt).cuda(), acc, bon)
+    torch.cuda.synchronize()
+    acc, bon = acc.cpu().numpy(), bon.cpu().numpy()
+    np.testing.assert_array_equal(acc, k + 1)
+    for b in range(n):
+        a_ref, bonus_ref = ref.verify_greedy(ids[b], tgt[b])[:2]
+        assert acc[b] == a_ref and bon[b] == bonus_ref, b
+
+
 def test_batch_rows_are_independent_and_repeatable():
     """Each request's drafts equal its batch-1 drafts; two runs agree bit for bit."""
     cfg = SMALL_BF16
