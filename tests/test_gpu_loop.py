@@ -108,3 +108,26 @@ def _run_loop(cfg, ctx0, iters, seed=0):
         print(f"[loop {cfg.name}] request {b}: context {ctx0[b]} -> {T_end} over {iters} "
               f"iterations, accept lengths {[r['accept_len'] for r in out['iterations']]}",
               flush=True)
+
+
+def test_advance_bookkeeping_and_clamp_at_cache_end():
+    """dflash_advance alone against its definition: rows b*16+j get sequence b and position
+    T_b + j, clamped to max_ctx - 1 for requests whose block would run past the cache end;
+    contexts grow by the accept length and the bonus becomes the next anchor."""
+    max_ctx = 64
+    T = np.array([0, 10, 48, 60, 63, 20], dtype=np.int32)
+    acc = np.array([1, 16, 5, 3, 1, 9], dtype=np.int32)
+    bonus = np.array([7, 0, 151935, 42, 3, 99], dtype=np.int32)
+    n = len(T)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ctx, anc = d(T.copy()), d(np.full(n, -1, np.int32))
+    seq = d(np.full(n * 16, -1, np.int32))
+    pos = d(np.full(n * 16, -1, np.int32))
+    B_.advance(d(acc), d(bonus), max_ctx, ctx, anc, seq, pos)
+    torch.cuda.synchronize()
+    j = np.arange(16)
+    np.testing.assert_array_equal(seq.cpu().numpy(), np.repeat(np.arange(n), 16))
+    np.testing.assert_array_equal(pos.cpu().numpy().reshape(n, 16),
+                                  np.minimum(T[:, None] + j[None, :], max_ctx - 1))
+    np.testing.assert_array_equal(ctx.cpu().numpy(), T + acc)
+    np.testing.assert_array_equal(anc.cpu().numpy(), bonus)
