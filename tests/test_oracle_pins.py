@@ -215,6 +215,70 @@ def test_argmax_planted_row_and_lowest_index_tie():
     assert o3["ids"][j] == 40 and o3["gap"][j] == 0.0
 
 
+def test_top2_second_value_against_sort():
+    """top2's second value (the one every near-tie excusal rests on) equals the second
+    entry of a descending library sort, on rows with distinct values, a duplicated
+    maximum (gap 0) and a duplicated runner-up; the index is the lowest maximal one."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((300, 97))
+    x[5, [3, 70]] = x[5].max() + 1.0                  # duplicated maximum
+    srt = np.sort(x[6])[::-1]
+    x[6, np.argsort(x[6])[-3]] = srt[1]               # duplicated runner-up
+    idx, v1, v2 = ref.top2(x)
+    desc = -np.sort(-x, axis=1)
+    np.testing.assert_array_equal(v1, desc[:, 0])
+    np.testing.assert_array_equal(v2, desc[:, 1])
+    np.testing.assert_array_equal(idx, [int(np.nonzero(r == r.max())[0][0]) for r in x])
+    assert idx[5] == 3 and v1[5] == v2[5]
+    assert v2[6] == srt[1] and v1[6] - v2[6] == srt[0] - srt[1]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_draft_step_equals_draft_block_over_the_grown_context(dtype):
+    """draft_step (inject the new positions, then draft, then verify) gives the same ids,
+    gaps, accept length and bonus as draft_block over prefill_context of the concatenated
+    features followed by verify_greedy -- injection is incremental."""
+    cfg = scaled(SMALL, name=f"pin-step-{dtype}", dtype=dtype)
+    w = synth.drafter_weights(cfg, seed=3, std=0.2, gain_std=0.2)
+    old = synth.target_features(cfg, 11, "step-old")
+    new = synth.target_features(cfg, 6, "step-new")
+    ks, vs = ref.prefill_context(cfg, w, old)
+    whole = ref.prefill_context(cfg, w, torch.cat([old, new], dim=0))
+    want = ref.draft_block(cfg, w, *whole, anchor=13)
+    t, _ = synth.planted_targets(want["ids"][None], cfg.vocab, f"step-{dtype}", k=np.array([6]))
+    got = ref.draft_step(cfg, w, ks, vs, new, anchor=13, target_ids=t[0])
+    np.testing.assert_array_equal(got["ids"], want["ids"])
+    np.testing.assert_allclose(got["gap"], want["gap"], rtol=1e-12, atol=1e-12)
+    acc, bonus, emitted = ref.verify_greedy(want["ids"], t[0])
+    assert (got["accept_len"], got["bonus"], got["emitted"]) == (acc, bonus, emitted)
+    assert acc == 7
+
+
+def test_inv_cdf_against_searchsorted_and_fallback():
+    """inv_cdf is the first index whose cumulative weight exceeds u * total (the library's
+    right-sided searchsorted), never a zero-weight index; u = 1 (no cumulative sum exceeds
+    the total) falls back to the last positive weight; the margin is the distance to the
+    nearest cell boundary, 0 on a boundary."""
+    rng = np.random.default_rng(22)
+    for _ in range(200):
+        w = rng.random(9) * (rng.random(9) < 0.6)
+        if not w.any():
+            continue
+        c = np.cumsum(w)
+        for u in rng.random(20):
+            j, mg = ref.inv_cdf(w, float(u))
+            assert j == int(np.searchsorted(c, u * c[-1], side="right"))
+            assert w[j] > 0
+            lo = c[j - 1] if j else 0.0
+            assert mg == pytest.approx(min(u * c[-1] - lo, c[j] - u * c[-1]) / c[-1])
+    w = np.array([0.0, 0.2, 0.3, 0.5, 0.0, 0.0])
+    assert ref.inv_cdf(w, 1.0) == (3, 0.0)
+    j, mg = ref.inv_cdf(w, 0.0)
+    assert j == 1 and mg == 0.0
+    j, mg = ref.inv_cdf(w, 0.5)                           # exactly on the 2|3 boundary
+    assert j == 3 and mg == 0.0
+
+
 # ------------------------------------------------------------------------------------------
 # bf16 storage points (reading R19)
 # ------------------------------------------------------------------------------------------
