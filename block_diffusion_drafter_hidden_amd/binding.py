@@ -78,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dflash_workspace_size": (SZ, [P, I32, I32, I32]),
         "dflash_workspace_init": (S, [P, SZ, P]),
         "dflash_fuse_inject_kv": (S, [P, P, P, P, P, P, I32, P, SZ, P]),
-        "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, SZ, P]),
+        "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "dflash_lm_head_argmax": (S, [P, P, P, I32, P, P, P, SZ, P]),
         "dflash_verify_accept": (S, [P, P, I32, P, P, P, P]),
         "dflash_advance": (S, [P, P, I32, I32, P, P, P, P, P]),
@@ -98,6 +98,40 @@ def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
     return C.c_void_p(t.data_ptr())
+
+
+def _model_dtype(ccfg: "Config"):
+    return torch.bfloat16 if ccfg.dtype == DFLASH_BF16 else torch.float32
+
+
+def _arg(t, name: str, dtype, shape=None, device=None, optional: bool = False):
+    """Check one tensor argument before its pointer crosses the ABI: a contiguous tensor
+    on a GPU (on `device` when given) with the dtype and shape the library reads.  Raises
+    ValueError; the library is not called."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name}: required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        want = tuple(shape)
+        if t.dim() != len(want) or any(w is not None and int(a) != w
+                                       for a, w in zip(t.shape, want)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
+    return t
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _stream(stream=None):
@@ -151,13 +185,23 @@ def workspace_init(ws: torch.Tensor, stream=None) -> None:
 
 
 def make_cache(k_pool, v_pool, block_table, ctx_lens, num_pages, max_pages) -> KVCache:
+    dev = _arg(k_pool, "k_pool", None).device
+    _arg(v_pool, "v_pool", k_pool.dtype, tuple(k_pool.shape[:2]) + (None,) * (k_pool.dim() - 2), dev)
+    if k_pool.dim() != 5 or k_pool.shape[1] != num_pages or k_pool.shape[3] != 16:
+        raise ValueError(f"k_pool: shape {tuple(k_pool.shape)}, expected [L, {num_pages}, n_kv, 16, d]")
+    _arg(block_table, "block_table", torch.int32, (None, max_pages), dev)
+    _arg(ctx_lens, "ctx_lens", torch.int32, (block_table.shape[0],), dev)
     return KVCache(k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
                    ctx_lens.data_ptr(), num_pages, max_pages)
 
 
 def fuse_inject_kv(ccfg: Config, packed, cache: KVCache, feats, seq_idx, pos, ws,
                    stream=None) -> None:
-    n_tok = int(feats.shape[0])
+    dev = _arg(ws, "ws", torch.uint8, (None,)).device
+    _arg(packed, "packed", torch.uint8, (None,), dev)
+    n_tok = int(_arg(feats, "feats", _model_dtype(ccfg), (None, ccfg.feat_dim), dev).shape[0])
+    _arg(seq_idx, "seq_idx", torch.int32, (n_tok,), dev)
+    _arg(pos, "pos", torch.int32, (n_tok,), dev)
     _check(load_library().dflash_fuse_inject_kv(
         C.byref(ccfg), _ptr(packed), C.byref(cache), _ptr(feats), _ptr(seq_idx), _ptr(pos),
         n_tok, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
@@ -165,23 +209,38 @@ def fuse_inject_kv(ccfg: Config, packed, cache: KVCache, feats, seq_idx, pos, ws
 
 
 def draft_block(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_ids, ws,
-                logits_out=None, stream=None) -> None:
-    batch = int(anchor_ids.shape[0])
+                logits_out=None, stream=None, top2_gap=None) -> None:
+    dev = _arg(ws, "ws", torch.uint8, (None,)).device
+    _arg(packed, "packed", torch.uint8, (None,), dev)
+    _arg(embed, "embed", _model_dtype(ccfg), (ccfg.vocab, ccfg.hidden), dev)
+    batch = int(_arg(anchor_ids, "anchor_ids", torch.int32, (None,), dev).shape[0])
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, 15), dev)
+    _arg(logits_out, "logits_out", torch.float32, (batch, 15, ccfg.vocab), dev, optional=True)
+    _arg(top2_gap, "top2_gap", torch.float32, (batch, 15), dev, optional=True)
     _check(load_library().dflash_draft_block(
         C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
-        _ptr(draft_ids), _ptr(logits_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(draft_ids), _ptr(top2_gap), _ptr(logits_out), _ptr(ws), _nbytes(ws),
         _stream(stream)), "dflash_draft_block")
 
 
 def lm_head_argmax(ccfg: Config, packed, y, ids_out, ws, logits_out=None, stream=None) -> None:
-    rows = int(y.shape[0])
+    dev = _arg(ws, "ws", torch.uint8, (None,)).device
+    _arg(packed, "packed", torch.uint8, (None,), dev)
+    rows = int(_arg(y, "y", torch.float32, (None, ccfg.hidden), dev).shape[0])
+    _arg(ids_out, "ids_out", torch.int32, (rows,), dev)
+    _arg(logits_out, "logits_out", torch.float32, (rows, ccfg.vocab), dev, optional=True)
     _check(load_library().dflash_lm_head_argmax(
         C.byref(ccfg), _ptr(packed), _ptr(y), rows, _ptr(ids_out), _ptr(logits_out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "dflash_lm_head_argmax")
 
 
 def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream=None) -> None:
-    batch = int(draft_ids.shape[0])
+    batch = int(_arg(draft_ids, "draft_ids", torch.int32, (None, 15)).shape[0])
+    dev = draft_ids.device
+    _arg(target_ids, "target_ids", torch.int32, (batch, 16), dev)
+    _arg(accept_len, "accept_len", torch.int32, (batch,), dev)
+    _arg(bonus, "bonus", torch.int32, (batch,), dev)
+    _arg(emitted, "emitted", torch.int32, (batch, 16), dev, optional=True)
     _check(load_library().dflash_verify_accept(
         _ptr(draft_ids), _ptr(target_ids), batch, _ptr(accept_len), _ptr(bonus),
         _ptr(emitted), _stream(stream)), "dflash_verify_accept")
@@ -189,7 +248,13 @@ def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream
 
 def advance(accept_len, bonus, max_ctx: int, ctx_lens, anchor_ids, inject_seq, inject_pos,
             stream=None) -> None:
-    batch = int(accept_len.shape[0])
+    batch = int(_arg(accept_len, "accept_len", torch.int32, (None,)).shape[0])
+    dev = accept_len.device
+    for name, t, shp in (("bonus", bonus, (batch,)), ("ctx_lens", ctx_lens, (batch,)),
+                         ("anchor_ids", anchor_ids, (batch,)),
+                         ("inject_seq", inject_seq, (batch * 16,)),
+                         ("inject_pos", inject_pos, (batch * 16,))):
+        _arg(t, name, torch.int32, shp, dev)
     _check(load_library().dflash_advance(
         _ptr(accept_len), _ptr(bonus), batch, int(max_ctx), _ptr(ctx_lens), _ptr(anchor_ids),
         _ptr(inject_seq), _ptr(inject_pos), _stream(stream)), "dflash_advance")
@@ -201,7 +266,16 @@ def verify_sampled_workspace_size(batch: int, vocab: int) -> int:
 
 def verify_accept_sampled(draft_logits, target_logits, u_draft, u_accept, u_resample,
                           draft_ids, accept_len, emitted, ws, stream=None) -> None:
-    batch, _, vocab = draft_logits.shape
+    batch, _, vocab = _arg(draft_logits, "draft_logits", torch.float32, (None, 15, None)).shape
+    dev = draft_logits.device
+    _arg(target_logits, "target_logits", torch.float32, (batch, 16, vocab), dev)
+    _arg(u_draft, "u_draft", torch.float32, (batch, 15), dev)
+    _arg(u_accept, "u_accept", torch.float32, (batch, 15), dev)
+    _arg(u_resample, "u_resample", torch.float32, (batch,), dev)
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, 15), dev)
+    _arg(accept_len, "accept_len", torch.int32, (batch,), dev)
+    _arg(emitted, "emitted", torch.int32, (batch, 16), dev)
+    _arg(ws, "ws", torch.uint8, (None,), dev)
     _check(load_library().dflash_verify_accept_sampled(
         _ptr(draft_logits), _ptr(target_logits), _ptr(u_draft), _ptr(u_accept),
         _ptr(u_resample), int(batch), int(vocab), _ptr(draft_ids), _ptr(accept_len),
@@ -264,9 +338,9 @@ class Drafter:
         fuse_inject_kv(self.ccfg, self.packed, cache.c(), feats, seq_idx, pos, self.ws, stream)
 
     def draft(self, cache: PagedCache, anchor_ids, draft_ids, logits_out=None,
-              stream=None) -> None:
+              stream=None, top2_gap=None) -> None:
         draft_block(self.ccfg, self.packed, self.embed, cache.c(), anchor_ids, draft_ids,
-                    self.ws, logits_out, stream)
+                    self.ws, logits_out, stream, top2_gap)
 
     def advance(self, cache: PagedCache, accept_len, bonus, anchor_ids, inject_seq,
                 inject_pos, stream=None) -> None:

@@ -4,6 +4,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 from block_diffusion_drafter_hidden_amd import binding as B
@@ -58,8 +59,8 @@ def test_invalid_config_rejected(field, value, status):
     assert B.workspace_size(c, 1, 16, 128) == 0
     lib = B.load_library()
     # Rejected on the host before any pointer is touched.
-    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None, 0,
-                                  None) == status
+    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None,
+                                  None, 0, None) == status
 
 
 def test_null_arguments_rejected_before_launch():
@@ -67,8 +68,8 @@ def test_null_arguments_rejected_before_launch():
     c = B.make_config(TINY)
     assert lib.dflash_verify_accept(None, None, 4, None, None, None, None) == -1
     assert lib.dflash_workspace_init(None, 0, None) == -1
-    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None, 0,
-                                  None) == -1
+    assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None,
+                                  None, 0, None) == -1
     assert lib.dflash_fuse_inject_kv(C.byref(c), None, None, None, None, None, 4, None, 0,
                                      None) == -1
     assert lib.dflash_verify_accept_sampled(None, None, None, None, None, 1, 8, None, None,
@@ -88,7 +89,7 @@ def test_small_workspace_rejected_before_launch():
     cache = B.KVCache(1, 1, 1, 1, 16, 8)
     fake = C.c_void_p(16)  # never dereferenced: the size check fails first
     st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(cache), fake, 1, fake, None,
-                                fake, 1024, None)
+                                None, fake, 1024, None)
     assert st == -3
     st = lib.dflash_workspace_init(fake, 16, None)
     assert st == -3
@@ -102,12 +103,26 @@ def test_size_limits_rejected_before_launch():
     fake = C.c_void_p(16)  # never dereferenced: the limit check fails first
     ok_cache = B.KVCache(1, 1, 1, 1, 16, 8)
     st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(ok_cache), fake, 4097, fake,
-                                None, fake, 1 << 40, None)
+                                None, None, fake, 1 << 40, None)
     assert st == -2
     long_cache = B.KVCache(1, 1, 1, 1, 16, 16385)
     st = lib.dflash_draft_block(C.byref(c), fake, fake, C.byref(long_cache), fake, 1, fake,
-                                None, fake, 1 << 40, None)
+                                None, None, fake, 1 << 40, None)
     assert st == -2
     st = lib.dflash_lm_head_argmax(C.byref(c), fake, fake, 65537, fake, None, fake, 1 << 40,
                                    None)
     assert st == -2
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The binding checks every tensor (GPU, contiguous, dtype, shape) before a pointer
+    crosses the ABI: an int64 index tensor or a host tensor is an error, not a misread."""
+    import torch
+    cpu32 = torch.zeros((2, 15), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.verify_accept(cpu32, torch.zeros((2, 16), dtype=torch.int32),
+                        torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="ws: required"):
+        B.draft_block(B.make_config(TINY), None, None, None, None, None, None)
+    with pytest.raises(ValueError, match="expected a torch tensor"):
+        B._arg(np.zeros(3), "x", torch.int32)
