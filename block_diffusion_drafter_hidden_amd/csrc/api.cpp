@@ -229,6 +229,7 @@ Plan lm_plan(const Dims& m, int rows) {
   }
   return pl;
 }
+// Best and runner-up keys per (part, row): two arrays of this many bytes each.
 size_t lm_keys_bytes(const Dims& m, int rows) {
   const Plan pl = lm_plan(m, rows);
   return (size_t)argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw) * rows * 8;
@@ -291,7 +292,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   const size_t R = (size_t)m.G * 16;
   p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
-  p.keys = c.take(lm_keys_bytes(m, rows));
+  p.keys = c.take(2 * lm_keys_bytes(m, rows));
   // k-split partials: row-major for the O and down projections, whole 128 x 128 blocks for
   // Q|K|V (one buffer, used by one GEMM at a time).
   const int splits = std::max(p.o.mt == kTallMT ? p.o.ksub : 1, p.dn.mt == kTallMT ? p.dn.ksub : 1);
@@ -336,10 +337,11 @@ constexpr int kInjectChunkRows = 1024;   // rows per fusion + injection launch p
 // Final RMSNorm + shared LM head + argmax over the vocabulary.  `xg` is x * final gain in
 // the fragment layout and ssq the rows' sums of squares (ssq_parts partials, row stride
 // ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
-// keys: workspace for the per-column-block argmax partials, lm_keys_bytes(m, rows) bytes.
+// keys: workspace for the per-column-block argmax partials, 2 * lm_keys_bytes(m, rows)
+// bytes (best keys, then runner-up keys, which are only written when gap_out is set).
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* xg,
                              const float* ssq, int ssq_parts, int ssq_ld, int rows,
-                             bool draft_rows, int* ids_out, float* logits_out,
+                             bool draft_rows, int* ids_out, float* gap_out, float* logits_out,
                              unsigned long long* keys, hipStream_t stream) {
   const Plan pl = lm_plan(m, rows);
   const int parts = argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw);
@@ -351,6 +353,7 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.ssq_ld = ssq_ld;
   g.eps = m.eps;
   g.keys = keys;
+  g.keys2 = gap_out ? keys + lm_keys_bytes(m, rows) / 8 : nullptr;
   g.keys_ld = rows;
   g.logits_out = logits_out;
   // The two waves of a k range take alternate k-tiles, so a workgroup reads its n-tiles'
@@ -360,7 +363,8 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.ldo = m.V;
   g.draft_rows = draft_rows ? 1 : 0;
   DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
-  DF_TRY(launch_argmax_finalize(keys, parts, rows, ids_out, rows, draft_rows ? 1 : 0, stream));
+  DF_TRY(launch_argmax_finalize(keys, g.keys2, parts, rows, ids_out, gap_out, rows,
+                                draft_rows ? 1 : 0, stream));
   return DFLASH_OK;
 }
 
@@ -550,8 +554,8 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
-                                 float* logits_out, void* workspace, size_t ws_bytes,
-                                 hipStream_t stream) {
+                                 float* top2_gap, float* logits_out, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
   Dims m;
   dflash_status st = check_config(cfg, &m);
   if (st != DFLASH_OK) return st;
@@ -678,8 +682,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       DF_TRY(launch_gemm(m.bf16, dp.dn.mt, dp.dn.npw, EPI_RESIDUAL, g, 1, stream));
     }
   }
-  return launch_lm_head(m, P, wb, xg, ssq, dn_parts, rows, rows, true, draft_ids, logits_out,
-                        reinterpret_cast<unsigned long long*>(ws + dp.keys), stream);
+  return launch_lm_head(m, P, wb, xg, ssq, dn_parts, rows, rows, true, draft_ids, top2_gap,
+                        logits_out, reinterpret_cast<unsigned long long*>(ws + dp.keys), stream);
 }
 
 dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed,
@@ -695,7 +699,7 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   // its residual stream, so the LM head runs exactly the draft step's kernel.
   const size_t frag_bytes = align_up((size_t)cdiv(rows, 16) * 16 * m.H * 4);
   const size_t ssq_bytes = align_up((size_t)rows * 4);
-  const size_t key_bytes = align_up(lm_keys_bytes(m, rows));
+  const size_t key_bytes = align_up(2 * lm_keys_bytes(m, rows));
   if (ws_bytes < kSyncBytes + frag_bytes + ssq_bytes + key_bytes) return DFLASH_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   float* xs = reinterpret_cast<float*>(ws + kSyncBytes);
@@ -706,8 +710,8 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   DF_TRY(launch_rows_to_fragments(hidden, rows, m.H, m.bf16,
                                   reinterpret_cast<const float*>(wb + P.final_norm), xs, ssq,
                                   stream));
-  return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, logits_out, keys,
-                        stream);
+  return launch_lm_head(m, P, wb, xs, ssq, 1, rows, rows, false, ids_out, nullptr, logits_out,
+                        keys, stream);
 }
 
 dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch,

@@ -24,7 +24,10 @@
 //     row l%16 -- exactly the P^T fragment the PV product needs once the MFMA k index is
 //     read as key (4*(l/16)+j) of the first page for j < 4 and of the second for j >= 4,
 //     the same order the V^T fragment uses.
-// No LDS and no barriers.  Cache K/V are exact bf16 operands; fp32 queries, probabilities
+// GQA groups of at most 2 heads load these fragments straight from the pages (no LDS,
+// no barriers); groups of 4 or more stage each 32-key step once per workgroup in
+// double-buffered LDS (one barrier per step) and read the fragments from there.  Cache
+// K/V are exact bf16 operands; fp32 queries, probabilities
 // and block keys/values enter as hi + lo bf16 pairs (the lo x lo product, ~2^-32 relative,
 // is dropped).  fp32 models use a VALU version of pass 1 with the same partial layout.
 //

@@ -141,6 +141,31 @@ __device__ inline unsigned long long argmax_key(float v, int idx) {
 __device__ inline int argmax_key_index(unsigned long long k) {
   return (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
 }
+// The value a key was made from (inverse of the order-preserving bit transform).
+__device__ inline float argmax_key_value(unsigned long long k) {
+  const unsigned u = (unsigned)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+// Best two keys (k1 > k2; key 0 = none): insert one key, or merge another best-two pair.
+// Keys are distinct (they carry the column index), so the merge is symmetric.
+__device__ inline void top2_push(unsigned long long& k1, unsigned long long& k2,
+                                 unsigned long long k) {
+  if (k > k1) {
+    k2 = k1;
+    k1 = k;
+  } else if (k > k2) {
+    k2 = k;
+  }
+}
+__device__ inline void top2_merge(unsigned long long& k1, unsigned long long& k2,
+                                  unsigned long long o1, unsigned long long o2) {
+  if (o1 > k1) {
+    k2 = o2 > k1 ? o2 : k1;
+    k1 = o1;
+  } else if (o1 > k2) {
+    k2 = o1;
+  }
+}
 
 // ---------------------------------------------------------------------------------------
 // Fragment ("swizzled") layout of fp32 activations.  An activation matrix [M][K] that feeds

@@ -95,6 +95,7 @@ struct GemmParams {
   // (value, index) keys of each workgroup's best column per row, keys[part * keys_ld + row],
   // part = the workgroup's column block; reduced over parts by the finalize kernel.
   unsigned long long* keys;
+  unsigned long long* keys2;   // may be null: the runner-up key of each part and row, same layout
   int keys_ld;
   float* logits_out;        // [rows][ldo] or null
   int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
@@ -115,9 +116,12 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
 
 // ids[m] = index of the largest key over parts, keys[part * keys_ld + m], for m < rows; with
 // draft_rows the rows are 16-slot blocks and only slots 1..15 produce ids (block b, slot j
-// -> ids[b*15 + j-1]).
-hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int keys_ld,
-                                  int* ids, int rows, int draft_rows, hipStream_t stream);
+// -> ids[b*15 + j-1]).  With keys2 (the parts' runner-up keys) and gap non-null, gap gets
+// the difference of the best and second-best values of the row, same indexing as ids.
+hipError_t launch_argmax_finalize(const unsigned long long* keys,
+                                  const unsigned long long* keys2, int parts, int keys_ld,
+                                  int* ids, float* gap, int rows, int draft_rows,
+                                  hipStream_t stream);
 
 // Column blocks (argmax parts) of an EPI_ARGMAX launch with this plan.
 inline int argmax_parts(int n_tiles, int mt, int npw, int tgpw) {

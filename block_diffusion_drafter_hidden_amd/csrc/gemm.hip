@@ -5,11 +5,10 @@
 // weights from HBM at full bandwidth and feed each 16-byte lane chunk straight into a 16x16
 // MFMA step.  Weights are bf16 (or fp32 for fp32 models); activations are fp32 in memory
 // and enter a bf16 MFMA as a sum of bf16 pieces (see AFrag), except the bf16 target
-// features of the fusion GEMM and, in the 128-row kernel, the LM head's input, which enters
-// as its leading bf16 piece only (the logits are the last values computed, so the error of
-// a bf16 input does not compound through later layers; measured at one request, the
-// streaming kernel runs the LM head faster with both pieces than with one, so it keeps
-// both).  Activations the drafter produces itself live in the
+// features of the fusion GEMM, which are exact in one piece.  (The LM head once took only
+// the leading piece of its input at many rows; its logits then erred by up to 2.1e-2 at the
+// 8B shapes, past half the 2e-2 band within which a drafted id may differ, so every kernel
+// now multiplies both pieces.)  Activations the drafter produces itself live in the
 // fragment layout (swz_off), so a wave's A operand for one k-tile is a couple of fully
 // coalesced 1 KB reads; the epilogues write their outputs in that layout for the next GEMM.
 //
@@ -238,22 +237,26 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       }
     }
     // One wave per row: lanes scan columns, then a wave-wide (value, index) maximum, stored
-    // as this workgroup's part of the row.
+    // as this workgroup's part of the row (with keys2: the best two).
     const int lane = tid % kWave, wave = tid / kWave, nw = nthr / kWave;
     for (int r = wave; r < rows; r += nw) {
       const int m = m0 + r;
       if (m >= p.M) continue;
-      unsigned long long best = 0;
+      unsigned long long best = 0, second = 0;
       for (int c = lane; c < cols; c += kWave) {
         const unsigned long long k = argmax_key(tl[r * ld + c], tile0 * 16 + c);
-        best = k > best ? k : best;
+        top2_push(best, second, k);
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long other = __shfl_xor(best, o, kWave);
-        best = other > best ? other : best;
+        const unsigned long long o1 = __shfl_xor(best, o, kWave);
+        const unsigned long long o2 = __shfl_xor(second, o, kWave);
+        top2_merge(best, second, o1, o2);
       }
-      if (lane == 0) p.keys[(long long)part * p.keys_ld + m] = best;
+      if (lane == 0) {
+        p.keys[(long long)part * p.keys_ld + m] = best;
+        if (p.keys2) p.keys2[(long long)part * p.keys_ld + m] = second;
+      }
     }
   }
 }
@@ -711,9 +714,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * p.KT * 1024 + lane * 8;
     }
     constexpr int kR = 3;
-    // Pieces per A value: the LM head multiplies the hi piece only (bf16 x bf16 products,
-    // fp32 accumulation); every other GEMM both.
-    constexpr int kQ = EPI == EPI_ARGMAX ? 1 : 2;
+    constexpr int kQ = 2;   // pieces per A value (hi and lo)
     i32x4 da[kR][2][kQ], dw[kR][2];   // [stage][m-tile][piece], [stage][chunk]
     auto load_a = [&](int kt, i32x4 (&a)[2][kQ]) {
       const long long off = (long long)(kb + min(kt, KT - 1)) * 1024;
@@ -875,9 +876,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 // but each of the 4 waves owns 64 rows (4 m-tiles) x the block's 128 columns, so the 8 KB of
 // W a wave reads from LDS per k-tile feed 32 MFMAs per A piece instead of 16, and each W
 // block read from HBM or L2 serves 256 rows.
-//   EPI_ARGMAX (one bf16 piece of the input): the epilogue runs in registers -- a lane
-//   scales its values by the row's 1/rms, keeps the best (value, index) key of its column
-//   over the 8 n-tiles, and the 16 lanes of a row group reduce with shuffles.
+//   EPI_ARGMAX: the epilogue runs in registers -- a lane scales its values by the row's
+//   1/rms, keeps the best (value, index) keys (the best two when the runner-up is asked
+//   for) of its column over the 8 n-tiles, and the 16 lanes of a row group reduce with
+//   shuffles.
 //   EPI_SWIGLU (hi + lo pieces): the finished block goes through a 128-row LDS tile in two
 //   halves to the same epilogue as the 128-row kernel.
 // ------------------------------------------------------------------------------------------
@@ -891,7 +893,7 @@ union WideSmem {
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
   static_assert(EPI == EPI_ARGMAX || EPI == EPI_SWIGLU, "LM head and gate|up");
-  constexpr int kQ = EPI == EPI_ARGMAX ? 1 : 2;   // bf16 pieces of the input
+  constexpr int kQ = 2;   // bf16 pieces of the input (hi and lo)
   __shared__ WideSmem sm;
   __shared__ float rstd_s[kWideRows];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1018,14 +1020,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
         const int m = rb * kWideRows + rl;
         const float rs = rstd_s[rl];
-        unsigned long long best = 0;
+        unsigned long long best = 0, second = 0;
 #pragma unroll
         for (int j = 0; j < kTallNT; ++j) {
           const int c = j * 16 + (lane & 15);
           const float v = acc[i][j][e] * rs;
           if (c < cols) {
             const unsigned long long k = argmax_key(v, cb * kTallN + c);
-            best = k > best ? k : best;
+            top2_push(best, second, k);
             if (p.logits_out && m < p.M && !(p.draft_rows && m % kBlock == 0)) {
               const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
               p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
@@ -1034,10 +1036,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-          const unsigned long long other = __shfl_xor(best, o, kWave);
-          best = other > best ? other : best;
+          const unsigned long long o1 = __shfl_xor(best, o, kWave);
+          const unsigned long long o2 = __shfl_xor(second, o, kWave);
+          top2_merge(best, second, o1, o2);
         }
-        if ((lane & 15) == 0 && m < p.M) p.keys[(long long)cb * p.keys_ld + m] = best;
+        if ((lane & 15) == 0 && m < p.M) {
+          p.keys[(long long)cb * p.keys_ld + m] = best;
+          if (p.keys2) p.keys2[(long long)cb * p.keys_ld + m] = second;
+        }
       }
   } else {
     // Two halves of 128 rows through the LDS tile (which reuses the W buffers).
@@ -1347,36 +1353,60 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
 }
 
 // One 256-thread workgroup per row: threads take the parts in strides (8 loads in flight
-// each), then a wave-wide and a workgroup-wide maximum.
+// each), then a wave-wide and a workgroup-wide maximum (the best two with keys2).
 __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* keys,
+                                                              const unsigned long long* keys2,
                                                               int parts, int keys_ld, int* ids,
-                                                              int rows, int draft_rows) {
-  __shared__ unsigned long long red[256 / kWave];
+                                                              float* gap, int rows,
+                                                              int draft_rows) {
+  __shared__ unsigned long long red[2][256 / kWave];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
-  unsigned long long best = 0;
+  unsigned long long best = 0, second = 0;
+  if (keys2) {
+#pragma unroll 4
+    for (int q = tid; q < parts; q += 256) {
+      const unsigned long long k1 = keys[(long long)q * keys_ld + m];
+      const unsigned long long k2 = keys2[(long long)q * keys_ld + m];
+      top2_merge(best, second, k1, k2);
+    }
+  } else {
 #pragma unroll 8
-  for (int q = tid; q < parts; q += 256) {
-    const unsigned long long k = keys[(long long)q * keys_ld + m];
-    best = k > best ? k : best;
+    for (int q = tid; q < parts; q += 256) {
+      const unsigned long long k = keys[(long long)q * keys_ld + m];
+      best = k > best ? k : best;
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const unsigned long long other = __shfl_xor(best, o, kWave);
-    best = other > best ? other : best;
+    const unsigned long long o1 = __shfl_xor(best, o, kWave);
+    const unsigned long long o2 = __shfl_xor(second, o, kWave);
+    top2_merge(best, second, o1, o2);
   }
-  if (lane == 0) red[tid / kWave] = best;
+  if (lane == 0) {
+    red[0][tid / kWave] = best;
+    red[1][tid / kWave] = second;
+  }
   __syncthreads();
   if (tid != 0) return;
-  for (int w = 1; w < 256 / kWave; ++w) best = red[w] > best ? red[w] : best;
+  for (int w = 1; w < 256 / kWave; ++w) top2_merge(best, second, red[0][w], red[1][w]);
   const int idx = argmax_key_index(best);
-  if (!draft_rows) ids[m] = idx;
-  else if (m % kBlock != 0) ids[(m / kBlock) * kDrafts + m % kBlock - 1] = idx;
+  const float g = argmax_key_value(best) - argmax_key_value(second);
+  if (!draft_rows) {
+    ids[m] = idx;
+    if (gap && keys2) gap[m] = g;
+  } else if (m % kBlock != 0) {
+    const long long o = (m / kBlock) * kDrafts + m % kBlock - 1;
+    ids[o] = idx;
+    if (gap && keys2) gap[o] = g;
+  }
 }
 
-hipError_t launch_argmax_finalize(const unsigned long long* keys, int parts, int keys_ld,
-                                  int* ids, int rows, int draft_rows, hipStream_t stream) {
-  argmax_finalize_kernel<<<rows, 256, 0, stream>>>(keys, parts, keys_ld, ids, rows,
-                                                  draft_rows);
+hipError_t launch_argmax_finalize(const unsigned long long* keys,
+                                  const unsigned long long* keys2, int parts, int keys_ld,
+                                  int* ids, float* gap, int rows, int draft_rows,
+                                  hipStream_t stream) {
+  argmax_finalize_kernel<<<rows, 256, 0, stream>>>(keys, gap ? keys2 : nullptr, parts, keys_ld,
+                                                  ids, gap, rows, draft_rows);
   return hipGetLastError();
 }
 

@@ -173,6 +173,11 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
  *   anchor_ids [batch] int32: last accepted token of each request (block slot 0).
  *   draft_ids  [batch, 15] int32 out: argmax over the vocabulary of slots 1..15, exact
  *              fp32 ties resolved to the lowest id.
+ *   top2_gap   [batch, 15] fp32 out, may be NULL: the largest logit of each slot minus the
+ *              second largest (0 for an exact tie).  A small gap marks a near-tie, whose id
+ *              can change under rounding of the logits (wiki, "Conditioning on target-model
+ *              features", closing paragraph: the draft tokens come from the target's shared
+ *              LM head).
  *   logits_out [batch, 15, V] fp32 out, may be NULL: the LM-head logits of slots 1..15.
  * Slot j of request b sits at position ctx_lens[b] + j and attends, without a mask, to
  * the ctx_lens[b] cached context entries and the 16 block slots.
@@ -181,8 +186,8 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
-                                 float* logits_out, void* workspace, size_t ws_bytes,
-                                 hipStream_t stream);
+                                 float* top2_gap, float* logits_out, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream);
 
 /* The last stage of dflash_draft_block on its own: final RMSNorm, the shared LM head and
  * the argmax over the vocabulary.

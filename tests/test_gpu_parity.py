@@ -6,9 +6,10 @@ lengths and bonus tokens bit-exact.  Cached K/V: fp32 within 1e-5 of RMS(ref); b
 the bf16 rounding of a value within 2e-5 (|exact| + RMS) of the exact one (fp32 accumulation
 of the projection lands that close; a value near a rounding boundary may go either way),
 and under 1% of elements may differ from the rounding of the exact value.
-Logits (diagnostic, both sides bf16 cache): mean error below 5e-3 and max below 5e-2; the
-residual difference is exactly those near-midpoint cache values, amplified by attention
-whose scores spread over several units.  Temperature-1 verify:
+Logits of a bf16 model (both sides bf16 cache): error at most 1e-2 (half the near-tie band)
+and 2e-3 on average, and the top-1/top-2 gap recomputed from the GPU logits within 2e-2 of
+the oracle's (gpu_setup.check_request); the residual difference is mostly the
+near-midpoint cache values, amplified by attention whose scores spread over several units.  Temperature-1 verify:
 bit-exact except where the oracle's decision margin is below 1e-9 of the mass (both sides
 evaluate the weights and their sums in fp64).
 """
@@ -116,17 +117,23 @@ def test_draft_ids_and_logits_match_oracle(cfg, ctx):
     (the merge instance for more than 16 chunks)."""
     s = G.build(cfg, ctx, tag="draft")
     anchors = synth.anchor_ids(cfg, len(ctx))
-    ids, logits = G.run_draft(s, anchors, want_logits=True)
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
     for b in range(len(ctx)):
+        if cfg.dtype == "bf16":
+            G.check_injected_request(cfg.name, cfg, s.w, b, int(anchors[b]), ids[b], logits[b],
+                                     gap[b], G.oracle_context(s, b))
+            continue
         ks, vs = G.oracle_context(s, b)
         orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
-        bad, excused = G.compare_ids(ids[b], orc, cfg.dtype)
-        assert bad == 0, (ids[b], orc["ids"], orc["gap"])
-        err = np.abs(logits[b] - orc["logits"])
         if cfg.dtype == "f32":
+            bad, excused = G.compare_ids(ids[b], orc, cfg.dtype)
+            assert bad == 0, (ids[b], orc["ids"], orc["gap"])
+            err = np.abs(logits[b] - orc["logits"])
             assert err.max() <= 1e-4 * np.abs(orc["logits"]).max()
-        else:
-            assert err.mean() < 5e-3 and err.max() < 5e-2, (err.mean(), err.max())
+            same = ids[b] == orc["ids"]
+            np.testing.assert_allclose(gap[b][same], orc["gap"][same], rtol=0,
+                                       atol=2e-4 * np.abs(orc["logits"]).max())
+
 
 
 @pytest.mark.parametrize("cfg,rows", [(SMALL_BF16, 1), (SMALL_BF16, 37), (SMALL_BF16, 150),
@@ -151,10 +158,8 @@ def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
     err = np.abs(logits.cpu().numpy() - lg).max()
     if cfg.dtype == "f32":
         assert err < 1e-5 * np.abs(lg).max(), err
-    elif rows <= 64:   # streaming kernel: both bf16 pieces of the fp32 input
+    else:   # both bf16 pieces of the fp32 input at every row count
         assert err < 1e-4 * np.abs(lg).max(), err
-    else:   # 128-row kernel: bf16 input, fp32 accumulation; well inside the 2e-2 near-tie band
-        assert err < 1e-2, err
 
 
 @pytest.mark.parametrize("n_q,n_kv,d,hidden", [(2, 2, 128, 512), (4, 2, 128, 512),
@@ -176,14 +181,10 @@ def test_multi_step_chunks_every_head_group(n_q, n_kv, d, hidden):
     ctx[0], ctx[1], ctx[2] = 1100, 33, 0   # longest, one step + one key, no context at all
     s = G.build(cfg, ctx, tag="chunks")
     anchors = synth.anchor_ids(cfg, Bn, tag="chunks-anchor")
-    ids, logits = G.run_draft(s, anchors, want_logits=True)
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
     for b in (0, 1, 2, 17):
-        ks, vs = G.oracle_context(s, b)
-        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
-        bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
-        assert bad == 0, (b, ids[b], orc["ids"])
-        err = np.abs(logits[b] - orc["logits"])
-        assert err.mean() < 5e-3 and err.max() < 5e-2, (b, err.mean(), err.max())
+        G.check_injected_request(cfg.name, cfg, s.w, b, int(anchors[b]), ids[b], logits[b],
+                                 gap[b], G.oracle_context(s, b))
 
 
 def test_ragged_batch_with_permuted_pages_matches_per_request_oracle():
@@ -238,10 +239,10 @@ def test_maximum_context_per_request():
 
 def test_maximum_batch_and_empty_injection():
     """The largest batch one draft call takes (4096 requests, 65536 block rows through the
-    128- and 256-row kernels) with short ragged contexts, some empty: 48 sampled requests
-    (every empty-context one among them) against the oracle, and greedy verify of planted
-    targets on all 4096 against the oracle's prefix matcher.  An injection of zero rows
-    returns without touching the cache."""
+    128- and 256-row kernels) with short ragged contexts, some empty: requests 0, 1, 2, the
+    last one and every empty-context one, plus 48 drawn at random, against the oracle,
+    and greedy verify of planted targets on all 4096 against the oracle's prefix matcher.
+    An injection of zero rows returns without touching the cache."""
     cfg = SMALL_BF16
     n = 4096
     ctx = synth.uniform_ints("maxbatch/ctx", (n,), 0, 40)
@@ -258,8 +259,8 @@ def test_maximum_batch_and_empty_injection():
     anchors = synth.anchor_ids(cfg, n, tag="maxbatch-anchor")
     ids, _ = G.run_draft(s, anchors)
     rng = np.random.Generator(np.random.PCG64(11))
-    sample = np.unique(np.concatenate([[0, 1, 2, n - 1], np.flatnonzero(ctx == 0),
-                                       rng.integers(0, n, 48)]))[:48]
+    forced = np.concatenate([[0, 1, 2, n - 1], np.flatnonzero(ctx == 0)])
+    sample = np.union1d(forced, rng.choice(n, 48, replace=False))   # every forced one kept
     excused = 0
     for b in sample:
         ks, vs = G.oracle_context(s, b)
