@@ -26,7 +26,8 @@ EXPORTS = (
     "dflash_workspace_init", "dflash_fuse_inject_kv", "dflash_draft_block",
     "dflash_lm_head_argmax",
     "dflash_verify_accept", "dflash_advance", "dflash_verify_sampled_workspace_size",
-    "dflash_verify_accept_sampled", "dflash_error_string",
+    "dflash_verify_accept_sampled", "dflash_error_string", "dflash_noalloc_scratch_bytes",
+    "dflash_draft_block_noalloc",
 )
 
 
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dflash_verify_sampled_workspace_size": (SZ, [I32, I32]),
         "dflash_verify_accept_sampled": (S, [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "dflash_error_string": (C.c_char_p, [S]),
+        "dflash_noalloc_scratch_bytes": (SZ, []),
+        "dflash_draft_block_noalloc": (S, [P, P, P, P, P, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -221,6 +224,25 @@ def draft_block(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_i
         C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
         _ptr(draft_ids), _ptr(top2_gap), _ptr(logits_out), _ptr(ws), _nbytes(ws),
         _stream(stream)), "dflash_draft_block")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().dflash_noalloc_scratch_bytes())
+
+
+def draft_block_noalloc(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_ids,
+                        logits_out=None, stream=None, top2_gap=None) -> None:
+    """dflash_draft_block_noalloc: the draft step on the library's own scratch array."""
+    dev = _arg(packed, "packed", torch.uint8, (None,)).device
+    _arg(embed, "embed", _model_dtype(ccfg), (ccfg.vocab, ccfg.hidden), dev)
+    batch = int(_arg(anchor_ids, "anchor_ids", torch.int32, (None,), dev).shape[0])
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, 15), dev)
+    _arg(logits_out, "logits_out", torch.float32, (batch, 15, ccfg.vocab), dev, optional=True)
+    _arg(top2_gap, "top2_gap", torch.float32, (batch, 15), dev, optional=True)
+    _check(load_library().dflash_draft_block_noalloc(
+        C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
+        _ptr(draft_ids), _ptr(top2_gap), _ptr(logits_out), _stream(stream)),
+        "dflash_draft_block_noalloc")
 
 
 def lm_head_argmax(ccfg: Config, packed, y, ids_out, ws, logits_out=None, stream=None) -> None:

@@ -21,7 +21,7 @@ OUT = os.path.join(PKG, "libdflash.so")
 OBJDIR = os.path.join(ROOT, "_build", "dflash")
 
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "attention.hip", "small.hip", "sampled.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "small.hip", "sampled.hip", "api.cpp", "noalloc.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Packed fp32 ops stay off for all device code.

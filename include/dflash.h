@@ -189,6 +189,27 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  float* top2_gap, float* logits_out, void* workspace,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* dflash_draft_block for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the workspace replaced by a scratch array compiled into the library
+ * (DFLASH_NOALLOC_SCRATCH_BYTES = 64 MiB on each device the library runs on, held until the
+ * process ends; dflash_noalloc_scratch_bytes() returns the size).  The call allocates
+ * nothing; the array's device address is looked up once per device, on the first call
+ * with that device current.  Every call on one device shares that device's array, and no
+ * call needs its previous contents: calls that overlap on one device (different streams,
+ * no ordering between them) race and must not be made.  DFLASH_ERR_WORKSPACE when the draft
+ * needs more scratch than the array holds (dflash_workspace_size(cfg, batch, 0,
+ * max_pages_per_seq * 16) > DFLASH_NOALLOC_SCRATCH_BYTES: e.g. the Qwen3-8B shape at batch
+ * 16 with a 2048-position cache fits, batch 32 does not); otherwise errors as
+ * dflash_draft_block. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t dflash_noalloc_scratch_bytes(void);
+dflash_status dflash_draft_block_noalloc(const dflash_config* cfg, const void* packed,
+                                         const void* embed, const dflash_kv_cache* cache,
+                                         const int32_t* anchor_ids, int32_t batch,
+                                         int32_t* draft_ids, float* top2_gap,
+                                         float* logits_out, hipStream_t stream);
+
 /* The last stage of dflash_draft_block on its own: final RMSNorm, the shared LM head and
  * the argmax over the vocabulary.
  *   hidden     [rows, H] fp32: residual-stream rows (before the final norm).

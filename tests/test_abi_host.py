@@ -126,3 +126,21 @@ def test_binding_rejects_bad_tensors_before_the_library():
         B.draft_block(B.make_config(TINY), None, None, None, None, None, None)
     with pytest.raises(ValueError, match="expected a torch tensor"):
         B._arg(np.zeros(3), "x", torch.int32)
+
+
+def test_noalloc_entry_rejects_before_touching_the_device():
+    """The no-alloc draft refuses a draft whose scratch need exceeds its fixed array, and
+    bad arguments, on the host (no device lookup, no launch)."""
+    lib = B.load_library()
+    c = B.make_config(QWEN3_8B)
+    limit = B.noalloc_scratch_bytes()
+    assert limit == 64 << 20
+    fake = C.c_void_p(16)  # never dereferenced
+    cache = B.KVCache(1, 1, 1, 1, 4096, 2048)     # 32768 positions per request
+    assert B.workspace_size(c, 32, 0, 2048 * 16) > limit
+    assert lib.dflash_draft_block_noalloc(C.byref(c), fake, fake, C.byref(cache), fake, 32,
+                                          fake, None, None, None) == -3
+    assert lib.dflash_draft_block_noalloc(C.byref(c), fake, fake, None, fake, 1, fake, None,
+                                          None, None) == -1
+    assert lib.dflash_draft_block_noalloc(C.byref(c), fake, fake, C.byref(cache), fake, 0,
+                                          fake, None, None, None) == -1
