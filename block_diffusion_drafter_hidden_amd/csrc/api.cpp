@@ -24,7 +24,9 @@ constexpr int kMaxBatch = 4096;                         // requests per draft ca
 constexpr int kMaxPagesPerSeq = 16384;   // 262144 positions per request
 static_assert(kMaxPagesPerSeq * 16 <= kAttnMaxChunks * kAttnMaxChunkKeys,
               "the attention's chunks cover the longest context");
-constexpr int kTargetWaves = 2048;
+// Waves a streaming-GEMM plan aims at: with the load ring, 4 k-slices per tile group ran the
+// one-request Q|K|V, O, down and fusion GEMMs 1-10% faster than 8 (same box).
+constexpr int kTargetWaves = 768;
 constexpr int kAttnTargetWGs = 128;   // context-chunk workgroups wanted at small batch
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -115,8 +117,8 @@ Packed packed_layout(const Dims& m) {
 // ---------------------------------------------------------------------------------------
 // GEMM planning.  Waves split the k range of a tile group (ksub), a workgroup holds tgpw tile
 // groups; the plan aims at >= kTargetWaves waves in flight with >= 8 k-tiles per wave.
-// (Sweeps over the batch-1 shapes on MI355X put the best plans at 2048-4096 waves of 8-16
-// k-tiles each; the LM head prefers 2 waves per k range and 2 tile groups of 4 n-tiles.)
+// (Sweeps over the batch-1 shapes on MI355X: the LM head prefers 2 waves per k range and 2
+// tile groups of 4 n-tiles; the other GEMMs 4 waves per k range.)
 // ---------------------------------------------------------------------------------------
 struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
@@ -222,7 +224,10 @@ struct Carver {
 // The LM head's plan (the streaming kernel prefers 2 waves per k range and 2 tile groups of
 // 4 n-tiles at one m-tile) and the bytes of its argmax partials.
 Plan lm_plan(const Dims& m, int rows) {
-  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, 4, 1, 16, m.bf16 != 0);
+  // 4 n-tiles per wave up to two m-tiles; at four m-tiles two (4 x 4 tiles of two
+  // accumulator chains and the load ring would not fit the register file).
+  const int mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  Plan pl = plan_gemm(m.V / 16, m.H / m.ktile, rows, mt == 4 ? 2 : 4, 1, 16, m.bf16 != 0);
   if (pl.mt == 1 && (m.V / 16 / 4) % 2 == 0 && m.H / m.ktile >= 32) {
     pl.ksub = 2;
     pl.tgpw = 2;
@@ -737,8 +742,8 @@ dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* targ
 }
 
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab) {
-  if (batch <= 0 || vocab <= 0) return 0;
-  return align_up((size_t)batch * 31 * 2 * sizeof(double));
+  if (batch <= 0 || vocab <= 0 || vocab > kMaxSampledVocab) return 0;
+  return align_up(verify_sampled_stats_bytes(batch, vocab));
 }
 
 dflash_status dflash_verify_accept_sampled(const float* draft_logits,
@@ -751,6 +756,7 @@ dflash_status dflash_verify_accept_sampled(const float* draft_logits,
   if (!draft_logits || !target_logits || !u_draft || !u_accept || !u_resample || !draft_ids ||
       !accept_len || !emitted || !workspace || batch <= 0 || vocab <= 0)
     return DFLASH_ERR_INVALID_ARG;
+  if (vocab > kMaxSampledVocab) return DFLASH_ERR_UNSUPPORTED;
   if (ws_bytes < dflash_verify_sampled_workspace_size(batch, vocab)) return DFLASH_ERR_WORKSPACE;
   SampledArgs a{};
   a.draft_logits = draft_logits;
@@ -760,6 +766,8 @@ dflash_status dflash_verify_accept_sampled(const float* draft_logits,
   a.u_resample = u_resample;
   a.vocab = vocab;
   a.stats = reinterpret_cast<double*>(workspace);
+  a.chunk_sums = a.stats + (size_t)batch * 31 * 2;
+  a.chunks_ld = (vocab + 255) / 256;
   a.draft_ids = draft_ids;
   a.accept_len = accept_len;
   a.emitted = emitted;

@@ -147,24 +147,20 @@ __device__ inline float argmax_key_value(unsigned long long k) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 // Best two keys (k1 > k2; key 0 = none): insert one key, or merge another best-two pair.
-// Keys are distinct (they carry the column index), so the merge is symmetric.
+// Keys are distinct (they carry the column index), so the merge is symmetric.  Written
+// with selects: the branchy form made the compiler keep these 64-bit values on the stack.
 __device__ inline void top2_push(unsigned long long& k1, unsigned long long& k2,
                                  unsigned long long k) {
-  if (k > k1) {
-    k2 = k1;
-    k1 = k;
-  } else if (k > k2) {
-    k2 = k;
-  }
+  const bool gt = k > k1;
+  k2 = gt ? k1 : (k > k2 ? k : k2);
+  k1 = gt ? k : k1;
 }
 __device__ inline void top2_merge(unsigned long long& k1, unsigned long long& k2,
                                   unsigned long long o1, unsigned long long o2) {
-  if (o1 > k1) {
-    k2 = o2 > k1 ? o2 : k1;
-    k1 = o1;
-  } else if (o1 > k2) {
-    k2 = o1;
-  }
+  const bool gt = o1 > k1;
+  const unsigned long long n2 = gt ? (o2 > k1 ? o2 : k1) : (o1 > k2 ? o1 : k2);
+  k1 = gt ? o1 : k1;
+  k2 = n2;
 }
 
 // ---------------------------------------------------------------------------------------

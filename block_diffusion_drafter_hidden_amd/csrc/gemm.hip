@@ -45,20 +45,6 @@ __device__ inline i32x4 load16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
 }
 
-// Raw A values of one k-tile fragment for one lane (kPerLane consecutive k).
-template <typename T, typename AT>
-__device__ inline void load_a_raw(const AT* p, bool valid, float* f) {
-  constexpr int n = Elem<T>::kPerLane;
-  if constexpr (sizeof(AT) == 4) {
-#pragma unroll
-    for (int q = 0; q < n / 4; ++q) {
-      const f32x4 v = valid ? *reinterpret_cast<const f32x4*>(p + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[4 * q + i] = v[i];
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 // Epilogues on the workgroup's dense fp32 tile: rows MT*16, columns cols (tile-major).
 // ------------------------------------------------------------------------------------------
@@ -264,17 +250,31 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
 // ------------------------------------------------------------------------------------------
 // Main kernel
 // ------------------------------------------------------------------------------------------
+// 16-byte A chunks per lane per k-tile and m-tile: the hi and lo pieces of the pair layout;
+// one chunk of bf16 features; kPer / 4 chunks of fp32 values.
+template <typename T, int AK> constexpr int kAChunks =
+    AK == A_HILO ? 2 : (AK == A_ROW_BF16 ? 1 : Elem<T>::kPerLane / 4);
+// Loads in flight per wave: a ring of R groups of KU k-tiles.  A group holds NPW weight
+// chunks and MT * kAChunks activation chunks per k-tile; the ring is sized to about 96
+// VGPRs (measured at one request: 2 x 3 k-tiles for Q|K|V, 2 x 4 for O / down, 2 x 2 for
+// the LM head streamed as fast as 4-deep unrolled batches or faster).
+template <typename T, int AK, int MT, int NPW> struct Ring {
+  static constexpr int kUnits = NPW + MT * kAChunks<T, AK>;
+  static constexpr int kTiles = 24 / kUnits < 2 ? 2 : (24 / kUnits > 8 ? 8 : 24 / kUnits);
+  static constexpr int KU = kTiles >= 4 ? 2 : 1;
+  static constexpr int R = kTiles / KU;
+};
+
 template <typename T, int AK, int MT, int NPW, int EPI, bool NORM>
 __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(GemmParams p) {
   __shared__ GemmSmem sm;
   constexpr int kTerms = EPI == EPI_INJECT ? 3 : 2;
   static_assert(AK != A_HILO || std::is_same<T, bf16>::value, "pair pieces feed bf16 MFMAs");
   typedef typename std::conditional<AK == A_ROW_BF16 || AK == A_HILO, bf16, float>::type AT;
-  typedef AFrag<T, AT, kTerms> Frag;
+  typedef AFrag<T, float, kTerms> FFrag;
   constexpr int kPer = Elem<T>::kPerLane;
-  // k-tiles whose loads are issued together (raw fp32 A and its pieces stay in registers).
-  constexpr int U0 = (NPW * MT >= 4) ? 2 : (NPW * MT == 2 ? 4 : 8);
-  constexpr int U = kTerms > 2 ? (U0 > 2 ? U0 / 2 : 2) : U0;
+  constexpr int NA = kAChunks<T, AK>;
+  constexpr int KU = Ring<T, AK, MT, NPW>::KU, R = Ring<T, AK, MT, NPW>::R;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -303,11 +303,13 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   const int wg_tile0 = group * p.tgpw * NPW;
   const int tile0 = wg_tile0 + tg * NPW;
   const int z = blockIdx.z;
-  // k-tiles of this wave: kt = kb + i*kstep for kt < ke.
+  // k-tiles of this wave: kb + i * kstep for i < nk.
   const int kw = (p.KT + ksub - 1) / ksub;
   const int kstep = p.kinter ? ksub : 1;
   const int kb = p.kinter ? ks : min(ks * kw, p.KT);
   const int ke = p.kinter ? p.KT : min(kb + kw, p.KT);
+  const int nk = ke > kb ? (ke - kb + kstep - 1) / kstep : 0;
+  const int G = (nk + KU - 1) / KU;   // groups of KU k-tiles
 
   const char* wp[NPW];
 #pragma unroll
@@ -316,25 +318,61 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
             (long long)(p.nt0 + tile0 + t) * p.nt_stride * kTileBytes + lane * 16;
   const long long kbytes = p.kt_stride * kTileBytes;
 
-  // A pointers per m-tile.  Row-major kinds: this lane's row and k-slice; fragment layout:
-  // this lane's 16 bytes of k-tile 0 (k-tiles are kPer/4 KB apart).
+  // A pointers per m-tile.  Row-major kinds: this lane's row and k-slice; fragment layouts:
+  // this lane's 16 bytes of k-tile 0.  M-tiles past the valid rows re-read the last valid
+  // one (their rows reach only output rows the epilogue never stores, and a row of the
+  // product depends on that row of A alone), so every load is in bounds and unconditional.
   constexpr int kGroups = kPer / 4;
   const AT* A = reinterpret_cast<const AT*>(p.A);
   const AT* arow[MT];
-  bool aval[MT];
+  const int n_mtiles_valid = (p.M + 15) / 16;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int mtile = mblock * MT + mt;
-    const int r = mtile * 16 + (lane & 15);
-    aval[mt] = r < p.M;
+    const int mtile = min(mblock * MT + mt, n_mtiles_valid - 1);
+    const int r = min(mtile * 16 + (lane & 15), p.M - 1);
     if constexpr (AK == A_SWZ)
       arow[mt] = A + (long long)mtile * p.KT * kGroups * 256 + lane * 4;
     else if constexpr (AK == A_HILO)
       arow[mt] = A + (long long)mtile * p.KT * 1024 + lane * 8;
     else
-      arow[mt] = A + (long long)(aval[mt] ? r : 0) * p.lda + (lane >> 4) * kPer;
+      arow[mt] = A + (long long)r * p.lda + (lane >> 4) * kPer;
   }
 
+  struct Group {
+    i32x4 w[KU][NPW];
+    i32x4 a[KU][MT][NA];
+  };
+  Group ring[R];
+  // Loads of group g; k-tiles past the wave's last re-read it (never out of bounds).
+  auto load = [&](Group& gr, int g) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int kt = kb + min(g * KU + u, nk - 1) * kstep;
+#pragma unroll
+      for (int t = 0; t < NPW; ++t) gr.w[u][t] = load16(wp[t] + (long long)kt * kbytes);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (AK == A_HILO) {
+          const AT* src = arow[mt] + (long long)kt * 1024;
+          gr.a[u][mt][0] = *reinterpret_cast<const i32x4*>(src);
+          gr.a[u][mt][1] = *reinterpret_cast<const i32x4*>(src + kHiLoStride);
+        } else if constexpr (AK == A_ROW_BF16) {
+          gr.a[u][mt][0] =
+              *reinterpret_cast<const i32x4*>(arow[mt] + (long long)kt * Elem<T>::kTile);
+        } else if constexpr (AK == A_SWZ) {
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+            gr.a[u][mt][q] = *reinterpret_cast<const i32x4*>(
+                arow[mt] + ((long long)kt * kGroups + q) * 256);
+        } else {
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+            gr.a[u][mt][q] = *reinterpret_cast<const i32x4*>(
+                arow[mt] + (long long)kt * Elem<T>::kTile + 4 * q);
+        }
+      }
+    }
+  };
   // acc takes the products of the first A piece, acc_lo those of the others: two
   // independent MFMA chains per tile (added together after the loop).
   f32x4 acc[NPW][MT], acc_lo[NPW][MT];
@@ -342,9 +380,51 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   for (int t = 0; t < NPW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = acc_lo[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // RMSNorm: this thread's share of the rows' partial sums of squares, fetched now and
-  // summed after the main loop.  Thread t always serves row t % rows (blockDim is a multiple
-  // of 64, rows = 16 * MT <= 64).
+  // MFMAs of group g; with `check`, k-tiles past the wave's last are skipped (wave-uniform).
+  auto compute = [&](const Group& gr, int g, bool check) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (check && g * KU + u >= nk) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (AK == A_HILO) {   // ready-made pieces: hi feeds acc, lo feeds acc_lo
+#pragma unroll
+          for (int t = 0; t < NPW; ++t) {
+            acc[t][mt] = mfma_tile<T>(gr.a[u][mt][0], gr.w[u][t], acc[t][mt]);
+            acc_lo[t][mt] = mfma_tile<T>(gr.a[u][mt][1], gr.w[u][t], acc_lo[t][mt]);
+          }
+        } else if constexpr (AK == A_ROW_BF16) {   // bf16 features: exact in one piece
+#pragma unroll
+          for (int t = 0; t < NPW; ++t)
+            acc[t][mt] = mfma_tile<T>(gr.a[u][mt][0], gr.w[u][t], acc[t][mt]);
+        } else {   // fp32 values: split into pieces right before their MFMAs
+          float f[kPer];
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * q + e] = __int_as_float(gr.a[u][mt][q][e]);
+          FFrag a;
+          a.from_floats(f);
+#pragma unroll
+          for (int t = 0; t < NPW; ++t)
+#pragma unroll
+            for (int q = 0; q < FFrag::kTerms; ++q)
+              if (q == 0) acc[t][mt] = mfma_tile<T>(a.part[q], gr.w[u][t], acc[t][mt]);
+              else acc_lo[t][mt] = mfma_tile<T>(a.part[q], gr.w[u][t], acc_lo[t][mt]);
+        }
+      }
+    }
+  };
+
+  // The ring's first loads go out before anything else, so the first weights arrive as
+  // early as possible; the values only the epilogue needs are fetched after them.
+  if (nk > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) load(ring[r], r);
+  }
+  // RMSNorm: this thread's share of the rows' partial sums of squares, summed after the
+  // main loop.  Thread t always serves row t % rows (blockDim is a multiple of 64, rows =
+  // 16 * MT <= 64).
   constexpr int kSsqPer = NORM ? 16 : 1;
   float sq[kSsqPer];
   if constexpr (NORM) {
@@ -356,7 +436,8 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
       sq[i] = idx < total && m < p.M ? p.ssq_in[(long long)(idx / rows) * p.ssq_ld + m] : 0.f;
     }
   }
-
+  // Residual values a thread adds in the epilogue (read now, so the epilogue has no
+  // dependent global load).
   constexpr int NPRE = EPI == EPI_RESIDUAL ? ResidualPrefetch<MT, NPW>::kN : 0;
   float xpre[NPRE > 0 ? NPRE : 1];
   if constexpr (NPRE > 0) {
@@ -373,88 +454,28 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
     }
   }
 
-  const i32x4 zero = {0, 0, 0, 0};
-  for (int kt = kb; kt < ke; kt += U * kstep) {
-    i32x4 b[U][NPW];
+  // Main loop: group g is multiplied while groups g + 1 .. g + R - 1 are in flight, then its
+  // registers are refilled with group g + R.  Full rounds of R groups whose refills are all
+  // needed run without conditions; the last groups follow.
+  if (nk > 0) {
+    int g = 0;
+    for (; g + 2 * R <= G; g += R) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < NPW; ++t)
-        b[u][t] = (kt + u * kstep < ke) ? load16(wp[t] + (long long)(kt + u * kstep) * kbytes)
-                                        : zero;
-    if constexpr (AK == A_HILO) {
-      // Ready-made pieces: hi feeds acc, lo feeds acc_lo.
-      i32x4 ah[U][MT], al[U][MT];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bool v = kt + u * kstep < ke && aval[mt];
-          const AT* src = arow[mt] + (long long)(kt + u * kstep) * 1024;
-          ah[u][mt] = v ? *reinterpret_cast<const i32x4*>(src) : zero;
-          al[u][mt] = v ? *reinterpret_cast<const i32x4*>(src + kHiLoStride) : zero;
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int t = 0; t < NPW; ++t) {
-            acc[t][mt] = mfma_tile<T>(ah[u][mt], b[u][t], acc[t][mt]);
-            acc_lo[t][mt] = mfma_tile<T>(al[u][mt], b[u][t], acc_lo[t][mt]);
-          }
-    } else if constexpr (sizeof(AT) == 2) {
-      Frag a[U][MT];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          a[u][mt].load(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile,
-                        kt + u * kstep < ke && aval[mt]);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int t = 0; t < NPW; ++t)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[t][mt] = mfma_tile<T>(a[u][mt].part[0], b[u][t], acc[t][mt]);
-    } else {
-      float f[U][MT][kPer];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bool v = kt + u * kstep < ke && aval[mt];
-          if constexpr (AK == A_SWZ) {
-#pragma unroll
-            for (int gq = 0; gq < kGroups; ++gq) {
-              const f32x4 a4 =
-                  v ? *reinterpret_cast<const f32x4*>(
-                          arow[mt] + ((long long)(kt + u * kstep) * kGroups + gq) * 256)
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int i = 0; i < 4; ++i) f[u][mt][4 * gq + i] = a4[i];
-            }
-          } else {
-            load_a_raw<T, AT>(arow[mt] + (long long)(kt + u * kstep) * Elem<T>::kTile, v,
-                              f[u][mt]);
-          }
-        }
-      // Split each fragment right before its MFMAs to keep few pieces alive.
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          Frag a;
-          a.from_floats(f[u][mt]);
-#pragma unroll
-          for (int t = 0; t < NPW; ++t)
-#pragma unroll
-            for (int q = 0; q < Frag::kTerms; ++q)
-              if (q == 0) acc[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc[t][mt]);
-              else acc_lo[t][mt] = mfma_tile<T>(a.part[q], b[u][t], acc_lo[t][mt]);
-        }
+      for (int r = 0; r < R; ++r) {
+        compute(ring[r], g + r, false);
+        load(ring[r], g + r + R);
+      }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (g + r < G) {
+        compute(ring[r], g + r, true);
+        if (g + r + R < G) load(ring[r], g + r + R);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (g + R + r < G) compute(ring[r], g + R + r, true);
   }
 
 #pragma unroll
@@ -514,7 +535,6 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   __syncthreads();
   run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, group, xpre);
 }
-
 
 // ------------------------------------------------------------------------------------------
 // Tall variant for many rows (batched drafts, prefill chunks): a workgroup of 4 waves owns a
@@ -1093,7 +1113,10 @@ template <typename T, int AK, int MT, int EPI, bool NORM>
 static hipError_t by_npw(int npw, const GemmParams& p, int layers, hipStream_t stream) {
   if (npw == 1) return go<T, AK, MT, 1, EPI, NORM>(p, layers, stream);
   if (npw == 2) return go<T, AK, MT, 2, EPI, NORM>(p, layers, stream);
-  if (npw == 4) return go<T, AK, MT, 4, EPI, NORM>(p, layers, stream);
+  // 4 n-tiles at 4 m-tiles would not fit the register file with the load ring.
+  if constexpr (MT < 4) {
+    if (npw == 4) return go<T, AK, MT, 4, EPI, NORM>(p, layers, stream);
+  }
   if constexpr (EPI == EPI_ARGMAX && MT == 1) {   // the LM head's wide, single-m-tile case
     if (npw == 8) return go<T, AK, MT, 8, EPI, NORM>(p, layers, stream);
   }
