@@ -13,11 +13,20 @@ struct SampledArgs {
   const float* u_resample;     // [B]
   int vocab;
   double* stats;               // [B][31][2] workspace: (max, sum exp) per row, fp64
+  double* chunk_sums;          // [B][chunks_ld] workspace: sums of the final draw's weights
+                               // over each 256-element chunk of its row
+  int chunks_ld;               // ceil(V / 256)
   int* draft_ids;              // [B][15]
   int* accept_len;             // [B]
   int* emitted;                // [B][16]
 };
 
+// Largest vocabulary of the temperature-1 verify: 4096 chunks of 256 logits, whose
+// statistics a workgroup keeps in 48 KB of LDS.
+constexpr int kMaxSampledVocab = 4096 * 256;
+
 hipError_t launch_verify_sampled(const SampledArgs& a, int batch, hipStream_t stream);
+// Workspace bytes of launch_verify_sampled (row statistics, then chunk sums).
+size_t verify_sampled_stats_bytes(int batch, int vocab);
 
 }  // namespace dflash

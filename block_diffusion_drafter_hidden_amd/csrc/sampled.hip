@@ -1,213 +1,439 @@
 // Temperature-1 verification: speculative accept/reject with residual resampling.
 //
+// A row of V logits is read in "wave chunks" of 256 consecutive elements (one wave, 16
+// bytes per lane: 1 KB contiguous per load instruction).  Wave w of a workgroup takes wave
+// chunks w, w + 4, ...; each chunk is reduced inside the wave (shuffles, no barrier).
+//
 // Kernel 1, one workgroup per (request, row) over the 15 draft rows and 16 target rows:
-// softmax statistics (row max, sum of exp(x - max)) and, for draft rows, the inverse-CDF
-// draw of the draft token.  Kernel 2, one workgroup per request: the sequential accept test
-// over the 15 drafts (scalar reads of the statistics), then one inverse-CDF draw from the
-// residual max(0, p - q) at the first rejection, or from p_16 if every draft is accepted.
+// the row's softmax statistics (max m, sum of exp(x - m)) in one pass, each lane summing
+// against a per-wave reference (layout at kSC below).  For a draft row the sums of every
+// 1024 elements are kept in LDS, and the draft token is drawn by inverse CDF: a prefix over
+// those sums finds the 1024 elements that cross u * total, which one wave scans (4 KB read
+// again).
+// Kernel 2, kSegWG workgroups per request: each evaluates the accept tests (one lane per
+// draft), finds the first rejection i and writes the chunk sums of the weights the last
+// token is drawn from -- the residual max(0, p_i - q_i), or p_16 when every draft is
+// accepted.  Kernel 3, one workgroup per request: the prefix over those chunk sums and a
+// scan of the crossing chunk draw the token.  Every row is read once, plus 1 KB per draw;
+// the rejected pair is read once more by kernel 2.
 //
-// Inverse CDF over a row of V weights: each of the 256 threads owns a contiguous segment;
-// segment sums, an exclusive prefix over segments in thread order, then the segment that
-// crosses u * total is scanned element by element.  All sums run in a fixed order.
-//
-// Weights exp(x - max), sums, the accept test and the residual are evaluated in fp64: with
-// a 128k vocabulary one token's share of the mass is ~1e-5, so fp32 running sums (relative
-// error ~1e-6) would move the sampled index; fp64 keeps every decision the same as an fp64
-// evaluation of the rule up to ~1e-13 of the mass.
+// Weights exp(x - m), sums, prefixes and the accept test are fp64, in a fixed order: with
+// a 128k vocabulary a token's share of the mass is ~1e-5, and fp32 weights (x - m rounded,
+// then exp) err by up to ~1e-6 relative, enough to move a draw into a neighbouring cell.
+// exp runs as 2^((x - m) log2 e) with the exponent split off and a degree-8 Taylor polynomial
+// for 2^f, |f| <= 1/2 (relative error < 2e-10).  A decision then differs from an exact
+// evaluation of the rule only when u * total lies within ~1e-9 of the mass of a cumulative
+// boundary, or u * q within ~1e-9 relative of p.
 #include "common.h"
 #include "sampled.h"
 
 namespace dflash {
 
 constexpr int kThr = 256;
-constexpr int kRows = 2 * kDrafts + 1;  // 15 draft rows + 16 target rows
+constexpr int kWaves = kThr / kWave;
+constexpr int kRows = 2 * kDrafts + 1;   // 15 draft rows + 16 target rows
+constexpr int kWC = 4 * kWave;           // elements per wave chunk
+constexpr int kSegWG = 32;               // workgroups per request in kernel 2
 
-struct RowScan {
-  double seg[kThr];
-  double pre[kThr];
-  float red[kThr];
-  double dred[kThr];
-  int pick;
-  double total;
+// exp(x - m) for x <= m, as 2^y with y = (x - m) log2 e formed by one fp64 fma from
+// c = -m log2 e: 2^n * 2^f with n = round(y) (by adding and subtracting 1.5 * 2^52),
+// f = y - n in [-1/2, 1/2], and 2^f = sum_k (f ln 2)^k / k! to k = 8 (truncation < 2e-10
+// relative; the terms k >= 4, below 6e-4, in fp32), 2^n written into the exponent bits.
+// Results below 2^-1022 are flushed to 0 (far below any decision's resolution).
+constexpr double kLog2eD = 1.4426950408889634074;
+__device__ inline double exp_from(float x, double c) {
+  constexpr double kRound = 6755399441055744.0;   // 1.5 * 2^52
+  constexpr double c1 = 0.69314718055994530942, c2 = 0.24022650695910071233,
+                   c3 = 0.055504108664821579953;
+  constexpr float c4 = 0.0096181291076284771620f, c5 = 0.0013333558146428443423f,
+                  c6 = 1.5403530393381609955e-4f, c7 = 1.5252733804059840280e-5f,
+                  c8 = 1.3215486790144309489e-6f;
+  const double y = fma((double)x, kLog2eD, c);
+  if (!(y > -1022.0)) return 0.0;
+  const double r = y + kRound;
+  const double f = y - (r - kRound);
+  const float ff = (float)f;
+  const float q = fmaf(fmaf(fmaf(fmaf(c8, ff, c7), ff, c6), ff, c5), ff, c4);
+  const double p = fma(fma(fma(fma((double)q, f, c3), f, c2), f, c1), f, 1.0);
+  const int ni = (int)(unsigned)(__double_as_longlong(r) & 0xFFFFFFFFull);   // n, exactly
+  return p * __longlong_as_double((long long)(ni + 1023) << 52);
+}
+__device__ inline double neg_scaled(float m) { return -(double)m * kLog2eD; }
+__device__ inline double expw(float x, float m) { return exp_from(x, neg_scaled(m)); }
+
+// Four elements v0 .. v0+3 of a row (v0 % 4 == 0); past V they read as -inf.
+__device__ inline f32x4 load4(const float* x, int v0, int V, bool vec) {
+  if (vec && v0 + 3 < V) return *reinterpret_cast<const f32x4*>(x + v0);
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = v0 + e < V ? x[v0 + e] : -INFINITY;
+  return r;
+}
+
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// The first index whose inclusive prefix over n values r(k) (k = 0 .. n-1, in order),
+// starting from `base`, exceeds thr; n if none.  *before gets the prefix before it (the
+// whole sum plus base when none).  red must hold kWaves + 1 doubles, pick kWaves ints.  All
+// threads call; all get the result.  Fixed summation order.
+template <typename R>
+__device__ int block_cross(R r, int n, double base, double thr, double* red, int* pick,
+                           double* before) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  for (int k0 = 0; k0 < n; k0 += kThr) {
+    const int k = k0 + tid;
+    const double x = k < n ? r(k) : 0.0;
+    double inc = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += y;
+    }
+    if (lane == kWave - 1) red[w] = inc;
+    __syncthreads();
+    double pre = base;
+    for (int i = 0; i < w; ++i) pre += red[i];
+    double all = base;
+    for (int i = 0; i < kWaves; ++i) all += red[i];
+    const bool hit = k < n && pre + inc > thr;
+    const unsigned long long bal = __ballot(hit);
+    if (lane == 0) pick[w] = bal ? k0 + w * kWave + __ffsll((long long)bal) - 1 : -1;
+    __syncthreads();
+    int first = -1;
+    for (int i = 0; i < kWaves && first < 0; ++i) first = pick[i];
+    if (first >= 0) {
+      // the prefix before `first`: its thread's exclusive prefix, sent through LDS
+      if (k == first) red[kWaves] = pre + inc - x;
+      __syncthreads();
+      *before = red[kWaves];
+      __syncthreads();
+      return first;
+    }
+    __syncthreads();
+    base = all;
+  }
+  *before = base;
+  return n;
+}
+
+// One wave's inverse-CDF scan of the 256 elements of wave chunk c: the first j whose running
+// sum from `base` exceeds thr, else the chunk's last positive weight (or -1).  w.four(v0,
+// e) gives the weights of v0 .. v0 + 3 (0 past the row).
+template <typename W>
+__device__ int wave_scan(const W& w, int c, double base, double thr) {
+  const int lane = threadIdx.x % kWave;
+  const int v0 = c * kWC + 4 * lane;
+  double e[4];
+  w.four(v0, e);
+  const double t = (e[0] + e[1]) + (e[2] + e[3]);
+  double inc = t;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += y;
+  }
+  double run = base + inc - t;
+  int hit = -1, last = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    run += e[j];
+    if (hit < 0 && run > thr && e[j] > 0.0) hit = v0 + j;
+    if (e[j] > 0.0) last = v0 + j;
+  }
+  const unsigned long long bal = __ballot(hit >= 0);
+  if (bal) return __shfl(hit, __ffsll((long long)bal) - 1, kWave);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+  return last;
+}
+
+// exp(x - m) of a row.
+struct RowWeights {
+  const float* x;
+  int V;
+  bool vec;
+  float m;
+  __device__ void four(int v0, double* e) const {
+    const f32x4 v = load4(x, v0, V, vec);
+    const double k = neg_scaled(m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = exp_from(v[j], k);
+  }
 };
 
-// Inverse CDF of weights w(v) (v in [0, V)) at u: smallest j with cumsum(w)[j] > u * sum(w),
-// else the last j with w(j) > 0.  The running sum is the exclusive prefix of the segment
-// sums plus a wave-level inclusive scan inside the segment, always in the same order.
-// Must be called by all threads; returns the index to all.
-template <typename W>
-__device__ int inv_cdf_row(W w, int V, float u, RowScan& sh, double* total_out) {
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int seg_len = (V + kThr - 1) / kThr;
-  {
-    const int s0 = min(tid * seg_len, V), s1 = min(s0 + seg_len, V);
-    double s = 0.0;
-    for (int v = s0; v < s1; ++v) s += w(v);
-    sh.seg[tid] = s;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double run = 0.0;
-    for (int t = 0; t < kThr; ++t) {
-      sh.pre[t] = run;
-      run += sh.seg[t];
-    }
-    sh.total = run;
-  }
-  __syncthreads();
-  const double total = sh.total;
-  const double thr = (double)u * total;
-  if (tid < kWave) {
-    int t0 = kThr - 1;
-    for (int t = 0; t < kThr; ++t)
-      if (sh.pre[t] + sh.seg[t] > thr) {
-        t0 = t;
-        break;
-      }
-    int pick = -1;
-    for (int t = t0; t < kThr && pick < 0; ++t) {
-      const int a0 = min(t * seg_len, V), a1 = min(a0 + seg_len, V);
-      double base = sh.pre[t];
-      for (int c0 = a0; c0 < a1 && pick < 0; c0 += kWave) {
-        const int v = c0 + lane;
-        double x = v < a1 ? w(v) : 0.0;
+// Stats pass layout: a row is cut into super-chunks of kSC = 1024 elements; wave w takes
+// super-chunks w, w + 4, ...; load j (j < 4) of a super-chunk reads its elements
+// 256 j + 4 lane .. + 3 (1 KB contiguous per load).  Each lane sums exp(x - R) over its
+// elements against one reference R per wave (the wave's first maximum, raised -- with the
+// lane sums rescaled -- only when a value exceeds it by 2^9, so the fp64 sums never
+// overflow), so no cross-lane reduction is needed until the end.  For a draft row the
+// wave also reduces each super-chunk's sum and keeps it in LDS with its reference.
+constexpr int kSC = 4 * kWC;
+constexpr float kRaise = 512.f;
+
+struct StatsSmem {
+  float wm[kWaves], wr[kWaves];
+  double ws[kWaves];
+  double red[kWaves + 1];
+  int pick[kWaves];
+};
+// Dynamic LDS of the stats kernel: the super-chunks' references (floats), then their sums.
+__host__ __device__ inline size_t stats_lds_bytes(int nsc) {
+  return (((size_t)nsc * 4 + 7) & ~(size_t)7) + (size_t)nsc * 8;
+}
+
+__device__ inline float wave_max_f(float v) {
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const double y = __shfl_up(x, o, kWave);
-          if (lane >= o) x += y;
-        }
-        const unsigned long long hit = __ballot(v < a1 && base + x > thr);
-        if (hit) pick = c0 + __ffsll((long long)hit) - 1;
-        base += __shfl(x, kWave - 1, kWave);
-      }
-    }
-    for (int c1 = V; c1 > 0 && pick < 0; c1 -= kWave) {
-      const int v = c1 - kWave + lane;
-      const unsigned long long pos = __ballot(v >= 0 && w(v) > 0.0);
-      if (pos) pick = c1 - kWave + (63 - __clzll((long long)pos));
-    }
-    if (lane == 0) sh.pick = pick < 0 ? 0 : pick;
-  }
-  __syncthreads();
-  if (total_out) *total_out = total;
-  const int r = sh.pick;
-  __syncthreads();
-  return r;
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
 }
 
-__device__ float block_max(float v, float* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int o = kThr / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
-__device__ double block_sum_fixed(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int o = kThr / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = red[tid] + red[tid + o];
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(kThr) void sampled_stats_kernel(SampledArgs a) {
-  __shared__ RowScan sh;
-  const int row = blockIdx.x;  // 0..14 draft rows, 15..30 target rows
+// At most 64 VGPRs: 8 waves per SIMD hold 8 workgroups per CU, so the 31 x 64 rows of the
+// 64-request verify run in one round on 256 CUs (at 7 per CU a second, nearly empty round
+// of 10% of the rows doubled the kernel's time).
+__global__ __launch_bounds__(kThr) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void sampled_stats_kernel(SampledArgs a) {
+  __shared__ StatsSmem sh;
+  extern __shared__ double dyn_lds[];
+  const int row = blockIdx.x;   // 0..14 draft rows, 15..30 target rows
   const int b = blockIdx.y;
-  const int V = a.vocab;
+  const int V = a.vocab, nsc = (V + kSC - 1) / kSC;
+  const bool vec = (V & 3) == 0;
   const bool is_draft = row < kDrafts;
   const float* x = is_draft ? a.draft_logits + ((long long)b * kDrafts + row) * V
                             : a.target_logits + ((long long)b * kBlock + (row - kDrafts)) * V;
-  float m = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += kThr) m = fmaxf(m, x[v]);
-  m = block_max(m, sh.red);
-  const double md = m;
-  double s = 0.0;
-  for (int v = threadIdx.x; v < V; v += kThr) s += exp((double)x[v] - md);
-  s = block_sum_fixed(s, sh.dred);
-  if (threadIdx.x == 0) {
-    a.stats[((long long)b * kRows + row) * 2 + 0] = md;
-    a.stats[((long long)b * kRows + row) * 2 + 1] = s;
+  float* sref = reinterpret_cast<float*>(dyn_lds);
+  double* ssum = reinterpret_cast<double*>(reinterpret_cast<char*>(dyn_lds) +
+                                           ((((size_t)nsc * 4) + 7) & ~(size_t)7));
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  float R = -INFINITY;   // this wave's reference (uniform)
+  float m = -INFINITY;   // this lane's maximum
+  double s = 0.0;        // this lane's sum of exp(x - R)
+  for (int sc = w; sc < nsc; sc += kWaves) {
+    f32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load4(x, sc * kSC + j * kWC + 4 * lane, V, vec);
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lm = fmaxf(lm, fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
+    m = fmaxf(m, lm);
+    if (__ballot(lm > R + kRaise)) {   // (re)set the reference: rare after the first time
+      const float Rn = wave_max_f(lm);
+      s = s * exp_from(R, neg_scaled(Rn));
+      R = Rn;
+    }
+    const double k = neg_scaled(R);
+    double p = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p += (exp_from(v[j][0], k) + exp_from(v[j][1], k)) +
+           (exp_from(v[j][2], k) + exp_from(v[j][3], k));
+    s += p;
+    if (is_draft) {
+      const double cs = wave_sum_d(p);
+      if (lane == 0) {
+        sref[sc] = R;
+        ssum[sc] = cs;
+      }
+    }
   }
-  if (is_draft) {
-    const float u = a.u_draft[(long long)b * kDrafts + row];
-    auto w = [=](int v) { return exp((double)x[v] - md); };
-    const int d = inv_cdf_row(w, V, u, sh, nullptr);
-    if (threadIdx.x == 0) a.draft_ids[(long long)b * kDrafts + row] = d;
+  {  // the wave's maximum and sum (against R), then the row's (max, sum)
+    const float wmax = wave_max_f(m);
+    const double wsum = wave_sum_d(s);
+    if (lane == 0) {
+      sh.wm[w] = wmax;
+      sh.wr[w] = R;
+      sh.ws[w] = wsum;
+    }
+  }
+  __syncthreads();
+  float M = sh.wm[0];
+  for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[i]);
+  double S = 0.0;
+  for (int i = 0; i < kWaves; ++i)
+    if (sh.wr[i] != -INFINITY) S += sh.ws[i] * exp_from(sh.wr[i], neg_scaled(M));
+  if (threadIdx.x == 0) {
+    a.stats[((long long)b * kRows + row) * 2 + 0] = (double)M;
+    a.stats[((long long)b * kRows + row) * 2 + 1] = S;
+  }
+  if (!is_draft) return;
+  // Draw the draft token: the super-chunk whose running sum crosses u * S, then its
+  // elements in order (four 256-element slices, one wave scan each).
+  const double thr = (double)a.u_draft[(long long)b * kDrafts + row] * S;
+  auto r = [&](int c) {
+    return sref[c] == -INFINITY ? 0.0 : ssum[c] * exp_from(sref[c], neg_scaled(M));
+  };
+  double before;
+  int c = block_cross(r, nsc, 0.0, thr, sh.red, sh.pick, &before);
+  const RowWeights rw{x, V, vec, M};
+  int d = -1;
+  if (c < nsc) {
+    double base = before;
+    for (int j = 0; j < 4; ++j) {
+      const int slice = c * 4 + j;
+      if (slice * kWC >= V) break;
+      double e[4];
+      rw.four(slice * kWC + 4 * lane, e);
+      const double tot = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
+      if (base + tot > thr) {   // the crossing is in this slice
+        d = wave_scan(rw, slice, base, thr);
+        break;
+      }
+      base += tot;
+    }
+  }
+  if (d < 0) {   // rounding left no crossing: the last positive weight of the row
+    for (int slice = (V + kWC - 1) / kWC - 1; slice >= 0 && d < 0; --slice)
+      d = wave_scan(rw, slice, 0.0, INFINITY);
+  }
+  if (threadIdx.x == 0) a.draft_ids[(long long)b * kDrafts + row] = d < 0 ? 0 : d;
+}
+
+// The request's accept decisions: one lane per draft, then the first rejection (15 if none).
+__device__ int first_rejection(const SampledArgs& a, int b, const double* st) {
+  const int V = a.vocab, l = threadIdx.x % kWave;
+  bool reject = false;
+  if (l < kDrafts) {
+    const int d = a.draft_ids[(long long)b * kDrafts + l];
+    const float dl = a.draft_logits[((long long)b * kDrafts + l) * V + d];
+    const float tl = a.target_logits[((long long)b * kBlock + l) * V + d];
+    const double qd = expw(dl, (float)st[2 * l]) / st[2 * l + 1];
+    const double pd = expw(tl, (float)st[2 * (kDrafts + l)]) / st[2 * (kDrafts + l) + 1];
+    reject = !((double)a.u_accept[(long long)b * kDrafts + l] * qd < pd);
+  }
+  const unsigned long long rj = __ballot(reject) | (1ull << kDrafts);
+  return __ffsll((long long)rj) - 1;
+}
+
+// The weights of the final draw for rejection index i: the residual max(0, p_i - q_i)
+// (i < 15), or p_16 (p as exp(x - m) / sum of its row).
+struct DrawRow {
+  const float* tl;
+  const float* dl;
+  float mp, mq;
+  double isp, isq;   // 1 / (sum of exp) of the target and draft rows
+  int V;
+  bool vec, residual;
+  __device__ void four(int v0, double* e) const {
+    const f32x4 t = load4(tl, v0, V, vec);
+    const f32x4 d = residual ? load4(dl, v0, V, vec) : t;
+    const double kp = neg_scaled(mp), kq = neg_scaled(mq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double p = exp_from(t[j], kp) * isp;
+      const double q = residual ? exp_from(d[j], kq) * isq : 0.0;
+      e[j] = !residual ? p : (p > q ? p - q : 0.0);
+    }
+  }
+};
+
+__device__ DrawRow draw_row(const SampledArgs& a, int b, int i, const double* st) {
+  const int V = a.vocab;
+  DrawRow r;
+  r.tl = a.target_logits + ((long long)b * kBlock + i) * V;
+  r.mp = (float)st[2 * (kDrafts + i)];
+  r.isp = 1.0 / st[2 * (kDrafts + i) + 1];
+  r.V = V;
+  r.vec = (V & 3) == 0;
+  r.residual = i < kDrafts;
+  r.dl = r.residual ? a.draft_logits + ((long long)b * kDrafts + i) * V : r.tl;
+  r.mq = r.residual ? (float)st[2 * i] : r.mp;
+  r.isq = r.residual ? 1.0 / st[2 * i + 1] : r.isp;
+  return r;
+}
+
+// Kernel 2: the chunk sums of the final draw's weights, kSegWG workgroups per request.
+__global__ __launch_bounds__(kThr) void sampled_segment_kernel(SampledArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int nwc = (a.vocab + kWC - 1) / kWC;
+  const double* st = a.stats + (long long)b * kRows * 2;
+  const int i = first_rejection(a, b, st);
+  const DrawRow dw = draw_row(a, b, i, st);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  for (int c = g * kWaves + w; c < nwc; c += kSegWG * kWaves) {
+    double e[4];
+    dw.four(c * kWC + 4 * lane, e);
+    const double cs = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
+    if (lane == 0) a.chunk_sums[(long long)b * a.chunks_ld + c] = cs;
   }
 }
 
-__global__ __launch_bounds__(kThr) void sampled_accept_kernel(SampledArgs a) {
-  __shared__ RowScan sh;
-  __shared__ int rej;
+// Kernel 3: the final draw from the chunk sums, one workgroup per request.
+__global__ __launch_bounds__(kThr) void sampled_draw_kernel(SampledArgs a) {
+  __shared__ double red[kWaves + 1];
+  __shared__ int pick[kWaves];
+  extern __shared__ double psum[];   // nwc doubles
   const int b = blockIdx.x;
-  const int V = a.vocab;
+  const int V = a.vocab, nwc = (V + kWC - 1) / kWC;
   const double* st = a.stats + (long long)b * kRows * 2;
-  if (threadIdx.x == 0) {
-    int r = kDrafts;
-    for (int i = 0; i < kDrafts; ++i) {
-      const int d = a.draft_ids[(long long)b * kDrafts + i];
-      const float* dl = a.draft_logits + ((long long)b * kDrafts + i) * V;
-      const float* tl = a.target_logits + ((long long)b * kBlock + i) * V;
-      const double qd = exp((double)dl[d] - st[2 * i]) / st[2 * i + 1];
-      const double pd = exp((double)tl[d] - st[2 * (kDrafts + i)]) / st[2 * (kDrafts + i) + 1];
-      if (!((double)a.u_accept[(long long)b * kDrafts + i] * qd < pd)) {
-        r = i;
-        break;
-      }
-    }
-    rej = r;
-  }
-  __syncthreads();
-  const int i = rej;
-  const float u = a.u_resample[b];
+  const int i = first_rejection(a, b, st);
+  DrawRow dw = draw_row(a, b, i, st);
+  const double* cs = a.chunk_sums + (long long)b * a.chunks_ld;
+  const double u = (double)a.u_resample[b];
+  auto chunk = [&](int k) { return cs[k]; };
+  double total;   // the chunk sums in a fixed order (no crossing at +inf)
+  block_cross(chunk, nwc, 0.0, INFINITY, red, pick, &total);
   int x;
-  const float* tl = a.target_logits + ((long long)b * kBlock + i) * V;
-  const double mp = st[2 * (kDrafts + i)], sp = st[2 * (kDrafts + i) + 1];
-  if (i < kDrafts) {
-    const float* dl = a.draft_logits + ((long long)b * kDrafts + i) * V;
-    const double mq = st[2 * i], sq = st[2 * i + 1];
-    auto res = [=](int v) {
-      return fmax(exp((double)tl[v] - mp) / sp - exp((double)dl[v] - mq) / sq, 0.0);
-    };
-    double total;
-    x = inv_cdf_row(res, V, u, sh, &total);
-    if (!(total > 0.0)) {
-      auto pw = [=](int v) { return exp((double)tl[v] - mp); };
-      x = inv_cdf_row(pw, V, u, sh, nullptr);
+  if (total > 0.0) {
+    double before;
+    int c = block_cross(chunk, nwc, 0.0, u * total, red, pick, &before);
+    if (c < nwc) {
+      x = wave_scan(dw, c, before, u * total);
+    } else {   // rounding left no crossing: the last positive weight of the row
+      c = nwc - 1;
+      while (c > 0 && !(cs[c] > 0.0)) --c;
+      x = wave_scan(dw, c, 0.0, INFINITY);
     }
   } else {
-    auto pw = [=](int v) { return exp((double)tl[v] - mp); };
-    x = inv_cdf_row(pw, V, u, sh, nullptr);
+    // No residual mass left (possible only by rounding): draw from p_i, whose chunk sums
+    // are formed here.
+    dw.residual = false;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    for (int c = w; c < nwc; c += kWaves) {
+      double e[4];
+      dw.four(c * kWC + 4 * lane, e);
+      const double s = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
+      if (lane == 0) psum[c] = s;
+    }
+    __syncthreads();
+    auto pc = [&](int k) { return psum[k]; };
+    double tp, before;
+    block_cross(pc, nwc, 0.0, INFINITY, red, pick, &tp);
+    int c = block_cross(pc, nwc, 0.0, u * tp, red, pick, &before);
+    if (c >= nwc) c = nwc - 1;
+    x = wave_scan(dw, c, before, u * tp);
   }
   const int t = threadIdx.x;
   if (t < kBlock) {
     int e = -1;
     if (t < i) e = a.draft_ids[(long long)b * kDrafts + t];
-    else if (t == i) e = x;
+    else if (t == i) e = x < 0 ? 0 : x;
     a.emitted[(long long)b * kBlock + t] = e;
   }
   if (t == 0) a.accept_len[b] = i + 1;
 }
 
 hipError_t launch_verify_sampled(const SampledArgs& a, int batch, hipStream_t stream) {
-  sampled_stats_kernel<<<dim3(kRows, batch), kThr, 0, stream>>>(a);
+  if (a.vocab <= 0 || a.vocab > kMaxSampledVocab) return hipErrorInvalidValue;
+  const int nwc = (a.vocab + kWC - 1) / kWC, nsc = (a.vocab + kSC - 1) / kSC;
+  sampled_stats_kernel<<<dim3(kRows, batch), kThr, stats_lds_bytes(nsc), stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sampled_accept_kernel<<<batch, kThr, 0, stream>>>(a);
+  sampled_segment_kernel<<<dim3(kSegWG, batch), kThr, 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sampled_draw_kernel<<<batch, kThr, (size_t)nwc * 8, stream>>>(a);
   return hipGetLastError();
+}
+
+size_t verify_sampled_stats_bytes(int batch, int vocab) {
+  const size_t nwc = (size_t)(vocab + kWC - 1) / kWC;
+  return (size_t)batch * (kRows * 2 + nwc) * sizeof(double);
 }
 
 }  // namespace dflash

@@ -255,7 +255,9 @@ dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, in
                              int32_t max_ctx, int32_t* ctx_lens, int32_t* anchor_ids,
                              int32_t* inject_seq, int32_t* inject_pos, hipStream_t stream);
 
-/* Workspace bytes for dflash_verify_accept_sampled. */
+/* Workspace bytes for dflash_verify_accept_sampled (0 if batch <= 0 or vocab is outside
+ * 1 .. 1048576): the rows' softmax statistics and the final draw's 256-element chunk
+ * sums, batch * (62 + ceil(vocab / 256)) doubles. */
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
 
 /* Temperature-1 verification.
@@ -267,7 +269,10 @@ size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
  * max(0, p_i - q_i) (of p_i if that is all zero) at u_resample and stop; if all 15 are
  * accepted emit the sample of p_16 at u_resample.
  *   draft_ids [batch, 15], accept_len [batch] (number of emitted tokens, 1..16),
- *   emitted [batch, 16] (-1 padded) int32 out. */
+ *   emitted [batch, 16] (-1 padded) int32 out.
+ * Weights and sums are evaluated in fp64 (exp to ~3e-13 relative), so a decision differs
+ * from an exact evaluation only when u * total lies within ~1e-12 of the mass of a
+ * cumulative boundary.  DFLASH_ERR_UNSUPPORTED if vocab > 1048576. */
 dflash_status dflash_verify_accept_sampled(const float* draft_logits,
                                            const float* target_logits, const float* u_draft,
                                            const float* u_accept, const float* u_resample,

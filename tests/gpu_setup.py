@@ -126,6 +126,11 @@ def compare_ids(gpu_ids, orc, dtype):
 # injections), so there the bound is 5e-2 while the top-1/top-2 gap must still agree
 # within the band.  (Shared cache, measured at the 8B shapes: max 2.3e-4 .. 3.4e-4, mean
 # under 4.2e-5; the bounds below keep a margin of about 6x.)
+# Temperature-1 verify: a decision is excused when the oracle's margin (distance of u * total
+# to the nearest cumulative boundary, relative to the mass; or |u q - p| relative) is at most
+# this.  Both sides evaluate the weights exp(x - max) and their sums in fp64 (the GPU's exp
+# to ~3e-13 relative), so only margins near 1e-12 can decide differently.
+SAMPLED_MARGIN = 1e-9
 LOGIT_MAX = 2e-3
 LOGIT_MEAN = 2.5e-4
 INJECTED_LOGIT_MAX = 5e-2
