@@ -37,6 +37,9 @@ def parse():
                     help="time the closed decoding loop (draft, verify, advance, inject) "
                          "against a seeded synthetic target instead of the single step")
     ap.add_argument("--kernel-reps", type=int, default=30)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra measurements of the default run (the Qwen3-8B-shaped "
+                         "step at batch 32, greedy verify alone, temperature-1 verify)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -201,23 +204,7 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     # ---------------- dominant kernel: LM head + argmax, timed alone ----------------
-    rows = Bn * 15
-    y = torch.randn((rows, cfg.hidden), device=dev, dtype=torch.float32)
-    ids_tmp = torch.empty(rows, dtype=torch.int32, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps)]
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
-        for a, b in evs:
-            a.record(s)
-            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
-            b.record(s)
-    torch.cuda.synchronize()
-    lm_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    es = 2 if cfg.dtype == "bf16" else 4
-    lm_bytes = cfg.vocab * cfg.hidden * es + rows * cfg.hidden * 4 + rows * 4
-    lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+    roofline = lm_head_roofline(dr, Bn * 15, s, args.kernel_reps, wl.name)
 
     if args.copy_mib > 0:   # a plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -239,55 +226,11 @@ def main():
                   "accept_len_gpu": int(accept.cpu()[0]),
                   "accept_len_oracle": int(ref.verify_greedy(orc["ids"], tgt_rows[0])[0])}
 
-    # Algorithmic bytes of one step (weights once, KV once, features, small activations).
-    H, F, V, I = cfg.hidden, cfg.feat_dim, cfg.vocab, cfg.intermediate
-    L, qd, kvd = cfg.n_layers, cfg.q_dim, cfg.kv_dim
-    w_layer = (qd + 2 * kvd) * H + H * qd + 2 * I * H + H * I
-    step_bytes = es * (H * F + L * 2 * kvd * H + L * w_layer + V * H)
-    step_bytes += es * Bn * n_new * F                                   # features read
-    step_bytes += es * int(sum(int(T) for T in ctx)) * L * 2 * kvd       # context K/V read
-
-    # Roofline time of the step: every kernel at the larger of its HBM time (algorithmic
-    # bytes / peak bandwidth) and its MFMA time (algorithmic flops / dense peak of the dtype),
-    # summed.  At one request every kernel is HBM-bound (this equals the HBM fraction); with a
-    # batch the GEMMs cross the ridge and the sum grows by their MFMA time.
-    peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
-
-    def roof_us(nbytes, flops):
-        return max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (peak_tf * 1e6))
-
-    R, Rn = Bn * 16, Bn * n_new
-    roof = roof_us(es * (H * F + Rn * F), 2.0 * Rn * H * F)                     # fusion
-    roof += roof_us(es * L * 2 * kvd * H, 2.0 * Rn * L * 2 * kvd * H)          # K|V injection
-    for n_out, k_in in (((qd + 2 * kvd), H), (H, qd), (2 * I, H), (H, I)):     # per layer
-        roof += L * roof_us(es * n_out * k_in, 2.0 * R * n_out * k_in)
-    keys = int(sum(int(T) + 16 for T in ctx))
-    roof += L * roof_us(es * int(sum(int(T) for T in ctx)) * 2 * kvd,         # attention
-                        4.0 * 16 * cfg.n_q_heads * cfg.head_dim * keys)
-    roof += roof_us(es * V * H, 2.0 * Bn * 15 * V * H)                        # LM head
+    acc_ = step_accounting(cfg, Bn, ctx, n_new, ms)
+    step_bytes, roof = acc_["step_bytes"], acc_["roof_us"]
     drafted = Bn * 15
     value = drafted / (ms * 1e-3)
 
-    # The LM head is HBM-bound while its rows are few (15 flop per weight byte at one
-    # request) and MFMA-bound past the ridge (peak flops / peak bytes): the roofline object
-    # takes whichever bound is the larger time.
-    lm_flops = 2.0 * V * H * rows
-    kern = ("gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>" if rows <= 64 or cfg.dtype != "bf16"
-            else "gemm_tall256<EPI_ARGMAX> (256-row blocks)")
-    roofline = {"kernel": f"shared LM head + argmax: {kern}; launch_us spans the entry "
-                          "point's three launches (rows to fragment layout, LM-head GEMM, "
-                          "argmax finalize)",
-                "launch_us": round(lm_us, 2), "bytes_per_launch": int(lm_bytes),
-                "flops_per_launch": int(lm_flops)}
-    mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
-    if lm_flops / (mfma_peak * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9):
-        tf = lm_flops / (lm_us * 1e-6) / 1e12
-        roofline.update({"bound": "mfma", "achieved": round(tf, 1), "peak": mfma_peak,
-                         "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": None})
-    else:
-        roofline.update({"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(wl.name)})
     out = {
         "metric": "drafted tokens/s (DFlash b16 draft step: inject + draft + verify)",
         "value": round(value, 1),
@@ -303,17 +246,228 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) target features, random ids)",
         "config": {"workload": wl.name, "batch": Bn, "context": int(ctx.max()),
                    "context_min": int(ctx.min()), "block": cfg.block_size,
-                   "layers": cfg.n_layers, "hidden": H, "vocab": V, "graph": graph is not None},
-        "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
+                   "graph": graph is not None},
+        "step_hbm_fraction": acc_["step_hbm_fraction"],
         "step_algorithmic_bytes": int(step_bytes),
-        "step_roofline_us": round(roof, 1),
-        "step_roofline_fraction": round(roof / (ms * 1e3), 4),
+        "step_roofline_us": acc_["step_roofline_us"],
+        "step_roofline_fraction": acc_["step_roofline_fraction"],
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s_timed": round(t_wall, 3),
     }
+    if wl.name == WORKLOADS["qwen3_b1"].name and not args.no_extra:
+        out.update(extra_measurements(args, dr, s))
     print(json.dumps(out), flush=True)
+
+
+def time_replays(fn, s, steps, warmup, graph=True):
+    """Capture fn once in a HIP graph on stream s, replay it `warmup` times, then time
+    `steps` replays between events on s.  Returns ms per replay."""
+    import torch
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    run = fn
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        run = g.replay
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(steps):
+            run()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def lm_head_roofline(dr, rows, s, reps, workload):
+    """The dominant kernel, the shared LM head + argmax, timed alone through
+    dflash_lm_head_argmax on `rows` seeded hidden rows, with HIP events on its stream.  It is
+    HBM-bound while its rows are few (15 flop per weight byte at one request) and MFMA-bound
+    past the ridge: the object takes whichever bound is the larger time."""
+    import torch
+    from block_diffusion_drafter_hidden_amd import binding as B
+    cfg, dev = dr.cfg, dr.device
+    y = torch.randn((rows, cfg.hidden), device=dev, dtype=torch.float32)
+    ids_tmp = torch.empty(rows, dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
+        for a, b in evs:
+            a.record(s)
+            B.lm_head_argmax(dr.ccfg, dr.packed, y, ids_tmp, dr.ws)
+            b.record(s)
+    torch.cuda.synchronize()
+    lm_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    es = 2 if cfg.dtype == "bf16" else 4
+    V, H = cfg.vocab, cfg.hidden
+    lm_bytes = V * H * es + rows * H * 4 + rows * 4
+    lm_flops = 2.0 * V * H * rows
+    kern = ("gemm_stream<bf16,A_HILO,1,4,EPI_ARGMAX>" if rows <= 64 or cfg.dtype != "bf16"
+            else "gemm_tall256<EPI_ARGMAX> (256-row blocks)")
+    out = {"kernel": f"shared LM head + argmax alone ({rows} rows): {kern}; launch_us spans "
+                     "the entry point's three launches (rows to fragment layout, LM-head "
+                     "GEMM, argmax finalize)",
+           "scope": "dominant kernel only; the whole step is step_hbm_fraction / "
+                    "step_roofline_fraction",
+           "launch_us": round(lm_us, 2), "bytes_per_launch": int(lm_bytes),
+           "flops_per_launch": int(lm_flops)}
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if lm_flops / (mfma_peak * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9):
+        tf = lm_flops / (lm_us * 1e-6) / 1e12
+        out.update({"bound": "mfma", "achieved": round(tf, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": None})
+    else:
+        gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+        out.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(workload)})
+    return out
+
+
+def extra_measurements(args, dr, s):
+    """The default run's other figures, as extra keys of its line: the Qwen3-8B-shaped step
+    at batch 32 (ragged contexts U[512, 8192], paged), greedy verify alone, and the
+    temperature-1 verify at 64 x 16 x 128256 fp32 logits."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_hidden_amd import binding as B
+    from workloads import WORKLOADS, synth
+
+    dev = dr.device
+    extra = {}
+    # ---------------- Qwen3-8B shape, batch 32, ragged contexts ----------------
+    wl = WORKLOADS["qwen3_b32"]
+    cfg, Bn, n_new = wl.cfg, wl.batch, wl.cfg.block_size
+    ctx = synth.context_lengths(wl)
+    log(f"[bench] {wl.name}: batch {Bn}, contexts {ctx.min()}..{ctx.max()}")
+    table, num_pages = synth.page_table(wl.name + "/bench", ctx, cfg.page_size, wl.seed)
+    d32 = dr.sibling(Bn, table.shape[1] * cfg.page_size, min(Bn * n_new, 1024))
+    cache = d32.new_cache(table, ctx, num_pages)
+    gen = torch.Generator(device=dev).manual_seed(synth.stream_seed(wl.seed, "bench/b32/fill"))
+    for pool in (cache.k_pool, cache.v_pool):   # context K/V of the injected scale (seeded)
+        pool.normal_(0.0, 3.0, generator=gen)
+    feats = torch.cat([synth.target_features(cfg, n_new, f"bench/b32/tail/b{b}", seed=wl.seed)
+                       for b in range(Bn)]).to(dev)
+    seq = torch.as_tensor(np.repeat(np.arange(Bn), n_new).astype(np.int32)).to(dev)
+    pos = torch.as_tensor(np.concatenate([np.arange(int(T) - n_new, int(T)) for T in ctx])
+                          .astype(np.int32)).to(dev)
+    anchors = torch.as_tensor(synth.anchor_ids(cfg, Bn, wl.seed)).to(dev)
+    fake = synth.uniform_ints("bench/b32/drafts", (Bn, 15), 0, cfg.vocab - 1, wl.seed)
+    target = torch.as_tensor(synth.planted_targets(fake, cfg.vocab, "bench/b32/plant",
+                                                   wl.seed)[0]).to(dev)
+    ids = torch.zeros((Bn, 15), dtype=torch.int32, device=dev)
+    acc = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    bon = torch.zeros_like(acc)
+
+    def step():
+        d32.inject(cache, feats, seq, pos)
+        d32.draft(cache, anchors, ids)
+        B.verify_accept(ids, target, acc, bon)
+
+    steps32 = max(5, args.steps // 2)
+    ms = time_replays(step, s, steps32, max(2, args.warmup // 2))
+    a32 = step_accounting(cfg, Bn, ctx, n_new, ms)
+    extra["batch32"] = {
+        "workload": wl.name, "batch": Bn, "context_min": int(ctx.min()),
+        "context_max": int(ctx.max()), "steps": steps32, "ms_per_step": round(ms, 4),
+        "drafted_tokens_per_s": round(Bn * 15 / (ms * 1e-3), 1),
+        "step_hbm_fraction": a32["step_hbm_fraction"],
+        "step_algorithmic_bytes": a32["step_bytes"],
+        "step_roofline_us": a32["step_roofline_us"],
+        "step_roofline_fraction": a32["step_roofline_fraction"],
+        "roofline": lm_head_roofline(d32, Bn * 15, s, max(5, args.kernel_reps // 3), wl.name),
+    }
+    log(f"[bench] batch 32: {ms:.4f} ms per step")
+    del cache, d32
+    torch.cuda.empty_cache()
+
+    # ---------------- greedy verify alone ----------------
+    gv = {}
+    for nb in (1, 32, 4096):
+        dd = torch.as_tensor(synth.uniform_ints(f"bench/gv/{nb}", (nb, 15), 0, 151935)).to(dev)
+        tt = torch.as_tensor(synth.planted_targets(dd.cpu().numpy(), 151936,
+                                                   f"bench/gv/plant/{nb}")[0]).to(dev)
+        aa = torch.zeros(nb, dtype=torch.int32, device=dev)
+        bb = torch.zeros_like(aa)
+        calls = 64   # per graph replay, so the replay's own launch cost is spread thin
+
+        def many():
+            for _ in range(calls):
+                B.verify_accept(dd, tt, aa, bb)
+        us = 1000.0 * time_replays(many, s, 20, 3) / calls
+        gv[f"batch{nb}"] = {"us_per_call": round(us, 2),
+                            "calls_per_s": round(1e6 / us, 1),
+                            "requests_per_s": round(nb * 1e6 / us, 1),
+                            "method": f"{calls} dependent calls per graph replay"}
+    extra["verify_greedy"] = gv
+
+    # ---------------- temperature-1 verify, 64 x 16 x 128256 ----------------
+    wl = WORKLOADS["llama_b64"]
+    dl, tl, ud, ua, ur = synth.sampled_verify_inputs(wl)
+    Bn, V = dl.shape[0], dl.shape[2]
+    t = lambda x: torch.as_tensor(x).to(dev).contiguous()
+    dl_d, tl_d, ud_d, ua_d, ur_d = t(dl), t(tl), t(ud), t(ua), t(ur)
+    del dl, tl
+    d_ids = torch.empty((Bn, 15), dtype=torch.int32, device=dev)
+    acc = torch.empty(Bn, dtype=torch.int32, device=dev)
+    emi = torch.empty((Bn, 16), dtype=torch.int32, device=dev)
+    ws = torch.empty(B.verify_sampled_workspace_size(Bn, V), dtype=torch.uint8, device=dev)
+    run = lambda: B.verify_accept_sampled(dl_d, tl_d, ud_d, ua_d, ur_d, d_ids, acc, emi, ws)
+    us = 1000.0 * time_replays(run, s, 20, 3)
+    nbytes = (Bn * 15 + Bn * 16) * V * 4    # every logit read once
+    gbs = nbytes / (us * 1e-6) / 1e9
+    extra["verify_sampled"] = {
+        "shape": f"{Bn} x (15 + 16) x {V} fp32 logits", "us_per_call": round(us, 1),
+        "requests_per_s": round(Bn * 1e6 / us, 1), "algorithmic_bytes": int(nbytes),
+        "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] temperature-1 verify: {us:.1f} us ({gbs:.0f} GB/s)")
+    return extra
+
+
+def step_accounting(cfg, Bn, ctx, n_new, ms):
+    """Algorithmic bytes of one step (weights once, context KV once, features; activations
+    are small) and its roofline time: every kernel at the larger of its HBM time (bytes /
+    peak bandwidth) and its MFMA time (flops / dense peak of the dtype), summed.  At one
+    request every kernel is HBM-bound (the roofline fraction equals the HBM fraction); with
+    a batch the GEMMs cross the ridge and the sum grows by their MFMA time."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    H, F, V, I = cfg.hidden, cfg.feat_dim, cfg.vocab, cfg.intermediate
+    L, qd, kvd = cfg.n_layers, cfg.q_dim, cfg.kv_dim
+    w_layer = (qd + 2 * kvd) * H + H * qd + 2 * I * H + H * I
+    step_bytes = es * (H * F + L * 2 * kvd * H + L * w_layer + V * H)
+    step_bytes += es * Bn * n_new * F                                   # features read
+    step_bytes += es * int(sum(int(T) for T in ctx)) * L * 2 * kvd       # context K/V read
+    peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
+
+    def roof_us(nbytes, flops):
+        return max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (peak_tf * 1e6))
+
+    R, Rn = Bn * 16, Bn * n_new
+    roof = roof_us(es * (H * F + Rn * F), 2.0 * Rn * H * F)                     # fusion
+    roof += roof_us(es * L * 2 * kvd * H, 2.0 * Rn * L * 2 * kvd * H)          # K|V injection
+    for n_out, k_in in (((qd + 2 * kvd), H), (H, qd), (2 * I, H), (H, I)):     # per layer
+        roof += L * roof_us(es * n_out * k_in, 2.0 * R * n_out * k_in)
+    keys = int(sum(int(T) + 16 for T in ctx))
+    roof += L * roof_us(es * int(sum(int(T) for T in ctx)) * 2 * kvd,         # attention
+                        4.0 * 16 * cfg.n_q_heads * cfg.head_dim * keys)
+    roof += roof_us(es * V * H, 2.0 * Bn * 15 * V * H)                        # LM head
+    return {"step_bytes": int(step_bytes), "roof_us": roof,
+            "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_roofline_us": round(roof, 1),
+            "step_roofline_fraction": round(roof / (ms * 1e3), 4)}
 
 
 def loop_bench(args, wl):

@@ -345,6 +345,17 @@ class Drafter:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         workspace_init(self.ws)
 
+    def sibling(self, max_batch: int, max_ctx: int, max_inject_rows: int = 256) -> "Drafter":
+        """Another drafter over the same packed weights with its own workspace (for a
+        different batch or context bound)."""
+        d = object.__new__(Drafter)
+        d.cfg, d.ccfg, d.device, d.packed, d.embed = (self.cfg, self.ccfg, self.device,
+                                                       self.packed, self.embed)
+        d.ws_bytes = workspace_size(self.ccfg, max_batch, max_inject_rows, max_ctx)
+        d.ws = torch.empty(d.ws_bytes, dtype=torch.uint8, device=self.device)
+        workspace_init(d.ws)
+        return d
+
     def new_cache(self, block_table, ctx_lens, num_pages: int) -> PagedCache:
         cfg = self.cfg
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

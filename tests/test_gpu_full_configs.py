@@ -185,7 +185,7 @@ def test_temperature1_verify_full_size():
     excused = 0
     for b in range(Bn):
         o = ref.verify_sampled(dl[b], tl[b], ud[b], ua[b], float(ur[b]))
-        if any(m[2] <= 1e-9 for m in o["margins"]):
+        if any(m[2] <= G.SAMPLED_MARGIN for m in o["margins"]):
             excused += 1
             continue
         np.testing.assert_array_equal(d_h[b], o["draft_ids"])
