@@ -54,6 +54,13 @@ Readings where the pages are silent:
       a - 1 accepted drafts join the context -- the target's hidden features of
       block slots 0..a-1 are injected at positions T..T+a-1 -- and the bonus
       token is the next anchor.
+  R21 the input-fusion variant [faq]: the fused feature is the drafter's input hidden
+      state at each context position (in place of a token embedding), and the context
+      rows run through the draft layers causally (row t attends to positions 0..t) before
+      the block is drafted; each layer caches the K/V of the context rows, as stored
+      values (bf16 for a bf16 drafter), and context rows attend to those stored values.
+  R22 block sizes other than 16 (8 and 32): the block is [anchor, mask x (B - 1)] at
+      positions T..T+B-1 and yields B - 1 drafts; everything else is unchanged.
 """
 from __future__ import annotations
 
@@ -164,6 +171,25 @@ def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
     return out
 
 
+def causal_attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
+    """Causal grouped-query attention over one sequence (reading R21): q, keys, vals hold
+    the same positions in order, [N, heads, d], and row t sees keys 0..t only.  Written as
+    the explicit softmax over the allowed keys; disallowed keys get no weight."""
+    N, n_q, d = q.shape
+    group = n_q // keys.shape[1]
+    allowed = np.tril(np.ones((N, N), dtype=bool))            # allowed[t, n] = n <= t
+    out = np.empty((N, n_q, d), dtype=np.float64)
+    for h in range(n_q):
+        g = h // group
+        s = q[:, h, :] @ keys[:, g, :].T / math.sqrt(d)        # [N, N]
+        s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.where(allowed, np.exp(s), 0.0)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ vals[:, g, :]
+    return out
+
+
 def embed_rows(table, ids) -> np.ndarray:
     """Rows `ids` of the embedding table, widened to float64."""
     if torch is not None and isinstance(table, torch.Tensor):
@@ -204,6 +230,43 @@ def prefill_context(cfg, weights: Dict, feats, positions=None, precision=None):
                          cfg.head_dim, cfg.rope_theta)
         ks.append(store(k, p))
         vs.append(store(v, p))
+    return ks, vs
+
+
+def prefill_input_fusion(cfg, weights: Dict, feats, precision=None):
+    """The input-fusion variant's context prefill [faq: KV injection versus input fusion],
+    for a fresh context at positions 0..T-1 (reading R21).
+
+    The fused feature c[t] = W_fuse . X[t] is the drafter's input hidden state at context
+    position t.  Every layer l takes the context rows as the block's rows are taken in
+    draft_block -- RMSNorm, Q/K/V with RoPE at position t, attention, output projection,
+    SwiGLU MLP, both residual adds -- except that attention is causal: row t attends to
+    the layer's cached K/V of positions 0..t, i.e. the stored (bf16 for a bf16 drafter)
+    values, its own included.  The result is each layer's cached K, V [T, n_kv, d]; the
+    last layer's attention and MLP feed nothing the draft step reads and are not run.
+    The draft step over this cache is draft_block, unchanged."""
+    p = precision_of(cfg, precision)
+    H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
+    T = feats.shape[0]
+    pos = np.arange(T)
+    x = fuse_features(feats, weights["w_fuse"])                    # [T, H] input rows
+    ks, vs = [], []
+    for l in range(cfg.n_layers):
+        u = rms_norm(x, weights[f"attn_norm.{l}"], cfg.rms_eps)
+        k = store(rope((u @ f64(weights[f"wk.{l}"]).T).reshape(T, nkv, d), pos,
+                       cfg.rope_theta), p)
+        v = store((u @ f64(weights[f"wv.{l}"]).T).reshape(T, nkv, d), p)
+        ks.append(k)
+        vs.append(v)
+        if l + 1 == cfg.n_layers:
+            break
+        q = rope((u @ f64(weights[f"wq.{l}"]).T).reshape(T, nq, d), pos, cfg.rope_theta)
+        o = causal_attention(q, k, v).reshape(T, nq * d)
+        x = x + o @ f64(weights[f"wo.{l}"]).T
+        u = rms_norm(x, weights[f"mlp_norm.{l}"], cfg.rms_eps)
+        g = u @ f64(weights[f"w_gate.{l}"]).T
+        up = u @ f64(weights[f"w_up.{l}"]).T
+        x = x + (silu(g) * up) @ f64(weights[f"w_down.{l}"]).T
     return ks, vs
 
 

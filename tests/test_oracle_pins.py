@@ -151,18 +151,47 @@ def test_attention_against_sdpa_and_special_cases():
 # Whole draft pass
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [0, 23])
-def test_draft_pass_matches_independent_torch_model(T):
+@pytest.mark.parametrize("T,nb", [(0, 16), (23, 16), (23, 8), (9, 32), (0, 32)])
+def test_draft_pass_matches_independent_torch_model(T, nb):
     """With zero context the step is a plain bidirectional pre-norm transformer over the
     block; with context, the injected K/V are extra keys of every layer.  Compared with an
-    independent float64 implementation built from torch library layers."""
-    cfg = SMALL
+    independent float64 implementation built from torch library layers, at block sizes 8,
+    16 and 32 (reading R22: B - 1 drafts per block)."""
+    cfg = scaled(SMALL, block_size=nb) if nb != 16 else SMALL
     w = small_model()
     ks, vs = context(cfg, w, T) if T else ([], [])
     out = ref.draft_block(cfg, w, ks, vs, anchor=17, want_logits=True)
     lib = tref.draft_logits(cfg, w, ks, vs, anchor=17).numpy()
     np.testing.assert_allclose(out["logits"], lib, rtol=1e-9, atol=1e-9)
     np.testing.assert_array_equal(out["ids"], lib.argmax(-1))
+    assert out["ids"].shape == (nb - 1,)
+
+
+def test_block_attention_with_zero_queries_is_the_mean_value():
+    """With W_q = 0 every score is 0, so each block row's attention output is the plain
+    mean of the values over all T context keys and all B block keys (no mask): a closed
+    form that fixes how many block keys the pass attends to, at B = 8, 16 and 32."""
+    for nb, T in ((8, 5), (16, 0), (32, 7)):
+        cfg = scaled(SMALL, name=f"pin-mean-{nb}", n_layers=1, block_size=nb)
+        w = dict(small_model(cfg))
+        w["wq.0"] = torch.zeros_like(w["wq.0"])
+        assert cfg.q_dim == cfg.hidden
+        w["wo.0"] = torch.eye(cfg.hidden, dtype=w["wo.0"].dtype)
+        w["w_down.0"] = torch.zeros_like(w["w_down.0"])      # layer output = x + o
+        feats = synth.target_features(cfg, T, f"mean{nb}") if T else None
+        ks, vs = ref.prefill_context(cfg, w, feats) if T else ([], [])
+        out = ref.draft_block(cfg, w, ks, vs, anchor=4, want_hidden=True)
+        x0, x1 = out["hidden"][0], out["hidden"][1]
+        # The block's own values, from the library: V = W_v RMSNorm(x0)
+        u = torch.nn.functional.rms_norm(torch.from_numpy(x0), (cfg.hidden,),
+                                         w["attn_norm.0"].double(), eps=cfg.rms_eps)
+        vb = (u @ w["wv.0"].double().T).numpy().reshape(nb, cfg.n_kv_heads, cfg.head_dim)
+        allv = np.concatenate([vs[0], vb], axis=0) if T else vb
+        mean = allv.mean(axis=0)                                  # [n_kv, d]
+        grp = cfg.n_q_heads // cfg.n_kv_heads
+        o = np.concatenate([mean[h // grp] for h in range(cfg.n_q_heads)])
+        np.testing.assert_allclose(x1 - x0, np.broadcast_to(o, x0.shape),
+                                   rtol=1e-12, atol=1e-12)
 
 
 def test_gqa_with_replicated_kv_equals_mha():
@@ -277,6 +306,131 @@ def test_inv_cdf_against_searchsorted_and_fallback():
     assert j == 1 and mg == 0.0
     j, mg = ref.inv_cdf(w, 0.5)                           # exactly on the 2|3 boundary
     assert j == 3 and mg == 0.0
+
+
+# ------------------------------------------------------------------------------------------
+# Input-fusion variant (reading R21)
+# ------------------------------------------------------------------------------------------
+
+def _fusion_case(dtype="f32", T=21, seed=4):
+    cfg = scaled(SMALL, name=f"pin-fusion-{dtype}", dtype=dtype)
+    w = synth.drafter_weights(cfg, seed=seed, std=0.2, gain_std=0.2)
+    feats = synth.target_features(cfg, T, f"fusion{T}", seed=seed)
+    return cfg, w, feats
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_input_fusion_matches_independent_torch_model(dtype):
+    """The input-fusion prefill equals an independent float64 torch model (library layers,
+    causal scaled_dot_product_attention); in bf16 mode both sides cast the cached K/V and
+    attend to the cast values.  Layer 0 is exact; later layers carry the two sides'
+    different bf16 casts (the torch side rounds through float32) in rare elements."""
+    cfg, w, feats = _fusion_case(dtype)
+    ks, vs = ref.prefill_input_fusion(cfg, w, feats)
+    tk, tv = tref.input_fusion_kv(cfg, w, feats, bf16=dtype == "bf16")
+    for l in range(cfg.n_layers):
+        for a, b in ((ks[l], tk[l].numpy()), (vs[l], tv[l].numpy())):
+            assert a.shape == (feats.shape[0], cfg.n_kv_heads, cfg.head_dim)
+            if dtype == "f32":
+                np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-10)
+            else:
+                np.testing.assert_array_equal(ref.round_bf16(a), a)
+                close = np.isclose(a, b, rtol=2 ** -7, atol=1e-9)
+                assert close.all() and (a != b).mean() < 0.01
+
+
+def test_input_fusion_is_causal():
+    """Row t's cache entries depend on context rows 0..t only: the prefill of a prefix is
+    the prefix of the prefill (every layer), and changing one row changes the later rows'
+    K/V from layer 1 on (through attention) but no earlier row's, and no other row's
+    layer-0 K/V (nothing mixes positions before the first attention)."""
+    cfg, w, feats = _fusion_case(T=19)
+    ks, vs = ref.prefill_input_fusion(cfg, w, feats)
+    for t in (1, 7, 16):
+        pk, pv = ref.prefill_input_fusion(cfg, w, feats[:t])
+        for l in range(cfg.n_layers):
+            np.testing.assert_allclose(pk[l], ks[l][:t], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(pv[l], vs[l][:t], rtol=1e-12, atol=1e-12)
+    f2 = feats.clone()
+    f2[9] = f2[9] + 1.0
+    k2, v2 = ref.prefill_input_fusion(cfg, w, f2)
+    for l in range(cfg.n_layers):
+        np.testing.assert_array_equal(k2[l][:9], ks[l][:9])
+        np.testing.assert_array_equal(v2[l][:9], vs[l][:9])
+        assert np.abs(k2[l][9] - ks[l][9]).max() > 1e-3
+        later = np.abs(v2[l][10:] - vs[l][10:]).max(axis=(1, 2))
+        if l == 0:
+            assert later.max() == 0.0
+        else:
+            assert later.min() > 1e-6
+
+
+def test_input_fusion_one_position_context():
+    """A one-position context: attention over a single key returns that key's value
+    exactly (its softmax weight is 1), so each layer is the block-free pass
+    x += W_o [v of the head's KV group] + MLP, written here with library layers; the
+    cached K/V follow from it.  This ties the layer residual structure, the head grouping
+    of the value and the norm placement to a closed form."""
+    cfg, w, feats = _fusion_case(T=1)
+    ks, vs = ref.prefill_input_fusion(cfg, w, feats)
+    F_ = torch.nn.functional
+    dbl = lambda t: t.detach().to(torch.float64)
+    x = F_.linear(dbl(feats), dbl(w["w_fuse"]))
+    grp = cfg.n_q_heads // cfg.n_kv_heads
+    for l in range(cfg.n_layers):
+        u = F_.rms_norm(x, (cfg.hidden,), dbl(w[f"attn_norm.{l}"]), eps=cfg.rms_eps)
+        k = F_.linear(u, dbl(w[f"wk.{l}"])).view(1, cfg.n_kv_heads, cfg.head_dim)
+        v = F_.linear(u, dbl(w[f"wv.{l}"])).view(1, cfg.n_kv_heads, cfg.head_dim)
+        np.testing.assert_allclose(ks[l], k.numpy(), rtol=1e-11, atol=1e-11)   # RoPE(0) = id
+        np.testing.assert_allclose(vs[l], v.numpy(), rtol=1e-11, atol=1e-11)
+        o = v.repeat_interleave(grp, dim=1).reshape(1, -1)
+        x = x + F_.linear(o, dbl(w[f"wo.{l}"]))
+        u = F_.rms_norm(x, (cfg.hidden,), dbl(w[f"mlp_norm.{l}"]), eps=cfg.rms_eps)
+        x = x + F_.linear(F_.silu(F_.linear(u, dbl(w[f"w_gate.{l}"]))) *
+                          F_.linear(u, dbl(w[f"w_up.{l}"])), dbl(w[f"w_down.{l}"]))
+
+
+def _fusion_error():
+    cfg, w, feats = _fusion_case(T=21)
+    ks, vs = ref.prefill_input_fusion(cfg, w, feats)
+    tk, tv = tref.input_fusion_kv(cfg, w, feats)
+    return max(float(np.abs(a - b.numpy()).max()) for a, b in zip(ks + vs, tk + tv))
+
+
+@pytest.mark.parametrize("mutation", ["no_mask", "mask_excludes_self", "mask_one_ahead",
+                                      "scale", "kv_group"])
+def test_input_fusion_pins_catch_planted_mistakes(monkeypatch, mutation):
+    assert _fusion_error() < 1e-9
+    orig = ref.causal_attention
+
+    def masked(allow_fn):
+        def attn(q, k, v):
+            N, n_q, d = q.shape
+            grp = n_q // k.shape[1]
+            allowed = allow_fn(N)
+            out = np.empty((N, n_q, d))
+            for h in range(n_q):
+                s = q[:, h] @ k[:, h // grp].T / math.sqrt(d)
+                s = np.where(allowed, s, -1e300)
+                p = np.where(allowed, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
+                p /= np.maximum(p.sum(axis=1, keepdims=True), 1e-300)
+                out[:, h] = p @ v[:, h // grp]
+            return out
+        return attn
+
+    if mutation == "no_mask":
+        monkeypatch.setattr(ref, "causal_attention", masked(lambda N: np.ones((N, N), bool)))
+    elif mutation == "mask_excludes_self":
+        monkeypatch.setattr(ref, "causal_attention",
+                            masked(lambda N: np.tril(np.ones((N, N), bool), -1) | (np.eye(N, dtype=bool) & (np.arange(N) == 0)[:, None])))
+    elif mutation == "mask_one_ahead":
+        monkeypatch.setattr(ref, "causal_attention", masked(lambda N: np.tril(np.ones((N, N), bool), 1)))
+    elif mutation == "scale":
+        monkeypatch.setattr(ref, "causal_attention", lambda q, k, v: orig(q * 2.0, k, v))
+    elif mutation == "kv_group":
+        monkeypatch.setattr(ref, "causal_attention",
+                            lambda q, k, v: orig(q, k[:, ::-1].copy(), v[:, ::-1].copy()))
+    assert _fusion_error() > 1e-4, mutation
 
 
 # ------------------------------------------------------------------------------------------

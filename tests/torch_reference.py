@@ -72,3 +72,30 @@ def draft_logits(cfg, weights, k_ctx, v_ctx, anchor: int) -> torch.Tensor:
         x = x + F.linear(h, _t(weights[f"w_down.{l}"]))
     y = F.rms_norm(x[1:], (cfg.hidden,), _t(weights["final_norm"]), eps=cfg.rms_eps)
     return F.linear(y, _t(weights["lm_head"]))
+
+
+def input_fusion_kv(cfg, weights, feats, bf16: bool = False):
+    """Cached K/V of every layer when the fused features are the drafter's input rows and
+    the context runs causally through the layers (positions 0..T-1).  With `bf16` the
+    cached values are cast to bf16 and the context rows attend to the cast values."""
+    T, d = feats.shape[0], cfg.head_dim
+    nq, nkv = cfg.n_q_heads, cfg.n_kv_heads
+    x = F.linear(_t(feats), _t(weights["w_fuse"]))
+    pos = torch.arange(T)
+    ks, vs = [], []
+    for l in range(cfg.n_layers):
+        u = F.rms_norm(x, (cfg.hidden,), _t(weights[f"attn_norm.{l}"]), eps=cfg.rms_eps)
+        k = _bf(rope_complex(F.linear(u, _t(weights[f"wk.{l}"])).view(T, nkv, d), pos,
+                             cfg.rope_theta), bf16)
+        v = _bf(F.linear(u, _t(weights[f"wv.{l}"])).view(T, nkv, d), bf16)
+        ks.append(k)
+        vs.append(v)
+        q = rope_complex(F.linear(u, _t(weights[f"wq.{l}"])).view(T, nq, d), pos, cfg.rope_theta)
+        kk = k.repeat_interleave(nq // nkv, dim=1).transpose(0, 1).contiguous()
+        vv = v.repeat_interleave(nq // nkv, dim=1).transpose(0, 1).contiguous()
+        o = F.scaled_dot_product_attention(q.transpose(0, 1).contiguous(), kk, vv, is_causal=True)
+        x = x + F.linear(o.transpose(0, 1).reshape(T, nq * d), _t(weights[f"wo.{l}"]))
+        u = F.rms_norm(x, (cfg.hidden,), _t(weights[f"mlp_norm.{l}"]), eps=cfg.rms_eps)
+        h = F.silu(F.linear(u, _t(weights[f"w_gate.{l}"]))) * F.linear(u, _t(weights[f"w_up.{l}"]))
+        x = x + F.linear(h, _t(weights[f"w_down.{l}"]))
+    return ks, vs
