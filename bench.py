@@ -434,7 +434,56 @@ def extra_measurements(args, dr, s):
         "requests_per_s": round(Bn * 1e6 / us, 1), "algorithmic_bytes": int(nbytes),
         "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4)}
     log(f"[bench] temperature-1 verify: {us:.1f} us ({gbs:.0f} GB/s)")
+    del dl_d, tl_d, ws
+    torch.cuda.empty_cache()
+
+    extra["prefill_2048"] = prefill_comparison(args, dr, s)
     return extra
+
+
+def prefill_comparison(args, dr, s, T=2048):
+    """Drafter prefill of a T-position context, KV injection against the input-fusion
+    variant, on the Qwen3-8B-shaped drafter (one request, a fresh cache, each as one call
+    replayed from a HIP graph).  KV injection: the fusion GEMM plus every layer's K|V
+    projection.  Input fusion: the fusion GEMM, then the context rows through the layers
+    (causal attention), the last layer only as far as its K|V."""
+    import torch
+    from workloads import WORKLOADS, synth
+
+    wl = WORKLOADS["qwen3_b1"]
+    cfg, dev = dr.cfg, dr.device
+    table, num_pages = synth.page_table(wl.name + "/prefill", [T], cfg.page_size, wl.seed)
+    d = dr.sibling(1, table.shape[1] * cfg.page_size, 1024)
+    cache = d.new_cache(table, [0], num_pages)
+    feats = synth.target_features(cfg, T, "bench/prefill", seed=wl.seed).to(dev)
+    seq = torch.zeros(T, dtype=torch.int32, device=dev)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    d.prefill_input_fusion(cache, feats, 0)       # sizes its workspace outside the graph
+    torch.cuda.synchronize()
+    reps = max(5, args.steps // 5)
+    inj_ms = time_replays(lambda: d.inject(cache, feats, seq, pos), s, reps, 2)
+    fus_ms = time_replays(lambda: d.prefill_input_fusion(cache, feats, 0), s, reps, 2)
+    H, F, L, I = cfg.hidden, cfg.feat_dim, cfg.n_layers, cfg.intermediate
+    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    kv = 2 * cfg.n_kv_heads * cfg.head_dim
+    qd = cfg.n_q_heads * cfg.head_dim
+    inj_flops = 2.0 * T * (F * H + L * kv * H)
+    layer = H * qkv + qd * H + 3 * H * I
+    attn = 2.0 * 2 * (T * (T + 1) / 2) * qd          # causal QK^T and PV
+    fus_flops = 2.0 * T * (F * H + (L - 1) * layer + H * qkv) + (L - 1) * attn
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    out = {"positions": T, "kv_injection_ms": round(inj_ms, 4),
+           "input_fusion_ms": round(fus_ms, 4),
+           "input_fusion_over_kv_injection": round(fus_ms / inj_ms, 2),
+           "kv_injection_tflops": round(inj_flops / (inj_ms * 1e-3) / 1e12, 1),
+           "input_fusion_tflops": round(fus_flops / (fus_ms * 1e-3) / 1e12, 1),
+           "mfma_peak_tflops": peak, "algorithmic_flops": {"kv_injection": int(inj_flops),
+                                                            "input_fusion": int(fus_flops)},
+           "replays": reps}
+    log(f"[bench] prefill {T}: KV injection {inj_ms:.3f} ms, input fusion {fus_ms:.3f} ms")
+    del cache, d
+    torch.cuda.empty_cache()
+    return out
 
 
 def step_accounting(cfg, Bn, ctx, n_new, ms):
@@ -587,12 +636,13 @@ def loop_bench(args, wl):
 
 
 def latency_bench(args, wl):
-    """Draft latency against drafter depth: one block pass (16 slots, 15 drafted tokens) of
-    the workload's drafter shape at batch 1 with 1, 2, 3, 5 and 8 layers, and 8 sequential
-    passes of the 1-layer drafter, each waiting for the previous one -- the cost shape of a
-    1-layer drafter that proposes one token per pass (at batch 1 a pass streams the layer and
-    LM-head weights whatever its row count, so a one-token pass costs what a block pass
-    costs).  Context K/V are seeded values (their content does not change the work)."""
+    """Draft latency against drafter depth and block size: one block pass of the workload's
+    drafter shape at batch 1 with 1, 2, 3, 5 and 8 layers and blocks of 8, 16 and 32 tokens
+    (7, 15 and 31 drafted), and 8 sequential passes of the 1-layer drafter, each waiting for
+    the previous one -- the cost shape of a 1-layer drafter that proposes one token per pass.
+    Those passes are 16-row passes: at batch 1 a pass streams the layer and LM-head weights
+    whatever its row count, which the LM head timed alone at 1 and at 16 rows shows.
+    Context K/V are seeded values (their content does not change the work)."""
     import torch
 
     from block_diffusion_drafter_hidden_amd import Drafter
@@ -630,7 +680,9 @@ def latency_bench(args, wl):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    rows, ar_ms = [], None
+    from block_diffusion_drafter_hidden_amd import binding as B
+
+    rows, ar_ms, lm_rows = [], None, {}
     for L in depths:
         cfg = scaled(wl.cfg, n_layers=L)
         keep = set(cfg.weight_shapes())
@@ -642,29 +694,41 @@ def latency_bench(args, wl):
         gen = torch.Generator(device=dev).manual_seed(synth.stream_seed(wl.seed, "latency/fill"))
         for pool in (cache.k_pool, cache.v_pool):
             pool.normal_(0.0, 3.0, generator=gen)
-        ms = timed(lambda: dr.draft(cache, anchors, ids), args.steps)
-        rows.append({"layers": L, "ms_per_block": round(ms, 4),
-                     "drafted_tokens_per_ms": round(15.0 / ms, 2)})
-        log(f"[latency] {L} layers: {ms:.4f} ms per 16-slot pass")
+        for nb in (8, 16, 32):
+            d = dr if nb == cfg.block_size else dr.sibling(
+                1, table.shape[1] * cfg.page_size, 256, block_size=nb)
+            ids_nb = torch.zeros((1, nb - 1), dtype=torch.int32, device=dev)
+            ms = timed(lambda: d.draft(cache, anchors, ids_nb), args.steps)
+            rows.append({"layers": L, "block": nb, "ms_per_block": round(ms, 4),
+                         "drafted_tokens_per_ms": round((nb - 1) / ms, 2)})
+            log(f"[latency] {L} layers, block {nb}: {ms:.4f} ms per pass")
         if L == 1:
             def ar8():
                 for _ in range(8):
                     dr.draft(cache, anchors, ids)
             ar_ms = timed(ar8, max(args.steps // 4, 5))
             log(f"[latency] 1 layer, 8 sequential passes: {ar_ms:.4f} ms")
+            for r in (1, 16):   # the LM head alone at 1 and 16 rows
+                y = torch.randn((r, cfg.hidden), device=dev, dtype=torch.float32)
+                o = torch.empty(r, dtype=torch.int32, device=dev)
+                lm_rows[f"lm_head_{r}_rows_ms"] = round(
+                    timed(lambda: B.lm_head_argmax(dr.ccfg, dr.packed, y, o, dr.ws),
+                          args.steps), 4)
         del dr, cache
         torch.cuda.empty_cache()
-    five = next(r["ms_per_block"] for r in rows if r["layers"] == 5)
+    five = next(r["ms_per_block"] for r in rows if r["layers"] == 5 and r["block"] == 16)
     out = {
-        "metric": "draft latency: one 16-slot block pass by drafter depth vs 8 sequential "
-                  "1-layer passes (batch 1)",
-        "value": round(five, 4), "unit": "ms per block (5 layers)", "n_gpus": 1,
+        "metric": "draft latency: one block pass by drafter depth and block size vs 8 "
+                  "sequential 1-layer passes (batch 1)",
+        "value": round(five, 4), "unit": "ms per block (5 layers, 16 tokens)", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
         "dtype": wl.cfg.dtype, "data": "synthetic (seeded weights, seeded context K/V)",
-        "config": {"workload": f"{wl.cfg.name}-batch1-ctx{T}-depth-sweep", "context": T},
+        "config": {"workload": f"{wl.cfg.name}-batch1-ctx{T}-depth-block-sweep",
+                   "context": T},
         "rows": rows,
         "one_layer_8_sequential_passes_ms": round(ar_ms, 4),
-        "five_layer_block_vs_8_sequential_1_layer": round(five / ar_ms, 3),
+        "five_layer_block16_vs_8_sequential_1_layer": round(five / ar_ms, 3),
+        **lm_rows,
     }
     print(json.dumps(out), flush=True)
 

@@ -27,7 +27,7 @@ EXPORTS = (
     "dflash_lm_head_argmax",
     "dflash_verify_accept", "dflash_advance", "dflash_verify_sampled_workspace_size",
     "dflash_verify_accept_sampled", "dflash_error_string", "dflash_noalloc_scratch_bytes",
-    "dflash_draft_block_noalloc",
+    "dflash_draft_block_noalloc", "dflash_prefill_workspace_size", "dflash_prefill_input_fusion",
 )
 
 
@@ -81,13 +81,15 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dflash_fuse_inject_kv": (S, [P, P, P, P, P, P, I32, P, SZ, P]),
         "dflash_draft_block": (S, [P, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "dflash_lm_head_argmax": (S, [P, P, P, I32, P, P, P, SZ, P]),
-        "dflash_verify_accept": (S, [P, P, I32, P, P, P, P]),
-        "dflash_advance": (S, [P, P, I32, I32, P, P, P, P, P]),
+        "dflash_verify_accept": (S, [P, P, I32, I32, P, P, P, P]),
+        "dflash_advance": (S, [P, P, I32, I32, I32, P, P, P, P, P]),
         "dflash_verify_sampled_workspace_size": (SZ, [I32, I32]),
         "dflash_verify_accept_sampled": (S, [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "dflash_error_string": (C.c_char_p, [S]),
         "dflash_noalloc_scratch_bytes": (SZ, []),
         "dflash_draft_block_noalloc": (S, [P, P, P, P, P, I32, P, P, P, P]),
+        "dflash_prefill_workspace_size": (SZ, [P, I32, I32]),
+        "dflash_prefill_input_fusion": (S, [P, P, P, P, I32, I32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -217,9 +219,10 @@ def draft_block(ccfg: Config, packed, embed, cache: KVCache, anchor_ids, draft_i
     _arg(packed, "packed", torch.uint8, (None,), dev)
     _arg(embed, "embed", _model_dtype(ccfg), (ccfg.vocab, ccfg.hidden), dev)
     batch = int(_arg(anchor_ids, "anchor_ids", torch.int32, (None,), dev).shape[0])
-    _arg(draft_ids, "draft_ids", torch.int32, (batch, 15), dev)
-    _arg(logits_out, "logits_out", torch.float32, (batch, 15, ccfg.vocab), dev, optional=True)
-    _arg(top2_gap, "top2_gap", torch.float32, (batch, 15), dev, optional=True)
+    nd = ccfg.block_size - 1
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, nd), dev)
+    _arg(logits_out, "logits_out", torch.float32, (batch, nd, ccfg.vocab), dev, optional=True)
+    _arg(top2_gap, "top2_gap", torch.float32, (batch, nd), dev, optional=True)
     _check(load_library().dflash_draft_block(
         C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
         _ptr(draft_ids), _ptr(top2_gap), _ptr(logits_out), _ptr(ws), _nbytes(ws),
@@ -236,9 +239,10 @@ def draft_block_noalloc(ccfg: Config, packed, embed, cache: KVCache, anchor_ids,
     dev = _arg(packed, "packed", torch.uint8, (None,)).device
     _arg(embed, "embed", _model_dtype(ccfg), (ccfg.vocab, ccfg.hidden), dev)
     batch = int(_arg(anchor_ids, "anchor_ids", torch.int32, (None,), dev).shape[0])
-    _arg(draft_ids, "draft_ids", torch.int32, (batch, 15), dev)
-    _arg(logits_out, "logits_out", torch.float32, (batch, 15, ccfg.vocab), dev, optional=True)
-    _arg(top2_gap, "top2_gap", torch.float32, (batch, 15), dev, optional=True)
+    nd = ccfg.block_size - 1
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, nd), dev)
+    _arg(logits_out, "logits_out", torch.float32, (batch, nd, ccfg.vocab), dev, optional=True)
+    _arg(top2_gap, "top2_gap", torch.float32, (batch, nd), dev, optional=True)
     _check(load_library().dflash_draft_block_noalloc(
         C.byref(ccfg), _ptr(packed), _ptr(embed), C.byref(cache), _ptr(anchor_ids), batch,
         _ptr(draft_ids), _ptr(top2_gap), _ptr(logits_out), _stream(stream)),
@@ -257,29 +261,46 @@ def lm_head_argmax(ccfg: Config, packed, y, ids_out, ws, logits_out=None, stream
 
 
 def verify_accept(draft_ids, target_ids, accept_len, bonus, emitted=None, stream=None) -> None:
-    batch = int(_arg(draft_ids, "draft_ids", torch.int32, (None, 15)).shape[0])
-    dev = draft_ids.device
-    _arg(target_ids, "target_ids", torch.int32, (batch, 16), dev)
+    """Greedy verify; the block size B is taken from target_ids [batch, B]."""
+    batch, nb = _arg(target_ids, "target_ids", torch.int32, (None, None)).shape
+    dev = target_ids.device
+    _arg(draft_ids, "draft_ids", torch.int32, (batch, nb - 1), dev)
     _arg(accept_len, "accept_len", torch.int32, (batch,), dev)
     _arg(bonus, "bonus", torch.int32, (batch,), dev)
-    _arg(emitted, "emitted", torch.int32, (batch, 16), dev, optional=True)
+    _arg(emitted, "emitted", torch.int32, (batch, nb), dev, optional=True)
     _check(load_library().dflash_verify_accept(
-        _ptr(draft_ids), _ptr(target_ids), batch, _ptr(accept_len), _ptr(bonus),
+        _ptr(draft_ids), _ptr(target_ids), int(batch), int(nb), _ptr(accept_len), _ptr(bonus),
         _ptr(emitted), _stream(stream)), "dflash_verify_accept")
 
 
 def advance(accept_len, bonus, max_ctx: int, ctx_lens, anchor_ids, inject_seq, inject_pos,
-            stream=None) -> None:
+            stream=None, block_size: int = 16) -> None:
     batch = int(_arg(accept_len, "accept_len", torch.int32, (None,)).shape[0])
     dev = accept_len.device
     for name, t, shp in (("bonus", bonus, (batch,)), ("ctx_lens", ctx_lens, (batch,)),
                          ("anchor_ids", anchor_ids, (batch,)),
-                         ("inject_seq", inject_seq, (batch * 16,)),
-                         ("inject_pos", inject_pos, (batch * 16,))):
+                         ("inject_seq", inject_seq, (batch * block_size,)),
+                         ("inject_pos", inject_pos, (batch * block_size,))):
         _arg(t, name, torch.int32, shp, dev)
     _check(load_library().dflash_advance(
-        _ptr(accept_len), _ptr(bonus), batch, int(max_ctx), _ptr(ctx_lens), _ptr(anchor_ids),
-        _ptr(inject_seq), _ptr(inject_pos), _stream(stream)), "dflash_advance")
+        _ptr(accept_len), _ptr(bonus), batch, int(block_size), int(max_ctx), _ptr(ctx_lens),
+        _ptr(anchor_ids), _ptr(inject_seq), _ptr(inject_pos), _stream(stream)),
+        "dflash_advance")
+
+
+def prefill_workspace_size(ccfg: Config, max_tok: int, max_ctx: int) -> int:
+    return int(load_library().dflash_prefill_workspace_size(C.byref(ccfg), max_tok, max_ctx))
+
+
+def prefill_input_fusion(ccfg: Config, packed, cache: KVCache, feats, seq: int, ws,
+                         stream=None) -> None:
+    """dflash_prefill_input_fusion: request `seq`'s next feats.shape[0] context rows."""
+    dev = _arg(ws, "ws", torch.uint8, (None,)).device
+    _arg(packed, "packed", torch.uint8, (None,), dev)
+    n_tok = int(_arg(feats, "feats", _model_dtype(ccfg), (None, ccfg.feat_dim), dev).shape[0])
+    _check(load_library().dflash_prefill_input_fusion(
+        C.byref(ccfg), _ptr(packed), C.byref(cache), _ptr(feats), int(seq), n_tok, _ptr(ws),
+        _nbytes(ws), _stream(stream)), "dflash_prefill_input_fusion")
 
 
 def verify_sampled_workspace_size(batch: int, vocab: int) -> int:
@@ -345,12 +366,18 @@ class Drafter:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         workspace_init(self.ws)
 
-    def sibling(self, max_batch: int, max_ctx: int, max_inject_rows: int = 256) -> "Drafter":
+    def sibling(self, max_batch: int, max_ctx: int, max_inject_rows: int = 256,
+                block_size: Optional[int] = None) -> "Drafter":
         """Another drafter over the same packed weights with its own workspace (for a
-        different batch or context bound)."""
+        different batch or context bound, or another block size: the packed weights do not
+        depend on it)."""
         d = object.__new__(Drafter)
         d.cfg, d.ccfg, d.device, d.packed, d.embed = (self.cfg, self.ccfg, self.device,
                                                        self.packed, self.embed)
+        if block_size is not None and block_size != self.cfg.block_size:
+            from dataclasses import replace
+            d.cfg = replace(self.cfg, block_size=block_size)
+            d.ccfg = make_config(d.cfg)
         d.ws_bytes = workspace_size(self.ccfg, max_batch, max_inject_rows, max_ctx)
         d.ws = torch.empty(d.ws_bytes, dtype=torch.uint8, device=self.device)
         workspace_init(d.ws)
@@ -378,4 +405,17 @@ class Drafter:
     def advance(self, cache: PagedCache, accept_len, bonus, anchor_ids, inject_seq,
                 inject_pos, stream=None) -> None:
         advance(accept_len, bonus, cache.max_pages * self.cfg.page_size, cache.ctx_lens,
-                anchor_ids, inject_seq, inject_pos, stream)
+                anchor_ids, inject_seq, inject_pos, stream, block_size=self.cfg.block_size)
+
+    def prefill_input_fusion(self, cache: PagedCache, feats, seq: int, ws=None,
+                             stream=None) -> None:
+        """Input-fusion context prefill of request `seq` (see dflash_prefill_input_fusion);
+        `ws` defaults to a workspace sized for feats on first use."""
+        if ws is None:
+            need = prefill_workspace_size(self.ccfg, int(feats.shape[0]),
+                                          cache.max_pages * self.cfg.page_size)
+            if getattr(self, "_pf_ws", None) is None or self._pf_ws.numel() < need:
+                self._pf_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                workspace_init(self._pf_ws)
+            ws = self._pf_ws
+        prefill_input_fusion(self.ccfg, self.packed, cache.c(), feats, seq, ws, stream)

@@ -10,6 +10,7 @@
 
 #include "dflash.h"
 #include "attention.h"
+#include "common.h"
 #include "gemm.h"
 #include "sampled.h"
 #include "small.h"
@@ -39,6 +40,8 @@ struct Dims {
   int ktile;   // K per k-tile
   float theta, eps;
   int mask;
+  int nb;      // block size: 8, 16 or 32
+  int rpr;     // rows per request of a draft pass: max(nb, 16)
 };
 
 dflash_status check_config(const dflash_config* c, Dims* o) {
@@ -46,7 +49,8 @@ dflash_status check_config(const dflash_config* c, Dims* o) {
   if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
       c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0 || c->feat_dim <= 0)
     return DFLASH_ERR_INVALID_ARG;
-  if (c->block_size != 16 || c->page_size != 16) return DFLASH_ERR_UNSUPPORTED;
+  if ((c->block_size != 8 && c->block_size != 16 && c->block_size != 32) || c->page_size != 16)
+    return DFLASH_ERR_UNSUPPORTED;
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
   if (c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_INVALID_ARG;
   if (c->hidden % 64 || c->feat_dim % 64 || c->intermediate % 64 || c->vocab % 64)
@@ -73,6 +77,8 @@ dflash_status check_config(const dflash_config* c, Dims* o) {
     o->theta = c->rope_theta;
     o->eps = c->rms_eps;
     o->mask = c->mask_token_id;
+    o->nb = c->block_size;
+    o->rpr = std::max(c->block_size, kQRows);
   }
   return DFLASH_OK;
 }
@@ -263,7 +269,8 @@ int ksplit_count(const Plan& pl, int n_tiles, int KT, int min_wgs, int max_s = 8
 
 DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   DraftPlan p{};
-  const int rows = B * 16;
+  const int rows = B * m.rpr;
+  const int tiles = rows / kQRows;
   const bool tall = m.bf16 != 0;
   p.qkv = plan_gemm((m.nq + 2 * m.nkv) * m.d / 16, m.H / m.ktile, rows, 2, 1, 16, tall);
   p.o = plan_gemm(m.H / 16, m.nq * m.d / m.ktile, rows, 1, 1, 16, tall);
@@ -276,7 +283,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   // 512 rows were slower than two).
   if (p.o.mt == kTallMT) p.o.ksub = ksplit_count(p.o, m.H / 16, m.nq * m.d / m.ktile, 512, 2);
   if (p.dn.mt == kTallMT) p.dn.ksub = ksplit_count(p.dn, m.H / 16, m.I / m.ktile, 512, 2);
-  const int kv_groups = B * m.nkv;
+  const int kv_groups = tiles * m.nkv;
   const int max_chunks = std::max(1, cdiv(std::max(max_ctx, 1), 32));
   // Context chunks per (request, KV group): enough workgroups to fill the chip at small
   // batch; otherwise the longest chunks the kernel takes (4096 keys), which minimize the
@@ -333,6 +340,52 @@ InjectPlan inject_plan(const Dims& m, int rows) {
 
 constexpr int kInjectChunkRows = 1024;   // rows per fusion + injection launch pair, at most
 
+// The input-fusion prefill: context rows pass through the layers in chunks of at most
+// kPrefillChunkRows rows, each chunk as kPrefillChunkRows / 16 groups of 16 rows that the
+// draft pass's kernels take as "requests" (rows padded to a multiple of 16).
+constexpr int kPrefillChunkRows = 2048;
+
+struct PrefillPlan {
+  DraftPlan dp;     // layer buffers for rows / 16 groups of 16 rows
+  size_t fpart;     // k-split partials of the fusion GEMM (the largest any chunk needs)
+  size_t gctx;      // [groups] cached context of each group
+  size_t total;
+};
+
+// The layer plan of a prefill chunk of `groups` 16-row groups.
+DraftPlan prefill_layer_plan(const Dims& m, int groups, int max_ctx) {
+  Dims g = m;
+  g.rpr = kQRows;   // one 16-row group per "request"
+  g.nb = kQRows;
+  return draft_plan(g, groups, max_ctx);
+}
+
+Plan prefill_fuse_plan(const Dims& m, int rows) {
+  Plan pl = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
+  if (pl.mt == kTallMT) pl.ksub = ksplit_count(pl, m.H / 16, m.F / m.ktile, 512);
+  return pl;
+}
+
+// rows: padded rows of the largest chunk (a multiple of 16, at most kPrefillChunkRows).
+PrefillPlan prefill_plan(const Dims& m, int rows, int max_ctx) {
+  PrefillPlan p{};
+  p.dp = prefill_layer_plan(m, rows / kQRows, max_ctx);
+  // A shorter (last) chunk can take more k-slices than a full one: the layer buffers and
+  // the fusion partials are sized for the largest need of any chunk length.
+  size_t layers = p.dp.total, part = 0;
+  for (int r = 16; r <= rows; r += 16) {
+    layers = std::max(layers, prefill_layer_plan(m, r / kQRows, max_ctx).total);
+    const Plan pl = prefill_fuse_plan(m, r);
+    const int splits = pl.mt == kTallMT ? pl.ksub : 1;
+    if (splits > 1) part = std::max(part, (size_t)splits * r * m.H * 4);
+  }
+  Carver c(layers);
+  p.fpart = c.take(part);
+  p.gctx = c.take((size_t)(rows / kQRows) * 4);
+  p.total = c.off;
+  return p;
+}
+
 #define DF_TRY(expr)                                  \
   do {                                                \
     hipError_t _e = (expr);                           \
@@ -344,9 +397,10 @@ constexpr int kInjectChunkRows = 1024;   // rows per fusion + injection launch p
 // ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
 // keys: workspace for the per-column-block argmax partials, 2 * lm_keys_bytes(m, rows)
 // bytes (best keys, then runner-up keys, which are only written when gap_out is set).
+// draft: the rows are draft blocks (m.rpr rows per request, ids of slots 1 .. m.nb - 1).
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* xg,
                              const float* ssq, int ssq_parts, int ssq_ld, int rows,
-                             bool draft_rows, int* ids_out, float* gap_out, float* logits_out,
+                             bool draft, int* ids_out, float* gap_out, float* logits_out,
                              unsigned long long* keys, hipStream_t stream) {
   const Plan pl = lm_plan(m, rows);
   const int parts = argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw);
@@ -366,10 +420,11 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   // request, same box; the other GEMMs measured slower this way).
   g.kinter = 1;
   g.ldo = m.V;
-  g.draft_rows = draft_rows ? 1 : 0;
+  g.draft_rpr = draft ? m.rpr : 0;
+  g.draft_nb = m.nb;
   DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
   DF_TRY(launch_argmax_finalize(keys, g.keys2, parts, rows, ids_out, gap_out, rows,
-                                draft_rows ? 1 : 0, stream));
+                                g.draft_rpr, g.draft_nb, stream));
   return DFLASH_OK;
 }
 
@@ -556,6 +611,172 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
   return DFLASH_OK;
 }
 
+size_t dflash_prefill_workspace_size(const dflash_config* cfg, int32_t max_tok,
+                                     int32_t max_ctx) {
+  Dims m;
+  if (check_config(cfg, &m) != DFLASH_OK) return 0;
+  if (max_tok < 0 || max_ctx < 0) return 0;
+  const int rows = std::min(cdiv(std::max(max_tok, 1), 16) * 16, kPrefillChunkRows);
+  return prefill_plan(m, rows, max_ctx).total;
+}
+
+dflash_status dflash_prefill_input_fusion(const dflash_config* cfg, const void* packed,
+                                          const dflash_kv_cache* cache, const void* feats,
+                                          int32_t seq, int32_t n_tok, void* workspace,
+                                          size_t ws_bytes, hipStream_t stream) {
+  Dims m;
+  dflash_status st = check_config(cfg, &m);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  if (!packed || !workspace || n_tok < 0 || seq < 0) return DFLASH_ERR_INVALID_ARG;
+  if (n_tok == 0) return DFLASH_OK;
+  if (!feats) return DFLASH_ERR_INVALID_ARG;
+  if (cache->max_pages_per_seq > kMaxPagesPerSeq) return DFLASH_ERR_UNSUPPORTED;
+  const int max_ctx = cache->max_pages_per_seq * 16;
+  if (n_tok > max_ctx) return DFLASH_ERR_INVALID_ARG;
+  const int chunk_rows = std::min(cdiv(n_tok, 16) * 16, kPrefillChunkRows);
+  const PrefillPlan pp = prefill_plan(m, chunk_rows, max_ctx);
+  if (ws_bytes < pp.total) return DFLASH_ERR_WORKSPACE;
+  const DraftPlan& dp = pp.dp;
+
+  const Packed P = packed_layout(m);
+  const char* wb = reinterpret_cast<const char*>(packed);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* x = reinterpret_cast<float*>(ws + dp.x);
+  float* xg = reinterpret_cast<float*>(ws + dp.xg);
+  float* ssq = reinterpret_cast<float*>(ws + dp.ssq);
+  int* gctx = reinterpret_cast<int*>(ws + pp.gctx);
+  const int32_t* table_row = cache->block_table + (size_t)seq * cache->max_pages_per_seq;
+  const long long pool_layer = (long long)cache->num_pages * m.nkv * 16 * m.d;
+
+  for (int r0 = 0; r0 < n_tok; r0 += kPrefillChunkRows) {
+    const int nv = std::min(kPrefillChunkRows, n_tok - r0);
+    const int rows = cdiv(nv, 16) * 16, groups = rows / kQRows;
+    // The plans of a shorter last chunk (same kernels, fewer m-blocks).
+    const DraftPlan cp = rows == chunk_rows ? dp : prefill_layer_plan(m, groups, max_ctx);
+    const int o_parts = residual_ssq_parts(cp.o, m.H / 16);
+    const int dn_parts = residual_ssq_parts(cp.dn, m.H / 16);
+    DF_TRY(launch_prefill_groups(cache->ctx_lens, seq, r0, groups, gctx, stream));
+    {  // the fused features are the input rows: x = W_fuse . X
+      const Plan fp = prefill_fuse_plan(m, nv);
+      GemmParams g = base_params(fp, wb + P.w_fuse, 0, m.F / m.ktile,
+                                 reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
+                                 m.F, nv, m.H / 16);
+      g.a_kind = m.bf16 ? A_ROW_BF16 : A_ROW_F32;
+      g.out = x;
+      g.ldo = m.H;
+      g.ksplit = fp.mt == kTallMT ? fp.ksub : 1;
+      g.partial = reinterpret_cast<float*>(ws + pp.fpart);
+      DF_TRY(launch_gemm(m.bf16, fp.mt, fp.npw, EPI_STORE, g, 1, stream));
+    }
+    DF_TRY(launch_prefill_rows(m.bf16, x, rows, nv, m.H,
+                               reinterpret_cast<const float*>(wb + P.layer0 + P.attn_norm), xg,
+                               ssq, stream));
+    for (int l = 0; l < m.L; ++l) {
+      const char* lb = wb + P.layer0 + (size_t)l * P.layer_stride;
+      {  // RMSNorm + Q|K|V + RoPE; K/V of the valid rows into the cache (stored values)
+        GemmParams g = base_params(cp.qkv, lb + P.wqkv, 0, m.H / m.ktile, xg, m.H, rows,
+                                   (m.nq + 2 * m.nkv) * m.d / 16);
+        g.a_kind = act_kind(m);
+        g.norm = 1;
+        g.ssq_in = ssq;
+        g.ssq_parts = l == 0 ? 1 : dn_parts;
+        g.ssq_ld = rows;
+        g.eps = m.eps;
+        g.q_out = reinterpret_cast<float*>(ws + cp.q);
+        g.bk_out = reinterpret_cast<float*>(ws + cp.bk);
+        g.bv_out = reinterpret_cast<float*>(ws + cp.bv);
+        g.ctx_lens = gctx;
+        g.rpr = kQRows;
+        g.n_q = m.nq;
+        g.n_kv = m.nkv;
+        g.head_dim = m.d;
+        set_rope(m, g);
+        g.k_pool = reinterpret_cast<char*>(cache->k_pool) + (size_t)l * pool_layer * m.es;
+        g.v_pool = reinterpret_cast<char*>(cache->v_pool) + (size_t)l * pool_layer * m.es;
+        g.block_table = table_row;
+        g.max_pages = cache->max_pages_per_seq;
+        g.kv_rows = nv;
+        g.ksplit = cp.qkv.mt == kTallMT ? cp.qkv.ksub : 1;
+        g.partial = reinterpret_cast<float*>(ws + cp.kpart);
+        DF_TRY(launch_gemm(m.bf16, cp.qkv.mt, cp.qkv.npw, EPI_QKV, g, 1, stream));
+      }
+      // The last layer's attention and MLP of the context rows feed nothing the draft reads.
+      if (l + 1 == m.L) break;
+      {  // causal attention: group g sees the cache up to its first row, then its own rows
+        AttnArgs a{};
+        a.q = reinterpret_cast<const float*>(ws + cp.q);
+        a.bk = reinterpret_cast<const float*>(ws + cp.bk);
+        a.bv = reinterpret_cast<const float*>(ws + cp.bv);
+        a.k_pool = reinterpret_cast<const char*>(cache->k_pool) + (size_t)l * pool_layer * m.es;
+        a.v_pool = reinterpret_cast<const char*>(cache->v_pool) + (size_t)l * pool_layer * m.es;
+        a.block_table = table_row;
+        a.table_ld = 0;
+        a.max_pages = cache->max_pages_per_seq;
+        a.ctx_lens = gctx;
+        a.rpr = kQRows;
+        a.nbk = kQRows;
+        a.causal = 1;
+        a.n_q = m.nq;
+        a.n_kv = m.nkv;
+        a.head_dim = m.d;
+        a.nc = cp.nc;
+        a.chunk = cp.chunk;
+        a.scale = 1.0f / std::sqrt((float)m.d);
+        a.part_o = reinterpret_cast<float*>(ws + cp.apart_o);
+        a.part_ml = reinterpret_cast<float*>(ws + cp.apart_ml);
+        a.out = ws + cp.ao;
+        a.out_hilo = m.bf16;
+        DF_TRY(launch_block_attention(m.bf16, a, groups, stream));
+      }
+      {  // output projection + residual
+        GemmParams g = base_params(cp.o, lb + P.wo, 0, m.nq * m.d / m.ktile, ws + cp.ao,
+                                   m.nq * m.d, rows, m.H / 16);
+        g.a_kind = act_kind(m);
+        g.out = x;
+        g.ldo = m.H;
+        g.xg_out = xg;
+        g.gamma_next = reinterpret_cast<const float*>(lb + P.mlp_norm);
+        g.ssq_out = ssq;
+        g.ssq_ld = rows;
+        g.ksplit = cp.o.mt == kTallMT ? cp.o.ksub : 1;
+        g.partial = reinterpret_cast<float*>(ws + cp.kpart);
+        DF_TRY(launch_gemm(m.bf16, cp.o.mt, cp.o.npw, EPI_RESIDUAL, g, 1, stream));
+      }
+      {  // RMSNorm + gate|up + SiLU * up
+        GemmParams g = base_params(cp.gu, lb + P.wgu, 0, m.H / m.ktile, xg, m.H, rows,
+                                   2 * m.I / 16);
+        g.a_kind = act_kind(m);
+        g.norm = 1;
+        g.ssq_in = ssq;
+        g.ssq_parts = o_parts;
+        g.ssq_ld = rows;
+        g.eps = m.eps;
+        g.out = ws + cp.h;
+        g.ldo = m.I;
+        DF_TRY(launch_gemm(m.bf16, cp.gu.mt, cp.gu.npw, EPI_SWIGLU, g, 1, stream));
+      }
+      {  // down projection + residual; x * gain of the next layer's attention norm
+        GemmParams g = base_params(cp.dn, lb + P.wd, 0, m.I / m.ktile, ws + cp.h, m.I, rows,
+                                   m.H / 16);
+        g.a_kind = act_kind(m);
+        g.out = x;
+        g.ldo = m.H;
+        g.xg_out = xg;
+        g.gamma_next = reinterpret_cast<const float*>(wb + P.layer0 +
+                                                      (size_t)(l + 1) * P.layer_stride +
+                                                      P.attn_norm);
+        g.ssq_out = ssq;
+        g.ssq_ld = rows;
+        g.ksplit = cp.dn.mt == kTallMT ? cp.dn.ksub : 1;
+        g.partial = reinterpret_cast<float*>(ws + cp.kpart);
+        DF_TRY(launch_gemm(m.bf16, cp.dn.mt, cp.dn.npw, EPI_RESIDUAL, g, 1, stream));
+      }
+    }
+  }
+  return DFLASH_OK;
+}
+
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
@@ -567,7 +788,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
   if (!packed || !embed || !anchor_ids || !draft_ids || !workspace || batch <= 0)
     return DFLASH_ERR_INVALID_ARG;
-  if (batch > kMaxBatch || cache->max_pages_per_seq > kMaxPagesPerSeq)
+  if ((long long)batch * m.rpr > kMaxBatch * 16 || cache->max_pages_per_seq > kMaxPagesPerSeq)
     return DFLASH_ERR_UNSUPPORTED;
   const int max_ctx = cache->max_pages_per_seq * 16;
   const DraftPlan dp = draft_plan(m, batch, max_ctx);
@@ -579,7 +800,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
   float* x = reinterpret_cast<float*>(ws + dp.x);
   float* xg = reinterpret_cast<float*>(ws + dp.xg);
   float* ssq = reinterpret_cast<float*>(ws + dp.ssq);
-  const int rows = batch * 16;
+  const int rows = batch * m.rpr;
   // Partial sums of squares per row left by the O projection (read by gate|up) and by the
   // down projection (read by the next Q|K|V and the LM head).
   const int o_parts = residual_ssq_parts(dp.o, m.H / 16);
@@ -592,6 +813,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
     e.mask_id = m.mask;
     e.embed = embed;
     e.hidden = m.H;
+    e.rpr = m.rpr;
     e.x = x;
     e.gamma = reinterpret_cast<const float*>(wb + P.layer0 + P.attn_norm);
     e.xg = xg;
@@ -613,6 +835,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       g.bk_out = reinterpret_cast<float*>(ws + dp.bk);
       g.bv_out = reinterpret_cast<float*>(ws + dp.bv);
       g.ctx_lens = cache->ctx_lens;
+      g.rpr = m.rpr;
       g.n_q = m.nq;
       g.n_kv = m.nkv;
       g.head_dim = m.d;
@@ -629,8 +852,12 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.k_pool = reinterpret_cast<const char*>(cache->k_pool) + (size_t)l * pool_layer * m.es;
       a.v_pool = reinterpret_cast<const char*>(cache->v_pool) + (size_t)l * pool_layer * m.es;
       a.block_table = cache->block_table;
+      a.table_ld = cache->max_pages_per_seq;
       a.max_pages = cache->max_pages_per_seq;
       a.ctx_lens = cache->ctx_lens;
+      a.rpr = m.rpr;
+      a.nbk = m.nb;
+      a.causal = 0;
       a.n_q = m.nq;
       a.n_kv = m.nkv;
       a.head_dim = m.d;
@@ -641,7 +868,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
       a.part_ml = reinterpret_cast<float*>(ws + dp.apart_ml);
       a.out = ws + dp.ao;
       a.out_hilo = m.bf16;
-      DF_TRY(launch_block_attention(m.bf16, a, batch, stream));
+      DF_TRY(launch_block_attention(m.bf16, a, rows / kQRows, stream));
     }
     {  // output projection + residual
       GemmParams g = base_params(dp.o, lb + P.wo, 0, m.nq * m.d / m.ktile, ws + dp.ao,
@@ -719,25 +946,32 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
                         keys, stream);
 }
 
+static bool valid_block(int32_t block_size) {
+  return block_size == 8 || block_size == 16 || block_size == 32;
+}
+
 dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch,
-                             int32_t max_ctx, int32_t* ctx_lens, int32_t* anchor_ids,
-                             int32_t* inject_seq, int32_t* inject_pos, hipStream_t stream) {
+                             int32_t block_size, int32_t max_ctx, int32_t* ctx_lens,
+                             int32_t* anchor_ids, int32_t* inject_seq, int32_t* inject_pos,
+                             hipStream_t stream) {
   if (!accept_len || !bonus || !ctx_lens || !anchor_ids || !inject_seq || !inject_pos ||
-      batch < 0 || max_ctx < 16)
+      batch < 0 || !valid_block(block_size) || max_ctx < block_size)
     return DFLASH_ERR_INVALID_ARG;
   if (batch == 0) return DFLASH_OK;
-  DF_TRY(launch_advance(accept_len, bonus, batch, max_ctx, ctx_lens, anchor_ids, inject_seq,
-                        inject_pos, stream));
+  DF_TRY(launch_advance(accept_len, bonus, batch, block_size, max_ctx, ctx_lens, anchor_ids,
+                        inject_seq, inject_pos, stream));
   return DFLASH_OK;
 }
 
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
-                                   int32_t batch, int32_t* accept_len, int32_t* bonus,
-                                   int32_t* emitted, hipStream_t stream) {
-  if (!draft_ids || !target_ids || !accept_len || !bonus || batch < 0)
+                                   int32_t batch, int32_t block_size, int32_t* accept_len,
+                                   int32_t* bonus, int32_t* emitted, hipStream_t stream) {
+  if (!draft_ids || !target_ids || !accept_len || !bonus || batch < 0 ||
+      !valid_block(block_size))
     return DFLASH_ERR_INVALID_ARG;
   if (batch == 0) return DFLASH_OK;
-  DF_TRY(launch_verify_greedy(draft_ids, target_ids, batch, accept_len, bonus, emitted, stream));
+  DF_TRY(launch_verify_greedy(draft_ids, target_ids, batch, block_size, accept_len, bonus,
+                              emitted, stream));
   return DFLASH_OK;
 }
 

@@ -1,15 +1,21 @@
-// Block attention of the DFlash draft pass: the 16 block queries of every head of one KV
-// group attend, without a mask, to the request's injected context (paged KV cache) and to
-// the 16 block keys.
+// Block attention of the DFlash draft pass: the block queries of every head of one KV group
+// attend, without a mask, to the request's injected context (paged KV cache) and to the
+// block's own keys.
 //
-// Pass 1 (partials), grid (nc, n_kv, batch): workgroup c covers context keys
+// Queries come in tiles of 16 rows (kQRows): a request has rpr = 16 rows (blocks of 8 or 16
+// tokens; a block of 8 pads its request to 16 rows) or 32 rows (two tiles) and rpr block
+// keys, of which the first nbk are valid.  The input-fusion prefill uses the same kernels
+// with one tile per 16 context rows: each tile has the earlier rows as its cached context
+// and its own 16 rows as block keys under a causal mask (row j sees block keys 0..j).
+//
+// Pass 1 (partials), grid (nc, n_kv, tiles): workgroup c covers context keys
 // [c*chunk, min((c+1)*chunk, T_b)) (chunk a multiple of 32, at most kAttnMaxChunkKeys,
 // fixed by the caller, so the page ids of a chunk are a few loads per lane issued before T_b
 // arrives), and
-// the last workgroup also the 16 block keys (so a grid of nc * n_kv * batch workgroups fills
+// the last workgroup also the block keys (so a grid of nc * n_kv * tiles workgroups fills
 // the chip in one round).  One wave per query head of the KV group.  Each wave keeps an
 // online softmax (running max m, sum l, unnormalized output o) and writes (m, l, o).
-// Pass 2 (merge), grid (n_q, d / 32, batch): rescales the nc partials of each head to a
+// Pass 2 (merge), grid (n_q, d / 32, tiles): rescales the nc partials of each head to a
 // common maximum and divides by the total sum, chunks in order, so results do not depend on
 // scheduling.
 //
@@ -33,7 +39,7 @@
 //
 // Partial layout: part_o[slot][head_in_group][dt][q][row][i] holds output dim
 // 16*dt + 4*q + i of block row `row` (a float4 per (dt, q, row)); part_ml[slot][head][row]
-// holds (m, l).  slot = (b * n_kv + g) * nc + c.
+// holds (m, l).  slot = (tile * n_kv + g) * nc + c.
 #include <type_traits>
 
 #include "attention.h"
@@ -44,7 +50,7 @@ namespace dflash {
 
 __device__ inline long long part_o_index(long long slot, int G, int hh, int D, int row,
                                          int dim) {
-  return ((((slot * G + hh) * (D / 16) + dim / 16) * 4 + (dim % 16) / 4) * kBlock + row) * 4 +
+  return ((((slot * G + hh) * (D / 16) + dim / 16) * 4 + (dim % 16) / 4) * kQRows + row) * 4 +
          dim % 4;
 }
 
@@ -214,29 +220,38 @@ struct HeadState {
     }
   }
 
-  // The 16 block keys from LDS (fp32 K [16][D], then V^T [D][16]), hi + lo on both
-  // operands.
-  __device__ void block(const char* blk_s, int n) {
+  // The RPR block keys from LDS (fp32 K [RPR][D], then V^T [D][RPR]; RPR = 16 or 32, the
+  // second 16 on the S^T tile of page 1), hi + lo on both operands.  Lane n (query row n of
+  // the tile) takes block keys below nk, its own limit (the valid keys, or the causal bound).
+  template <int RPR>
+  __device__ void block(const char* blk_s, int n, int nk) {
     const float* bk_s = reinterpret_cast<const float*>(blk_s);
-    const float* bv_s = reinterpret_cast<const float*>(blk_s + kBlock * D * 4);
+    const float* bv_s = reinterpret_cast<const float*>(blk_s + RPR * D * 4);
+    constexpr int NP = RPR / 16;   // 16-key pages of the block
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f32x4 k0 = *reinterpret_cast<const f32x4*>(bk_s + n * D + ks * 32 + q * 8);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(bk_s + n * D + ks * 32 + q * 8 + 4);
-      const float f[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-      i32x4 kh, kl;
-      split8(f, kh, kl);
-      s[0] = mfma_tile<bf16>(kh, qf[ks][0], s[0]);
-      s[0] = mfma_tile<bf16>(kh, qf[ks][1], s[0]);
-      s[0] = mfma_tile<bf16>(kl, qf[ks][0], s[0]);
-    }
+    for (int pg = 0; pg < NP; ++pg)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float* kr = bk_s + (16 * pg + n) * D + ks * 32 + q * 8;
+        const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
+        const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+        const float f[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        i32x4 kh, kl;
+        split8(f, kh, kl);
+        s[pg] = mfma_tile<bf16>(kh, qf[ks][0], s[pg]);
+        s[pg] = mfma_tile<bf16>(kh, qf[ks][1], s[pg]);
+        s[pg] = mfma_tile<bf16>(kl, qf[ks][0], s[pg]);
+      }
     i32x4 ph, pl;
-    softmax<true>(s, kBlock, ph, pl);
+    softmax<true>(s, nk, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(bv_s + (16 * dt + n) * kBlock + q * 4);
-      const float f[8] = {vv[0], vv[1], vv[2], vv[3], 0.f, 0.f, 0.f, 0.f};
+      const float* vr = bv_s + (16 * dt + n) * RPR + q * 4;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(vr);
+      f32x4 v1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NP == 2) v1 = *reinterpret_cast<const f32x4*>(vr + 16);
+      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       i32x4 vh, vl;
       split8(f, vh, vl);
       o[dt] = mfma_tile<bf16>(vh, ph, o[dt]);
@@ -247,11 +262,11 @@ struct HeadState {
 
   // Partial of this chunk (layout in the file header).
   __device__ void store(const AttnArgs& a, long long slot, int G, int hh, int n) const {
-    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kBlock);
+    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kQRows);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kBlock + n] = o[dt];
+    for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kQRows + n] = o[dt];
     if (q == 0) {
-      float* ml = a.part_ml + ((slot * G + hh) * kBlock + n) * 2;
+      float* ml = a.part_ml + ((slot * G + hh) * kQRows + n) * 2;
       ml[0] = m_run;
       ml[1] = l_run;
     }
@@ -261,26 +276,37 @@ struct HeadState {
 // Everything a partial workgroup needs before its first step: the chunk's key range, the
 // page ids (lane i: logical page i of the chunk, at most 64, clamped into the table row and
 // fetched together with T_b), the block K/V copied into LDS by the last chunk's workgroup,
-// and this wave's Q rows.
+// this wave's Q rows, and the lane's limit on the block keys.
 template <int D>
 struct ChunkSetup {
   int kbeg, kend, npg, nsteps;
   int pid[kAttnPidRegs];   // pid[r] in lane i: physical page of logical page 64 r + i
   bool has_block;
+  int blk_nk;              // block keys below this index are seen by the lane's query row
 };
 
-template <int D, int G>
+// Request of tile `tile` (rpr / 16 tiles per request) and the lane's block-key limit for
+// query row n of the tile.
+__device__ inline int tile_request(const AttnArgs& a, int tile) { return tile * kQRows / a.rpr; }
+__device__ inline int block_key_limit(const AttnArgs& a, int tile, int n) {
+  const int row = tile * kQRows % a.rpr + n;   // row of the request's block
+  return a.causal ? min(a.nbk, row + 1) : a.nbk;
+}
+
+template <int D, int G, int RPR>
 __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
                                             f32x4 (&qraw)[D / 32][2]) {
-  constexpr int kBlockBytes = kBlock * D * 4;        // the block's K, or its V^T, in fp32
+  constexpr int kBlockBytes = RPR * D * 4;           // the block's K, or its V^T, in fp32
   constexpr int kCopies = 2 * kBlockBytes / 1024;    // 1 KB (64 lanes x 16 B) per copy
   static_assert(kCopies % G == 0, "block copies split evenly over the waves");
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const int b = tile_request(a, tile);
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int n = lane & 15, q = lane >> 4;
   ChunkSetup<D> cs;
+  cs.blk_nk = block_key_limit(a, tile, n);
   const int kbeg0 = c * a.chunk;
-  const int* table = a.block_table + (long long)b * a.max_pages;
+  const int* table = a.block_table + (long long)b * a.table_ld;
   int pid[kAttnPidRegs];
 #pragma unroll
   for (int r = 0; r < kAttnPidRegs; ++r)
@@ -290,8 +316,8 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
   cs.kbeg = min(kbeg0, T_b);
   cs.kend = min(kbeg0 + a.chunk, T_b);
 
-  // The last chunk's workgroup copies the block's fp32 keys [16][d] and transposed values
-  // [d][16] (contiguous per KV group) into LDS with direct loads, which need no registers.
+  // The last chunk's workgroup copies the block's fp32 keys [RPR][d] and transposed values
+  // [d][RPR] (contiguous per KV group) into LDS with direct loads, which need no registers.
   // The other workgroups issue the same copies from the first kilobyte of the arrays (and
   // never read them), so that every wave's load count is the same on every path.
   {
@@ -313,7 +339,7 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
   __builtin_amdgcn_sched_barrier(0);
 
   // Q^T rows of this head (B operand of S^T): lane holds block row n, dims 32*ks + 8q .. +8.
-  const float* src = a.q + ((long long)(b * kBlock + n) * a.n_q + g * G + hh) * D + q * 8;
+  const float* src = a.q + ((long long)(tile * kQRows + n) * a.n_q + g * G + hh) * D + q * 8;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     qraw[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 32);
@@ -348,16 +374,16 @@ struct StepRegs {
   int nk;                  // valid keys of the step (1..32)
 };
 
-template <int D, int G>
+template <int D, int G, int RPR>
 __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlock * D * 4];   // K, then V^T
+  __shared__ __attribute__((aligned(16))) char blk_s[2 * RPR * D * 4];   // K, then V^T
   const int g = blockIdx.y;
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int n = lane & 15, q = lane >> 4;
   const int nkv = a.n_kv;
   f32x4 qraw[KS][2];
-  const ChunkSetup<D> cs = chunk_setup<D, G>(a, blk_s, qraw);
+  const ChunkSetup<D> cs = chunk_setup<D, G, RPR>(a, blk_s, qraw);
 
   const bf16* kpool = reinterpret_cast<const bf16*>(a.k_pool);
   const bf16* vpool = reinterpret_cast<const bf16*>(a.v_pool);
@@ -421,7 +447,7 @@ __global__ __launch_bounds__(G * kWave, 2) void attn_partial_bf16(AttnArgs a) {
   if (cs.has_block) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    hs.block(blk_s, n);
+    hs.template block<RPR>(blk_s, n, cs.blk_nk);
   }
   hs.store(a, ((long long)blockIdx.z * nkv + g) * a.nc + blockIdx.x, G, hh, n);
 }
@@ -455,7 +481,7 @@ struct LdsStep {
 template <int D>
 __device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
-template <int D, int G>
+template <int D, int G, int RPR>
 __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_partial_lds(
     AttnArgs a) {
   using L = LdsStep<D, G>;
@@ -463,14 +489,14 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   // Register stages (steps ahead).  d = 64 with G = 8 runs two workgroups per CU (four
   // waves per SIMD, at most 128 registers), which needs the shallower ring.
   constexpr int RS = (D == 64 && G == 8) ? 2 : 4;
-  __shared__ __attribute__((aligned(16))) char blk_s[2 * kBlock * D * 4];
+  __shared__ __attribute__((aligned(16))) char blk_s[2 * RPR * D * 4];
   __shared__ __attribute__((aligned(16))) char kv_s[2][L::kStepBytes];
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid % kWave, hh = tid / kWave;
   const int n = lane & 15, q = lane >> 4;
   const int nkv = a.n_kv;
   f32x4 qraw[KS][2];
-  const ChunkSetup<D> cs = chunk_setup<D, G>(a, blk_s, qraw);
+  const ChunkSetup<D> cs = chunk_setup<D, G, RPR>(a, blk_s, qraw);
   const int nsteps = cs.nsteps;
 
   // Static description of this thread's pieces: quarter (page, K or V), source byte offset
@@ -576,7 +602,7 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   if (cs.has_block) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    hs.block(blk_s, n);
+    hs.template block<RPR>(blk_s, n, cs.blk_nk);
   }
   hs.store(a, ((long long)blockIdx.z * nkv + g) * a.nc + blockIdx.x, G, hh, n);
 }
@@ -589,7 +615,7 @@ constexpr int kThreads = 256;   // 4 waves
 
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
-  constexpr int G = R / kBlock;
+  constexpr int G = R / kQRows;
   constexpr int OPH = kThreads / D;
   constexpr int NRO = R / OPH;
   constexpr int SPH = kThreads / kKeys;
@@ -600,9 +626,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   __shared__ float p_s[R][kKeys + 1];
   __shared__ float m_s[R], l_s[R], sc_s[R];
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const int b = tile_request(a, tile);
   const int tid = threadIdx.x;
-  const int nq = a.n_q, nkv = a.n_kv;
+  const int nq = a.n_q, nkv = a.n_kv, rpr = a.rpr;
   const int T_b = a.ctx_lens[b];
   const bool has_block = c == a.nc - 1;
   const float qscale = a.scale * kLog2e;   // base-2 scores, as in the MFMA kernel
@@ -610,8 +637,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
   const int kend = min(kbeg + a.chunk, T_b);
   for (int idx = tid; idx < R * D; idx += kThreads) {
     const int r = idx / D, i = idx % D;
-    const int hh = r / kBlock, j = r % kBlock;
-    q_s[r][i] = a.q[((long long)(b * kBlock + j) * nq + g * G + hh) * D + i] * qscale;
+    const int hh = r / kQRows, j = r % kQRows;
+    q_s[r][i] = a.q[((long long)(tile * kQRows + j) * nq + g * G + hh) * D + i] * qscale;
   }
   if (tid < R) {
     m_s[tid] = -INFINITY;
@@ -624,22 +651,23 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
 
   const float* kpool = reinterpret_cast<const float*>(a.k_pool);
   const float* vpool = reinterpret_cast<const float*>(a.v_pool);
-  // Context steps of 32 keys, then (last workgroup) one step over the 16 block keys.
+  // Context steps of 32 keys, then (last workgroup) one step over the rpr block keys (at
+  // most 32), of which row r sees those below block_key_limit.
   const int n_ctx_steps = (kend - kbeg + kKeys - 1) / kKeys;
   for (int st = 0; st < n_ctx_steps + (has_block ? 1 : 0); ++st) {
     const bool is_block = st == n_ctx_steps;
     const int k0 = is_block ? 0 : kbeg + st * kKeys;
-    const int nk = is_block ? kBlock : min(kKeys, kend - k0);
+    const int nk = is_block ? rpr : min(kKeys, kend - k0);
     for (int idx = tid; idx < kKeys * D; idx += kThreads) {
       const int kk = idx / D, i = idx % D;
       float kv = 0.f, vv = 0.f;
       if (kk < nk) {
         const int t = k0 + kk;
         if (is_block) {
-          kv = a.bk[((long long)(b * nkv + g) * kBlock + t) * D + i];
-          vv = a.bv[((long long)(b * nkv + g) * D + i) * kBlock + t];
+          kv = a.bk[((long long)(b * nkv + g) * rpr + t) * D + i];
+          vv = a.bv[((long long)(b * nkv + g) * D + i) * rpr + t];
         } else {
-          const long long page = a.block_table[(long long)b * a.max_pages + t / kPage];
+          const long long page = a.block_table[(long long)b * a.table_ld + t / kPage];
           kv = kpool[((page * nkv + g) * kPage + t % kPage) * D + i];
           vv = vpool[((page * nkv + g) * D + i) * kPage + t % kPage];
         }
@@ -659,7 +687,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
         for (int n = 0; n < NRS; ++n) s[n] += q_s[r0 + n * SPH][i] * kv;
       }
 #pragma unroll
-      for (int n = 0; n < NRS; ++n) p_s[r0 + n * SPH][cc] = cc < nk ? s[n] : -INFINITY;
+      for (int n = 0; n < NRS; ++n) {
+        const int r = r0 + n * SPH;
+        const int lim = is_block ? block_key_limit(a, tile, r % kQRows) : nk;
+        p_s[r][cc] = cc < lim ? s[n] : -INFINITY;
+      }
     }
     __syncthreads();
     if (tid < R) {
@@ -690,12 +722,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_f32(AttnArgs a) {
     }
     __syncthreads();
   }
-  const long long slot = ((long long)b * nkv + g) * a.nc + c;
+  const long long slot = ((long long)tile * nkv + g) * a.nc + c;
   const int i = tid % D, r0 = tid / D;
 #pragma unroll
   for (int n = 0; n < NRO; ++n) {
     const int r = r0 + n * OPH;
-    a.part_o[part_o_index(slot, G, r / kBlock, D, r % kBlock, i)] = o[n];
+    a.part_o[part_o_index(slot, G, r / kQRows, D, r % kQRows, i)] = o[n];
   }
   if (tid < R) {
     a.part_ml[(slot * R + tid) * 2 + 0] = m_s[tid];
@@ -717,17 +749,17 @@ constexpr int kMergeThreads = 128;   // float4s of a 16 x 32 slice
 template <int D, int NCMAX>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
   constexpr int kMergeBatch = NCMAX < 40 ? NCMAX : 40;
-  constexpr int NCL = kMergeThreads / kBlock;   // chunk lanes per row
+  constexpr int NCL = kMergeThreads / kQRows;   // chunk lanes per row
   constexpr int NT = D * 4;                     // float4s of one head's 16 x D partial
-  __shared__ float w_s[NCMAX + 1][kBlock];
-  __shared__ float m_s[NCMAX + 1][kBlock];
-  __shared__ float red[NCL][kBlock];
-  __shared__ float M_s[kBlock], invL_s[kBlock];
-  const int h = blockIdx.x, slice = blockIdx.y, b = blockIdx.z;
+  __shared__ float w_s[NCMAX + 1][kQRows];
+  __shared__ float m_s[NCMAX + 1][kQRows];
+  __shared__ float red[NCL][kQRows];
+  __shared__ float M_s[kQRows], invL_s[kQRows];
+  const int h = blockIdx.x, slice = blockIdx.y, tile = blockIdx.z;
   const int G = a.n_q / a.n_kv;
   const int g = h / G, hh = h % G;
   const int nch = a.nc;
-  const long long slot0 = ((long long)b * a.n_kv + g) * nch;
+  const long long slot0 = ((long long)tile * a.n_kv + g) * nch;
   const int tid = threadIdx.x;
   const int f = slice * kMergeThreads + tid;     // float4 index (dt, q, row) within the head
   const long long cstride = (long long)G * NT;   // float4s between chunks
@@ -739,10 +771,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
     v[c] = c < nch ? src[c * cstride] : f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Row maximum and weights.  Thread (row j, chunk lane cl).
-  const int j = tid % kBlock, cl = tid / kBlock;
+  const int j = tid % kQRows, cl = tid / kQRows;
   float mx = -INFINITY;
   for (int c = cl; c < nch; c += NCL) {
-    const float* ml = a.part_ml + (((slot0 + c) * G + hh) * kBlock + j) * 2;
+    const float* ml = a.part_ml + (((slot0 + c) * G + hh) * kQRows + j) * 2;
     const float m = ml[0], l = ml[1];
     const float mm = l > 0.f ? m : -INFINITY;   // empty chunks carry no weight
     m_s[c][j] = mm;
@@ -751,7 +783,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
   }
   red[cl][j] = mx;
   __syncthreads();
-  if (tid < kBlock) {
+  if (tid < kQRows) {
     float M = -INFINITY;
     for (int r = 0; r < NCL; ++r) M = fmaxf(M, red[r][tid]);
     M_s[tid] = M;
@@ -767,7 +799,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
   __syncthreads();
   red[cl][j] = lsum;
   __syncthreads();
-  if (tid < kBlock) {
+  if (tid < kQRows) {
     float L = 0.f;
     for (int r = 0; r < NCL; ++r) L += red[r][tid];
     invL_s[tid] = 1.0f / L;
@@ -775,7 +807,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
   __syncthreads();
 
   // float4 f = (dt, q, row): row f % 16, dims 16*(f/64) + 4*((f/16)%4) .. +3.
-  const int row = f % kBlock;
+  const int row = f % kQRows;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kMergeBatch; ++c)
@@ -788,41 +820,46 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(AttnArgs a) {
     for (int c = 0; c < kMergeBatch; ++c)
       if (c0 + c < nch) acc += w_s[c0 + c][row] * v[c];
   }
-  const int dim = 16 * (f / (4 * kBlock)) + 4 * ((f / kBlock) % 4);
+  const int dim = 16 * (f / (4 * kQRows)) + 4 * ((f / kQRows) % 4);
   const f32x4 res = acc * invL_s[row];
   if (a.out_hilo) {
     store_hilo4(reinterpret_cast<bf16*>(a.out),
-                hilo_off(b * kBlock + row, h * D + dim, a.n_q * D / 32), res);
+                hilo_off(tile * kQRows + row, h * D + dim, a.n_q * D / 32), res);
   } else {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) +
-                              swz_off(b * kBlock + row, h * D + dim, a.n_q * D / 16, 4)) = res;
+                              swz_off(tile * kQRows + row, h * D + dim, a.n_q * D / 16, 4)) = res;
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // Launch
 // ------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int RPR>
 static void launch_partial_bf16(int G, dim3 grid, const AttnArgs& a, hipStream_t stream) {
   switch (G) {
-    case 1: attn_partial_bf16<D, 1><<<grid, 1 * kWave, 0, stream>>>(a); break;
-    case 2: attn_partial_bf16<D, 2><<<grid, 2 * kWave, 0, stream>>>(a); break;
-    case 4: attn_partial_lds<D, 4><<<grid, 4 * kWave, 0, stream>>>(a); break;
-    case 8: attn_partial_lds<D, 8><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    case 1: attn_partial_bf16<D, 1, RPR><<<grid, 1 * kWave, 0, stream>>>(a); break;
+    case 2: attn_partial_bf16<D, 2, RPR><<<grid, 2 * kWave, 0, stream>>>(a); break;
+    case 4: attn_partial_lds<D, 4, RPR><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 8: attn_partial_lds<D, 8, RPR><<<grid, 8 * kWave, 0, stream>>>(a); break;
     default: break;
   }
 }
 
-static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
+static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int tiles,
                                  hipStream_t stream) {
-  dim3 grid(a.nc, a.n_kv, batch);
+  dim3 grid(a.nc, a.n_kv, tiles);
   const int G = a.n_q / a.n_kv;
   if (!block_attention_supported(bf16_dtype, a.head_dim, G)) return hipErrorInvalidValue;
   if (bf16_dtype) {
-    if (a.head_dim == 128) launch_partial_bf16<128>(G, grid, a, stream);
-    else launch_partial_bf16<64>(G, grid, a, stream);
+    if (a.head_dim == 128) {
+      if (a.rpr == 32) launch_partial_bf16<128, 32>(G, grid, a, stream);
+      else launch_partial_bf16<128, 16>(G, grid, a, stream);
+    } else {
+      if (a.rpr == 32) launch_partial_bf16<64, 32>(G, grid, a, stream);
+      else launch_partial_bf16<64, 16>(G, grid, a, stream);
+    }
   } else {
-    const int R = G * kBlock;
+    const int R = G * kQRows;
     if (a.head_dim == 128) {
       if (R == 32) attn_partial_f32<128, 32><<<grid, kThreads, 0, stream>>>(a);
       else attn_partial_f32<128, 64><<<grid, kThreads, 0, stream>>>(a);
@@ -835,14 +872,16 @@ static hipError_t launch_partial(int bf16_dtype, const AttnArgs& a, int batch,
   return hipGetLastError();
 }
 
-hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int batch,
+hipError_t launch_block_attention(int bf16_dtype, const AttnArgs& a, int tiles,
                                   hipStream_t stream) {
   if (a.nc < 1 || a.nc > kAttnMaxChunks || a.chunk < 32 || a.chunk % 32 ||
       a.chunk > kAttnMaxChunkKeys)
     return hipErrorInvalidValue;
-  hipError_t e = launch_partial(bf16_dtype, a, batch, stream);
+  if ((a.rpr != 16 && a.rpr != 32) || a.nbk < 1 || a.nbk > a.rpr || tiles % (a.rpr / 16))
+    return hipErrorInvalidValue;
+  hipError_t e = launch_partial(bf16_dtype, a, tiles, stream);
   if (e != hipSuccess) return e;
-  dim3 grid(a.n_q, a.head_dim / 32, batch);
+  dim3 grid(a.n_q, a.head_dim / 32, tiles);
   constexpr int kSmallNc = 16;
   if (a.head_dim == 128) {
     if (a.nc <= kSmallNc) attn_merge<128, kSmallNc><<<grid, kMergeThreads, 0, stream>>>(a);

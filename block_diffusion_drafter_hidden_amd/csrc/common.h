@@ -14,9 +14,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kBlock = 16;      // block slots: anchor + 15 masks
+constexpr int kBlock = 16;      // block slots of the temperature-1 verify: anchor + 15 masks
 constexpr int kDrafts = 15;
 constexpr int kPage = 16;
+constexpr int kQRows = 16;      // query rows of one attention tile (one MFMA row block)
+constexpr int kMaxBlock = 32;   // largest draft block (block sizes 8, 16 and 32)
+
+// Rows of a draft pass: `rpr` rows per request (16, or 32 for a 32-token block), of which
+// slots 0 .. nb-1 are the block [anchor, mask x (nb - 1)] (a block of 8 pads its request to
+// 16 rows).  Slot j in 1 .. nb-1 of request b yields draft row b * (nb - 1) + j - 1; other
+// rows yield none (-1).
+__host__ __device__ inline long long draft_out_row(int m, int rpr, int nb) {
+  const int b = m / rpr, j = m % rpr;
+  return (j >= 1 && j < nb) ? (long long)b * (nb - 1) + j - 1 : -1;
+}
 
 // ---------------------------------------------------------------------------------------
 // Element types.  A "k-tile" is the K extent one lane loads as 16 bytes per MFMA row/col:

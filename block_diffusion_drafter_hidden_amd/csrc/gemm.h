@@ -78,12 +78,16 @@ struct GemmParams {
   float* ssq_out;
   // EPI_QKV
   float* q_out;             // [M][n_q][d]
-  float* bk_out;            // [batch][n_kv][16 slots][d]
-  float* bv_out;            // [batch][n_kv][d][16 slots] (transposed)
-  const int* ctx_lens;      // [batch]; slot j of request b sits at ctx_lens[b] + j
+  float* bk_out;            // [batch][n_kv][rpr slots][d]
+  float* bv_out;            // [batch][n_kv][d][rpr slots] (transposed)
+  const int* ctx_lens;      // [batch]; row j of request b (rows b*rpr ..) sits at ctx_lens[b] + j
+  int rpr;                  // rows per request: 16 or 32
   int n_q, n_kv, head_dim;
   double inv_freq[64];      // RoPE frequencies theta^(-2i/d), i < d/2 (d <= 128)
-  // EPI_INJECT
+  // EPI_INJECT, and EPI_QKV when k_pool is set (the input-fusion prefill): K/V of rows
+  // m < kv_rows are also written to the paged cache (EPI_QKV: at its position, page
+  // block_table[position / 16] of one request's table row; the block K/V then hold the
+  // stored values).
   void* k_pool;
   void* v_pool;
   long long pool_layer_elems;  // elements per layer of a pool
@@ -91,6 +95,7 @@ struct GemmParams {
   int max_pages;
   const int* seq_idx;
   const int* pos;
+  int kv_rows;
   // EPI_ARGMAX
   // (value, index) keys of each workgroup's best column per row, keys[part * keys_ld + row],
   // part = the workgroup's column block; reduced over parts by the finalize kernel.
@@ -98,7 +103,8 @@ struct GemmParams {
   unsigned long long* keys2;   // may be null: the runner-up key of each part and row, same layout
   int keys_ld;
   float* logits_out;        // [rows][ldo] or null
-  int draft_rows;           // rows are 16-slot blocks; logits row of (b, j >= 1) is b*15 + j-1
+  int draft_rpr;            // 0: plain rows; else rows are blocks of draft_rpr rows, and
+  int draft_nb;             // slot j in 1..draft_nb-1 of block b is logits row b*(nb-1) + j-1
   // 128-row kernel with EPI_RESIDUAL, EPI_STORE or EPI_QKV: the k range is split over
   // `ksplit` workgroups per output block (grid.y) and a reduction kernel adds the slices in
   // slice order and applies the epilogue.  Store / residual: slice s writes its fp32 partial
@@ -115,12 +121,13 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
                        int layers, hipStream_t stream);
 
 // ids[m] = index of the largest key over parts, keys[part * keys_ld + m], for m < rows; with
-// draft_rows the rows are 16-slot blocks and only slots 1..15 produce ids (block b, slot j
-// -> ids[b*15 + j-1]).  With keys2 (the parts' runner-up keys) and gap non-null, gap gets
-// the difference of the best and second-best values of the row, same indexing as ids.
+// draft_rpr the rows are blocks of draft_rpr rows and only slots 1..draft_nb-1 produce ids
+// (block b, slot j -> ids[b*(draft_nb-1) + j-1]).  With keys2 (the parts' runner-up keys)
+// and gap non-null, gap gets the difference of the best and second-best values of the row,
+// same indexing as ids.
 hipError_t launch_argmax_finalize(const unsigned long long* keys,
                                   const unsigned long long* keys2, int parts, int keys_ld,
-                                  int* ids, float* gap, int rows, int draft_rows,
+                                  int* ids, float* gap, int rows, int draft_rpr, int draft_nb,
                                   hipStream_t stream);
 
 // Column blocks (argmax parts) of an EPI_ARGMAX launch with this plan.

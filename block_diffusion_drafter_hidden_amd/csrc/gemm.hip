@@ -162,7 +162,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       int d0, d1;  // head dims of the two columns
       int position;
       if constexpr (EPI == EPI_QKV) {
-        position = p.ctx_lens[m / kBlock] + m % kBlock;
+        position = p.ctx_lens[m / p.rpr] + m % p.rpr;
       } else {
         position = p.pos[m];
       }
@@ -180,19 +180,41 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         d1 = d0 + 1;
       }
       if constexpr (EPI == EPI_QKV) {
-        const int b = m / kBlock, slot = m % kBlock;
+        const int rpr = p.rpr, b = m / rpr, slot = m % rpr;
         if (head < p.n_q) {
           float* dst = p.q_out + ((long long)m * p.n_q + head) * d;
           dst[d0] = a0;
           dst[d1] = a1;
-        } else if (head < p.n_q + p.n_kv) {
-          float* dst = p.bk_out + (((long long)b * p.n_kv + head - p.n_q) * kBlock + slot) * d;
-          dst[d0] = a0;
-          dst[d1] = a1;
         } else {
-          float* dst = p.bv_out + ((long long)b * p.n_kv + head - p.n_q - p.n_kv) * d * kBlock;
-          dst[d0 * kBlock + slot] = a0;
-          dst[d1 * kBlock + slot] = a1;
+          const bool is_k = head < p.n_q + p.n_kv;
+          const int h = is_k ? head - p.n_q : head - p.n_q - p.n_kv;
+          if (p.k_pool) {   // input-fusion prefill: the cache takes the row, and the block
+                            // keys/values the stored (rounded) value
+            a0 = Elem<T>::to_f(Elem<T>::from_f(a0));
+            a1 = Elem<T>::to_f(Elem<T>::from_f(a1));
+            if (m < p.kv_rows) {
+              const long long page = p.block_table[position / kPage];
+              const int ps = position % kPage;
+              if (is_k) {
+                T* dst = reinterpret_cast<T*>(p.k_pool) + ((page * p.n_kv + h) * kPage + ps) * d;
+                dst[d0] = Elem<T>::from_f(a0);
+                dst[d1] = Elem<T>::from_f(a1);
+              } else {
+                T* dst = reinterpret_cast<T*>(p.v_pool) + (page * p.n_kv + h) * d * kPage + ps;
+                dst[d0 * kPage] = Elem<T>::from_f(a0);
+                dst[d1 * kPage] = Elem<T>::from_f(a1);
+              }
+            }
+          }
+          if (is_k) {
+            float* dst = p.bk_out + (((long long)b * p.n_kv + h) * rpr + slot) * d;
+            dst[d0] = a0;
+            dst[d1] = a1;
+          } else {
+            float* dst = p.bv_out + ((long long)b * p.n_kv + h) * d * rpr;
+            dst[d0 * rpr + slot] = a0;
+            dst[d1 * rpr + slot] = a1;
+          }
         }
       } else {
         const int seq = p.seq_idx[m];
@@ -217,8 +239,9 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       for (int idx = tid; idx < rows * cols; idx += nthr) {
         const int r = idx / cols, c = idx % cols;
         const int m = m0 + r;
-        if (m >= p.M || (p.draft_rows && m % kBlock == 0)) continue;
-        const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
+        if (m >= p.M) continue;
+        const long long orow = p.draft_rpr ? draft_out_row(m, p.draft_rpr, p.draft_nb) : m;
+        if (orow < 0) continue;
         p.logits_out[orow * p.ldo + tile0 * 16 + c] = tl[r * ld + c];
       }
     }
@@ -1048,9 +1071,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
           if (c < cols) {
             const unsigned long long k = argmax_key(v, cb * kTallN + c);
             top2_push(best, second, k);
-            if (p.logits_out && m < p.M && !(p.draft_rows && m % kBlock == 0)) {
-              const long long orow = p.draft_rows ? (m / kBlock) * kDrafts + m % kBlock - 1 : m;
-              p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
+            if (p.logits_out && m < p.M) {
+              const long long orow = p.draft_rpr ? draft_out_row(m, p.draft_rpr, p.draft_nb) : m;
+              if (orow >= 0) p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
             }
           }
         }
@@ -1381,7 +1404,7 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
                                                               const unsigned long long* keys2,
                                                               int parts, int keys_ld, int* ids,
                                                               float* gap, int rows,
-                                                              int draft_rows) {
+                                                              int draft_rpr, int draft_nb) {
   __shared__ unsigned long long red[2][256 / kWave];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
   unsigned long long best = 0, second = 0;
@@ -1414,11 +1437,8 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
   for (int w = 1; w < 256 / kWave; ++w) top2_merge(best, second, red[0][w], red[1][w]);
   const int idx = argmax_key_index(best);
   const float g = argmax_key_value(best) - argmax_key_value(second);
-  if (!draft_rows) {
-    ids[m] = idx;
-    if (gap && keys2) gap[m] = g;
-  } else if (m % kBlock != 0) {
-    const long long o = (m / kBlock) * kDrafts + m % kBlock - 1;
+  const long long o = draft_rpr ? draft_out_row(m, draft_rpr, draft_nb) : m;
+  if (o >= 0) {
     ids[o] = idx;
     if (gap && keys2) gap[o] = g;
   }
@@ -1426,10 +1446,10 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
 
 hipError_t launch_argmax_finalize(const unsigned long long* keys,
                                   const unsigned long long* keys2, int parts, int keys_ld,
-                                  int* ids, float* gap, int rows, int draft_rows,
+                                  int* ids, float* gap, int rows, int draft_rpr, int draft_nb,
                                   hipStream_t stream) {
   argmax_finalize_kernel<<<rows, 256, 0, stream>>>(keys, gap ? keys2 : nullptr, parts, keys_ld,
-                                                  ids, gap, rows, draft_rows);
+                                                  ids, gap, rows, draft_rpr, draft_nb);
   return hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ struct EmbedArgs {
   int mask_id;
   const void* embed;      // [vocab][hidden] model dtype
   int hidden;
-  float* x;               // residual stream, fp32 fragment layout (rows = batch * 16)
+  int rpr;                // rows per request (16, or 32 for a 32-token block)
+  float* x;               // residual stream, fp32 fragment layout (rows = batch * rpr)
   const float* gamma;     // first layer's attention RMSNorm gain [hidden]
   void* xg;               // x * gamma: pair fragment layout (bf16 models), else as x
   float* ssq;             // [rows] sum of squares of each row
@@ -40,11 +41,18 @@ hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_
 hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hilo,
                                     const float* gamma, void* dst, float* ssq,
                                     hipStream_t stream);
-hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
-                                int* bonus, int* emitted, hipStream_t stream);
-// ctx_lens[b] += accept[b], anchors[b] = bonus[b]; inj_seq / inj_pos [batch * 16] get the
+// Input-fusion prefill helpers: the rows' norm inputs (padding rows >= n_valid zeroed) and
+// the cached context of each 16-row group, ctx_lens[seq] + r0 + 16 g.
+hipError_t launch_prefill_rows(int bf16_dtype, float* x, int rows, int n_valid, int hidden,
+                               const float* gamma, void* xg, float* ssq, hipStream_t stream);
+hipError_t launch_prefill_groups(const int* ctx_lens, int seq, int r0, int groups,
+                                 int* group_ctx, hipStream_t stream);
+// Block of nb tokens: draft [batch][nb - 1], target [batch][nb], emitted [batch][nb].
+hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int nb,
+                                int* accept, int* bonus, int* emitted, hipStream_t stream);
+// ctx_lens[b] += accept[b], anchors[b] = bonus[b]; inj_seq / inj_pos [batch * nb] get the
 // request index and the positions old ctx_lens[b] + j (clamped to max_ctx - 1).
-hipError_t launch_advance(const int* accept, const int* bonus, int batch, int max_ctx,
+hipError_t launch_advance(const int* accept, const int* bonus, int batch, int nb, int max_ctx,
                           int* ctx_lens, int* anchors, int* inj_seq, int* inj_pos,
                           hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

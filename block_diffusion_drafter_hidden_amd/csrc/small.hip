@@ -87,15 +87,15 @@ __device__ inline float block_sum256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Block embedding: row b*16 + j of x is the embedding of the anchor (j = 0) or of the mask
-// token (j >= 1), widened to fp32 and written in the fragment layout (4 columns per store),
-// together with x * gamma of the first RMSNorm (pair fragment layout for bf16 models) and
-// the row's sum of squares.
+// Block embedding: row b*rpr + j of x is the embedding of the anchor (j = 0) or of the mask
+// token (j >= 1; the padding rows of an 8-token block too), widened to fp32 and written in
+// the fragment layout (4 columns per store), together with x * gamma of the first RMSNorm
+// (pair fragment layout for bf16 models) and the row's sum of squares.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   __shared__ float red[4];
   const int m = blockIdx.x;
-  const int b = m / kBlock, j = m % kBlock;
+  const int b = m / a.rpr, j = m % a.rpr;
   const int tok = j == 0 ? a.anchor_ids[b] : a.mask_id;
   const T* e = reinterpret_cast<const T*>(a.embed) + (long long)tok * a.hidden;
   constexpr int kPer = Elem<T>::kPerLane;
@@ -147,6 +147,61 @@ __global__ __launch_bounds__(256) void rows_to_fragments_kernel(const float* __r
   if (threadIdx.x == 0) ssq[r] = ss;
 }
 
+// Input rows of the input-fusion prefill: x (fp32 fragment layout, rows < n_valid written by
+// the fusion GEMM) gives x * gamma and the row's sum of squares, as the embedding kernel does
+// for a draft block; rows n_valid .. rows-1 (the last 16-row group's padding) become zero in
+// x, x * gamma and the sums.
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_rows_kernel(float* x, int hidden, int n_valid,
+                                                           const float* gamma, void* xg,
+                                                           float* ssq) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  constexpr int kPer = Elem<T>::kPerLane;
+  const int KT = hidden / (4 * kPer);
+  const bool pad = m >= n_valid;
+  float ss = 0.f;
+  for (int i = 4 * threadIdx.x; i < hidden; i += 4 * blockDim.x) {
+    const long long off = swz_off(m, i, KT, kPer);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (pad) *reinterpret_cast<f32x4*>(x + off) = v;
+    else v = *reinterpret_cast<const f32x4*>(x + off);
+    const f32x4 g = *reinterpret_cast<const f32x4*>(gamma + i);
+    if constexpr (std::is_same<T, bf16>::value)
+      store_hilo4(reinterpret_cast<bf16*>(xg), hilo_off(m, i, hidden / 32), v * g);
+    else
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(xg) + off) = v * g;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum256(ss, red);
+  if (threadIdx.x == 0) ssq[m] = ss;
+}
+
+hipError_t launch_prefill_rows(int bf16_dtype, float* x, int rows, int n_valid, int hidden,
+                               const float* gamma, void* xg, float* ssq, hipStream_t stream) {
+  if (bf16_dtype)
+    prefill_rows_kernel<bf16><<<rows, 256, 0, stream>>>(x, hidden, n_valid, gamma, xg, ssq);
+  else
+    prefill_rows_kernel<float><<<rows, 256, 0, stream>>>(x, hidden, n_valid, gamma, xg, ssq);
+  return hipGetLastError();
+}
+
+// Context length seen by each 16-row group of an input-fusion prefill chunk: group g of a
+// chunk starting r0 rows into the prefill of request `seq` sees ctx_lens[seq] + r0 + 16 g
+// cached positions.
+__global__ void prefill_groups_kernel(const int* __restrict__ ctx_lens, int seq, int r0,
+                                      int groups, int* __restrict__ group_ctx) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g < groups) group_ctx[g] = ctx_lens[seq] + r0 + kQRows * g;
+}
+
+hipError_t launch_prefill_groups(const int* ctx_lens, int seq, int r0, int groups,
+                                 int* group_ctx, hipStream_t stream) {
+  prefill_groups_kernel<<<(groups + 255) / 256, 256, 0, stream>>>(ctx_lens, seq, r0, groups,
+                                                                  group_ctx);
+  return hipGetLastError();
+}
+
 hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hilo,
                                     const float* gamma, void* dst, float* ssq,
                                     hipStream_t stream) {
@@ -155,53 +210,55 @@ hipError_t launch_rows_to_fragments(const float* src, int rows, int cols, int hi
 }
 
 // ------------------------------------------------------------------------------------------
-// Greedy verification, one wave per request.  Lane i < 15 compares d_{i+1} with t_i; the
-// ballot of mismatches gives m = index of the lowest mismatching lane (15 if none), with
-// no data-dependent branch.
+// Greedy verification, one wave per request, for a block of nb tokens (nd = nb - 1 drafts).
+// Lane i < nd compares d_{i+1} with t_i; the ballot of mismatches gives m = index of the
+// lowest mismatching lane (nd if none), with no data-dependent branch.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void verify_greedy_kernel(const int* __restrict__ draft,
                                                            const int* __restrict__ target,
-                                                           int batch, int* __restrict__ accept,
+                                                           int nb, int* __restrict__ accept,
                                                            int* __restrict__ bonus,
                                                            int* __restrict__ emitted) {
   const int b = blockIdx.x;
   const int l = threadIdx.x;
-  const int d = l < kDrafts ? draft[(long long)b * kDrafts + l] : 0;
-  const int t = l < kBlock ? target[(long long)b * kBlock + l] : 0;
-  const unsigned long long miss = __ballot(l < kDrafts && d != t) | (1ull << kDrafts);
+  const int nd = nb - 1;
+  const int d = l < nd ? draft[(long long)b * nd + l] : 0;
+  const int t = l < nb ? target[(long long)b * nb + l] : 0;
+  const unsigned long long miss = __ballot(l < nd && d != t) | (1ull << nd);
   const int m = __ffsll((long long)miss) - 1;  // lowest set bit
   if (l == 0) {
     accept[b] = m + 1;
-    bonus[b] = target[(long long)b * kBlock + m];
+    bonus[b] = target[(long long)b * nb + m];
   }
-  if (emitted && l < kBlock) {
+  if (emitted && l < nb) {
     const int tm = __shfl(t, m, kWave);
-    emitted[(long long)b * kBlock + l] = l < m ? d : (l == m ? tm : -1);
+    emitted[(long long)b * nb + l] = l < m ? d : (l == m ? tm : -1);
   }
 }
 
-hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int* accept,
-                                int* bonus, int* emitted, hipStream_t stream) {
-  verify_greedy_kernel<<<batch, 64, 0, stream>>>(draft, target, batch, accept, bonus, emitted);
+hipError_t launch_verify_greedy(const int* draft, const int* target, int batch, int nb,
+                                int* accept, int* bonus, int* emitted, hipStream_t stream) {
+  verify_greedy_kernel<<<batch, 64, 0, stream>>>(draft, target, nb, accept, bonus, emitted);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
-// Closed-loop bookkeeping after a verify: the block's 16 positions become the injection
+// Closed-loop bookkeeping after a verify: the block's nb positions become the injection
 // rows of the next fuse-inject call, then the context grows by the accepted length and the
 // bonus token becomes the next anchor.  One wave per request; every lane reads T_b before
 // lane 0 rewrites it (the store depends on the loaded value).
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void advance_kernel(const int* __restrict__ accept,
-                                                     const int* __restrict__ bonus, int max_ctx,
-                                                     int* ctx_lens, int* __restrict__ anchors,
+                                                     const int* __restrict__ bonus, int nb,
+                                                     int max_ctx, int* ctx_lens,
+                                                     int* __restrict__ anchors,
                                                      int* __restrict__ inj_seq,
                                                      int* __restrict__ inj_pos) {
   const int b = blockIdx.x, l = threadIdx.x;
   const int T = ctx_lens[b];
-  if (l < kBlock) {
-    inj_seq[(long long)b * kBlock + l] = b;
-    inj_pos[(long long)b * kBlock + l] = min(max(T + l, 0), max_ctx - 1);
+  if (l < nb) {
+    inj_seq[(long long)b * nb + l] = b;
+    inj_pos[(long long)b * nb + l] = min(max(T + l, 0), max_ctx - 1);
   }
   if (l == 0) {
     ctx_lens[b] = T + accept[b];
@@ -209,11 +266,11 @@ __global__ __launch_bounds__(64) void advance_kernel(const int* __restrict__ acc
   }
 }
 
-hipError_t launch_advance(const int* accept, const int* bonus, int batch, int max_ctx,
+hipError_t launch_advance(const int* accept, const int* bonus, int batch, int nb, int max_ctx,
                           int* ctx_lens, int* anchors, int* inj_seq, int* inj_pos,
                           hipStream_t stream) {
-  advance_kernel<<<batch, 64, 0, stream>>>(accept, bonus, max_ctx, ctx_lens, anchors, inj_seq,
-                                           inj_pos);
+  advance_kernel<<<batch, 64, 0, stream>>>(accept, bonus, nb, max_ctx, ctx_lens, anchors,
+                                           inj_seq, inj_pos);
   return hipGetLastError();
 }
 

@@ -11,10 +11,12 @@
  *                           on DFlash, section "How does DFlash speculative decoding
  *                           work?": context features go into the key-value projections of
  *                           the draft layers).
- *   dflash_draft_block      one non-causal forward pass over the block [anchor, mask x 15]
- *                           that drafts 15 tokens with the shared LM head and argmax (wiki,
- *                           "Parallel drafting with block diffusion"; blog, same section:
- *                           one forward pass predicts a block of masked future tokens).
+ *   dflash_draft_block      one non-causal forward pass over the block [anchor, mask x
+ *                           (B - 1)], B = 16 (or 8 or 32), that drafts B - 1 tokens with the
+ *                           shared LM head and argmax (wiki, "Parallel drafting with block
+ *                           diffusion": one pass drafts a whole block, at a cost roughly
+ *                           independent of its size; blog, same section: one forward pass
+ *                           predicts a block of masked future tokens).
  *   dflash_verify_accept    greedy verification: the longest prefix of drafts that matches
  *                           the target's argmax, plus one target token (blog, same section:
  *                           the target accepts the longest valid prefix).
@@ -29,6 +31,13 @@
  *                           residual resampling, which keeps the target's output
  *                           distribution; blog, same section; wiki, "Performance
  *                           comparison", sampling at temperature 1).
+ *   dflash_prefill_input_fusion
+ *                           the input-fusion variant's context prefill: the fused features
+ *                           enter the drafter as its input rows and run causally through
+ *                           the layers, which cache their K/V (z-lab/dflash overview page,
+ *                           FAQ on KV injection versus input fusion; the variant KV
+ *                           injection is compared with, whose prefill processes every
+ *                           context token fully).
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers unless stated otherwise; the caller owns
@@ -45,10 +54,8 @@
  * Numerics: bf16 models keep weights, target features and the KV cache in bf16; every
  * activation (fused feature, residual stream, normed inputs, q/k/v, attention output,
  * SwiGLU product) is fp32 in memory and enters the bf16 MFMA as a hi + lo pair of bf16
- * values (the fused feature as three pieces), accumulating in fp32.  The LM head's normed
- * input enters as its hi piece alone when the call has more than 64 rows (bf16 x bf16
- * products, fp32 logits).  RoPE angles are computed in fp64.  f32 models use fp32
- * everywhere.
+ * values (the fused feature as three pieces), accumulating in fp32.  RoPE angles are
+ * computed in fp64.  f32 models use fp32 everywhere.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -72,7 +79,7 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
-/* Drafter shape.  Requirements checked by every call: block_size == 16,
+/* Drafter shape.  Requirements checked by every call: block_size in {8, 16, 32},
  * page_size == 16, hidden % 64 == 0, feat_dim % 64 == 0, intermediate % 64 == 0,
  * vocab % 64 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0, and a query-head
  * group G = n_q_heads / n_kv_heads in {1, 2, 4, 8} for bf16 (in {2, 4, 8}, and not 8 with
@@ -86,7 +93,8 @@ typedef struct {
   int32_t intermediate;   /* I, SwiGLU width */
   int32_t vocab;          /* V */
   int32_t feat_dim;       /* F = (number of fused target layers) * (target hidden size) */
-  int32_t block_size;     /* 16: slot 0 = last accepted token, slots 1..15 = mask */
+  int32_t block_size;     /* B = 16 (8, 32): slot 0 = last accepted token, slots 1..B-1 =
+                             mask */
   int32_t page_size;      /* 16 tokens per KV page */
   int32_t mask_token_id;
   float rope_theta;
@@ -168,21 +176,21 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
                                     const int32_t* seq_idx, const int32_t* pos, int32_t n_tok,
                                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Draft one block per request.
+/* Draft one block per request; B = cfg->block_size.
  *   embed      [V, H] model dtype: the target's embedding table (shared, not packed).
  *   anchor_ids [batch] int32: last accepted token of each request (block slot 0).
- *   draft_ids  [batch, 15] int32 out: argmax over the vocabulary of slots 1..15, exact
+ *   draft_ids  [batch, B-1] int32 out: argmax over the vocabulary of slots 1..B-1, exact
  *              fp32 ties resolved to the lowest id.
- *   top2_gap   [batch, 15] fp32 out, may be NULL: the largest logit of each slot minus the
+ *   top2_gap   [batch, B-1] fp32 out, may be NULL: the largest logit of each slot minus the
  *              second largest (0 for an exact tie).  A small gap marks a near-tie, whose id
  *              can change under rounding of the logits (wiki, "Conditioning on target-model
  *              features", closing paragraph: the draft tokens come from the target's shared
  *              LM head).
- *   logits_out [batch, 15, V] fp32 out, may be NULL: the LM-head logits of slots 1..15.
+ *   logits_out [batch, B-1, V] fp32 out, may be NULL: the LM-head logits of slots 1..B-1.
  * Slot j of request b sits at position ctx_lens[b] + j and attends, without a mask, to
- * the ctx_lens[b] cached context entries and the 16 block slots.
- * DFLASH_ERR_UNSUPPORTED if batch > 4096 or the cache's max_pages_per_seq > 16384
- * (262144 positions per request). */
+ * the ctx_lens[b] cached context entries and the B block slots.
+ * DFLASH_ERR_UNSUPPORTED if batch * max(B, 16) > 65536 or the cache's max_pages_per_seq >
+ * 16384 (262144 positions per request). */
 dflash_status dflash_draft_block(const dflash_config* cfg, const void* packed,
                                  const void* embed, const dflash_kv_cache* cache,
                                  const int32_t* anchor_ids, int32_t batch, int32_t* draft_ids,
@@ -224,22 +232,24 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
                                     float* logits_out, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
 
-/* Greedy verification.
- *   draft_ids  [batch, 15] int32: d_1..d_15.
- *   target_ids [batch, 16] int32: t_0..t_15, the target's argmax after block slot j.
+/* Greedy verification of blocks of B = block_size tokens (8, 16 or 32).
+ *   draft_ids  [batch, B-1] int32: d_1..d_{B-1}.
+ *   target_ids [batch, B] int32: t_0..t_{B-1}, the target's argmax after block slot j.
  *   accept_len [batch] int32 out: m + 1, m = number of leading i with d_i == t_{i-1}.
  *   bonus      [batch] int32 out: t_m.
- *   emitted    [batch, 16] int32 out, may be NULL: d_1..d_m, t_m, then -1 padding. */
+ *   emitted    [batch, B] int32 out, may be NULL: d_1..d_m, t_m, then -1 padding.
+ * DFLASH_ERR_INVALID_ARG for a null input or output, batch < 0 or another block size. */
 dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* target_ids,
-                                   int32_t batch, int32_t* accept_len, int32_t* bonus,
-                                   int32_t* emitted, hipStream_t stream);
+                                   int32_t batch, int32_t block_size, int32_t* accept_len,
+                                   int32_t* bonus, int32_t* emitted, hipStream_t stream);
 
 /* Closed-loop bookkeeping after dflash_verify_accept, so that a whole decoding iteration
  * (draft -> verify -> advance -> inject) runs on the stream without the host reading any
- * result.  For each request b, with T_b the context length before the call:
- *   inject_seq [batch * 16] int32 out: b for rows b*16 .. b*16+15;
- *   inject_pos [batch * 16] int32 out: T_b + j for row b*16 + j -- the positions of the
- *              block's 16 slots (slot 0 = the anchor at T_b), whose target hidden features
+ * result.  For each request b, with T_b the context length before the call and B =
+ * block_size (8, 16 or 32):
+ *   inject_seq [batch * B] int32 out: b for rows b*B .. b*B+B-1;
+ *   inject_pos [batch * B] int32 out: T_b + j for row b*B + j -- the positions of the
+ *              block's B slots (slot 0 = the anchor at T_b), whose target hidden features
  *              the next dflash_fuse_inject_kv call writes into the cache;
  *   ctx_lens   [batch] int32 in/out: T_b -> T_b + accept_len[b] (the anchor and the
  *              accepted drafts join the context);
@@ -248,19 +258,20 @@ dflash_status dflash_verify_accept(const int32_t* draft_ids, const int32_t* targ
  * the cache holds per request (max_pages_per_seq * 16).  Rows j >= accept_len[b] write
  * positions past the new context length: no draft reads them, and the next iteration's
  * injection (which starts at the new T_b) overwrites them first.  Precondition:
- * T_b + 16 <= max_ctx; positions are clamped to max_ctx - 1 so that no access leaves the
- * request's page-table row.  DFLASH_ERR_INVALID_ARG for null pointers, batch < 0 or
- * max_ctx < 16; batch 0 launches nothing. */
+ * T_b + B <= max_ctx; positions are clamped to max_ctx - 1 so that no access leaves the
+ * request's page-table row.  DFLASH_ERR_INVALID_ARG for null pointers, batch < 0, another
+ * block size or max_ctx < B; batch 0 launches nothing. */
 dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch,
-                             int32_t max_ctx, int32_t* ctx_lens, int32_t* anchor_ids,
-                             int32_t* inject_seq, int32_t* inject_pos, hipStream_t stream);
+                             int32_t block_size, int32_t max_ctx, int32_t* ctx_lens,
+                             int32_t* anchor_ids, int32_t* inject_seq, int32_t* inject_pos,
+                             hipStream_t stream);
 
 /* Workspace bytes for dflash_verify_accept_sampled (0 if batch <= 0 or vocab is outside
  * 1 .. 1048576): the rows' softmax statistics and the final draw's 256-element chunk
  * sums, batch * (62 + ceil(vocab / 256)) doubles. */
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
 
-/* Temperature-1 verification.
+/* Temperature-1 verification (blocks of 16 tokens).
  *   draft_logits  [batch, 15, vocab] fp32, target_logits [batch, 16, vocab] fp32.
  *   u_draft, u_accept [batch, 15], u_resample [batch]: uniforms in [0, 1).
  * q_i = softmax(draft_logits[i-1]), p_i = softmax(target_logits[i-1]).
@@ -280,6 +291,34 @@ dflash_status dflash_verify_accept_sampled(const float* draft_logits,
                                            int32_t* accept_len, int32_t* emitted,
                                            void* workspace, size_t ws_bytes,
                                            hipStream_t stream);
+
+/* Bytes of workspace dflash_prefill_input_fusion needs for up to `max_tok` context rows
+ * per call and a cache of `max_ctx` positions per request (max_pages_per_seq * 16).
+ * Returns 0 if an argument is invalid. */
+size_t dflash_prefill_workspace_size(const dflash_config* cfg, int32_t max_tok,
+                                     int32_t max_ctx);
+
+/* Context prefill of the input-fusion variant (z-lab/dflash overview page, FAQ on KV
+ * injection versus input fusion), the alternative to dflash_fuse_inject_kv: instead of
+ * projecting the fused feature straight into K/V, the drafter takes the fused feature
+ * c_t = W_fuse . X_t as its input hidden state at context position t and runs the context
+ * rows through its layers, attention being causal over the context (row t attends to
+ * positions 0..t); each layer writes the K/V of the rows into its paged cache, and the
+ * rows attend to those stored values (bf16 for a bf16 drafter).  The last layer's attention
+ * and MLP of the context rows are not run: the draft step reads only the cached K/V, and
+ * dflash_draft_block drafts over this cache unchanged.
+ *   feats [n_tok, F] model dtype: concatenated target hidden states of request `seq`'s
+ *         next n_tok context positions, ctx_lens[seq] .. ctx_lens[seq] + n_tok - 1 (the
+ *         cache already holds positions 0 .. ctx_lens[seq] - 1 of this variant).
+ *   seq   request index (row of block_table).
+ * ctx_lens is read, not changed: the caller advances it.  Rows are processed in chunks of
+ * 2048 positions, in order.  Precondition: ctx_lens[seq] + n_tok <= max_pages_per_seq * 16.
+ * DFLASH_ERR_WORKSPACE if ws_bytes < dflash_prefill_workspace_size(cfg, n_tok, max_ctx);
+ * n_tok 0 launches nothing. */
+dflash_status dflash_prefill_input_fusion(const dflash_config* cfg, const void* packed,
+                                          const dflash_kv_cache* cache, const void* feats,
+                                          int32_t seq, int32_t n_tok, void* workspace,
+                                          size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* dflash_error_string(dflash_status status);

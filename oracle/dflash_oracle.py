@@ -233,7 +233,7 @@ def prefill_context(cfg, weights: Dict, feats, positions=None, precision=None):
     return ks, vs
 
 
-def prefill_input_fusion(cfg, weights: Dict, feats, precision=None):
+def prefill_input_fusion(cfg, weights: Dict, feats, precision=None, want_unrounded=False):
     """The input-fusion variant's context prefill [faq: KV injection versus input fusion],
     for a fresh context at positions 0..T-1 (reading R21).
 
@@ -244,20 +244,23 @@ def prefill_input_fusion(cfg, weights: Dict, feats, precision=None):
     the layer's cached K/V of positions 0..t, i.e. the stored (bf16 for a bf16 drafter)
     values, its own included.  The result is each layer's cached K, V [T, n_kv, d]; the
     last layer's attention and MLP feed nothing the draft step reads and are not run.
-    The draft step over this cache is draft_block, unchanged."""
+    The draft step over this cache is draft_block, unchanged.  With want_unrounded, also
+    returns each layer's K, V before they are stored (the values the cache rounds)."""
     p = precision_of(cfg, precision)
     H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
     T = feats.shape[0]
     pos = np.arange(T)
     x = fuse_features(feats, weights["w_fuse"])                    # [T, H] input rows
-    ks, vs = [], []
+    ks, vs, ku, vu = [], [], [], []
     for l in range(cfg.n_layers):
         u = rms_norm(x, weights[f"attn_norm.{l}"], cfg.rms_eps)
-        k = store(rope((u @ f64(weights[f"wk.{l}"]).T).reshape(T, nkv, d), pos,
-                       cfg.rope_theta), p)
-        v = store((u @ f64(weights[f"wv.{l}"]).T).reshape(T, nkv, d), p)
+        k_raw = rope((u @ f64(weights[f"wk.{l}"]).T).reshape(T, nkv, d), pos, cfg.rope_theta)
+        v_raw = (u @ f64(weights[f"wv.{l}"]).T).reshape(T, nkv, d)
+        k, v = store(k_raw, p), store(v_raw, p)
         ks.append(k)
         vs.append(v)
+        ku.append(k_raw)
+        vu.append(v_raw)
         if l + 1 == cfg.n_layers:
             break
         q = rope((u @ f64(weights[f"wq.{l}"]).T).reshape(T, nq, d), pos, cfg.rope_theta)
@@ -267,7 +270,7 @@ def prefill_input_fusion(cfg, weights: Dict, feats, precision=None):
         g = u @ f64(weights[f"w_gate.{l}"]).T
         up = u @ f64(weights[f"w_up.{l}"]).T
         x = x + (silu(g) * up) @ f64(weights[f"w_down.{l}"]).T
-    return ks, vs
+    return (ks, vs, ku, vu) if want_unrounded else (ks, vs)
 
 
 def draft_block(cfg, weights: Dict, k_ctx: Sequence[np.ndarray], v_ctx: Sequence[np.ndarray],

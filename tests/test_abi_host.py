@@ -47,10 +47,19 @@ def test_workspace_size_grows_with_batch_and_context():
     a = B.workspace_size(c, 1, 16, 2048)
     b = B.workspace_size(c, 32, 512, 8192)
     assert 0 < a < b
+    # A 32-token block has twice the rows of a 16-token one; an 8-token block pads to 16.
+    c8, c32 = B.make_config(scaled(QWEN3_8B, block_size=8)), B.make_config(scaled(QWEN3_8B, block_size=32))
+    assert B.workspace_size(c8, 4, 0, 2048) == B.workspace_size(c, 4, 0, 2048)
+    assert B.workspace_size(c32, 4, 0, 2048) > B.workspace_size(c, 4, 0, 2048)
+    assert B.workspace_size(c32, 4, 0, 2048) == B.workspace_size(c, 8, 0, 2048)
+    # The input-fusion prefill: chunks of at most 2048 rows.
+    p1 = B.prefill_workspace_size(c, 16, 4096)
+    p2 = B.prefill_workspace_size(c, 2048, 4096)
+    assert 0 < p1 < p2 == B.prefill_workspace_size(c, 100000, 4096)
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("block_size", 8, -2), ("page_size", 32, -2), ("head_dim", 96, -2), ("hidden", 100, -2),
+    ("block_size", 12, -2), ("block_size", 64, -2), ("page_size", 32, -2), ("head_dim", 96, -2), ("hidden", 100, -2),
     ("n_kv_heads", 3, -1), ("dtype", 5, -2), ("mask_token_id", -1, -1), ("vocab", 4000, -2)])
 def test_invalid_config_rejected(field, value, status):
     c = B.make_config(TINY)
@@ -66,7 +75,7 @@ def test_invalid_config_rejected(field, value, status):
 def test_null_arguments_rejected_before_launch():
     lib = B.load_library()
     c = B.make_config(TINY)
-    assert lib.dflash_verify_accept(None, None, 4, None, None, None, None) == -1
+    assert lib.dflash_verify_accept(None, None, 4, 16, None, None, None, None) == -1
     assert lib.dflash_workspace_init(None, 0, None) == -1
     assert lib.dflash_draft_block(C.byref(c), None, None, None, None, 1, None, None, None,
                                   None, 0, None) == -1
@@ -76,11 +85,26 @@ def test_null_arguments_rejected_before_launch():
                                             None, None, 0, None) == -1
     assert lib.dflash_verify_sampled_workspace_size(0, 8) == 0
     fake = C.c_void_p(16)  # never dereferenced: validation fails first
-    assert lib.dflash_advance(None, fake, 2, 64, fake, fake, fake, fake, None) == -1
-    assert lib.dflash_advance(fake, fake, 2, 64, fake, fake, None, fake, None) == -1
-    assert lib.dflash_advance(fake, fake, -1, 64, fake, fake, fake, fake, None) == -1
-    assert lib.dflash_advance(fake, fake, 2, 8, fake, fake, fake, fake, None) == -1
-    assert lib.dflash_advance(fake, fake, 0, 64, fake, fake, fake, fake, None) == 0
+    assert lib.dflash_advance(None, fake, 2, 16, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 16, 64, fake, fake, None, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, -1, 16, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 16, 8, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 32, 16, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 2, 12, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 0, 64, 64, fake, fake, fake, fake, None) == -1
+    assert lib.dflash_advance(fake, fake, 0, 16, 64, fake, fake, fake, fake, None) == 0
+    assert lib.dflash_advance(fake, fake, 0, 8, 64, fake, fake, fake, fake, None) == 0
+    for nb, st in ((8, 0), (16, 0), (32, 0), (4, -1), (24, -1)):
+        assert lib.dflash_verify_accept(fake, fake, 0, nb, fake, fake, None, None) == st
+    cache = B.KVCache(1, 1, 1, 1, 16, 8)
+    assert lib.dflash_prefill_input_fusion(C.byref(c), None, C.byref(cache), fake, 0, 4, fake,
+                                           1 << 30, None) == -1
+    assert lib.dflash_prefill_input_fusion(C.byref(c), fake, C.byref(cache), None, 0, 4, fake,
+                                           1 << 30, None) == -1
+    assert lib.dflash_prefill_input_fusion(C.byref(c), fake, C.byref(cache), fake, -1, 4, fake,
+                                           1 << 30, None) == -1
+    assert lib.dflash_prefill_input_fusion(C.byref(c), fake, C.byref(cache), fake, 0, 0, fake,
+                                           1 << 30, None) == 0
 
 
 def test_small_workspace_rejected_before_launch():
@@ -112,6 +136,17 @@ def test_size_limits_rejected_before_launch():
     st = lib.dflash_lm_head_argmax(C.byref(c), fake, fake, 65537, fake, None, fake, 1 << 40,
                                    None)
     assert st == -2
+    c32 = B.make_config(scaled(TINY, block_size=32))   # 32 rows per request: 2048 requests
+    st = lib.dflash_draft_block(C.byref(c32), fake, fake, C.byref(ok_cache), fake, 2049, fake,
+                                None, None, fake, 1 << 40, None)
+    assert st == -2
+    # Prefill: more rows than the cache holds per request; too small a workspace.
+    st = lib.dflash_prefill_input_fusion(C.byref(c), fake, C.byref(ok_cache), fake, 0, 129,
+                                         fake, 1 << 40, None)
+    assert st == -1
+    st = lib.dflash_prefill_input_fusion(C.byref(c), fake, C.byref(ok_cache), fake, 0, 64,
+                                         fake, 4096, None)
+    assert st == -3
 
 
 def test_binding_rejects_bad_tensors_before_the_library():
@@ -122,6 +157,10 @@ def test_binding_rejects_bad_tensors_before_the_library():
     with pytest.raises(ValueError, match="GPU tensor"):
         B.verify_accept(cpu32, torch.zeros((2, 16), dtype=torch.int32),
                         torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.prefill_input_fusion(B.make_config(TINY), None, None,
+                               torch.zeros((3, TINY.feat_dim)), 0,
+                               torch.zeros(8, dtype=torch.uint8))
     with pytest.raises(ValueError, match="ws: required"):
         B.draft_block(B.make_config(TINY), None, None, None, None, None, None)
     with pytest.raises(ValueError, match="expected a torch tensor"):
