@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--loop", action="store_true",
                     help="time the closed decoding loop (draft, verify, advance, inject) "
                          "against a seeded synthetic target instead of the single step")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time only the drafter prefill of 2048 positions, KV injection "
+                         "against the input-fusion variant")
     ap.add_argument("--kernel-reps", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra measurements of the default run (the Qwen3-8B-shaped "
@@ -86,6 +89,8 @@ def main():
         return loop_bench(args, wl)
     if args.latency_shape:
         return latency_bench(args, wl)
+    if args.prefill:
+        return prefill_bench(args, wl)
     cfg = wl.cfg
     Bn = wl.batch
     ctx = synth.context_lengths(wl)
@@ -439,6 +444,32 @@ def extra_measurements(args, dr, s):
 
     extra["prefill_2048"] = prefill_comparison(args, dr, s)
     return extra
+
+
+def prefill_bench(args, wl):
+    """--prefill: the prefill comparison alone, as its own JSON line."""
+    import torch
+    from block_diffusion_drafter_hidden_amd import Drafter
+    from workloads import WORKLOADS, synth
+
+    wl = WORKLOADS["qwen3_b1"]
+    dev = torch.device("cuda:0")
+    log(f"[prefill] {wl.name}: generating weights")
+    w = synth.drafter_weights(wl.cfg, seed=wl.seed)
+    wd = {k: v.to(dev) for k, v in w.items()}
+    del w
+    dr = Drafter(wl.cfg, wd, max_batch=1, max_ctx=2048, max_inject_rows=16, device=dev)
+    del wd
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    out = prefill_comparison(args, dr, s)
+    print(json.dumps({
+        "metric": "drafter prefill time of a 2048-position context: KV injection vs input "
+                  "fusion", "value": out["input_fusion_over_kv_injection"],
+        "unit": "input-fusion time / KV-injection time", "n_gpus": 1, "steps": out["replays"],
+        "warmup": 2, "higher_is_better": True, "dtype": wl.cfg.dtype,
+        "data": "synthetic (seeded weights and target features)",
+        "config": {"workload": f"{wl.cfg.name}-prefill-2048"}, **out}), flush=True)
 
 
 def prefill_comparison(args, dr, s, T=2048):

@@ -378,7 +378,7 @@ class Drafter:
             from dataclasses import replace
             d.cfg = replace(self.cfg, block_size=block_size)
             d.ccfg = make_config(d.cfg)
-        d.ws_bytes = workspace_size(self.ccfg, max_batch, max_inject_rows, max_ctx)
+        d.ws_bytes = workspace_size(d.ccfg, max_batch, max_inject_rows, max_ctx)
         d.ws = torch.empty(d.ws_bytes, dtype=torch.uint8, device=self.device)
         workspace_init(d.ws)
         return d
