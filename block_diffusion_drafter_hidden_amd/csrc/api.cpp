@@ -87,7 +87,7 @@ dflash_status check_config(const dflash_config* c, Dims* o) {
 // Packed weight buffer layout.
 // ---------------------------------------------------------------------------------------
 struct Packed {
-  size_t final_norm, w_fuse, lm_head, layer0, layer_stride;
+  size_t final_norm, w_fuse, lm_head, lm_norms, lm_wmax, layer0, layer_stride;
   size_t attn_norm, mlp_norm, wqkv, wo, wgu, wd;  // offsets inside one layer
   size_t total;
 };
@@ -101,6 +101,10 @@ Packed packed_layout(const Dims& m) {
   off = align_up(off + (size_t)m.H * m.F * m.es);
   p.lm_head = off;
   off = align_up(off + (size_t)m.V * m.H * m.es);
+  p.lm_norms = off;   // the LM head's row norms, then the largest of them
+  off = align_up(off + (size_t)m.V * 4);
+  p.lm_wmax = off;
+  off = align_up(off + 4);
   p.layer0 = off;
   size_t lo = 0;
   p.attn_norm = lo;
@@ -304,7 +308,7 @@ DraftPlan draft_plan(const Dims& m, int B, int max_ctx) {
   const size_t R = (size_t)m.G * 16;
   p.apart_o = c.take((size_t)kv_groups * p.nc * R * m.d * 4);
   p.apart_ml = c.take((size_t)kv_groups * p.nc * R * 2 * 4);
-  p.keys = c.take(2 * lm_keys_bytes(m, rows));
+  p.keys = c.take(3 * lm_keys_bytes(m, rows));
   // k-split partials: row-major for the O and down projections, whole 128 x 128 blocks for
   // Q|K|V (one buffer, used by one GEMM at a time).
   const int splits = std::max(p.o.mt == kTallMT ? p.o.ksub : 1, p.dn.mt == kTallMT ? p.dn.ksub : 1);
@@ -395,8 +399,9 @@ PrefillPlan prefill_plan(const Dims& m, int rows, int max_ctx) {
 // Final RMSNorm + shared LM head + argmax over the vocabulary.  `xg` is x * final gain in
 // the fragment layout and ssq the rows' sums of squares (ssq_parts partials, row stride
 // ssq_ld); with draft_rows the rows are 16-slot blocks and slot 0 is computed and dropped.
-// keys: workspace for the per-column-block argmax partials, 2 * lm_keys_bytes(m, rows)
-// bytes (best keys, then runner-up keys, which are only written when gap_out is set).
+// keys: workspace for the per-column-block argmax partials, 3 * lm_keys_bytes(m, rows)
+// bytes (best keys, then runner-up keys, written when gap_out is set or in refine mode,
+// then third keys, refine mode only).
 // draft: the rows are draft blocks (m.rpr rows per request, ids of slots 1 .. m.nb - 1).
 dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, const void* xg,
                              const float* ssq, int ssq_parts, int ssq_ld, int rows,
@@ -404,6 +409,11 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
                              unsigned long long* keys, hipStream_t stream) {
   const Plan pl = lm_plan(m, rows);
   const int parts = argmax_parts(m.V / 16, pl.mt, pl.npw, pl.tgpw);
+  // Past 64 rows (the 256-row kernel, where the LM head is matrix-core bound) and without
+  // logits to return: the hi piece alone, then the exact top two of the columns that can
+  // still win (launch_argmax_refine) -- half the matrix-core work, the same ids and gaps.
+  const bool refine = pl.mt == kTallMT && !logits_out && m.H <= kRefineMaxHidden &&
+                      parts <= 2048;
   GemmParams g = base_params(pl, wb + P.lm_head, 0, m.H / m.ktile, xg, m.H, rows, m.V / 16);
   g.a_kind = act_kind(m);
   g.norm = 1;
@@ -412,8 +422,10 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.ssq_ld = ssq_ld;
   g.eps = m.eps;
   g.keys = keys;
-  g.keys2 = gap_out ? keys + lm_keys_bytes(m, rows) / 8 : nullptr;
-  g.keys_ld = rows;
+  g.keys2 = (gap_out || refine) ? keys + lm_keys_bytes(m, rows) / 8 : nullptr;
+  g.keys3 = refine ? keys + 2 * (lm_keys_bytes(m, rows) / 8) : nullptr;
+  g.refine = refine ? 1 : 0;
+  g.keys_ld = refine ? parts : rows;
   g.logits_out = logits_out;
   // The two waves of a k range take alternate k-tiles, so a workgroup reads its n-tiles'
   // weights front to back together (streaming kernel; LM-head launch 204.5 -> 202.5 us at one
@@ -423,6 +435,32 @@ dflash_status launch_lm_head(const Dims& m, const Packed& P, const char* wb, con
   g.draft_rpr = draft ? m.rpr : 0;
   g.draft_nb = m.nb;
   DF_TRY(launch_gemm(m.bf16, pl.mt, pl.npw, EPI_ARGMAX, g, 1, stream));
+  if (refine) {
+    RefineArgs r{};
+    r.keys = keys;
+    r.keys2 = g.keys2;
+    r.keys3 = g.keys3;
+    r.parts = parts;
+    r.keys_ld = parts;
+    r.part_cols = 16 * kTallNT;
+    r.a = xg;
+    r.KT = m.H / m.ktile;
+    r.ssq = ssq;
+    r.ssq_parts = ssq_parts;
+    r.ssq_ld = ssq_ld;
+    r.eps = m.eps;
+    r.w = wb + P.lm_head;
+    r.nt_stride = m.H / m.ktile;
+    r.kt_stride = 1;
+    r.vocab = m.V;
+    r.wmax = reinterpret_cast<const float*>(wb + P.lm_wmax);
+    r.ids = ids_out;
+    r.gap = gap_out;
+    r.draft_rpr = g.draft_rpr;
+    r.draft_nb = g.draft_nb;
+    DF_TRY(launch_argmax_refine(r, rows, stream));
+    return DFLASH_OK;
+  }
   DF_TRY(launch_argmax_finalize(keys, g.keys2, parts, rows, ids_out, gap_out, rows,
                                 g.draft_rpr, g.draft_nb, stream));
   return DFLASH_OK;
@@ -485,6 +523,9 @@ dflash_status dflash_pack_weights(const dflash_config* cfg, const dflash_weights
                       stream));
   DF_TRY(pack1(w->w_fuse, m.H, m.F, P.w_fuse));
   DF_TRY(pack1(w->lm_head, m.V, m.H, P.lm_head));
+  DF_TRY(launch_row_norm_max(m.bf16, w->lm_head, m.V, m.H,
+                             reinterpret_cast<float*>(base + P.lm_norms),
+                             reinterpret_cast<float*>(base + P.lm_wmax), stream));
   for (int l = 0; l < m.L; ++l) {
     const size_t lb = P.layer0 + (size_t)l * P.layer_stride;
     DF_TRY(launch_widen(m.bf16, w->attn_norm[l], reinterpret_cast<float*>(base + lb + P.attn_norm),
@@ -931,7 +972,7 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* packed
   // its residual stream, so the LM head runs exactly the draft step's kernel.
   const size_t frag_bytes = align_up((size_t)cdiv(rows, 16) * 16 * m.H * 4);
   const size_t ssq_bytes = align_up((size_t)rows * 4);
-  const size_t key_bytes = align_up(2 * lm_keys_bytes(m, rows));
+  const size_t key_bytes = align_up(3 * lm_keys_bytes(m, rows));
   if (ws_bytes < kSyncBytes + frag_bytes + ssq_bytes + key_bytes) return DFLASH_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   float* xs = reinterpret_cast<float*>(ws + kSyncBytes);

@@ -173,6 +173,14 @@ __device__ inline void top2_merge(unsigned long long& k1, unsigned long long& k2
   k1 = gt ? o1 : k1;
   k2 = n2;
 }
+// Best three keys (k1 > k2 > k3; key 0 = none).
+__device__ inline void top3_push(unsigned long long& k1, unsigned long long& k2,
+                                 unsigned long long& k3, unsigned long long k) {
+  const bool g1 = k > k1, g2 = k > k2, g3 = k > k3;
+  k3 = g2 ? k2 : (g3 ? k : k3);
+  k2 = g1 ? k1 : (g2 ? k : k2);
+  k1 = g1 ? k : k1;
+}
 
 // ---------------------------------------------------------------------------------------
 // Fragment ("swizzled") layout of fp32 activations.  An activation matrix [M][K] that feeds

@@ -101,10 +101,15 @@ struct GemmParams {
   // part = the workgroup's column block; reduced over parts by the finalize kernel.
   unsigned long long* keys;
   unsigned long long* keys2;   // may be null: the runner-up key of each part and row, same layout
+  unsigned long long* keys3;   // refine mode: the third key of each part and row
   int keys_ld;
   float* logits_out;        // [rows][ldo] or null
   int draft_rpr;            // 0: plain rows; else rows are blocks of draft_rpr rows, and
   int draft_nb;             // slot j in 1..draft_nb-1 of block b is logits row b*(nb-1) + j-1
+  // 256-row LM head only: multiply the hi piece of the input alone and leave each column
+  // block's best three keys of those values for launch_argmax_refine, row-major:
+  // keys[row * keys_ld + part] (keys_ld = the number of parts), likewise keys2, keys3.
+  int refine;
   // 128-row kernel with EPI_RESIDUAL, EPI_STORE or EPI_QKV: the k range is split over
   // `ksplit` workgroups per output block (grid.y) and a reduction kernel adds the slices in
   // slice order and applies the epilogue.  Store / residual: slice s writes its fp32 partial
@@ -129,6 +134,35 @@ hipError_t launch_argmax_finalize(const unsigned long long* keys,
                                   const unsigned long long* keys2, int parts, int keys_ld,
                                   int* ids, float* gap, int rows, int draft_rpr, int draft_nb,
                                   hipStream_t stream);
+
+// Exact argmax and top-2 gap of LM-head rows from a refine-mode launch (hi piece only).
+// The bf16 input row is y = (hi + lo) * rstd; the hi-only value of a column differs from its
+// exact value by at most rstd * |lo| * wmax (wmax: the largest LM-head row norm), so every
+// column that can be among a row's top two has a hi value within twice that (plus a
+// bound on both fp32 sums' rounding) of the second-best hi value.  Those columns -- each
+// part's best three, or the whole part when its third-best is within the bound -- are
+// recomputed exactly from the packed weights.  ids / gap / draft rows as for
+// launch_argmax_finalize.
+struct RefineArgs {
+  const unsigned long long* keys;    // [rows][keys_ld] best hi-value key per row and part
+  const unsigned long long* keys2;   // second keys, same layout
+  const unsigned long long* keys3;   // third keys, same layout
+  int parts, keys_ld, part_cols;
+  const void* a;                     // LM-head input rows, pair fragment layout (bf16 pieces)
+  int KT;                            // k-tiles of 32 (hidden / 32)
+  const float* ssq;                  // partial sums of squares of the rows (as the GEMM's)
+  int ssq_parts, ssq_ld;
+  float eps;
+  const char* w;                     // packed LM head
+  long long nt_stride, kt_stride;
+  int vocab;
+  const float* wmax;                 // largest LM-head row norm (device)
+  int* ids;
+  float* gap;
+  int draft_rpr, draft_nb;
+};
+constexpr int kRefineMaxHidden = 8192;
+hipError_t launch_argmax_refine(const RefineArgs& a, int rows, hipStream_t stream);
 
 // Column blocks (argmax parts) of an EPI_ARGMAX launch with this plan.
 inline int argmax_parts(int n_tiles, int mt, int npw, int tgpw) {

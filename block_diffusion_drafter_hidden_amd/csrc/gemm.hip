@@ -933,10 +933,12 @@ union WideSmem {
   float tile[kTallM * (kTallN + 1)];   // epilogue tile: 128 rows of the block
 };
 
-template <int EPI>
+// kQ: bf16 pieces of the input multiplied (2: hi and lo; 1: hi alone, the LM head's
+// refine mode).
+template <int EPI, int kQ>
 __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
   static_assert(EPI == EPI_ARGMAX || EPI == EPI_SWIGLU, "LM head and gate|up");
-  constexpr int kQ = 2;   // bf16 pieces of the input (hi and lo)
+  static_assert(kQ == 2 || EPI == EPI_ARGMAX, "gate|up takes both pieces");
   __shared__ WideSmem sm;
   __shared__ float rstd_s[kWideRows];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1063,14 +1065,15 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
         const int m = rb * kWideRows + rl;
         const float rs = rstd_s[rl];
-        unsigned long long best = 0, second = 0;
+        unsigned long long best = 0, second = 0, third = 0;
 #pragma unroll
         for (int j = 0; j < kTallNT; ++j) {
           const int c = j * 16 + (lane & 15);
           const float v = acc[i][j][e] * rs;
           if (c < cols) {
             const unsigned long long k = argmax_key(v, cb * kTallN + c);
-            top2_push(best, second, k);
+            if constexpr (kQ == 1) top3_push(best, second, third, k);
+            else top2_push(best, second, k);
             if (p.logits_out && m < p.M) {
               const long long orow = p.draft_rpr ? draft_out_row(m, p.draft_rpr, p.draft_nb) : m;
               if (orow >= 0) p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
@@ -1081,11 +1084,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         for (int o = 1; o < 16; o <<= 1) {
           const unsigned long long o1 = __shfl_xor(best, o, kWave);
           const unsigned long long o2 = __shfl_xor(second, o, kWave);
-          top2_merge(best, second, o1, o2);
+          if constexpr (kQ == 1) {
+            const unsigned long long o3 = __shfl_xor(third, o, kWave);
+            top3_push(best, second, third, o1);
+            top3_push(best, second, third, o2);
+            top3_push(best, second, third, o3);
+          } else {
+            top2_merge(best, second, o1, o2);
+          }
         }
         if ((lane & 15) == 0 && m < p.M) {
-          p.keys[(long long)cb * p.keys_ld + m] = best;
-          if (p.keys2) p.keys2[(long long)cb * p.keys_ld + m] = second;
+          if constexpr (kQ == 1) {
+            // refine mode: row-major [row][part], so the refinement reads a row's parts in
+            // one coalesced sweep
+            const long long ki = (long long)m * p.keys_ld + cb;
+            p.keys[ki] = best;
+            p.keys2[ki] = second;
+            p.keys3[ki] = third;
+          } else {
+            p.keys[(long long)cb * p.keys_ld + m] = best;
+            if (p.keys2) p.keys2[(long long)cb * p.keys_ld + m] = second;
+          }
         }
       }
   } else {
@@ -1380,8 +1399,9 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
       if (layers != 1) return hipErrorInvalidValue;
       const int ncb = ncb_t, nrb = nrb_w;
       const int ncb_grid = nrb <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
-      if (epi == EPI_SWIGLU) gemm_tall256<EPI_SWIGLU><<<ncb_grid * nrb, 256, 0, stream>>>(p);
-      else gemm_tall256<EPI_ARGMAX><<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      if (epi == EPI_SWIGLU) gemm_tall256<EPI_SWIGLU, 2><<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      else if (p.refine) gemm_tall256<EPI_ARGMAX, 1><<<ncb_grid * nrb, 256, 0, stream>>>(p);
+      else gemm_tall256<EPI_ARGMAX, 2><<<ncb_grid * nrb, 256, 0, stream>>>(p);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
@@ -1442,6 +1462,204 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
     ids[o] = idx;
     if (gap && keys2) gap[o] = g;
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// LM-head refinement (see RefineArgs): one 256-thread workgroup per row.
+// ------------------------------------------------------------------------------------------
+constexpr int kRefineThreads = 256;
+constexpr int kRefinePartsPerThread = 8;   // parts <= 2048 (vocab <= 262144 at 128 columns)
+constexpr int kRefineMaxCand = 512;        // columns named one by one
+constexpr int kRefineMaxOvf = 32;          // whole parts
+
+__global__ __launch_bounds__(kRefineThreads) void argmax_refine_kernel(RefineArgs a) {
+  __shared__ float y_s[kRefineMaxHidden];
+  __shared__ int cand_s[kRefineMaxCand];
+  __shared__ int ovf_s[kRefineMaxOvf];
+  __shared__ int n_cand, n_ovf;
+  __shared__ unsigned long long red1[kRefineThreads / kWave], red2[kRefineThreads / kWave];
+  __shared__ float fred[2][kRefineThreads / kWave];
+  __shared__ float sq_s[kRefineThreads];
+  constexpr int kWaves = kRefineThreads / kWave;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const long long o = a.draft_rpr ? draft_out_row(m, a.draft_rpr, a.draft_nb) : m;
+  if (o < 0) return;   // uniform over the workgroup
+  const int H = a.KT * 32;
+
+  // Best two hi values of the row over all parts (each part's best three are its keys).
+  unsigned long long k1[kRefinePartsPerThread], k2[kRefinePartsPerThread];
+  unsigned long long k3[kRefinePartsPerThread];
+  const long long kb = (long long)m * a.keys_ld;
+#pragma unroll
+  for (int i = 0; i < kRefinePartsPerThread; ++i) {
+    const int q = tid + i * kRefineThreads;
+    k1[i] = q < a.parts ? a.keys[kb + q] : 0ull;
+    k2[i] = q < a.parts ? a.keys2[kb + q] : 0ull;
+    k3[i] = q < a.parts ? a.keys3[kb + q] : 0ull;
+  }
+  // The row's sum-of-squares partials (thread i holds partial i; at most 256 of them) and
+  // its hi / lo pieces, all requested before any is used.
+  const float sq_i = tid < a.ssq_parts ? a.ssq[(long long)tid * a.ssq_ld + m] : 0.f;
+  const bf16* arow = reinterpret_cast<const bf16*>(a.a);
+  constexpr int kYIt = kRefineMaxHidden / (4 * kRefineThreads);
+  bf16x4 hv[kYIt], lv[kYIt];
+#pragma unroll
+  for (int it = 0; it < kYIt; ++it) {
+    const int k = 4 * (tid + it * kRefineThreads);
+    if (k < H) {
+      const long long off = hilo_off(m, k, a.KT);
+      hv[it] = *reinterpret_cast<const bf16x4*>(arow + off);
+      lv[it] = *reinterpret_cast<const bf16x4*>(arow + off + kHiLoStride);
+    }
+  }
+  unsigned long long best = 0, second = 0;
+#pragma unroll
+  for (int i = 0; i < kRefinePartsPerThread; ++i) top2_merge(best, second, k1[i], k2[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o1 = __shfl_xor(best, off, kWave);
+    const unsigned long long o2 = __shfl_xor(second, off, kWave);
+    top2_merge(best, second, o1, o2);
+  }
+  if (lane == 0) {
+    red1[wave] = best;
+    red2[wave] = second;
+  }
+  if (tid == 0) {
+    n_cand = 0;
+    n_ovf = 0;
+  }
+  sq_s[tid] = sq_i;
+  __syncthreads();
+  // 1 / rms as the GEMM forms it (the partials added in order), the exact input row
+  // y = (hi + lo) * rstd in LDS, and the norms of lo and of y.
+  float ssum = 0.f;
+  for (int i = 0; i < a.ssq_parts; ++i) ssum += sq_s[i];
+  const float rstd = 1.0f / sqrtf(ssum / (float)H + a.eps);
+  float lo2 = 0.f, y2 = 0.f;
+#pragma unroll
+  for (int it = 0; it < kYIt; ++it) {
+    const int k = 4 * (tid + it * kRefineThreads);
+    if (k < H) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lj = (float)lv[it][j];
+        const float yj = ((float)hv[it][j] + lj) * rstd;
+        y_s[k + j] = yj;
+        lo2 += lj * lj;
+        y2 += yj * yj;
+      }
+    }
+  }
+  lo2 = wave_sum(lo2);
+  y2 = wave_sum(y2);
+  if (lane == 0) {
+    fred[0][wave] = lo2;
+    fred[1][wave] = y2;
+  }
+  __syncthreads();
+  best = red1[0];
+  second = red2[0];
+  lo2 = fred[0][0];
+  y2 = fred[1][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    top2_merge(best, second, red1[w], red2[w]);
+    lo2 += fred[0][w];
+    y2 += fred[1][w];
+  }
+  // Candidate threshold: the second-best hi value minus twice the hi-versus-exact bound,
+  // minus the rounding of both fp32 sums (at most H u sum|w y| each, u = 2^-24).
+  const float wmax = *a.wmax;
+  const float beta = rstd * sqrtf(lo2) * wmax;
+  const float ynorm = sqrtf(y2);
+  const float v1 = argmax_key_value(best), v2 = argmax_key_value(second);
+  const float margin = 4.0f * (float)H * 5.9604645e-8f * wmax * ynorm +
+                       1e-6f * (fabsf(v1) + 1.0f);
+  const float tau = v2 - 2.0f * beta - margin;
+#pragma unroll
+  for (int i = 0; i < kRefinePartsPerThread; ++i) {
+    const int q = tid + i * kRefineThreads;
+    if (q >= a.parts) continue;
+    if (k3[i] != 0ull && argmax_key_value(k3[i]) >= tau) {   // more may hide in this part
+      const int s = atomicAdd(&n_ovf, 1);
+      if (s < kRefineMaxOvf) ovf_s[s] = q;
+      continue;
+    }
+    if (k1[i] != 0ull && argmax_key_value(k1[i]) >= tau) {
+      const int s = atomicAdd(&n_cand, 1);
+      if (s < kRefineMaxCand) cand_s[s] = argmax_key_index(k1[i]);
+    }
+    if (k2[i] != 0ull && argmax_key_value(k2[i]) >= tau) {
+      const int s = atomicAdd(&n_cand, 1);
+      if (s < kRefineMaxCand) cand_s[s] = argmax_key_index(k2[i]);
+    }
+  }
+  __syncthreads();
+  const int nc = n_cand, nv = n_ovf;
+  const bool all = nc > kRefineMaxCand || nv > kRefineMaxOvf;   // too many: every column
+  const int work = all ? a.vocab : nc + nv * a.part_cols;
+
+  // Exact value of each listed column: one wave per column, 8-element chunks of the packed
+  // row (tile (v/16, kt), lane (q * 16 + v % 16) holds k = 32 kt + 8 q .. + 8).
+  const int nchunks = a.KT * 4;
+  best = 0ull;
+  second = 0ull;
+  for (int it = wave; it < work; it += kWaves) {
+    int col;
+    if (all) col = it;
+    else if (it < nc) col = cand_s[it];
+    else col = ovf_s[(it - nc) / a.part_cols] * a.part_cols + (it - nc) % a.part_cols;
+    if (col >= a.vocab) continue;   // uniform over the wave
+    const char* wt = a.w + (long long)(col >> 4) * a.nt_stride * kTileBytes;
+    float sacc = 0.f;
+    constexpr int kU = 8;   // chunk loads a lane issues together
+    for (int c0 = 0; c0 < nchunks; c0 += kU * kWave) {
+      i32x4 wv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        const int kt = c >> 2, q = c & 3;
+        wv[u] = c < nchunks ? *reinterpret_cast<const i32x4*>(
+                                  wt + (long long)kt * a.kt_stride * kTileBytes +
+                                  (q * 16 + (col & 15)) * 16)
+                            : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < nchunks) {
+          const bf16x8 wb = __builtin_bit_cast(bf16x8, wv[u]);
+          const float* yk = y_s + (c >> 2) * 32 + (c & 3) * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc += (float)wb[j] * yk[j];
+        }
+      }
+    }
+    sacc = wave_sum(sacc);
+    top2_push(best, second, argmax_key(sacc, col));
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red1[wave] = best;
+    red2[wave] = second;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  best = red1[0];
+  second = red2[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) top2_merge(best, second, red1[w], red2[w]);
+  a.ids[o] = argmax_key_index(best);
+  if (a.gap) a.gap[o] = argmax_key_value(best) - argmax_key_value(second);
+}
+
+hipError_t launch_argmax_refine(const RefineArgs& a, int rows, hipStream_t stream) {
+  if (a.KT * 32 > kRefineMaxHidden || a.parts > kRefineThreads * kRefinePartsPerThread ||
+      a.part_cols != kTallN || !a.keys2 || !a.keys3 || !a.wmax || a.ssq_parts > kRefineThreads)
+    return hipErrorInvalidValue;
+  argmax_refine_kernel<<<rows, kRefineThreads, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax_finalize(const unsigned long long* keys,

@@ -34,6 +34,10 @@ struct EmbedArgs {
 
 hipError_t launch_pack(int bf16_dtype, const PackArgs& a, hipStream_t stream);
 hipError_t launch_widen(int bf16_dtype, const void* src, float* dst, int n, hipStream_t stream);
+// norms[r] = Euclidean norm of row r of the row-major [rows][cols] matrix w (model dtype),
+// *out_max = the largest of them.
+hipError_t launch_row_norm_max(int bf16_dtype, const void* w, int rows, int cols, float* norms,
+                               float* out_max, hipStream_t stream);
 hipError_t launch_embed(int bf16_dtype, const EmbedArgs& a, int rows, hipStream_t stream);
 // Row-major fp32 [rows][cols] -> dst = src * gamma, in the pair fragment layout (hilo = 1,
 // bf16 models) or the fp32 fragment layout with kPer 4 (fp32 models), and ssq[r] = sum of

@@ -87,6 +87,50 @@ __device__ inline float block_sum256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Euclidean norm of every row of a row-major [rows][cols] matrix: one wave per row.
+template <typename T>
+__global__ __launch_bounds__(256) void row_norms_kernel(const T* __restrict__ w, int rows,
+                                                        int cols, float* __restrict__ norms) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (row >= rows) return;
+  const T* r = w + (long long)row * cols;
+  float ss = 0.f;
+  for (int c = lane; c < cols; c += kWave) {
+    const float v = Elem<T>::to_f(r[c]);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) norms[row] = sqrtf(ss);
+}
+
+// The largest of n values, by one workgroup.
+__global__ __launch_bounds__(256) void max_kernel(const float* __restrict__ v, int n,
+                                                  float* __restrict__ out) {
+  __shared__ float red[256];
+  float mx = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) mx = fmaxf(mx, v[i]);
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+hipError_t launch_row_norm_max(int bf16_dtype, const void* w, int rows, int cols, float* norms,
+                               float* out_max, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (bf16_dtype)
+    row_norms_kernel<bf16><<<blocks, 256, 0, stream>>>(reinterpret_cast<const bf16*>(w), rows,
+                                                       cols, norms);
+  else
+    row_norms_kernel<float><<<blocks, 256, 0, stream>>>(reinterpret_cast<const float*>(w), rows,
+                                                        cols, norms);
+  max_kernel<<<1, 256, 0, stream>>>(norms, rows, out_max);
+  return hipGetLastError();
+}
+
 // Block embedding: row b*rpr + j of x is the embedding of the anchor (j = 0) or of the mask
 // token (j >= 1; the padding rows of an 8-token block too), widened to fp32 and written in
 // the fragment layout (4 columns per store), together with x * gamma of the first RMSNorm

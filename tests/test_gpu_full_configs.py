@@ -98,7 +98,7 @@ def draft_and_check(wl, n_injected, n_pool, tag, lm_rows=None):
     torch.cuda.synchronize()
     ids_h, gap_h = ids.cpu().numpy(), gap.cpu().numpy()
     assert ((ids_h >= 0) & (ids_h < cfg.vocab)).all() and (gap_h >= 0).all()
-    orc_ids = {}
+    orc_ids, orc_gaps = {}, {}
     for b in sorted(sampled):
         how = "injected" if b in injected else "read back"
         print(f"[{tag}] oracle request {b} (context {int(ctx[b])}, {how})", flush=True)
@@ -125,7 +125,29 @@ def draft_and_check(wl, n_injected, n_pool, tag, lm_rows=None):
             del ks, vs
             G.check_request(tag, b, ids_h[b], lg_b, gap_h[b], orc, cfg.dtype)
         orc_ids[b] = orc["ids"]
+        orc_gaps[b] = (orc["gap"], orc["top1"], orc["top2"])
     del logits
+    # The same draft without logits: past 4 requests the LM head then multiplies the hi
+    # piece of its input alone and recomputes exactly the columns that can still be among a
+    # row's top two.  Ids and gaps against the oracle on the sampled requests, and against
+    # the call above (both exact fp32 evaluations, in different orders) on every request.
+    ids2 = torch.full((Bn, 15), -7, dtype=torch.int32, device="cuda")
+    gap2 = torch.full((Bn, 15), -1.0, dtype=torch.float32, device="cuda")
+    dr.draft(cache, torch.from_numpy(anchors).cuda(), ids2, None, top2_gap=gap2)
+    torch.cuda.synchronize()
+    ids2_h, gap2_h = ids2.cpu().numpy(), gap2.cpu().numpy()
+    same = ids2_h == ids_h
+    print(f"[{tag}] draft without logits: {int((~same).sum())} ids differ from the logits "
+          f"call (gaps there {gap_h[~same]}), gap difference max "
+          f"{np.abs(gap2_h - gap_h)[same].max():.3e}", flush=True)
+    assert (same | (gap_h < 1e-3)).all()
+    assert np.abs(gap2_h - gap_h)[same].max() < 1e-3
+    for b in sorted(sampled):
+        orc_b = {"ids": orc_ids[b], "gap": orc_gaps[b][0], "top1": orc_gaps[b][1],
+                 "top2": orc_gaps[b][2]}
+        bad, _ = G.compare_ids(ids2_h[b], orc_b, cfg.dtype)
+        agree = ids2_h[b] == orc_ids[b]
+        assert bad == 0 and (np.abs(gap2_h[b] - orc_gaps[b][0])[agree] < G.GAP_TOL).all()
     # Greedy verify of the whole batch against planted targets (the sampled requests' targets
     # are planted from the oracle's drafts, the others from the GPU's).
     base = np.stack([orc_ids.get(b, ids_h[b]) for b in range(Bn)])

@@ -162,6 +162,38 @@ def test_lm_head_argmax_entry_matches_oracle(cfg, rows):
         assert err < 1e-4 * np.abs(lg).max(), err
 
 
+def test_lm_head_refine_planted_ties_and_fallback():
+    """The 256-row LM head without logits (hi piece, then exact recomputation of the columns
+    that can win), on 80 caller rows of the small bf16 model: row 0 has 1000 exactly tied
+    best columns (whole parts recomputed), row 1 has 5000 (more parts than the list holds:
+    every column recomputed), the other rows are ordinary.  Ids against the oracle; the
+    ties go to the lowest index."""
+    cfg = SMALL_BF16
+    rows = 80
+    w = synth.drafter_weights(cfg, seed=4)
+    hidden = synth.normal(f"{cfg.name}/refine-rows", (rows, cfg.hidden), std=1.0, dtype="f32",
+                          seed=4)
+    y = ref.rms_norm(ref.f64(hidden), w["final_norm"], cfg.rms_eps)
+    lm = w["lm_head"].clone()
+    for r, lo_, hi_ in ((0, 1000, 2000), (1, 3000, 8000)):
+        u = torch.from_numpy(y[r] / np.linalg.norm(y[r]) * 0.5).to(lm.dtype)
+        lm[lo_:hi_] = u          # bf16 rows, identical: exact ties in every evaluation
+    w["lm_head"] = lm
+    wd = {k: v.to("cuda") for k, v in w.items()}
+    dr = Drafter(cfg, wd, max_batch=(rows + 15) // 16, max_ctx=16, max_inject_rows=16)
+    ids = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    B.lm_head_argmax(dr.ccfg, dr.packed, hidden.to("cuda"), ids, dr.ws)   # no logits: refine
+    torch.cuda.synchronize()
+    lg = y @ ref.f64(w["lm_head"]).T
+    i1, top1, top2 = ref.top2(lg)
+    orc = {"ids": i1, "gap": top1 - top2, "top1": top1, "top2": top2}
+    got = ids.cpu().numpy()
+    assert i1[0] == 1000 and i1[1] == 3000
+    assert got[0] == 1000 and got[1] == 3000
+    bad, _ = G.compare_ids(got, orc, cfg.dtype)
+    assert bad == 0
+
+
 @pytest.mark.parametrize("n_q,n_kv,d,hidden", [(2, 2, 128, 512), (4, 2, 128, 512),
                                               (8, 2, 128, 512), (16, 2, 128, 512),
                                               (4, 2, 64, 512), (8, 2, 64, 512),
