@@ -37,10 +37,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source flags.  The attention kernels never produce or consume a NaN (scores are finite,
+# masked keys are -inf), so maxima need no NaN quieting.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o",
+           obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -126,7 +126,8 @@ struct HeadState {
   static constexpr int DT = D / 16;   // dim tiles of O^T
   i32x4 qf[KS][2];                    // Q^T fragments (hi, lo), base-2 scaled
   f32x4 o[DT];                        // O^T accumulator: dims 16dt + 4q + i of block row n
-  float m_run, l_run;
+  float m_run;                        // the row's reference maximum (same in its 4 lanes)
+  float l_run;                        // this lane's part of the row's sum (its keys only)
   int q;                              // lane / 16
 
   __device__ void init(const f32x4 (&qraw)[KS][2], float qscale, int lane) {
@@ -160,15 +161,17 @@ struct HeadState {
     }
     const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const float m_new = fmaxf(m_run, rows_max(mx));   // finite: key 0 of a step is valid
-    if (__ballot(m_new > m_run + kRescaleSlack)) {     // always on the first step
+    // The row maximum is formed only when some lane's scores pass its reference by the
+    // slack (a branch uniform over the wave; always on the first step).
+    if (__ballot(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, rows_max(mx));   // finite: key 0 of a step is valid
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
       l_run *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
       m_run = m_new;
     }
-    float pv[8], ps = 0.f;
+    float pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
     if (kMasked) {
@@ -176,9 +179,9 @@ struct HeadState {
       for (int e = 0; e < 8; ++e)
         if (16 * (e / 4) + 4 * q + e % 4 >= nk) pv[e] = 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ps += pv[e];
-    l_run += rows_sum(ps);
+    // The lane keeps its own part of the row sum; the four lanes of a row are added once,
+    // when the partial is stored.
+    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     split8(pv, p_hi, p_lo);
   }
 
@@ -265,10 +268,11 @@ struct HeadState {
     f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (slot * G + hh) * (DT * 4 * kQRows);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) po[(dt * 4 + q) * kQRows + n] = o[dt];
+    const float l_row = rows_sum(l_run);
     if (q == 0) {
       float* ml = a.part_ml + ((slot * G + hh) * kQRows + n) * 2;
       ml[0] = m_run;
-      ml[1] = l_run;
+      ml[1] = l_row;
     }
   }
 };
@@ -354,10 +358,14 @@ __device__ inline ChunkSetup<D> chunk_setup(const AttnArgs& a, char* blk_s,
   return cs;
 }
 
-// Physical page of the chunk's logical page li (wave-uniform li), clamped as above.
+// Physical page of the chunk's logical page li (wave-uniform li), clamped as above.  The
+// index arithmetic is made scalar (li is uniform), so a lookup is a readlane per page-id
+// register and scalar selects.
 template <int D>
 __device__ inline long long chunk_page(const ChunkSetup<D>& cs, int li) {
-  const int lc = max(min(li, cs.npg - 1), 0), reg = lc / kWave, ln = lc % kWave;
+  li = __builtin_amdgcn_readfirstlane(li);
+  const int npg = __builtin_amdgcn_readfirstlane(cs.npg);
+  const int lc = max(min(li, npg - 1), 0), reg = lc / kWave, ln = lc % kWave;
   int page = __builtin_amdgcn_readlane(cs.pid[0], ln);
 #pragma unroll
   for (int r = 1; r < kAttnPidRegs; ++r) {
@@ -487,7 +495,8 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   using L = LdsStep<D, G>;
   constexpr int KS = D / 32, DT = D / 16, NL = L::NL;
   // Register stages (steps ahead).  d = 64 with G = 8 runs two workgroups per CU (four
-  // waves per SIMD, at most 128 registers), which needs the shallower ring.
+  // waves per SIMD, at most 128 registers), which needs the shallower ring (three stages fit
+  // but measured slower: gpt-oss batch 128 20.79 -> 21.64 ms per step).
   constexpr int RS = (D == 64 && G == 8) ? 2 : 4;
   __shared__ __attribute__((aligned(16))) char blk_s[2 * RPR * D * 4];
   __shared__ __attribute__((aligned(16))) char kv_s[2][L::kStepBytes];
@@ -580,8 +589,8 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
       load_pieces(t + i + RS, rs[i]);
-      compute(hs, i & 1, t + i, std::false_type{});   // at least RS more steps follow: full
-      store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
+      compute(hs, (t + i) & 1, t + i, std::false_type{});   // RS more steps follow: full
+      store_pieces((t + i + 1) & 1, rs[(i + 1) % RS]);
       __syncthreads();
     }
   }
@@ -592,8 +601,8 @@ __global__ __launch_bounds__(G * kWave, (D == 64 && G == 8) ? 4 : 2) void attn_p
   for (int i = 0; i < 2 * RS - 1; ++i) {
     if (t + i + 1 < nsteps) {
       if (i < RS && t + i + RS < nsteps) load_pieces(t + i + RS, rs[i % RS]);
-      compute(hs, i & 1, t + i, std::false_type{});
-      store_pieces((i + 1) & 1, rs[(i + 1) % RS]);
+      compute(hs, (t + i) & 1, t + i, std::false_type{});
+      store_pieces((t + i + 1) & 1, rs[(i + 1) % RS]);
       __syncthreads();
     }
   }
