@@ -430,14 +430,20 @@ def extra_measurements(args, dr, s):
     acc = torch.empty(Bn, dtype=torch.int32, device=dev)
     emi = torch.empty((Bn, 16), dtype=torch.int32, device=dev)
     ws = torch.empty(B.verify_sampled_workspace_size(Bn, V), dtype=torch.uint8, device=dev)
-    run = lambda: B.verify_accept_sampled(dl_d, tl_d, ud_d, ua_d, ur_d, d_ids, acc, emi, ws)
-    us = 1000.0 * time_replays(run, s, 20, 3)
+    calls = 4   # back-to-back calls per graph replay, so the replay's own launch cost is
+                # spread over them (the inputs, 1.02 GB, do not fit the memory-side cache)
+
+    def run():
+        for _ in range(calls):
+            B.verify_accept_sampled(dl_d, tl_d, ud_d, ua_d, ur_d, d_ids, acc, emi, ws)
+    us = 1000.0 * time_replays(run, s, 10, 2) / calls
     nbytes = (Bn * 15 + Bn * 16) * V * 4    # every logit read once
     gbs = nbytes / (us * 1e-6) / 1e9
     extra["verify_sampled"] = {
         "shape": f"{Bn} x (15 + 16) x {V} fp32 logits", "us_per_call": round(us, 1),
         "requests_per_s": round(Bn * 1e6 / us, 1), "algorithmic_bytes": int(nbytes),
-        "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4)}
+        "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
+        "method": f"{calls} dependent calls per graph replay"}
     log(f"[bench] temperature-1 verify: {us:.1f} us ({gbs:.0f} GB/s)")
     del dl_d, tl_d, ws
     torch.cuda.empty_cache()

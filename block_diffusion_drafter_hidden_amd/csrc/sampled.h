@@ -19,6 +19,9 @@ struct SampledArgs {
   int* draft_ids;              // [B][15]
   int* accept_len;             // [B]
   int* emitted;                // [B][16]
+  double exp_k[4];             // set by launch_verify_sampled: log2(e) and the fp64
+                               // coefficients of 2^f (kernel arguments live in scalar
+                               // registers, which the fp64 fma takes directly)
 };
 
 // Largest vocabulary of the temperature-1 verify: 4096 chunks of 256 logits, whose

@@ -36,30 +36,25 @@ constexpr int kWC = 4 * kWave;           // elements per wave chunk
 constexpr int kSegWG = 32;               // workgroups per request in kernel 2
 
 // exp(x - m) for x <= m, as 2^y with y = (x - m) log2 e formed by one fp64 fma from
-// c = -m log2 e: 2^n * 2^f with n = round(y) (by adding and subtracting 1.5 * 2^52),
-// f = y - n in [-1/2, 1/2], and 2^f = sum_k (f ln 2)^k / k! to k = 8 (truncation < 2e-10
-// relative; the terms k >= 4, below 6e-4, in fp32), 2^n written into the exponent bits.
-// Results below 2^-1022 are flushed to 0 (far below any decision's resolution).
+// c = -m log2 e: 2^n * 2^f with n = rint(y), f = y - n in [-1/2, 1/2], and
+// 2^f = sum_k (f ln 2)^k / k! to k = 8 (truncation < 2e-10 relative; the terms k >= 4,
+// below 6e-4, in fp32), then scaled by 2^n (ldexp, which also gives the subnormal range;
+// y is clamped at -1100, where the result is 0, so x = -inf gives 0).  The fp64 constants
+// (log2 e, (ln 2)^k / k! for k = 1..3) come in `k` from the kernel arguments.
 constexpr double kLog2eD = 1.4426950408889634074;
-__device__ inline double exp_from(float x, double c) {
-  constexpr double kRound = 6755399441055744.0;   // 1.5 * 2^52
-  constexpr double c1 = 0.69314718055994530942, c2 = 0.24022650695910071233,
-                   c3 = 0.055504108664821579953;
+__device__ inline double exp_from(float x, double c, const double (&k)[4]) {
   constexpr float c4 = 0.0096181291076284771620f, c5 = 0.0013333558146428443423f,
                   c6 = 1.5403530393381609955e-4f, c7 = 1.5252733804059840280e-5f,
                   c8 = 1.3215486790144309489e-6f;
-  const double y = fma((double)x, kLog2eD, c);
-  if (!(y > -1022.0)) return 0.0;
-  const double r = y + kRound;
-  const double f = y - (r - kRound);
+  const double y = __builtin_fmax(fma((double)x, k[0], c), -1100.0);
+  const double n = __builtin_rint(y);
+  const double f = y - n;
   const float ff = (float)f;
   const float q = fmaf(fmaf(fmaf(fmaf(c8, ff, c7), ff, c6), ff, c5), ff, c4);
-  const double p = fma(fma(fma(fma((double)q, f, c3), f, c2), f, c1), f, 1.0);
-  const int ni = (int)(unsigned)(__double_as_longlong(r) & 0xFFFFFFFFull);   // n, exactly
-  return p * __longlong_as_double((long long)(ni + 1023) << 52);
+  const double p = fma(fma(fma(fma((double)q, f, k[3]), f, k[2]), f, k[1]), f, 1.0);
+  return __builtin_ldexp(p, (int)n);
 }
 __device__ inline double neg_scaled(float m) { return -(double)m * kLog2eD; }
-__device__ inline double expw(float x, float m) { return exp_from(x, neg_scaled(m)); }
 
 // Four elements v0 .. v0+3 of a row (v0 % 4 == 0); past V they read as -inf.
 __device__ inline f32x4 load4(const float* x, int v0, int V, bool vec) {
@@ -157,11 +152,13 @@ struct RowWeights {
   int V;
   bool vec;
   float m;
+  const double* ek;
   __device__ void four(int v0, double* e) const {
     const f32x4 v = load4(x, v0, V, vec);
     const double k = neg_scaled(m);
+    const double(&kk)[4] = *reinterpret_cast<const double(*)[4]>(ek);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) e[j] = exp_from(v[j], k);
+    for (int j = 0; j < 4; ++j) e[j] = exp_from(v[j], k, kk);
   }
 };
 
@@ -224,15 +221,15 @@ void sampled_stats_kernel(SampledArgs a) {
     m = fmaxf(m, lm);
     if (__ballot(lm > R + kRaise)) {   // (re)set the reference: rare after the first time
       const float Rn = wave_max_f(lm);
-      s = s * exp_from(R, neg_scaled(Rn));
+      s = s * exp_from(R, neg_scaled(Rn), a.exp_k);
       R = Rn;
     }
     const double k = neg_scaled(R);
     double p = 0.0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      p += (exp_from(v[j][0], k) + exp_from(v[j][1], k)) +
-           (exp_from(v[j][2], k) + exp_from(v[j][3], k));
+      p += (exp_from(v[j][0], k, a.exp_k) + exp_from(v[j][1], k, a.exp_k)) +
+           (exp_from(v[j][2], k, a.exp_k) + exp_from(v[j][3], k, a.exp_k));
     s += p;
     if (is_draft) {
       const double cs = wave_sum_d(p);
@@ -256,7 +253,7 @@ void sampled_stats_kernel(SampledArgs a) {
   for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[i]);
   double S = 0.0;
   for (int i = 0; i < kWaves; ++i)
-    if (sh.wr[i] != -INFINITY) S += sh.ws[i] * exp_from(sh.wr[i], neg_scaled(M));
+    if (sh.wr[i] != -INFINITY) S += sh.ws[i] * exp_from(sh.wr[i], neg_scaled(M), a.exp_k);
   if (threadIdx.x == 0) {
     a.stats[((long long)b * kRows + row) * 2 + 0] = (double)M;
     a.stats[((long long)b * kRows + row) * 2 + 1] = S;
@@ -266,11 +263,11 @@ void sampled_stats_kernel(SampledArgs a) {
   // elements in order (four 256-element slices, one wave scan each).
   const double thr = (double)a.u_draft[(long long)b * kDrafts + row] * S;
   auto r = [&](int c) {
-    return sref[c] == -INFINITY ? 0.0 : ssum[c] * exp_from(sref[c], neg_scaled(M));
+    return sref[c] == -INFINITY ? 0.0 : ssum[c] * exp_from(sref[c], neg_scaled(M), a.exp_k);
   };
   double before;
   int c = block_cross(r, nsc, 0.0, thr, sh.red, sh.pick, &before);
-  const RowWeights rw{x, V, vec, M};
+  const RowWeights rw{x, V, vec, M, a.exp_k};
   int d = -1;
   if (c < nsc) {
     double base = before;
@@ -302,8 +299,9 @@ __device__ int first_rejection(const SampledArgs& a, int b, const double* st) {
     const int d = a.draft_ids[(long long)b * kDrafts + l];
     const float dl = a.draft_logits[((long long)b * kDrafts + l) * V + d];
     const float tl = a.target_logits[((long long)b * kBlock + l) * V + d];
-    const double qd = expw(dl, (float)st[2 * l]) / st[2 * l + 1];
-    const double pd = expw(tl, (float)st[2 * (kDrafts + l)]) / st[2 * (kDrafts + l) + 1];
+    const double qd = exp_from(dl, neg_scaled((float)st[2 * l]), a.exp_k) / st[2 * l + 1];
+    const double pd = exp_from(tl, neg_scaled((float)st[2 * (kDrafts + l)]), a.exp_k) /
+                      st[2 * (kDrafts + l) + 1];
     reject = !((double)a.u_accept[(long long)b * kDrafts + l] * qd < pd);
   }
   const unsigned long long rj = __ballot(reject) | (1ull << kDrafts);
@@ -319,14 +317,16 @@ struct DrawRow {
   double isp, isq;   // 1 / (sum of exp) of the target and draft rows
   int V;
   bool vec, residual;
+  const double* ek;
   __device__ void four(int v0, double* e) const {
     const f32x4 t = load4(tl, v0, V, vec);
     const f32x4 d = residual ? load4(dl, v0, V, vec) : t;
     const double kp = neg_scaled(mp), kq = neg_scaled(mq);
+    const double(&kk)[4] = *reinterpret_cast<const double(*)[4]>(ek);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double p = exp_from(t[j], kp) * isp;
-      const double q = residual ? exp_from(d[j], kq) * isq : 0.0;
+      const double p = exp_from(t[j], kp, kk) * isp;
+      const double q = residual ? exp_from(d[j], kq, kk) * isq : 0.0;
       e[j] = !residual ? p : (p > q ? p - q : 0.0);
     }
   }
@@ -344,6 +344,7 @@ __device__ DrawRow draw_row(const SampledArgs& a, int b, int i, const double* st
   r.dl = r.residual ? a.draft_logits + ((long long)b * kDrafts + i) * V : r.tl;
   r.mq = r.residual ? (float)st[2 * i] : r.mp;
   r.isq = r.residual ? 1.0 / st[2 * i + 1] : r.isp;
+  r.ek = a.exp_k;
   return r;
 }
 
@@ -418,8 +419,13 @@ __global__ __launch_bounds__(kThr) void sampled_draw_kernel(SampledArgs a) {
   if (t == 0) a.accept_len[b] = i + 1;
 }
 
-hipError_t launch_verify_sampled(const SampledArgs& a, int batch, hipStream_t stream) {
-  if (a.vocab <= 0 || a.vocab > kMaxSampledVocab) return hipErrorInvalidValue;
+hipError_t launch_verify_sampled(const SampledArgs& args, int batch, hipStream_t stream) {
+  if (args.vocab <= 0 || args.vocab > kMaxSampledVocab) return hipErrorInvalidValue;
+  SampledArgs a = args;
+  a.exp_k[0] = kLog2eD;
+  a.exp_k[1] = 0.69314718055994530942;    // (ln 2)^k / k!, k = 1, 2, 3
+  a.exp_k[2] = 0.24022650695910071233;
+  a.exp_k[3] = 0.055504108664821579953;
   const int nwc = (a.vocab + kWC - 1) / kWC, nsc = (a.vocab + kSC - 1) / kSC;
   sampled_stats_kernel<<<dim3(kRows, batch), kThr, stats_lds_bytes(nsc), stream>>>(a);
   hipError_t e = hipGetLastError();
