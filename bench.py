@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="time only the drafter prefill of 2048 positions, KV injection "
                          "against the input-fusion variant")
+    ap.add_argument("--verify-sampled", action="store_true",
+                    help="time only the temperature-1 verify (64 x 16 x 128256 logits)")
     ap.add_argument("--kernel-reps", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra measurements of the default run (the Qwen3-8B-shaped "
@@ -91,6 +93,15 @@ def main():
         return latency_bench(args, wl)
     if args.prefill:
         return prefill_bench(args, wl)
+    if args.verify_sampled:
+        s = torch.cuda.Stream(device=torch.device("cuda:0"))
+        out = verify_sampled_timing(torch.device("cuda:0"), s)
+        print(json.dumps({"metric": "temperature-1 verify time", "value": out["us_per_call"],
+                          "unit": "us per call", "n_gpus": 1, "higher_is_better": False,
+                          "dtype": "f32 logits, f64 weights", "data": "synthetic",
+                          "config": {"workload": "llama3.1-8b-shaped-batch64-verify"},
+                          **out}), flush=True)
+        return
     cfg = wl.cfg
     Bn = wl.batch
     ctx = synth.context_lengths(wl)
@@ -419,7 +430,19 @@ def extra_measurements(args, dr, s):
                             "method": f"{calls} dependent calls per graph replay"}
     extra["verify_greedy"] = gv
 
-    # ---------------- temperature-1 verify, 64 x 16 x 128256 ----------------
+    extra["verify_sampled"] = verify_sampled_timing(dev, s)
+
+    extra["prefill_2048"] = prefill_comparison(args, dr, s)
+    return extra
+
+
+def verify_sampled_timing(dev, s):
+    """Temperature-1 verify at 64 x 16 x 128256 fp32 logits (the LLaMA-shaped batch-64
+    configuration), four dependent calls per graph replay."""
+    import torch
+    from block_diffusion_drafter_hidden_amd import binding as B
+    from workloads import WORKLOADS, synth
+
     wl = WORKLOADS["llama_b64"]
     dl, tl, ud, ua, ur = synth.sampled_verify_inputs(wl)
     Bn, V = dl.shape[0], dl.shape[2]
@@ -439,17 +462,14 @@ def extra_measurements(args, dr, s):
     us = 1000.0 * time_replays(run, s, 10, 2) / calls
     nbytes = (Bn * 15 + Bn * 16) * V * 4    # every logit read once
     gbs = nbytes / (us * 1e-6) / 1e9
-    extra["verify_sampled"] = {
-        "shape": f"{Bn} x (15 + 16) x {V} fp32 logits", "us_per_call": round(us, 1),
-        "requests_per_s": round(Bn * 1e6 / us, 1), "algorithmic_bytes": int(nbytes),
-        "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
-        "method": f"{calls} dependent calls per graph replay"}
     log(f"[bench] temperature-1 verify: {us:.1f} us ({gbs:.0f} GB/s)")
+    out = {"shape": f"{Bn} x (15 + 16) x {V} fp32 logits", "us_per_call": round(us, 1),
+           "requests_per_s": round(Bn * 1e6 / us, 1), "algorithmic_bytes": int(nbytes),
+           "achieved_GBs": round(gbs, 1), "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
+           "method": f"{calls} dependent calls per graph replay"}
     del dl_d, tl_d, ws
     torch.cuda.empty_cache()
-
-    extra["prefill_2048"] = prefill_comparison(args, dr, s)
-    return extra
+    return out
 
 
 def prefill_bench(args, wl):
