@@ -77,10 +77,47 @@ def test_block_sizes_bf16_shared_cache_match_oracle(nb):
     G.fill_cache(s.cache, 7, f"blkbf{nb}")
     anchors = synth.anchor_ids(cfg, len(ctx), tag=f"blkbf{nb}-anchor")
     ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
+    # The same draft without logits (at 32 tokens the 96 rows take the 256-row LM head, which
+    # then multiplies the hi piece alone and recomputes the candidate columns exactly).
+    a = torch.as_tensor(np.asarray(anchors, dtype=np.int32)).to("cuda")
+    ids2 = torch.full((len(ctx), nb - 1), -7, dtype=torch.int32, device="cuda")
+    gap2 = torch.full((len(ctx), nb - 1), -1.0, dtype=torch.float32, device="cuda")
+    s.dr.draft(s.cache, a, ids2, None, top2_gap=gap2)
+    torch.cuda.synchronize()
+    ids2, gap2 = ids2.cpu().numpy(), gap2.cpu().numpy()
     for b in range(len(ctx)):
         ks, vs = G.pool_context(s.cache, s.table, b, int(ctx[b]))
         orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
         G.check_request(f"block {nb}", b, ids[b], logits[b], gap[b], orc, cfg.dtype)
+        bad, _ = G.compare_ids(ids2[b], orc, cfg.dtype)
+        agree = ids2[b] == orc["ids"]
+        assert bad == 0 and (np.abs(gap2[b] - orc["gap"])[agree] < G.GAP_TOL).all()
+
+
+def test_block8_batched_rows_take_the_tall_kernels():
+    """Five requests with 8-token blocks: 80 padded rows, so every GEMM runs the 128-row
+    kernel and the LM head the 256-row kernel (with logits: both pieces; without: the hi
+    piece and the refinement), with 7 drafts per request mapped out of 16-row blocks."""
+    nb = 8
+    cfg = scaled(SMALL_BF16, name="variants-bf16-b8x5", block_size=nb)
+    ctx = [33, 0, 190, 16, 77]
+    s = G.build(cfg, ctx, tag="blk8x5", inject=False)
+    G.fill_cache(s.cache, 9, "blk8x5")
+    anchors = synth.anchor_ids(cfg, len(ctx), tag="blk8x5-anchor")
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
+    a = torch.as_tensor(np.asarray(anchors, dtype=np.int32)).to("cuda")
+    ids2 = torch.full((len(ctx), nb - 1), -7, dtype=torch.int32, device="cuda")
+    gap2 = torch.full((len(ctx), nb - 1), -1.0, dtype=torch.float32, device="cuda")
+    s.dr.draft(s.cache, a, ids2, None, top2_gap=gap2)
+    torch.cuda.synchronize()
+    ids2, gap2 = ids2.cpu().numpy(), gap2.cpu().numpy()
+    for b in range(len(ctx)):
+        ks, vs = G.pool_context(s.cache, s.table, b, int(ctx[b]))
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
+        G.check_request("block 8 x 5", b, ids[b], logits[b], gap[b], orc, cfg.dtype)
+        bad, _ = G.compare_ids(ids2[b], orc, cfg.dtype)
+        agree = ids2[b] == orc["ids"]
+        assert bad == 0 and (np.abs(gap2[b] - orc["gap"])[agree] < G.GAP_TOL).all()
 
 
 @pytest.mark.parametrize("nb", [8, 32])
@@ -169,6 +206,25 @@ def test_prefill_input_fusion_tiny_f32_matches_oracle():
         assert bad == 0
         err = np.abs(logits[b] - orc["logits"])
         assert err.max() <= 1e-4 * np.abs(orc["logits"]).max(), err.max()
+
+
+def test_prefill_input_fusion_edge_lengths_tiny_f32():
+    """fp32 tiny model: prefills of 1 position (one group of 1 row and 15 padding rows), 16
+    (one whole group) and 17 (a whole group and a 1-row group), each then drafted over;
+    cache and draft against the oracle."""
+    cfg = TINY
+    s = prefill_setup(cfg, [1, 16, 17], "pf-edges")
+    for b, T in enumerate([1, 16, 17]):
+        prefill_calls(s, b, [T])
+    anchors = synth.anchor_ids(cfg, 3, tag="pf-edges-anchor")
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
+    for b in range(3):
+        ks, vs = ref.prefill_input_fusion(cfg, s.w, s.feats[b])
+        check_prefill_cache(s, b, int(s.ctx_lens[b]), (ks, vs), "prefill edges")
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
+        bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
+        assert bad == 0
+        assert np.abs(logits[b] - orc["logits"]).max() <= 1e-4 * np.abs(orc["logits"]).max()
 
 
 def test_prefill_input_fusion_qwen_shape_bf16_matches_oracle():
