@@ -39,7 +39,7 @@ def hipcc() -> str:
 
 # Per-source flags.  The attention kernels never produce or consume a NaN (scores are finite,
 # masked keys are -inf), so maxima need no NaN quieting.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+EXTRA = {"attention.hip": ["-fno-honor-nans"], "sampled.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

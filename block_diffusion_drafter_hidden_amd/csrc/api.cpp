@@ -1043,6 +1043,7 @@ dflash_status dflash_verify_accept_sampled(const float* draft_logits,
   a.stats = reinterpret_cast<double*>(workspace);
   a.chunk_sums = a.stats + (size_t)batch * 31 * 2;
   a.chunks_ld = (vocab + 255) / 256;
+  a.picks = reinterpret_cast<float*>(a.chunk_sums + (size_t)batch * a.chunks_ld);
   a.draft_ids = draft_ids;
   a.accept_len = accept_len;
   a.emitted = emitted;

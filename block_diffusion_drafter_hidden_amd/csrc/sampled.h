@@ -16,6 +16,8 @@ struct SampledArgs {
   double* chunk_sums;          // [B][chunks_ld] workspace: sums of the final draw's weights
                                // over each 256-element chunk of its row
   int chunks_ld;               // ceil(V / 256)
+  float* picks;                // [B][15][2] workspace: each drawn draft token's draft and
+                               // target logits
   int* draft_ids;              // [B][15]
   int* accept_len;             // [B]
   int* emitted;                // [B][16]
@@ -29,7 +31,7 @@ struct SampledArgs {
 constexpr int kMaxSampledVocab = 4096 * 256;
 
 hipError_t launch_verify_sampled(const SampledArgs& a, int batch, hipStream_t stream);
-// Workspace bytes of launch_verify_sampled (row statistics, then chunk sums).
+// Workspace bytes of launch_verify_sampled (row statistics, chunk sums, picked logits).
 size_t verify_sampled_stats_bytes(int batch, int vocab);
 
 }  // namespace dflash

@@ -13,15 +13,15 @@
 // Kernel 2, kSegWG workgroups per request: each evaluates the accept tests (one lane per
 // draft), finds the first rejection i and writes the chunk sums of the weights the last
 // token is drawn from -- the residual max(0, p_i - q_i), or p_16 when every draft is
-// accepted.  Kernel 3, one workgroup per request: the prefix over those chunk sums and a
-// scan of the crossing chunk draw the token.  Every row is read once, plus 1 KB per draw;
+// accepted.  Kernel 3, one workgroup per request: the prefix over those chunk sums (staged
+// in LDS) and a scan of the crossing chunk draw the token.  Every row is read once, plus 1 KB per draw;
 // the rejected pair is read once more by kernel 2.
 //
 // Weights exp(x - m), sums, prefixes and the accept test are fp64, in a fixed order: with
 // a 128k vocabulary a token's share of the mass is ~1e-5, and fp32 weights (x - m rounded,
 // then exp) err by up to ~1e-6 relative, enough to move a draw into a neighbouring cell.
 // exp runs as 2^((x - m) log2 e) with the exponent split off and a degree-8 Taylor polynomial
-// for 2^f, |f| <= 1/2 (relative error < 2e-10).  A decision then differs from an exact
+// for 2^f, |f| <= 1/2 (relative error < 4e-10).  A decision then differs from an exact
 // evaluation of the rule only when u * total lies within ~1e-9 of the mass of a cumulative
 // boundary, or u * q within ~1e-9 relative of p.
 #include "common.h"
@@ -37,8 +37,8 @@ constexpr int kSegWG = 32;               // workgroups per request in kernel 2
 
 // exp(x - m) for x <= m, as 2^y with y = (x - m) log2 e formed by one fp64 fma from
 // c = -m log2 e: 2^n * 2^f with n = rint(y), f = y - n in [-1/2, 1/2], and
-// 2^f = sum_k (f ln 2)^k / k! to k = 8 (truncation < 2e-10 relative; the terms k >= 4,
-// below 6e-4, in fp32), then scaled by 2^n (ldexp, which also gives the subnormal range;
+// 2^f = sum_k (f ln 2)^k / k! to k = 8 (truncation < 2.1e-10 relative; the terms k >= 4,
+// below 6.6e-4, in fp32, err by < 1.5e-10), then scaled by 2^n (ldexp, which also gives the subnormal range;
 // y is clamped at -1100, where the result is 0, so x = -inf gives 0).  The fp64 constants
 // (log2 e, (ln 2)^k / k! for k = 1..3) come in `k` from the kernel arguments.
 constexpr double kLog2eD = 1.4426950408889634074;
@@ -115,15 +115,11 @@ __device__ int block_cross(R r, int n, double base, double thr, double* red, int
   return n;
 }
 
-// One wave's inverse-CDF scan of the 256 elements of wave chunk c: the first j whose running
-// sum from `base` exceeds thr, else the chunk's last positive weight (or -1).  w.four(v0,
-// e) gives the weights of v0 .. v0 + 3 (0 past the row).
-template <typename W>
-__device__ int wave_scan(const W& w, int c, double base, double thr) {
+// One wave's inverse-CDF scan of the 256 weights of wave chunk c, lane l holding e[0..3] of
+// elements v0 = 256 c + 4 l .. v0 + 3: the first j whose running sum from `base` exceeds
+// thr, else the chunk's last positive weight (or -1).
+__device__ int wave_scan_e(const double (&e)[4], int v0, double base, double thr) {
   const int lane = threadIdx.x % kWave;
-  const int v0 = c * kWC + 4 * lane;
-  double e[4];
-  w.four(v0, e);
   const double t = (e[0] + e[1]) + (e[2] + e[3]);
   double inc = t;
 #pragma unroll
@@ -144,6 +140,15 @@ __device__ int wave_scan(const W& w, int c, double base, double thr) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
   return last;
+}
+// The same scan, loading the weights: w.four(v0, e) gives those of v0 .. v0 + 3 (0 past the
+// row).
+template <typename W>
+__device__ int wave_scan(const W& w, int c, double base, double thr) {
+  const int v0 = c * kWC + 4 * (threadIdx.x % kWave);
+  double e[4];
+  w.four(v0, e);
+  return wave_scan_e(e, v0, base, thr);
 }
 
 // exp(x - m) of a row.
@@ -177,6 +182,8 @@ struct StatsSmem {
   double ws[kWaves];
   double red[kWaves + 1];
   int pick[kWaves];
+  double slice_tot[kWaves];   // the crossing super-chunk's four slice sums
+  int draw;                   // the drawn draft token
 };
 // Dynamic LDS of the stats kernel: the super-chunks' references (floats), then their sums.
 __host__ __device__ inline size_t stats_lds_bytes(int nsc) {
@@ -210,10 +217,7 @@ void sampled_stats_kernel(SampledArgs a) {
   float R = -INFINITY;   // this wave's reference (uniform)
   float m = -INFINITY;   // this lane's maximum
   double s = 0.0;        // this lane's sum of exp(x - R)
-  for (int sc = w; sc < nsc; sc += kWaves) {
-    f32x4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = load4(x, sc * kSC + j * kWC + 4 * lane, V, vec);
+  auto chunk = [&](int sc, const f32x4 (&v)[4]) {
     float lm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -224,13 +228,15 @@ void sampled_stats_kernel(SampledArgs a) {
       s = s * exp_from(R, neg_scaled(Rn), a.exp_k);
       R = Rn;
     }
-    const double k = neg_scaled(R);
     double p = 0.0;
+    if (R != -INFINITY) {   // else every value so far is -inf: weights 0
+      const double k = neg_scaled(R);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      p += (exp_from(v[j][0], k, a.exp_k) + exp_from(v[j][1], k, a.exp_k)) +
-           (exp_from(v[j][2], k, a.exp_k) + exp_from(v[j][3], k, a.exp_k));
-    s += p;
+      for (int j = 0; j < 4; ++j)
+        p += (exp_from(v[j][0], k, a.exp_k) + exp_from(v[j][1], k, a.exp_k)) +
+             (exp_from(v[j][2], k, a.exp_k) + exp_from(v[j][3], k, a.exp_k));
+      s += p;
+    }
     if (is_draft) {
       const double cs = wave_sum_d(p);
       if (lane == 0) {
@@ -238,6 +244,24 @@ void sampled_stats_kernel(SampledArgs a) {
         ssum[sc] = cs;
       }
     }
+  };
+  // Whole super-chunks with plain 16-byte loads (non-temporal: the logits are streamed once;
+  // measured 4% faster), then the row's partial last one (if any) with bounds-checked loads.
+  const int nfull = vec ? V / kSC : 0;
+  int sc = w;
+  for (; sc < nfull; sc += kWaves) {
+    const float* src = x + (long long)sc * kSC + 4 * lane;
+    f32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + j * kWC));
+    chunk(sc, v);
+  }
+  for (; sc < nsc; sc += kWaves) {
+    f32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load4(x, sc * kSC + j * kWC + 4 * lane, V, vec);
+    chunk(sc, v);
   }
   {  // the wave's maximum and sum (against R), then the row's (max, sum)
     const float wmax = wave_max_f(m);
@@ -270,35 +294,52 @@ void sampled_stats_kernel(SampledArgs a) {
   const RowWeights rw{x, V, vec, M, a.exp_k};
   int d = -1;
   if (c < nsc) {
+    // Wave w weighs slice 4 c + w of the crossing super-chunk; the slices' sums, added in
+    // slice order from `before`, name the slice that crosses, whose wave scans it.
+    const int slice = c * 4 + w, v0 = slice * kWC + 4 * lane;
+    double e[4] = {0.0, 0.0, 0.0, 0.0};
+    if (slice * kWC < V) rw.four(v0, e);
+    const double tot = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
+    if (lane == 0) sh.slice_tot[w] = tot;
+    if (threadIdx.x == 0) sh.draw = -1;
+    __syncthreads();
     double base = before;
-    for (int j = 0; j < 4; ++j) {
-      const int slice = c * 4 + j;
-      if (slice * kWC >= V) break;
-      double e[4];
-      rw.four(slice * kWC + 4 * lane, e);
-      const double tot = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
-      if (base + tot > thr) {   // the crossing is in this slice
-        d = wave_scan(rw, slice, base, thr);
+    int js = -1;
+    for (int j = 0; j < 4 && (c * 4 + j) * kWC < V; ++j) {
+      if (base + sh.slice_tot[j] > thr) {
+        js = j;
         break;
       }
-      base += tot;
+      base += sh.slice_tot[j];
     }
+    if (w == js) {
+      const int dd = wave_scan_e(e, v0, base, thr);
+      if (lane == 0) sh.draw = dd;
+    }
+    __syncthreads();
+    d = sh.draw;
   }
   if (d < 0) {   // rounding left no crossing: the last positive weight of the row
     for (int slice = (V + kWC - 1) / kWC - 1; slice >= 0 && d < 0; --slice)
       d = wave_scan(rw, slice, 0.0, INFINITY);
   }
-  if (threadIdx.x == 0) a.draft_ids[(long long)b * kDrafts + row] = d < 0 ? 0 : d;
+  if (threadIdx.x == 0) {
+    if (d < 0) d = 0;
+    a.draft_ids[(long long)b * kDrafts + row] = d;
+    // the drawn token's draft and target logits, for the accept test
+    float* pk = a.picks + ((long long)b * kDrafts + row) * 2;
+    pk[0] = x[d];
+    pk[1] = a.target_logits[((long long)b * kBlock + row) * V + d];
+  }
 }
 
 // The request's accept decisions: one lane per draft, then the first rejection (15 if none).
 __device__ int first_rejection(const SampledArgs& a, int b, const double* st) {
-  const int V = a.vocab, l = threadIdx.x % kWave;
+  const int l = threadIdx.x % kWave;
   bool reject = false;
   if (l < kDrafts) {
-    const int d = a.draft_ids[(long long)b * kDrafts + l];
-    const float dl = a.draft_logits[((long long)b * kDrafts + l) * V + d];
-    const float tl = a.target_logits[((long long)b * kBlock + l) * V + d];
+    const float dl = a.picks[((long long)b * kDrafts + l) * 2 + 0];
+    const float tl = a.picks[((long long)b * kDrafts + l) * 2 + 1];
     const double qd = exp_from(dl, neg_scaled((float)st[2 * l]), a.exp_k) / st[2 * l + 1];
     const double pd = exp_from(tl, neg_scaled((float)st[2 * (kDrafts + l)]), a.exp_k) /
                       st[2 * (kDrafts + l) + 1];
@@ -318,9 +359,8 @@ struct DrawRow {
   int V;
   bool vec, residual;
   const double* ek;
-  __device__ void four(int v0, double* e) const {
-    const f32x4 t = load4(tl, v0, V, vec);
-    const f32x4 d = residual ? load4(dl, v0, V, vec) : t;
+  // The weights of four elements from their target (t) and draft (d) logits.
+  __device__ void weights(const f32x4& t, const f32x4& d, double* e) const {
     const double kp = neg_scaled(mp), kq = neg_scaled(mq);
     const double(&kk)[4] = *reinterpret_cast<const double(*)[4]>(ek);
 #pragma unroll
@@ -329,6 +369,11 @@ struct DrawRow {
       const double q = residual ? exp_from(d[j], kq, kk) * isq : 0.0;
       e[j] = !residual ? p : (p > q ? p - q : 0.0);
     }
+  }
+  __device__ void four(int v0, double* e) const {
+    const f32x4 t = load4(tl, v0, V, vec);
+    const f32x4 d = residual ? load4(dl, v0, V, vec) : t;
+    weights(t, d, e);
   }
 };
 
@@ -348,19 +393,41 @@ __device__ DrawRow draw_row(const SampledArgs& a, int b, int i, const double* st
   return r;
 }
 
-// Kernel 2: the chunk sums of the final draw's weights, kSegWG workgroups per request.
+// Kernel 2: the chunk sums of the final draw's weights, kSegWG workgroups per request.  A
+// wave takes wave chunks w, w + kSegWG * kWaves, ... and issues the loads of up to kSegBatch
+// of them before the first weight.
+constexpr int kSegBatch = 4;
 __global__ __launch_bounds__(kThr) void sampled_segment_kernel(SampledArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
-  const int nwc = (a.vocab + kWC - 1) / kWC;
+  const int V = a.vocab, nwc = (V + kWC - 1) / kWC;
   const double* st = a.stats + (long long)b * kRows * 2;
   const int i = first_rejection(a, b, st);
   const DrawRow dw = draw_row(a, b, i, st);
+  const int nfull = dw.vec ? V / kWC : 0;   // wave chunks read without bounds checks
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  for (int c = g * kWaves + w; c < nwc; c += kSegWG * kWaves) {
-    double e[4];
-    dw.four(c * kWC + 4 * lane, e);
-    const double cs = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
-    if (lane == 0) a.chunk_sums[(long long)b * a.chunks_ld + c] = cs;
+  constexpr int kStride = kSegWG * kWaves;
+  for (int c0 = g * kWaves + w; c0 < nwc; c0 += kSegBatch * kStride) {
+    f32x4 t[kSegBatch], d[kSegBatch];
+#pragma unroll
+    for (int u = 0; u < kSegBatch; ++u) {
+      const int c = c0 + u * kStride, v0 = c * kWC + 4 * lane;
+      if (c < nfull) {
+        t[u] = *reinterpret_cast<const f32x4*>(dw.tl + v0);
+        d[u] = dw.residual ? *reinterpret_cast<const f32x4*>(dw.dl + v0) : t[u];
+      } else if (c < nwc) {
+        t[u] = load4(dw.tl, v0, V, dw.vec);
+        d[u] = dw.residual ? load4(dw.dl, v0, V, dw.vec) : t[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSegBatch; ++u) {
+      const int c = c0 + u * kStride;
+      if (c >= nwc) break;
+      double e[4];
+      dw.weights(t[u], d[u], e);
+      const double cs = wave_sum_d((e[0] + e[1]) + (e[2] + e[3]));
+      if (lane == 0) a.chunk_sums[(long long)b * a.chunks_ld + c] = cs;
+    }
   }
 }
 
@@ -368,14 +435,17 @@ __global__ __launch_bounds__(kThr) void sampled_segment_kernel(SampledArgs a) {
 __global__ __launch_bounds__(kThr) void sampled_draw_kernel(SampledArgs a) {
   __shared__ double red[kWaves + 1];
   __shared__ int pick[kWaves];
-  extern __shared__ double psum[];   // nwc doubles
+  extern __shared__ double psum[];   // nwc doubles: the chunk sums (then p's, below)
   const int b = blockIdx.x;
   const int V = a.vocab, nwc = (V + kWC - 1) / kWC;
   const double* st = a.stats + (long long)b * kRows * 2;
+  const double* cs_g = a.chunk_sums + (long long)b * a.chunks_ld;
+  for (int k = threadIdx.x; k < nwc; k += kThr) psum[k] = cs_g[k];   // the chunk sums
   const int i = first_rejection(a, b, st);
   DrawRow dw = draw_row(a, b, i, st);
-  const double* cs = a.chunk_sums + (long long)b * a.chunks_ld;
   const double u = (double)a.u_resample[b];
+  __syncthreads();
+  const double* cs = psum;
   auto chunk = [&](int k) { return cs[k]; };
   double total;   // the chunk sums in a fixed order (no crossing at +inf)
   block_cross(chunk, nwc, 0.0, INFINITY, red, pick, &total);
@@ -392,7 +462,7 @@ __global__ __launch_bounds__(kThr) void sampled_draw_kernel(SampledArgs a) {
     }
   } else {
     // No residual mass left (possible only by rounding): draw from p_i, whose chunk sums
-    // are formed here.
+    // are formed here, in place of the residual's.
     dw.residual = false;
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
     for (int c = w; c < nwc; c += kWaves) {
@@ -439,7 +509,8 @@ hipError_t launch_verify_sampled(const SampledArgs& args, int batch, hipStream_t
 
 size_t verify_sampled_stats_bytes(int batch, int vocab) {
   const size_t nwc = (size_t)(vocab + kWC - 1) / kWC;
-  return (size_t)batch * (kRows * 2 + nwc) * sizeof(double);
+  return (size_t)batch * (kRows * 2 + nwc) * sizeof(double) +
+         (size_t)batch * kDrafts * 2 * sizeof(float);
 }
 
 }  // namespace dflash

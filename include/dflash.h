@@ -268,7 +268,8 @@ dflash_status dflash_advance(const int32_t* accept_len, const int32_t* bonus, in
 
 /* Workspace bytes for dflash_verify_accept_sampled (0 if batch <= 0 or vocab is outside
  * 1 .. 1048576): the rows' softmax statistics and the final draw's 256-element chunk
- * sums, batch * (62 + ceil(vocab / 256)) doubles. */
+ * sums, batch * (62 + ceil(vocab / 256)) doubles, then each drawn draft token's two
+ * logits, batch * 30 floats. */
 size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
 
 /* Temperature-1 verification (blocks of 16 tokens).
@@ -281,8 +282,8 @@ size_t dflash_verify_sampled_workspace_size(int32_t batch, int32_t vocab);
  * accepted emit the sample of p_16 at u_resample.
  *   draft_ids [batch, 15], accept_len [batch] (number of emitted tokens, 1..16),
  *   emitted [batch, 16] (-1 padded) int32 out.
- * Weights and sums are evaluated in fp64 (exp to ~3e-13 relative), so a decision differs
- * from an exact evaluation only when u * total lies within ~1e-12 of the mass of a
+ * Weights and sums are evaluated in fp64 (exp to below 4e-10 relative), so a decision
+ * differs from an exact evaluation only when u * total lies within ~1e-9 of the mass of a
  * cumulative boundary.  DFLASH_ERR_UNSUPPORTED if vocab > 1048576. */
 dflash_status dflash_verify_accept_sampled(const float* draft_logits,
                                            const float* target_logits, const float* u_draft,

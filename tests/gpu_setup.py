@@ -131,7 +131,7 @@ def compare_ids(gpu_ids, orc, dtype):
 # Temperature-1 verify: a decision is excused when the oracle's margin (distance of u * total
 # to the nearest cumulative boundary, relative to the mass; or |u q - p| relative) is at most
 # this.  Both sides evaluate the weights exp(x - max) and their sums in fp64 (the GPU's exp
-# to ~3e-13 relative), so only margins near 1e-12 can decide differently.
+# to below 4e-10 relative), so only margins below ~4e-10 can decide differently.
 SAMPLED_MARGIN = 1e-9
 LOGIT_MAX = 2e-3
 LOGIT_MEAN = 2.5e-4

@@ -390,3 +390,43 @@ def test_verify_sampled_matches_oracle(batch, vocab):
         assert list(emi[b, :acc[b]]) == o["emitted"] and (emi[b, acc[b]:] == -1).all()
     assert acc[0] == 16
     assert excused <= batch // 2
+
+
+def test_verify_sampled_masked_logits():
+    """Rows with -inf logits (masked tokens) have weight 0: two whole leading 1024-logit
+    super-chunks (waves whose first values are all -inf), a random 30% of every row, and
+    rows with three finite logits; bit-exact against the oracle."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS["llama_b64"]
+    batch, vocab = 3, 5003
+    dl, tl, ud, ua, ur = synth.sampled_verify_inputs(wl, batch=batch, vocab=vocab)
+    dl, tl = torch.as_tensor(dl).numpy().copy(), torch.as_tensor(tl).numpy().copy()
+    dl[0, :, :2048] = -np.inf
+    tl[0, :, :2048] = -np.inf
+    mask = synth.uniforms("masked/mask", (2, 31, vocab), 7) < 0.3
+    dl[1][mask[0, :15]] = -np.inf
+    tl[1][mask[1, :16]] = -np.inf
+    keep = np.array([5, 2500, 5002])
+    tl[2, :, :] = -np.inf
+    tl[2][:, keep] = synth.normal("masked/keep", (16, 3), std=2.0, dtype="f32", seed=7).numpy()
+    dl[2, :, :] = -np.inf   # the draft proposes kept tokens only, close to the target
+    dl[2][:, keep] = tl[2, :15][:, keep] + synth.normal("masked/near", (15, 3), std=0.3,
+                                                        dtype="f32", seed=7).numpy()
+    dl[2, :5] = tl[2, :5]   # q = p: the first five drafts are accepted
+    dev = lambda x: torch.as_tensor(x).cuda().contiguous()
+    ids = torch.empty((batch, 15), dtype=torch.int32, device="cuda")
+    acc = torch.empty(batch, dtype=torch.int32, device="cuda")
+    emi = torch.empty((batch, 16), dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.verify_sampled_workspace_size(batch, vocab), dtype=torch.uint8,
+                     device="cuda")
+    B.verify_accept_sampled(dev(dl), dev(tl), dev(ud), dev(ua), dev(ur), ids, acc, emi, ws)
+    torch.cuda.synchronize()
+    ids, acc, emi = ids.cpu().numpy(), acc.cpu().numpy(), emi.cpu().numpy()
+    for b in range(batch):
+        o = ref.verify_sampled(dl[b], tl[b], ud[b], ua[b], float(ur[b]))
+        assert not [m for m in o["margins"] if m[2] <= G.SAMPLED_MARGIN], b
+        np.testing.assert_array_equal(ids[b], o["draft_ids"])
+        assert acc[b] == o["accept_len"]
+        assert list(emi[b, :acc[b]]) == o["emitted"] and (emi[b, acc[b]:] == -1).all()
+        assert np.isfinite(dl[b][np.arange(15), ids[b]]).all()   # never a masked token
+    assert acc[2] >= 6 and set(emi[2, :acc[2]].tolist()) <= set(keep.tolist())
