@@ -333,6 +333,14 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   const int ke = p.kinter ? p.KT : min(kb + kw, p.KT);
   const int nk = ke > kb ? (ke - kb + kstep - 1) / kstep : 0;
   const int G = (nk + KU - 1) / KU;   // groups of KU k-tiles
+  // LM head: the workgroups of one XCD (dispatch goes round-robin over the 8) start their k
+  // ranges at different k-tiles, so they do not all ask L2 for the same activation lines at
+  // once (measured on the batch-1 draft pass: 192.5 -> 189 us).  Each wave still multiplies
+  // every k-tile of its range once, in a rotated order.  The other GEMMs keep the plain
+  // order (their gain was under 1 us, and their results then depend on the k-split alone,
+  // not on how a call's rows are grouped).
+  int krot = 0;
+  if constexpr (EPI == EPI_ARGMAX) krot = nk > 0 ? (int)(((unsigned)group >> 3) * 5u % (unsigned)nk) : 0;
 
   const char* wp[NPW];
 #pragma unroll
@@ -370,7 +378,9 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   auto load = [&](Group& gr, int g) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int kt = kb + min(g * KU + u, nk - 1) * kstep;
+      int ki = min(g * KU + u, nk - 1) + krot;
+      if (ki >= nk) ki -= nk;
+      const int kt = kb + ki * kstep;
 #pragma unroll
       for (int t = 0; t < NPW; ++t) gr.w[u][t] = load16(wp[t] + (long long)kt * kbytes);
 #pragma unroll
