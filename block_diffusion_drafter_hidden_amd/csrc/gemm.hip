@@ -1620,7 +1620,7 @@ __global__ __launch_bounds__(kRefineThreads) void argmax_refine_kernel(RefineArg
     if (all) col = it;
     else if (it < nc) col = cand_s[it];
     else col = ovf_s[(it - nc) / a.part_cols] * a.part_cols + (it - nc) % a.part_cols;
-    if (col >= a.vocab) continue;   // uniform over the wave
+    if (col < 0 || col >= a.vocab) continue;   // uniform over the wave
     const char* wt = a.w + (long long)(col >> 4) * a.nt_stride * kTileBytes;
     float sacc = 0.f;
     constexpr int kU = 8;   // chunk loads a lane issues together
