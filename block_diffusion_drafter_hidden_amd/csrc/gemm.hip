@@ -929,18 +929,22 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
 // but each of the 4 waves owns 64 rows (4 m-tiles) x the block's 128 columns, so the 8 KB of
 // W a wave reads from LDS per k-tile feed 32 MFMAs per A piece instead of 16, and each W
 // block read from HBM or L2 serves 256 rows.
-//   EPI_ARGMAX: the epilogue runs in registers -- a lane scales its values by the row's
-//   1/rms, keeps the best (value, index) keys (the best two when the runner-up is asked
-//   for) of its column over the 8 n-tiles, and the 16 lanes of a row group reduce with
-//   shuffles.
+//   EPI_ARGMAX, hi piece (refine mode): the block goes through a 128-row LDS tile in two
+//   halves, two threads scan each row for its best three (value, index) keys and merge them
+//   (measured against the in-register selection below: LM-head entry point at 480 rows
+//   747 -> 694 us, at 1920 rows 2873 -> 2630 us).
+//   EPI_ARGMAX, both pieces (logits out): in registers -- a lane scales its values by the
+//   row's 1/rms, keeps the best two (value, index) keys of its column over the 8 n-tiles,
+//   and the 16 lanes of a row group reduce with shuffles.
 //   EPI_SWIGLU (hi + lo pieces): the finished block goes through a 128-row LDS tile in two
 //   halves to the same epilogue as the 128-row kernel.
 // ------------------------------------------------------------------------------------------
 constexpr int kWideRows = 256, kWideMT = kWideRows / 16;
 
+constexpr int kWideLd = kTallN + 4;   // row stride of the selection tile (16-byte rows)
 union WideSmem {
   i32x4 w[2][kTallNT][kWave];          // [buf][n-tile][lane]: packed bf16 B fragments
-  float tile[kTallM * (kTallN + 1)];   // epilogue tile: 128 rows of the block
+  float tile[kTallM * kWideLd];        // epilogue tile: 128 rows of the block
 };
 
 // kQ: bf16 pieces of the input multiplied (2: hi and lo; 1: hi alone, the LM head's
@@ -1067,7 +1071,61 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
 
   // acc[i][j][e]: row 64 wave + 16 i + 4 (lane / 16) + e, column 16 j + lane % 16.
   const int cols = ntv * 16;
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (EPI == EPI_ARGMAX && kQ == 1) {
+    // Refine mode: the best three keys of every (row, 128-column part).  The block goes
+    // through LDS in two 128-row halves; two threads scan one row (64 columns each, in
+    // column order, so among equal values the lower index stays ahead), then merge.  The
+    // keys are those of the in-register selection below (NaN values are never picked).
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wave / 2 == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < kTallNT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = (wave % 2) * 64 + i * 16 + (lane >> 4) * 4 + e;   // row in the half
+              sm.tile[r * kWideLd + j * 16 + (lane & 15)] = acc[i][j][e] * rstd_s[half * kTallM + r];
+            }
+      }
+      __syncthreads();
+      const int r = tid >> 1, c0 = (tid & 1) * 64, cend = min(c0 + 64, cols);
+      float v1 = -INFINITY, v2 = -INFINITY, v3 = -INFINITY;
+      int i1 = -1, i2 = -1, i3 = -1;
+      for (int c = c0; c < cend; c += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.tile[r * kWideLd + c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = x[e];
+          const bool g1 = v > v1, g2 = v > v2, g3 = v > v3;
+          v3 = g2 ? v2 : (g3 ? v : v3);
+          i3 = g2 ? i2 : (g3 ? c + e : i3);
+          v2 = g1 ? v1 : (g2 ? v : v2);
+          i2 = g1 ? i1 : (g2 ? c + e : i2);
+          v1 = g1 ? v : v1;
+          i1 = g1 ? c + e : i1;
+        }
+      }
+      const int base = cb * kTallN;
+      unsigned long long k1 = i1 >= 0 ? argmax_key(v1, base + i1) : 0ull;
+      unsigned long long k2 = i2 >= 0 ? argmax_key(v2, base + i2) : 0ull;
+      unsigned long long k3 = i3 >= 0 ? argmax_key(v3, base + i3) : 0ull;
+      const unsigned long long o1 = __shfl_xor(k1, 1, kWave), o2 = __shfl_xor(k2, 1, kWave),
+                               o3 = __shfl_xor(k3, 1, kWave);
+      top3_push(k1, k2, k3, o1);
+      top3_push(k1, k2, k3, o2);
+      top3_push(k1, k2, k3, o3);
+      const int m = rb * kWideRows + half * kTallM + r;
+      if ((tid & 1) == 0 && m < p.M) {   // row-major [row][part]: one sweep per row later
+        const long long ki = (long long)m * p.keys_ld + cb;
+        p.keys[ki] = k1;
+        p.keys2[ki] = k2;
+        p.keys3[ki] = k3;
+      }
+      __syncthreads();
+    }
+  } else if constexpr (EPI == EPI_ARGMAX) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1075,15 +1133,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         const int rl = wave * 64 + i * 16 + (lane >> 4) * 4 + e;
         const int m = rb * kWideRows + rl;
         const float rs = rstd_s[rl];
-        unsigned long long best = 0, second = 0, third = 0;
+        unsigned long long best = 0, second = 0;
 #pragma unroll
         for (int j = 0; j < kTallNT; ++j) {
           const int c = j * 16 + (lane & 15);
           const float v = acc[i][j][e] * rs;
           if (c < cols) {
-            const unsigned long long k = argmax_key(v, cb * kTallN + c);
-            if constexpr (kQ == 1) top3_push(best, second, third, k);
-            else top2_push(best, second, k);
+            top2_push(best, second, argmax_key(v, cb * kTallN + c));
             if (p.logits_out && m < p.M) {
               const long long orow = p.draft_rpr ? draft_out_row(m, p.draft_rpr, p.draft_nb) : m;
               if (orow >= 0) p.logits_out[orow * p.ldo + cb * kTallN + c] = v;
@@ -1094,27 +1150,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
         for (int o = 1; o < 16; o <<= 1) {
           const unsigned long long o1 = __shfl_xor(best, o, kWave);
           const unsigned long long o2 = __shfl_xor(second, o, kWave);
-          if constexpr (kQ == 1) {
-            const unsigned long long o3 = __shfl_xor(third, o, kWave);
-            top3_push(best, second, third, o1);
-            top3_push(best, second, third, o2);
-            top3_push(best, second, third, o3);
-          } else {
-            top2_merge(best, second, o1, o2);
-          }
+          top2_merge(best, second, o1, o2);
         }
         if ((lane & 15) == 0 && m < p.M) {
-          if constexpr (kQ == 1) {
-            // refine mode: row-major [row][part], so the refinement reads a row's parts in
-            // one coalesced sweep
-            const long long ki = (long long)m * p.keys_ld + cb;
-            p.keys[ki] = best;
-            p.keys2[ki] = second;
-            p.keys3[ki] = third;
-          } else {
-            p.keys[(long long)cb * p.keys_ld + m] = best;
-            if (p.keys2) p.keys2[(long long)cb * p.keys_ld + m] = second;
-          }
+          p.keys[(long long)cb * p.keys_ld + m] = best;
+          if (p.keys2) p.keys2[(long long)cb * p.keys_ld + m] = second;
         }
       }
   } else {
