@@ -132,6 +132,7 @@ Packed packed_layout(const Dims& m) {
 // ---------------------------------------------------------------------------------------
 struct Plan {
   int mt, n_mblocks, npw, ksub, tgpw;
+  bool rows256;   // the fusion over 256-row blocks (gemm_rows256), always through partials
 };
 
 // Rows above which bf16 GEMMs use the 128 x 128 tall kernel (weights read once per 128 rows
@@ -327,17 +328,37 @@ struct InjectPlan {
   size_t c, fpart, total;
 };
 
+// The fusion GEMM (narrow N = H, deep K = F) splits K: over waves at few rows, over
+// workgroups in the 128-row kernel, and from 256 bf16 rows on it runs over 256-row blocks
+// (gemm_rows256) with the k-slices that give 512 workgroups.
+Plan fuse_plan(const Dims& m, int rows) {
+  Plan pl = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
+  if (pl.mt != kTallMT) return pl;
+  const int KT = m.F / m.ktile;
+  if (rows >= 256) {
+    pl.rows256 = true;
+    const long long blocks = (long long)cdiv(m.H / 16, 8) * cdiv(rows, 256);
+    int s = 1;
+    while (blocks * s < 512 && KT / (s * 2) >= 32 && s < 8) s *= 2;
+    pl.ksub = s;
+    return pl;
+  }
+  pl.ksub = ksplit_count(pl, m.H / 16, KT, 512);
+  return pl;
+}
+// Bytes of the fusion's k-slice partials.
+size_t fuse_partial_bytes(const Dims& m, const Plan& pl, int rows) {
+  const int splits = pl.mt == kTallMT ? pl.ksub : 1;
+  return splits > 1 || pl.rows256 ? (size_t)splits * rows * m.H * 4 : 0;
+}
+
 InjectPlan inject_plan(const Dims& m, int rows) {
   InjectPlan p{};
-  // The fusion (narrow N, deep K) splits K: over waves at few rows, over workgroups in the
-  // 128-row kernel.
-  p.fuse = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
-  if (p.fuse.mt == kTallMT) p.fuse.ksub = ksplit_count(p.fuse, m.H / 16, m.F / m.ktile, 512);
+  p.fuse = fuse_plan(m, rows);
   p.kv = plan_gemm(2 * m.nkv * m.d / 16, m.H / m.ktile, rows, 2, m.L, 4, m.bf16 != 0);
   Carver c(kSyncBytes);
   p.c = c.take((size_t)cdiv(rows, 16) * 16 * m.H * 4);   // fragment layout: rows padded
-  const int splits = p.fuse.mt == kTallMT ? p.fuse.ksub : 1;
-  p.fpart = c.take(splits > 1 ? (size_t)splits * rows * m.H * 4 : 0);
+  p.fpart = c.take(fuse_partial_bytes(m, p.fuse, rows));
   p.total = c.off;
   return p;
 }
@@ -364,11 +385,7 @@ DraftPlan prefill_layer_plan(const Dims& m, int groups, int max_ctx) {
   return draft_plan(g, groups, max_ctx);
 }
 
-Plan prefill_fuse_plan(const Dims& m, int rows) {
-  Plan pl = plan_gemm(m.H / 16, m.F / m.ktile, rows, 1, 1, 16, m.bf16 != 0);
-  if (pl.mt == kTallMT) pl.ksub = ksplit_count(pl, m.H / 16, m.F / m.ktile, 512);
-  return pl;
-}
+Plan prefill_fuse_plan(const Dims& m, int rows) { return fuse_plan(m, rows); }
 
 // rows: padded rows of the largest chunk (a multiple of 16, at most kPrefillChunkRows).
 PrefillPlan prefill_plan(const Dims& m, int rows, int max_ctx) {
@@ -379,9 +396,7 @@ PrefillPlan prefill_plan(const Dims& m, int rows, int max_ctx) {
   size_t layers = p.dp.total, part = 0;
   for (int r = 16; r <= rows; r += 16) {
     layers = std::max(layers, prefill_layer_plan(m, r / kQRows, max_ctx).total);
-    const Plan pl = prefill_fuse_plan(m, r);
-    const int splits = pl.mt == kTallMT ? pl.ksub : 1;
-    if (splits > 1) part = std::max(part, (size_t)splits * r * m.H * 4);
+    part = std::max(part, fuse_partial_bytes(m, prefill_fuse_plan(m, r), r));
   }
   Carver c(layers);
   p.fpart = c.take(part);
@@ -573,8 +588,13 @@ size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch,
   if (max_batch < 0 || max_inject_rows < 0 || max_ctx < 0) return 0;
   size_t need = kSyncBytes;
   if (max_batch > 0) need = std::max(need, draft_plan(m, max_batch, max_ctx).total);
-  if (max_inject_rows > 0)
-    need = std::max(need, inject_plan(m, std::min(max_inject_rows, kInjectChunkRows)).total);
+  if (max_inject_rows > 0) {
+    // every injection of up to max_inject_rows rows in one chunk (fewer rows can take more
+    // k-slices of the fusion)
+    const int R = std::min(max_inject_rows, kInjectChunkRows);
+    for (int r = 16; r < R; r += 16) need = std::max(need, inject_plan(m, r).total);
+    need = std::max(need, inject_plan(m, R).total);
+  }
   return need;
 }
 
@@ -619,7 +639,9 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
   for (int r0 = 0; r0 < n_tok; r0 += chunk_rows) {
     const int rows = std::min(chunk_rows, n_tok - r0);
     InjectPlan cp = rows == chunk_rows ? ip : inject_plan(m, rows);
-    if (cp.total > ws_bytes) cp.fuse.ksub = 1;   // a short last chunk's extra k-slices: unsplit
+    // a short last chunk's extra k-slices: unsplit (its partial then needs rows x H floats,
+    // within the first chunk's)
+    if (cp.total > ws_bytes) cp.fuse.ksub = 1;
     {  // fusion of the concatenated target features: c = W_fuse . X (fp32 out)
       GemmParams g = base_params(cp.fuse, wb + P.w_fuse, 0, m.F / m.ktile,
                                  reinterpret_cast<const char*>(feats) + (size_t)r0 * m.F * m.es,
@@ -628,6 +650,7 @@ dflash_status dflash_fuse_inject_kv(const dflash_config* cfg, const void* packed
       g.out = cbuf;
       g.ldo = m.H;
       g.ksplit = cp.fuse.mt == kTallMT ? cp.fuse.ksub : 1;
+      g.rows256 = cp.fuse.rows256;
       g.partial = reinterpret_cast<float*>(ws + cp.fpart);
       DF_TRY(launch_gemm(m.bf16, cp.fuse.mt, cp.fuse.npw, EPI_STORE, g, 1, stream));
     }
@@ -707,6 +730,7 @@ dflash_status dflash_prefill_input_fusion(const dflash_config* cfg, const void* 
       g.out = x;
       g.ldo = m.H;
       g.ksplit = fp.mt == kTallMT ? fp.ksub : 1;
+      g.rows256 = fp.rows256;
       g.partial = reinterpret_cast<float*>(ws + pp.fpart);
       DF_TRY(launch_gemm(m.bf16, fp.mt, fp.npw, EPI_STORE, g, 1, stream));
     }

@@ -118,6 +118,9 @@ struct GemmParams {
   // ksplit <= 1: no split.
   int ksplit;
   float* partial;
+  // bf16 feature rows with EPI_STORE: 256-row blocks (gemm_rows256), always through the
+  // k-slice partials and their reduction (ksplit >= 1).
+  int rows256;
 };
 
 // dtype_bf16: weight type; npw: n-tiles per wave (1, 2 or 4); the A kind and RMSNorm come

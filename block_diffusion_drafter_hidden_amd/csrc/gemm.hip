@@ -1401,6 +1401,133 @@ __global__ __launch_bounds__(256) void ksplit_tile_reduce_kernel(GemmParams p, i
                                              rb * kTileSubs + sub, 0, cb, xpre);
 }
 
+// ------------------------------------------------------------------------------------------
+// The deep-K fusion of bf16 feature rows over 256-row blocks, k split over grid.y: the
+// 256-row LM head's scheme (W staged in LDS per k-tile, each wave's 64 rows of A loaded
+// straight into registers as fragments -- a bf16 row's 16 bytes at k 8 (l / 16) are lane l's
+// fragment -- and every W fragment read from LDS feeding four MFMAs) instead of the 128-row
+// kernel's staging of both operands, whose 64 x 64 wave tiles asked for about the LDS peak.
+// Each slice writes its fp32 partial to partial[slice][row][col]; ksplit_reduce_kernel
+// adds the slices in order.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void gemm_rows256(GemmParams p) {
+  __shared__ i32x4 w_s[2][kTallNT][kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT, nrb = (p.M + kWideRows - 1) / kWideRows;
+  int cb, rb;   // same XCD-aware order as the 128-row kernel
+  if (nrb <= kTallColRows) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    cb = (slot / nrb) * kXcds + xcd;
+    rb = slot % nrb;
+    if (cb >= ncb) return;
+  } else {
+    cb = blockIdx.x % ncb;
+    rb = blockIdx.x / ncb;
+  }
+  const int S = max(p.ksplit, 1), sl = blockIdx.y;
+  const int kb = (sl * p.KT) / S, KT = ((sl + 1) * p.KT) / S - kb;
+  const int ntv = min(kTallNT, p.n_tiles - cb * kTallNT);
+  const char* W = p.W + (long long)(p.nt0 + cb * kTallNT) * p.nt_stride * kTileBytes;
+  // This wave's 4 m-tiles; rows past M re-read row M - 1 (never stored).
+  const bf16* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = min(rb * kWideRows + wave * 64 + i * 16 + (lane & 15), p.M - 1);
+    ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)row * p.lda + (lane >> 4) * 8;
+  }
+  constexpr int kR = 2;
+  i32x4 da[kR][4], dw[kR][2];
+  auto load_a = [&](int kt, i32x4 (&a)[4]) {
+    const long long off = (long long)(kb + min(kt, KT - 1)) * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const i32x4*>(ap[i] + off);
+  };
+  auto load_w = [&](int kt, i32x4 (&w)[2]) {
+    const int ktc = kb + min(kt, KT - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256, nt = min(c / 64, ntv - 1), l = c % 64;
+      w[i] = load16(W + ((long long)nt * p.nt_stride + (long long)ktc * p.kt_stride) *
+                            kTileBytes + l * 16);
+    }
+  };
+  auto store_w = [&](int buf, const i32x4 (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      w_s[buf][c / 64][c % 64] = w[i];
+    }
+  };
+  f32x4 acc[4][kTallNT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kTallNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const i32x4 (&a)[4]) {
+#pragma unroll
+    for (int j = 0; j < kTallNT; ++j) {
+      const i32x4 wf = w_s[buf][j][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_tile<bf16>(a[i], wf, acc[i][j]);
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    load_w(r, dw[r]);
+    load_a(r, da[r]);
+  }
+  store_w(0, dw[0]);
+  __syncthreads();
+  // Iteration kt: W of k-tile kt is in LDS buffer kt & 1; its register stage is refilled
+  // with k-tile kt + kR; W of k-tile kt + 1 moves to the other buffer.
+  const int KTr = KT - KT % kR;
+  for (int kt0 = 0; kt0 < KTr; kt0 += kR) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int kt = kt0 + r;
+      load_w(kt + kR, dw[r]);
+      compute(kt & 1, da[r]);
+      load_a(kt + kR, da[r]);
+      store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kR - 1; ++r) {
+    const int kt = KTr + r;
+    if (kt < KT) {
+      compute(kt & 1, da[r]);
+      store_w((kt + 1) & 1, dw[(r + 1) % kR]);
+      __syncthreads();
+    }
+  }
+  // acc[i][j][e]: row 64 wave + 16 i + 4 (lane / 16) + e, column 16 j + lane % 16.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = rb * kWideRows + wave * 64 + i * 16 + (lane >> 4) * 4 + e;
+      if (m >= p.M) continue;
+      float* dst = p.partial + ((long long)sl * p.M + m) * p.ldo + cb * kTallN + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < kTallNT; ++j)
+        if (j < ntv) dst[j * 16] = acc[i][j][e];
+    }
+}
+
+static hipError_t go_rows256(const GemmParams& p, hipStream_t stream) {
+  const int splits = std::max(p.ksplit, 1);
+  const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
+  const int nrb = (p.M + kWideRows - 1) / kWideRows;
+  if (!p.partial || p.KT < splits || p.ldo % 16 != 0 || p.lda % 8 != 0 || p.M < 1)
+    return hipErrorInvalidValue;
+  const int ncb_grid = nrb <= kTallColRows ? (ncb + kXcds - 1) / kXcds * kXcds : ncb;
+  gemm_rows256<<<dim3(ncb_grid * nrb, splits, 1), 256, 0, stream>>>(p);
+  const long long threads = (long long)p.M * p.n_tiles * 4;
+  ksplit_reduce_kernel<EPI_STORE><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, splits);
+  return hipGetLastError();
+}
+
 template <int AK, int EPI, bool NORM>
 static hipError_t go_tall(const GemmParams& p, int layers, hipStream_t stream) {
   const int ncb = (p.n_tiles + kTallNT - 1) / kTallNT;
@@ -1433,8 +1560,10 @@ hipError_t launch_gemm(int dtype_bf16, int mt, int npw, int epi, const GemmParam
     const bool norm = p.norm != 0;
     if (p.a_kind == A_SWZ && epi == EPI_INJECT && !norm)
       return go_tall<A_SWZ, EPI_INJECT, false>(p, layers, stream);
-    if (p.a_kind == A_ROW_BF16 && epi == EPI_STORE && !norm && p.lda % 8 == 0)
+    if (p.a_kind == A_ROW_BF16 && epi == EPI_STORE && !norm && p.lda % 8 == 0) {
+      if (p.rows256) return layers == 1 ? go_rows256(p, stream) : hipErrorInvalidValue;
       return go_tall<A_ROW_BF16, EPI_STORE, false>(p, layers, stream);
+    }
     if (p.a_kind != A_HILO) return hipErrorInvalidValue;
     if (epi == EPI_RESIDUAL && !norm) return go_tall<A_HILO, EPI_RESIDUAL, false>(p, layers, stream);
     if (epi == EPI_QKV && norm) return go_tall<A_HILO, EPI_QKV, true>(p, layers, stream);
