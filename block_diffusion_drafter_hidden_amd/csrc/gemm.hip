@@ -744,9 +744,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     }
   };
 
-  // Wave tiles.  Staged kinds: 64 x 64 quarters (wm, wn).  Pair layout: a 32-row x 128-column
-  // strip per wave (rows 32 wave .. + 32), so no two waves need the same A fragment.
-  constexpr bool kDirect = AK == A_HILO;
+  // Wave tiles.  Staged kinds: 64 x 64 quarters (wm, wn).  Pair layout and fp32 fragments: a
+  // 32-row x 128-column strip per wave (rows 32 wave .. + 32), so no two waves need the same
+  // A fragment.
+  constexpr bool kDirect = AK == A_HILO || AK == A_SWZ;
   constexpr int MI = kDirect ? 2 : 4, NJ = kDirect ? 8 : 4;
   const int row0 = kDirect ? wave * 32 : wm * 64, col0 = kDirect ? 0 : wn * 64;
   f32x4 acc[MI][NJ];
@@ -760,22 +761,34 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     // hi and lo fragments (1 KB each, coalesced) straight into registers, kR k-tiles ahead.
     // Only W is shared, so only W goes through LDS: 8 KB written and 32 KB read per k-tile
     // instead of 24 KB and 48 KB, with a third of the LDS instructions.
+    // fp32 fragments (the injection's fused features): the lane's 8 values of a k-tile are
+    // two 16-byte halves, split in registers into three bf16 pieces -- by every wave for its
+    // own rows, instead of once per workgroup through LDS (measured: the LDS traffic of the
+    // staged pieces had bound the 512-row injection).
+    constexpr bool kSwz = AK == A_SWZ;
     const bf16* ap[2];
+    const float* af32[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int mtc = min(mtile0 + wave * 2 + i, n_mtiles_valid - 1);
       ap[i] = reinterpret_cast<const bf16*>(p.A) + (long long)mtc * p.KT * 1024 + lane * 8;
+      af32[i] = A + (long long)mtc * p.KT * 512 + lane * 4;
     }
     constexpr int kR = 3;
-    constexpr int kQ = 2;   // pieces per A value (hi and lo)
-    i32x4 da[kR][2][kQ], dw[kR][2];   // [stage][m-tile][piece], [stage][chunk]
-    auto load_a = [&](int kt, i32x4 (&a)[2][kQ]) {
-      const long long off = (long long)(kb + min(kt, KT - 1)) * 1024;
+    constexpr int kQ = kSwz ? 3 : 2;   // pieces per A value (hi and lo; three of an fp32)
+    i32x4 da[kR][2][2], dw[kR][2];   // [stage][m-tile][piece or fp32 half], [stage][chunk]
+    auto load_a = [&](int kt, i32x4 (&a)[2][2]) {
+      const int ktc = kb + min(kt, KT - 1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < kQ; ++q)
-          a[i][q] = *reinterpret_cast<const i32x4*>(ap[i] + off + q * kHiLoStride);
+        for (int q = 0; q < 2; ++q) {
+          if constexpr (kSwz)
+            a[i][q] = *reinterpret_cast<const i32x4*>(af32[i] + ((long long)ktc * 2 + q) * 256);
+          else
+            a[i][q] = *reinterpret_cast<const i32x4*>(ap[i] + (long long)ktc * 1024 +
+                                                       q * kHiLoStride);
+        }
     };
     auto load_w = [&](int kt, i32x4 (&w)[2]) {
       const int ktc = kb + min(kt, KT - 1);
@@ -793,17 +806,39 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
         sm.st.w[buf][c / 64][c % 64] = w[i];
       }
     };
-    // Piece-major MFMA order: the two products into one accumulator are 16 apart.
-    auto compute = [&](int buf, const i32x4 (&a)[2][kQ]) {
+    // Piece-major MFMA order: the products into one accumulator are 16 apart.
+    auto compute = [&](int buf, const i32x4 (&a)[2][2]) {
       i32x4 wf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) wf[j] = sm.st.w[buf][j][lane];
+      i32x4 pc[2][kQ];   // the A pieces of the two m-tiles
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (kSwz) {   // values 0-3 from the first half, 4-7 from the second
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[e] = __int_as_float(a[i][0][e]);
+            f[4 + e] = __int_as_float(a[i][1][e]);
+          }
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            int h[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) h[u] = bf16_pair_split(f[2 * u], f[2 * u + 1]);
+            pc[i][q] = i32x4{h[0], h[1], h[2], h[3]};
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) pc[i][q] = a[i][q];
+        }
+      }
 #pragma unroll
       for (int q = 0; q < kQ; ++q)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = mfma_tile<bf16>(a[i][q], wf[j], acc[i][j]);
+          for (int j = 0; j < 8; ++j) acc[i][j] = mfma_tile<bf16>(pc[i][q], wf[j], acc[i][j]);
     };
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
