@@ -392,6 +392,42 @@ def test_verify_sampled_matches_oracle(batch, vocab):
     assert excused <= batch // 2
 
 
+@pytest.mark.parametrize("vocab", [5003, 4100, 1001])
+def test_verify_sampled_mass_in_the_last_partial_chunk(vocab):
+    """The mass of every row sits in its last 40 logits, so the draft draws, the accept tests
+    and the final draw all land in the row's partial last 1024-logit super-chunk and its last
+    256-logit chunk (bounds-checked loads; 1001 and 5003 are not multiples of 4 either);
+    bit-exact against the oracle."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS["llama_b64"]
+    batch = 4
+    dl, tl, ud, ua, ur = synth.sampled_verify_inputs(wl, batch=batch, vocab=vocab)
+    dl, tl = torch.as_tensor(dl).numpy().copy(), torch.as_tensor(tl).numpy().copy()
+    dl[:, :, -40:] += 12.0
+    tl[:, :, -40:] += 12.0
+    dl[0, :8] = tl[0, :8]   # request 0 accepts its first eight drafts
+    dev = lambda x: torch.as_tensor(x).cuda().contiguous()
+    ids = torch.empty((batch, 15), dtype=torch.int32, device="cuda")
+    acc = torch.empty(batch, dtype=torch.int32, device="cuda")
+    emi = torch.empty((batch, 16), dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.verify_sampled_workspace_size(batch, vocab), dtype=torch.uint8,
+                     device="cuda")
+    B.verify_accept_sampled(dev(dl), dev(tl), dev(ud), dev(ua), dev(ur), ids, acc, emi, ws)
+    torch.cuda.synchronize()
+    ids, acc, emi = ids.cpu().numpy(), acc.cpu().numpy(), emi.cpu().numpy()
+    excused = 0
+    for b in range(batch):
+        o = ref.verify_sampled(dl[b], tl[b], ud[b], ua[b], float(ur[b]))
+        if [m for m in o["margins"] if m[2] <= G.SAMPLED_MARGIN]:
+            excused += 1
+            continue
+        np.testing.assert_array_equal(ids[b], o["draft_ids"])
+        assert acc[b] == o["accept_len"]
+        assert list(emi[b, :acc[b]]) == o["emitted"] and (emi[b, acc[b]:] == -1).all()
+    assert excused <= 1
+    assert (ids >= vocab - 40).mean() > 0.9 and acc[0] >= 9
+
+
 def test_verify_sampled_masked_logits():
     """Rows with -inf logits (masked tokens) have weight 0: two whole leading 1024-logit
     super-chunks (waves whose first values are all -inf), a random 30% of every row, and
