@@ -28,7 +28,7 @@ class Setup:
 
 
 def build(cfg, ctx_lens, tag="t", seed=0, extra=16, weight_std=0.02, gain_std=0.02,
-          inject=True, max_batch=None) -> Setup:
+          inject=True, max_batch=None, max_inject_rows=256) -> Setup:
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
     B = len(ctx_lens)
     w = synth.drafter_weights(cfg, seed=seed, std=weight_std, gain_std=gain_std)
@@ -36,7 +36,7 @@ def build(cfg, ctx_lens, tag="t", seed=0, extra=16, weight_std=0.02, gain_std=0.
     table, num_pages = synth.page_table(f"{cfg.name}/{tag}", ctx_lens + extra, cfg.page_size,
                                         seed, spare_pages=3)
     dr = Drafter(cfg, wd, max_batch=max_batch or B, max_ctx=table.shape[1] * cfg.page_size,
-                 max_inject_rows=256)
+                 max_inject_rows=max_inject_rows)
     cache = dr.new_cache(table, ctx_lens, num_pages)
     feats = [synth.target_features(cfg, int(T), f"{tag}/ctx/b{b}", seed=seed)
              for b, T in enumerate(ctx_lens)]

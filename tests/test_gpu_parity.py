@@ -44,6 +44,12 @@ NARROW_SPLIT = scaled(QWEN3_8B, name="narrow-split", n_layers=2, hidden=576, n_q
                       n_feat_layers=3, target_hidden=576)
 
 
+# Deep fused feature (8 target layers: F = 4096) on a ragged hidden width (576: 4.5 column
+# blocks): from 256 rows the fusion runs over 256-row blocks with its K split in four slices,
+# and a 300-row injection ends in a ragged row block.
+DEEP_FEAT = scaled(NARROW_SPLIT, name="deep-feat", n_feat_layers=8, target_hidden=512)
+
+
 def rel_err(a, b):
     return float(np.abs(a - b).max() / np.sqrt(np.mean(b * b)))
 
@@ -77,9 +83,10 @@ def test_verify_greedy_bit_exact():
 # KV injection
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_OSS])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_OSS, DEEP_FEAT])
 def test_injected_cache_matches_oracle(cfg):
-    s = G.build(cfg, [37, 300, 16], tag="inj")
+    # DEEP_FEAT: a workspace for all 353 rows at once, so the fusion takes the 256-row blocks
+    s = G.build(cfg, [37, 300, 16], tag="inj", max_inject_rows=512 if cfg is DEEP_FEAT else 256)
     for b, T in enumerate(s.ctx_lens):
         ks, vs = ref.prefill_context(cfg, s.w, s.feats[b], precision="exact")
         gk, gv = G.gather_pool(s, b, T, "k"), G.gather_pool(s, b, T, "v")
