@@ -23,7 +23,7 @@ import torch
 import oracle.dflash_oracle as ref
 from block_diffusion_drafter_hidden_amd import Drafter, binding as B
 from tests import gpu_setup as G
-from workloads import TINY, QWEN3_8B, scaled, synth
+from workloads import GPT_OSS_120B, TINY, QWEN3_8B, scaled, synth
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not G.gpu_available(), reason="needs a GPU")]
@@ -65,17 +65,30 @@ def test_block_sizes_tiny_f32_match_oracle(nb):
                                    atol=2e-4 * np.abs(orc["logits"]).max())
 
 
+# gpt-oss head layout (GQA 8, d = 64) and GQA 8 at d = 128, at a small width.
+SMALL_OSS_BF16 = scaled(GPT_OSS_120B, name="variants-oss-bf16", n_layers=2, hidden=512,
+                        n_q_heads=16, n_kv_heads=2, head_dim=64, intermediate=1024,
+                        vocab=8192, n_feat_layers=3, target_hidden=512)
+SMALL_G8_D128_BF16 = scaled(SMALL_BF16, name="variants-g8d128-bf16", n_q_heads=16,
+                            n_kv_heads=2)
+LAYOUTS = {"gqa4-d128": SMALL_BF16, "gqa8-d64": SMALL_OSS_BF16,
+           "gqa8-d128": SMALL_G8_D128_BF16}
+
+
+@pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("nb", [8, 32])
-def test_block_sizes_bf16_shared_cache_match_oracle(nb):
-    """bf16 model with the 8B head layout, seeded shared cache (both sides read the same
-    K/V), three requests with ragged contexts; a block of 32 is two query tiles per request
-    over the same 32 block keys."""
-    cfg = scaled(SMALL_BF16, name=f"variants-bf16-b{nb}", block_size=nb)
+def test_block_sizes_bf16_shared_cache_match_oracle(nb, layout):
+    """bf16 model with the 8B head layout (and the GQA-8 layouts of the gpt-oss shape at
+    d = 64 and of d = 128), seeded shared cache (both sides read the same K/V), three
+    requests with ragged contexts; a block of 32 is two query tiles per request over the
+    same 32 block keys."""
+    cfg = scaled(LAYOUTS[layout], name=f"variants-{layout}-b{nb}", block_size=nb)
     ctx = [200, 17, 0]
-    print(f"[block {nb}] bf16 ctx {ctx}", flush=True)
-    s = G.build(cfg, ctx, tag=f"blkbf{nb}", inject=False)
-    G.fill_cache(s.cache, 7, f"blkbf{nb}")
-    anchors = synth.anchor_ids(cfg, len(ctx), tag=f"blkbf{nb}-anchor")
+    print(f"[block {nb}] bf16 {layout} ctx {ctx}", flush=True)
+    tag = f"blkbf{nb}" if layout == "gqa4-d128" else f"blkbf{nb}-{layout}"
+    s = G.build(cfg, ctx, tag=tag, inject=False)
+    G.fill_cache(s.cache, 7, tag)
+    anchors = synth.anchor_ids(cfg, len(ctx), tag=f"{tag}-anchor")
     ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
     # The same draft without logits (at 32 tokens the 96 rows take the 256-row LM head, which
     # then multiplies the hi piece alone and recomputes the candidate columns exactly).
