@@ -72,16 +72,19 @@ SMALL_OSS_BF16 = scaled(GPT_OSS_120B, name="variants-oss-bf16", n_layers=2, hidd
 SMALL_G8_D128_BF16 = scaled(SMALL_BF16, name="variants-g8d128-bf16", n_q_heads=16,
                             n_kv_heads=2)
 LAYOUTS = {"gqa4-d128": SMALL_BF16, "gqa8-d64": SMALL_OSS_BF16,
-           "gqa8-d128": SMALL_G8_D128_BF16}
+           "gqa8-d128": SMALL_G8_D128_BF16,
+           # groups of one and two heads: fragments loaded straight from the pages
+           "gqa1-d128": scaled(SMALL_BF16, name="variants-g1d128-bf16", n_q_heads=2),
+           "gqa2-d64": scaled(SMALL_OSS_BF16, name="variants-g2d64-bf16", n_q_heads=4)}
 
 
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("nb", [8, 32])
 def test_block_sizes_bf16_shared_cache_match_oracle(nb, layout):
     """bf16 model with the 8B head layout (and the GQA-8 layouts of the gpt-oss shape at
-    d = 64 and of d = 128), seeded shared cache (both sides read the same K/V), three
-    requests with ragged contexts; a block of 32 is two query tiles per request over the
-    same 32 block keys."""
+    d = 64 and of d = 128, and groups of one and two heads), seeded shared cache (both sides
+    read the same K/V), three requests with ragged contexts; a block of 32 is two query
+    tiles per request over the same 32 block keys."""
     cfg = scaled(LAYOUTS[layout], name=f"variants-{layout}-b{nb}", block_size=nb)
     ctx = [200, 17, 0]
     print(f"[block {nb}] bf16 {layout} ctx {ctx}", flush=True)
