@@ -261,6 +261,25 @@ def test_prefill_input_fusion_qwen_shape_bf16_matches_oracle():
                                  logits[b], gap[b], (ks, vs))
 
 
+@pytest.mark.parametrize("layout", ["gqa8-d64", "gqa8-d128", "gqa2-d64", "gqa1-d128"])
+def test_prefill_input_fusion_head_layouts_bf16(layout):
+    """The causal prefill with the other head layouts at a small width (GQA 8 at d = 64 and
+    128 through LDS, groups of two and one head straight from the pages): request 0
+    prefills 72 positions in one call, request 1 73 in two calls (40 + 33).  Cache of every
+    layer, then a draft over it, against the oracle."""
+    cfg = LAYOUTS[layout]
+    s = prefill_setup(cfg, [72, 73], f"pf-{layout}")
+    prefill_calls(s, 0, [72])
+    prefill_calls(s, 1, [40, 73])
+    anchors = synth.anchor_ids(cfg, 2, tag=f"pf-{layout}-anchor")
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
+    for b in range(2):
+        ks, vs, ku, vu = ref.prefill_input_fusion(cfg, s.w, s.feats[b], want_unrounded=True)
+        check_prefill_cache(s, b, int(s.ctx_lens[b]), (ku, vu), f"prefill {layout}")
+        G.check_injected_request(f"prefill {layout}", cfg, s.w, b, int(anchors[b]), ids[b],
+                                 logits[b], gap[b], (ks, vs))
+
+
 def test_prefill_input_fusion_2048_positions_prefix():
     """The benchmark's prefill (2048 positions of the Qwen3-8B-shaped drafter, one call):
     the cache of the first 48 positions depends on those rows only (causal attention), so it
