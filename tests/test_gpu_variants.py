@@ -78,6 +78,31 @@ LAYOUTS = {"gqa4-d128": SMALL_BF16, "gqa8-d64": SMALL_OSS_BF16,
            "gqa2-d64": scaled(SMALL_OSS_BF16, name="variants-g2d64-bf16", n_q_heads=4)}
 
 
+@pytest.mark.parametrize("n_q,n_kv,d", [(8, 2, 64), (16, 2, 64), (4, 2, 128), (8, 2, 128)])
+def test_f32_head_groups_match_oracle(n_q, n_kv, d):
+    """fp32 models with the other head groups of the fp32 attention kernel (GQA 4 and 8 at
+    d = 64, GQA 2 and 4 at d = 128; TINY is GQA 2 at d = 64), injected contexts spanning
+    several 32-key steps with a ragged tail and an empty one: ids, logits and gaps against
+    the oracle as in the TINY block-size test."""
+    cfg = scaled(TINY, name=f"tiny-q{n_q}-kv{n_kv}-d{d}", n_q_heads=n_q, n_kv_heads=n_kv,
+                 head_dim=d)
+    ctx = [150, 0, 77]
+    print(f"[f32 heads] {cfg.name} ctx {ctx}", flush=True)
+    s = G.build(cfg, ctx, tag=f"f32-{cfg.name}")
+    anchors = synth.anchor_ids(cfg, len(ctx), tag=f"f32-{cfg.name}-anchor")
+    ids, logits, gap = G.run_draft(s, anchors, want_logits=True, want_gap=True)
+    for b in range(len(ctx)):
+        ks, vs = G.oracle_context(s, b)
+        orc = ref.draft_block(cfg, s.w, ks, vs, int(anchors[b]), want_logits=True)
+        bad, _ = G.compare_ids(ids[b], orc, cfg.dtype)
+        assert bad == 0, (b, ids[b], orc["ids"])
+        err = np.abs(logits[b] - orc["logits"])
+        assert err.max() <= 1e-4 * np.abs(orc["logits"]).max(), (b, err.max())
+        same = ids[b] == orc["ids"]
+        np.testing.assert_allclose(gap[b][same], orc["gap"][same], rtol=0,
+                                   atol=2e-4 * np.abs(orc["logits"]).max())
+
+
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("nb", [8, 32])
 def test_block_sizes_bf16_shared_cache_match_oracle(nb, layout):
