@@ -939,18 +939,41 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
       }
   __syncthreads();
   if (S > 1) {
-    if constexpr (kRowSplit<EPI>) {   // k-slice partial, row-major [slice][row][column]
-      for (int idx = tid; idx < kTallM * cols; idx += 256) {
-        const int r = idx / cols, c = idx % cols, m = rb * kTallM + r;
-        if (m < p.M)
-          p.partial[((long long)sl * p.M + m) * p.ldo + cb * kTallN + c] = sm.tile[r * ld + c];
+    if constexpr (EPI == EPI_RESIDUAL) {
+      // k-slice partial in the residual stream's fragment layout, [slice][offset of x]: 16-byte
+      // pieces of 4 columns of one row, consecutive threads writing consecutive pieces, so
+      // the reduction reads each slice as contiguously as it reads x (M and the block's
+      // columns are multiples of 16 and 32 here).
+      const int kto = p.ldo / 32, nkt = cols / 32;
+      float* dst = p.partial + (long long)sl * p.M * p.ldo;
+      for (int pc = tid; pc < kTallMT * nkt * 128; pc += 256) {
+        const int ln = pc % 64, jb = (pc / 64) % 2, ktl = (pc / 128) % nkt, mtl = pc / 128 / nkt;
+        const int r = mtl * 16 + (ln & 15), m = rb * kTallM + r;
+        if (m >= p.M) continue;
+        const float* t = sm.tile + r * ld + ktl * 32 + 8 * (ln >> 4) + 4 * jb;
+        const f32x4 v = f32x4{t[0], t[1], t[2], t[3]};
+        *reinterpret_cast<f32x4*>(
+            dst + ((((long long)(m >> 4) * kto + cb * (kTallN / 32) + ktl) * 2 + jb) * 256 + ln * 4)) =
+            v;
+      }
+    } else if constexpr (kRowSplit<EPI>) {   // k-slice partial, row-major [slice][row][column]
+      const int quads = cols / 4;             // 16-byte stores of 4 columns
+      for (int idx = tid; idx < kTallM * quads; idx += 256) {
+        const int r = idx / quads, c = 4 * (idx % quads), m = rb * kTallM + r;
+        if (m >= p.M) continue;
+        const float* t = sm.tile + r * ld + c;
+        *reinterpret_cast<f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo + cb * kTallN +
+                                  c) = f32x4{t[0], t[1], t[2], t[3]};
       }
     } else if constexpr (kTileSplit<EPI>) {   // whole block [slice][block][row][128 columns]
       const long long blk = (long long)rb * ncb + cb;
       float* dst = p.partial + ((long long)sl * ncb * nrb + blk) * (kTallM * kTallN);
-      for (int idx = tid; idx < kTallM * cols; idx += 256) {
-        const int r = idx / cols, c = idx % cols;
-        if (rb * kTallM + r < p.M) dst[r * kTallN + c] = sm.tile[r * ld + c];
+      const int quads = cols / 4;
+      for (int idx = tid; idx < kTallM * quads; idx += 256) {
+        const int r = idx / quads, c = 4 * (idx % quads);
+        if (rb * kTallM + r >= p.M) continue;
+        const float* t = sm.tile + r * ld + c;
+        *reinterpret_cast<f32x4*>(dst + r * kTallN + c) = f32x4{t[0], t[1], t[2], t[3]};
       }
     }
     return;
@@ -1337,12 +1360,13 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
         if (p.xg_out) g[i] = *reinterpret_cast<const f32x4*>(p.gamma_next + col[i]);
       }
     }
+    // The slices' partials are in x's fragment layout (gemm_tall's k-slice epilogue).
     for (int sl = 0; sl < splits; ++sl)
 #pragma unroll
       for (int i = 0; i < kP; ++i)
         if (ok[i])
-          v[i] += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + r) * p.ldo +
-                                                 col[i]);
+          v[i] += *reinterpret_cast<const f32x4*>(p.partial + (long long)sl * p.M * p.ldo +
+                                                 xoff[i]);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < kP; ++i) {
