@@ -132,6 +132,29 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         }
       }
     }
+  } else if constexpr (EPI == EPI_SWIGLU && std::is_same<T, bf16>::value) {
+    // Thread: the 8 outputs of one n-tile for one row -- one lane fragment of the pair
+    // layout, stored as two 16-byte pieces (hi, lo); consecutive threads take consecutive
+    // rows, i.e. consecutive fragments.
+    const int ntl = cols / 16;
+    for (int idx = tid; idx < rows * ntl; idx += nthr) {
+      const int r = idx % rows, jt = idx / rows;
+      const int m = m0 + r;
+      if (m >= p.M) continue;
+      const float* g = tl + r * ld + jt * 16;
+      float h[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) h[c] = silu(g[c]) * g[8 + c];
+      int hi[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        hi[u] = bf16_pair_split(h[2 * u], h[2 * u + 1]);
+        lo[u] = bf16_pair(h[2 * u], h[2 * u + 1]);
+      }
+      bf16* dst = reinterpret_cast<bf16*>(p.out) + hilo_off(m, (tile0 + jt) * 8, kto);
+      *reinterpret_cast<i32x4*>(dst) = i32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<i32x4*>(dst + kHiLoStride) = i32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
     const int half_cols = cols / 2;
     for (int idx = tid; idx < rows * half_cols; idx += nthr) {
