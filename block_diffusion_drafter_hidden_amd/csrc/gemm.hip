@@ -171,6 +171,28 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         reinterpret_cast<float*>(p.out)[swz_off(m, (tile0 + jt) * 8 + c, kto, kPer)] = h;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+    // Each row's position (and the cache page it lands in) is looked up once, into LDS,
+    // instead of by every pair of the row (dependent global loads in the pair loop).
+    constexpr int kEpiRows = 128;
+    static_assert(MT * 16 <= kEpiRows, "rows of an epilogue tile");
+    __shared__ int row_pos[kEpiRows];
+    __shared__ int row_page[kEpiRows];
+    for (int r = tid; r < rows; r += nthr) {
+      const int m = m0 + r;
+      int position = 0, page = 0;
+      if (m < p.M) {
+        if constexpr (EPI == EPI_QKV) {
+          position = p.ctx_lens[m / p.rpr] + m % p.rpr;
+          if (p.k_pool && m < p.kv_rows) page = p.block_table[position / kPage];
+        } else {
+          position = p.pos[m];
+          page = p.block_table[(long long)p.seq_idx[m] * p.max_pages + position / kPage];
+        }
+      }
+      row_pos[r] = position;
+      row_page[r] = page;
+    }
+    __syncthreads();
     const int d = p.head_dim, half = d / 2, tph = d / 16;
     const int pairs = cols / 2;
     for (int idx = tid; idx < rows * pairs; idx += nthr) {
@@ -183,12 +205,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       float a0 = tl[r * ld + jt * 16 + 2 * pp], a1 = tl[r * ld + jt * 16 + 2 * pp + 1];
       const bool rope = EPI == EPI_QKV ? head < p.n_q + p.n_kv : head < p.n_kv;
       int d0, d1;  // head dims of the two columns
-      int position;
-      if constexpr (EPI == EPI_QKV) {
-        position = p.ctx_lens[m / p.rpr] + m % p.rpr;
-      } else {
-        position = p.pos[m];
-      }
+      const int position = row_pos[r];
       if (rope) {
         const int i = 8 * t + pp;
         float cs, sn;
@@ -216,7 +233,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
             a0 = Elem<T>::to_f(Elem<T>::from_f(a0));
             a1 = Elem<T>::to_f(Elem<T>::from_f(a1));
             if (m < p.kv_rows) {
-              const long long page = p.block_table[position / kPage];
+              const long long page = row_page[r];
               const int ps = position % kPage;
               if (is_k) {
                 T* dst = reinterpret_cast<T*>(p.k_pool) + ((page * p.n_kv + h) * kPage + ps) * d;
@@ -240,8 +257,7 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
           }
         }
       } else {
-        const int seq = p.seq_idx[m];
-        const int page = p.block_table[(long long)seq * p.max_pages + position / kPage];
+        const int page = row_page[r];
         const int slot = position % kPage;
         const int h = rope ? head : head - p.n_kv;
         if (rope) {   // K page: [16 slots][d]
