@@ -145,17 +145,32 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   constexpr int kPer = Elem<T>::kPerLane;
   const int KT = a.hidden / (4 * kPer);
   float ss = 0.f;
-  for (int i = 4 * threadIdx.x; i < a.hidden; i += 4 * blockDim.x) {
-    const f32x4 v = {Elem<T>::to_f(e[i]), Elem<T>::to_f(e[i + 1]), Elem<T>::to_f(e[i + 2]),
+  // Four chunks of 4 values per thread per trip, all loaded before the first store.
+  constexpr int kU = 4;
+  for (int i0 = 4 * threadIdx.x; i0 < a.hidden; i0 += 4 * blockDim.x * kU) {
+    f32x4 v[kU], g[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * 4 * blockDim.x;
+      v[u] = g[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < a.hidden) {
+        v[u] = f32x4{Elem<T>::to_f(e[i]), Elem<T>::to_f(e[i + 1]), Elem<T>::to_f(e[i + 2]),
                      Elem<T>::to_f(e[i + 3])};
-    const f32x4 g = *reinterpret_cast<const f32x4*>(a.gamma + i);
-    const long long off = swz_off(m, i, KT, kPer);
-    *reinterpret_cast<f32x4*>(a.x + off) = v;
-    if constexpr (std::is_same<T, bf16>::value)
-      store_hilo4(reinterpret_cast<bf16*>(a.xg), hilo_off(m, i, a.hidden / 32), v * g);
-    else
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.xg) + off) = v * g;
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        g[u] = *reinterpret_cast<const f32x4*>(a.gamma + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * 4 * blockDim.x;
+      if (i >= a.hidden) continue;
+      const long long off = swz_off(m, i, KT, kPer);
+      *reinterpret_cast<f32x4*>(a.x + off) = v[u];
+      if constexpr (std::is_same<T, bf16>::value)
+        store_hilo4(reinterpret_cast<bf16*>(a.xg), hilo_off(m, i, a.hidden / 32), v[u] * g[u]);
+      else
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.xg) + off) = v[u] * g[u];
+      ss += v[u][0] * v[u][0] + v[u][1] * v[u][1] + v[u][2] * v[u][2] + v[u][3] * v[u][3];
+    }
   }
   ss = block_sum256(ss, red);
   if (threadIdx.x == 0) a.ssq[m] = ss;
