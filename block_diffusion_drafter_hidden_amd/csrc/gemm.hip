@@ -48,11 +48,18 @@ __device__ inline i32x4 load16(const void* p) {
 // ------------------------------------------------------------------------------------------
 // Epilogues on the workgroup's dense fp32 tile: rows MT*16, columns cols (tile-major).
 // ------------------------------------------------------------------------------------------
-// Residual values a thread adds in the epilogue, read at kernel start so the epilogue has no
-// dependent global load: iteration i of the epilogue loop uses xpre[i].
+// Residual values (and gains) a thread uses in the epilogue, read at kernel start so the
+// epilogue has no dependent global load: iteration i of the epilogue loop uses element i.
 template <int MT, int NPW>
 struct ResidualPrefetch {
   static constexpr int kN = 4 * NPW * MT <= 8 ? 4 * NPW * MT : 0;   // per thread, ksub = 1 bound
+};
+// The prefetched values of a thread's first N epilogue elements: residual x and the next
+// RMSNorm's gain of the element's column.
+template <int N>
+struct EpiPrefetch {
+  float x[N > 0 ? N : 1];
+  float g[N > 0 ? N : 1];
 };
 
 // `part`: the workgroup's column-block index (the argmax partial it writes).  SG: n-tiles per
@@ -60,7 +67,7 @@ struct ResidualPrefetch {
 // kTallNT: one per 128-column block, the 128-row kernel).
 template <typename T, int MT, int EPI, int NPRE, int SG = 1>
 __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0, int mblock,
-                             int z, int part, const float (&xpre)[NPRE > 0 ? NPRE : 1]) {
+                             int z, int part, const EpiPrefetch<NPRE>& pre) {
   const int rows = MT * 16;
   const int ld = cols + 1;
   const int m0 = mblock * rows;
@@ -70,8 +77,9 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
   constexpr int kPer = Elem<T>::kPerLane;
   const int kto = p.ldo / (4 * kPer);   // k-tiles of the output as the next GEMM's A
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESIDUAL) {
-    // Element idx of the tile; `pre` is its prefetched residual value when known.
-    auto store = [&](int idx, const float* pre) {
+    // Element idx of the tile; `xp` and `gp` are its prefetched residual value and gain when
+    // known.
+    auto store = [&](int idx, const float* xp, const float* gp) {
       const int r = idx / cols, c = idx % cols;
       const int m = m0 + r;
       if (m >= p.M) return;
@@ -80,10 +88,10 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
       if constexpr (EPI == EPI_STORE) {
         *o = tl[r * ld + c];
       } else {
-        const float v = (pre ? *pre : *o) + tl[r * ld + c];
+        const float v = (xp ? *xp : *o) + tl[r * ld + c];
         *o = v;
         if (p.xg_out) {
-          const float xg = v * p.gamma_next[tile0 * 16 + c];
+          const float xg = v * (gp ? *gp : p.gamma_next[tile0 * 16 + c]);
           if constexpr (std::is_same<T, bf16>::value)
             store_hilo(reinterpret_cast<bf16*>(p.xg_out), hilo_off(m, tile0 * 16 + c, kto), xg);
           else
@@ -96,10 +104,10 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
     if constexpr (NPRE > 0) {   // iterations covered by the prefetch (static indices)
 #pragma unroll
       for (int i = 0; i < NPRE; ++i)
-        if (tid + i * nthr < rows * cols) store(tid + i * nthr, &xpre[i]);
+        if (tid + i * nthr < rows * cols) store(tid + i * nthr, &pre.x[i], &pre.g[i]);
       idx0 = tid + NPRE * nthr;
     }
-    for (int idx = idx0; idx < rows * cols; idx += nthr) store(idx, nullptr);
+    for (int idx = idx0; idx < rows * cols; idx += nthr) store(idx, nullptr, nullptr);
     if constexpr (EPI == EPI_RESIDUAL && SG > 1) {
       if (p.xg_out) {   // one partial sum of squares per row over the whole column block
         __syncthreads();
@@ -511,7 +519,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   // Residual values a thread adds in the epilogue (read now, so the epilogue has no
   // dependent global load).
   constexpr int NPRE = EPI == EPI_RESIDUAL ? ResidualPrefetch<MT, NPW>::kN : 0;
-  float xpre[NPRE > 0 ? NPRE : 1];
+  EpiPrefetch<NPRE> pre;
   if constexpr (NPRE > 0) {
     const int rows = MT * 16, cols = p.tgpw * NPW * 16;
     const int kto = p.ldo / (4 * kPer);
@@ -519,10 +527,11 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
     for (int i = 0; i < NPRE; ++i) {
       const int idx = threadIdx.x + i * blockDim.x;
       const int m = mblock * rows + idx / cols;
-      xpre[i] = idx < rows * cols && m < p.M
-                    ? reinterpret_cast<const float*>(p.out)[swz_off(m, wg_tile0 * 16 + idx % cols,
+      const bool ok = idx < rows * cols && m < p.M;
+      pre.x[i] = ok ? reinterpret_cast<const float*>(p.out)[swz_off(m, wg_tile0 * 16 + idx % cols,
                                                                    kto, kPer)]
                     : 0.f;
+      pre.g[i] = ok && p.xg_out ? p.gamma_next[wg_tile0 * 16 + idx % cols] : 0.f;
     }
   }
 
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
         }
   }
   __syncthreads();
-  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, group, xpre);
+  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, group, pre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1017,8 +1026,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tall(GemmParams p) {
     }
     return;
   }
-  const float xpre[1] = {0.f};
-  run_epilogue<bf16, kTallMT, EPI, 0, kTallNT>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, xpre);
+  const EpiPrefetch<0> pre{};
+  run_epilogue<bf16, kTallMT, EPI, 0, kTallNT>(p, sm.tile, cols, cb * kTallNT, rb, z, cb, pre);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1257,7 +1266,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
   } else {
     // Two halves of 128 rows through the LDS tile (which reuses the W buffers).
     const int ld = cols + 1;
-    const float xpre[1] = {0.f};
+    const EpiPrefetch<0> pre{};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (wave / 2 == half) {
@@ -1274,7 +1283,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tall256(GemmParams p) {
       }
       __syncthreads();
       run_epilogue<bf16, kTallMT, EPI, 0, kTallNT>(p, sm.tile, cols, cb * kTallNT, 2 * rb + half,
-                                                  0, cb, xpre);
+                                                  0, cb, pre);
       __syncthreads();
     }
   }
@@ -1494,9 +1503,9 @@ __global__ __launch_bounds__(256) void ksplit_tile_reduce_kernel(GemmParams p, i
     }
   }
   __syncthreads();
-  const float xpre[1] = {0.f};
+  const EpiPrefetch<0> pre{};
   run_epilogue<bf16, kSubRows / 16, EPI, 0>(p, tile, cols, cb * kTallNT,
-                                             rb * kTileSubs + sub, 0, cb, xpre);
+                                             rb * kTileSubs + sub, 0, cb, pre);
 }
 
 // ------------------------------------------------------------------------------------------
