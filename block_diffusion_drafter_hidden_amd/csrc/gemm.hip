@@ -62,10 +62,43 @@ struct EpiPrefetch {
   float g[N > 0 ? N : 1];
 };
 
+// Per-row position and cache page of the Q|K|V and injection epilogues, looked up once per
+// row into LDS (not by every pair of the row): by the epilogue itself, or, in the streaming
+// kernel, at kernel start so the lookups' latency hides under the main loop.
+constexpr int kEpiRows = 128;
+__device__ inline int* epi_row_pos() {
+  __shared__ int buf[kEpiRows];
+  return buf;
+}
+__device__ inline int* epi_row_page() {
+  __shared__ int buf[kEpiRows];
+  return buf;
+}
+template <int EPI>
+__device__ inline void epi_rows_fill(const GemmParams& p, int m0, int rows) {
+  int* row_pos = epi_row_pos();
+  int* row_page = epi_row_page();
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+    const int m = m0 + r;
+    int position = 0, page = 0;
+    if (m < p.M) {
+      if constexpr (EPI == EPI_QKV) {
+        position = p.ctx_lens[m / p.rpr] + m % p.rpr;
+        if (p.k_pool && m < p.kv_rows) page = p.block_table[position / kPage];
+      } else {
+        position = p.pos[m];
+        page = p.block_table[(long long)p.seq_idx[m] * p.max_pages + position / kPage];
+      }
+    }
+    row_pos[r] = position;
+    row_page[r] = page;
+  }
+}
+
 // `part`: the workgroup's column-block index (the argmax partial it writes).  SG: n-tiles per
 // partial sum of squares of the residual epilogue (1: one per n-tile, the streaming kernel;
 // kTallNT: one per 128-column block, the 128-row kernel).
-template <typename T, int MT, int EPI, int NPRE, int SG = 1>
+template <typename T, int MT, int EPI, int NPRE, int SG = 1, bool kRowsFilled = false>
 __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0, int mblock,
                              int z, int part, const EpiPrefetch<NPRE>& pre) {
   const int rows = MT * 16;
@@ -179,28 +212,13 @@ __device__ void run_epilogue(const GemmParams& p, float* tl, int cols, int tile0
         reinterpret_cast<float*>(p.out)[swz_off(m, (tile0 + jt) * 8 + c, kto, kPer)] = h;
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
-    // Each row's position (and the cache page it lands in) is looked up once, into LDS,
-    // instead of by every pair of the row (dependent global loads in the pair loop).
-    constexpr int kEpiRows = 128;
     static_assert(MT * 16 <= kEpiRows, "rows of an epilogue tile");
-    __shared__ int row_pos[kEpiRows];
-    __shared__ int row_page[kEpiRows];
-    for (int r = tid; r < rows; r += nthr) {
-      const int m = m0 + r;
-      int position = 0, page = 0;
-      if (m < p.M) {
-        if constexpr (EPI == EPI_QKV) {
-          position = p.ctx_lens[m / p.rpr] + m % p.rpr;
-          if (p.k_pool && m < p.kv_rows) page = p.block_table[position / kPage];
-        } else {
-          position = p.pos[m];
-          page = p.block_table[(long long)p.seq_idx[m] * p.max_pages + position / kPage];
-        }
-      }
-      row_pos[r] = position;
-      row_page[r] = page;
+    if constexpr (!kRowsFilled) {
+      epi_rows_fill<EPI>(p, m0, rows);
+      __syncthreads();
     }
-    __syncthreads();
+    const int* row_pos = epi_row_pos();
+    const int* row_page = epi_row_page();
     const int d = p.head_dim, half = d / 2, tph = d / 16;
     const int pairs = cols / 2;
     for (int idx = tid; idx < rows * pairs; idx += nthr) {
@@ -373,6 +391,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
   const int wg_tile0 = group * p.tgpw * NPW;
   const int tile0 = wg_tile0 + tg * NPW;
   const int z = blockIdx.z;
+  if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) epi_rows_fill<EPI>(p, mblock * MT * 16, MT * 16);
   // k-tiles of this wave: kb + i * kstep for i < nk.
   const int kw = (p.KT + ksub - 1) / ksub;
   const int kstep = p.kinter ? ksub : 1;
@@ -614,7 +633,7 @@ __global__ __launch_bounds__(NPW >= 8 ? 256 : kMaxGemmThreads) void gemm_stream(
         }
   }
   __syncthreads();
-  run_epilogue<T, MT, EPI, NPRE>(p, sm.tile, cols, wg_tile0, mblock, z, group, pre);
+  run_epilogue<T, MT, EPI, NPRE, 1, true>(p, sm.tile, cols, wg_tile0, mblock, z, group, pre);
 }
 
 // ------------------------------------------------------------------------------------------
