@@ -1427,8 +1427,26 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
         if (p.xg_out) g[i] = *reinterpret_cast<const f32x4*>(p.gamma_next + col[i]);
       }
     }
-    // The slices' partials are in x's fragment layout (gemm_tall's k-slice epilogue).
-    for (int sl = 0; sl < splits; ++sl)
+    // The slices' partials are in x's fragment layout (gemm_tall's k-slice epilogue).  The
+    // first two slices' loads are all in flight together; further slices follow in order.
+    {
+      f32x4 s1[kP];
+#pragma unroll
+      for (int i = 0; i < kP; ++i) {
+        s1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (ok[i]) {
+          v[i] = *reinterpret_cast<const f32x4*>(p.partial + xoff[i]);
+          if (splits > 1)
+            s1[i] = *reinterpret_cast<const f32x4*>(p.partial + (long long)p.M * p.ldo + xoff[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kP; ++i) {
+        v[i] = f32x4{0.f, 0.f, 0.f, 0.f} + v[i];   // the sum starts from 0, as for any slice count
+        if (splits > 1) v[i] += s1[i];
+      }
+    }
+    for (int sl = 2; sl < splits; ++sl)
 #pragma unroll
       for (int i = 0; i < kP; ++i)
         if (ok[i])
@@ -1480,6 +1498,23 @@ __global__ __launch_bounds__(256) void ksplit_tile_reduce_kernel(GemmParams p, i
   const int m0 = rb * kTallM + sub * kSubRows;
   const int rows = min(kSubRows, p.M - m0);
   if (rows <= 0) return;
+  // The first two slices' loads go out first, all in flight together (further slices follow
+  // in order after the norm's sums).
+  const int q4 = cols / 4;   // 16-byte chunks per row
+  const float* src = p.partial + (long long)blk * (kTallM * kTallN) +
+                     (long long)sub * kSubRows * kTallN;
+  const long long sstride = (long long)nblk * (kTallM * kTallN);
+  constexpr int kPer = kSubRows * kTallN / 4 / 256;   // chunks per thread (full block)
+  f32x4 v[kPer], s1[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + j * 256, r = q / q4, c = (q % q4) * 4;
+    v[j] = s1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r < rows) {
+      v[j] = *reinterpret_cast<const f32x4*>(src + r * kTallN + c);
+      if (splits > 1) s1[j] = *reinterpret_cast<const f32x4*>(src + sstride + r * kTallN + c);
+    }
+  }
   if constexpr (NORM) {   // thread t: row t % 32, parts t / 32 + 8 i; then the 8 sums in order
     const int r = tid % kSubRows, m = m0 + r;
     float s = 0.f;
@@ -1496,15 +1531,12 @@ __global__ __launch_bounds__(256) void ksplit_tile_reduce_kernel(GemmParams p, i
     }
     __syncthreads();
   }
-  const int q4 = cols / 4;   // 16-byte chunks per row
-  const float* src = p.partial + (long long)blk * (kTallM * kTallN) +
-                     (long long)sub * kSubRows * kTallN;
-  const long long sstride = (long long)nblk * (kTallM * kTallN);
-  constexpr int kPer = kSubRows * kTallN / 4 / 256;   // chunks per thread (full block)
-  f32x4 v[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sl = 0; sl < splits; ++sl) {
+  for (int j = 0; j < kPer; ++j) {
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f} + v[j];   // the sum starts from 0, as for any slice count
+    if (splits > 1) v[j] += s1[j];
+  }
+  for (int sl = 2; sl < splits; ++sl) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = tid + j * 256, r = q / q4, c = (q % q4) * 4;
