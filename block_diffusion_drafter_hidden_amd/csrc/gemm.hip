@@ -1391,9 +1391,20 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(GemmParams p, int sp
   const int kto = p.ldo / 32;
   auto reduce_quad = [&](int m, int cq) -> f32x4 {
     const int col = cq * 4;
+    // Four slices' loads in flight at a time, added in slice order.
+    constexpr int kU = 4;
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sl = 0; sl < splits; ++sl)
-      v += *reinterpret_cast<const f32x4*>(p.partial + ((long long)sl * p.M + m) * p.ldo + col);
+    for (int s0 = 0; s0 < splits; s0 += kU) {
+      f32x4 t[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        t[u] = s0 + u < splits ? *reinterpret_cast<const f32x4*>(
+                                     p.partial + ((long long)(s0 + u) * p.M + m) * p.ldo + col)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (s0 + u < splits) v += t[u];
+    }
     f32x4* xp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + swz_off(m, col, kto, 8));
     const f32x4 xn = EPI == EPI_RESIDUAL ? *xp + v : v;
     *xp = xn;
